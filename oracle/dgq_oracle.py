@@ -332,9 +332,9 @@ class AppendState:
         self.clamped = 0
 
     def _base(self) -> Optional[SegParams]:
-        if not self.segs:
-            return None
-        return self.segs[-2] if self.span_own else self.segs[-1]
+        """The segment before the open span, or None when the span starts the sequence."""
+        before = self.segs[:-1] if self.span_own else self.segs
+        return before[-1] if before else None
 
     def append(self, k_row: np.ndarray, v_row: np.ndarray) -> None:
         k_row = np.asarray(k_row, dtype=np.float16).reshape(self.head_dim)

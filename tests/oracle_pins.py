@@ -384,6 +384,25 @@ def check_append_matches_prefix_rule(seed=2):
         assert np.array_equal(snap.vcodes, O.encode_by_segment(v, snap.segs, "v"))
 
 
+def check_append_from_empty(block_size=16):
+    """An empty prefix: the first block is segment 0 (no boundary bit at token 0) with the range
+    of its own tokens (numpy min/max); the next blocks are compared with it as usual."""
+    rng = np.random.default_rng(8)
+    k = (rng.standard_normal((3 * block_size, 8)) * 0.2).astype(np.float16)
+    v = (rng.standard_normal((3 * block_size, 8)) * 0.2).astype(np.float16)
+    st = O.AppendState(O.compress_head(k[:0], v[:0]), k[:0], block_size)
+    for t in range(3 * block_size):
+        st.append(k[t], v[t])
+        snap = st.snapshot()
+        first = snap.segs[0]
+        assert first.start == 0 and not snap.bits[0]
+        if t < block_size:
+            assert len(snap.segs) == 1
+            assert first.kmin == np.min(k[:t + 1]).astype(np.float32) and first.kmax == np.max(k[:t + 1]).astype(np.float32)
+    assert list(np.flatnonzero(snap.bits)) == snap.starts[1:]
+    assert np.array_equal(snap.kcodes, O.encode_by_segment(k, snap.segs, "k"))
+
+
 # -- group-64 baseline -----------------------------------------------------------------------------
 
 def check_group64():
@@ -405,5 +424,5 @@ ALL_CHECKS = [
     check_selection_twin, check_step_change_cut, check_segment_invariants, check_tiny_recovery,
     check_minmax_library, check_bits, check_codes, check_constant_segment_exact,
     check_dequant_closed_form, check_attention, check_append_join, check_append_cut,
-    check_append_capacity, check_append_matches_prefix_rule, check_group64,
+    check_append_capacity, check_append_matches_prefix_rule, check_append_from_empty, check_group64,
 ]
