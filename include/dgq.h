@@ -1,0 +1,218 @@
+/*
+ * dgq.h -- C ABI of libdgq: dynamic-group INT8 compression of the attention KV cache and paged
+ * INT8 decode attention, for AMD Instinct MI355X (gfx950).
+ *
+ * Sources of the method (titles of the pages; addresses for the reader):
+ *   DGQ article           http://www.pptc.cn/news/101026  -- section 2.2 (per-head variance curve,
+ *                         16-token sliding window, 3~5 segments cut at variance change points,
+ *                         per-segment min/max, INT8 codes, 1-bit segment identifier), section 3.1
+ *                         (dequantize inside the paged attention step), section 3.2 (identifier
+ *                         storage), section 3.3 (memory formula: 1 byte per element + 1 bit per
+ *                         token per head).
+ *   PagedAttention article https://deepseek.csdn.net/6a0bbfa610ee7a33f27399ed.html -- logical
+ *                         blocks mapped to discrete physical blocks through a block table with a
+ *                         free list; block-granular allocation; paged forward pass with
+ *                         block_tables; 64-token blocks for long contexts.
+ *   Quantization article  http://cnnetsun.cn/a/2561798 -- section 2.1 asymmetric quantization
+ *                         template clamp(round(x / scale) + zero_point, lo, hi).
+ *
+ * Conventions for every entry point
+ *   - Device pointers are caller-owned HIP device memory; the library never allocates or frees
+ *     device memory and never synchronizes a stream.  Work is queued on `stream` in order.
+ *   - Host pointers are marked (host).  The block pool handle is owned by the library until
+ *     dgq_pool_destroy.
+ *   - Every call returns a dgq_status_t.  Arguments are checked on the host before anything is
+ *     queued; a failed check queues nothing and writes nothing.  A failed kernel launch returns
+ *     DGQ_ERR_HIP; dgq_last_error() gives the HIP error text of the calling thread's last failure.
+ *   - Conditions that depend on device data are never turned into errors: they are counted in
+ *     the cache's status words (see dgq_cache_t.status), which the caller reads after a sync.
+ *   - Device data is not trusted to be consistent: a block id outside the pool, a sequence length
+ *     above max_seq_len or a cu_seqlens entry outside the input is never followed out of bounds;
+ *     it is skipped or clamped and counted in status[2], and the affected results are unspecified.
+ *   - fp16 data is passed as uint16_t (IEEE binary16 bit patterns).
+ *
+ * Paged layout (per layer; the block table is shared by all layers)
+ *   k_pool, v_pool: int8 [num_blocks][num_kv_heads][block_size * head_dim].  One (block, head)
+ *   tile holds the codes of block_size tokens.  Inside a tile the codes are stored in the order
+ *   the decode kernel's matrix-core instructions consume them, so that every wave-wide 16-byte
+ *   load reads 256 contiguous bytes or more.  With M = head_dim / 64, a token tau of the block
+ *   (0 <= tau < block_size) and a channel d:
+ *     K, block_size 64: T = tau/16, r = tau%16, m = d/64, j = (d%64)/16, e = d%16
+ *                       offset = (((T*M + m)*4 + j)*16 + r)*16 + e
+ *     K, block_size 16: T = tau/4, i = tau%4 (m, j, e as above)
+ *                       offset = ((((T*M + m)*4 + j)*4 + i)*16) + e
+ *     V, block_size 64: n = d/16, r = d%16, j = (tau%16)/4, e = 4*(tau/16) + tau%4
+ *                       offset = ((n*4 + j)*16 + r)*16 + e
+ *     V, block_size 16: offset = d*16 + tau
+ *   A code is the signed byte c in [-128, 127]; the value it stands for is (c + 128) * scale + min
+ *   with the (scale, min) of the token's segment.
+ *   bits: uint8 [num_blocks][num_kv_heads][block_size/8]; bit (tau % 8) of byte tau/8 is 1 iff
+ *   the token starts a segment other than the first (the 1-bit identifier, kept in its own
+ *   tensor as in the DGQ article's original scheme).
+ */
+#ifndef DGQ_H
+#define DGQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum dgq_status {
+  DGQ_OK = 0,
+  DGQ_ERR_INVALID_ARG = -1,         /* null pointer, bad size, misaligned buffer, bad stride */
+  DGQ_ERR_UNSUPPORTED = -2,         /* valid but unsupported shape (head_dim, block_size, group) */
+  DGQ_ERR_POOL_EXHAUSTED = -3,      /* not enough free blocks; nothing was allocated */
+  DGQ_ERR_WORKSPACE_TOO_SMALL = -4, /* ws_bytes below the matching *_workspace_size() */
+  DGQ_ERR_HIP = -5                  /* a HIP call failed; see dgq_last_error() */
+} dgq_status_t;
+
+/* Shape and method parameters, passed to every call.  Defaults: win 16, max_segments 5,
+ * seg_capacity 16, tau 2.0. */
+typedef struct dgq_params {
+  int32_t num_kv_heads;  /* >= 1 */
+  int32_t num_q_heads;   /* num_kv_heads * G with G in {1, 2, 4}; query head g uses kv head g / G */
+  int32_t head_dim;      /* 64 or 128 */
+  int32_t block_size;    /* tokens per physical block: 16 or 64 */
+  int32_t win;           /* sliding-window length of the variance curve; must be 16 (DGQ 2.2) */
+  int32_t max_segments;  /* 1..8 segments per (sequence, kv head) from dgq_compress */
+  int32_t seg_capacity;  /* segment-table rows per (sequence, kv head): max_segments..64 */
+  int32_t reserved;      /* must be 0 */
+  double tau;            /* change-point threshold on the window-variance ratio, finite, >= 1 */
+} dgq_params_t;
+
+/* One segment-table row (32 bytes).  kscale = fp32((kmax - kmin) / 255), likewise vscale. */
+typedef struct dgq_seg {
+  int32_t start;         /* first token of the segment */
+  float kmin, kmax, vmin, vmax;
+  float kscale, vscale;
+  int32_t reserved;
+} dgq_seg_t;
+
+/* Append state of one (sequence, kv head), 208 bytes; written by dgq_compress, advanced by
+ * dgq_append.  The open span is [r0, length): tokens appended since the tail block was last
+ * sealed.  The ring holds the fixed-point moments of the 16 sealed tokens before r0. */
+typedef struct dgq_tail {
+  int32_t r0;
+  int32_t ring_len;      /* 0..16 */
+  int32_t span_own;      /* 1 if the open span has its own segment-table row */
+  int32_t reserved;
+  int32_t ring_a[16];    /* oldest first */
+  int64_t ring_b[16];
+} dgq_tail_t;
+
+/* The compressed cache of one layer: caller-owned device buffers. */
+typedef struct dgq_cache {
+  int8_t *k_pool;        /* [num_blocks][num_kv_heads][block_size*head_dim], 16-byte aligned */
+  int8_t *v_pool;        /* same */
+  uint8_t *bits;         /* [num_blocks][num_kv_heads][block_size/8] */
+  dgq_seg_t *segs;       /* [batch][num_kv_heads][seg_capacity] */
+  int32_t *nseg;         /* [batch][num_kv_heads] rows in use */
+  dgq_tail_t *tail;      /* [batch][num_kv_heads] */
+  uint16_t *k_stage;     /* [batch][num_kv_heads][block_size][head_dim] fp16 copy of the open span */
+  uint16_t *v_stage;     /* same */
+  unsigned long long *status; /* [4] counters, only ever incremented (the caller zeroes them):
+                                 [0] appends that wanted a new segment but found the table full
+                                     (the span joins the segment before it; codes saturate);
+                                 [1] groups of inputs that held a non-finite value (their codes
+                                     are unspecified);
+                                 [2] device-side inconsistencies that were skipped or clamped
+                                     instead of read out of bounds: a sequence length above
+                                     max_seq_len or outside cu_seqlens, a block id >= num_blocks,
+                                     an append state that does not fit the new position;
+                                 [3] reserved. */
+  int32_t num_blocks;    /* blocks in each pool */
+  int32_t batch;         /* rows of segs/nseg/tail/stage */
+} dgq_cache_t;
+
+/* Human-readable text for a status code (static storage). */
+const char *dgq_status_string(int32_t status);
+/* HIP error text of the calling thread's last DGQ_ERR_HIP (static per thread; "" if none). */
+const char *dgq_last_error(void);
+
+/* ---- Block pool (PagedAttention article, "PagedAttention implementation": BlockTable with a
+ * free list, block-granular allocation and release).  Host-only, no device work. ---- */
+
+/* Create a pool of num_blocks ids 0..num_blocks-1, all free; *pool (host) receives the handle. */
+dgq_status_t dgq_pool_create(int32_t num_blocks, void **pool);
+/* Destroy a pool (NULL is a no-op). */
+dgq_status_t dgq_pool_destroy(void *pool);
+/* Take n ids into ids (host, n entries).  All or nothing: DGQ_ERR_POOL_EXHAUSTED leaves the pool
+ * unchanged.  Ids come from the free list in last-freed-first order. */
+dgq_status_t dgq_block_alloc(void *pool, int32_t n, int32_t *ids);
+/* Return n ids (host).  DGQ_ERR_INVALID_ARG, with the pool unchanged, if any id is out of range,
+ * already free, or repeated in the list. */
+dgq_status_t dgq_block_free(void *pool, int32_t n, const int32_t *ids);
+/* Number of free ids, or -1 for a NULL pool. */
+int32_t dgq_pool_num_free(const void *pool);
+
+/* ---- Workspace sizes (bytes; 0 for invalid arguments) ---- */
+
+/* dgq_compress scratch for `batch` sequences of at most max_seq_len tokens, total_tokens in all. */
+size_t dgq_compress_workspace_size(const dgq_params_t *p, int32_t batch, int64_t total_tokens,
+                                   int32_t max_seq_len);
+/* paged_decode_attn_int8 scratch (split-sequence partial results). */
+size_t dgq_decode_workspace_size(const dgq_params_t *p, int32_t batch, int32_t max_seq_len);
+
+/* ---- DGQ compression (DGQ article 2.2) ----
+ * For every (sequence b, kv head h): the variance curve of the keys over a sliding 16-token
+ * window, cuts at its change points (2..max_segments segments when the sequence has >= 32
+ * tokens), per-segment K and V min/max, INT8 codes of every token written into the blocks the
+ * block table names, boundary bits, the segment table, and the append state (open span empty at
+ * the compressed length).
+ *   k, v        fp16 token-major input; element (token t of sequence b, head h, channel d) is at
+ *               [ (cu_seqlens[b] + t) * stride_tok + h * stride_head + d ].  16-byte aligned;
+ *               stride_tok and stride_head multiples of 8 elements.
+ *   cu_seqlens  (device) int32 [batch+1], nondecreasing, cu_seqlens[0] = 0; sequence b has
+ *               cu_seqlens[b+1] - cu_seqlens[b] <= max_seq_len tokens.
+ *   total_tokens (host) cu_seqlens[batch].
+ *   block_table (device) int32 [batch][max_blocks]; max_seq_len <= max_blocks * block_size.
+ *   cache       (host struct, device buffers) with cache->batch >= batch.
+ *   ws          device scratch of dgq_compress_workspace_size() bytes, 256-byte aligned.
+ * Non-finite inputs increment status[1]; their codes are unspecified. */
+dgq_status_t dgq_compress(const dgq_params_t *p, const uint16_t *k, const uint16_t *v,
+                          int64_t stride_tok, int64_t stride_head, const int32_t *cu_seqlens,
+                          int32_t batch, int32_t max_seq_len, int64_t total_tokens,
+                          const int32_t *block_table, int32_t max_blocks,
+                          const dgq_cache_t *cache, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* ---- Append one token per sequence (DGQ article 2.2: the segmentation is revisited as new
+ * tokens arrive; only the tail block's open span is re-decided, frozen blocks are never
+ * rewritten) ----
+ *   k_tok, v_tok (device) fp16 [batch][num_kv_heads][head_dim], 16-byte aligned.
+ *   seq_lens     (device) int32 [batch]: tokens already cached; the new token lands at that
+ *                position, whose block must already be in block_table.  The caller advances
+ *                seq_lens afterwards.
+ * Rule: the span joins the segment before it unless a span key or value falls outside that
+ * segment's range, or the span's first 16 tokens' window variance differs from the 16 tokens
+ * before the span by a ratio >= tau; then the span is a segment of its own (at most one per
+ * tail block).  The span's codes are rewritten with the chosen range; when the block fills, the
+ * span is sealed.  A full segment table makes the span join instead and increments status[0]. */
+dgq_status_t dgq_append(const dgq_params_t *p, const uint16_t *k_tok, const uint16_t *v_tok,
+                        const int32_t *seq_lens, int32_t batch, const int32_t *block_table,
+                        int32_t max_blocks, const dgq_cache_t *cache, hipStream_t stream);
+
+/* ---- Paged INT8 decode attention (DGQ article 3.1: dequantize while attending; PagedAttention
+ * article: paged forward pass through block_tables) ----
+ * out[b][g][:] = sum_t softmax_t(softmax_scale * q[b][g] . khat_t) * vhat_t over the seq_lens[b]
+ * cached tokens of kv head g / G, where khat, vhat are the dequantized codes.  The dequantization
+ * is folded into the dot products; no dequantized copy is written.
+ *   q    (device) fp16 [batch][num_q_heads][head_dim], 16-byte aligned.
+ *   out  (device) fp32 [batch][num_q_heads][head_dim]; an empty sequence gives zeros.
+ *   seq_lens (device) int32 [batch], each <= max_seq_len <= max_blocks * block_size.
+ *   ws   device scratch of dgq_decode_workspace_size() bytes, 256-byte aligned. */
+dgq_status_t paged_decode_attn_int8(const dgq_params_t *p, const uint16_t *q,
+                                    const dgq_cache_t *cache, const int32_t *block_table,
+                                    int32_t max_blocks, const int32_t *seq_lens, int32_t batch,
+                                    int32_t max_seq_len, float softmax_scale, float *out,
+                                    void *ws, size_t ws_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DGQ_H */

@@ -1,0 +1,19 @@
+"""MI355X-native dynamic-group INT8 KV-cache compression (DGQ) with paged INT8 decode attention.
+
+The compute lives in ``libdgq.so`` (hand-written HIP for gfx950, C ABI in ``include/dgq.h``);
+this package is its Python binding.  Importing it does not load the library; the first call
+does, and fails loudly if it is not built.
+"""
+
+from ._lib import DGQError, EXPORTS, LIB_PATH, load  # noqa: F401
+from .api import (  # noqa: F401
+    BlockPool,
+    DGQCache,
+    DGQParams,
+    compress_workspace_size,
+    decode_workspace_size,
+    dgq_append,
+    dgq_compress,
+    paged_decode_attn_int8,
+    workspace,
+)

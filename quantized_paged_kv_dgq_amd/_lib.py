@@ -1,0 +1,136 @@
+"""ctypes view of libdgq.so (include/dgq.h).  Argument marshalling only."""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdgq.so")
+
+DGQ_OK = 0
+DGQ_ERR_INVALID_ARG = -1
+DGQ_ERR_UNSUPPORTED = -2
+DGQ_ERR_POOL_EXHAUSTED = -3
+DGQ_ERR_WORKSPACE_TOO_SMALL = -4
+DGQ_ERR_HIP = -5
+
+
+class Params(ctypes.Structure):
+    _fields_ = [
+        ("num_kv_heads", ctypes.c_int32),
+        ("num_q_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("win", ctypes.c_int32),
+        ("max_segments", ctypes.c_int32),
+        ("seg_capacity", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+        ("tau", ctypes.c_double),
+    ]
+
+
+class Seg(ctypes.Structure):
+    _fields_ = [
+        ("start", ctypes.c_int32),
+        ("kmin", ctypes.c_float), ("kmax", ctypes.c_float),
+        ("vmin", ctypes.c_float), ("vmax", ctypes.c_float),
+        ("kscale", ctypes.c_float), ("vscale", ctypes.c_float),
+        ("reserved", ctypes.c_int32),
+    ]
+
+
+class Tail(ctypes.Structure):
+    _fields_ = [
+        ("r0", ctypes.c_int32),
+        ("ring_len", ctypes.c_int32),
+        ("span_own", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+        ("ring_a", ctypes.c_int32 * 16),
+        ("ring_b", ctypes.c_int64 * 16),
+    ]
+
+
+class Cache(ctypes.Structure):
+    _fields_ = [
+        ("k_pool", ctypes.c_void_p),
+        ("v_pool", ctypes.c_void_p),
+        ("bits", ctypes.c_void_p),
+        ("segs", ctypes.c_void_p),
+        ("nseg", ctypes.c_void_p),
+        ("tail", ctypes.c_void_p),
+        ("k_stage", ctypes.c_void_p),
+        ("v_stage", ctypes.c_void_p),
+        ("status", ctypes.c_void_p),
+        ("num_blocks", ctypes.c_int32),
+        ("batch", ctypes.c_int32),
+    ]
+
+
+assert ctypes.sizeof(Params) == 40
+assert ctypes.sizeof(Seg) == 32
+assert ctypes.sizeof(Tail) == 208
+
+# Every symbol include/dgq.h declares.
+EXPORTS = [
+    "dgq_status_string", "dgq_last_error",
+    "dgq_pool_create", "dgq_pool_destroy", "dgq_block_alloc", "dgq_block_free", "dgq_pool_num_free",
+    "dgq_compress_workspace_size", "dgq_decode_workspace_size",
+    "dgq_compress", "dgq_append", "paged_decode_attn_int8",
+]
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load libdgq.so; raises if it is not built (there is no fallback path)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"libdgq.so is not built at {LIB_PATH}; run __graft_entry__.build()")
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.POINTER
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    lib.dgq_status_string.argtypes = [i32]
+    lib.dgq_status_string.restype = ctypes.c_char_p
+    lib.dgq_last_error.argtypes = []
+    lib.dgq_last_error.restype = ctypes.c_char_p
+    lib.dgq_pool_create.argtypes = [i32, P(vp)]
+    lib.dgq_pool_create.restype = i32
+    lib.dgq_pool_destroy.argtypes = [vp]
+    lib.dgq_pool_destroy.restype = i32
+    lib.dgq_block_alloc.argtypes = [vp, i32, P(i32)]
+    lib.dgq_block_alloc.restype = i32
+    lib.dgq_block_free.argtypes = [vp, i32, P(i32)]
+    lib.dgq_block_free.restype = i32
+    lib.dgq_pool_num_free.argtypes = [vp]
+    lib.dgq_pool_num_free.restype = i32
+    lib.dgq_compress_workspace_size.argtypes = [P(Params), i32, i64, i32]
+    lib.dgq_compress_workspace_size.restype = sz
+    lib.dgq_decode_workspace_size.argtypes = [P(Params), i32, i32]
+    lib.dgq_decode_workspace_size.restype = sz
+    lib.dgq_compress.argtypes = [P(Params), vp, vp, i64, i64, vp, i32, i32, i64, vp, i32,
+                                 P(Cache), vp, sz, vp]
+    lib.dgq_compress.restype = i32
+    lib.dgq_append.argtypes = [P(Params), vp, vp, vp, i32, vp, i32, P(Cache), vp]
+    lib.dgq_append.restype = i32
+    lib.paged_decode_attn_int8.argtypes = [P(Params), vp, P(Cache), vp, i32, vp, i32, i32,
+                                           ctypes.c_float, vp, vp, sz, vp]
+    lib.paged_decode_attn_int8.restype = i32
+    _lib = lib
+    return lib
+
+
+class DGQError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        lib = load()
+        text = lib.dgq_status_string(status).decode()
+        detail = lib.dgq_last_error().decode() if status == DGQ_ERR_HIP else ""
+        super().__init__(f"{where}: {text} ({status}){': ' + detail if detail else ''}")
+        self.status = status
+
+
+def check(status: int, where: str) -> None:
+    if status != DGQ_OK:
+        raise DGQError(status, where)

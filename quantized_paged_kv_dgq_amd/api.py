@@ -1,0 +1,176 @@
+"""Python binding of libdgq with the C ABI's names (include/dgq.h).
+
+Only argument marshalling lives here: tensors become device pointers, the current torch stream
+becomes the HIP stream, and status codes become exceptions.  Every step of compression, append
+and decode runs in the library's HIP kernels; there is no fallback path.  torch provides device
+memory (the caller-owned buffers of a cache and the scratch workspaces) and streams.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+from typing import Optional, Sequence
+
+import torch
+
+from . import _lib
+from ._lib import Cache, Params, check
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _need(cond: bool, msg: str) -> None:
+    if not cond:
+        raise ValueError(msg)
+
+
+class DGQParams:
+    """dgq_params_t: shapes and method constants (window 16; segments 2..max_segments; tau)."""
+
+    def __init__(self, num_kv_heads: int, num_q_heads: int, head_dim: int, block_size: int,
+                 max_segments: int = 5, seg_capacity: int = 16, tau: float = 2.0, win: int = 16):
+        self.c = Params(num_kv_heads, num_q_heads, head_dim, block_size, win, max_segments,
+                        seg_capacity, 0, float(tau))
+
+    def __getattr__(self, name):
+        return getattr(self.__dict__["c"], name)
+
+    @property
+    def group(self) -> int:
+        return self.c.num_q_heads // self.c.num_kv_heads
+
+
+class DGQCache:
+    """The caller-owned device buffers of one layer's compressed cache (dgq_cache_t)."""
+
+    def __init__(self, params: DGQParams, num_blocks: int, batch: int, device="cuda"):
+        p = params.c
+        dev = torch.device(device)
+        tile = p.block_size * p.head_dim
+        self.params = params
+        self.num_blocks = num_blocks
+        self.batch = batch
+        self.k_pool = torch.zeros((num_blocks, p.num_kv_heads, tile), dtype=torch.int8, device=dev)
+        self.v_pool = torch.zeros_like(self.k_pool)
+        self.bits = torch.zeros((num_blocks, p.num_kv_heads, p.block_size // 8), dtype=torch.uint8, device=dev)
+        self.segs = torch.zeros((batch, p.num_kv_heads, p.seg_capacity, 8), dtype=torch.int32, device=dev)
+        self.nseg = torch.zeros((batch, p.num_kv_heads), dtype=torch.int32, device=dev)
+        self.tail = torch.zeros((batch, p.num_kv_heads, 52), dtype=torch.int32, device=dev)
+        self.k_stage = torch.zeros((batch, p.num_kv_heads, p.block_size, p.head_dim), dtype=torch.float16, device=dev)
+        self.v_stage = torch.zeros_like(self.k_stage)
+        self.status = torch.zeros(4, dtype=torch.int64, device=dev)
+        self.c = Cache(_ptr(self.k_pool), _ptr(self.v_pool), _ptr(self.bits), _ptr(self.segs),
+                       _ptr(self.nseg), _ptr(self.tail), _ptr(self.k_stage), _ptr(self.v_stage),
+                       _ptr(self.status), num_blocks, batch)
+
+    # host-side views for tests and reports (copies)
+    def segment_table(self):
+        """(starts int32 [B][H][cap], params float32 [B][H][cap][6], nseg [B][H]) on the host."""
+        raw = self.segs.cpu()
+        return raw[..., 0].numpy(), raw[..., 1:7].contiguous().view(torch.float32).numpy(), self.nseg.cpu().numpy()
+
+
+class BlockPool:
+    """Host block pool (dgq_pool_*): free list with all-or-nothing allocation."""
+
+    def __init__(self, num_blocks: int):
+        lib = _lib.load()
+        h = ctypes.c_void_p()
+        check(lib.dgq_pool_create(num_blocks, ctypes.byref(h)), "dgq_pool_create")
+        self._h = h
+
+    def alloc(self, n: int) -> list:
+        ids = (ctypes.c_int32 * max(n, 1))()
+        check(_lib.load().dgq_block_alloc(self._h, n, ids), "dgq_block_alloc")
+        return list(ids[:n])
+
+    def free(self, ids: Sequence[int]) -> None:
+        arr = (ctypes.c_int32 * max(len(ids), 1))(*ids)
+        check(_lib.load().dgq_block_free(self._h, len(ids), arr), "dgq_block_free")
+
+    @property
+    def num_free(self) -> int:
+        return _lib.load().dgq_pool_num_free(self._h)
+
+    def close(self) -> None:
+        if self._h:
+            _lib.load().dgq_pool_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def compress_workspace_size(params: DGQParams, batch: int, total_tokens: int, max_seq_len: int) -> int:
+    return int(_lib.load().dgq_compress_workspace_size(ctypes.byref(params.c), batch, total_tokens, max_seq_len))
+
+
+def decode_workspace_size(params: DGQParams, batch: int, max_seq_len: int) -> int:
+    return int(_lib.load().dgq_decode_workspace_size(ctypes.byref(params.c), batch, max_seq_len))
+
+
+def workspace(nbytes: int, device="cuda") -> torch.Tensor:
+    """A device scratch buffer (256-byte aligned by the caching allocator)."""
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+def dgq_compress(params: DGQParams, k: torch.Tensor, v: torch.Tensor, cu_seqlens: torch.Tensor,
+                 block_table: torch.Tensor, cache: DGQCache, max_seq_len: int, total_tokens: int,
+                 ws: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Compress token-major fp16 K/V [total][Hkv][D] (see dgq_compress in include/dgq.h)."""
+    _need(k.dtype == torch.float16 and v.dtype == torch.float16, "k, v must be float16")
+    _need(k.shape == v.shape and k.stride() == v.stride() and k.dim() == 3, "k, v: [tokens][heads][dim], same strides")
+    _need(k.stride(2) == 1, "channels must be contiguous")
+    _need(cu_seqlens.dtype == torch.int32 and block_table.dtype == torch.int32, "int32 index tensors")
+    batch = cu_seqlens.numel() - 1
+    if ws is None:
+        ws = workspace(compress_workspace_size(params, batch, total_tokens, max_seq_len), k.device)
+    st = _lib.load().dgq_compress(
+        ctypes.byref(params.c), _ptr(k), _ptr(v), k.stride(0), k.stride(1), _ptr(cu_seqlens), batch,
+        max_seq_len, total_tokens, _ptr(block_table), block_table.shape[1], ctypes.byref(cache.c),
+        _ptr(ws), ws.numel(), _stream(stream))
+    check(st, "dgq_compress")
+
+
+def dgq_append(params: DGQParams, k_tok: torch.Tensor, v_tok: torch.Tensor, seq_lens: torch.Tensor,
+               block_table: torch.Tensor, cache: DGQCache, stream=None) -> None:
+    """Append one fp16 token per sequence, k_tok/v_tok [B][Hkv][D] (see dgq_append)."""
+    _need(k_tok.dtype == torch.float16 and k_tok.is_contiguous() and v_tok.is_contiguous(), "contiguous float16 tokens")
+    _need(seq_lens.dtype == torch.int32 and block_table.dtype == torch.int32, "int32 index tensors")
+    st = _lib.load().dgq_append(
+        ctypes.byref(params.c), _ptr(k_tok), _ptr(v_tok), _ptr(seq_lens), seq_lens.numel(),
+        _ptr(block_table), block_table.shape[1], ctypes.byref(cache.c), _stream(stream))
+    check(st, "dgq_append")
+
+
+def paged_decode_attn_int8(params: DGQParams, q: torch.Tensor, cache: DGQCache,
+                           block_table: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int,
+                           softmax_scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                           ws: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Decode attention of q [B][Hq][D] fp16 over the compressed cache; returns fp32 [B][Hq][D]."""
+    _need(q.dtype == torch.float16 and q.is_contiguous(), "q: contiguous float16 [B][Hq][D]")
+    _need(seq_lens.dtype == torch.int32 and block_table.dtype == torch.int32, "int32 index tensors")
+    batch = q.shape[0]
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(params.c.head_dim)
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    if ws is None:
+        ws = workspace(decode_workspace_size(params, batch, max_seq_len), q.device)
+    st = _lib.load().paged_decode_attn_int8(
+        ctypes.byref(params.c), _ptr(q), ctypes.byref(cache.c), _ptr(block_table), block_table.shape[1],
+        _ptr(seq_lens), batch, max_seq_len, float(softmax_scale), _ptr(out), _ptr(ws), ws.numel(),
+        _stream(stream))
+    check(st, "paged_decode_attn_int8")
+    return out

@@ -1,0 +1,144 @@
+// Exported C entry points of libdgq: argument checks on the host, then the kernel launches.
+// Nothing is queued unless every check passes.
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+
+#include "dgq_internal.h"
+
+namespace dgq {
+
+static thread_local char g_last_error[256] = "";
+
+dgq_status_t hip_fail(hipError_t err, const char *where) {
+  std::snprintf(g_last_error, sizeof g_last_error, "%s: %s", where, hipGetErrorString(err));
+  return DGQ_ERR_HIP;
+}
+
+static bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+static dgq_status_t check_params(const dgq_params_t *p) {
+  if (p == nullptr) return DGQ_ERR_INVALID_ARG;
+  if (p->num_kv_heads < 1 || p->num_q_heads < 1 || p->num_q_heads % p->num_kv_heads != 0)
+    return DGQ_ERR_INVALID_ARG;
+  const int g = p->num_q_heads / p->num_kv_heads;
+  if (g != 1 && g != 2 && g != 4) return DGQ_ERR_UNSUPPORTED;
+  if (p->head_dim != 64 && p->head_dim != 128) return DGQ_ERR_UNSUPPORTED;
+  if (p->block_size != 16 && p->block_size != 64) return DGQ_ERR_UNSUPPORTED;
+  if (p->win != kWin) return DGQ_ERR_UNSUPPORTED;
+  if (p->max_segments < 1 || p->max_segments > kMaxCuts + 1) return DGQ_ERR_INVALID_ARG;
+  if (p->seg_capacity < p->max_segments || p->seg_capacity > kMaxSegCap) return DGQ_ERR_INVALID_ARG;
+  if (p->reserved != 0) return DGQ_ERR_INVALID_ARG;
+  if (!std::isfinite(p->tau) || p->tau < 1.0) return DGQ_ERR_INVALID_ARG;
+  return DGQ_OK;
+}
+
+static dgq_status_t check_cache(const dgq_cache_t *c, int32_t batch, bool need_stage) {
+  if (c == nullptr) return DGQ_ERR_INVALID_ARG;
+  if (!c->k_pool || !c->v_pool || !c->bits || !c->segs || !c->nseg || !c->tail || !c->status)
+    return DGQ_ERR_INVALID_ARG;
+  if (need_stage && (!c->k_stage || !c->v_stage)) return DGQ_ERR_INVALID_ARG;
+  if (!aligned(c->k_pool, 16) || !aligned(c->v_pool, 16) || !aligned(c->segs, 16) ||
+      !aligned(c->tail, 16) || !aligned(c->status, 8))
+    return DGQ_ERR_INVALID_ARG;
+  if (need_stage && (!aligned(c->k_stage, 16) || !aligned(c->v_stage, 16))) return DGQ_ERR_INVALID_ARG;
+  if (c->num_blocks < 1 || c->batch < batch) return DGQ_ERR_INVALID_ARG;
+  return DGQ_OK;
+}
+
+static dgq_status_t check_table(const dgq_params_t *p, const int32_t *block_table,
+                                int32_t max_blocks, int32_t max_seq_len) {
+  if (block_table == nullptr || max_blocks < 1 || max_seq_len < 0) return DGQ_ERR_INVALID_ARG;
+  if ((int64_t)max_seq_len > (int64_t)max_blocks * p->block_size) return DGQ_ERR_INVALID_ARG;
+  return DGQ_OK;
+}
+
+}  // namespace dgq
+
+using namespace dgq;
+
+extern "C" const char *dgq_status_string(int32_t status) {
+  switch (status) {
+    case DGQ_OK: return "ok";
+    case DGQ_ERR_INVALID_ARG: return "invalid argument";
+    case DGQ_ERR_UNSUPPORTED: return "unsupported shape";
+    case DGQ_ERR_POOL_EXHAUSTED: return "block pool exhausted";
+    case DGQ_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case DGQ_ERR_HIP: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+extern "C" const char *dgq_last_error(void) { return g_last_error; }
+
+extern "C" size_t dgq_compress_workspace_size(const dgq_params_t *p, int32_t batch,
+                                              int64_t total_tokens, int32_t max_seq_len) {
+  if (check_params(p) != DGQ_OK || batch < 0 || total_tokens < 0 || max_seq_len < 0) return 0;
+  return compress_layout(p, batch, total_tokens, max_seq_len).total;
+}
+
+extern "C" size_t dgq_decode_workspace_size(const dgq_params_t *p, int32_t batch, int32_t max_seq_len) {
+  if (check_params(p) != DGQ_OK || batch < 0 || max_seq_len < 0) return 0;
+  return decode_workspace_bytes(p, batch, max_seq_len);
+}
+
+extern "C" dgq_status_t dgq_compress(const dgq_params_t *p, const uint16_t *k, const uint16_t *v,
+                                     int64_t stride_tok, int64_t stride_head,
+                                     const int32_t *cu_seqlens, int32_t batch, int32_t max_seq_len,
+                                     int64_t total_tokens, const int32_t *block_table,
+                                     int32_t max_blocks, const dgq_cache_t *cache, void *ws,
+                                     size_t ws_bytes, hipStream_t stream) {
+  dgq_status_t st = check_params(p);
+  if (st != DGQ_OK) return st;
+  if (batch < 0 || max_seq_len < 0 || total_tokens < 0) return DGQ_ERR_INVALID_ARG;
+  if (batch == 0) return DGQ_OK;
+  if (total_tokens > (int64_t)batch * max_seq_len || total_tokens >= (int64_t)1 << 31)
+    return DGQ_ERR_INVALID_ARG;
+  if (!k || !v || !cu_seqlens || !aligned(k, 16) || !aligned(v, 16)) return DGQ_ERR_INVALID_ARG;
+  if (stride_tok <= 0 || stride_head < 0 || stride_tok % 8 != 0 || stride_head % 8 != 0)
+    return DGQ_ERR_INVALID_ARG;
+  if (p->num_kv_heads > 1 && stride_head < p->head_dim && stride_tok < (int64_t)p->num_kv_heads * p->head_dim)
+    return DGQ_ERR_INVALID_ARG;
+  if ((st = check_table(p, block_table, max_blocks, max_seq_len)) != DGQ_OK) return st;
+  if ((st = check_cache(cache, batch, false)) != DGQ_OK) return st;
+  const size_t need = compress_layout(p, batch, total_tokens, max_seq_len).total;
+  if (ws == nullptr || !aligned(ws, 256)) return DGQ_ERR_INVALID_ARG;
+  if (ws_bytes < need) return DGQ_ERR_WORKSPACE_TOO_SMALL;
+  return launch_compress(p, k, v, stride_tok, stride_head, cu_seqlens, batch, max_seq_len,
+                         total_tokens, block_table, max_blocks, cache, ws, stream);
+}
+
+extern "C" dgq_status_t dgq_append(const dgq_params_t *p, const uint16_t *k_tok,
+                                   const uint16_t *v_tok, const int32_t *seq_lens, int32_t batch,
+                                   const int32_t *block_table, int32_t max_blocks,
+                                   const dgq_cache_t *cache, hipStream_t stream) {
+  dgq_status_t st = check_params(p);
+  if (st != DGQ_OK) return st;
+  if (batch < 0) return DGQ_ERR_INVALID_ARG;
+  if (batch == 0) return DGQ_OK;
+  if (!k_tok || !v_tok || !seq_lens || !aligned(k_tok, 16) || !aligned(v_tok, 16)) return DGQ_ERR_INVALID_ARG;
+  if (block_table == nullptr || max_blocks < 1) return DGQ_ERR_INVALID_ARG;
+  if ((st = check_cache(cache, batch, true)) != DGQ_OK) return st;
+  return launch_append(p, k_tok, v_tok, seq_lens, batch, block_table, max_blocks, cache, stream);
+}
+
+extern "C" dgq_status_t paged_decode_attn_int8(const dgq_params_t *p, const uint16_t *q,
+                                               const dgq_cache_t *cache, const int32_t *block_table,
+                                               int32_t max_blocks, const int32_t *seq_lens,
+                                               int32_t batch, int32_t max_seq_len,
+                                               float softmax_scale, float *out, void *ws,
+                                               size_t ws_bytes, hipStream_t stream) {
+  dgq_status_t st = check_params(p);
+  if (st != DGQ_OK) return st;
+  if (batch < 0 || max_seq_len < 0) return DGQ_ERR_INVALID_ARG;
+  if (batch == 0) return DGQ_OK;
+  if (!q || !out || !seq_lens || !aligned(q, 16) || !aligned(out, 4)) return DGQ_ERR_INVALID_ARG;
+  if (!std::isfinite(softmax_scale)) return DGQ_ERR_INVALID_ARG;
+  if ((st = check_table(p, block_table, max_blocks, max_seq_len)) != DGQ_OK) return st;
+  if ((st = check_cache(cache, batch, false)) != DGQ_OK) return st;
+  const size_t need = decode_workspace_bytes(p, batch, max_seq_len);
+  if (ws == nullptr || !aligned(ws, 256)) return DGQ_ERR_INVALID_ARG;
+  if (ws_bytes < need) return DGQ_ERR_WORKSPACE_TOO_SMALL;
+  return launch_decode(p, q, cache, block_table, max_blocks, seq_lens, batch, max_seq_len,
+                       softmax_scale, out, ws, stream);
+}

@@ -1,0 +1,614 @@
+// DGQ compression of a batch of sequences (DGQ article 2.2), in four passes on one stream:
+//
+//  1. stats   -- one read of fp16 K/V.  Per token: exact fixed-point key moments a_t = sum n,
+//                b_t = sum n^2 (n = rint(clamp(x, -32, 32) * 512)); per 16-token sub-block:
+//                K and V min/max.  Four lanes per token, 64 contiguous bytes per lane group.
+//  2. scores  -- per candidate cut t in [16, L-16]: the 16-token window statistics
+//                Q = N * sum b - (sum a)^2 left and right of t (integers, exact), and
+//                score = (max + 1) / (min + 1) in float64; the best (score, t) of every
+//                256-candidate tile.
+//  3. select  -- one workgroup per (sequence, kv head): greedy cut selection from the tile
+//                maxima (re-scanning only tiles next to a taken cut), then each segment's K/V
+//                min/max from the sub-block extrema plus a raw re-read of the at most two
+//                sub-blocks a cut splits; writes the segment table, nseg and the append state.
+//  4. encode  -- second read of fp16 K/V; writes INT8 codes into the paged pool in the tile order
+//                of the decode kernel (values through LDS, since their tiles are channel-major),
+//                and the boundary bits.
+#include <climits>
+#include <cmath>
+
+#include "dgq_internal.h"
+
+namespace dgq {
+
+struct CompressArgs {
+  const uint16_t *k;
+  const uint16_t *v;
+  int64_t stride_tok, stride_head;
+  const int32_t *cu;
+  const int32_t *block_table;
+  int32_t max_blocks;
+  int32_t hkv, batch, max_segments, seg_cap, nsub, ntile, max_seq_len;
+  int64_t total;
+  double tau;
+  // workspace
+  int32_t *ws_a;        // [hkv][total]
+  int64_t *ws_b;        // [hkv][total]
+  double *ws_score;     // [hkv][total]
+  float4 *ws_ext;       // [batch][hkv][nsub]: kmin, kmax, vmin, vmax
+  double2 *ws_tile;     // [batch][hkv][ntile]: (score, t as double)
+  dgq_cache_t cache;
+};
+
+// -------------------------------------------------------------------------------------------
+// 1. stats
+// -------------------------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void stats_kernel(CompressArgs a) {
+  const int tile = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  int c0, L;
+  bool bad_seq;
+  seq_range(a.cu, b, a.max_seq_len, a.total, c0, L, bad_seq);
+  if (tile * 64 >= L) return;
+  const int tid = threadIdx.x;
+  const int t = tile * 64 + (tid >> 2), q = tid & 3;
+  const bool valid = t < L;
+  float kmn = INFINITY, kmx = -INFINITY, vmn = INFINITY, vmx = -INFINITY, bad = 0.f;
+  int asum = 0;
+  long long bsum = 0;
+  if (valid) {
+    const size_t row = (size_t)(c0 + t) * a.stride_tok + (size_t)h * a.stride_head;
+    const uint4 *kr = reinterpret_cast<const uint4 *>(a.k + row);
+    const uint4 *vr = reinterpret_cast<const uint4 *>(a.v + row);
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c) {
+      const uint4 kw = kr[q + 4 * c], vw = vr[q + 4 * c];
+      const uint32_t ks[4] = {kw.x, kw.y, kw.z, kw.w};
+      const uint32_t vs[4] = {vw.x, vw.y, vw.z, vw.w};
+      unsigned int bpart = 0;   // <= 8 * 2^28 < 2^32
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x = half_bits_to_float(e & 1 ? ks[e >> 1] >> 16 : ks[e >> 1] & 0xFFFFu);
+        const float y = half_bits_to_float(e & 1 ? vs[e >> 1] >> 16 : vs[e >> 1] & 0xFFFFu);
+        kmn = fminf(kmn, x);
+        kmx = fmaxf(kmx, x);
+        vmn = fminf(vmn, y);
+        vmx = fmaxf(vmx, y);
+        bad = fmaf(x, 0.f, bad);
+        bad = fmaf(y, 0.f, bad);
+        const int n = dgq_fixed_point(x);
+        asum += n;
+        bpart += (unsigned int)(n * n);
+      }
+      bsum += bpart;
+    }
+  }
+#pragma unroll
+  for (int o = 1; o <= 2; o <<= 1) {
+    asum += __shfl_xor(asum, o);
+    bsum += __shfl_xor(bsum, o);
+  }
+  if (valid && q == 0) {
+    const size_t idx = (size_t)h * a.total + c0 + t;
+    a.ws_a[idx] = asum;
+    a.ws_b[idx] = bsum;
+  }
+  // sub-block extrema: wave w covers tokens tile*64 + 16w .. +15
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    kmn = fminf(kmn, __shfl_xor(kmn, o));
+    kmx = fmaxf(kmx, __shfl_xor(kmx, o));
+    vmn = fminf(vmn, __shfl_xor(vmn, o));
+    vmx = fmaxf(vmx, __shfl_xor(vmx, o));
+  }
+  const int w = tid >> 6;
+  const int sb = tile * 4 + w;
+  if ((tid & 63) == 0 && sb * 16 < L) a.ws_ext[((size_t)b * a.hkv + h) * a.nsub + sb] = make_float4(kmn, kmx, vmn, vmx);
+  const bool any_bad = __ballot(!(bad == 0.f)) != 0ull;
+  if (any_bad && (tid & 63) == 0) atomicAdd(a.cache.status + 1, 1ull);
+}
+
+// -------------------------------------------------------------------------------------------
+// 2. scores
+// -------------------------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void scores_kernel(CompressArgs a) {
+  const int tile = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  int c0, L;
+  bool bad_seq;
+  seq_range(a.cu, b, a.max_seq_len, a.total, c0, L, bad_seq);
+  if (L < 2 * kWin || tile * 256 > L - kWin) return;
+  __shared__ int sa[256 + 2 * kWin];
+  __shared__ long long sbm[256 + 2 * kWin];
+  __shared__ double best_s[4];
+  __shared__ int best_t[4];
+  const int tid = threadIdx.x;
+  const int base = tile * 256 - kWin;
+  for (int i = tid; i < 256 + 2 * kWin; i += 256) {
+    const int tok = base + i;
+    if (tok >= 0 && tok < L) {
+      const size_t idx = (size_t)h * a.total + c0 + tok;
+      sa[i] = a.ws_a[idx];
+      sbm[i] = a.ws_b[idx];
+    } else {
+      sa[i] = 0;
+      sbm[i] = 0;
+    }
+  }
+  __syncthreads();
+  const int t = tile * 256 + tid;
+  double score = -INFINITY;
+  int tb = INT_MAX;
+  if (t >= kWin && t <= L - kWin) {
+    long long al = 0, ar = 0, bl = 0, br = 0;
+#pragma unroll
+    for (int i = 0; i < kWin; ++i) {
+      al += sa[tid + i];
+      bl += sbm[tid + i];
+      ar += sa[tid + kWin + i];
+      br += sbm[tid + kWin + i];
+    }
+    const long long nel = (long long)kWin * D;
+    const long long ql = nel * bl - al * al;
+    const long long qr = nel * br - ar * ar;
+    const long long hi = ql > qr ? ql : qr, lo = ql > qr ? qr : ql;
+    score = (double)(hi + 1) / (double)(lo + 1);
+    a.ws_score[(size_t)h * a.total + c0 + t] = score;
+    tb = t;
+  }
+  // best (score, smallest t) of the tile
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const double s2 = __shfl_xor(score, o);
+    const int t2 = __shfl_xor(tb, o);
+    if (s2 > score || (s2 == score && t2 < tb)) {
+      score = s2;
+      tb = t2;
+    }
+  }
+  if ((tid & 63) == 0) {
+    best_s[tid >> 6] = score;
+    best_t[tid >> 6] = tb;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    double s = best_s[0];
+    int tt = best_t[0];
+    for (int w = 1; w < 4; ++w)
+      if (best_s[w] > s || (best_s[w] == s && best_t[w] < tt)) {
+        s = best_s[w];
+        tt = best_t[w];
+      }
+    a.ws_tile[((size_t)b * a.hkv + h) * a.ntile + tile] = make_double2(s, (double)tt);
+  }
+}
+
+// -------------------------------------------------------------------------------------------
+// 3. select
+// -------------------------------------------------------------------------------------------
+__device__ __forceinline__ void block_best(double &s, int &t, double *ss, int *st) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const double s2 = __shfl_xor(s, o);
+    const int t2 = __shfl_xor(t, o);
+    if (s2 > s || (s2 == s && t2 < t)) {
+      s = s2;
+      t = t2;
+    }
+  }
+  __syncthreads();
+  if ((tid & 63) == 0) {
+    ss[tid >> 6] = s;
+    st[tid >> 6] = t;
+  }
+  __syncthreads();
+  s = ss[0];
+  t = st[0];
+  for (int w = 1; w < 4; ++w)
+    if (ss[w] > s || (ss[w] == s && st[w] < t)) {
+      s = ss[w];
+      t = st[w];
+    }
+}
+
+__device__ __forceinline__ void block_minmax(float4 &r, float4 *sh) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    r.x = fminf(r.x, __shfl_xor(r.x, o));
+    r.y = fmaxf(r.y, __shfl_xor(r.y, o));
+    r.z = fminf(r.z, __shfl_xor(r.z, o));
+    r.w = fmaxf(r.w, __shfl_xor(r.w, o));
+  }
+  __syncthreads();
+  if ((tid & 63) == 0) sh[tid >> 6] = r;
+  __syncthreads();
+  r = sh[0];
+  for (int w = 1; w < 4; ++w) {
+    r.x = fminf(r.x, sh[w].x);
+    r.y = fmaxf(r.y, sh[w].y);
+    r.z = fminf(r.z, sh[w].z);
+    r.w = fmaxf(r.w, sh[w].w);
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void select_kernel(CompressArgs a) {
+  const int h = blockIdx.x, b = blockIdx.y;
+  int c0, L;
+  bool bad_seq;
+  seq_range(a.cu, b, a.max_seq_len, a.total, c0, L, bad_seq);
+  const int tid = threadIdx.x;
+  const size_t bh = (size_t)b * a.hkv + h;
+  __shared__ int cuts[kMaxCuts + 1];
+  __shared__ int ncuts;
+  __shared__ double ss[4];
+  __shared__ int st[4];
+  __shared__ float4 sh4[4];
+  if (tid == 0) {
+    ncuts = 0;
+    if (bad_seq && h == 0) atomicAdd(a.cache.status + 2, 1ull);
+  }
+  __syncthreads();
+
+  double2 *tiles = a.ws_tile + bh * a.ntile;
+  if (L >= 2 * kWin && a.max_segments > 1) {
+    const int ntiles = (L - kWin) / 256 + 1;
+    for (int r = 0; r < a.max_segments - 1; ++r) {
+      double s = -INFINITY;
+      int t = INT_MAX;
+      for (int c = tid; c < ntiles; c += 256) {
+        const double2 e = tiles[c];
+        const int te = (int)e.y;
+        if (e.x > s || (e.x == s && te < t)) {
+          s = e.x;
+          t = te;
+        }
+      }
+      block_best(s, t, ss, st);
+      if (s == -INFINITY) break;
+      if (r > 0 && !(s >= a.tau)) break;
+      __syncthreads();
+      if (tid == 0) cuts[ncuts] = t;
+      __syncthreads();
+      if (tid == 0) ncuts = ncuts + 1;
+      __syncthreads();
+      const int nc = ncuts;
+      // re-scan the tiles that the suppressed window [t-15, t+15] touches
+      const int lo_tile = max(0, (t - (kWin - 1)) / 256), hi_tile = min(ntiles - 1, (t + kWin - 1) / 256);
+      for (int c = lo_tile; c <= hi_tile; ++c) {
+        const int tc = c * 256 + tid;
+        double sc = -INFINITY;
+        int tt = INT_MAX;
+        if (tc >= kWin && tc <= L - kWin) {
+          bool alive = true;
+          for (int k = 0; k < nc; ++k) alive = alive && abs(tc - cuts[k]) > kWin - 1;
+          if (alive) {
+            sc = a.ws_score[(size_t)h * a.total + c0 + tc];
+            tt = tc;
+          }
+        }
+        block_best(sc, tt, ss, st);
+        if (tid == 0) tiles[c] = make_double2(sc, (double)tt);
+        __syncthreads();
+      }
+    }
+  }
+  __syncthreads();
+  const int nc = ncuts;
+  // starts = [0] + sorted cuts
+  __shared__ int starts[kMaxCuts + 2];
+  if (tid == 0) {
+    int tmp[kMaxCuts + 1];
+    for (int i = 0; i < nc; ++i) tmp[i] = cuts[i];
+    for (int i = 1; i < nc; ++i) {
+      const int x = tmp[i];
+      int k = i - 1;
+      while (k >= 0 && tmp[k] > x) {
+        tmp[k + 1] = tmp[k];
+        --k;
+      }
+      tmp[k + 1] = x;
+    }
+    starts[0] = 0;
+    for (int i = 0; i < nc; ++i) starts[i + 1] = tmp[i];
+    starts[nc + 1] = L;
+  }
+  __syncthreads();
+  const int nseg = L > 0 ? nc + 1 : 0;
+  const float4 *ext = a.ws_ext + bh * a.nsub;
+  for (int sgi = 0; sgi < nseg; ++sgi) {
+    const int s = starts[sgi], e = starts[sgi + 1];
+    float4 r = make_float4(INFINITY, -INFINITY, INFINITY, -INFINITY);
+    const int i0 = s / 16, i1 = (e - 1) / 16;
+    for (int i = i0 + tid; i <= i1; i += 256) {
+      const bool full = (16 * i >= s) && (min(16 * i + 16, L) <= e);
+      if (full) {
+        const float4 x = ext[i];
+        r.x = fminf(r.x, x.x);
+        r.y = fmaxf(r.y, x.y);
+        r.z = fminf(r.z, x.z);
+        r.w = fmaxf(r.w, x.w);
+      }
+    }
+    // raw re-read of the split sub-blocks at either end
+    for (int side = 0; side < 2; ++side) {
+      const int i = side == 0 ? i0 : i1;
+      if (side == 1 && i1 == i0) break;
+      const int ts = max(16 * i, s), te = min(16 * i + 16, e);
+      const bool full = (16 * i >= s) && (min(16 * i + 16, L) <= e);
+      if (full) continue;
+      const int nel = (te - ts) * D;
+      for (int x = tid; x < nel; x += 256) {
+        const int tok = ts + x / D, d = x % D;
+        const size_t off = (size_t)(c0 + tok) * a.stride_tok + (size_t)h * a.stride_head + d;
+        const float kx = half_bits_to_float(a.k[off]);
+        const float vx = half_bits_to_float(a.v[off]);
+        r.x = fminf(r.x, kx);
+        r.y = fmaxf(r.y, kx);
+        r.z = fminf(r.z, vx);
+        r.w = fmaxf(r.w, vx);
+      }
+    }
+    block_minmax(r, sh4);
+    if (tid == 0) {
+      dgq_seg_t row;
+      row.start = s;
+      row.kmin = r.x + 0.0f;
+      row.kmax = r.y + 0.0f;
+      row.vmin = r.z + 0.0f;
+      row.vmax = r.w + 0.0f;
+      row.kscale = dgq_scale(row.kmin, row.kmax);
+      row.vscale = dgq_scale(row.vmin, row.vmax);
+      row.reserved = 0;
+      a.cache.segs[bh * a.seg_cap + sgi] = row;
+    }
+    __syncthreads();
+  }
+  if (tid == 0) {
+    a.cache.nseg[bh] = nseg;
+    dgq_tail_t tl;
+    tl.r0 = L;
+    const int rl = min(kWin, L);
+    tl.ring_len = rl;
+    tl.span_own = 0;
+    tl.reserved = 0;
+    for (int i = 0; i < kWin; ++i) {
+      if (i < rl) {
+        const size_t idx = (size_t)h * a.total + c0 + (L - rl + i);
+        tl.ring_a[i] = a.ws_a[idx];
+        tl.ring_b[i] = a.ws_b[idx];
+      } else {
+        tl.ring_a[i] = 0;
+        tl.ring_b[i] = 0;
+      }
+    }
+    a.cache.tail[bh] = tl;
+  }
+}
+
+// -------------------------------------------------------------------------------------------
+// 4. encode
+// -------------------------------------------------------------------------------------------
+template <int D, int BS>
+__global__ __launch_bounds__(256) void encode_kernel(CompressArgs a) {
+  constexpr int VROW = D + 8;   // padded LDS row (halves)
+  const int chunk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  int c0, L;
+  bool bad_seq;
+  seq_range(a.cu, b, a.max_seq_len, a.total, c0, L, bad_seq);
+  const int t0 = chunk * kChunk;
+  if (t0 >= L) return;
+  const int tid = threadIdx.x;
+  const size_t bh = (size_t)b * a.hkv + h;
+  __shared__ int s_start[kMaxSegCap];
+  __shared__ float s_kmin[kMaxSegCap], s_kinv[kMaxSegCap], s_vmin[kMaxSegCap], s_vinv[kMaxSegCap];
+  __shared__ int segidx[kChunk];
+  __shared__ uint16_t vt[kChunk * VROW];
+  const int ns = a.cache.nseg[bh];
+  if (tid < ns) {
+    const dgq_seg_t row = a.cache.segs[bh * a.seg_cap + tid];
+    s_start[tid] = row.start;
+    s_kmin[tid] = row.kmin;
+    s_kinv[tid] = dgq_inv(row.kmin, row.kmax);
+    s_vmin[tid] = row.vmin;
+    s_vinv[tid] = dgq_inv(row.vmin, row.vmax);
+  }
+  __syncthreads();
+  if (tid < kChunk) {
+    const int tok = t0 + tid;
+    int idx = 0;
+    for (int k = 1; k < ns; ++k) idx += tok >= s_start[k] ? 1 : 0;
+    segidx[tid] = idx;
+  }
+  // stage the value rows of the chunk
+  constexpr int VPR = D / 8;   // uint4 per row
+  for (int x = tid; x < kChunk * VPR; x += 256) {
+    const int tau = x / VPR, cc = x % VPR;
+    uint4 w = make_uint4(0u, 0u, 0u, 0u);
+    if (t0 + tau < L)
+      w = *reinterpret_cast<const uint4 *>(a.v + (size_t)(c0 + t0 + tau) * a.stride_tok + (size_t)h * a.stride_head + 8 * cc);
+    uint32_t *dst = reinterpret_cast<uint32_t *>(vt + tau * VROW + 8 * cc);
+    dst[0] = w.x;
+    dst[1] = w.y;
+    dst[2] = w.z;
+    dst[3] = w.w;
+  }
+  __syncthreads();
+
+  const int32_t *bt = a.block_table + (size_t)b * a.max_blocks;
+  const int nblk_seq = (L + BS - 1) / BS;
+  const size_t tile_bytes = (size_t)BS * D;
+
+  // keys: one unit = 16 channels of one token = 16 contiguous bytes of the tile
+  constexpr int KU = kChunk * D / 16;
+  for (int u = tid; u < KU; u += 256) {
+    const int tau = u / (D / 16), d0 = 16 * (u % (D / 16));
+    const int tok = t0 + tau;
+    if (tok >= L) continue;
+    const int sg = segidx[tau];
+    const float mn = s_kmin[sg], inv = s_kinv[sg];
+    const uint4 *src = reinterpret_cast<const uint4 *>(a.k + (size_t)(c0 + tok) * a.stride_tok + (size_t)h * a.stride_head + d0);
+    const uint4 w0 = src[0], w1 = src[1];
+    const uint32_t ws[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+    uint32_t outw[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const float x = half_bits_to_float(e & 1 ? ws[e >> 1] >> 16 : ws[e >> 1] & 0xFFFFu);
+      const uint32_t c = (uint32_t)(dgq_encode_value(x, mn, inv) & 0xFF);
+      outw[e >> 2] |= c << (8 * (e & 3));
+    }
+    bool bad_blk = false;
+    const int blk = checked_block(bt[tok / BS], a.cache.num_blocks, bad_blk);
+    if (bad_blk) {
+      atomicAdd(a.cache.status + 2, 1ull);
+      continue;
+    }
+    int8_t *dst = a.cache.k_pool + ((size_t)blk * a.hkv + h) * tile_bytes + k_tile_offset<D, BS>(tok % BS, d0);
+    *reinterpret_cast<uint4 *>(dst) = make_uint4(outw[0], outw[1], outw[2], outw[3]);
+  }
+
+  // values: one unit = 16 tokens of one channel = 16 contiguous bytes of the tile
+  for (int u = tid; u < KU; u += 256) {
+    int d, blk_local, taus[16];
+    if constexpr (BS == 64) {
+      const int n = u / 64, jj = (u / 16) % 4, r = u % 16;
+      d = 16 * n + r;
+      blk_local = 0;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) taus[e] = 16 * (e >> 2) + 4 * jj + (e & 3);
+    } else {
+      blk_local = u / D;
+      d = u % D;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) taus[e] = 16 * blk_local + e;
+    }
+    const int lblk = (t0 + (BS == 64 ? 0 : 16 * blk_local)) / BS;
+    if (lblk >= nblk_seq) continue;
+    uint32_t outw[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int tau = taus[e];
+      uint32_t c = 0u;
+      if (t0 + tau < L) {
+        const int sg = segidx[tau];
+        const float x = half_bits_to_float(vt[tau * VROW + d]);
+        c = (uint32_t)(dgq_encode_value(x, s_vmin[sg], s_vinv[sg]) & 0xFF);
+      }
+      outw[e >> 2] |= c << (8 * (e & 3));
+    }
+    bool bad_blk = false;
+    const int blk = checked_block(bt[lblk], a.cache.num_blocks, bad_blk);
+    if (bad_blk) continue;   // counted once per unit by the key loop above
+    int8_t *tilep = a.cache.v_pool + ((size_t)blk * a.hkv + h) * tile_bytes;
+    int off;
+    if constexpr (BS == 64) {
+      const int n = u / 64, jj = (u / 16) % 4, r = u % 16;
+      off = ((n * 4 + jj) * 16 + r) * 16;
+    } else {
+      off = d * 16;
+    }
+    *reinterpret_cast<uint4 *>(tilep + off) = make_uint4(outw[0], outw[1], outw[2], outw[3]);
+  }
+
+  // boundary bits: 8 bytes per chunk (one 64-token block, or four 16-token blocks)
+  if (tid < kChunk / 8) {
+    const int tok0 = t0 + 8 * tid;
+    const int lblk = tok0 / BS;
+    if (lblk < nblk_seq) {
+      uint32_t byte = 0;
+      for (int i = 0; i < 8; ++i) {
+        const int tok = tok0 + i;
+        bool start = false;
+        for (int k = 1; k < ns; ++k) start = start || (s_start[k] == tok);
+        if (tok < L && start) byte |= 1u << i;
+      }
+      bool bad_blk = false;
+      const int blk = checked_block(bt[lblk], a.cache.num_blocks, bad_blk);
+      if (!bad_blk) a.cache.bits[((size_t)blk * a.hkv + h) * (BS / 8) + (tok0 % BS) / 8] = (uint8_t)byte;
+    }
+  }
+}
+
+CompressLayout compress_layout(const dgq_params_t *p, int32_t batch, int64_t total_tokens,
+                               int32_t max_seq_len) {
+  CompressLayout l;
+  const size_t hkv = (size_t)p->num_kv_heads, tot = (size_t)(total_tokens > 0 ? total_tokens : 0);
+  l.nsub = (max_seq_len + 15) / 16;
+  if (l.nsub < 1) l.nsub = 1;
+  l.ntile = (max_seq_len + 255) / 256;
+  if (l.ntile < 1) l.ntile = 1;
+  size_t off = 0;
+  l.a_off = off;
+  off = align_up(off + hkv * tot * sizeof(int32_t), 256);
+  l.b_off = off;
+  off = align_up(off + hkv * tot * sizeof(int64_t), 256);
+  l.score_off = off;
+  off = align_up(off + hkv * tot * sizeof(double), 256);
+  l.ext_off = off;
+  off = align_up(off + (size_t)batch * hkv * l.nsub * sizeof(float4), 256);
+  l.tile_off = off;
+  off = align_up(off + (size_t)batch * hkv * l.ntile * sizeof(double2), 256);
+  l.total = off;
+  return l;
+}
+
+template <int D>
+static dgq_status_t launch_all(const CompressArgs &a, int bs, int max_seq_len, hipStream_t s) {
+  const int batch = a.batch, hkv = a.hkv;
+  dim3 g64((max_seq_len + 63) / 64, hkv, batch);
+  dim3 g256((max_seq_len + 255) / 256, hkv, batch);
+  dgq_status_t st;
+  if (max_seq_len > 0) {
+    hipLaunchKernelGGL(stats_kernel<D>, g64, dim3(256), 0, s, a);
+    st = check_launch("dgq_compress stats kernel");
+    if (st != DGQ_OK) return st;
+    hipLaunchKernelGGL(scores_kernel<D>, g256, dim3(256), 0, s, a);
+    st = check_launch("dgq_compress scores kernel");
+    if (st != DGQ_OK) return st;
+  }
+  hipLaunchKernelGGL(select_kernel<D>, dim3(hkv, batch), dim3(256), 0, s, a);
+  st = check_launch("dgq_compress select kernel");
+  if (st != DGQ_OK) return st;
+  if (max_seq_len == 0) return DGQ_OK;
+  if (bs == 64) hipLaunchKernelGGL((encode_kernel<D, 64>), g64, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((encode_kernel<D, 16>), g64, dim3(256), 0, s, a);
+  return check_launch("dgq_compress encode kernel");
+}
+
+dgq_status_t launch_compress(const dgq_params_t *p, const uint16_t *k, const uint16_t *v,
+                             int64_t stride_tok, int64_t stride_head, const int32_t *cu_seqlens,
+                             int32_t batch, int32_t max_seq_len, int64_t total_tokens,
+                             const int32_t *block_table, int32_t max_blocks,
+                             const dgq_cache_t *cache, void *ws, hipStream_t stream) {
+  const CompressLayout l = compress_layout(p, batch, total_tokens, max_seq_len);
+  char *w = reinterpret_cast<char *>(ws);
+  CompressArgs a;
+  a.k = k;
+  a.v = v;
+  a.stride_tok = stride_tok;
+  a.stride_head = stride_head;
+  a.cu = cu_seqlens;
+  a.block_table = block_table;
+  a.max_blocks = max_blocks;
+  a.hkv = p->num_kv_heads;
+  a.batch = batch;
+  a.max_segments = p->max_segments;
+  a.seg_cap = p->seg_capacity;
+  a.nsub = l.nsub;
+  a.ntile = l.ntile;
+  a.max_seq_len = max_seq_len;
+  a.total = total_tokens;
+  a.tau = p->tau;
+  a.ws_a = reinterpret_cast<int32_t *>(w + l.a_off);
+  a.ws_b = reinterpret_cast<int64_t *>(w + l.b_off);
+  a.ws_score = reinterpret_cast<double *>(w + l.score_off);
+  a.ws_ext = reinterpret_cast<float4 *>(w + l.ext_off);
+  a.ws_tile = reinterpret_cast<double2 *>(w + l.tile_off);
+  a.cache = *cache;
+  if (p->head_dim == 128) return launch_all<128>(a, p->block_size, max_seq_len, stream);
+  return launch_all<64>(a, p->block_size, max_seq_len, stream);
+}
+
+}  // namespace dgq

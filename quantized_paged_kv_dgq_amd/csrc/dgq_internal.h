@@ -1,0 +1,157 @@
+// Internal declarations shared by the libdgq translation units (not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+#include "dgq.h"
+
+namespace dgq {
+
+constexpr int kWin = 16;          // sliding-window length (DGQ article 2.2)
+constexpr int kChunk = 64;        // tokens per decode / encode chunk
+constexpr int kMaxSegCap = 64;    // segment-table rows per (sequence, kv head), upper bound
+constexpr int kMaxCuts = 7;       // max_segments <= 8
+
+// Record a HIP failure for dgq_last_error(); returns DGQ_ERR_HIP.
+dgq_status_t hip_fail(hipError_t err, const char *where);
+
+// Check the last launch on this thread.
+inline dgq_status_t check_launch(const char *where) {
+  hipError_t e = hipGetLastError();
+  return e == hipSuccess ? DGQ_OK : hip_fail(e, where);
+}
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// ---- decode ----
+struct DecodePlan {
+  int part_tokens;  // tokens per workgroup, multiple of kChunk
+  int nparts;       // partitions per sequence at max_seq_len
+};
+DecodePlan decode_plan(const dgq_params_t *p, int32_t batch, int32_t max_seq_len);
+size_t decode_workspace_bytes(const dgq_params_t *p, int32_t batch, int32_t max_seq_len);
+
+dgq_status_t launch_decode(const dgq_params_t *p, const uint16_t *q, const dgq_cache_t *cache,
+                           const int32_t *block_table, int32_t max_blocks,
+                           const int32_t *seq_lens, int32_t batch, int32_t max_seq_len,
+                           float softmax_scale, float *out, void *ws, hipStream_t stream);
+
+// ---- compress ----
+struct CompressLayout {
+  size_t a_off, b_off, score_off, ext_off, tile_off, total;
+  int nsub;    // 16-token sub-blocks per sequence at max_seq_len
+  int ntile;   // 256-candidate tiles per sequence at max_seq_len
+};
+CompressLayout compress_layout(const dgq_params_t *p, int32_t batch, int64_t total_tokens,
+                               int32_t max_seq_len);
+
+dgq_status_t launch_compress(const dgq_params_t *p, const uint16_t *k, const uint16_t *v,
+                             int64_t stride_tok, int64_t stride_head, const int32_t *cu_seqlens,
+                             int32_t batch, int32_t max_seq_len, int64_t total_tokens,
+                             const int32_t *block_table, int32_t max_blocks,
+                             const dgq_cache_t *cache, void *ws, hipStream_t stream);
+
+// ---- append ----
+dgq_status_t launch_append(const dgq_params_t *p, const uint16_t *k_tok, const uint16_t *v_tok,
+                           const int32_t *seq_lens, int32_t batch, const int32_t *block_table,
+                           int32_t max_blocks, const dgq_cache_t *cache, hipStream_t stream);
+
+}  // namespace dgq
+
+// ---- device helpers ----
+#if defined(__HIPCC__)
+namespace dgq {
+
+__device__ __forceinline__ float half_bits_to_float(uint32_t h) {
+  union { uint16_t u; _Float16 f; } c;
+  c.u = (uint16_t)h;
+  return (float)c.f;
+}
+
+// Byte offset of (token tau of its block, channel d) inside one (block, head) K tile.
+template <int D, int BS>
+__device__ __forceinline__ int k_tile_offset(int tau, int d) {
+  constexpr int M = D / 64;
+  const int m = d >> 6, j = (d & 63) >> 4, e = d & 15;
+  if constexpr (BS == 64) {
+    const int T = tau >> 4, r = tau & 15;
+    return (((T * M + m) * 4 + j) * 16 + r) * 16 + e;
+  } else {
+    const int T = tau >> 2, i = tau & 3;
+    return ((((T * M + m) * 4 + j) * 4 + i) * 16) + e;
+  }
+}
+
+// Byte offset of (token tau, channel d) inside one (block, head) V tile.
+template <int D, int BS>
+__device__ __forceinline__ int v_tile_offset(int tau, int d) {
+  if constexpr (BS == 64) {
+    const int n = d >> 4, r = d & 15, j = (tau & 15) >> 2, e = ((tau >> 4) << 2) | (tau & 3);
+    return ((n * 4 + j) * 16 + r) * 16 + e;
+  } else {
+    return d * 16 + tau;
+  }
+}
+
+// DGQ code of one value (exact IEEE steps: subtract, multiply, round to nearest even, clamp).
+__device__ __forceinline__ int dgq_encode_value(float x, float mn, float inv) {
+#pragma clang fp contract(off)
+  const float dlt = x - mn;
+  const float u = dlt * inv;
+  float r = __builtin_rintf(u);
+  r = fminf(fmaxf(r, 0.0f), 255.0f);
+  return (int)r - 128;
+}
+
+// fp32(255 / fp32(mx - mn)), or 0 for an empty range.  The float64 quotient rounded to float32
+// equals the correctly rounded float32 quotient (53 >= 2*24 + 2 bits).
+__device__ __forceinline__ float dgq_inv(float mn, float mx) {
+#pragma clang fp contract(off)
+  const float diff = mx - mn;
+  return diff > 0.0f ? (float)(255.0 / (double)diff) : 0.0f;
+}
+
+__device__ __forceinline__ float dgq_scale(float mn, float mx) {
+#pragma clang fp contract(off)
+  const float diff = mx - mn;
+  return (float)((double)diff / 255.0);
+}
+
+// Bounds of sequence b in the packed input, clamped so that no kernel reads past max_seq_len or
+// the packed token count; an inconsistency is counted in status[2] (by the caller's lane 0).
+__device__ __forceinline__ void seq_range(const int32_t *cu, int b, int max_seq_len, int64_t total,
+                                          int &c0, int &L, bool &bad) {
+  c0 = cu[b];
+  const int c1 = cu[b + 1];
+  L = c1 - c0;
+  bad = false;
+  if (c0 < 0 || L < 0 || (int64_t)c1 > total) {
+    L = 0;
+    c0 = 0;
+    bad = true;
+  } else if (L > max_seq_len) {
+    L = max_seq_len;
+    bad = true;
+  }
+}
+
+// Physical block id, replaced by 0 (and flagged) when it is not a pool block.
+__device__ __forceinline__ int checked_block(int id, int num_blocks, bool &bad) {
+  if ((unsigned)id >= (unsigned)num_blocks) {
+    bad = true;
+    return 0;
+  }
+  return id;
+}
+
+// Fixed-point image for the variance statistics: rint(clamp(x, -32, 32) * 512).
+__device__ __forceinline__ int dgq_fixed_point(float x) {
+  const float c = fminf(fmaxf(x, -32.0f), 32.0f);
+  return (int)__builtin_rintf(c * 512.0f);
+}
+
+}  // namespace dgq
+#endif

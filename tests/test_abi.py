@@ -1,0 +1,122 @@
+"""The C ABI on the CPU: the library loads, exports every symbol include/dgq.h declares, the host
+block pool behaves, and argument checks reject bad calls before any device work."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from quantized_paged_kv_dgq_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.fail("libdgq.so is not built; run __graft_entry__.build()")
+    return _lib.load()
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "dgq.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)) - {"sizeof"})
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == set(_lib.EXPORTS), names
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    assert lib.dgq_status_string(0) == b"ok"
+    assert lib.dgq_status_string(-3) == b"block pool exhausted"
+    assert lib.dgq_status_string(42) == b"unknown status"
+
+
+def test_pool(lib):
+    h = ctypes.c_void_p()
+    assert lib.dgq_pool_create(8, ctypes.byref(h)) == 0
+    assert lib.dgq_pool_num_free(h) == 8
+    ids = (ctypes.c_int32 * 8)()
+    assert lib.dgq_block_alloc(h, 3, ids) == 0
+    assert list(ids[:3]) == [0, 1, 2]
+    assert lib.dgq_pool_num_free(h) == 5
+    # all or nothing
+    assert lib.dgq_block_alloc(h, 6, ids) == _lib.DGQ_ERR_POOL_EXHAUSTED
+    assert lib.dgq_pool_num_free(h) == 5
+    # double free / out of range / repeated id leave the pool unchanged
+    bad = (ctypes.c_int32 * 2)(3, 3)
+    assert lib.dgq_block_free(h, 1, (ctypes.c_int32 * 1)(3)) == _lib.DGQ_ERR_INVALID_ARG  # 3 is free
+    assert lib.dgq_block_free(h, 2, (ctypes.c_int32 * 2)(1, 1)) == _lib.DGQ_ERR_INVALID_ARG
+    assert lib.dgq_block_free(h, 1, (ctypes.c_int32 * 1)(99)) == _lib.DGQ_ERR_INVALID_ARG
+    assert lib.dgq_pool_num_free(h) == 5
+    del bad
+    assert lib.dgq_block_free(h, 2, (ctypes.c_int32 * 2)(2, 0)) == 0
+    assert lib.dgq_pool_num_free(h) == 7
+    # last freed first
+    assert lib.dgq_block_alloc(h, 2, ids) == 0 and list(ids[:2]) == [0, 2]
+    assert lib.dgq_pool_destroy(h) == 0
+    assert lib.dgq_pool_num_free(None) == -1
+    assert lib.dgq_pool_create(-1, ctypes.byref(h)) == _lib.DGQ_ERR_INVALID_ARG
+
+
+def _params(**kw):
+    base = dict(num_kv_heads=8, num_q_heads=32, head_dim=128, block_size=16, win=16,
+                max_segments=5, seg_capacity=16, reserved=0, tau=2.0)
+    base.update(kw)
+    return _lib.Params(**base)
+
+
+def test_workspace_sizes(lib):
+    p = _params()
+    assert lib.dgq_compress_workspace_size(ctypes.byref(p), 16, 16 * 8192, 8192) > 16 * 8192 * 8 * 20
+    assert lib.dgq_decode_workspace_size(ctypes.byref(p), 16, 8192) > 0
+    for bad in (_params(head_dim=96), _params(block_size=32), _params(win=8), _params(num_q_heads=20),
+                _params(max_segments=9), _params(seg_capacity=4), _params(tau=0.5), _params(reserved=1)):
+        assert lib.dgq_compress_workspace_size(ctypes.byref(bad), 1, 10, 10) == 0
+        assert lib.dgq_decode_workspace_size(ctypes.byref(bad), 1, 10) == 0
+
+
+def test_argument_checks_queue_nothing(lib):
+    """Every bad call fails in the host checks (no device pointer is ever touched)."""
+    p = _params()
+    fake = ctypes.c_void_p(1 << 20)         # never dereferenced: the checks fail first
+    cache = _lib.Cache(fake, fake, fake, fake, fake, fake, fake, fake, fake, 64, 4)
+    # unsupported shapes
+    for bad, code in ((_params(head_dim=96), _lib.DGQ_ERR_UNSUPPORTED),
+                      (_params(num_q_heads=20), _lib.DGQ_ERR_INVALID_ARG),
+                      (_params(num_q_heads=24), _lib.DGQ_ERR_UNSUPPORTED),
+                      (_params(num_q_heads=64), _lib.DGQ_ERR_UNSUPPORTED)):
+        assert lib.paged_decode_attn_int8(ctypes.byref(bad), fake, ctypes.byref(cache), fake, 4, fake,
+                                          1, 64, 1.0, fake, fake, 1 << 30, None) == code
+    # null query
+    assert lib.paged_decode_attn_int8(ctypes.byref(p), None, ctypes.byref(cache), fake, 4, fake, 1, 64,
+                                      1.0, fake, fake, 1 << 30, None) == _lib.DGQ_ERR_INVALID_ARG
+    # max_seq_len beyond the table
+    assert lib.paged_decode_attn_int8(ctypes.byref(p), fake, ctypes.byref(cache), fake, 4, fake, 1, 65,
+                                      1.0, fake, fake, 1 << 30, None) == _lib.DGQ_ERR_INVALID_ARG
+    # workspace too small
+    assert lib.paged_decode_attn_int8(ctypes.byref(p), fake, ctypes.byref(cache), fake, 4, fake, 1, 64,
+                                      1.0, fake, fake, 16, None) == _lib.DGQ_ERR_WORKSPACE_TOO_SMALL
+    # misaligned input / bad strides / too many tokens for the batch
+    odd = ctypes.c_void_p((1 << 20) + 2)
+    assert lib.dgq_compress(ctypes.byref(p), odd, fake, 1024, 128, fake, 1, 64, 64, fake, 4,
+                            ctypes.byref(cache), fake, 1 << 30, None) == _lib.DGQ_ERR_INVALID_ARG
+    assert lib.dgq_compress(ctypes.byref(p), fake, fake, 1020, 128, fake, 1, 64, 64, fake, 4,
+                            ctypes.byref(cache), fake, 1 << 30, None) == _lib.DGQ_ERR_INVALID_ARG
+    assert lib.dgq_compress(ctypes.byref(p), fake, fake, 1024, 128, fake, 1, 64, 65, fake, 4,
+                            ctypes.byref(cache), fake, 1 << 30, None) == _lib.DGQ_ERR_INVALID_ARG
+    # cache too small for the batch
+    assert lib.dgq_compress(ctypes.byref(p), fake, fake, 1024, 128, fake, 5, 64, 64, fake, 4,
+                            ctypes.byref(cache), fake, 1 << 30, None) == _lib.DGQ_ERR_INVALID_ARG
+    # append without staging buffers
+    nostage = _lib.Cache(fake, fake, fake, fake, fake, fake, None, None, fake, 64, 4)
+    assert lib.dgq_append(ctypes.byref(p), fake, fake, fake, 1, fake, 4, ctypes.byref(nostage),
+                          None) == _lib.DGQ_ERR_INVALID_ARG
+    # an empty batch is a no-op
+    assert lib.dgq_append(ctypes.byref(p), None, None, None, 0, None, 0, None, None) == 0

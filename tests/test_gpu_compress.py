@@ -1,0 +1,161 @@
+"""dgq_compress on the GPU against the oracle: segment starts and min/max bit-exact, scales
+bit-exact, codes equal (the bound allows 1 LSB on <= 1e-4 of elements), boundary bits, append
+state; then decode of the GPU-compressed cache against the oracle."""
+
+import numpy as np
+import pytest
+import torch
+
+import dgq_data
+import gpu_helpers as H
+import paged_layout as PL
+from oracle import dgq_oracle as O
+import quantized_paged_kv_dgq_amd as Q
+
+pytestmark = pytest.mark.gpu
+
+
+def compress_and_check(cfg, seed, params=None, k=None, v=None, cu=None, lens=None, check_decode=True,
+                       spare_blocks=0):
+    if k is None:
+        k, v, cu, lens, dk, dv = H.upload_batch(cfg, seed)
+    else:
+        dk, dv = torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda()
+    lens = np.asarray(lens, np.int64)
+    if params is None:
+        params = H.params_for(cfg)
+    p = params.c
+    table, nblk = dgq_data.block_tables(cfg, seed, lens_total=np.maximum(lens, 1), spare_blocks=spare_blocks)
+    cache = Q.DGQCache(params, nblk, cfg.batch)
+    max_len = int(max(lens.max(), 1))
+    dtable = torch.from_numpy(table).cuda()
+    Q.dgq_compress(params, dk, dv, torch.from_numpy(np.asarray(cu, np.int32)).cuda(), dtable, cache,
+                   max_len, int(cu[-1]))
+    torch.cuda.synchronize()
+    status = cache.status.cpu().numpy()
+    assert status[2] == 0 and status[1] == 0, status
+
+    heads = {}
+    for b in range(cfg.batch):
+        for h in range(cfg.hkv):
+            kk = k[cu[b]:cu[b + 1], h]
+            vv = v[cu[b]:cu[b + 1], h]
+            heads[(b, h)] = O.compress_head(kk, vv, p.max_segments, p.tau)
+    H.compare_segments(cache, heads, cfg.batch, cfg.hkv)
+    bits = cache.bits.cpu().numpy()
+    tails = cache.tail.cpu().numpy()
+    for b in range(cfg.batch):
+        for h in range(cfg.hkv):
+            hc = heads[(b, h)]
+            kc, vc = H.read_codes(cache, table, b, h, hc.length)
+            H.compare_codes(kc, hc.kcodes, f"K codes b{b} h{h}")
+            H.compare_codes(vc, hc.vcodes, f"V codes b{b} h{h}")
+            got_bits = PL.gather_bits(bits, table[b], h, hc.length, p.block_size)
+            assert np.array_equal(got_bits, hc.bits), (b, h)
+            # append state: r0 = length, ring = moments of the last min(16, L) tokens
+            tl = tails[b, h]
+            assert tl[0] == hc.length and tl[1] == min(16, hc.length) and tl[2] == 0
+            a_t, b_t = O.token_moments(k[cu[b]:cu[b + 1], h])
+            rl = tl[1]
+            assert np.array_equal(tl[4:4 + rl], a_t[hc.length - rl:])
+            assert np.array_equal(tl[20:52].view(np.int64)[:rl], b_t[hc.length - rl:])
+    if check_decode:
+        q16 = dgq_data.queries(cfg, seed)
+        out = Q.paged_decode_attn_int8(params, torch.from_numpy(q16).cuda(), cache, dtable,
+                                       torch.from_numpy(lens.astype(np.int32)).cuda(), max_len)
+        ref = H.oracle_decode(q16, heads, lens, cfg.hkv, cfg.group)
+        err = H.rel_err_rows(out.cpu().numpy(), ref)
+        print(f"decode after GPU compress: max rel err {err:.3e}")
+        assert err <= 2e-3
+    return cache, heads, table
+
+
+CASES = [
+    ("tiny", 1, {}, 0),
+    ("llama_bs16", 2, dict(batch=2, seq_len=1500), 1),
+    ("long_bs64_outliers", 3, dict(seq_len=4100), 2),
+    ("mha_g1_mixed", 4, dict(batch=6, seq_len=900, min_len=1), 3),
+    ("stream_prefix_bs64", 5, dict(batch=3, seq_len=200, append_steps=0), 4),
+    ("d64_g2", 1, dict(hq=4, block_size=64, seq_len=1111, batch=2), 5),
+]
+
+
+@pytest.mark.parametrize("name,cid,over,seed", CASES, ids=[c[0] for c in CASES])
+def test_compress_matches_oracle(name, cid, over, seed):
+    cfg = dgq_data.get_config(cid, **over)
+    H.say("compress", name, over)
+    compress_and_check(cfg, seed)
+
+
+@pytest.mark.parametrize("max_segments,tau", [(1, 2.0), (2, 2.0), (8, 1.0), (5, 1.5)])
+def test_compress_segment_policies(max_segments, tau):
+    cfg = dgq_data.get_config(2, batch=2, seq_len=2000)
+    H.say("compress policy", max_segments, tau)
+    compress_and_check(cfg, 12, params=H.params_for(cfg, max_segments=max_segments, tau=tau))
+
+
+def _custom(cfg, seqs):
+    """Pack explicit per-(b, h) arrays [L][D] into token-major K/V."""
+    lens = np.array([s[0].shape[0] for s in seqs], np.int64)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    k = np.zeros((int(cu[-1]), cfg.hkv, cfg.head_dim), np.float16)
+    v = np.zeros_like(k)
+    for b, (kk, vv) in enumerate(seqs):
+        k[cu[b]:cu[b + 1]] = kk
+        v[cu[b]:cu[b + 1]] = vv
+    return k, v, cu, lens
+
+
+def test_compress_edge_cases():
+    """Lengths 0, 1, 31, 32, 33; constant runs (exact reconstruction); subnormals and signed
+    zeros; exact score ties; values beyond the statistics clamp."""
+    cfg = dgq_data.get_config(1, batch=9, hq=2)
+    rng = np.random.default_rng(0)
+    d = cfg.head_dim
+    seqs = []
+    for length in (0, 1, 31, 32, 33):
+        x = (rng.standard_normal((length, 2, d)) * 0.2).astype(np.float16)
+        seqs.append((x, (x * 0.5).astype(np.float16)))
+    # constant run inside Gaussian data
+    x = (rng.standard_normal((200, 2, d)) * 0.3).astype(np.float16)
+    x[64:128] = np.float16(0.0)
+    y = x.copy()
+    y[64:128] = np.float16(-0.125)
+    seqs.append((x, y))
+    # subnormals, signed zeros
+    x = (rng.standard_normal((150, 2, d)) * 1e-5).astype(np.float16)
+    x[::7] = np.float16(-0.0)
+    seqs.append((x, (-x).astype(np.float16)))
+    # periodic data: many equal scores (ties broken by the smallest t)
+    x = np.zeros((160, 2, d), np.float16)
+    x[::2] = np.float16(0.5)
+    x[40:80] = np.float16(0.0)
+    x[120:] = np.float16(0.25)
+    seqs.append((x, x.copy()))
+    # beyond the +-32 statistics clamp, up to the fp16 limits
+    x = (rng.standard_normal((100, 2, d)) * 40).astype(np.float16)
+    x[50, 0, :4] = np.array([65504, -65504, 1000, -3000], np.float16)
+    seqs.append((x, (x / 3).astype(np.float16)))
+    k, v, cu, lens = _custom(cfg, seqs)
+    H.say("compress edge cases")
+    cache, heads, _ = compress_and_check(cfg, 13, k=k, v=v, cu=cu, lens=lens)
+    hc = heads[(5, 0)]
+    assert hc.starts[1:3] == [64, 128] or 64 in hc.starts
+
+
+def test_compress_repeatable():
+    """Integer statistics make the result independent of scheduling: two runs are identical."""
+    cfg = dgq_data.get_config(2, batch=2, seq_len=1024)
+    k, v, cu, lens, dk, dv = H.upload_batch(cfg, 21)
+    params = H.params_for(cfg)
+    table, nblk = dgq_data.block_tables(cfg, 21)
+    dtable = torch.from_numpy(table).cuda()
+    dcu = torch.from_numpy(cu).cuda()
+    outs = []
+    for _ in range(2):
+        cache = Q.DGQCache(params, nblk, cfg.batch)
+        Q.dgq_compress(params, dk, dv, dcu, dtable, cache, 1024, int(cu[-1]))
+        torch.cuda.synchronize()
+        outs.append((cache.k_pool.cpu(), cache.v_pool.cpu(), cache.segs.cpu(), cache.bits.cpu()))
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)

@@ -1,0 +1,118 @@
+"""paged_decode_attn_int8 on the GPU against the oracle, fed with the oracle's own compression
+(so decode is checked independently of the GPU compressor)."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import dgq_data
+import gpu_helpers as H
+from oracle import dgq_oracle as O
+import quantized_paged_kv_dgq_amd as Q
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-3   # max relative error of the attention output in fp32
+
+
+def _heads_for(cfg, seed, lens):
+    heads = {}
+    for b in range(cfg.batch):
+        for h in range(cfg.hkv):
+            k, v = dgq_data.head_kv(cfg, seed, 0, b, h, int(lens[b]))
+            heads[(b, h)] = O.compress_head(k[:lens[b]], v[:lens[b]])
+    return heads
+
+
+def _run(cfg, seed, lens, heads=None, table=None, num_blocks=None, fill=None, seg_capacity=16):
+    lens = np.asarray(lens, np.int64)
+    if heads is None:
+        heads = _heads_for(cfg, seed, lens)
+    if table is None:
+        table, num_blocks = dgq_data.block_tables(cfg, seed, lens_total=np.maximum(lens, 1))
+    params = H.params_for(cfg, seg_capacity=seg_capacity)
+    cache = H.cache_from_oracle(params, heads, table, num_blocks, cfg.batch, fill=fill)
+    q16 = dgq_data.queries(cfg, seed)
+    max_len = int(max(lens.max(), 1))
+    out = Q.paged_decode_attn_int8(params, torch.from_numpy(q16).cuda(), cache,
+                                   torch.from_numpy(table).cuda(), torch.from_numpy(lens.astype(np.int32)).cuda(),
+                                   max_len)
+    torch.cuda.synchronize()
+    assert int(cache.status[2].item()) == 0
+    return out.cpu().numpy(), H.oracle_decode(q16, heads, lens, cfg.hkv, cfg.group), heads, q16
+
+
+CASES = [
+    ("tiny", 1, {}, 0, None),
+    ("llama_bs16_g4_ragged", 2, dict(batch=2, seq_len=1000), 1, None),
+    ("long_bs64_g4_outliers", 3, dict(seq_len=3000), 2, None),
+    ("mha_g1_bs16_mixed", 4, dict(batch=5, seq_len=700, min_len=1), 3, None),
+    ("stream_bs64_g4", 5, dict(batch=3, seq_len=300, append_steps=0), 4, None),
+    ("d64_g2_bs64", 1, dict(hq=4, block_size=64, seq_len=333), 5, None),
+    ("short_and_empty", 2, dict(batch=4, seq_len=70), 6, [70, 1, 0, 17]),
+]
+
+
+@pytest.mark.parametrize("name,cid,over,seed,lens", CASES, ids=[c[0] for c in CASES])
+def test_decode_matches_oracle(name, cid, over, seed, lens):
+    cfg = dgq_data.get_config(cid, **over)
+    if lens is None:
+        lens = dgq_data.seq_lens(cfg, seed)
+    H.say("decode", name, dict(over), "lens", list(np.asarray(lens)[:8]))
+    out, ref, _, _ = _run(cfg, seed, lens)
+    err = H.rel_err_rows(out, ref)
+    print(f"{name}: max rel err vs oracle {err:.3e}")
+    assert err <= TOL
+
+
+def test_decode_many_segments_any_positions():
+    """Eleven segments starting anywhere (mid-block, adjacent, last token): the per-token
+    segment lookup path."""
+    cfg = dgq_data.get_config(2, batch=1, seq_len=700)
+    k, v = dgq_data.head_kv(cfg, 7, 0, 0, 0, 700)
+    starts = [0, 5, 17, 64, 65, 100, 250, 251, 400, 640, 699]
+    heads = {}
+    for h in range(cfg.hkv):
+        kk, vv = dgq_data.head_kv(cfg, 7, 0, 0, h, 700)
+        segs = O.segment_params(kk, vv, starts)
+        heads[(0, h)] = O.HeadCompressed(700, segs, O.encode_by_segment(kk, segs, "k"),
+                                         O.encode_by_segment(vv, segs, "v"), O.boundary_bits(starts, 700))
+    H.say("decode many segments")
+    out, ref, _, _ = _run(cfg, 7, [700], heads=heads)
+    assert H.rel_err_rows(out, ref) <= TOL
+
+
+def test_decode_independent_of_physical_blocks_and_unused_bytes():
+    """The same logical cache under two block permutations, and with unused pool bytes zero or
+    random, gives bit-identical outputs."""
+    cfg = dgq_data.get_config(2, batch=2, seq_len=500)
+    lens = [500, 333]
+    heads = _heads_for(cfg, 9, np.array(lens))
+    t1, n = dgq_data.block_tables(cfg, 9, lens_total=np.array(lens), spare_blocks=7)
+    rng = np.random.default_rng(1)
+    perm = rng.permutation(n)
+    t2 = np.where(t1 >= 0, perm[np.maximum(t1, 0)], -1).astype(np.int32)
+    H.say("decode permutation invariance")
+    o1, ref, _, _ = _run(cfg, 9, lens, heads=heads, table=t1, num_blocks=n, fill=0)
+    o2, _, _, _ = _run(cfg, 9, lens, heads=heads, table=t2, num_blocks=n, fill=None)
+    assert np.array_equal(o1, o2)
+    assert H.rel_err_rows(o1, ref) <= TOL
+
+
+def test_decode_vs_unquantized_fp16_reported():
+    """Report (not gate) the error of quantized attention against fp16 attention."""
+    cfg = dgq_data.get_config(2, batch=2, seq_len=2048)
+    lens = dgq_data.seq_lens(cfg, 11)
+    out, ref, heads, q16 = _run(cfg, 11, lens)
+    exact = np.zeros_like(ref)
+    for b in range(cfg.batch):
+        for h in range(cfg.hkv):
+            k, v = dgq_data.head_kv(cfg, 11, 0, b, h, int(lens[b]))
+            g = cfg.group
+            exact[b, h * g:(h + 1) * g] = O.decode_attention(q16[b, h * g:(h + 1) * g], k.astype(np.float64),
+                                                             v.astype(np.float64))
+    print(f"DGQ attention vs fp16 attention: max rel err {H.rel_err_rows(out, exact):.3e}; "
+          f"oracle DGQ vs fp16 {H.rel_err_rows(ref, exact):.3e}")
+    assert H.rel_err_rows(out, ref) <= TOL
