@@ -1,0 +1,233 @@
+"""Benchmark of the DGQ hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of the Llama-3-8B-shaped layer workload
+(16 sequences x 8192 tokens, 8 KV / 32 query heads, head_dim 128, 16-token blocks shuffled in
+the pool):
+
+  1. dgq_compress        the batch's fp16 K/V (16 x 8192 tokens) into INT8 DGQ blocks;
+  2. dgq_append          one fp16 token per sequence into that cache;
+  3. paged_decode_attn_int8  one decode query per sequence over a cache of 8193 tokens.
+
+Four caches rotate: step i compresses and appends into cache i % 4 and decodes cache (i+2) % 4,
+which was written two steps earlier, so the decode's 256 MiB of codes are read from HBM and not
+from the 256 MB Infinity Cache.  Inputs are resident in HBM before the timed region.
+
+Prints one JSON line.  ``value`` is the decode attention's throughput in GB/s of algorithmic
+bytes (INT8 K/V codes + block table + segment tables + q + out), from HIP events recorded around
+every decode call on the stream the kernels run on.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=20.0,
+                    help="time budget of the CPU oracle baseline (0 to skip)")
+    return ap.parse_args()
+
+
+def cpu_baseline(cfg, seed, budget_s):
+    """The oracle as it is, on one host core, on a bounded sample of the same workload: whole
+    (sequence, kv head) units of config 2 until the budget is spent."""
+    from threadpoolctl import threadpool_limits
+
+    import dgq_data
+    from oracle import dgq_oracle as O
+
+    q16 = dgq_data.queries(cfg, seed)
+    units = [(b, h) for b in range(cfg.batch) for h in range(cfg.hkv)]
+    t_comp = t_dec = 0.0
+    done = 0
+    tokens = 0
+    with threadpool_limits(limits=1):
+        start = time.perf_counter()
+        for b, h in units:
+            k, v = dgq_data.head_kv(cfg, seed, 0, b, h, cfg.seq_len)
+            t0 = time.perf_counter()
+            hc = O.compress_head(k, v)
+            t1 = time.perf_counter()
+            O.decode_attention(q16[b, h * cfg.group:(h + 1) * cfg.group], hc.khat(), hc.vhat())
+            t2 = time.perf_counter()
+            t_comp += t1 - t0
+            t_dec += t2 - t1
+            done += 1
+            tokens += cfg.seq_len
+            if time.perf_counter() - start > budget_s and done >= 2:
+                break
+    dec_bytes = done * 2 * cfg.seq_len * cfg.head_dim
+    return {
+        "value": dec_bytes / t_dec / 1e9,
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{done} of {len(units)} (sequence, kv head) units of the {cfg.seq_len}-token layer; "
+                  f"decode = dequantize + float64 attention for the {cfg.group} query heads",
+        "compress_tokens_per_s": tokens / t_comp,
+        "seconds": t_comp + t_dec,
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the path has no multi-GPU "
+              "part in this build", file=sys.stderr)
+        sys.exit(2)
+
+    import dgq_data
+
+    cfg = dgq_data.get_config(2)
+    cpu = cpu_baseline(cfg, args.seed, args.cpu_seconds) if args.cpu_seconds > 0 else None
+
+    import torch
+
+    import quantized_paged_kv_dgq_amd as Q
+
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda")
+    B, L, hkv, hq, d, bs = cfg.batch, cfg.seq_len, cfg.hkv, cfg.hq, cfg.head_dim, cfg.block_size
+    k, v, cu, lens = dgq_data.batch_kv_device(cfg, args.seed, 0, dev)
+    total = int(cu[-1])
+    dcu = cu.to(dev)
+    table, nblk = dgq_data.block_tables(cfg, args.seed, lens_total=lens + 1)
+    dtable = torch.from_numpy(table).to(dev)
+    params = Q.DGQParams(hkv, hq, d, bs)
+    ncache = 4
+    caches = [Q.DGQCache(params, nblk, B, dev) for _ in range(ncache)]
+    ws_c = Q.workspace(Q.compress_workspace_size(params, B, total, L), dev)
+    ws_d = Q.workspace(Q.decode_workspace_size(params, B, L + 1), dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(args.seed + 17)
+    k_tok = (torch.randn((B, hkv, d), generator=gen, device=dev) * 0.2).half()
+    v_tok = (torch.randn((B, hkv, d), generator=gen, device=dev) * 0.2).half()
+    q = torch.from_numpy(dgq_data.queries(cfg, args.seed)).to(dev)
+    pos = torch.full((B,), L, dtype=torch.int32, device=dev)
+    dec_lens = torch.full((B,), L + 1, dtype=torch.int32, device=dev)
+    out = torch.empty((B, hq, d), dtype=torch.float32, device=dev)
+
+    def compress(i):
+        Q.dgq_compress(params, k, v, dcu, dtable, caches[i % ncache], L, total, ws=ws_c)
+
+    def append(i):
+        Q.dgq_append(params, k_tok, v_tok, pos, dtable, caches[i % ncache])
+
+    def decode(i):
+        Q.paged_decode_attn_int8(params, q, caches[(i + 2) % ncache], dtable, dec_lens, L + 1, out=out, ws=ws_d)
+
+    # fill every cache once (untimed), then warm up
+    for i in range(ncache):
+        compress(i)
+        append(i)
+    for i in range(args.warmup):
+        compress(i)
+        append(i)
+        decode(i)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record()
+    for i in range(K):
+        e = ev[i]
+        e[0].record()
+        compress(i)
+        e[1].record()
+        append(i)
+        e[2].record()
+        decode(i)
+        e[3].record()
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t_start.elapsed_time(t_end)
+    comp_ms = np.array([e[0].elapsed_time(e[1]) for e in ev])
+    app_ms = np.array([e[1].elapsed_time(e[2]) for e in ev])
+    dec_ms = np.array([e[2].elapsed_time(e[3]) for e in ev])
+
+    # algorithmic bytes
+    Ld = L + 1
+    nseg = torch.stack([c.nseg for c in caches]).cpu().numpy()
+    seg_rows = float(nseg.mean()) * B * hkv
+    dec_bytes = (B * 2 * Ld * hkv * d + B * math.ceil(Ld / bs) * 4 + seg_rows * 32
+                 + B * hq * d * 2 + B * hq * d * 4)
+    comp_elems = total * hkv * d * 2
+    comp_bytes = comp_elems * 3 + total * hkv / 8 + seg_rows * 32
+    dec_s = float(np.mean(dec_ms)) / 1e3
+    comp_s = float(np.mean(comp_ms)) / 1e3
+    dec_gbs = dec_bytes / dec_s / 1e9
+    comp_gbs = comp_bytes / comp_s / 1e9
+    hist = np.bincount(nseg.reshape(-1), minlength=6).tolist()
+
+    rec = {
+        "metric": "INT8 paged decode-attn GB/s (% HBM peak) + dgq_compress tokens/s",
+        "value": round(dec_gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(total_ms / K, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i8",
+        "data": "synthetic",
+        "config": {
+            "workload": "Llama-3-8B-shaped layer: 16 seqs x 8192 tokens, 8 KV / 32 q heads, head_dim 128, "
+                        "16-token blocks shuffled; step = compress + append 1 token + decode 1 query",
+            "global_batch": B, "seq_len": L, "block_size": bs, "kv_heads": hkv, "q_heads": hq, "head_dim": d,
+        },
+        "decode_frac_hbm_peak": round(dec_gbs / HBM_PEAK_GBS, 4),
+        "decode_us": round(dec_s * 1e6, 2),
+        "decode_kv_tokens_per_s": round(B * Ld / dec_s, 1),
+        "compress_tokens_per_s": round(total / comp_s, 1),
+        "compress_gbs_alg": round(comp_gbs, 1),
+        "compress_us": round(comp_s * 1e6, 2),
+        "append_us": round(float(np.mean(app_ms)) * 1e3, 2),
+        "segments_per_head_hist": hist,
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(dec_gbs, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "kernel": "paged_decode_attn_int8 (partition + merge kernels, HIP events around the call)",
+        },
+        "roofline_compress": {
+            "bound": "hbm", "achieved": round(comp_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(comp_gbs / HBM_PEAK_GBS, 4),
+            "kernel": "dgq_compress (stats + scores + select + encode, HIP events around the call)",
+        },
+        "wall_s_timed": round(wall, 4),
+    }
+    if cpu is not None:
+        rec["cpu_baseline"] = cpu
+    print(json.dumps(rec))
+
+
+if __name__ == "__main__":
+    main()

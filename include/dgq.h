@@ -204,7 +204,10 @@ dgq_status_t dgq_append(const dgq_params_t *p, const uint16_t *k_tok, const uint
  *   q    (device) fp16 [batch][num_q_heads][head_dim], 16-byte aligned.
  *   out  (device) fp32 [batch][num_q_heads][head_dim]; an empty sequence gives zeros.
  *   seq_lens (device) int32 [batch], each <= max_seq_len <= max_blocks * block_size.
- *   ws   device scratch of dgq_decode_workspace_size() bytes, 256-byte aligned. */
+ *   ws   device scratch of dgq_decode_workspace_size() bytes, 256-byte aligned.  Its first
+ *        bytes are completion counters of the split-sequence merge: they must be zero before the
+ *        first call that uses this buffer (zero-fill it once when allocating it), and every call
+ *        leaves them zero again.  Calls that share one workspace must not overlap in time. */
 dgq_status_t paged_decode_attn_int8(const dgq_params_t *p, const uint16_t *q,
                                     const dgq_cache_t *cache, const int32_t *block_table,
                                     int32_t max_blocks, const int32_t *seq_lens, int32_t batch,

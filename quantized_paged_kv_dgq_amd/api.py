@@ -121,8 +121,9 @@ def decode_workspace_size(params: DGQParams, batch: int, max_seq_len: int) -> in
 
 
 def workspace(nbytes: int, device="cuda") -> torch.Tensor:
-    """A device scratch buffer (256-byte aligned by the caching allocator)."""
-    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+    """A device scratch buffer (256-byte aligned by the caching allocator), zero-filled: the
+    decode workspace's completion counters must start at zero (the library leaves them zero)."""
+    return torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=device)
 
 
 def dgq_compress(params: DGQParams, k: torch.Tensor, v: torch.Tensor, cu_seqlens: torch.Tensor,

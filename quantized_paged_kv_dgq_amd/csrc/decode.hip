@@ -6,7 +6,9 @@
 // block table).
 //
 // How (gfx950):
-//  * One wave per (partition, kv head, sequence).  A partition is a run of 64-token chunks.
+//  * A workgroup of four waves per (partition, kv head, sequence); each wave takes a run of
+//    64-token chunks, the waves are merged in LDS, and a second kernel merges partitions by
+//    log-sum-exp.
 //  * The dequantization is folded into integer dot products: q . khat_t = ks_t * (q . c_t) +
 //    midK_t * sum(q) and sum_t p_t vhat_t = sum_t (p_t vs_t) c_t + sum_t p_t midV_t, where
 //    (ks, midK, vs, midV) belong to the segment of token t and mid = min + 128 * scale.
@@ -17,8 +19,11 @@
 //    of the second product (16 channels x 64 tokens); both come straight from the pool, whose
 //    tile order matches the operand layouts, so every load is a 16-byte lane load of contiguous
 //    memory and no code is ever converted to float.
-//  * Online softmax in base 2 per chunk; partial (max, sum, output) per partition; a second
-//    kernel merges partitions by log-sum-exp.
+//  * The PV products accumulate in the int32 matrix accumulators across chunks and are folded
+//    into the float output only when the running maximum of some query head moves.
+//  * Loads are software-pipelined: the next chunk's keys are requested as soon as the QK product
+//    has consumed the key registers, its values as soon as the PV product has consumed the value
+//    registers; the partition's block ids are read once, one per lane.
 #include <climits>
 #include <cmath>
 
@@ -28,6 +33,8 @@ namespace dgq {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 
+constexpr int kWaves = 4;   // waves per decode workgroup
+
 struct DecodeArgs {
   const uint16_t *q;
   const int8_t *k_pool;
@@ -36,6 +43,7 @@ struct DecodeArgs {
   const int32_t *nseg;
   const int32_t *block_table;
   const int32_t *seq_lens;
+  unsigned *counters;  // [batch][hkv]: workgroups done; zero between calls
   float *part_ml;   // [batch][hq][nparts][2]
   float *part_o;    // [batch][hq][nparts][D]
   float *out;       // [batch][hq][D]
@@ -44,296 +52,518 @@ struct DecodeArgs {
   float sm_log2;    // softmax_scale * log2(e)
 };
 
+// x from the lane whose index differs in bit 0 (XOR1) or bit 1 (XOR2), within quads (DPP).
+__device__ __forceinline__ float quad_xor1(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float quad_xor2(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, false));
+}
+
 __device__ __forceinline__ float readlane_f(float x, int lane) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), lane));
 }
 
-// The signed byte `piece` (0: bits 16.., 1: bits 8.., 2: bits 0..) of the balanced base-256
-// digits of X, as an unsigned byte pattern; piece 3 is always 0.
-__device__ __forceinline__ uint32_t piece_byte(int x, int piece) {
-  const int v = piece == 0 ? ((x + 0x8080) >> 16) : piece == 1 ? ((x + 0x80) >> 8) : x;
-  return piece < 3 ? (uint32_t)(v & 0xFF) : 0u;
+// Rounding to an integer by adding 1.5 * 2^23: for |v| <= 2^22 the float sum's bit pattern is
+// 0x4B400000 + rint(v) (round to nearest even).
+constexpr float kMagic = 12582912.0f;
+constexpr int kMagicBits = 0x4B400000;
+
+// A lane's byte of the balanced base-256 digits (d0, d1, d2) of an integer X, |X| <= 2^22,
+// X = d0 * 65536 + d1 * 256 + d2 with d1, d2 in [-128, 127]: byte k = ((X + add_k) >> shift_k)
+// & 0xFF with (add, shift) = (0x8080, 16), (0x80, 8), (0, 0).  Column byte 3 (and columns of
+// absent heads) read width 0, i.e. always 0.
+struct ByteSel {
+  int add;          // add_k - kMagicBits: applied to the magic-rounded float's bit pattern
+  unsigned shift;
+  unsigned width;   // 8, or 0 for an unused column
+};
+
+__device__ __forceinline__ ByteSel byte_sel(int piece, bool live) {
+  ByteSel s;
+  s.add = (piece == 0 ? 0x8080 : piece == 1 ? 0x80 : 0) - kMagicBits;
+  s.shift = piece < 3 ? 16u - 8u * (unsigned)piece : 0u;
+  s.width = live ? 8u : 0u;
+  return s;
+}
+
+// byte of rint(v) (v given as a float, |v| <= 2^22), rounding by fma(v, 1, magic)
+__device__ __forceinline__ uint32_t sel_byte(float rounded_magic, const ByteSel &s) {
+  return __builtin_amdgcn_ubfe((uint32_t)(__float_as_int(rounded_magic) + s.add), s.shift, s.width);
 }
 
 template <int D, int G, int BS>
-__global__ __launch_bounds__(64) void decode_partition_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(64 * kWaves) void decode_partition_kernel(DecodeArgs a) {
   constexpr int M = D / 64;    // 64-channel slices of a key row
   constexpr int NT = D / 16;   // 16-channel tiles of the output
   const int p = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int L_raw = a.seq_lens[b];
-  const int L = L_raw < 0 ? 0 : (L_raw > a.max_seq_len ? a.max_seq_len : L_raw);
-  if (p == 0 && threadIdx.x == 0 && h == 0 && L != L_raw) atomicAdd(a.status + 2, 1ull);
-  const int t_begin = p * a.part_tokens;
-  if (t_begin >= L) return;
-  const int t_end = min(L, t_begin + a.part_tokens);
-
-  const int lane = threadIdx.x;
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
   const int j = lane >> 4, col = lane & 15, g = col >> 2, piece = col & 3;
   const bool live = (g < G) && (piece < 3);
-
-  // ---- segment table: lane k holds row k ----
+  const ByteSel bsel = byte_sel(piece, live);
   const int bh = b * a.hkv + h;
-  const int ns = min(a.nseg[bh], a.seg_cap);
-  int s_start = INT_MAX;
-  float s_ks = 0.f, s_midk = 0.f, s_vs = 0.f, s_midv = 0.f;
-  if (lane < ns) {
-    const dgq_seg_t sg = a.segs[(size_t)bh * a.seg_cap + lane];
-    s_start = sg.start;
-    s_ks = sg.kscale;
-    s_midk = sg.kmin + 128.0f * sg.kscale;
-    s_vs = sg.vscale;
-    s_midv = sg.vmin + 128.0f * sg.vscale;
-  }
-  float vsmax = s_vs;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) vsmax = fmaxf(vsmax, __shfl_xor(vsmax, o));
-  const float wfac_unit = vsmax > 0.f ? 4194304.0f / vsmax : 0.f;   // 2^22 / vsmax
-  const float s_wf = s_vs * wfac_unit;
+  const int wg_begin = p * a.part_tokens * kWaves;
+  const int t_begin = wg_begin + wave * a.part_tokens;
 
-  // ---- query: three signed bytes per channel, one per column of the B operand ----
+  // Loads that do not depend on the sequence length go out together with it: the partition's
+  // block ids (one per lane, inside the table row), the segment-table row of this lane and the
+  // query slice of this lane.
+  const int32_t *bt = a.block_table + (size_t)b * a.max_blocks;
+  const int blk0 = t_begin / BS;
+  const int blk_raw = blk0 + lane < a.max_blocks ? bt[blk0 + lane] : 0;
+  const int ns_raw = a.nseg[bh];
+  dgq_seg_t seg_raw = {};
+  if (lane < a.seg_cap) seg_raw = a.segs[(size_t)bh * a.seg_cap + lane];
   const int qh = h * G + (g < G ? g : 0);
   const uint16_t *qrow = a.q + ((size_t)b * a.hq + qh) * D;
-  float qv[M][16];
-  float amax = 0.f, qsum = 0.f;
+  uint4 qraw[M][2];
 #pragma unroll
   for (int m = 0; m < M; ++m) {
     const uint4 *src = reinterpret_cast<const uint4 *>(qrow + 64 * m + 16 * j);
-    const uint4 w0 = src[0], w1 = src[1];
-    const uint32_t ws[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      qv[m][2 * e] = half_bits_to_float(ws[e] & 0xFFFFu);
-      qv[m][2 * e + 1] = half_bits_to_float(ws[e] >> 16);
-    }
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      amax = fmaxf(amax, fabsf(qv[m][e]));
-      qsum += qv[m][e];
-    }
+    qraw[m][0] = src[0];
+    qraw[m][1] = src[1];
   }
-  amax = fmaxf(amax, __shfl_xor(amax, 16));
-  amax = fmaxf(amax, __shfl_xor(amax, 32));
-  qsum += __shfl_xor(qsum, 16);
-  qsum += __shfl_xor(qsum, 32);
-  int qexp = 0;
-  if (amax > 0.f) {
-    int ex;
-    frexpf(amax, &ex);
-    qexp = 22 - ex;   // amax * 2^qexp in [2^21, 2^22)
-  }
-  v4i qfrag[M];
-#pragma unroll
-  for (int m = 0; m < M; ++m) {
-    uint32_t wv[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int x = (int)__builtin_rintf(ldexpf(qv[m][e], qexp));
-      const uint32_t by = live ? piece_byte(x, piece) : 0u;
-      wv[e >> 2] |= by << (8 * (e & 3));
-    }
-    qfrag[m] = v4i{(int)wv[0], (int)wv[1], (int)wv[2], (int)wv[3]};
-  }
-  // per-lane weight of this byte's partial dot product, in log2 units of the softmax
-  const float wq = live ? ldexpf(a.sm_log2, 16 - 8 * piece - qexp) : 0.f;
-  const float qsum_s = qsum * a.sm_log2;
 
-  // ---- main loop over 64-token chunks ----
+  const int L_raw = a.seq_lens[b];
+  const int L = L_raw < 0 ? 0 : (L_raw > a.max_seq_len ? a.max_seq_len : L_raw);
+  if (p == 0 && threadIdx.x == 0 && h == 0 && L != L_raw) atomicAdd(a.status + 2, 1ull);
+  if (L == 0 && p == 0) {                          // an empty sequence attends to nothing: zeros
+    for (int e = threadIdx.x; e < G * D; e += 64 * kWaves) a.out[((size_t)b * a.hq + h * G) * D + e] = 0.f;
+    return;
+  }
+  if (wg_begin >= L) return;                       // the whole workgroup has nothing to do
+  const bool active = t_begin < L;
+  const int t_end = min(L, t_begin + a.part_tokens);
+  __shared__ float sh_o[kWaves][G][D];
+  __shared__ float sh_m[kWaves][G], sh_l[kWaves][G];
+  // float output of each lane (C layout), folded from the int32 sums only when a maximum moves
+  __shared__ float sh_acc[kWaves][NT * 4][64];
+
   float m_run = -INFINITY, l_run = 0.f, mv_run = 0.f;
-  float O[NT][4];
+  float (*oacc)[64] = sh_acc[wave];
 #pragma unroll
-  for (int n = 0; n < NT; ++n)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) O[n][i] = 0.f;
+  for (int r = 0; r < NT * 4; ++r) oacc[r][lane] = 0.f;
+  float wv = 0.f;
 
-  const int nblk_seq = (L + BS - 1) / BS;
-  const int32_t *bt = a.block_table + (size_t)b * a.max_blocks;
-  const size_t tile_bytes = (size_t)BS * D;
-
-  for (int t0 = t_begin; t0 < t_end; t0 += kChunk) {
-    v4i kf[4][M];
-    v4i vf[NT];
-    bool bad_blk = false;
-    if constexpr (BS == 64) {
-      const size_t blk = (size_t)checked_block(bt[t0 / 64], a.num_blocks, bad_blk);
-      const int8_t *kb = a.k_pool + (blk * a.hkv + h) * tile_bytes;
-      const int8_t *vb = a.v_pool + (blk * a.hkv + h) * tile_bytes;
-#pragma unroll
-      for (int T = 0; T < 4; ++T)
-#pragma unroll
-        for (int m = 0; m < M; ++m)
-          kf[T][m] = *reinterpret_cast<const v4i *>(kb + (((T * M + m) * 64) + lane) * 16);
-#pragma unroll
-      for (int n = 0; n < NT; ++n) vf[n] = *reinterpret_cast<const v4i *>(vb + (n * 64 + lane) * 16);
-    } else {
-      const int lb = t0 / 16;
-      int bk = lb + ((lane & 15) >> 2);
-      bk = bk < nblk_seq ? bk : lb;
-      int bv = lb + j;
-      bv = bv < nblk_seq ? bv : lb;
-      const int8_t *kb = a.k_pool + ((size_t)checked_block(bt[bk], a.num_blocks, bad_blk) * a.hkv + h) * tile_bytes;
-      const int8_t *vb = a.v_pool + ((size_t)checked_block(bt[bv], a.num_blocks, bad_blk) * a.hkv + h) * tile_bytes;
-#pragma unroll
-      for (int T = 0; T < 4; ++T)
-#pragma unroll
-        for (int m = 0; m < M; ++m)
-          kf[T][m] = *reinterpret_cast<const v4i *>(kb + ((((T * M + m) * 4 + j) * 4 + (lane & 3)) * 16));
-#pragma unroll
-      for (int n = 0; n < NT; ++n) vf[n] = *reinterpret_cast<const v4i *>(vb + (16 * n + (lane & 15)) * 16);
+  if (active) {
+    // ---- segment table: lane k holds row k ----
+    const int ns = min(ns_raw, a.seg_cap);
+    int s_start = INT_MAX;
+    float s_ks = 0.f, s_midk = 0.f, s_vs = 0.f, s_midv = 0.f;
+    if (lane < ns) {
+      const dgq_seg_t sg = seg_raw;
+      s_start = sg.start;
+      s_ks = sg.kscale;
+      s_midk = sg.kmin + 128.0f * sg.kscale;
+      s_vs = sg.vscale;
+      s_midv = sg.vmin + 128.0f * sg.vscale;
     }
+    float vsmax = s_vs;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) vsmax = fmaxf(vsmax, __shfl_xor(vsmax, o));
+    const float wfac_unit = vsmax > 0.f ? 4194304.0f / vsmax : 0.f;   // 2^22 / vsmax
+    const float s_wf = s_vs * wfac_unit;
+    wv = live ? ldexpf(vsmax, -6 - 8 * piece) : 0.f;                // 2^(16-8*piece) * vsmax / 2^22
 
-    if (__ballot(bad_blk) != 0ull && lane == 0) atomicAdd(a.status + 2, 1ull);
-
-    // S^T = K . Q^T : rows = tokens of tile T, columns = (query head, byte)
-    float S[4][4];
+    // ---- query: three signed bytes per channel, one per column of the B operand ----
+    float qv[M][16];
+    float amax = 0.f, qsum = 0.f;
 #pragma unroll
-    for (int T = 0; T < 4; ++T) {
-      v4i acc = {0, 0, 0, 0};
+    for (int m = 0; m < M; ++m) {
+      const uint4 w0 = qraw[m][0], w1 = qraw[m][1];
+      const uint32_t ws[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
 #pragma unroll
-      for (int m = 0; m < M; ++m) acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(kf[T][m], qfrag[m], acc, 0, 0, 0);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) S[T][i] = (float)acc[i] * wq;
-    }
-#pragma unroll
-    for (int T = 0; T < 4; ++T)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float s = S[T][i];
-        s += __shfl_xor(s, 1);
-        s += __shfl_xor(s, 2);
-        S[T][i] = s;
+      for (int e = 0; e < 8; ++e) {
+        qv[m][2 * e] = half_bits_to_float(ws[e] & 0xFFFFu);
+        qv[m][2 * e + 1] = half_bits_to_float(ws[e] >> 16);
       }
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        amax = fmaxf(amax, fabsf(qv[m][e]));
+        qsum += qv[m][e];
+      }
+    }
+    amax = fmaxf(amax, __shfl_xor(amax, 16));
+    amax = fmaxf(amax, __shfl_xor(amax, 32));
+    qsum += __shfl_xor(qsum, 16);
+    qsum += __shfl_xor(qsum, 32);
+    int qexp = 0;
+    if (amax > 0.f) {
+      int ex;
+      frexpf(amax, &ex);
+      qexp = 22 - ex;   // amax * 2^qexp in [2^21, 2^22)
+    }
+    const float qmul = ldexpf(1.0f, qexp);
+    v4i qfrag[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      uint32_t wq4[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int e = 0; e < 16; ++e) wq4[e >> 2] |= sel_byte(fmaf(qv[m][e], qmul, kMagic), bsel) << (8 * (e & 3));
+      qfrag[m] = v4i{(int)wq4[0], (int)wq4[1], (int)wq4[2], (int)wq4[3]};
+    }
+    // per-lane weight of this byte's partial dot product, in log2 units of the softmax
+    const float wq = live ? ldexpf(a.sm_log2, 16 - 8 * piece - qexp) : 0.f;
+    const float qsum_s = qsum * a.sm_log2;
 
-    // token of (T, i) for this lane
-    auto tok_of = [&](int T, int i) -> int {
-      return BS == 64 ? t0 + 16 * T + 4 * j + i : t0 + 16 * j + 4 * T + i;
+    // ---- block ids of the partition: lane i holds the partition's i-th block (<= 64 blocks) ----
+    const int nblk_part = (t_end - 1) / BS - blk0 + 1;
+    int my_blk = 0;
+    {
+      bool bad = false;
+      if (lane < nblk_part) my_blk = checked_block(blk_raw, a.num_blocks, bad);
+      if (__ballot(bad) != 0ull && lane == 0) atomicAdd(a.status + 2, 1ull);
+    }
+    const size_t tile_bytes = (size_t)BS * D;
+    const int8_t *kpool = a.k_pool + (size_t)h * tile_bytes;
+    const int8_t *vpool = a.v_pool + (size_t)h * tile_bytes;
+    const size_t blk_stride = (size_t)a.hkv * tile_bytes;
+
+    // Fragment loads of chunk c (64 tokens) of the partition.  Keys: tile T (16 tokens) x slice m
+    // (64 channels) per A operand; values: channel tile n (16 channels) x 64 tokens per A operand.
+    auto load_k = [&](int c, v4i (&kf)[4][M]) {
+      if constexpr (BS == 64) {
+        const int blk = __builtin_amdgcn_readlane(my_blk, c);
+        const int8_t *kb = kpool + (size_t)blk * blk_stride;
+#pragma unroll
+        for (int T = 0; T < 4; ++T)
+#pragma unroll
+          for (int m = 0; m < M; ++m)
+            kf[T][m] = *reinterpret_cast<const v4i *>(kb + (((T * M + m) * 64) + lane) * 16);
+      } else {
+        const int bi = min(4 * c + ((lane & 15) >> 2), nblk_part - 1);
+        const int8_t *kb = kpool + (size_t)__shfl(my_blk, bi) * blk_stride;
+#pragma unroll
+        for (int T = 0; T < 4; ++T)
+#pragma unroll
+          for (int m = 0; m < M; ++m)
+            kf[T][m] = *reinterpret_cast<const v4i *>(kb + ((((T * M + m) * 4 + j) * 4 + (lane & 3)) * 16));
+      }
+    };
+    auto load_v = [&](int c, v4i (&vf)[NT]) {
+      if constexpr (BS == 64) {
+        const int blk = __builtin_amdgcn_readlane(my_blk, c);
+        const int8_t *vb = vpool + (size_t)blk * blk_stride;
+#pragma unroll
+        for (int n = 0; n < NT; ++n) vf[n] = *reinterpret_cast<const v4i *>(vb + (n * 64 + lane) * 16);
+      } else {
+        const int bi = min(4 * c + j, nblk_part - 1);
+        const int8_t *vb = vpool + (size_t)__shfl(my_blk, bi) * blk_stride;
+#pragma unroll
+        for (int n = 0; n < NT; ++n) vf[n] = *reinterpret_cast<const v4i *>(vb + (16 * n + (lane & 15)) * 16);
+      }
+    };
+    // segment index of token t (rows are sorted by start; row 0 starts at 0)
+    auto seg_of = [&](int t) -> int {
+      int idx = 0;
+      for (int k = 1; k < ns; ++k) idx += (t >= __builtin_amdgcn_readlane(s_start, k)) ? 1 : 0;
+      return idx;
     };
 
-    const int t_last = min(t0 + kChunk, t_end) - 1;
-    const int sf = max(__popcll(__ballot(s_start <= t0)) - 1, 0);
-    const int sl = max(__popcll(__ballot(s_start <= t_last)) - 1, 0);
-    float s2[4][4], wf[4][4], mvv[4][4];
-    if (sf == sl) {
-      const float ks = readlane_f(s_ks, sf), mk = readlane_f(s_midk, sf) * qsum_s;
-      const float wfs = readlane_f(s_wf, sf), mvs = readlane_f(s_midv, sf);
+    v4i cacc[NT];   // int32 PV sums since the last fold into O
 #pragma unroll
-      for (int T = 0; T < 4; ++T)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int t = tok_of(T, i);
-          s2[T][i] = t < t_end ? fmaf(ks, S[T][i], mk) : -INFINITY;
-          wf[T][i] = wfs;
-          mvv[T][i] = mvs;
-        }
-    } else {
-#pragma unroll
-      for (int T = 0; T < 4; ++T)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int t = tok_of(T, i);
-          int idx = 0;
-          for (int k = 1; k < ns; ++k) idx += (t >= __builtin_amdgcn_readlane(s_start, k)) ? 1 : 0;
-          const float ks = __shfl(s_ks, idx), mk = __shfl(s_midk, idx) * qsum_s;
-          wf[T][i] = __shfl(s_wf, idx);
-          mvv[T][i] = __shfl(s_midv, idx);
-          s2[T][i] = t < t_end ? fmaf(ks, S[T][i], mk) : -INFINITY;
-        }
-    }
+    for (int n = 0; n < NT; ++n) cacc[n] = v4i{0, 0, 0, 0};
 
-    // online softmax (base 2)
-    float cmax = -INFINITY;
+    const int nchunks = (t_end - t_begin + kChunk - 1) / kChunk;
+    v4i kf[4][M];
+    v4i vf[NT];
+    load_k(0, kf);
+    load_v(0, vf);
+    for (int c = 0; c < nchunks; ++c) {
+      const int t0 = t_begin + c * kChunk;
+
+      // S^T = K . Q^T : rows = tokens of tile T, columns = (query head, byte)
+      float S[4][4];
 #pragma unroll
-    for (int T = 0; T < 4; ++T)
+      for (int T = 0; T < 4; ++T) {
+        v4i acc = {0, 0, 0, 0};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) cmax = fmaxf(cmax, s2[T][i]);
-    cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
-    cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
-    const float m_new = fmaxf(m_run, cmax);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
-    float psum = 0.f, pmv = 0.f;
-    uint32_t pw[4] = {0u, 0u, 0u, 0u};
+        for (int m = 0; m < M; ++m) acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(kf[T][m], qfrag[m], acc, 0, 0, 0);
 #pragma unroll
-    for (int T = 0; T < 4; ++T)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float pr = __builtin_amdgcn_exp2f(s2[T][i] - m_new);
-        psum += pr;
-        pmv = fmaf(pr, mvv[T][i], pmv);
-        const int x = (int)__builtin_rintf(pr * wf[T][i]);
-        const uint32_t by = live ? piece_byte(x, piece) : 0u;
-        pw[T] |= by << (8 * i);
+        for (int i = 0; i < 4; ++i) S[T][i] = (float)acc[i] * wq;
       }
-    l_run = fmaf(l_run, alpha, psum);
-    mv_run = fmaf(mv_run, alpha, pmv);
-    const v4i pfrag = v4i{(int)pw[0], (int)pw[1], (int)pw[2], (int)pw[3]};
+      if (c + 1 < nchunks) load_k(c + 1, kf);
+#pragma unroll
+      for (int T = 0; T < 4; ++T)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float s = S[T][i];
+          s += quad_xor1(s);
+          s += quad_xor2(s);
+          S[T][i] = s;
+        }
 
-    // O^T += V^T . P^T : rows = channels of tile n, columns = (query head, byte)
+      // token of (T, i) for this lane
+      auto tok_of = [&](int T, int i) -> int {
+        return BS == 64 ? t0 + 16 * T + 4 * j + i : t0 + 16 * j + 4 * T + i;
+      };
+
+      // scores in log2 units, with the segment's (ks, midK) of every token
+      const int t_last = min(t0 + kChunk, t_end) - 1;
+      const int sf = max(__popcll(__ballot(s_start <= t0)) - 1, 0);
+      const int sl = max(__popcll(__ballot(s_start <= t_last)) - 1, 0);
+      const bool uni = sf == sl;
+      if (uni) {
+        const float ks = readlane_f(s_ks, sf), mk = readlane_f(s_midk, sf) * qsum_s;
 #pragma unroll
-    for (int n = 0; n < NT; ++n) {
-      v4i c = {0, 0, 0, 0};
-      c = __builtin_amdgcn_mfma_i32_16x16x64_i8(vf[n], pfrag, c, 0, 0, 0);
+        for (int T = 0; T < 4; ++T)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) O[n][i] = fmaf(O[n][i], alpha, (float)c[i]);
+          for (int i = 0; i < 4; ++i) S[T][i] = fmaf(ks, S[T][i], mk);
+      } else {
+#pragma unroll
+        for (int T = 0; T < 4; ++T)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int idx = seg_of(tok_of(T, i));
+            S[T][i] = fmaf(__shfl(s_ks, idx), S[T][i], __shfl(s_midk, idx) * qsum_s);
+          }
+      }
+      if (t0 + kChunk > t_end) {   // partial last chunk: tokens past the end weigh nothing
+#pragma unroll
+        for (int T = 0; T < 4; ++T)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) S[T][i] = tok_of(T, i) < t_end ? S[T][i] : -INFINITY;
+      }
+
+      // online softmax (base 2)
+      float cmax = -INFINITY;
+#pragma unroll
+      for (int T = 0; T < 4; ++T)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) cmax = fmaxf(cmax, S[T][i]);
+      cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
+      cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
+      const float m_new = fmaxf(m_run, cmax);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      if (__ballot(m_new > m_run) != 0ull) {
+        // some head's maximum moved: fold the int32 sums (relative to the old maximum) into O
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) oacc[4 * n + i][lane] = (oacc[4 * n + i][lane] + (float)cacc[n][i]) * alpha;
+          cacc[n] = v4i{0, 0, 0, 0};
+        }
+      }
+      m_run = m_new;
+      float psum = 0.f, pmv = 0.f;
+      uint32_t pw[4] = {0u, 0u, 0u, 0u};
+      if (uni) {
+        const float wfs = readlane_f(s_wf, sf), mvs = readlane_f(s_midv, sf);
+#pragma unroll
+        for (int T = 0; T < 4; ++T)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float pr = __builtin_amdgcn_exp2f(S[T][i] - m_new);
+            psum += pr;
+            pw[T] |= sel_byte(fmaf(pr, wfs, kMagic), bsel) << (8 * i);
+          }
+        pmv = psum * mvs;
+      } else {
+#pragma unroll
+        for (int T = 0; T < 4; ++T)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int idx = seg_of(tok_of(T, i));
+            const float pr = __builtin_amdgcn_exp2f(S[T][i] - m_new);
+            psum += pr;
+            pmv = fmaf(pr, __shfl(s_midv, idx), pmv);
+            pw[T] |= sel_byte(fmaf(pr, __shfl(s_wf, idx), kMagic), bsel) << (8 * i);
+          }
+      }
+      l_run = fmaf(l_run, alpha, psum);
+      mv_run = fmaf(mv_run, alpha, pmv);
+      const v4i pfrag = v4i{(int)pw[0], (int)pw[1], (int)pw[2], (int)pw[3]};
+
+      // O^T += V^T . P^T : rows = channels of tile n, columns = (query head, byte)
+#pragma unroll
+      for (int n = 0; n < NT; ++n) cacc[n] = __builtin_amdgcn_mfma_i32_16x16x64_i8(vf[n], pfrag, cacc[n], 0, 0, 0);
+      if (c + 1 < nchunks) load_v(c + 1, vf);
     }
+#pragma unroll
+    for (int n = 0; n < NT; ++n)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) oacc[4 * n + i][lane] += (float)cacc[n][i];
   }
 
-  // ---- epilogue: combine the byte columns, add the mid term, write the partial ----
-  const float wv = live ? ldexpf(vsmax, -6 - 8 * piece) : 0.f;   // 2^(16-8*piece) * vsmax / 2^22
+  // ---- epilogue: combine the byte columns and the mid term per wave, then merge the waves of
+  // the workgroup in LDS and write one partial (m, l, o) per query head ----
   l_run += __shfl_xor(l_run, 16);
   l_run += __shfl_xor(l_run, 32);
   mv_run += __shfl_xor(mv_run, 16);
   mv_run += __shfl_xor(mv_run, 32);
-  const size_t prow = ((size_t)b * a.hq + qh) * a.nparts + p;
-  float *po = a.part_o + prow * D;
 #pragma unroll
   for (int n = 0; n < NT; ++n)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      float v = O[n][i] * wv;
-      v += __shfl_xor(v, 1);
-      v += __shfl_xor(v, 2);
-      if (piece == 0 && g < G) po[16 * n + 4 * j + i] = v + mv_run;
+      float v = oacc[4 * n + i][lane] * wv;
+      v += quad_xor1(v);
+      v += quad_xor2(v);
+      if (piece == 0 && g < G) sh_o[wave][g][16 * n + 4 * j + i] = active ? v + mv_run : 0.f;
     }
   if (j == 0 && piece == 0 && g < G) {
-    a.part_ml[prow * 2 + 0] = m_run;
-    a.part_ml[prow * 2 + 1] = l_run;
+    sh_m[wave][g] = active ? m_run : -INFINITY;
+    sh_l[wave][g] = active ? l_run : 0.f;
   }
-}
-
-template <int D>
-__global__ __launch_bounds__(D) void decode_reduce_kernel(DecodeArgs a) {
-  const int qh = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
-  const int L_raw = a.seq_lens[b];
-  const int L = L_raw < 0 ? 0 : (L_raw > a.max_seq_len ? a.max_seq_len : L_raw);
-  const int P = (L + a.part_tokens - 1) / a.part_tokens;
-  const size_t row = (size_t)b * a.hq + qh;
-  float res = 0.f;
-  if (P > 0) {
-    const float *ml = a.part_ml + row * a.nparts * 2;
-    const float *po = a.part_o + row * a.nparts * D;
+  __syncthreads();
+  const int P = (L + a.part_tokens * kWaves - 1) / (a.part_tokens * kWaves);   // workgroups of (b, h)
+  for (int e = threadIdx.x; e < G * D; e += 64 * kWaves) {
+    const int gg = e / D, d = e % D;
     float mx = -INFINITY;
-    for (int p = 0; p < P; ++p) mx = fmaxf(mx, ml[2 * p]);
-    float num = 0.f, den = 0.f;
-    for (int p = 0; p < P; ++p) {
-      const float w = __builtin_amdgcn_exp2f(ml[2 * p] - mx);
-      num = fmaf(w, po[(size_t)p * D + d], num);
-      den = fmaf(w, ml[2 * p + 1], den);
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) mx = fmaxf(mx, sh_m[w][gg]);
+    float o = 0.f, l = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float sc = __builtin_amdgcn_exp2f(sh_m[w][gg] - mx);
+      o = fmaf(sc, sh_o[w][gg][d], o);
+      l = fmaf(sc, sh_l[w][gg], l);
     }
-    res = num / den;
+    const size_t row = (size_t)b * a.hq + h * G + gg;
+    if (P == 1) {
+      a.out[row * D + d] = o / l;                    // the only workgroup of (b, h)
+    } else {
+      // device-scope stores: written through to the level all XCDs see
+      const size_t prow = row * a.nparts + p;
+      __hip_atomic_store(a.part_o + prow * D + d, o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (d == 0) {
+        __hip_atomic_store(a.part_ml + prow * 2 + 0, mx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(a.part_ml + prow * 2 + 1, l, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
   }
-  a.out[row * D + d] = res;
+  if (P == 1) return;
+
+  // ---- the last workgroup of (b, h) to finish merges all partials by log-sum-exp ----
+  // Publish: wait until this workgroup's device-scope stores have completed, then count it.
+  // (A device-scope fence would also write back the whole L2, which is not needed here: the
+  // partials themselves were stored at device scope and are read back at device scope.)
+  __shared__ int sh_last;
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const unsigned prev = __hip_atomic_fetch_add(a.counters + (size_t)b * a.hkv + h, 1u, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+    sh_last = prev == (unsigned)(P - 1);
+  }
+  __syncthreads();
+  if (!sh_last) return;
+
+  // Merge: weights 2^(m_p - M) per (head, partition) in LDS, then independent loads of the
+  // partial outputs.  A partial must not be read from a stale cached copy of an earlier call:
+  // with many partials the merging workgroup drops this XCD's cached lines once (device-scope
+  // acquire) and reads float4s through the caches; with few it reads each value at device scope
+  // and leaves the caches alone.  Partitions are taken in tiles of TP so that one thread holds
+  // one (head, partition) pair per tile.
+  const bool via_cache = P >= 16;
+  if (via_cache) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  constexpr int NTH = 64 * kWaves;
+  constexpr int TP = NTH / G;                        // partitions per tile
+  constexpr int NQ = D / 4;                          // float4 columns of a head's output
+  constexpr int SPLIT = NTH / (G * NQ);              // threads per output column
+  __shared__ float sh_pm[NTH], sh_pw[NTH], sh_scale[G], sh_M[G], sh_den[G];
+  __shared__ float4 sh_part[NTH];
+  const int tid = threadIdx.x;
+  if (tid < G) {
+    sh_M[tid] = -INFINITY;
+    sh_den[tid] = 0.f;
+  }
+  const int ocol = tid % (G * NQ), part = tid / (G * NQ);
+  const int cg = ocol / NQ, cq = ocol % NQ;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int p0 = 0; p0 < P; p0 += TP) {
+    const int np = min(TP, P - p0);
+    const int tg = tid / TP, tp = tid % TP;
+    float mv = -INFINITY, lv = 0.f;
+    if (tp < np) {
+      float *ml2 = a.part_ml + (((size_t)b * a.hq + h * G + tg) * a.nparts + p0 + tp) * 2;
+      if (via_cache) {
+        const float2 v2 = *reinterpret_cast<const float2 *>(ml2);
+        mv = v2.x;
+        lv = v2.y;
+      } else {
+        mv = __hip_atomic_load(ml2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        lv = __hip_atomic_load(ml2 + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    __syncthreads();
+    sh_pm[tid] = mv;
+    __syncthreads();
+    if (tid < G) {   // new running maximum of head tid over this tile
+      float mt = sh_M[tid];
+      for (int k = 0; k < np; ++k) mt = fmaxf(mt, sh_pm[tid * TP + k]);
+      sh_scale[tid] = __builtin_amdgcn_exp2f(sh_M[tid] - mt);
+      sh_M[tid] = mt;
+    }
+    __syncthreads();
+    const float w = tp < np ? __builtin_amdgcn_exp2f(mv - sh_M[tg]) : 0.f;
+    sh_pw[tid] = w;
+    sh_pm[tid] = w * lv;
+    __syncthreads();
+    if (tid < G) {
+      float dsum = 0.f;
+      for (int k = 0; k < np; ++k) dsum += sh_pm[tid * TP + k];
+      sh_den[tid] = sh_den[tid] * sh_scale[tid] + dsum;
+    }
+    // output columns: thread (column, part) sums partitions part, part + SPLIT, ...
+    const float sc = sh_scale[cg];
+    acc = make_float4(acc.x * sc, acc.y * sc, acc.z * sc, acc.w * sc);
+    float *po = a.part_o + (((size_t)b * a.hq + h * G + cg) * a.nparts + p0) * D + 4 * cq;
+    if (via_cache) {
+#pragma unroll 8
+      for (int k = part; k < np; k += SPLIT) {
+        const float wk = sh_pw[cg * TP + k];
+        const float4 o4 = *reinterpret_cast<const float4 *>(po + (size_t)k * D);
+        acc.x = fmaf(wk, o4.x, acc.x);
+        acc.y = fmaf(wk, o4.y, acc.y);
+        acc.z = fmaf(wk, o4.z, acc.z);
+        acc.w = fmaf(wk, o4.w, acc.w);
+      }
+    } else {
+#pragma unroll 4
+      for (int k = part; k < np; k += SPLIT) {
+        const float wk = sh_pw[cg * TP + k];
+        float *src = po + (size_t)k * D;
+        acc.x = fmaf(wk, __hip_atomic_load(src + 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), acc.x);
+        acc.y = fmaf(wk, __hip_atomic_load(src + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), acc.y);
+        acc.z = fmaf(wk, __hip_atomic_load(src + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), acc.z);
+        acc.w = fmaf(wk, __hip_atomic_load(src + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), acc.w);
+      }
+    }
+  }
+  sh_part[tid] = acc;
+  __syncthreads();
+  if (tid < G * NQ) {
+    float4 r = sh_part[tid];
+    for (int k = 1; k < SPLIT; ++k) {
+      const float4 x = sh_part[tid + k * G * NQ];
+      r.x += x.x;
+      r.y += x.y;
+      r.z += x.z;
+      r.w += x.w;
+    }
+    const float inv = 1.0f / sh_den[cg];
+    reinterpret_cast<float4 *>(a.out + ((size_t)b * a.hq + h * G + cg) * D)[cq] =
+        make_float4(r.x * inv, r.y * inv, r.z * inv, r.w * inv);
+  }
+  if (tid == 0)   // ready for the next call
+    __hip_atomic_store(a.counters + (size_t)b * a.hkv + h, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 DecodePlan decode_plan(const dgq_params_t *p, int32_t batch, int32_t max_seq_len) {
+  // Each wave takes `per` consecutive 64-token chunks; a workgroup of kWaves waves takes
+  // kWaves * per chunks and writes one partial.  Aim at about one wave of residency on the chip
+  // (2048 waves at two waves per SIMD), with at most 16 chunks per wave.
   DecodePlan plan;
   const int64_t chunks_seq = (max_seq_len + kChunk - 1) / kChunk;
   const int64_t total = (int64_t)batch * p->num_kv_heads * chunks_seq;
-  const int64_t target = 2048;   // about one wave of residency on 256 CUs
+  const int64_t target = 2048;
   int64_t per = total > 0 ? (total + target - 1) / target : 1;
   if (per < 1) per = 1;
   if (per > 16) per = 16;
   plan.part_tokens = (int)(per * kChunk);
-  plan.nparts = (int)((max_seq_len + plan.part_tokens - 1) / plan.part_tokens);
+  const int64_t span = (int64_t)plan.part_tokens * kWaves;
+  plan.nparts = (int)((max_seq_len + span - 1) / span);
   if (plan.nparts < 1) plan.nparts = 1;
   return plan;
 }
@@ -341,7 +571,7 @@ DecodePlan decode_plan(const dgq_params_t *p, int32_t batch, int32_t max_seq_len
 template <int D, int G, int BS>
 static void launch_part(const DecodeArgs &a, int batch, hipStream_t s) {
   dim3 grid(a.nparts, a.hkv, batch);
-  hipLaunchKernelGGL((decode_partition_kernel<D, G, BS>), grid, dim3(64), 0, s, a);
+  hipLaunchKernelGGL((decode_partition_kernel<D, G, BS>), grid, dim3(64 * kWaves), 0, s, a);
 }
 
 template <int D, int G>
@@ -371,7 +601,9 @@ dgq_status_t launch_decode(const dgq_params_t *p, const uint16_t *q, const dgq_c
   a.nseg = cache->nseg;
   a.block_table = block_table;
   a.seq_lens = seq_lens;
-  a.part_ml = reinterpret_cast<float *>(ws);
+  char *w = reinterpret_cast<char *>(ws);
+  a.counters = reinterpret_cast<unsigned *>(w);
+  a.part_ml = reinterpret_cast<float *>(w + align_up((size_t)batch * p->num_kv_heads * sizeof(unsigned), 256));
   a.part_o = a.part_ml + align_up((size_t)batch * p->num_q_heads * plan.nparts * 2, 64);
   a.out = out;
   a.hkv = p->num_kv_heads;
@@ -386,18 +618,14 @@ dgq_status_t launch_decode(const dgq_params_t *p, const uint16_t *q, const dgq_c
   a.sm_log2 = softmax_scale * 1.4426950408889634f;
   if (D == 128) launch_part_g<128>(a, G, p->block_size, batch, stream);
   else launch_part_g<64>(a, G, p->block_size, batch, stream);
-  dgq_status_t st = check_launch("paged_decode_attn_int8 partition kernel");
-  if (st != DGQ_OK) return st;
-  dim3 grid(p->num_q_heads, batch);
-  if (D == 128) hipLaunchKernelGGL(decode_reduce_kernel<128>, grid, dim3(128), 0, stream, a);
-  else hipLaunchKernelGGL(decode_reduce_kernel<64>, grid, dim3(64), 0, stream, a);
-  return check_launch("paged_decode_attn_int8 reduce kernel");
+  return check_launch("paged_decode_attn_int8 kernel");
 }
 
 size_t decode_workspace_bytes(const dgq_params_t *p, int32_t batch, int32_t max_seq_len) {
   const DecodePlan plan = decode_plan(p, batch, max_seq_len);
   const size_t rows = (size_t)batch * p->num_q_heads * plan.nparts;
-  return (align_up(rows * 2, 64) + rows * p->head_dim) * sizeof(float) + 256;
+  return align_up((size_t)batch * p->num_kv_heads * sizeof(unsigned), 256) +
+         (align_up(rows * 2, 64) + rows * p->head_dim) * sizeof(float) + 256;
 }
 
 }  // namespace dgq

@@ -116,3 +116,29 @@ def test_decode_vs_unquantized_fp16_reported():
     print(f"DGQ attention vs fp16 attention: max rel err {H.rel_err_rows(out, exact):.3e}; "
           f"oracle DGQ vs fp16 {H.rel_err_rows(ref, exact):.3e}")
     assert H.rel_err_rows(out, ref) <= TOL
+
+
+@pytest.mark.parametrize("cid,over", [(2, dict(batch=4, seq_len=8192)), (3, dict(seq_len=32768))],
+                         ids=["bs16_4x8192", "bs64_1x32768"])
+def test_decode_split_merge_repeatable(cid, over):
+    """Many workgroups per (sequence, head): the last one to finish merges the partials of the
+    others.  Thirty calls on one workspace give bit-identical outputs that match the oracle."""
+    cfg = dgq_data.get_config(cid, **over)
+    lens = dgq_data.seq_lens(cfg, 15)
+    heads = _heads_for(cfg, 15, lens)
+    table, nblk = dgq_data.block_tables(cfg, 15, lens_total=lens)
+    params = H.params_for(cfg)
+    cache = H.cache_from_oracle(params, heads, table, nblk, cfg.batch)
+    q16 = dgq_data.queries(cfg, 15)
+    dq, dt = torch.from_numpy(q16).cuda(), torch.from_numpy(table).cuda()
+    dl = torch.from_numpy(lens.astype(np.int32)).cuda()
+    ws = Q.workspace(Q.decode_workspace_size(params, cfg.batch, int(lens.max())))
+    H.say("decode split merge", cid, over)
+    outs = [Q.paged_decode_attn_int8(params, dq, cache, dt, dl, int(lens.max()), ws=ws).clone() for _ in range(30)]
+    torch.cuda.synchronize()
+    for o in outs[1:]:
+        assert torch.equal(o, outs[0])
+    ref = H.oracle_decode(q16, heads, lens, cfg.hkv, cfg.group)
+    assert H.rel_err_rows(outs[0].cpu().numpy(), ref) <= TOL
+    # the merge leaves its completion counters at zero
+    assert int(ws[: cfg.batch * cfg.hkv * 4].view(torch.int32).abs().sum().item()) == 0
