@@ -43,7 +43,46 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=20.0,
                     help="time budget of the CPU oracle baseline (0 to skip)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 512 MiB device copy (torch) a few times: the reference "
+                         "kernel of known size for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE")
     return ap.parse_args()
+
+
+def kernel_source_digest() -> str:
+    import hashlib
+    path = os.path.join(ROOT, "quantized_paged_kv_dgq_amd", "csrc", "decode.hip")
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per decode launch from the committed counter profile, if it was taken on the
+    current decode kernel source (else None)."""
+    path = os.path.join(ROOT, "profiles", "decode_llama3_8b_layer_hbm_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("decode_source_sha256_16") != kernel_source_digest():
+        return None
+    try:
+        return int(float(kv["decode_hbm_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_calibration():
+    import torch
+
+    src = torch.empty(512 << 20, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration": {"bytes_read": 512 << 20, "bytes_written": 512 << 20, "launches": 5}}))
 
 
 def cpu_baseline(cfg, seed, budget_s):
@@ -89,6 +128,9 @@ def cpu_baseline(cfg, seed, budget_s):
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the path has no multi-GPU "
               "part in this build", file=sys.stderr)
@@ -214,8 +256,9 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
-            "traffic": None,
-            "kernel": "paged_decode_attn_int8 (partition + merge kernels, HIP events around the call)",
+            "traffic": measured_traffic(),
+            "kernel": "decode_partition_kernel<128,4,16> (one launch per paged_decode_attn_int8 call; "
+                      "HIP events around the call on its stream)",
         },
         "roofline_compress": {
             "bound": "hbm", "achieved": round(comp_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",

@@ -40,6 +40,15 @@ struct CompressArgs {
   dgq_cache_t cache;
 };
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// Codes are not read again until a later decode: store them non-temporally so they go to HBM
+// instead of settling as dirty lines in the Infinity Cache, whose write-back would otherwise be
+// paid by whichever kernel runs next.
+__device__ __forceinline__ void store_stream(int8_t *dst, const uint32_t (&w)[4]) {
+  __builtin_nontemporal_store(u32x4{w[0], w[1], w[2], w[3]}, reinterpret_cast<u32x4 *>(dst));
+}
+
 // -------------------------------------------------------------------------------------------
 // 1. stats
 // -------------------------------------------------------------------------------------------
@@ -466,7 +475,7 @@ __global__ __launch_bounds__(256) void encode_kernel(CompressArgs a) {
       continue;
     }
     int8_t *dst = a.cache.k_pool + ((size_t)blk * a.hkv + h) * tile_bytes + k_tile_offset<D, BS>(tok % BS, d0);
-    *reinterpret_cast<uint4 *>(dst) = make_uint4(outw[0], outw[1], outw[2], outw[3]);
+    store_stream(dst, outw);
   }
 
   // values: one unit = 16 tokens of one channel = 16 contiguous bytes of the tile
@@ -509,7 +518,7 @@ __global__ __launch_bounds__(256) void encode_kernel(CompressArgs a) {
     } else {
       off = d * 16;
     }
-    *reinterpret_cast<uint4 *>(tilep + off) = make_uint4(outw[0], outw[1], outw[2], outw[3]);
+    store_stream(tilep + off, outw);
   }
 
   // boundary bits: 8 bytes per chunk (one 64-token block, or four 16-token blocks)
