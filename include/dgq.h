@@ -202,7 +202,8 @@ dgq_status_t dgq_append(const dgq_params_t *p, const uint16_t *k_tok, const uint
  * cached tokens of kv head g / G, where khat, vhat are the dequantized codes.  The dequantization
  * is folded into the dot products; no dequantized copy is written.
  *   q    (device) fp16 [batch][num_q_heads][head_dim], 16-byte aligned.
- *   out  (device) fp32 [batch][num_q_heads][head_dim]; an empty sequence gives zeros.
+ *   out  (device) fp32 [batch][num_q_heads][head_dim], 16-byte aligned; an empty sequence gives
+ *        zeros.
  *   seq_lens (device) int32 [batch], each <= max_seq_len <= max_blocks * block_size.
  *   ws   device scratch of dgq_decode_workspace_size() bytes, 256-byte aligned.  Its first
  *        bytes are completion counters of the split-sequence merge: they must be zero before the
@@ -213,6 +214,40 @@ dgq_status_t paged_decode_attn_int8(const dgq_params_t *p, const uint16_t *q,
                                     int32_t max_blocks, const int32_t *seq_lens, int32_t batch,
                                     int32_t max_seq_len, float softmax_scale, float *out,
                                     void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* ---- Fixed 64-channel group INT8 baseline (DGQ article 2.2: the LLM.int8()-style grouping the
+ * DGQ design is compared against -- every 64-channel chunk of every token has its own min/max).
+ * Same pool layout, code formula and dequantization as DGQ; the ranges are kept per (token,
+ * group) instead of per segment.  Provided to compare error and throughput on the same data. ---- */
+typedef struct dgq_g64_cache {
+  int8_t *k_pool;        /* [num_blocks][num_kv_heads][block_size*head_dim], layout as dgq_cache_t */
+  int8_t *v_pool;
+  uint32_t *k_range;     /* [num_blocks][num_kv_heads][block_size][head_dim/64]: fp16 min in bits
+                            0..15, fp16 max in bits 16..31 */
+  uint32_t *v_range;
+  unsigned long long *status;  /* [4], as dgq_cache_t.status ([2] used) */
+  int32_t num_blocks;
+  int32_t reserved;
+} dgq_g64_cache_t;
+
+/* Quantize rows into the group-64 cache.  Rows cu_seqlens[b] .. cu_seqlens[b+1]-1 of k/v (token-
+ * major, strides as dgq_compress) go to cache positions first_pos[b] + r (first_pos may be NULL:
+ * all zero); max_rows bounds the rows per sequence, total_rows = cu_seqlens[batch], and every
+ * position must be < max_seq_len <= max_blocks * block_size.  Used both for a whole prefix and
+ * for one appended token per sequence (cu_seqlens = 0, 1, ..., batch; first_pos = lengths). */
+dgq_status_t dgq_g64_quantize(const dgq_params_t *p, const uint16_t *k, const uint16_t *v,
+                              int64_t stride_tok, int64_t stride_head, const int32_t *cu_seqlens,
+                              const int32_t *first_pos, int32_t batch, int32_t max_rows,
+                              int64_t total_rows, const int32_t *block_table, int32_t max_blocks,
+                              int32_t max_seq_len, const dgq_g64_cache_t *cache, hipStream_t stream);
+
+/* Paged decode attention over a group-64 cache; arguments and workspace (including its zeroed
+ * counters, dgq_decode_workspace_size) as paged_decode_attn_int8. */
+dgq_status_t paged_decode_attn_g64(const dgq_params_t *p, const uint16_t *q,
+                                   const dgq_g64_cache_t *cache, const int32_t *block_table,
+                                   int32_t max_blocks, const int32_t *seq_lens, int32_t batch,
+                                   int32_t max_seq_len, float softmax_scale, float *out, void *ws,
+                                   size_t ws_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -410,31 +410,33 @@ GROUP = 64
 
 
 def group64_compress(x16: np.ndarray):
-    """Codes int8 [L][D] and per-(token, group) min/max float16 [L][D/64] of one head."""
+    """Codes int8 [L][D] and per-(token, group) min/max float16 [L][D/64] of one head: R8 applied
+    to every 64-channel group of every token with that group's own range."""
     x16 = np.asarray(x16, dtype=np.float16)
     length, head_dim = x16.shape
     ng = head_dim // GROUP
-    codes = np.empty((length, head_dim), dtype=np.int8)
-    gmin = np.empty((length, ng), dtype=np.float16)
-    gmax = np.empty((length, ng), dtype=np.float16)
-    for t in range(length):
-        for g in range(ng):
-            chunk = x16[t, g * GROUP:(g + 1) * GROUP]
-            mn, mx = range_of(chunk)
-            gmin[t, g], gmax[t, g] = np.float16(mn), np.float16(mx)
-            codes[t, g * GROUP:(g + 1) * GROUP] = encode(chunk, mn, mx)
-    return codes, gmin, gmax
+    x = canonical_f32(x16).reshape(length, ng, GROUP)
+    mn = x.min(axis=2)
+    mx = x.max(axis=2)
+    diff = (mx - mn).astype(np.float32)
+    with np.errstate(divide="ignore"):
+        inv = np.where(diff > 0, np.float32(CODE_LEVELS) / diff, np.float32(0.0)).astype(np.float32)
+    d = (x - mn[:, :, None]).astype(np.float32)
+    u = (d * inv[:, :, None]).astype(np.float32)
+    codes = (np.clip(np.rint(u), 0, CODE_LEVELS).astype(np.int16) - 128).astype(np.int8)
+    return codes.reshape(length, head_dim), mn.astype(np.float16), mx.astype(np.float16)
 
 
 def group64_dequant(codes: np.ndarray, gmin: np.ndarray, gmax: np.ndarray) -> np.ndarray:
+    """R9 per (token, group)."""
     length, head_dim = codes.shape
-    out = np.empty((length, head_dim), dtype=np.float64)
-    for g in range(head_dim // GROUP):
-        sl = slice(g * GROUP, (g + 1) * GROUP)
-        for t in range(length):
-            mn = np.float32(gmin[t, g])
-            out[t, sl] = dequant(codes[t, sl], mn, quant_scale(mn, np.float32(gmax[t, g])))
-    return out
+    ng = head_dim // GROUP
+    mn = np.asarray(gmin, np.float16).astype(np.float32)
+    mx = np.asarray(gmax, np.float16).astype(np.float32)
+    scale = ((mx - mn).astype(np.float32) / np.float32(CODE_LEVELS)).astype(np.float32)
+    c = codes.reshape(length, ng, GROUP).astype(np.float64)
+    out = (c + 128.0) * scale.astype(np.float64)[:, :, None] + mn.astype(np.float64)[:, :, None]
+    return out.reshape(length, head_dim)
 
 
 # ----------------------------------------------------------------------------------------------

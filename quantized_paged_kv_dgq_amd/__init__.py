@@ -9,11 +9,14 @@ from ._lib import DGQError, EXPORTS, LIB_PATH, load  # noqa: F401
 from .api import (  # noqa: F401
     BlockPool,
     DGQCache,
+    DGQG64Cache,
     DGQParams,
     compress_workspace_size,
     decode_workspace_size,
     dgq_append,
     dgq_compress,
+    dgq_g64_quantize,
+    paged_decode_attn_g64,
     paged_decode_attn_int8,
     workspace,
 )

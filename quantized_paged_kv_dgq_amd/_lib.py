@@ -51,6 +51,18 @@ class Tail(ctypes.Structure):
     ]
 
 
+class G64Cache(ctypes.Structure):
+    _fields_ = [
+        ("k_pool", ctypes.c_void_p),
+        ("v_pool", ctypes.c_void_p),
+        ("k_range", ctypes.c_void_p),
+        ("v_range", ctypes.c_void_p),
+        ("status", ctypes.c_void_p),
+        ("num_blocks", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+    ]
+
+
 class Cache(ctypes.Structure):
     _fields_ = [
         ("k_pool", ctypes.c_void_p),
@@ -77,6 +89,7 @@ EXPORTS = [
     "dgq_pool_create", "dgq_pool_destroy", "dgq_block_alloc", "dgq_block_free", "dgq_pool_num_free",
     "dgq_compress_workspace_size", "dgq_decode_workspace_size",
     "dgq_compress", "dgq_append", "paged_decode_attn_int8",
+    "dgq_g64_quantize", "paged_decode_attn_g64",
 ]
 
 _lib = None
@@ -118,6 +131,12 @@ def load() -> ctypes.CDLL:
     lib.paged_decode_attn_int8.argtypes = [P(Params), vp, P(Cache), vp, i32, vp, i32, i32,
                                            ctypes.c_float, vp, vp, sz, vp]
     lib.paged_decode_attn_int8.restype = i32
+    lib.dgq_g64_quantize.argtypes = [P(Params), vp, vp, i64, i64, vp, vp, i32, i32, i64, vp, i32, i32,
+                                     P(G64Cache), vp]
+    lib.dgq_g64_quantize.restype = i32
+    lib.paged_decode_attn_g64.argtypes = [P(Params), vp, P(G64Cache), vp, i32, vp, i32, i32,
+                                          ctypes.c_float, vp, vp, sz, vp]
+    lib.paged_decode_attn_g64.restype = i32
     _lib = lib
     return lib
 

@@ -15,7 +15,7 @@ from typing import Optional, Sequence
 import torch
 
 from . import _lib
-from ._lib import Cache, Params, check
+from ._lib import Cache, G64Cache, Params, check
 
 
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
@@ -76,6 +76,25 @@ class DGQCache:
         """(starts int32 [B][H][cap], params float32 [B][H][cap][6], nseg [B][H]) on the host."""
         raw = self.segs.cpu()
         return raw[..., 0].numpy(), raw[..., 1:7].contiguous().view(torch.float32).numpy(), self.nseg.cpu().numpy()
+
+
+class DGQG64Cache:
+    """Device buffers of one layer's fixed 64-channel group cache (dgq_g64_cache_t)."""
+
+    def __init__(self, params: DGQParams, num_blocks: int, device="cuda"):
+        p = params.c
+        dev = torch.device(device)
+        tile = p.block_size * p.head_dim
+        self.params = params
+        self.num_blocks = num_blocks
+        self.k_pool = torch.zeros((num_blocks, p.num_kv_heads, tile), dtype=torch.int8, device=dev)
+        self.v_pool = torch.zeros_like(self.k_pool)
+        ng = p.head_dim // 64
+        self.k_range = torch.zeros((num_blocks, p.num_kv_heads, p.block_size, ng), dtype=torch.int32, device=dev)
+        self.v_range = torch.zeros_like(self.k_range)
+        self.status = torch.zeros(4, dtype=torch.int64, device=dev)
+        self.c = G64Cache(_ptr(self.k_pool), _ptr(self.v_pool), _ptr(self.k_range), _ptr(self.v_range),
+                          _ptr(self.status), num_blocks, 0)
 
 
 class BlockPool:
@@ -174,4 +193,38 @@ def paged_decode_attn_int8(params: DGQParams, q: torch.Tensor, cache: DGQCache,
         _ptr(seq_lens), batch, max_seq_len, float(softmax_scale), _ptr(out), _ptr(ws), ws.numel(),
         _stream(stream))
     check(st, "paged_decode_attn_int8")
+    return out
+
+
+def dgq_g64_quantize(params: DGQParams, k: torch.Tensor, v: torch.Tensor, cu_seqlens: torch.Tensor,
+                     block_table: torch.Tensor, cache: DGQG64Cache, max_rows: int, total_rows: int,
+                     max_seq_len: int, first_pos: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Quantize rows into the group-64 cache (see dgq_g64_quantize in include/dgq.h)."""
+    _need(k.dtype == torch.float16 and v.dtype == torch.float16 and k.stride() == v.stride(), "float16 k, v")
+    _need(k.stride(-1) == 1, "channels must be contiguous")
+    batch = cu_seqlens.numel() - 1
+    st = _lib.load().dgq_g64_quantize(
+        ctypes.byref(params.c), _ptr(k), _ptr(v), k.stride(0), k.stride(1), _ptr(cu_seqlens), _ptr(first_pos),
+        batch, max_rows, total_rows, _ptr(block_table), block_table.shape[1], max_seq_len, ctypes.byref(cache.c),
+        _stream(stream))
+    check(st, "dgq_g64_quantize")
+
+
+def paged_decode_attn_g64(params: DGQParams, q: torch.Tensor, cache: DGQG64Cache, block_table: torch.Tensor,
+                          seq_lens: torch.Tensor, max_seq_len: int, softmax_scale: Optional[float] = None,
+                          out: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
+                          stream=None) -> torch.Tensor:
+    """Decode attention over a group-64 cache; returns fp32 [B][Hq][D]."""
+    _need(q.dtype == torch.float16 and q.is_contiguous(), "q: contiguous float16 [B][Hq][D]")
+    batch = q.shape[0]
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(params.c.head_dim)
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    if ws is None:
+        ws = workspace(decode_workspace_size(params, batch, max_seq_len), q.device)
+    st = _lib.load().paged_decode_attn_g64(
+        ctypes.byref(params.c), _ptr(q), ctypes.byref(cache.c), _ptr(block_table), block_table.shape[1],
+        _ptr(seq_lens), batch, max_seq_len, float(softmax_scale), _ptr(out), _ptr(ws), ws.numel(), _stream(stream))
+    check(st, "paged_decode_attn_g64")
     return out

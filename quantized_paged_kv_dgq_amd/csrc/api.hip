@@ -132,7 +132,7 @@ extern "C" dgq_status_t paged_decode_attn_int8(const dgq_params_t *p, const uint
   if (st != DGQ_OK) return st;
   if (batch < 0 || max_seq_len < 0) return DGQ_ERR_INVALID_ARG;
   if (batch == 0) return DGQ_OK;
-  if (!q || !out || !seq_lens || !aligned(q, 16) || !aligned(out, 4)) return DGQ_ERR_INVALID_ARG;
+  if (!q || !out || !seq_lens || !aligned(q, 16) || !aligned(out, 16)) return DGQ_ERR_INVALID_ARG;
   if (!std::isfinite(softmax_scale)) return DGQ_ERR_INVALID_ARG;
   if ((st = check_table(p, block_table, max_blocks, max_seq_len)) != DGQ_OK) return st;
   if ((st = check_cache(cache, batch, false)) != DGQ_OK) return st;
@@ -141,4 +141,52 @@ extern "C" dgq_status_t paged_decode_attn_int8(const dgq_params_t *p, const uint
   if (ws_bytes < need) return DGQ_ERR_WORKSPACE_TOO_SMALL;
   return launch_decode(p, q, cache, block_table, max_blocks, seq_lens, batch, max_seq_len,
                        softmax_scale, out, ws, stream);
+}
+
+static dgq_status_t check_g64_cache(const dgq_g64_cache_t *c) {
+  if (c == nullptr || !c->k_pool || !c->v_pool || !c->k_range || !c->v_range || !c->status) return DGQ_ERR_INVALID_ARG;
+  if (!aligned(c->k_pool, 16) || !aligned(c->v_pool, 16) || !aligned(c->k_range, 4) ||
+      !aligned(c->v_range, 4) || !aligned(c->status, 8) || c->num_blocks < 1)
+    return DGQ_ERR_INVALID_ARG;
+  return DGQ_OK;
+}
+
+extern "C" dgq_status_t dgq_g64_quantize(const dgq_params_t *p, const uint16_t *k, const uint16_t *v,
+                                         int64_t stride_tok, int64_t stride_head,
+                                         const int32_t *cu_seqlens, const int32_t *first_pos,
+                                         int32_t batch, int32_t max_rows, int64_t total_rows,
+                                         const int32_t *block_table, int32_t max_blocks,
+                                         int32_t max_seq_len, const dgq_g64_cache_t *cache,
+                                         hipStream_t stream) {
+  dgq_status_t st = check_params(p);
+  if (st != DGQ_OK) return st;
+  if (batch < 0 || max_rows < 0 || total_rows < 0 || max_seq_len < 0) return DGQ_ERR_INVALID_ARG;
+  if (batch == 0) return DGQ_OK;
+  if (total_rows > (int64_t)batch * max_rows || total_rows >= (int64_t)1 << 31) return DGQ_ERR_INVALID_ARG;
+  if (!k || !v || !cu_seqlens || !aligned(k, 16) || !aligned(v, 16)) return DGQ_ERR_INVALID_ARG;
+  if (stride_tok <= 0 || stride_head < 0 || stride_tok % 8 != 0 || stride_head % 8 != 0) return DGQ_ERR_INVALID_ARG;
+  if ((st = check_table(p, block_table, max_blocks, max_seq_len)) != DGQ_OK) return st;
+  if ((st = check_g64_cache(cache)) != DGQ_OK) return st;
+  return launch_g64_quantize(p, k, v, stride_tok, stride_head, cu_seqlens, first_pos, batch, max_rows,
+                             total_rows, block_table, max_blocks, max_seq_len, cache, stream);
+}
+
+extern "C" dgq_status_t paged_decode_attn_g64(const dgq_params_t *p, const uint16_t *q,
+                                              const dgq_g64_cache_t *cache, const int32_t *block_table,
+                                              int32_t max_blocks, const int32_t *seq_lens, int32_t batch,
+                                              int32_t max_seq_len, float softmax_scale, float *out,
+                                              void *ws, size_t ws_bytes, hipStream_t stream) {
+  dgq_status_t st = check_params(p);
+  if (st != DGQ_OK) return st;
+  if (batch < 0 || max_seq_len < 0) return DGQ_ERR_INVALID_ARG;
+  if (batch == 0) return DGQ_OK;
+  if (!q || !out || !seq_lens || !aligned(q, 16) || !aligned(out, 16)) return DGQ_ERR_INVALID_ARG;
+  if (!std::isfinite(softmax_scale)) return DGQ_ERR_INVALID_ARG;
+  if ((st = check_table(p, block_table, max_blocks, max_seq_len)) != DGQ_OK) return st;
+  if ((st = check_g64_cache(cache)) != DGQ_OK) return st;
+  const size_t need = decode_workspace_bytes(p, batch, max_seq_len);
+  if (ws == nullptr || !aligned(ws, 256)) return DGQ_ERR_INVALID_ARG;
+  if (ws_bytes < need) return DGQ_ERR_WORKSPACE_TOO_SMALL;
+  return launch_g64_decode(p, q, cache, block_table, max_blocks, seq_lens, batch, max_seq_len,
+                           softmax_scale, out, ws, stream);
 }

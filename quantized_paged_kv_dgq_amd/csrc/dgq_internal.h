@@ -59,6 +59,17 @@ dgq_status_t launch_append(const dgq_params_t *p, const uint16_t *k_tok, const u
                            const int32_t *seq_lens, int32_t batch, const int32_t *block_table,
                            int32_t max_blocks, const dgq_cache_t *cache, hipStream_t stream);
 
+// ---- fixed 64-channel group baseline ----
+dgq_status_t launch_g64_quantize(const dgq_params_t *p, const uint16_t *k, const uint16_t *v,
+                                 int64_t stride_tok, int64_t stride_head, const int32_t *cu_seqlens,
+                                 const int32_t *first_pos, int32_t batch, int32_t max_rows,
+                                 int64_t total_rows, const int32_t *block_table, int32_t max_blocks,
+                                 int32_t max_seq_len, const dgq_g64_cache_t *cache, hipStream_t stream);
+dgq_status_t launch_g64_decode(const dgq_params_t *p, const uint16_t *q, const dgq_g64_cache_t *cache,
+                               const int32_t *block_table, int32_t max_blocks, const int32_t *seq_lens,
+                               int32_t batch, int32_t max_seq_len, float softmax_scale, float *out,
+                               void *ws, hipStream_t stream);
+
 }  // namespace dgq
 
 // ---- device helpers ----

@@ -406,17 +406,23 @@ def check_append_from_empty(block_size=16):
 # -- group-64 baseline -----------------------------------------------------------------------------
 
 def check_group64():
+    """Every (token, 64-channel group) is R8 with its own range: compared with the one-segment
+    compression of that group alone (a different route through the oracle) and with numpy's
+    min/max; reconstruction and nearest-code property."""
     rng = np.random.default_rng(4)
     x = (rng.standard_normal((40, 128)) * 0.2).astype(np.float16)
+    x[3, :64] = np.float16(0.5)                 # a constant group
     codes, gmin, gmax = O.group64_compress(x)
     for t in range(40):
         for g in range(2):
             sl = slice(64 * g, 64 * g + 64)
             assert gmin[t, g] == np.min(x[t, sl]) and gmax[t, g] == np.max(x[t, sl])
+            assert np.array_equal(codes[t, sl], O.encode(x[t, sl], np.float32(gmin[t, g]), np.float32(gmax[t, g])))
             sc = O.quant_scale(np.float32(gmin[t, g]), np.float32(gmax[t, g]))
             assert _nearest_code_ok(x[t, sl], codes[t, sl], np.float32(gmin[t, g]), sc)
     rec = O.group64_dequant(codes, gmin, gmax)
     assert np.max(np.abs(rec - x.astype(np.float64))) < 0.01
+    assert np.all(rec[3, :64] == 0.5)
 
 
 ALL_CHECKS = [
