@@ -12,6 +12,11 @@ Four caches rotate: step i compresses and appends into cache i % 4 and decodes c
 which was written two steps earlier, so the decode's 256 MiB of codes are read from HBM and not
 from the 256 MB Infinity Cache.  Inputs are resident in HBM before the timed region.
 
+After the timed DGQ steps, the fixed 64-channel group INT8 baseline runs the same step shape on
+the same data (quantize the batch + the appended token, decode over 8193 tokens; two caches
+rotate), and both decoders' outputs are compared with float32 attention over the unquantized
+fp16 keys/values ("group64_baseline", "quality_vs_fp16").
+
 Prints one JSON line.  ``value`` is the decode attention's throughput in GB/s of algorithmic
 bytes (INT8 K/V codes + block table + segment tables + q + out), from HIP events recorded around
 every decode call on the stream the kernels run on.
@@ -49,10 +54,16 @@ def parse():
     return ap.parse_args()
 
 
+DECODE_SOURCES = ("decode.hip", "decode_common.h", "dgq_internal.h")
+
+
 def kernel_source_digest() -> str:
+    """Digest of the sources the INT8 decode kernel is compiled from."""
     import hashlib
-    path = os.path.join(ROOT, "quantized_paged_kv_dgq_amd", "csrc", "decode.hip")
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for name in DECODE_SOURCES:
+        h.update(open(os.path.join(ROOT, "quantized_paged_kv_dgq_amd", "csrc", name), "rb").read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic():
@@ -65,7 +76,7 @@ def measured_traffic():
     for line in open(path):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
-            kv[k.strip()] = v.strip()
+            kv[k.strip()] = v.split("#", 1)[0].strip()
     if kv.get("decode_source_sha256_16") != kernel_source_digest():
         return None
     try:
@@ -124,6 +135,33 @@ def cpu_baseline(cfg, seed, budget_s):
         "compress_tokens_per_s": tokens / t_comp,
         "seconds": t_comp + t_dec,
     }
+
+
+def quality_vs_fp16(cfg, k, v, cu, k_tok, v_tok, q, out_dgq, out_g64):
+    """Max and mean over (sequence, query head) of ||o - o_fp16||_inf / ||o_fp16||_inf, where
+    o_fp16 is float32 attention over the unquantized fp16 keys/values (all 8193 tokens)."""
+    import torch
+
+    B, hkv, hq, d = cfg.batch, cfg.hkv, cfg.hq, cfg.head_dim
+    G = hq // hkv
+    ref = torch.empty_like(out_dgq)
+    for b in range(B):
+        a, e = int(cu[b]), int(cu[b + 1])
+        kb = torch.cat([k[a:e], k_tok[b:b + 1]]).float().permute(1, 0, 2).contiguous()   # [hkv][L][d]
+        vb = torch.cat([v[a:e], v_tok[b:b + 1]]).float().permute(1, 0, 2).contiguous()
+        qb = q[b].float().view(hkv, G, d).contiguous()
+        sc = torch.bmm(qb, kb.transpose(1, 2).contiguous()) / math.sqrt(d)
+        ref[b] = torch.bmm(torch.softmax(sc, dim=-1), vb).reshape(hq, d)
+    den = ref.abs().amax(-1)
+
+    def err(o):
+        r = (o - ref).abs().amax(-1) / den
+        return float(r.max()), float(r.mean())
+
+    e1, e2 = err(out_dgq), err(out_g64)
+    return {"dgq_max_rel_err": round(e1[0], 6), "dgq_mean_rel_err": round(e1[1], 6),
+            "group64_max_rel_err": round(e2[0], 6), "group64_mean_rel_err": round(e2[1], 6),
+            "rows": B * hq, "reference": "float32 attention over the unquantized fp16 K/V"}
 
 
 def main():
@@ -210,6 +248,37 @@ def main():
     app_ms = np.array([e[1].elapsed_time(e[2]) for e in ev])
     dec_ms = np.array([e[2].elapsed_time(e[3]) for e in ev])
 
+    # the group-64 baseline on the same data, same step shape: quantize the batch, quantize the
+    # appended token, decode over 8193 tokens; two caches rotate so the decoded one is cold
+    g_caches = [Q.DGQG64Cache(params, nblk, dev) for _ in range(2)]
+    one = torch.arange(B + 1, dtype=torch.int32, device=dev)
+    out_g = torch.empty_like(out)
+
+    def g_quant(i):
+        c = g_caches[i % 2]
+        Q.dgq_g64_quantize(params, k, v, dcu, dtable, c, L, total, L + 1)
+        Q.dgq_g64_quantize(params, k_tok, v_tok, one, dtable, c, 1, B, L + 1, first_pos=pos)
+
+    def g_decode(i):
+        Q.paged_decode_attn_g64(params, q, g_caches[(i + 1) % 2], dtable, dec_lens, L + 1, out=out_g, ws=ws_d)
+
+    for i in range(2 + args.warmup):
+        g_quant(i)
+        g_decode(i)
+    torch.cuda.synchronize()
+    gev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    for i in range(K):
+        e = gev[i]
+        e[0].record()
+        g_quant(i)
+        e[1].record()
+        g_decode(i)
+        e[2].record()
+    torch.cuda.synchronize()
+    gq_ms = np.array([e[0].elapsed_time(e[1]) for e in gev])
+    gd_ms = np.array([e[1].elapsed_time(e[2]) for e in gev])
+    quality = quality_vs_fp16(cfg, k, v, cu, k_tok, v_tok, q, out, out_g)
+
     # algorithmic bytes
     Ld = L + 1
     nseg = torch.stack([c.nseg for c in caches]).cpu().numpy()
@@ -223,6 +292,9 @@ def main():
     dec_gbs = dec_bytes / dec_s / 1e9
     comp_gbs = comp_bytes / comp_s / 1e9
     hist = np.bincount(nseg.reshape(-1), minlength=6).tolist()
+    g_dec_s = float(np.mean(gd_ms)) / 1e3
+    g_dec_bytes = (B * 2 * Ld * hkv * d + B * Ld * hkv * (d // 64) * 4 * 2 + B * math.ceil(Ld / bs) * 4
+                   + B * hq * d * 2 + B * hq * d * 4)
 
     rec = {
         "metric": "INT8 paged decode-attn GB/s (% HBM peak) + dgq_compress tokens/s",
@@ -266,6 +338,17 @@ def main():
             "kernel": "dgq_compress (stats + scores + select + encode, HIP events around the call)",
         },
         "wall_s_timed": round(wall, 4),
+        "group64_baseline": {
+            "decode_us": round(g_dec_s * 1e6, 2),
+            "decode_gbs_alg": round(g_dec_bytes / g_dec_s / 1e9, 1),
+            "decode_frac_hbm_peak": round(g_dec_bytes / g_dec_s / 1e9 / HBM_PEAK_GBS, 4),
+            "quantize_us": round(float(np.mean(gq_ms)) * 1e3, 2),
+            "quantize_tokens_per_s": round((total + B) / (float(np.mean(gq_ms)) / 1e3), 1),
+            "decode_bytes": int(g_dec_bytes),
+            "dgq_decode_bytes": int(dec_bytes),
+            "dgq_decode_speedup": round(g_dec_s / dec_s, 4),
+        },
+        "quality_vs_fp16": quality,
     }
     if cpu is not None:
         rec["cpu_baseline"] = cpu
