@@ -6,9 +6,9 @@
 // block table).
 //
 // How (gfx950):
-//  * A workgroup of four waves per (partition, kv head, sequence); each wave takes a run of
-//    64-token chunks, the waves are merged in LDS, and a second kernel merges partitions by
-//    log-sum-exp.
+//  * A workgroup of four waves per (partition, kv head, sequence); the partition's 64-token
+//    chunks are split evenly over the waves, the waves are merged in LDS, and the last workgroup
+//    of each (sequence, kv head) to finish merges the partitions by log-sum-exp.
 //  * The dequantization is folded into integer dot products: q . khat_t = ks_t * (q . c_t) +
 //    midK_t * sum(q) and sum_t p_t vhat_t = sum_t (p_t vs_t) c_t + sum_t p_t midV_t, where
 //    (ks, midK, vs, midV) belong to the segment of token t and mid = min + 128 * scale.
@@ -42,15 +42,15 @@ __global__ __launch_bounds__(64 * kWaves) void decode_partition_kernel(DecodeArg
   const bool live = (g < G) && (piece < 3);
   const ByteSel bsel = byte_sel(piece, live);
   const int bh = b * a.hkv + h;
-  const int wg_begin = p * a.part_tokens * kWaves;
-  const int t_begin = wg_begin + wave * a.part_tokens;
+  const int span = a.part_tokens * kWaves;
+  const int wg_begin = p * span;
 
-  // Loads that do not depend on the sequence length go out together with it: the partition's
-  // block ids (one per lane, inside the table row), the segment-table row of this lane and the
-  // query slice of this lane.
+  // Loads that do not depend on the sequence length go out together with it: the block ids of
+  // the workgroup's span (one per thread, inside the table row; the span holds at most one block
+  // per thread), the segment-table row of this lane and the query slice of this lane.
   const int32_t *bt = a.block_table + (size_t)b * a.max_blocks;
-  const int blk0 = t_begin / BS;
-  const int blk_raw = blk0 + lane < a.max_blocks ? bt[blk0 + lane] : 0;
+  const int wblk0 = wg_begin / BS;
+  const int wblk_raw = wblk0 + (int)threadIdx.x < a.max_blocks ? bt[wblk0 + threadIdx.x] : 0;
   const int ns_raw = a.nseg[bh];
   dgq_seg_t seg_raw = {};
   if (lane < a.seg_cap) seg_raw = a.segs[(size_t)bh * a.seg_cap + lane];
@@ -72,8 +72,12 @@ __global__ __launch_bounds__(64 * kWaves) void decode_partition_kernel(DecodeArg
     return;
   }
   if (wg_begin >= L) return;                       // the whole workgroup has nothing to do
-  const bool active = t_begin < L;
-  const int t_end = min(L, t_begin + a.part_tokens);
+  const WaveRange wr = wave_range(wg_begin, span, L, wave);
+  const int t_begin = wr.t_begin, t_end = wr.t_end;
+  const bool active = t_begin < t_end;
+  __shared__ int sh_blk[64 * kWaves];
+  sh_blk[threadIdx.x] = wblk_raw;
+  __syncthreads();
   __shared__ float sh_o[kWaves][G][D];
   __shared__ float sh_m[kWaves][G], sh_l[kWaves][G];
   // float output of each lane (C layout), folded from the int32 sums only when a maximum moves
@@ -146,12 +150,13 @@ __global__ __launch_bounds__(64 * kWaves) void decode_partition_kernel(DecodeArg
     const float wq = live ? ldexpf(a.sm_log2, 16 - 8 * piece - qexp) : 0.f;
     const float qsum_s = qsum * a.sm_log2;
 
-    // ---- block ids of the partition: lane i holds the partition's i-th block (<= 64 blocks) ----
+    // ---- block ids of the wave's run: lane i holds its i-th block (<= 64 blocks) ----
+    const int blk0 = t_begin / BS;
     const int nblk_part = (t_end - 1) / BS - blk0 + 1;
     int my_blk = 0;
     {
       bool bad = false;
-      if (lane < nblk_part) my_blk = checked_block(blk_raw, a.num_blocks, bad);
+      if (lane < nblk_part) my_blk = checked_block(sh_blk[blk0 - wblk0 + lane], a.num_blocks, bad);
       if (__ballot(bad) != 0ull && lane == 0) atomicAdd(a.status + 2, 1ull);
     }
     const size_t tile_bytes = (size_t)BS * D;
@@ -348,16 +353,18 @@ __global__ __launch_bounds__(64 * kWaves) void decode_partition_kernel(DecodeArg
 }
 
 DecodePlan decode_plan(const dgq_params_t *p, int32_t batch, int32_t max_seq_len) {
-  // Each wave takes `per` consecutive 64-token chunks; a workgroup of kWaves waves takes
-  // kWaves * per chunks and writes one partial.  Aim at about one wave of residency on the chip
-  // (2048 waves at two waves per SIMD), with at most 16 chunks per wave.
+  // Each workgroup takes kWaves * per consecutive 64-token chunks of one (sequence, kv head) and
+  // writes one partial; its waves split them evenly.  Aim at about one workgroup per compute unit
+  // (1024 waves): fewer, longer workgroups leave fewer partials to merge, and one wave per SIMD
+  // already keeps enough loads in flight.  A wave's run spans at most 64 blocks (one block id per
+  // lane), so per <= block_size.
   DecodePlan plan;
   const int64_t chunks_seq = (max_seq_len + kChunk - 1) / kChunk;
   const int64_t total = (int64_t)batch * p->num_kv_heads * chunks_seq;
-  const int64_t target = 2048;
+  const int64_t target = 1024;
   int64_t per = total > 0 ? (total + target - 1) / target : 1;
   if (per < 1) per = 1;
-  if (per > 16) per = 16;
+  if (per > p->block_size) per = p->block_size;
   plan.part_tokens = (int)(per * kChunk);
   const int64_t span = (int64_t)plan.part_tokens * kWaves;
   plan.nparts = (int)((max_seq_len + span - 1) / span);

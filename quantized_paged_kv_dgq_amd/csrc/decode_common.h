@@ -11,6 +11,7 @@
 namespace dgq {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v2i_t __attribute__((ext_vector_type(2)));
 
 constexpr int kWaves = 4;   // waves per decode workgroup
 
@@ -79,6 +80,31 @@ DecodeArgs make_decode_args(const dgq_params_t *p, const uint16_t *q, const int8
                             int32_t batch, int32_t max_seq_len, float softmax_scale, float *out,
                             void *ws);
 
+// Token range [t_begin, t_end) of one wave: the workgroup's tokens [wg_begin, min(L, wg_begin +
+// span)) are dealt to the kWaves waves as nearly equal runs of whole 64-token chunks, so a short
+// sequence or a sequence's last partition still keeps every wave busy.
+struct WaveRange {
+  int t_begin, t_end;
+};
+__device__ __forceinline__ WaveRange wave_range(int wg_begin, int span, int L, int wave) {
+  const int wg_end = min(L, wg_begin + span);
+  const int nch = (wg_end - wg_begin + kChunk - 1) / kChunk;
+  const int c0 = wave * nch / kWaves, c1 = (wave + 1) * nch / kWaves;
+  return {wg_begin + c0 * kChunk, min(wg_end, wg_begin + c1 * kChunk)};
+}
+
+// Buffer resource over `bytes` bytes at `base` (raw, untyped, 32-bit data format): loads past the
+// end return zero, stores past the end are dropped.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+// Cache policy of the partials: agent (device) scope, i.e. coherent across the XCDs' L2 caches,
+// the same policy as relaxed device-scope atomic loads and stores.
+constexpr int kAgentScope = 16;
+
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v2f __attribute__((ext_vector_type(2)));
+
 // Merge the kWaves per-wave results of a workgroup (already in sh_o / sh_m / sh_l) into one
 // partial; with one workgroup per (sequence, kv head) write the output directly, otherwise publish
 // the partial and let the last workgroup of (b, h) merge all partials by log-sum-exp.
@@ -86,30 +112,42 @@ template <int D, int G>
 __device__ __forceinline__ void finish_partition(const DecodeArgs &a, int b, int h, int p, int L,
                                                  float (&sh_o)[kWaves][G][D], float (&sh_m)[kWaves][G],
                                                  float (&sh_l)[kWaves][G]) {
+  constexpr int NTH = 64 * kWaves;
+  constexpr int NQ = D / 4;                          // float4 columns of a head's output
+  static_assert(G * NQ <= NTH, "one float4 column per thread");
   __syncthreads();
+  const int tid = threadIdx.x;
   const int P = (L + a.part_tokens * kWaves - 1) / (a.part_tokens * kWaves);   // workgroups of (b, h)
-  for (int e = threadIdx.x; e < G * D; e += 64 * kWaves) {
-    const int gg = e / D, d = e % D;
+  const size_t row0 = (size_t)b * a.hq + h * G;      // first query head row of this kv head
+  if (tid < G * NQ) {
+    const int gg = tid / NQ, d = 4 * (tid % NQ);
     float mx = -INFINITY;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) mx = fmaxf(mx, sh_m[w][gg]);
-    float o = 0.f, l = 0.f;
+    v4f o = {0.f, 0.f, 0.f, 0.f};
+    float l = 0.f;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
       const float sc = __builtin_amdgcn_exp2f(sh_m[w][gg] - mx);
-      o = fmaf(sc, sh_o[w][gg][d], o);
+      o.x = fmaf(sc, sh_o[w][gg][d + 0], o.x);
+      o.y = fmaf(sc, sh_o[w][gg][d + 1], o.y);
+      o.z = fmaf(sc, sh_o[w][gg][d + 2], o.z);
+      o.w = fmaf(sc, sh_o[w][gg][d + 3], o.w);
       l = fmaf(sc, sh_l[w][gg], l);
     }
-    const size_t row = (size_t)b * a.hq + h * G + gg;
-    if (P == 1) {
-      a.out[row * D + d] = o / l;                    // the only workgroup of (b, h)
+    if (P == 1) {                                    // the only workgroup of (b, h)
+      const float inv = 1.0f / l;
+      *reinterpret_cast<float4 *>(a.out + (row0 + gg) * D + d) = make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
     } else {
-      // device-scope stores: written through to the level all XCDs see
-      const size_t prow = row * a.nparts + p;
-      __hip_atomic_store(a.part_o + prow * D + d, o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      // partial p of head row0 + gg, stored at device scope (to the level all XCDs see); the
+      // buffer resource covers the G heads of this kv head, so it is the same for every lane
+      const int prow = gg * a.nparts + p;
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i, o), raw_rsrc(a.part_o + row0 * a.nparts * D, G * a.nparts * D * 4),
+                                             (prow * D + d) * 4, 0, kAgentScope);
       if (d == 0) {
-        __hip_atomic_store(a.part_ml + prow * 2 + 0, mx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(a.part_ml + prow * 2 + 1, l, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const v2f ml = {mx, l};
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2i_t, ml), raw_rsrc(a.part_ml + row0 * a.nparts * 2, G * a.nparts * 8),
+                                              prow * 8, 0, kAgentScope);
       }
     }
   }
@@ -117,12 +155,10 @@ __device__ __forceinline__ void finish_partition(const DecodeArgs &a, int b, int
 
   // ---- the last workgroup of (b, h) to finish merges all partials by log-sum-exp ----
   // Publish: wait until this workgroup's device-scope stores have completed, then count it.
-  // (A device-scope fence would also write back the whole L2, which is not needed here: the
-  // partials themselves were stored at device scope and are read back at device scope.)
   __shared__ int sh_last;
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if (threadIdx.x == 0) {
+  if (tid == 0) {
     const unsigned prev = __hip_atomic_fetch_add(a.counters + (size_t)b * a.hkv + h, 1u, __ATOMIC_RELAXED,
                                                  __HIP_MEMORY_SCOPE_AGENT);
     sh_last = prev == (unsigned)(P - 1);
@@ -130,102 +166,72 @@ __device__ __forceinline__ void finish_partition(const DecodeArgs &a, int b, int
   __syncthreads();
   if (!sh_last) return;
 
-  // Merge: weights 2^(m_p - M) per (head, partition) in LDS, then independent loads of the
-  // partial outputs.  A partial must not be read from a stale cached copy of an earlier call:
-  // with many partials the merging workgroup drops this XCD's cached lines once (device-scope
-  // acquire) and reads float4s through the caches; with few it reads each value at device scope
-  // and leaves the caches alone.  Partitions are taken in tiles of TP so that one thread holds
-  // one (head, partition) pair per tile.
-  const bool via_cache = P >= 16;
-  if (via_cache) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  constexpr int NTH = 64 * kWaves;
-  constexpr int TP = NTH / G;                        // partitions per tile
-  constexpr int NQ = D / 4;                          // float4 columns of a head's output
-  constexpr int SPLIT = NTH / (G * NQ);              // threads per output column
-  __shared__ float sh_pm[NTH], sh_pw[NTH], sh_scale[G], sh_M[G], sh_den[G];
-  __shared__ float4 sh_part[NTH];
-  const int tid = threadIdx.x;
-  if (tid < G) {
-    sh_M[tid] = -INFINITY;
-    sh_den[tid] = 0.f;
-  }
+  // Merge.  Thread (column, part) takes partitions part, part + SPLIT, ... of its head and
+  // column; each round issues the (m, l) and output loads of KB partitions at once (device-scope
+  // loads, so no stale cached copy of an earlier call is read), then folds them with a running
+  // maximum.  The SPLIT threads of a column are combined in LDS at the end.
+  constexpr int SPLIT = NTH / (G * NQ);
+  constexpr int KB = 16;
   const int ocol = tid % (G * NQ), part = tid / (G * NQ);
-  const int cg = ocol / NQ, cq = ocol % NQ;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int p0 = 0; p0 < P; p0 += TP) {
-    const int np = min(TP, P - p0);
-    const int tg = tid / TP, tp = tid % TP;
-    float mv = -INFINITY, lv = 0.f;
-    if (tp < np) {
-      float *ml2 = a.part_ml + (((size_t)b * a.hq + h * G + tg) * a.nparts + p0 + tp) * 2;
-      if (via_cache) {
-        const float2 v2 = *reinterpret_cast<const float2 *>(ml2);
-        mv = v2.x;
-        lv = v2.y;
-      } else {
-        mv = __hip_atomic_load(ml2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        lv = __hip_atomic_load(ml2 + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
+  const int cg = ocol / NQ, d = 4 * (ocol % NQ);
+  const int prow = cg * a.nparts;                    // this head's first partial in the resource
+  const __amdgpu_buffer_rsrc_t r_o = raw_rsrc(a.part_o + row0 * a.nparts * D, G * a.nparts * D * 4);
+  const __amdgpu_buffer_rsrc_t r_ml = raw_rsrc(a.part_ml + row0 * a.nparts * 2, G * a.nparts * 8);
+  float mt = -INFINITY, den = 0.f;
+  v4f acc = {0.f, 0.f, 0.f, 0.f};
+  for (int k0 = part; k0 < P; k0 += SPLIT * KB) {
+    v2f ml[KB];
+    v4f o[KB];
+#pragma unroll
+    for (int u = 0; u < KB; ++u) {
+      const int k = min(k0 + u * SPLIT, P - 1);
+      ml[u] = __builtin_bit_cast(v2f, __builtin_amdgcn_raw_buffer_load_b64(r_ml, (prow + k) * 8, 0, kAgentScope));
+      o[u] = __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(r_o, ((prow + k) * D + d) * 4, 0, kAgentScope));
     }
-    __syncthreads();
-    sh_pm[tid] = mv;
-    __syncthreads();
-    if (tid < G) {   // new running maximum of head tid over this tile
-      float mt = sh_M[tid];
-      for (int k = 0; k < np; ++k) mt = fmaxf(mt, sh_pm[tid * TP + k]);
-      sh_scale[tid] = __builtin_amdgcn_exp2f(sh_M[tid] - mt);
-      sh_M[tid] = mt;
+    float bm = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < KB; ++u) {
+      if (k0 + u * SPLIT >= P) ml[u].x = -INFINITY;  // past the last partition: weight 0
+      bm = fmaxf(bm, ml[u].x);
     }
-    __syncthreads();
-    const float w = tp < np ? __builtin_amdgcn_exp2f(mv - sh_M[tg]) : 0.f;
-    sh_pw[tid] = w;
-    sh_pm[tid] = w * lv;
-    __syncthreads();
-    if (tid < G) {
-      float dsum = 0.f;
-      for (int k = 0; k < np; ++k) dsum += sh_pm[tid * TP + k];
-      sh_den[tid] = sh_den[tid] * sh_scale[tid] + dsum;
+    if (bm > mt) {                                   // bm is finite: partition k0 is real
+      const float sc = __builtin_amdgcn_exp2f(mt - bm);
+      acc *= sc;
+      den *= sc;
+      mt = bm;
     }
-    // output columns: thread (column, part) sums partitions part, part + SPLIT, ...
-    const float sc = sh_scale[cg];
-    acc = make_float4(acc.x * sc, acc.y * sc, acc.z * sc, acc.w * sc);
-    float *po = a.part_o + (((size_t)b * a.hq + h * G + cg) * a.nparts + p0) * D + 4 * cq;
-    if (via_cache) {
-#pragma unroll 8
-      for (int k = part; k < np; k += SPLIT) {
-        const float wk = sh_pw[cg * TP + k];
-        const float4 o4 = *reinterpret_cast<const float4 *>(po + (size_t)k * D);
-        acc.x = fmaf(wk, o4.x, acc.x);
-        acc.y = fmaf(wk, o4.y, acc.y);
-        acc.z = fmaf(wk, o4.z, acc.z);
-        acc.w = fmaf(wk, o4.w, acc.w);
-      }
-    } else {
-#pragma unroll 4
-      for (int k = part; k < np; k += SPLIT) {
-        const float wk = sh_pw[cg * TP + k];
-        float *src = po + (size_t)k * D;
-        acc.x = fmaf(wk, __hip_atomic_load(src + 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), acc.x);
-        acc.y = fmaf(wk, __hip_atomic_load(src + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), acc.y);
-        acc.z = fmaf(wk, __hip_atomic_load(src + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), acc.z);
-        acc.w = fmaf(wk, __hip_atomic_load(src + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), acc.w);
-      }
+#pragma unroll
+    for (int u = 0; u < KB; ++u) {
+      const float w = __builtin_amdgcn_exp2f(ml[u].x - mt);
+      acc += w * o[u];
+      den = fmaf(w, ml[u].y, den);
     }
   }
-  sh_part[tid] = acc;
+  __shared__ float4 sh_part[NTH];
+  __shared__ float sh_pm[NTH], sh_pd[NTH];
+  sh_part[tid] = make_float4(acc.x, acc.y, acc.z, acc.w);
+  sh_pm[tid] = mt;
+  sh_pd[tid] = den;
   __syncthreads();
   if (tid < G * NQ) {
-    float4 r = sh_part[tid];
-    for (int k = 1; k < SPLIT; ++k) {
-      const float4 x = sh_part[tid + k * G * NQ];
-      r.x += x.x;
-      r.y += x.y;
-      r.z += x.z;
-      r.w += x.w;
+    float M = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < SPLIT; ++k) M = fmaxf(M, sh_pm[tid + k * G * NQ]);
+    float4 r = make_float4(0.f, 0.f, 0.f, 0.f);
+    float dn = 0.f;
+#pragma unroll
+    for (int k = 0; k < SPLIT; ++k) {
+      const int src = tid + k * G * NQ;
+      const float sc = __builtin_amdgcn_exp2f(sh_pm[src] - M);   // 0 for a thread with no partitions
+      const float4 x = sh_part[src];
+      r.x = fmaf(sc, x.x, r.x);
+      r.y = fmaf(sc, x.y, r.y);
+      r.z = fmaf(sc, x.z, r.z);
+      r.w = fmaf(sc, x.w, r.w);
+      dn = fmaf(sc, sh_pd[src], dn);
     }
-    const float inv = 1.0f / sh_den[cg];
-    reinterpret_cast<float4 *>(a.out + ((size_t)b * a.hq + h * G + cg) * D)[cq] =
-        make_float4(r.x * inv, r.y * inv, r.z * inv, r.w * inv);
+    const float inv = 1.0f / dn;
+    *reinterpret_cast<float4 *>(a.out + (row0 + cg) * D + d) = make_float4(r.x * inv, r.y * inv, r.z * inv, r.w * inv);
   }
   if (tid == 0)   // ready for the next call
     __hip_atomic_store(a.counters + (size_t)b * a.hkv + h, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

@@ -200,9 +200,9 @@ __global__ __launch_bounds__(64 * kWaves) void g64_decode_kernel(DecodeArgs a) {
   }
   const int wg_begin = p * a.part_tokens * kWaves;
   if (wg_begin >= L) return;
-  const int t_begin = wg_begin + wave * a.part_tokens;
-  const bool active = t_begin < L;
-  const int t_end = min(L, t_begin + a.part_tokens);
+  const WaveRange wr = wave_range(wg_begin, a.part_tokens * kWaves, L, wave);
+  const int t_begin = wr.t_begin, t_end = wr.t_end;
+  const bool active = t_begin < t_end;
   __shared__ float sh_o[kWaves][G][D];
   __shared__ float sh_m[kWaves][G], sh_l[kWaves][G];
   __shared__ uint32_t sh_rng[kWaves][2][kChunk][M];   // this chunk's K and V ranges

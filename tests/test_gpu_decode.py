@@ -122,23 +122,28 @@ def test_decode_vs_unquantized_fp16_reported():
                          ids=["bs16_4x8192", "bs64_1x32768"])
 def test_decode_split_merge_repeatable(cid, over):
     """Many workgroups per (sequence, head): the last one to finish merges the partials of the
-    others.  Thirty calls on one workspace give bit-identical outputs that match the oracle."""
+    others.  Thirty calls on one workspace, alternating two query sets, give bit-identical outputs
+    per query set that match the oracle: a merge that read a partial left by the previous call
+    (the other query set) would not."""
     cfg = dgq_data.get_config(cid, **over)
     lens = dgq_data.seq_lens(cfg, 15)
     heads = _heads_for(cfg, 15, lens)
     table, nblk = dgq_data.block_tables(cfg, 15, lens_total=lens)
     params = H.params_for(cfg)
     cache = H.cache_from_oracle(params, heads, table, nblk, cfg.batch)
-    q16 = dgq_data.queries(cfg, 15)
-    dq, dt = torch.from_numpy(q16).cuda(), torch.from_numpy(table).cuda()
+    qs = [dgq_data.queries(cfg, 15, 0, step) for step in (0, 1)]
+    dqs = [torch.from_numpy(q).cuda() for q in qs]
+    dt = torch.from_numpy(table).cuda()
     dl = torch.from_numpy(lens.astype(np.int32)).cuda()
     ws = Q.workspace(Q.decode_workspace_size(params, cfg.batch, int(lens.max())))
     H.say("decode split merge", cid, over)
-    outs = [Q.paged_decode_attn_int8(params, dq, cache, dt, dl, int(lens.max()), ws=ws).clone() for _ in range(30)]
+    outs = [Q.paged_decode_attn_int8(params, dqs[i % 2], cache, dt, dl, int(lens.max()), ws=ws).clone()
+            for i in range(30)]
     torch.cuda.synchronize()
-    for o in outs[1:]:
-        assert torch.equal(o, outs[0])
-    ref = H.oracle_decode(q16, heads, lens, cfg.hkv, cfg.group)
-    assert H.rel_err_rows(outs[0].cpu().numpy(), ref) <= TOL
+    for i, o in enumerate(outs[2:], start=2):
+        assert torch.equal(o, outs[i % 2]), i
+    for i in (0, 1):
+        ref = H.oracle_decode(qs[i], heads, lens, cfg.hkv, cfg.group)
+        assert H.rel_err_rows(outs[i].cpu().numpy(), ref) <= TOL
     # the merge leaves its completion counters at zero
     assert int(ws[: cfg.batch * cfg.hkv * 4].view(torch.int32).abs().sum().item()) == 0
