@@ -15,6 +15,7 @@
 //                of the decode kernel (values through LDS, since their tiles are channel-major),
 //                and the boundary bits.
 #include <climits>
+#include <type_traits>
 #include <cmath>
 
 #include "dgq_internal.h"
@@ -398,6 +399,344 @@ __global__ __launch_bounds__(256) void select_kernel(CompressArgs a) {
 }
 
 // -------------------------------------------------------------------------------------------
+// 2+3 fused, for sequences of at most kSmallSeq tokens: one workgroup of 512 threads per
+// (sequence, kv head) holds the key moments in LDS, keeps the scores of its 16 candidates per
+// thread in registers, runs the greedy rounds with no memory traffic, and reduces all segments'
+// min/max in one pass over the sub-block extrema (plus the raw tokens of sub-blocks a cut splits).
+// Wave reductions use DPP row operations and lane reads, not LDS permutes.
+// -------------------------------------------------------------------------------------------
+constexpr int kSmallSeq = 8192;
+constexpr int kSmallThreads = 512;
+constexpr int kSmallWaves = kSmallThreads / 64;
+constexpr int kPerThread = kSmallSeq / kSmallThreads;   // 16 candidates per thread
+static_assert(kPerThread == kWin, "one 16-token sub-block per thread");
+
+// LDS slot of token t, t in [-16, kSmallSeq + 16): one pad slot after every 16 tokens, so that
+// thread i reading token 16 i + u (all i of a wave at once) hits distinct banks; the 16 slots on
+// either side of the sequence hold zeros, so window sums need no bounds tests
+__device__ __forceinline__ int skew(int t) { return (t + kWin) + ((t + kWin) >> 4); }
+constexpr int kSkewed = (kSmallSeq + 2 * kWin) + (kSmallSeq + 2 * kWin) / 16;
+
+template <int C>
+__device__ __forceinline__ int dpp_i(int x) {
+  return __builtin_amdgcn_mov_dpp(x, C, 0xF, 0xF, false);
+}
+template <int C>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __int_as_float(dpp_i<C>(__float_as_int(x)));
+}
+template <int C>
+__device__ __forceinline__ double dpp_d(double x) {
+  const long long v = __double_as_longlong(x);
+  const int lo = dpp_i<C>((int)v), hi = dpp_i<C>((int)(v >> 32));
+  return __longlong_as_double((long long)(unsigned)lo | ((long long)hi << 32));
+}
+__device__ __forceinline__ float readlane_f(float x, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
+}
+__device__ __forceinline__ double readlane_d(double x, int l) {
+  const long long v = __double_as_longlong(x);
+  const int lo = __builtin_amdgcn_readlane((int)v, l), hi = __builtin_amdgcn_readlane((int)(v >> 32), l);
+  return __longlong_as_double((long long)(unsigned)lo | ((long long)hi << 32));
+}
+// DPP controls: swap neighbours, swap pairs (within quads), rotate a 16-lane row by 4 and by 8
+constexpr int kQuadSwap1 = 0xB1, kQuadSwap2 = 0x4E, kRowRor4 = 0x124, kRowRor8 = 0x128;
+
+// (score desc, t asc): true if (s2, t2) comes first
+__device__ __forceinline__ bool better(double s2, int t2, double s, int t) {
+  return s2 > s || (s2 == s && t2 < t);
+}
+template <int C>
+__device__ __forceinline__ void best_step(double &s, int &t) {
+  const double s2 = dpp_d<C>(s);
+  const int t2 = dpp_i<C>(t);
+  if (better(s2, t2, s, t)) {
+    s = s2;
+    t = t2;
+  }
+}
+// best over the wave, returned uniform
+__device__ __forceinline__ void wave_best(double &s, int &t) {
+  best_step<kQuadSwap1>(s, t);
+  best_step<kQuadSwap2>(s, t);
+  best_step<kRowRor4>(s, t);
+  best_step<kRowRor8>(s, t);   // every lane holds its row's best
+  double bs = readlane_d(s, 0);
+  int bt = __builtin_amdgcn_readlane(t, 0);
+#pragma unroll
+  for (int r = 1; r < 4; ++r) {
+    const double s2 = readlane_d(s, 16 * r);
+    const int t2 = __builtin_amdgcn_readlane(t, 16 * r);
+    if (better(s2, t2, bs, bt)) {
+      bs = s2;
+      bt = t2;
+    }
+  }
+  s = bs;
+  t = bt;
+}
+// (min, max, min, max) over the wave, returned uniform
+__device__ __forceinline__ float4 wave_minmax(float4 r) {
+  auto step = [&](auto tag) {
+    constexpr int C = decltype(tag)::value;
+    r.x = fminf(r.x, dpp_f<C>(r.x));
+    r.y = fmaxf(r.y, dpp_f<C>(r.y));
+    r.z = fminf(r.z, dpp_f<C>(r.z));
+    r.w = fmaxf(r.w, dpp_f<C>(r.w));
+  };
+  step(std::integral_constant<int, kQuadSwap1>{});
+  step(std::integral_constant<int, kQuadSwap2>{});
+  step(std::integral_constant<int, kRowRor4>{});
+  step(std::integral_constant<int, kRowRor8>{});
+  float4 o = make_float4(readlane_f(r.x, 0), readlane_f(r.y, 0), readlane_f(r.z, 0), readlane_f(r.w, 0));
+#pragma unroll
+  for (int q = 1; q < 4; ++q) {
+    o.x = fminf(o.x, readlane_f(r.x, 16 * q));
+    o.y = fmaxf(o.y, readlane_f(r.y, 16 * q));
+    o.z = fminf(o.z, readlane_f(r.z, 16 * q));
+    o.w = fmaxf(o.w, readlane_f(r.w, 16 * q));
+  }
+  return o;
+}
+
+template <int D>
+__global__ __launch_bounds__(kSmallThreads) void select_small_kernel(CompressArgs a) {
+  constexpr int NW = kSmallWaves;
+  constexpr int MS = kMaxCuts + 1;   // segments
+  const int h = blockIdx.x, b = blockIdx.y;
+  int c0, L;
+  bool bad_seq;
+  seq_range(a.cu, b, a.max_seq_len, a.total, c0, L, bad_seq);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const size_t bh = (size_t)b * a.hkv + h;
+  __shared__ int sa[kSkewed];
+  __shared__ double sbd[kSkewed];   // key moments b_t (< 2^36, exact in double)
+  __shared__ float4 sext[kSmallSeq / kWin];
+  __shared__ double gbs[2 * NW];   // wave bests (score, t) of a round, double-buffered
+  __shared__ int gbt[2 * NW];
+  __shared__ float4 sred[NW][MS];
+  __shared__ int scut[kMaxCuts];
+  __shared__ int sstart[MS + 1];
+  __shared__ long long sring_b[kWin];
+  if (tid == 0 && bad_seq && h == 0) atomicAdd(a.cache.status + 2, 1ull);
+
+  // ---- key moments and sub-block extrema of the sequence into LDS (all loads issued at once) ----
+  const size_t mrow = (size_t)h * a.total + c0;
+  {
+    int ra[kPerThread];
+    long long rb[kPerThread];
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i) {
+      const int t = tid + kSmallThreads * i;
+      ra[i] = t < L ? a.ws_a[mrow + t] : 0;
+      rb[i] = t < L ? a.ws_b[mrow + t] : 0;
+    }
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i) {
+      const int t = tid + kSmallThreads * i;
+      sa[skew(t)] = ra[i];
+      sbd[skew(t)] = (double)rb[i];
+      if (t < L && t >= L - kWin) sring_b[t - (L - kWin)] = rb[i];   // kept for the append state
+    }
+  }
+  if (tid < 2 * kWin) {   // the zero pads
+    const int t = tid < kWin ? tid - kWin : kSmallSeq + tid - kWin;
+    sa[skew(t)] = 0;
+    sbd[skew(t)] = 0.0;
+  }
+  const int nsub = (L + kWin - 1) / kWin;
+  if (tid < nsub) sext[tid] = a.ws_ext[bh * a.nsub + tid];
+  __syncthreads();
+
+  // ---- scores of this thread's candidates t = 16 * tid + i (window sums slide over LDS) ----
+  // Q = N * sum b - (sum a)^2 is exact in double: |sum a| <= 2^25, N * sum b <= 2^51, N = 2^k.
+  const int tb = kPerThread * tid;
+  double sc[kPerThread];
+  {
+    const double nel = (double)(kWin * D);
+    int A = 0;
+    double Bm = 0.0;
+    const int s0 = tb - kWin;
+#pragma unroll
+    for (int u = 0; u < kWin; ++u) {
+      A += sa[skew(s0 + u)];
+      Bm += sbd[skew(s0 + u)];
+    }
+    double q[2 * kWin];
+#pragma unroll
+    for (int k = 0; k < 2 * kWin; ++k) {
+      const double Ad = (double)A;
+      q[k] = fma(-Ad, Ad, nel * Bm);
+      if (k + 1 < 2 * kWin) {
+        A += sa[skew(s0 + k + kWin)] - sa[skew(s0 + k)];
+        Bm += sbd[skew(s0 + k + kWin)] - sbd[skew(s0 + k)];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i) {
+      const int t = tb + i;
+      sc[i] = -INFINITY;
+      if (t >= kWin && t <= L - kWin) {
+        const double ql = q[i], qr = q[i + kWin];
+        sc[i] = (fmax(ql, qr) + 1.0) / (fmin(ql, qr) + 1.0);
+      }
+    }
+  }
+
+  // ---- greedy selection: every thread keeps its 16 scores in registers; per round one wave
+  // reduction (DPP), one exchange of the 8 wave bests through LDS, and the suppression of the
+  // taken cut's neighbours in registers ----
+  int nc = 0;
+  if (L >= 2 * kWin) {
+    for (int r = 0; r < a.max_segments - 1; ++r) {
+      double s = -INFINITY;
+      int t = INT_MAX;
+#pragma unroll
+      for (int i = 0; i < kPerThread; ++i)
+        if (sc[i] > s) {   // ascending t: the first maximum is the smallest t
+          s = sc[i];
+          t = tb + i;
+        }
+      wave_best(s, t);
+      const int buf = r & 1;
+      if (lane == 0) {
+        gbs[NW * buf + wave] = s;
+        gbt[NW * buf + wave] = t;
+      }
+      __syncthreads();
+      s = gbs[NW * buf];
+      t = gbt[NW * buf];
+#pragma unroll
+      for (int w = 1; w < NW; ++w)
+        if (better(gbs[NW * buf + w], gbt[NW * buf + w], s, t)) {
+          s = gbs[NW * buf + w];
+          t = gbt[NW * buf + w];
+        }
+      if (s == -INFINITY) break;
+      if (r > 0 && !(s >= a.tau)) break;
+      if (tid == 0) scut[nc] = t;
+      ++nc;
+#pragma unroll
+      for (int i = 0; i < kPerThread; ++i)
+        if (abs(tb + i - t) <= kWin - 1) sc[i] = -INFINITY;
+    }
+  }
+  const int nseg = L > 0 ? nc + 1 : 0;
+  // starts = [0] + sorted cuts, then L
+  if (tid == 0) {
+    sstart[0] = 0;
+    for (int i = 0; i < nc; ++i) {
+      const int x = scut[i];
+      int k = i;
+      while (k > 0 && sstart[k] > x) {
+        sstart[k + 1] = sstart[k];
+        --k;
+      }
+      sstart[k + 1] = x;
+    }
+    sstart[max(nseg, 1)] = L;
+  }
+  __syncthreads();
+  const int *starts = sstart;
+
+  // ---- all segments' K/V min/max ----
+  // (1) whole sub-blocks: thread tid holds sub-block tid; for each segment j (a rolled loop) the
+  //     waves reduce the extrema of the sub-blocks that lie inside j.
+  // (2) a sub-block that a cut splits (cuts are >= 16 apart, so one cut per sub-block; a cut at a
+  //     multiple of 16 splits none) is re-read raw by one wave per cut: wave c - 1 takes cut c and
+  //     reduces the parts left and right of it.
+  const float4 ident = make_float4(INFINITY, -INFINITY, INFINITY, -INFINITY);
+  auto fold = [&](float4 &r, const float4 x) {
+    r.x = fminf(r.x, x.x);
+    r.y = fmaxf(r.y, x.y);
+    r.z = fminf(r.z, x.z);
+    r.w = fmaxf(r.w, x.w);
+  };
+  int my_seg = -1;   // segment holding all of sub-block tid, or -1
+  if (tid < nsub) {
+    const int t0 = kWin * tid, t1 = min(t0 + kWin, L) - 1;
+    int j0 = 0, j1 = 0;
+    for (int k = 1; k < nseg; ++k) {
+      j0 += t0 >= starts[k] ? 1 : 0;
+      j1 += t1 >= starts[k] ? 1 : 0;
+    }
+    if (j0 == j1) my_seg = j0;
+  }
+  const float4 my_ext = my_seg >= 0 ? sext[tid] : ident;
+#pragma unroll 1
+  for (int j = 0; j < nseg; ++j) {
+    const float4 r = wave_minmax(my_seg == j ? my_ext : ident);
+    if (lane == 0) sred[wave][j] = r;
+  }
+  __shared__ float4 sraw[kMaxCuts][2];   // cut c: (left part, right part)
+  if (wave + 1 < nseg) {
+    const int cut = starts[wave + 1];
+    float4 left = ident, right = ident;
+    if (cut % kWin != 0) {
+      const int t0 = cut - cut % kWin;
+      constexpr int PER_LANE = kWin * D / 64;   // halves of the sub-block per lane
+#pragma unroll
+      for (int e0 = 0; e0 < PER_LANE; e0 += 8) {
+        const int x = lane * PER_LANE + e0;
+        const int tok = t0 + x / D, d = x % D;
+        if (tok < L) {
+          const size_t off = (size_t)(c0 + tok) * a.stride_tok + (size_t)h * a.stride_head + d;
+          const uint4 kw = *reinterpret_cast<const uint4 *>(a.k + off);
+          const uint4 vw = *reinterpret_cast<const uint4 *>(a.v + off);
+          const uint32_t kk[4] = {kw.x, kw.y, kw.z, kw.w}, vv[4] = {vw.x, vw.y, vw.z, vw.w};
+          float4 r = ident;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float k0 = half_bits_to_float(kk[e] & 0xFFFFu), k1 = half_bits_to_float(kk[e] >> 16);
+            const float v0 = half_bits_to_float(vv[e] & 0xFFFFu), v1 = half_bits_to_float(vv[e] >> 16);
+            fold(r, make_float4(fminf(k0, k1), fmaxf(k0, k1), fminf(v0, v1), fmaxf(v0, v1)));
+          }
+          fold(tok < cut ? left : right, r);
+        }
+      }
+    }
+    left = wave_minmax(left);
+    right = wave_minmax(right);
+    if (lane == 0) {
+      sraw[wave][0] = left;
+      sraw[wave][1] = right;
+    }
+  }
+  __syncthreads();
+  if (tid < nseg) {
+    float4 r = sred[0][tid];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) fold(r, sred[w][tid]);
+    if (tid > 0) fold(r, sraw[tid - 1][1]);        // right of the cut that starts segment tid
+    if (tid + 1 < nseg) fold(r, sraw[tid][0]);      // left of the cut that ends it
+    dgq_seg_t row;
+    row.start = starts[tid];
+    row.kmin = r.x + 0.0f;
+    row.kmax = r.y + 0.0f;
+    row.vmin = r.z + 0.0f;
+    row.vmax = r.w + 0.0f;
+    row.kscale = dgq_scale(row.kmin, row.kmax);
+    row.vscale = dgq_scale(row.vmin, row.vmax);
+    row.reserved = 0;
+    a.cache.segs[bh * a.seg_cap + tid] = row;
+  }
+  // append state: open span starts at L, ring = the last min(16, L) tokens' moments
+  const int rl = min(kWin, L);
+  dgq_tail_t *tl = a.cache.tail + bh;
+  if (tid < kWin) {
+    tl->ring_a[tid] = tid < rl ? sa[skew(L - rl + tid)] : 0;
+    tl->ring_b[tid] = tid < rl ? sring_b[kWin - rl + tid] : 0;
+  }
+  if (tid == 0) {
+    a.cache.nseg[bh] = nseg;
+    tl->r0 = L;
+    tl->ring_len = rl;
+    tl->span_own = 0;
+    tl->reserved = 0;
+  }
+}
+
+// -------------------------------------------------------------------------------------------
 // 4. encode
 // -------------------------------------------------------------------------------------------
 template <int D, int BS>
@@ -569,15 +908,19 @@ static dgq_status_t launch_all(const CompressArgs &a, int bs, int max_seq_len, h
   dim3 g64((max_seq_len + 63) / 64, hkv, batch);
   dim3 g256((max_seq_len + 255) / 256, hkv, batch);
   dgq_status_t st;
+  const bool small = max_seq_len <= kSmallSeq && a.max_segments <= kMaxCuts + 1;
   if (max_seq_len > 0) {
     hipLaunchKernelGGL(stats_kernel<D>, g64, dim3(256), 0, s, a);
     st = check_launch("dgq_compress stats kernel");
     if (st != DGQ_OK) return st;
-    hipLaunchKernelGGL(scores_kernel<D>, g256, dim3(256), 0, s, a);
-    st = check_launch("dgq_compress scores kernel");
-    if (st != DGQ_OK) return st;
+    if (!small) {
+      hipLaunchKernelGGL(scores_kernel<D>, g256, dim3(256), 0, s, a);
+      st = check_launch("dgq_compress scores kernel");
+      if (st != DGQ_OK) return st;
+    }
   }
-  hipLaunchKernelGGL(select_kernel<D>, dim3(hkv, batch), dim3(256), 0, s, a);
+  if (small) hipLaunchKernelGGL(select_small_kernel<D>, dim3(hkv, batch), dim3(kSmallThreads), 0, s, a);
+  else hipLaunchKernelGGL(select_kernel<D>, dim3(hkv, batch), dim3(256), 0, s, a);
   st = check_launch("dgq_compress select kernel");
   if (st != DGQ_OK) return st;
   if (max_seq_len == 0) return DGQ_OK;

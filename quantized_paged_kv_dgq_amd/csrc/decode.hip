@@ -24,6 +24,7 @@
 //  * Loads are software-pipelined: the next chunk's keys are requested as soon as the QK product
 //    has consumed the key registers, its values as soon as the PV product has consumed the value
 //    registers; the partition's block ids are read once, one per lane.
+#include <algorithm>
 #include <climits>
 #include <cmath>
 
@@ -46,11 +47,11 @@ __global__ __launch_bounds__(64 * kWaves) void decode_partition_kernel(DecodeArg
   const int wg_begin = p * span;
 
   // Loads that do not depend on the sequence length go out together with it: the block ids of
-  // the workgroup's span (one per thread, inside the table row; the span holds at most one block
-  // per thread), the segment-table row of this lane and the query slice of this lane.
+  // the workgroup's span, the segment-table row of this lane and the query slice of this lane.
   const int32_t *bt = a.block_table + (size_t)b * a.max_blocks;
   const int wblk0 = wg_begin / BS;
-  const int wblk_raw = wblk0 + (int)threadIdx.x < a.max_blocks ? bt[wblk0 + threadIdx.x] : 0;
+  SpanBlocks<BS> span_blk;
+  span_blk.load(bt, a.max_blocks, wblk0);
   const int ns_raw = a.nseg[bh];
   dgq_seg_t seg_raw = {};
   if (lane < a.seg_cap) seg_raw = a.segs[(size_t)bh * a.seg_cap + lane];
@@ -71,12 +72,12 @@ __global__ __launch_bounds__(64 * kWaves) void decode_partition_kernel(DecodeArg
     for (int e = threadIdx.x; e < G * D; e += 64 * kWaves) a.out[((size_t)b * a.hq + h * G) * D + e] = 0.f;
     return;
   }
-  if (wg_begin >= L) return;                       // the whole workgroup has nothing to do
+  if (p >= parts_of(L, span)) return;              // the whole workgroup has nothing to do
   const WaveRange wr = wave_range(wg_begin, span, L, wave);
   const int t_begin = wr.t_begin, t_end = wr.t_end;
   const bool active = t_begin < t_end;
-  __shared__ int sh_blk[64 * kWaves];
-  sh_blk[threadIdx.x] = wblk_raw;
+  __shared__ int sh_blk[SpanBlocks<BS>::kBlocks];
+  span_blk.publish(wblk0, (L + BS - 1) / BS, a.num_blocks, sh_blk, a.status);
   __syncthreads();
   __shared__ float sh_o[kWaves][G][D];
   __shared__ float sh_m[kWaves][G], sh_l[kWaves][G];
@@ -150,15 +151,8 @@ __global__ __launch_bounds__(64 * kWaves) void decode_partition_kernel(DecodeArg
     const float wq = live ? ldexpf(a.sm_log2, 16 - 8 * piece - qexp) : 0.f;
     const float qsum_s = qsum * a.sm_log2;
 
-    // ---- block ids of the wave's run: lane i holds its i-th block (<= 64 blocks) ----
-    const int blk0 = t_begin / BS;
-    const int nblk_part = (t_end - 1) / BS - blk0 + 1;
-    int my_blk = 0;
-    {
-      bool bad = false;
-      if (lane < nblk_part) my_blk = checked_block(sh_blk[blk0 - wblk0 + lane], a.num_blocks, bad);
-      if (__ballot(bad) != 0ull && lane == 0) atomicAdd(a.status + 2, 1ull);
-    }
+    // block ids come from sh_blk: chunk c of the wave is local chunk lc0 + c of the workgroup
+    const int lc0 = (t_begin - wg_begin) / kChunk;
     const size_t tile_bytes = (size_t)BS * D;
     const int8_t *kpool = a.k_pool + (size_t)h * tile_bytes;
     const int8_t *vpool = a.v_pool + (size_t)h * tile_bytes;
@@ -168,7 +162,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_partition_kernel(DecodeArg
     // (64 channels) per A operand; values: channel tile n (16 channels) x 64 tokens per A operand.
     auto load_k = [&](int c, v4i (&kf)[4][M]) {
       if constexpr (BS == 64) {
-        const int blk = __builtin_amdgcn_readlane(my_blk, c);
+        const int blk = __builtin_amdgcn_readfirstlane(sh_blk[lc0 + c]);
         const int8_t *kb = kpool + (size_t)blk * blk_stride;
 #pragma unroll
         for (int T = 0; T < 4; ++T)
@@ -176,8 +170,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_partition_kernel(DecodeArg
           for (int m = 0; m < M; ++m)
             kf[T][m] = *reinterpret_cast<const v4i *>(kb + (((T * M + m) * 64) + lane) * 16);
       } else {
-        const int bi = min(4 * c + ((lane & 15) >> 2), nblk_part - 1);
-        const int8_t *kb = kpool + (size_t)__shfl(my_blk, bi) * blk_stride;
+        const int8_t *kb = kpool + (size_t)sh_blk[4 * (lc0 + c) + ((lane & 15) >> 2)] * blk_stride;
 #pragma unroll
         for (int T = 0; T < 4; ++T)
 #pragma unroll
@@ -187,13 +180,12 @@ __global__ __launch_bounds__(64 * kWaves) void decode_partition_kernel(DecodeArg
     };
     auto load_v = [&](int c, v4i (&vf)[NT]) {
       if constexpr (BS == 64) {
-        const int blk = __builtin_amdgcn_readlane(my_blk, c);
+        const int blk = __builtin_amdgcn_readfirstlane(sh_blk[lc0 + c]);
         const int8_t *vb = vpool + (size_t)blk * blk_stride;
 #pragma unroll
         for (int n = 0; n < NT; ++n) vf[n] = *reinterpret_cast<const v4i *>(vb + (n * 64 + lane) * 16);
       } else {
-        const int bi = min(4 * c + j, nblk_part - 1);
-        const int8_t *vb = vpool + (size_t)__shfl(my_blk, bi) * blk_stride;
+        const int8_t *vb = vpool + (size_t)sh_blk[4 * (lc0 + c) + j] * blk_stride;
 #pragma unroll
         for (int n = 0; n < NT; ++n) vf[n] = *reinterpret_cast<const v4i *>(vb + (16 * n + (lane & 15)) * 16);
       }
@@ -352,23 +344,26 @@ __global__ __launch_bounds__(64 * kWaves) void decode_partition_kernel(DecodeArg
   finish_partition<D, G>(a, b, h, p, L, sh_o, sh_m, sh_l);
 }
 
-DecodePlan decode_plan(const dgq_params_t *p, int32_t batch, int32_t max_seq_len) {
-  // Each workgroup takes kWaves * per consecutive 64-token chunks of one (sequence, kv head) and
-  // writes one partial; its waves split them evenly.  Aim at about one workgroup per compute unit
-  // (1024 waves): fewer, longer workgroups leave fewer partials to merge, and one wave per SIMD
-  // already keeps enough loads in flight.  A wave's run spans at most 64 blocks (one block id per
-  // lane), so per <= block_size.
+DecodePlan decode_plan(const dgq_params_t *p, int32_t batch, int32_t max_seq_len, int64_t target_waves) {
+  // Each workgroup takes up to kWaves * per consecutive 64-token chunks of one (sequence, kv
+  // head) and writes one partial; its waves split them evenly.  Aim at target_waves in all (1024 =
+  // one workgroup per compute unit for the DGQ decode: fewer, longer workgroups leave fewer
+  // partials to merge, and one wave per SIMD already keeps enough loads in flight).  Then even out
+  // the partitions of the longest sequence, so that no workgroup is left with a small remainder.
   DecodePlan plan;
-  const int64_t chunks_seq = (max_seq_len + kChunk - 1) / kChunk;
+  // a partial last chunk rides along with the last partition (parts_of), so count full chunks
+  const int64_t chunks_seq = std::max<int64_t>(max_seq_len / kChunk, 1);
   const int64_t total = (int64_t)batch * p->num_kv_heads * chunks_seq;
-  const int64_t target = 1024;
+  const int64_t target = target_waves;
   int64_t per = total > 0 ? (total + target - 1) / target : 1;
   if (per < 1) per = 1;
-  if (per > p->block_size) per = p->block_size;
+  if (per > kMaxRun) per = kMaxRun;
+  int64_t nparts = (chunks_seq + per * kWaves - 1) / (per * kWaves);
+  if (nparts < 1) nparts = 1;
+  per = (chunks_seq + nparts * kWaves - 1) / (nparts * kWaves);
+  if (per < 1) per = 1;
   plan.part_tokens = (int)(per * kChunk);
-  const int64_t span = (int64_t)plan.part_tokens * kWaves;
-  plan.nparts = (int)((max_seq_len + span - 1) / span);
-  if (plan.nparts < 1) plan.nparts = 1;
+  plan.nparts = (int)nparts;
   return plan;
 }
 
@@ -395,8 +390,8 @@ DecodeArgs make_decode_args(const dgq_params_t *p, const uint16_t *q, const int8
                             const int8_t *v_pool, int32_t num_blocks, unsigned long long *status,
                             const int32_t *block_table, int32_t max_blocks, const int32_t *seq_lens,
                             int32_t batch, int32_t max_seq_len, float softmax_scale, float *out,
-                            void *ws) {
-  const DecodePlan plan = decode_plan(p, batch, max_seq_len);
+                            void *ws, int64_t target_waves) {
+  const DecodePlan plan = decode_plan(p, batch, max_seq_len, target_waves);
   DecodeArgs a = {};
   a.q = q;
   a.k_pool = k_pool;
@@ -426,7 +421,8 @@ dgq_status_t launch_decode(const dgq_params_t *p, const uint16_t *q, const dgq_c
                            const int32_t *seq_lens, int32_t batch, int32_t max_seq_len,
                            float softmax_scale, float *out, void *ws, hipStream_t stream) {
   DecodeArgs a = make_decode_args(p, q, cache->k_pool, cache->v_pool, cache->num_blocks, cache->status,
-                                  block_table, max_blocks, seq_lens, batch, max_seq_len, softmax_scale, out, ws);
+                                  block_table, max_blocks, seq_lens, batch, max_seq_len, softmax_scale, out, ws,
+                                  kDgqDecodeWaves);
   a.segs = cache->segs;
   a.nseg = cache->nseg;
   const int D = p->head_dim, G = p->num_q_heads / p->num_kv_heads;
@@ -436,8 +432,10 @@ dgq_status_t launch_decode(const dgq_params_t *p, const uint16_t *q, const dgq_c
 }
 
 size_t decode_workspace_bytes(const dgq_params_t *p, int32_t batch, int32_t max_seq_len) {
-  const DecodePlan plan = decode_plan(p, batch, max_seq_len);
-  const size_t rows = (size_t)batch * p->num_q_heads * plan.nparts;
+  // one size for both decoders: the larger partial count of their two plans
+  const int32_t nparts = std::max(decode_plan(p, batch, max_seq_len, kDgqDecodeWaves).nparts,
+                                  decode_plan(p, batch, max_seq_len, kG64DecodeWaves).nparts);
+  const size_t rows = (size_t)batch * p->num_q_heads * nparts;
   return align_up((size_t)batch * p->num_kv_heads * sizeof(unsigned), 256) +
          (align_up(rows * 2, 64) + rows * p->head_dim) * sizeof(float) + 256;
 }

@@ -14,6 +14,7 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v2i_t __attribute__((ext_vector_type(2)));
 
 constexpr int kWaves = 4;   // waves per decode workgroup
+constexpr int kMaxRun = 64; // 64-token chunks per wave at most (a workgroup spans <= 16384 tokens)
 
 struct DecodeArgs {
   const uint16_t *q;
@@ -78,20 +79,59 @@ DecodeArgs make_decode_args(const dgq_params_t *p, const uint16_t *q, const int8
                             const int8_t *v_pool, int32_t num_blocks, unsigned long long *status,
                             const int32_t *block_table, int32_t max_blocks, const int32_t *seq_lens,
                             int32_t batch, int32_t max_seq_len, float softmax_scale, float *out,
-                            void *ws);
+                            void *ws, int64_t target_waves);
 
-// Token range [t_begin, t_end) of one wave: the workgroup's tokens [wg_begin, min(L, wg_begin +
-// span)) are dealt to the kWaves waves as nearly equal runs of whole 64-token chunks, so a short
-// sequence or a sequence's last partition still keeps every wave busy.
+// Workgroups (partitions) of a sequence of L tokens with `span` tokens each: a partial 64-token
+// chunk at the end joins the last partition instead of opening one of its own.
+__host__ __device__ __forceinline__ int parts_of(int L, int span) {
+  const int full = (L / kChunk) * kChunk;
+  const int P = (full + span - 1) / span;
+  return P > 1 ? P : 1;
+}
+
+// Token range [t_begin, t_end) of one wave: the workgroup's tokens [wg_begin, wg_end) (wg_end =
+// wg_begin + span, or L for the last partition) are dealt to the kWaves waves as nearly equal runs
+// of whole 64-token chunks, so a short sequence or a sequence's last partition still keeps every
+// wave busy.
 struct WaveRange {
   int t_begin, t_end;
 };
 __device__ __forceinline__ WaveRange wave_range(int wg_begin, int span, int L, int wave) {
-  const int wg_end = min(L, wg_begin + span);
+  const int wg_end = wg_begin / span + 1 == parts_of(L, span) ? L : min(L, wg_begin + span);
   const int nch = (wg_end - wg_begin + kChunk - 1) / kChunk;
   const int c0 = wave * nch / kWaves, c1 = (wave + 1) * nch / kWaves;
   return {wg_begin + c0 * kChunk, min(wg_end, wg_begin + c1 * kChunk)};
 }
+
+// The block ids of a workgroup's span, kept in LDS: read from the table before the sequence
+// length is known (NB per thread, coalesced), then published once it is: the sequence's blocks
+// validated (a bad id is counted and replaced by 0), slots past its last block set to 0, a valid
+// block that is only ever read for masked tokens of a partial last chunk.
+template <int BS>
+struct SpanBlocks {
+  // a span of kWaves * kMaxRun chunks plus the partial chunk a last partition may absorb
+  static constexpr int kBlocks = (kWaves * kMaxRun + 1) * kChunk / BS;
+  static constexpr int NB = (kBlocks + 64 * kWaves - 1) / (64 * kWaves);
+  int raw[NB];
+
+  __device__ __forceinline__ void load(const int32_t *bt, int max_blocks, int wblk0) {
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int slot = (int)threadIdx.x + 64 * kWaves * i;
+      raw[i] = slot < kBlocks && wblk0 + slot < max_blocks ? bt[wblk0 + slot] : 0;
+    }
+  }
+  __device__ __forceinline__ void publish(int wblk0, int nblk_seq, int num_blocks, int *sh_blk,
+                                          unsigned long long *status) const {
+    bool bad = false;
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int slot = (int)threadIdx.x + 64 * kWaves * i;
+      if (slot < kBlocks) sh_blk[slot] = wblk0 + slot < nblk_seq ? checked_block(raw[i], num_blocks, bad) : 0;
+    }
+    if (__ballot(bad) != 0ull && (threadIdx.x & 63) == 0) atomicAdd(status + 2, 1ull);
+  }
+};
 
 // Buffer resource over `bytes` bytes at `base` (raw, untyped, 32-bit data format): loads past the
 // end return zero, stores past the end are dropped.
@@ -117,7 +157,7 @@ __device__ __forceinline__ void finish_partition(const DecodeArgs &a, int b, int
   static_assert(G * NQ <= NTH, "one float4 column per thread");
   __syncthreads();
   const int tid = threadIdx.x;
-  const int P = (L + a.part_tokens * kWaves - 1) / (a.part_tokens * kWaves);   // workgroups of (b, h)
+  const int P = parts_of(L, a.part_tokens * kWaves);   // workgroups of (b, h)
   const size_t row0 = (size_t)b * a.hq + h * G;      // first query head row of this kv head
   if (tid < G * NQ) {
     const int gg = tid / NQ, d = 4 * (tid % NQ);

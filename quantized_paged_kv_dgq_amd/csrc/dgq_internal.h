@@ -31,7 +31,11 @@ struct DecodePlan {
   int part_tokens;  // tokens per workgroup, multiple of kChunk
   int nparts;       // partitions per sequence at max_seq_len
 };
-DecodePlan decode_plan(const dgq_params_t *p, int32_t batch, int32_t max_seq_len);
+// Waves a decode launch aims at: the DGQ decode runs one 4-wave workgroup per CU; the group-64
+// baseline does more work per chunk and wants two.
+constexpr int64_t kDgqDecodeWaves = 1024;
+constexpr int64_t kG64DecodeWaves = 2048;
+DecodePlan decode_plan(const dgq_params_t *p, int32_t batch, int32_t max_seq_len, int64_t target_waves);
 size_t decode_workspace_bytes(const dgq_params_t *p, int32_t batch, int32_t max_seq_len);
 
 dgq_status_t launch_decode(const dgq_params_t *p, const uint16_t *q, const dgq_cache_t *cache,

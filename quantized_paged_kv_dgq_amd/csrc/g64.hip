@@ -199,10 +199,18 @@ __global__ __launch_bounds__(64 * kWaves) void g64_decode_kernel(DecodeArgs a) {
     return;
   }
   const int wg_begin = p * a.part_tokens * kWaves;
-  if (wg_begin >= L) return;
+  if (p >= parts_of(L, a.part_tokens * kWaves)) return;
   const WaveRange wr = wave_range(wg_begin, a.part_tokens * kWaves, L, wave);
   const int t_begin = wr.t_begin, t_end = wr.t_end;
   const bool active = t_begin < t_end;
+  const int wblk0 = wg_begin / BS;
+  __shared__ int sh_blk[SpanBlocks<BS>::kBlocks];
+  {
+    SpanBlocks<BS> span_blk;
+    span_blk.load(a.block_table + (size_t)b * a.max_blocks, a.max_blocks, wblk0);
+    span_blk.publish(wblk0, (L + BS - 1) / BS, a.num_blocks, sh_blk, a.status);
+  }
+  __syncthreads();
   __shared__ float sh_o[kWaves][G][D];
   __shared__ float sh_m[kWaves][G], sh_l[kWaves][G];
   __shared__ uint32_t sh_rng[kWaves][2][kChunk][M];   // this chunk's K and V ranges
@@ -262,15 +270,8 @@ __global__ __launch_bounds__(64 * kWaves) void g64_decode_kernel(DecodeArgs a) {
     const float wq = live ? ldexpf(a.sm_log2, 16 - 8 * piece - qexp) : 0.f;
     const float wpiece = live ? ldexpf(1.0f, -6 - 8 * piece) : 0.f;   // 2^(16 - 8 piece) / 2^22
 
-    const int32_t *bt = a.block_table + (size_t)b * a.max_blocks;
-    const int blk0 = t_begin / BS;
-    const int nblk_part = (t_end - 1) / BS - blk0 + 1;
-    int my_blk = 0;
-    {
-      bool bad = false;
-      if (lane < nblk_part) my_blk = checked_block(bt[blk0 + lane], a.num_blocks, bad);
-      if (__ballot(bad) != 0ull && lane == 0) atomicAdd(a.status + 2, 1ull);
-    }
+    // block ids come from sh_blk: chunk c of the wave is local chunk lc0 + c of the workgroup
+    const int lc0 = (t_begin - wg_begin) / kChunk;
     const size_t tile_bytes = (size_t)BS * D;
     const size_t blk_stride = (size_t)a.hkv * tile_bytes;
     const int8_t *kpool = a.k_pool + (size_t)h * tile_bytes;
@@ -282,9 +283,7 @@ __global__ __launch_bounds__(64 * kWaves) void g64_decode_kernel(DecodeArgs a) {
       v4i kf[4][M], vf[NT];
       // ranges of the chunk: lane = token of the chunk
       {
-        int blk_l;
-        if constexpr (BS == 64) blk_l = __builtin_amdgcn_readlane(my_blk, c);
-        else blk_l = __shfl(my_blk, min(4 * c + (lane >> 4), nblk_part - 1));
+        const int blk_l = BS == 64 ? sh_blk[lc0 + c] : sh_blk[4 * (lc0 + c) + (lane >> 4)];
         const size_t ridx = (((size_t)blk_l * a.hkv + h) * BS + (t0 + lane) % BS) * M;
 #pragma unroll
         for (int m = 0; m < M; ++m) {
@@ -293,7 +292,7 @@ __global__ __launch_bounds__(64 * kWaves) void g64_decode_kernel(DecodeArgs a) {
         }
       }
       if constexpr (BS == 64) {
-        const int blk = __builtin_amdgcn_readlane(my_blk, c);
+        const int blk = __builtin_amdgcn_readfirstlane(sh_blk[lc0 + c]);
         const int8_t *kb = kpool + (size_t)blk * blk_stride;
         const int8_t *vb = vpool + (size_t)blk * blk_stride;
 #pragma unroll
@@ -303,9 +302,8 @@ __global__ __launch_bounds__(64 * kWaves) void g64_decode_kernel(DecodeArgs a) {
 #pragma unroll
         for (int n = 0; n < NT; ++n) vf[n] = *reinterpret_cast<const v4i *>(vb + (n * 64 + lane) * 16);
       } else {
-        const int bk = min(4 * c + ((lane & 15) >> 2), nblk_part - 1), bv = min(4 * c + j, nblk_part - 1);
-        const int8_t *kb = kpool + (size_t)__shfl(my_blk, bk) * blk_stride;
-        const int8_t *vb = vpool + (size_t)__shfl(my_blk, bv) * blk_stride;
+        const int8_t *kb = kpool + (size_t)sh_blk[4 * (lc0 + c) + ((lane & 15) >> 2)] * blk_stride;
+        const int8_t *vb = vpool + (size_t)sh_blk[4 * (lc0 + c) + j] * blk_stride;
 #pragma unroll
         for (int T = 0; T < 4; ++T)
 #pragma unroll
@@ -481,7 +479,8 @@ dgq_status_t launch_g64_decode(const dgq_params_t *p, const uint16_t *q, const d
                                int32_t batch, int32_t max_seq_len, float softmax_scale, float *out,
                                void *ws, hipStream_t stream) {
   DecodeArgs a = make_decode_args(p, q, cache->k_pool, cache->v_pool, cache->num_blocks, cache->status,
-                                  block_table, max_blocks, seq_lens, batch, max_seq_len, softmax_scale, out, ws);
+                                  block_table, max_blocks, seq_lens, batch, max_seq_len, softmax_scale, out, ws,
+                                  kG64DecodeWaves);
   a.k_range = cache->k_range;
   a.v_range = cache->v_range;
   const int G = p->num_q_heads / p->num_kv_heads;
