@@ -17,6 +17,10 @@ the same data (quantize the batch + the appended token, decode over 8193 tokens;
 rotate), and both decoders' outputs are compared with float32 attention over the unquantized
 fp16 keys/values ("group64_baseline", "quality_vs_fp16").
 
+Finally the 128K long-context workload (32 layers of one 131,072-token sequence, each layer
+compressed into its own cache, decode looped over the layers) is timed per layer
+("long_context_128k").
+
 Prints one JSON line.  ``value`` is the decode attention's throughput in GB/s of algorithmic
 bytes (INT8 K/V codes + block table + segment tables + q + out), from HIP events recorded around
 every decode call on the stream the kernels run on.
@@ -48,6 +52,8 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=20.0,
                     help="time budget of the CPU oracle baseline (0 to skip)")
+    ap.add_argument("--no-long-context", action="store_true",
+                    help="skip the 32-layer 128K long-context decode/compress figures")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 512 MiB device copy (torch) a few times: the reference "
                          "kernel of known size for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE")
@@ -162,6 +168,62 @@ def quality_vs_fp16(cfg, k, v, cu, k_tok, v_tok, q, out_dgq, out_g64):
     return {"dgq_max_rel_err": round(e1[0], 6), "dgq_mean_rel_err": round(e1[1], 6),
             "group64_max_rel_err": round(e2[0], 6), "group64_mean_rel_err": round(e2[1], 6),
             "rows": B * hq, "reference": "float32 attention over the unquantized fp16 K/V"}
+
+
+def long_context(seed, dev, Q):
+    """The 128K long-context workload: 32 layers of one 131,072-token sequence (8 KV / 32 query
+    heads, head_dim 128, 64-token blocks, 1% outliers at 8 sigma), each layer compressed into its
+    own cache, then one decode query per layer, looped over the layers.  8 GiB of codes in all, so
+    every layer's decode reads HBM.  Per-layer medians of HIP-event times."""
+    import torch
+
+    import dgq_data
+
+    cfg = dgq_data.get_config(3)
+    L, hkv, hq, d, bs = cfg.seq_len, cfg.hkv, cfg.hq, cfg.head_dim, cfg.block_size
+    params = Q.DGQParams(hkv, hq, d, bs)
+    table, nblk = dgq_data.block_tables(cfg, seed)
+    dtable = torch.from_numpy(table).to(dev)
+    caches = [Q.DGQCache(params, nblk, 1, dev) for _ in range(cfg.layers)]
+    ws_c = Q.workspace(Q.compress_workspace_size(params, 1, L, L), dev)
+    ws_d = Q.workspace(Q.decode_workspace_size(params, 1, L), dev)
+    comp_ms = []
+    for layer in range(cfg.layers):
+        k, v, cu, _ = dgq_data.batch_kv_device(cfg, seed, layer, dev)
+        dcu = cu.to(dev)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        Q.dgq_compress(params, k, v, dcu, dtable, caches[layer], L, L, ws=ws_c)
+        e1.record()
+        comp_ms.append((e0, e1))
+        del k, v
+    qs = [torch.from_numpy(dgq_data.queries(cfg, seed, layer)).to(dev) for layer in range(cfg.layers)]
+    lens = torch.full((1,), L, dtype=torch.int32, device=dev)
+    out = torch.empty((1, hq, d), dtype=torch.float32, device=dev)
+    dec = []
+    for rep in range(3):
+        for layer in range(cfg.layers):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            Q.paged_decode_attn_int8(params, qs[layer], caches[layer], dtable, lens, L, out=out, ws=ws_d)
+            e1.record()
+            if rep > 0:
+                dec.append((e0, e1))
+    torch.cuda.synchronize()
+    c_us = float(np.median([a.elapsed_time(b) for a, b in comp_ms])) * 1e3
+    d_us = float(np.median([a.elapsed_time(b) for a, b in dec])) * 1e3
+    nseg = torch.stack([c.nseg for c in caches]).cpu().numpy()
+    dec_bytes = (2 * L * hkv * d + math.ceil(L / bs) * 4 + float(nseg.mean()) * hkv * 32 + hq * d * 2 + hq * d * 4)
+    return {
+        "workload": "128K long context: 1 seq x 131072 tokens, 32 layers looped, 8 KV / 32 q heads, "
+                    "head_dim 128, 64-token blocks, 1% outliers at 8 sigma",
+        "decode_us_per_layer": round(d_us, 2),
+        "decode_gbs_alg": round(dec_bytes / d_us / 1e3, 1),
+        "decode_frac_hbm_peak": round(dec_bytes / d_us / 1e3 / HBM_PEAK_GBS, 4),
+        "compress_us_per_layer": round(c_us, 2),
+        "compress_tokens_per_s": round(L / (c_us / 1e6), 1),
+        "segments_per_head_hist": np.bincount(nseg.reshape(-1), minlength=6).tolist(),
+    }
 
 
 def main():
@@ -350,6 +412,10 @@ def main():
         },
         "quality_vs_fp16": quality,
     }
+    if not args.no_long_context:
+        del caches, g_caches, k, v, ws_c
+        torch.cuda.empty_cache()
+        rec["long_context_128k"] = long_context(args.seed, dev, Q)
     if cpu is not None:
         rec["cpu_baseline"] = cpu
     print(json.dumps(rec))
