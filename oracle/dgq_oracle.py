@@ -46,6 +46,14 @@ R9  Dequantized value = (code + 128) * scale + min.
 R10 Decode: softmax(q . k_hat / sqrt(head_dim)) . v_hat over all cached tokens, query head g uses
     kv head g // (hq / hkv); no mask, no rotary step (the synthetic keys stand for post-rotary keys).
 R11 Append: see ``AppendState``.  (parity unpinned: the rule is ours)
+R12 Segment-count policies, both off by default.  Length-aware cap (DGQ article 3.2): a sequence
+    of L tokens gets at most 2 segments below 2048 tokens, 3 below 16384, else
+    floor(log2(L / 1024)) + 2 but never more than 5; the cap lowers max_segments, never raises it.
+    Variance floor MIN_VAR (DGQ article 5.3, "tokens whose variance is below the threshold go into
+    one group"): a candidate cut is dropped when both of its windows have a population variance
+    (over the window's 16 x head_dim values, on the fixed-point grid) below min_var, i.e. when
+    max(Q_left, Q_right) < min_var * N^2 * 512^2; the append window test obeys the same floor.
+    (parity unpinned: "both windows below" is our reading of the floor)
 """
 
 from __future__ import annotations
@@ -99,20 +107,32 @@ def window_q(a: np.ndarray, b: np.ndarray, head_dim: int) -> np.ndarray:
     return n_elems * sum_b - sum_a * sum_a
 
 
-def change_scores(q: np.ndarray, length: int) -> np.ndarray:
-    """R4: score of every candidate t = 16 .. L-16 (index i <-> t = 16 + i), float64."""
+def variance_floor_q(min_var: float, head_dim: int) -> float:
+    """R12: the variance floor on the Q scale, N^2 * 512^2 * min_var (an exact power-of-two scaling
+    of min_var for head_dim 64 and 128)."""
+    n_elems = WIN * head_dim
+    return float(np.float64(min_var) * np.float64(n_elems * n_elems) * np.float64(FP_SCALE * FP_SCALE))
+
+
+def change_scores(q: np.ndarray, length: int, floor_q: float = 0.0) -> np.ndarray:
+    """R4: score of every candidate t = 16 .. L-16 (index i <-> t = 16 + i), float64; with a
+    variance floor (R12) a candidate whose two windows are both below it scores -inf."""
     if length < 2 * WIN:
         return np.zeros(0, dtype=np.float64)
     left = q[0:length - 2 * WIN + 1]          # window [t-16, t)
     right = q[WIN:length - WIN + 1]           # window [t, t+16)
     hi = np.maximum(left, right).astype(np.float64) + 1.0
     lo = np.minimum(left, right).astype(np.float64) + 1.0
-    return hi / lo
+    score = hi / lo
+    if floor_q > 0.0:
+        score = np.where(np.maximum(left, right).astype(np.float64) < floor_q, -np.inf, score)
+    return score
 
 
 def select_cuts(scores: np.ndarray, max_segments: int = MAX_SEGMENTS, tau: float = TAU) -> List[int]:
-    """R5: greedy change-point selection; returns the sorted cut positions t."""
-    alive = np.ones(len(scores), dtype=bool)
+    """R5: greedy change-point selection; returns the sorted cut positions t.  Candidates scoring
+    -inf (below the variance floor) are never taken."""
+    alive = np.isfinite(scores)
     cuts: List[int] = []
     for _ in range(max(0, max_segments - 1)):
         if not alive.any():
@@ -126,15 +146,28 @@ def select_cuts(scores: np.ndarray, max_segments: int = MAX_SEGMENTS, tau: float
     return sorted(cuts)
 
 
-def segment_starts(k16: np.ndarray, max_segments: int = MAX_SEGMENTS, tau: float = TAU) -> List[int]:
+def length_aware_cap(length: int) -> int:
+    """R12, DGQ article 3.2: the most segments a sequence of `length` tokens may get."""
+    if length < 2048:
+        return 2
+    if length < 16384:
+        return 3
+    return min(5, int(math.floor(math.log2(length / 1024))) + 2)
+
+
+def segment_starts(k16: np.ndarray, max_segments: int = MAX_SEGMENTS, tau: float = TAU,
+                   min_var: float = 0.0, length_aware: bool = False) -> List[int]:
     """Segment start positions of one head's keys ([] for an empty sequence)."""
     length, head_dim = k16.shape
     if length == 0:
         return []
+    if length_aware:
+        max_segments = min(max_segments, length_aware_cap(length))
     if length < 2 * WIN or max_segments <= 1:
         return [0]
     a, b = token_moments(k16)
-    return [0] + select_cuts(change_scores(window_q(a, b, head_dim), length), max_segments, tau)
+    scores = change_scores(window_q(a, b, head_dim), length, variance_floor_q(min_var, head_dim))
+    return [0] + select_cuts(scores, max_segments, tau)
 
 
 @dataclasses.dataclass
@@ -258,14 +291,14 @@ def encode_by_segment(x16: np.ndarray, segs: List[SegParams], which: str) -> np.
 
 
 def compress_head(k16: np.ndarray, v16: np.ndarray, max_segments: int = MAX_SEGMENTS,
-                  tau: float = TAU) -> HeadCompressed:
+                  tau: float = TAU, min_var: float = 0.0, length_aware: bool = False) -> HeadCompressed:
     """The whole DGQ compression of one (sequence, kv head): cuts, params, codes, bits."""
     k16 = np.asarray(k16, dtype=np.float16)
     v16 = np.asarray(v16, dtype=np.float16)
     if not (np.isfinite(k16).all() and np.isfinite(v16).all()):
         raise ValueError("DGQ compression needs finite inputs")
     length = k16.shape[0]
-    starts = segment_starts(k16, max_segments, tau)
+    starts = segment_starts(k16, max_segments, tau, min_var, length_aware)
     segs = segment_params(k16, v16, starts)
     return HeadCompressed(length, segs, encode_by_segment(k16, segs, "k"),
                           encode_by_segment(v16, segs, "v"), boundary_bits(starts, length))
@@ -297,8 +330,8 @@ class AppendState:
     2. S = the segment holding token r0 - 1 (the base segment);
     3. the span needs its own segment if it already has one, or if the table is empty, or if any
        span key lies outside [S.kmin, S.kmax] or any span value outside [S.vmin, S.vmax], or if the
-       span has 16 tokens, the ring holds the 16 tokens before r0, and the score of (ring window,
-       first 16 span tokens) is >= tau;
+       span has 16 tokens, the ring holds the 16 tokens before r0, the score of (ring window,
+       first 16 span tokens) is >= tau and (R12) not both windows are below the variance floor;
     4. if so, the span is a segment starting at r0 whose min/max cover the span (bit r0 set when
        r0 > 0); with a full table it joins S instead, codes saturate, and the clamp counter goes
        up by one for this append;
@@ -311,8 +344,9 @@ class AppendState:
     """
 
     def __init__(self, comp: HeadCompressed, k16_prefix: np.ndarray, block_size: int,
-                 seg_capacity: int = SEG_CAPACITY, tau: float = TAU):
+                 seg_capacity: int = SEG_CAPACITY, tau: float = TAU, min_var: float = 0.0):
         self.head_dim = comp.kcodes.shape[1]
+        self.floor_q = variance_floor_q(min_var, self.head_dim)
         self.block_size = block_size
         self.capacity = seg_capacity
         self.tau = tau
@@ -361,7 +395,8 @@ class AppendState:
                 a, b = token_moments(span_k[:WIN])
                 q_left = window_q_of(self.ring_a, self.ring_b, self.head_dim)
                 q_right = window_q_of(a, b, self.head_dim)
-                want_own = pair_score(q_left, q_right) >= self.tau
+                above_floor = not (float(np.float64(max(q_left, q_right))) < self.floor_q)
+                want_own = above_floor and pair_score(q_left, q_right) >= self.tau
 
         if want_own and not self.span_own:
             if len(self.segs) >= self.capacity:

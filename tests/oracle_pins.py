@@ -425,10 +425,60 @@ def check_group64():
     assert np.all(rec[3, :64] == 0.5)
 
 
+# -- segment-count policies (R12) ------------------------------------------------------------------
+
+def check_length_cap():
+    """The length-aware cap of the DGQ article, section 3.2, at the edges of its three ranges
+    (values worked out by hand from the page's rule: 2 below 2048 tokens, 3 below 16384, else
+    floor(log2(L / 1024)) + 2 capped at 5)."""
+    for length, want in [(1, 2), (2047, 2), (2048, 3), (16383, 3), (16384, 5), (131072, 5)]:
+        assert O.length_aware_cap(length) == want, (length, O.length_aware_cap(length), want)
+    # four strong change points: the cap, not the data, limits the segment count
+    rng = np.random.default_rng(12)
+    for length, cap in [(1500, 2), (3000, 3)]:
+        sig = np.repeat([0.02, 0.4, 0.02, 0.4, 0.02], length // 5 + 1)[:length]
+        x = (rng.standard_normal((length, 64)) * sig[:, None]).astype(np.float16)
+        free = O.segment_starts(x, max_segments=5)
+        capped = O.segment_starts(x, max_segments=5, length_aware=True)
+        assert len(free) == 5 and len(capped) == cap, (length, free, capped)
+        assert capped == O.segment_starts(x, max_segments=cap)
+
+
+def check_min_var_floor():
+    """The variance floor (R12) against numpy's population variance of each window, and the
+    low-variance change that the floor suppresses."""
+    rng = np.random.default_rng(13)
+    d, length = 64, 240
+    sig = np.where(np.arange(length) < 120, 0.01, 0.03)
+    x = (rng.standard_normal((length, d)) * sig[:, None]).astype(np.float16)
+    n = O.fixed_point(x).astype(np.float64) / O.FP_SCALE
+    a, b = O.token_moments(x)
+    q = O.window_q(a, b, d)
+    for min_var in (2e-4, 5e-4, 2e-3):
+        sc = O.change_scores(q, length, O.variance_floor_q(min_var, d))
+        for i, t in enumerate(range(W, length - W + 1)):
+            vmax = max(np.var(n[t - W:t]), np.var(n[t:t + W]))
+            assert (sc[i] == -np.inf) == (vmax < min_var), (min_var, t, vmax, sc[i])
+    # both sides below the floor: no cut at all; floor between them: the change is still cut
+    assert O.segment_starts(x, max_segments=2) == O.segment_starts(x, max_segments=2, min_var=5e-4)
+    assert len(O.segment_starts(x, max_segments=2)) == 2
+    assert O.segment_starts(x, max_segments=2, min_var=2e-3) == [0]
+    # the append window test obeys the floor: a quiet span after a louder ring would be cut
+    # without it (variance ratio 100) and joins with it
+    pre = np.tile(np.array([[0.02], [-0.02]], np.float16), (32, d))            # 64 tokens, var 4e-4
+    for min_var, want_cut in [(0.0, True), (1e-3, False)]:
+        st = O.AppendState(O.compress_head(pre, pre, max_segments=1), pre, 64, 8, 2.0, min_var)
+        for i in range(W):
+            row = np.full(d, 0.002 if i % 2 == 0 else -0.002, np.float16)
+            st.append(row, row)
+        assert (len(st.segs) == 2) == want_cut, (min_var, len(st.segs))
+
+
 ALL_CHECKS = [
     check_fixed_point, check_window_q_against_variance, check_scores_closed_form,
     check_selection_twin, check_step_change_cut, check_segment_invariants, check_tiny_recovery,
     check_minmax_library, check_bits, check_codes, check_constant_segment_exact,
     check_dequant_closed_form, check_attention, check_append_join, check_append_cut,
     check_append_capacity, check_append_matches_prefix_rule, check_append_from_empty, check_group64,
+    check_length_cap, check_min_var_floor,
 ]

@@ -29,7 +29,7 @@ def _window_q_no_square(a, b, head_dim):
     return O.WIN * head_dim * (cb[O.WIN:] - cb[:-O.WIN]) - (ca[O.WIN:] - ca[:-O.WIN])
 
 
-def _scores_shifted(q, length):
+def _scores_shifted(q, length, floor_q=0.0):
     if length < 2 * O.WIN:
         return np.zeros(0)
     left = q[1:length - 2 * O.WIN + 2]
@@ -39,7 +39,7 @@ def _scores_shifted(q, length):
     return (np.maximum(left, right) + 1.0) / (np.minimum(left, right) + 1.0)
 
 
-def _scores_no_plus_one(q, length):
+def _scores_no_plus_one(q, length, floor_q=0.0):
     if length < 2 * O.WIN:
         return np.zeros(0)
     left = q[0:length - 2 * O.WIN + 1].astype(np.float64)
@@ -163,7 +163,26 @@ class _AppendNoReencode(O.AppendState):
             self.vcodes[i] = keep_v[i]
 
 
+def _scores_floor_on_min(q, length, floor_q=0.0):
+    if length < 2 * O.WIN:
+        return np.zeros(0)
+    left = q[0:length - 2 * O.WIN + 1]
+    right = q[O.WIN:length - O.WIN + 1]
+    sc = (np.maximum(left, right) + 1.0) / (np.minimum(left, right) + 1.0)
+    return np.where(np.minimum(left, right) < floor_q, -np.inf, sc) if floor_q > 0 else sc
+
+
+def _cap_inclusive(length):
+    if length <= 2048:
+        return 2
+    if length <= 16384:
+        return 3
+    return min(5, int(math.floor(math.log2(length / 1024))) + 2)
+
+
 MUTATIONS = {
+    "variance_floor_on_min_window": ("change_scores", _scores_floor_on_min, [P.check_min_var_floor]),
+    "length_cap_inclusive_edges": ("length_aware_cap", _cap_inclusive, [P.check_length_cap]),
     "window_15_tokens": ("window_q", _window_q_short, [P.check_window_q_against_variance]),
     "window_drops_square": ("window_q", _window_q_no_square, [P.check_window_q_against_variance]),
     "score_left_window_shift": ("change_scores", _scores_shifted, [P.check_scores_closed_form, P.check_step_change_cut]),
