@@ -71,8 +71,15 @@ typedef enum dgq_status {
   DGQ_ERR_HIP = -5                  /* a HIP call failed; see dgq_last_error() */
 } dgq_status_t;
 
-/* Shape and method parameters, passed to every call.  Defaults: win 16, max_segments 5,
- * seg_capacity 16, tau 2.0. */
+/* Segment-count policies (dgq_params_t.flags), DGQ article 3.2 and 5.3: */
+enum {
+  /* Length-aware cap: a sequence of L tokens gets at most 2 segments below 2048 tokens, 3 below
+   * 16384, else min(5, floor(log2(L / 1024)) + 2); the cap only lowers max_segments. */
+  DGQ_POLICY_LENGTH_AWARE = 1u
+};
+
+/* Shape and method parameters, passed to every call (48 bytes).  Defaults: win 16,
+ * max_segments 5, seg_capacity 16, flags 0, tau 2.0, min_var 0. */
 typedef struct dgq_params {
   int32_t num_kv_heads;  /* >= 1 */
   int32_t num_q_heads;   /* num_kv_heads * G with G in {1, 2, 4}; query head g uses kv head g / G */
@@ -81,8 +88,11 @@ typedef struct dgq_params {
   int32_t win;           /* sliding-window length of the variance curve; must be 16 (DGQ 2.2) */
   int32_t max_segments;  /* 1..8 segments per (sequence, kv head) from dgq_compress */
   int32_t seg_capacity;  /* segment-table rows per (sequence, kv head): max_segments..64 */
-  int32_t reserved;      /* must be 0 */
+  uint32_t flags;        /* DGQ_POLICY_* bits; other bits must be 0 */
   double tau;            /* change-point threshold on the window-variance ratio, finite, >= 1 */
+  double min_var;        /* variance floor, finite, >= 0 (0 = off): a candidate cut whose two
+                            16-token windows both have a population variance below it is not a
+                            change point, in dgq_compress and in dgq_append's window test */
 } dgq_params_t;
 
 /* One segment-table row (32 bytes).  kscale = fp32((kmax - kmin) / 255), likewise vscale. */

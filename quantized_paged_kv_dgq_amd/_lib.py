@@ -25,8 +25,9 @@ class Params(ctypes.Structure):
         ("win", ctypes.c_int32),
         ("max_segments", ctypes.c_int32),
         ("seg_capacity", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("flags", ctypes.c_uint32),
         ("tau", ctypes.c_double),
+        ("min_var", ctypes.c_double),
     ]
 
 
@@ -79,7 +80,9 @@ class Cache(ctypes.Structure):
     ]
 
 
-assert ctypes.sizeof(Params) == 40
+DGQ_POLICY_LENGTH_AWARE = 1
+
+assert ctypes.sizeof(Params) == 48
 assert ctypes.sizeof(Seg) == 32
 assert ctypes.sizeof(Tail) == 208
 

@@ -15,7 +15,7 @@ from typing import Optional, Sequence
 import torch
 
 from . import _lib
-from ._lib import Cache, G64Cache, Params, check
+from ._lib import DGQ_POLICY_LENGTH_AWARE, Cache, G64Cache, Params, check
 
 
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
@@ -33,12 +33,16 @@ def _need(cond: bool, msg: str) -> None:
 
 
 class DGQParams:
-    """dgq_params_t: shapes and method constants (window 16; segments 2..max_segments; tau)."""
+    """dgq_params_t: shapes and method constants (window 16; segments 2..max_segments; tau), plus
+    the segment-count policies: ``length_aware`` (cap by sequence length) and ``min_var``
+    (variance floor below which a window pair is not a change point)."""
 
     def __init__(self, num_kv_heads: int, num_q_heads: int, head_dim: int, block_size: int,
-                 max_segments: int = 5, seg_capacity: int = 16, tau: float = 2.0, win: int = 16):
+                 max_segments: int = 5, seg_capacity: int = 16, tau: float = 2.0, win: int = 16,
+                 length_aware: bool = False, min_var: float = 0.0):
+        flags = DGQ_POLICY_LENGTH_AWARE if length_aware else 0
         self.c = Params(num_kv_heads, num_q_heads, head_dim, block_size, win, max_segments,
-                        seg_capacity, 0, float(tau))
+                        seg_capacity, flags, float(tau), float(min_var))
 
     def __getattr__(self, name):
         return getattr(self.__dict__["c"], name)
@@ -46,6 +50,10 @@ class DGQParams:
     @property
     def group(self) -> int:
         return self.c.num_q_heads // self.c.num_kv_heads
+
+    @property
+    def length_aware(self) -> bool:
+        return bool(self.c.flags & DGQ_POLICY_LENGTH_AWARE)
 
 
 class DGQCache:

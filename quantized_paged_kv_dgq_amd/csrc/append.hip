@@ -21,6 +21,7 @@ struct AppendArgs {
   const int32_t *block_table;
   int32_t max_blocks, hkv, seg_cap, num_blocks;
   double tau;
+  double qfloor;   // variance floor on the Q scale (0 = off)
   dgq_cache_t cache;
 };
 
@@ -156,7 +157,7 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
         const long long nel = (long long)kWin * D;
         const long long ql = nel * lb - la * la, qr = nel * rb - ra * ra;
         const long long hi = ql > qr ? ql : qr, lo = ql > qr ? qr : ql;
-        want = (double)(hi + 1) / (double)(lo + 1) >= a.tau;
+        want = !((double)hi < a.qfloor) && (double)(hi + 1) / (double)(lo + 1) >= a.tau;
       }
     }
     int clampv = 0;
@@ -297,6 +298,7 @@ dgq_status_t launch_append(const dgq_params_t *p, const uint16_t *k_tok, const u
   a.hkv = p->num_kv_heads;
   a.seg_cap = p->seg_capacity;
   a.tau = p->tau;
+  a.qfloor = variance_floor_q(p->min_var, p->head_dim);
   a.cache = *cache;
   if (p->head_dim == 128) launch_bs<128>(a, p->block_size, batch, stream);
   else launch_bs<64>(a, p->block_size, batch, stream);

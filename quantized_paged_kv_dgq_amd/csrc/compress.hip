@@ -32,6 +32,8 @@ struct CompressArgs {
   int32_t hkv, batch, max_segments, seg_cap, nsub, ntile, max_seq_len;
   int64_t total;
   double tau;
+  double qfloor;        // variance floor on the Q scale (0 = off)
+  int32_t length_aware; // DGQ_POLICY_LENGTH_AWARE: per-sequence segment cap
   // workspace
   int32_t *ws_a;        // [hkv][total]
   int64_t *ws_b;        // [hkv][total]
@@ -162,7 +164,7 @@ __global__ __launch_bounds__(256) void scores_kernel(CompressArgs a) {
     const long long ql = nel * bl - al * al;
     const long long qr = nel * br - ar * ar;
     const long long hi = ql > qr ? ql : qr, lo = ql > qr ? qr : ql;
-    score = (double)(hi + 1) / (double)(lo + 1);
+    score = (double)hi < a.qfloor ? -INFINITY : (double)(hi + 1) / (double)(lo + 1);
     a.ws_score[(size_t)h * a.total + c0 + t] = score;
     tb = t;
   }
@@ -263,9 +265,10 @@ __global__ __launch_bounds__(256) void select_kernel(CompressArgs a) {
   __syncthreads();
 
   double2 *tiles = a.ws_tile + bh * a.ntile;
-  if (L >= 2 * kWin && a.max_segments > 1) {
+  const int max_seg = a.length_aware ? min(a.max_segments, length_aware_cap(L)) : a.max_segments;
+  if (L >= 2 * kWin && max_seg > 1) {
     const int ntiles = (L - kWin) / 256 + 1;
-    for (int r = 0; r < a.max_segments - 1; ++r) {
+    for (int r = 0; r < max_seg - 1; ++r) {
       double s = -INFINITY;
       int t = INT_MAX;
       for (int c = tid; c < ntiles; c += 256) {
@@ -578,7 +581,7 @@ __global__ __launch_bounds__(kSmallThreads) void select_small_kernel(CompressArg
       sc[i] = -INFINITY;
       if (t >= kWin && t <= L - kWin) {
         const double ql = q[i], qr = q[i + kWin];
-        sc[i] = (fmax(ql, qr) + 1.0) / (fmin(ql, qr) + 1.0);
+        sc[i] = fmax(ql, qr) < a.qfloor ? -INFINITY : (fmax(ql, qr) + 1.0) / (fmin(ql, qr) + 1.0);
       }
     }
   }
@@ -587,8 +590,9 @@ __global__ __launch_bounds__(kSmallThreads) void select_small_kernel(CompressArg
   // reduction (DPP), one exchange of the 8 wave bests through LDS, and the suppression of the
   // taken cut's neighbours in registers ----
   int nc = 0;
+  const int max_seg = a.length_aware ? min(a.max_segments, length_aware_cap(L)) : a.max_segments;
   if (L >= 2 * kWin) {
-    for (int r = 0; r < a.max_segments - 1; ++r) {
+    for (int r = 0; r < max_seg - 1; ++r) {
       double s = -INFINITY;
       int t = INT_MAX;
 #pragma unroll
@@ -953,6 +957,8 @@ dgq_status_t launch_compress(const dgq_params_t *p, const uint16_t *k, const uin
   a.max_seq_len = max_seq_len;
   a.total = total_tokens;
   a.tau = p->tau;
+  a.qfloor = variance_floor_q(p->min_var, p->head_dim);
+  a.length_aware = (p->flags & DGQ_POLICY_LENGTH_AWARE) != 0;
   a.ws_a = reinterpret_cast<int32_t *>(w + l.a_off);
   a.ws_b = reinterpret_cast<int64_t *>(w + l.b_off);
   a.ws_score = reinterpret_cast<double *>(w + l.score_off);

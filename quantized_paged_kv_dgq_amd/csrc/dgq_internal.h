@@ -15,6 +15,23 @@ constexpr int kChunk = 64;        // tokens per decode / encode chunk
 constexpr int kMaxSegCap = 64;    // segment-table rows per (sequence, kv head), upper bound
 constexpr int kMaxCuts = 7;       // max_segments <= 8
 
+// The variance floor on the window-statistic scale: Q = N^2 * 512^2 * (population variance of the
+// window), N = 16 * head_dim, so the floor is min_var * N^2 * 2^18 (an exact power-of-two scaling).
+inline double variance_floor_q(double min_var, int head_dim) {
+  const double n = 16.0 * head_dim;
+  return min_var * (n * n) * 262144.0;
+}
+
+// Most segments a sequence of L tokens may get under the length-aware policy (DGQ article 3.2):
+// 2 below 2048 tokens, 3 below 16384, else floor(log2(L / 1024)) + 2, at most 5.
+__host__ __device__ inline int length_aware_cap(int L) {
+  if (L < 2048) return 2;
+  if (L < 16384) return 3;
+  int lg = 0;
+  for (int x = L; x > 1; x >>= 1) ++lg;   // floor(log2 L)
+  return lg - 10 + 2 < 5 ? lg - 10 + 2 : 5;
+}
+
 // Record a HIP failure for dgq_last_error(); returns DGQ_ERR_HIP.
 dgq_status_t hip_fail(hipError_t err, const char *where);
 

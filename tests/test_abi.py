@@ -67,7 +67,7 @@ def test_pool(lib):
 
 def _params(**kw):
     base = dict(num_kv_heads=8, num_q_heads=32, head_dim=128, block_size=16, win=16,
-                max_segments=5, seg_capacity=16, reserved=0, tau=2.0)
+                max_segments=5, seg_capacity=16, flags=0, tau=2.0, min_var=0.0)
     base.update(kw)
     return _lib.Params(**base)
 
@@ -77,9 +77,17 @@ def test_workspace_sizes(lib):
     assert lib.dgq_compress_workspace_size(ctypes.byref(p), 16, 16 * 8192, 8192) > 16 * 8192 * 8 * 20
     assert lib.dgq_decode_workspace_size(ctypes.byref(p), 16, 8192) > 0
     for bad in (_params(head_dim=96), _params(block_size=32), _params(win=8), _params(num_q_heads=20),
-                _params(max_segments=9), _params(seg_capacity=4), _params(tau=0.5), _params(reserved=1)):
+                _params(max_segments=9), _params(seg_capacity=4), _params(tau=0.5), _params(flags=2),
+                _params(min_var=-1.0), _params(min_var=float("nan"))):
         assert lib.dgq_compress_workspace_size(ctypes.byref(bad), 1, 10, 10) == 0
         assert lib.dgq_decode_workspace_size(ctypes.byref(bad), 1, 10) == 0
+
+
+def test_policy_params_accepted(lib):
+    """The length-aware flag and a variance floor are valid parameters."""
+    for good in (_params(flags=_lib.DGQ_POLICY_LENGTH_AWARE), _params(min_var=0.01),
+                 _params(flags=1, min_var=1e-4)):
+        assert lib.dgq_compress_workspace_size(ctypes.byref(good), 1, 10, 10) > 0
 
 
 def test_argument_checks_queue_nothing(lib):

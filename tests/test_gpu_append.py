@@ -38,8 +38,9 @@ def run_stream(cfg, seed, steps, params=None, check_every=None, k=None, v=None, 
         for h in range(hkv):
             kk = k[cu[b]:cu[b] + lens[b], h]
             vv = v[cu[b]:cu[b] + lens[b], h]
-            states[(b, h)] = O.AppendState(O.compress_head(kk, vv, p.max_segments, p.tau), kk, p.block_size,
-                                           p.seg_capacity, p.tau)
+            states[(b, h)] = O.AppendState(O.compress_head(kk, vv, p.max_segments, p.tau, p.min_var,
+                                                           params.length_aware),
+                                           kk, p.block_size, p.seg_capacity, p.tau, p.min_var)
     check_every = check_every or steps
     for s in range(steps):
         pos = lens + s
@@ -106,6 +107,15 @@ def test_stream_from_empty_and_short_prefixes():
     v = (k * 0.7).astype(np.float16)
     H.say("append stream from short prefixes")
     run_stream(cfg, 2, 100, check_every=20, k=k, v=v, cu=cu, lens=lens)
+
+
+@pytest.mark.parametrize("min_var", [1e-3, 0.03])
+def test_stream_with_variance_floor_and_length_cap(min_var):
+    """Appends under the variance floor (the window test ignores quiet window pairs) after a
+    length-capped compress."""
+    cfg = dgq_data.get_config(5, batch=3, seq_len=200, append_steps=150)
+    H.say("append with floor", min_var)
+    run_stream(cfg, 8, 150, params=H.params_for(cfg, length_aware=True, min_var=min_var), check_every=50)
 
 
 def test_stream_table_full_clamps_and_counts():

@@ -40,7 +40,7 @@ def compress_and_check(cfg, seed, params=None, k=None, v=None, cu=None, lens=Non
         for h in range(cfg.hkv):
             kk = k[cu[b]:cu[b + 1], h]
             vv = v[cu[b]:cu[b + 1], h]
-            heads[(b, h)] = O.compress_head(kk, vv, p.max_segments, p.tau)
+            heads[(b, h)] = O.compress_head(kk, vv, p.max_segments, p.tau, p.min_var, params.length_aware)
     H.compare_segments(cache, heads, cfg.batch, cfg.hkv)
     bits = cache.bits.cpu().numpy()
     tails = cache.tail.cpu().numpy()
@@ -92,6 +92,27 @@ def test_compress_segment_policies(max_segments, tau):
     cfg = dgq_data.get_config(2, batch=2, seq_len=2000)
     H.say("compress policy", max_segments, tau)
     compress_and_check(cfg, 12, params=H.params_for(cfg, max_segments=max_segments, tau=tau))
+
+
+POLICY_CASES = [
+    ("mixed_lengths_capped", 4, dict(batch=6, seq_len=5000, min_len=300), True, 0.0),
+    ("floor_1e-3", 2, dict(batch=2, seq_len=3000), False, 1e-3),
+    ("floor_0.02_capped", 2, dict(batch=2, seq_len=3000), True, 0.02),
+    ("long_path_floor_capped", 3, dict(seq_len=20000), True, 5e-3),
+    ("d64_floor_capped", 1, dict(hq=4, block_size=64, seq_len=3000, batch=2), True, 0.01),
+]
+
+
+@pytest.mark.parametrize("name,cid,over,length_aware,min_var", POLICY_CASES, ids=[c[0] for c in POLICY_CASES])
+def test_compress_length_cap_and_variance_floor(name, cid, over, length_aware, min_var):
+    """The segment-count policies of the DGQ article (3.2: length-aware cap; 5.3: variance floor)
+    on the short-sequence (fused) and long-sequence (tiled) selection paths."""
+    cfg = dgq_data.get_config(cid, **over)
+    H.say("compress policies", name, over, length_aware, min_var)
+    params = H.params_for(cfg, length_aware=length_aware, min_var=min_var)
+    cache, heads, _ = compress_and_check(cfg, 21, params=params)
+    counts = np.bincount([len(hc.segs) for hc in heads.values()], minlength=6)
+    print(f"{name}: segments per head {counts.tolist()}")
 
 
 def _custom(cfg, seqs):
