@@ -17,6 +17,10 @@ the same data (quantize the batch + the appended token, decode over 8193 tokens;
 rotate), and both decoders' outputs are compared with float32 attention over the unquantized
 fp16 keys/values ("group64_baseline", "quality_vs_fp16").
 
+The segment-count policies (segment cap, tau, the length-aware cap, the variance floor) are then
+run on the same batch: segment histogram, compress time and error against fp16 attention
+("segment_policies").  The streaming workload (64 x 2048-token prefixes, 256 append + decode steps) is timed three
+ways: two launches per step, the fused append + decode, and the group-64 baseline ("streaming").
 Finally the 128K long-context workload (32 layers of one 131,072-token sequence, each layer
 compressed into its own cache, decode looped over the layers) is timed per layer
 ("long_context_128k").
@@ -53,7 +57,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=20.0,
                     help="time budget of the CPU oracle baseline (0 to skip)")
     ap.add_argument("--no-long-context", action="store_true",
-                    help="skip the 32-layer 128K long-context decode/compress figures")
+                    help="skip the streaming and the 32-layer 128K long-context figures")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 512 MiB device copy (torch) a few times: the reference "
                          "kernel of known size for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE")
@@ -143,31 +147,169 @@ def cpu_baseline(cfg, seed, budget_s):
     }
 
 
-def quality_vs_fp16(cfg, k, v, cu, k_tok, v_tok, q, out_dgq, out_g64):
-    """Max and mean over (sequence, query head) of ||o - o_fp16||_inf / ||o_fp16||_inf, where
-    o_fp16 is float32 attention over the unquantized fp16 keys/values (all 8193 tokens)."""
+def fp16_reference(cfg, k, v, cu, q, k_tok=None, v_tok=None):
+    """float32 attention of q over the unquantized fp16 keys/values (plus one appended token)."""
     import torch
 
     B, hkv, hq, d = cfg.batch, cfg.hkv, cfg.hq, cfg.head_dim
     G = hq // hkv
-    ref = torch.empty_like(out_dgq)
+    ref = torch.empty((B, hq, d), dtype=torch.float32, device=q.device)
     for b in range(B):
         a, e = int(cu[b]), int(cu[b + 1])
-        kb = torch.cat([k[a:e], k_tok[b:b + 1]]).float().permute(1, 0, 2).contiguous()   # [hkv][L][d]
-        vb = torch.cat([v[a:e], v_tok[b:b + 1]]).float().permute(1, 0, 2).contiguous()
+        kb, vb = k[a:e], v[a:e]
+        if k_tok is not None:
+            kb, vb = torch.cat([kb, k_tok[b:b + 1]]), torch.cat([vb, v_tok[b:b + 1]])
+        kb = kb.float().permute(1, 0, 2).contiguous()   # [hkv][L][d]
+        vb = vb.float().permute(1, 0, 2).contiguous()
         qb = q[b].float().view(hkv, G, d).contiguous()
         sc = torch.bmm(qb, kb.transpose(1, 2).contiguous()) / math.sqrt(d)
         ref[b] = torch.bmm(torch.softmax(sc, dim=-1), vb).reshape(hq, d)
-    den = ref.abs().amax(-1)
+    return ref
 
-    def err(o):
-        r = (o - ref).abs().amax(-1) / den
-        return float(r.max()), float(r.mean())
 
-    e1, e2 = err(out_dgq), err(out_g64)
+def rel_err_rows(o, ref):
+    """(max, mean) over (sequence, query head) of ||o - ref||_inf / ||ref||_inf."""
+    r = (o - ref).abs().amax(-1) / ref.abs().amax(-1)
+    return float(r.max()), float(r.mean())
+
+
+def quality_vs_fp16(cfg, k, v, cu, k_tok, v_tok, q, out_dgq, out_g64):
+    """Max and mean over (sequence, query head) of ||o - o_fp16||_inf / ||o_fp16||_inf, where
+    o_fp16 is float32 attention over the unquantized fp16 keys/values (all 8193 tokens)."""
+    ref = fp16_reference(cfg, k, v, cu, q, k_tok, v_tok)
+    e1, e2 = rel_err_rows(out_dgq, ref), rel_err_rows(out_g64, ref)
     return {"dgq_max_rel_err": round(e1[0], 6), "dgq_mean_rel_err": round(e1[1], 6),
             "group64_max_rel_err": round(e2[0], 6), "group64_mean_rel_err": round(e2[1], 6),
-            "rows": B * hq, "reference": "float32 attention over the unquantized fp16 K/V"}
+            "rows": cfg.batch * cfg.hq, "reference": "float32 attention over the unquantized fp16 K/V"}
+
+
+POLICIES = [
+    ("default: max 5 segments, tau 2", {}),
+    ("max 3 segments", dict(max_segments=3)),
+    ("max 8 segments", dict(max_segments=8)),
+    ("tau 4", dict(tau=4.0)),
+    ("length-aware cap (3 at 8192 tokens)", dict(length_aware=True)),
+    ("variance floor 1e-3", dict(min_var=1e-3)),
+    ("variance floor 1e-2", dict(min_var=1e-2)),
+]
+
+
+def segment_policies(cfg, k, v, cu, dcu, dtable, nblk, q, dev, Q):
+    """Segment-count policies on the same batch (8192 tokens per sequence, no append): segment
+    histogram, compress time (HIP events, median of 5) and decode error against float32
+    attention over the unquantized keys/values."""
+    import torch
+
+    B, L, hkv, hq, d, bs = cfg.batch, cfg.seq_len, cfg.hkv, cfg.hq, cfg.head_dim, cfg.block_size
+    total = int(cu[-1])
+    ref = fp16_reference(cfg, k, v, cu, q)
+    lens = torch.full((B,), L, dtype=torch.int32, device=dev)
+    rows = []
+    for name, kw in POLICIES:
+        params = Q.DGQParams(hkv, hq, d, bs, seg_capacity=16, **kw)
+        cache = Q.DGQCache(params, nblk, B, dev)
+        ws = Q.workspace(Q.compress_workspace_size(params, B, total, L), dev)
+        ts = []
+        for _ in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            Q.dgq_compress(params, k, v, dcu, dtable, cache, L, total, ws=ws)
+            e1.record()
+            ts.append((e0, e1))
+        out = Q.paged_decode_attn_int8(params, q, cache, dtable, lens, L)
+        torch.cuda.synchronize()
+        nseg = cache.nseg.cpu().numpy().reshape(-1)
+        err = rel_err_rows(out, ref)
+        rows.append({"policy": name, "segments_hist": np.bincount(nseg, minlength=9).tolist(),
+                     "mean_segments": round(float(nseg.mean()), 3),
+                     "compress_us": round(float(np.median([a.elapsed_time(b) for a, b in ts])) * 1e3, 2),
+                     "max_rel_err_vs_fp16": round(err[0], 6), "mean_rel_err_vs_fp16": round(err[1], 6)})
+        del cache, ws
+    return rows
+
+
+def streaming(seed, dev, Q):
+    """The streaming workload: 64 sequences with a 2048-token prefix compressed, then 256 steps of
+    (append one token per sequence, decode one query per sequence), 8 KV / 32 query heads,
+    head_dim 128, 64-token blocks.  Three copies of the same cache run the step three ways: DGQ
+    dgq_append + paged_decode_attn_int8 (two launches), DGQ dgq_append_decode (one launch), and the
+    group-64 baseline (quantize the token, decode).  Per-step medians of HIP-event times, and the
+    last step's error against float32 attention over the unquantized keys/values."""
+    import torch
+
+    import dgq_data
+
+    cfg = dgq_data.get_config(5)
+    B, L, S, hkv, hq, d, bs = cfg.batch, cfg.seq_len, cfg.append_steps, cfg.hkv, cfg.hq, cfg.head_dim, cfg.block_size
+    k, v, cu, lens = dgq_data.batch_kv_device(cfg, seed, 0, dev)
+    cu = cu.numpy().astype(np.int64)
+    idx = torch.cat([torch.arange(int(cu[b]), int(cu[b]) + L) for b in range(B)]).to(dev)
+    pk, pv = k.index_select(0, idx), v.index_select(0, idx)
+    pcu = torch.arange(0, B * L + 1, L, dtype=torch.int32, device=dev)
+    table, nblk = dgq_data.block_tables(cfg, seed, lens_total=np.full(B, L + S))
+    dtable = torch.from_numpy(table).to(dev)
+    params = Q.DGQParams(hkv, hq, d, bs)
+    sep, fused = Q.DGQCache(params, nblk, B, dev), Q.DGQCache(params, nblk, B, dev)
+    g64 = Q.DGQG64Cache(params, nblk, dev)
+    for c in (sep, fused):
+        Q.dgq_compress(params, pk, pv, pcu, dtable, c, L, B * L)
+    Q.dgq_g64_quantize(params, pk, pv, pcu, dtable, g64, L, B * L, L + S)
+    del pk, pv
+    ws = [Q.workspace(Q.decode_workspace_size(params, B, L + S), dev) for _ in range(3)]
+    outs = [torch.empty((B, hq, d), dtype=torch.float32, device=dev) for _ in range(3)]
+    one = torch.arange(B + 1, dtype=torch.int32, device=dev)
+    cu_dev = torch.from_numpy(cu).to(dev)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(S)]
+    # every step's inputs are on the device before the timed loop, so the GPU never waits for the host
+    steps = torch.arange(S, device=dev)
+    tok_idx = (cu_dev[:-1][None, :] + L + steps[:, None]).reshape(-1)
+    k_steps = k.index_select(0, tok_idx).view(S, B, hkv, d)
+    v_steps = v.index_select(0, tok_idx).view(S, B, hkv, d)
+    q_steps = torch.from_numpy(np.stack([dgq_data.queries(cfg, seed, 0, s) for s in range(S)])).to(dev)
+    pos_steps = (L + steps[:, None].expand(S, B)).to(torch.int32).contiguous()
+    pos1_steps = (pos_steps + 1).contiguous()
+    torch.cuda.synchronize()
+    for s in range(S):
+        pos, pos1 = pos_steps[s], pos1_steps[s]
+        kt, vt, q = k_steps[s], v_steps[s], q_steps[s]
+        e = ev[s]
+        e[0].record()
+        Q.dgq_append(params, kt, vt, pos, dtable, sep)
+        Q.paged_decode_attn_int8(params, q, sep, dtable, pos1, L + S, out=outs[0], ws=ws[0])
+        e[1].record()
+        Q.dgq_append_decode(params, kt, vt, pos, q, dtable, fused, L + S, out=outs[1], ws=ws[1])
+        e[2].record()
+        Q.dgq_g64_quantize(params, kt, vt, one, dtable, g64, 1, B, L + S, first_pos=pos)
+        Q.paged_decode_attn_g64(params, q, g64, dtable, pos1, L + S, out=outs[2], ws=ws[2])
+        e[3].record()
+    torch.cuda.synchronize()
+    t = np.array([[x[i].elapsed_time(x[i + 1]) for i in range(3)] for x in ev]) * 1e3
+    med = np.median(t[8:], axis=0)
+    # reference over the L + S tokens of every sequence
+    k_all = [k[int(cu[b]):int(cu[b]) + L + S] for b in range(B)]
+    v_all = [v[int(cu[b]):int(cu[b]) + L + S] for b in range(B)]
+    G = hq // hkv
+    ref = torch.empty((B, hq, d), dtype=torch.float32, device=dev)
+    for b in range(B):
+        kb = k_all[b].float().permute(1, 0, 2).contiguous()
+        vb = v_all[b].float().permute(1, 0, 2).contiguous()
+        qb = q[b].float().view(hkv, G, d).contiguous()
+        sc = torch.bmm(qb, kb.transpose(1, 2).contiguous()) / math.sqrt(d)
+        ref[b] = torch.bmm(torch.softmax(sc, dim=-1), vb).reshape(hq, d)
+    e_dgq, e_g64 = rel_err_rows(outs[1], ref), rel_err_rows(outs[2], ref)
+    nseg = fused.nseg.cpu().numpy().reshape(-1)
+    return {
+        "workload": "streaming: 64 seqs x 2048-token prefix + 256 steps of append 1 token + decode 1 query, "
+                    "8 KV / 32 q heads, head_dim 128, 64-token blocks",
+        "dgq_append_then_decode_us_per_step": round(float(med[0]), 2),
+        "dgq_fused_append_decode_us_per_step": round(float(med[1]), 2),
+        "group64_quantize_then_decode_us_per_step": round(float(med[2]), 2),
+        "fused_tokens_per_s": round(B / (float(med[1]) / 1e6), 1),
+        "fused_outputs_equal_separate": bool(torch.equal(outs[0], outs[1])),
+        "dgq_max_rel_err_vs_fp16": round(e_dgq[0], 6), "dgq_mean_rel_err_vs_fp16": round(e_dgq[1], 6),
+        "group64_max_rel_err_vs_fp16": round(e_g64[0], 6), "group64_mean_rel_err_vs_fp16": round(e_g64[1], 6),
+        "segments_per_head_hist": np.bincount(nseg, minlength=10).tolist(),
+    }
 
 
 def long_context(seed, dev, Q):
@@ -340,6 +482,7 @@ def main():
     gq_ms = np.array([e[0].elapsed_time(e[1]) for e in gev])
     gd_ms = np.array([e[1].elapsed_time(e[2]) for e in gev])
     quality = quality_vs_fp16(cfg, k, v, cu, k_tok, v_tok, q, out, out_g)
+    policies = segment_policies(cfg, k, v, cu, dcu, dtable, nblk, q, dev, Q)
 
     # algorithmic bytes
     Ld = L + 1
@@ -411,9 +554,12 @@ def main():
             "dgq_decode_speedup": round(g_dec_s / dec_s, 4),
         },
         "quality_vs_fp16": quality,
+        "segment_policies": policies,
     }
     if not args.no_long_context:
         del caches, g_caches, k, v, ws_c
+        torch.cuda.empty_cache()
+        rec["streaming"] = streaming(args.seed, dev, Q)
         torch.cuda.empty_cache()
         rec["long_context_128k"] = long_context(args.seed, dev, Q)
     if cpu is not None:

@@ -225,6 +225,24 @@ dgq_status_t paged_decode_attn_int8(const dgq_params_t *p, const uint16_t *q,
                                     int32_t max_seq_len, float softmax_scale, float *out,
                                     void *ws, size_t ws_bytes, hipStream_t stream);
 
+/* ---- Fused decode step: dgq_append followed by paged_decode_attn_int8, in one launch (DGQ
+ * article 3.1: the new token's key/value is quantized inside the paged attention step).
+ *   seq_lens     (device) int32 [batch]: tokens BEFORE this step; the token is appended at that
+ *                position and the query attends to seq_lens[b] + 1 tokens.
+ *   max_seq_len  bound on seq_lens[b] + 1; <= max_blocks * block_size.
+ *   k_tok, v_tok, block_table, cache: as dgq_append; q, softmax_scale, out: as
+ *                paged_decode_attn_int8; ws: dgq_decode_workspace_size(p, batch, max_seq_len) bytes,
+ *                zero-filled once (shared with paged_decode_attn_int8 under the same rules).
+ * Results equal dgq_append followed by paged_decode_attn_int8 with lengths seq_lens + 1: the
+ * workgroup whose partition holds the tail block appends first and decodes with the updated
+ * segment rows; the new row count is published after every workgroup of the (sequence, head) is
+ * done, so no workgroup sees a half-written row. ---- */
+dgq_status_t dgq_append_decode(const dgq_params_t *p, const uint16_t *k_tok, const uint16_t *v_tok,
+                               const int32_t *seq_lens, const uint16_t *q, int32_t batch,
+                               const int32_t *block_table, int32_t max_blocks, int32_t max_seq_len,
+                               float softmax_scale, const dgq_cache_t *cache, float *out, void *ws,
+                               size_t ws_bytes, hipStream_t stream);
+
 /* ---- Fixed 64-channel group INT8 baseline (DGQ article 2.2: the LLM.int8()-style grouping the
  * DGQ design is compared against -- every 64-channel chunk of every token has its own min/max).
  * Same pool layout, code formula and dequantization as DGQ; the ranges are kept per (token,

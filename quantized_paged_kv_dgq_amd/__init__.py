@@ -14,6 +14,7 @@ from .api import (  # noqa: F401
     compress_workspace_size,
     decode_workspace_size,
     dgq_append,
+    dgq_append_decode,
     dgq_compress,
     dgq_g64_quantize,
     paged_decode_attn_g64,

@@ -91,7 +91,7 @@ EXPORTS = [
     "dgq_status_string", "dgq_last_error",
     "dgq_pool_create", "dgq_pool_destroy", "dgq_block_alloc", "dgq_block_free", "dgq_pool_num_free",
     "dgq_compress_workspace_size", "dgq_decode_workspace_size",
-    "dgq_compress", "dgq_append", "paged_decode_attn_int8",
+    "dgq_compress", "dgq_append", "paged_decode_attn_int8", "dgq_append_decode",
     "dgq_g64_quantize", "paged_decode_attn_g64",
 ]
 
@@ -134,6 +134,9 @@ def load() -> ctypes.CDLL:
     lib.paged_decode_attn_int8.argtypes = [P(Params), vp, P(Cache), vp, i32, vp, i32, i32,
                                            ctypes.c_float, vp, vp, sz, vp]
     lib.paged_decode_attn_int8.restype = i32
+    lib.dgq_append_decode.argtypes = [P(Params), vp, vp, vp, vp, i32, vp, i32, i32, ctypes.c_float,
+                                      P(Cache), vp, vp, sz, vp]
+    lib.dgq_append_decode.restype = i32
     lib.dgq_g64_quantize.argtypes = [P(Params), vp, vp, i64, i64, vp, vp, i32, i32, i64, vp, i32, i32,
                                      P(G64Cache), vp]
     lib.dgq_g64_quantize.restype = i32

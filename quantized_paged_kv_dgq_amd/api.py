@@ -204,6 +204,30 @@ def paged_decode_attn_int8(params: DGQParams, q: torch.Tensor, cache: DGQCache,
     return out
 
 
+def dgq_append_decode(params: DGQParams, k_tok: torch.Tensor, v_tok: torch.Tensor, seq_lens: torch.Tensor,
+                      q: torch.Tensor, block_table: torch.Tensor, cache: DGQCache, max_seq_len: int,
+                      softmax_scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                      ws: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Append one token per sequence (k_tok/v_tok [B][Hkv][D] at positions seq_lens) and decode
+    q [B][Hq][D] over seq_lens + 1 tokens, in one launch (see dgq_append_decode); returns fp32."""
+    _need(k_tok.dtype == torch.float16 and k_tok.is_contiguous() and v_tok.is_contiguous(), "contiguous float16 tokens")
+    _need(q.dtype == torch.float16 and q.is_contiguous(), "q: contiguous float16 [B][Hq][D]")
+    _need(seq_lens.dtype == torch.int32 and block_table.dtype == torch.int32, "int32 index tensors")
+    batch = q.shape[0]
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(params.c.head_dim)
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    if ws is None:
+        ws = workspace(decode_workspace_size(params, batch, max_seq_len), q.device)
+    st = _lib.load().dgq_append_decode(
+        ctypes.byref(params.c), _ptr(k_tok), _ptr(v_tok), _ptr(seq_lens), _ptr(q), batch, _ptr(block_table),
+        block_table.shape[1], max_seq_len, float(softmax_scale), ctypes.byref(cache.c), _ptr(out), _ptr(ws),
+        ws.numel(), _stream(stream))
+    check(st, "dgq_append_decode")
+    return out
+
+
 def dgq_g64_quantize(params: DGQParams, k: torch.Tensor, v: torch.Tensor, cu_seqlens: torch.Tensor,
                      block_table: torch.Tensor, cache: DGQG64Cache, max_rows: int, total_rows: int,
                      max_seq_len: int, first_pos: Optional[torch.Tensor] = None, stream=None) -> None:

@@ -144,6 +144,28 @@ extern "C" dgq_status_t paged_decode_attn_int8(const dgq_params_t *p, const uint
                        softmax_scale, out, ws, stream);
 }
 
+extern "C" dgq_status_t dgq_append_decode(const dgq_params_t *p, const uint16_t *k_tok,
+                                          const uint16_t *v_tok, const int32_t *seq_lens,
+                                          const uint16_t *q, int32_t batch, const int32_t *block_table,
+                                          int32_t max_blocks, int32_t max_seq_len, float softmax_scale,
+                                          const dgq_cache_t *cache, float *out, void *ws,
+                                          size_t ws_bytes, hipStream_t stream) {
+  dgq_status_t st = check_params(p);
+  if (st != DGQ_OK) return st;
+  if (batch < 0 || max_seq_len < 1) return DGQ_ERR_INVALID_ARG;
+  if (batch == 0) return DGQ_OK;
+  if (!k_tok || !v_tok || !aligned(k_tok, 16) || !aligned(v_tok, 16)) return DGQ_ERR_INVALID_ARG;
+  if (!q || !out || !seq_lens || !aligned(q, 16) || !aligned(out, 16)) return DGQ_ERR_INVALID_ARG;
+  if (!std::isfinite(softmax_scale)) return DGQ_ERR_INVALID_ARG;
+  if ((st = check_table(p, block_table, max_blocks, max_seq_len)) != DGQ_OK) return st;
+  if ((st = check_cache(cache, batch, true)) != DGQ_OK) return st;
+  const size_t need = decode_workspace_bytes(p, batch, max_seq_len);
+  if (ws == nullptr || !aligned(ws, 256)) return DGQ_ERR_INVALID_ARG;
+  if (ws_bytes < need) return DGQ_ERR_WORKSPACE_TOO_SMALL;
+  return launch_append_decode(p, k_tok, v_tok, seq_lens, q, batch, block_table, max_blocks, max_seq_len,
+                              softmax_scale, cache, out, ws, stream);
+}
+
 static dgq_status_t check_g64_cache(const dgq_g64_cache_t *c) {
   if (c == nullptr || !c->k_pool || !c->v_pool || !c->k_range || !c->v_range || !c->status) return DGQ_ERR_INVALID_ARG;
   if (!aligned(c->k_pool, 16) || !aligned(c->v_pool, 16) || !aligned(c->k_range, 4) ||

@@ -1,282 +1,12 @@
-// Append one token per sequence to a DGQ-compressed cache, re-deciding only the open span of the
-// tail block (DGQ article 2.2: the grouping is re-examined as tokens are generated).
-//
-// One workgroup per (sequence, kv head).  The span [r0, L] (L = tokens before this call) lives
-// in an fp16 staging copy; the decision "join the segment before the span" versus "own segment"
-// is re-taken from the span's K/V ranges and, once the span has 16 tokens, from the ratio of its
-// first 16-token window variance to the 16 sealed tokens before it (the same fixed-point window
-// statistic and score as the compressor).  The span's codes are rewritten with the chosen range;
-// frozen tokens are never touched.  When the block fills, the span is sealed.
-#include <climits>
-#include <cmath>
-
-#include "dgq_internal.h"
+// dgq_append: one workgroup per (sequence, kv head) runs append_one (append_common.h).
+#include "append_common.h"
 
 namespace dgq {
 
-struct AppendArgs {
-  const uint16_t *k_tok;
-  const uint16_t *v_tok;
-  const int32_t *seq_lens;
-  const int32_t *block_table;
-  int32_t max_blocks, hkv, seg_cap, num_blocks;
-  double tau;
-  double qfloor;   // variance floor on the Q scale (0 = off)
-  dgq_cache_t cache;
-};
-
 template <int D, int BS>
 __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
-  const int h = blockIdx.x, b = blockIdx.y;
-  const int tid = threadIdx.x;
-  const size_t bh = (size_t)b * a.hkv + h;
-  const int t = a.seq_lens[b];                 // position of the new token
-  __shared__ dgq_tail_t tl;
-  __shared__ int ns_sh, use_row, own_now, clamp_now;
-  __shared__ float rk[4];                      // span ranges: kmin kmax vmin vmax
-  __shared__ float4 red4[4];
-  __shared__ long long span_a[kWin];
-  __shared__ long long span_b[kWin];
-  __shared__ long long tail_a[kWin];
-  __shared__ long long tail_b[kWin];
-  __shared__ dgq_seg_t chosen;
-  if (tid == 0) {
-    tl = a.cache.tail[bh];
-    ns_sh = a.cache.nseg[bh];
-  }
-  __syncthreads();
-  const int r0 = tl.r0;
-  const int slot0 = r0 < 0 ? 0 : r0 % BS;
-  const int span_len = t + 1 - r0;             // including the new token
-  {
-    // the state must place the new token inside the open span's block, and the block must exist
-    bool bad = t < 0 || r0 < 0 || r0 > t || slot0 + span_len > BS || t / BS >= a.max_blocks ||
-               ns_sh < 0 || ns_sh > a.seg_cap || tl.ring_len < 0 || tl.ring_len > kWin;
-    if (!bad) checked_block(a.block_table[(size_t)b * a.max_blocks + r0 / BS], a.cache.num_blocks, bad);
-    if (bad) {
-      if (tid == 0) atomicAdd(a.cache.status + 2, 1ull);
-      return;
-    }
-  }
-  uint16_t *ks = a.cache.k_stage + bh * (size_t)BS * D;
-  uint16_t *vs = a.cache.v_stage + bh * (size_t)BS * D;
-
-  // 1. stage the new token
-  const int slot = t % BS;
-  for (int d = tid; d < D; d += 256) {
-    ks[slot * D + d] = a.k_tok[bh * D + d];
-    vs[slot * D + d] = a.v_tok[bh * D + d];
-  }
-  __syncthreads();
-
-  // 2. span ranges (and a non-finite check of the new token)
-  float4 r = make_float4(INFINITY, -INFINITY, INFINITY, -INFINITY);
-  float bad = 0.f;
-  for (int x = tid; x < span_len * D; x += 256) {
-    const int s = slot0 + x / D, d = x % D;
-    const float kx = half_bits_to_float(ks[s * D + d]);
-    const float vx = half_bits_to_float(vs[s * D + d]);
-    r.x = fminf(r.x, kx);
-    r.y = fmaxf(r.y, kx);
-    r.z = fminf(r.z, vx);
-    r.w = fmaxf(r.w, vx);
-    if (s == slot) {
-      bad = fmaf(kx, 0.f, bad);
-      bad = fmaf(vx, 0.f, bad);
-    }
-  }
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    r.x = fminf(r.x, __shfl_xor(r.x, o));
-    r.y = fmaxf(r.y, __shfl_xor(r.y, o));
-    r.z = fminf(r.z, __shfl_xor(r.z, o));
-    r.w = fmaxf(r.w, __shfl_xor(r.w, o));
-  }
-  const bool wave_bad = __ballot(!(bad == 0.f)) != 0ull;
-  if ((tid & 63) == 0) {
-    red4[tid >> 6] = r;
-    if (wave_bad) atomicAdd(a.cache.status + 1, 1ull);
-  }
-  __syncthreads();
-  if (tid == 0) {
-    float4 q = red4[0];
-    for (int w = 1; w < 4; ++w) {
-      q.x = fminf(q.x, red4[w].x);
-      q.y = fmaxf(q.y, red4[w].y);
-      q.z = fminf(q.z, red4[w].z);
-      q.w = fmaxf(q.w, red4[w].w);
-    }
-    rk[0] = q.x + 0.0f;
-    rk[1] = q.y + 0.0f;
-    rk[2] = q.z + 0.0f;
-    rk[3] = q.w + 0.0f;
-  }
-
-  // 3. window statistics of the span's first 16 tokens (only needed once it has 16)
-  const bool window_test = span_len >= kWin && tl.ring_len == kWin && !tl.span_own;
-  if (window_test) {
-    // moments of span token i (i < 16): wave w handles tokens 4w..4w+3, 16 lanes each
-    const int w = tid >> 6, lane = tid & 63;
-    for (int i = 4 * w + (lane >> 4); i < 4 * w + 4; i += 4) {
-      int as = 0;
-      long long bs2 = 0;
-      for (int d = lane & 15; d < D; d += 16) {
-        const int n = dgq_fixed_point(half_bits_to_float(ks[(slot0 + i) * D + d]));
-        as += n;
-        bs2 += (long long)(n * n);
-      }
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) {
-        as += __shfl_xor(as, o);
-        bs2 += __shfl_xor(bs2, o);
-      }
-      if ((lane & 15) == 0) {
-        span_a[i] = as;
-        span_b[i] = bs2;
-      }
-    }
-  }
-  __syncthreads();
-
-  // 4. decision (one thread)
-  if (tid == 0) {
-    int ns = ns_sh;
-    const int base = tl.span_own ? ns - 2 : ns - 1;
-    bool want = tl.span_own != 0 || base < 0;
-    if (!want) {
-      const dgq_seg_t S = a.cache.segs[bh * a.seg_cap + base];
-      want = rk[0] < S.kmin || rk[1] > S.kmax || rk[2] < S.vmin || rk[3] > S.vmax;
-      if (!want && window_test) {
-        long long la = 0, lb = 0, ra = 0, rb = 0;
-        for (int i = 0; i < kWin; ++i) {
-          la += tl.ring_a[i];
-          lb += tl.ring_b[i];
-          ra += span_a[i];
-          rb += span_b[i];
-        }
-        const long long nel = (long long)kWin * D;
-        const long long ql = nel * lb - la * la, qr = nel * rb - ra * ra;
-        const long long hi = ql > qr ? ql : qr, lo = ql > qr ? qr : ql;
-        want = !((double)hi < a.qfloor) && (double)(hi + 1) / (double)(lo + 1) >= a.tau;
-      }
-    }
-    int clampv = 0;
-    if (want && !tl.span_own) {
-      if (ns >= a.seg_cap) {
-        clampv = 1;
-        want = false;
-      } else {
-        dgq_seg_t row;
-        row.start = r0;
-        row.kmin = rk[0];
-        row.kmax = rk[1];
-        row.vmin = rk[2];
-        row.vmax = rk[3];
-        row.kscale = dgq_scale(row.kmin, row.kmax);
-        row.vscale = dgq_scale(row.vmin, row.vmax);
-        row.reserved = 0;
-        a.cache.segs[bh * a.seg_cap + ns] = row;
-        ns += 1;
-        tl.span_own = 1;
-        if (r0 > 0) {
-          const int blk = a.block_table[(size_t)b * a.max_blocks + r0 / BS];
-          uint8_t *byte = a.cache.bits + ((size_t)blk * a.hkv + h) * (BS / 8) + (r0 % BS) / 8;
-          *byte = (uint8_t)(*byte | (1u << (r0 % 8)));
-        }
-      }
-    } else if (want && tl.span_own) {
-      dgq_seg_t row = a.cache.segs[bh * a.seg_cap + ns - 1];
-      row.kmin = rk[0];
-      row.kmax = rk[1];
-      row.vmin = rk[2];
-      row.vmax = rk[3];
-      row.kscale = dgq_scale(row.kmin, row.kmax);
-      row.vscale = dgq_scale(row.vmin, row.vmax);
-      a.cache.segs[bh * a.seg_cap + ns - 1] = row;
-    }
-    ns_sh = ns;
-    use_row = tl.span_own ? ns - 1 : base;
-    chosen = a.cache.segs[bh * a.seg_cap + use_row];
-    own_now = tl.span_own;
-    clamp_now = clampv;
-    if (clampv) atomicAdd(a.cache.status + 0, 1ull);
-  }
-  __syncthreads();
-
-  // 5. re-encode the span with the chosen segment's range
-  const dgq_seg_t row = chosen;
-  const float kinv = dgq_inv(row.kmin, row.kmax), vinv = dgq_inv(row.vmin, row.vmax);
-  const int32_t *bt = a.block_table + (size_t)b * a.max_blocks;
-  const int blk = bt[r0 / BS];
-  int8_t *kt = a.cache.k_pool + ((size_t)blk * a.hkv + h) * (size_t)BS * D;
-  int8_t *vt = a.cache.v_pool + ((size_t)blk * a.hkv + h) * (size_t)BS * D;
-  for (int x = tid; x < span_len * D; x += 256) {
-    const int s = slot0 + x / D, d = x % D;
-    const float kx = half_bits_to_float(ks[s * D + d]);
-    const float vx = half_bits_to_float(vs[s * D + d]);
-    kt[k_tile_offset<D, BS>(s, d)] = (int8_t)dgq_encode_value(kx, row.kmin, kinv);
-    vt[v_tile_offset<D, BS>(s, d)] = (int8_t)dgq_encode_value(vx, row.vmin, vinv);
-  }
-
-  // 6. seal a full block: the ring keeps the moments of the last 16 sealed tokens
-  const bool seal = (t + 1) % BS == 0;
-  const int m_tail = span_len < kWin ? span_len : kWin;   // span tokens that enter the ring
-  if (seal) {
-    const int w = tid >> 6, lane = tid & 63;
-    for (int i = 4 * w + (lane >> 4); i < kWin; i += 16) {
-      int as = 0;
-      long long bs2 = 0;
-      if (i < m_tail) {
-        const int s = slot0 + span_len - m_tail + i;
-        for (int d = lane & 15; d < D; d += 16) {
-          const int n = dgq_fixed_point(half_bits_to_float(ks[s * D + d]));
-          as += n;
-          bs2 += (long long)(n * n);
-        }
-      }
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) {
-        as += __shfl_xor(as, o);
-        bs2 += __shfl_xor(bs2, o);
-      }
-      if ((lane & 15) == 0) {
-        tail_a[i] = as;
-        tail_b[i] = bs2;
-      }
-    }
-  }
-  __syncthreads();
-  if (tid == 0) {
-    a.cache.nseg[bh] = ns_sh;
-    if (seal) {
-      // new ring = last 16 of (old ring, span tokens)
-      const int old_keep = m_tail < kWin ? (tl.ring_len < kWin - m_tail ? tl.ring_len : kWin - m_tail) : 0;
-      int32_t na[kWin];
-      long long nb[kWin];
-      int n = 0;
-      for (int i = tl.ring_len - old_keep; i < tl.ring_len; ++i) {
-        na[n] = tl.ring_a[i];
-        nb[n] = tl.ring_b[i];
-        ++n;
-      }
-      for (int i = 0; i < m_tail; ++i) {
-        na[n] = (int32_t)tail_a[i];
-        nb[n] = tail_b[i];
-        ++n;
-      }
-      for (int i = 0; i < kWin; ++i) {
-        tl.ring_a[i] = i < n ? na[i] : 0;
-        tl.ring_b[i] = i < n ? nb[i] : 0;
-      }
-      tl.ring_len = n;
-      tl.r0 = t + 1;
-      tl.span_own = 0;
-    } else {
-      tl.span_own = own_now;
-    }
-    (void)clamp_now;
-    a.cache.tail[bh] = tl;
-  }
+  __shared__ AppendOut out;
+  append_one<D, BS>(a, blockIdx.y, blockIdx.x, true, out);
 }
 
 template <int D>
@@ -286,9 +16,9 @@ static void launch_bs(const AppendArgs &a, int bs, int batch, hipStream_t s) {
   else hipLaunchKernelGGL((append_kernel<D, 16>), grid, dim3(256), 0, s, a);
 }
 
-dgq_status_t launch_append(const dgq_params_t *p, const uint16_t *k_tok, const uint16_t *v_tok,
-                           const int32_t *seq_lens, int32_t batch, const int32_t *block_table,
-                           int32_t max_blocks, const dgq_cache_t *cache, hipStream_t stream) {
+AppendArgs make_append_args(const dgq_params_t *p, const uint16_t *k_tok, const uint16_t *v_tok,
+                            const int32_t *seq_lens, const int32_t *block_table, int32_t max_blocks,
+                            const dgq_cache_t *cache) {
   AppendArgs a;
   a.k_tok = k_tok;
   a.v_tok = v_tok;
@@ -297,9 +27,17 @@ dgq_status_t launch_append(const dgq_params_t *p, const uint16_t *k_tok, const u
   a.max_blocks = max_blocks;
   a.hkv = p->num_kv_heads;
   a.seg_cap = p->seg_capacity;
+  a.num_blocks = cache->num_blocks;
   a.tau = p->tau;
   a.qfloor = variance_floor_q(p->min_var, p->head_dim);
   a.cache = *cache;
+  return a;
+}
+
+dgq_status_t launch_append(const dgq_params_t *p, const uint16_t *k_tok, const uint16_t *v_tok,
+                           const int32_t *seq_lens, int32_t batch, const int32_t *block_table,
+                           int32_t max_blocks, const dgq_cache_t *cache, hipStream_t stream) {
+  const AppendArgs a = make_append_args(p, k_tok, v_tok, seq_lens, block_table, max_blocks, cache);
   if (p->head_dim == 128) launch_bs<128>(a, p->block_size, batch, stream);
   else launch_bs<64>(a, p->block_size, batch, stream);
   return check_launch("dgq_append kernel");

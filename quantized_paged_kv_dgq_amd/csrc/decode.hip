@@ -28,6 +28,7 @@
 #include <climits>
 #include <cmath>
 
+#include "append_common.h"
 #include "decode_common.h"
 
 namespace dgq {
@@ -103,7 +104,10 @@ __global__ __launch_bounds__(64 * kWaves) void decode_partition_kernel(DecodeArg
       s_vs = sg.vscale;
       s_midv = sg.vmin + 128.0f * sg.vscale;
     }
-    float vsmax = s_vs;
+    // the largest value scale among the segments this wave's tokens can use (rows starting after
+    // its last token cannot apply; leaving them out also keeps the result equal to the fused
+    // append + decode step, where the open span's row may change while other workgroups run)
+    float vsmax = s_start <= t_end - 1 ? s_vs : 0.f;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) vsmax = fmaxf(vsmax, __shfl_xor(vsmax, o));
     const float wfac_unit = vsmax > 0.f ? 4194304.0f / vsmax : 0.f;   // 2^22 / vsmax
@@ -344,6 +348,343 @@ __global__ __launch_bounds__(64 * kWaves) void decode_partition_kernel(DecodeArg
   finish_partition<D, G>(a, b, h, p, L, sh_o, sh_m, sh_l);
 }
 
+// The fused append + decode step.  The same decode as decode_partition_kernel, except that
+// seq_lens holds the lengths before this step's token: the workgroup of the last partition of
+// (b, h), the one whose tokens include the tail block, first appends the token (append_one) and
+// decodes with the updated segment rows; the new row count is published once every workgroup of
+// (b, h) is done.  (The plain kernel keeps its own copy of the body: compiling it through this
+// templated body, APPEND = false, made it about 3 % slower.)
+template <int D, int G, int BS, bool APPEND>
+__device__ __forceinline__ void decode_body(const DecodeArgs &a, const AppendArgs *ap) {
+  constexpr int M = D / 64;    // 64-channel slices of a key row
+  constexpr int NT = D / 16;   // 16-channel tiles of the output
+  const int p = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int j = lane >> 4, col = lane & 15, g = col >> 2, piece = col & 3;
+  const bool live = (g < G) && (piece < 3);
+  const ByteSel bsel = byte_sel(piece, live);
+  const int bh = b * a.hkv + h;
+  const int span = a.part_tokens * kWaves;
+  const int wg_begin = p * span;
+
+  // Loads that do not depend on the sequence length go out together with it: the block ids of
+  // the workgroup's span, the segment-table row of this lane and the query slice of this lane.
+  const int32_t *bt = a.block_table + (size_t)b * a.max_blocks;
+  const int wblk0 = wg_begin / BS;
+  SpanBlocks<BS> span_blk;
+  span_blk.load(bt, a.max_blocks, wblk0);
+  const int ns_raw = a.nseg[bh];
+  dgq_seg_t seg_raw = {};
+  if (lane < a.seg_cap) seg_raw = a.segs[(size_t)bh * a.seg_cap + lane];
+  const int qh = h * G + (g < G ? g : 0);
+  const uint16_t *qrow = a.q + ((size_t)b * a.hq + qh) * D;
+  uint4 qraw[M][2];
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    const uint4 *src = reinterpret_cast<const uint4 *>(qrow + 64 * m + 16 * j);
+    qraw[m][0] = src[0];
+    qraw[m][1] = src[1];
+  }
+
+  const int L_raw = a.seq_lens[b] + (APPEND ? 1 : 0);
+  const int L = L_raw < 0 ? 0 : (L_raw > a.max_seq_len ? a.max_seq_len : L_raw);
+  if (p == 0 && threadIdx.x == 0 && h == 0 && L != L_raw) atomicAdd(a.status + 2, 1ull);
+  if (L == 0 && p == 0) {                          // an empty sequence attends to nothing: zeros
+    for (int e = threadIdx.x; e < G * D; e += 64 * kWaves) a.out[((size_t)b * a.hq + h * G) * D + e] = 0.f;
+    return;
+  }
+  const int P = parts_of(L, span);
+  if (p >= P) return;                              // the whole workgroup has nothing to do
+  __shared__ AppendOut aout;
+  if (APPEND && p == P - 1) append_one<D, BS>(*ap, b, h, false, aout);
+  const WaveRange wr = wave_range(wg_begin, span, L, wave);
+  const int t_begin = wr.t_begin, t_end = wr.t_end;
+  const bool active = t_begin < t_end;
+  __shared__ int sh_blk[SpanBlocks<BS>::kBlocks];
+  span_blk.publish(wblk0, (L + BS - 1) / BS, a.num_blocks, sh_blk, a.status);
+  __syncthreads();
+  __shared__ float sh_o[kWaves][G][D];
+  __shared__ float sh_m[kWaves][G], sh_l[kWaves][G];
+  // float output of each lane (C layout), folded from the int32 sums only when a maximum moves
+  __shared__ float sh_acc[kWaves][NT * 4][64];
+
+  float m_run = -INFINITY, l_run = 0.f, mv_run = 0.f;
+  float (*oacc)[64] = sh_acc[wave];
+#pragma unroll
+  for (int r = 0; r < NT * 4; ++r) oacc[r][lane] = 0.f;
+  float wv = 0.f;
+
+  if (active) {
+    // ---- segment table: lane k holds row k (after this step's append, for its workgroup) ----
+    const bool appended = APPEND && p == P - 1;
+    const int ns = min(appended ? aout.ns : ns_raw, a.seg_cap);
+    int s_start = INT_MAX;
+    float s_ks = 0.f, s_midk = 0.f, s_vs = 0.f, s_midv = 0.f;
+    if (lane < ns) {
+      const dgq_seg_t sg = appended && lane == aout.use_row ? aout.chosen : seg_raw;
+      s_start = sg.start;
+      s_ks = sg.kscale;
+      s_midk = sg.kmin + 128.0f * sg.kscale;
+      s_vs = sg.vscale;
+      s_midv = sg.vmin + 128.0f * sg.vscale;
+    }
+    // the largest value scale among the segments this wave's tokens can use (rows starting after
+    // its last token are left out: they cannot apply, and in the fused step the open span's row
+    // may be rewritten while other workgroups run)
+    float vsmax = s_start <= t_end - 1 ? s_vs : 0.f;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) vsmax = fmaxf(vsmax, __shfl_xor(vsmax, o));
+    const float wfac_unit = vsmax > 0.f ? 4194304.0f / vsmax : 0.f;   // 2^22 / vsmax
+    const float s_wf = s_vs * wfac_unit;
+    wv = live ? ldexpf(vsmax, -6 - 8 * piece) : 0.f;                // 2^(16-8*piece) * vsmax / 2^22
+
+    // ---- query: three signed bytes per channel, one per column of the B operand ----
+    float qv[M][16];
+    float amax = 0.f, qsum = 0.f;
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      const uint4 w0 = qraw[m][0], w1 = qraw[m][1];
+      const uint32_t ws[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        qv[m][2 * e] = half_bits_to_float(ws[e] & 0xFFFFu);
+        qv[m][2 * e + 1] = half_bits_to_float(ws[e] >> 16);
+      }
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        amax = fmaxf(amax, fabsf(qv[m][e]));
+        qsum += qv[m][e];
+      }
+    }
+    amax = fmaxf(amax, __shfl_xor(amax, 16));
+    amax = fmaxf(amax, __shfl_xor(amax, 32));
+    qsum += __shfl_xor(qsum, 16);
+    qsum += __shfl_xor(qsum, 32);
+    int qexp = 0;
+    if (amax > 0.f) {
+      int ex;
+      frexpf(amax, &ex);
+      qexp = 22 - ex;   // amax * 2^qexp in [2^21, 2^22)
+    }
+    const float qmul = ldexpf(1.0f, qexp);
+    v4i qfrag[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      uint32_t wq4[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int e = 0; e < 16; ++e) wq4[e >> 2] |= sel_byte(fmaf(qv[m][e], qmul, kMagic), bsel) << (8 * (e & 3));
+      qfrag[m] = v4i{(int)wq4[0], (int)wq4[1], (int)wq4[2], (int)wq4[3]};
+    }
+    // per-lane weight of this byte's partial dot product, in log2 units of the softmax
+    const float wq = live ? ldexpf(a.sm_log2, 16 - 8 * piece - qexp) : 0.f;
+    const float qsum_s = qsum * a.sm_log2;
+
+    // block ids come from sh_blk: chunk c of the wave is local chunk lc0 + c of the workgroup
+    const int lc0 = (t_begin - wg_begin) / kChunk;
+    const size_t tile_bytes = (size_t)BS * D;
+    const int8_t *kpool = a.k_pool + (size_t)h * tile_bytes;
+    const int8_t *vpool = a.v_pool + (size_t)h * tile_bytes;
+    const size_t blk_stride = (size_t)a.hkv * tile_bytes;
+
+    // Fragment loads of chunk c (64 tokens) of the partition.  Keys: tile T (16 tokens) x slice m
+    // (64 channels) per A operand; values: channel tile n (16 channels) x 64 tokens per A operand.
+    auto load_k = [&](int c, v4i (&kf)[4][M]) {
+      if constexpr (BS == 64) {
+        const int blk = __builtin_amdgcn_readfirstlane(sh_blk[lc0 + c]);
+        const int8_t *kb = kpool + (size_t)blk * blk_stride;
+#pragma unroll
+        for (int T = 0; T < 4; ++T)
+#pragma unroll
+          for (int m = 0; m < M; ++m)
+            kf[T][m] = *reinterpret_cast<const v4i *>(kb + (((T * M + m) * 64) + lane) * 16);
+      } else {
+        const int8_t *kb = kpool + (size_t)sh_blk[4 * (lc0 + c) + ((lane & 15) >> 2)] * blk_stride;
+#pragma unroll
+        for (int T = 0; T < 4; ++T)
+#pragma unroll
+          for (int m = 0; m < M; ++m)
+            kf[T][m] = *reinterpret_cast<const v4i *>(kb + ((((T * M + m) * 4 + j) * 4 + (lane & 3)) * 16));
+      }
+    };
+    auto load_v = [&](int c, v4i (&vf)[NT]) {
+      if constexpr (BS == 64) {
+        const int blk = __builtin_amdgcn_readfirstlane(sh_blk[lc0 + c]);
+        const int8_t *vb = vpool + (size_t)blk * blk_stride;
+#pragma unroll
+        for (int n = 0; n < NT; ++n) vf[n] = *reinterpret_cast<const v4i *>(vb + (n * 64 + lane) * 16);
+      } else {
+        const int8_t *vb = vpool + (size_t)sh_blk[4 * (lc0 + c) + j] * blk_stride;
+#pragma unroll
+        for (int n = 0; n < NT; ++n) vf[n] = *reinterpret_cast<const v4i *>(vb + (16 * n + (lane & 15)) * 16);
+      }
+    };
+    // segment index of token t (rows are sorted by start; row 0 starts at 0)
+    auto seg_of = [&](int t) -> int {
+      int idx = 0;
+      for (int k = 1; k < ns; ++k) idx += (t >= __builtin_amdgcn_readlane(s_start, k)) ? 1 : 0;
+      return idx;
+    };
+
+    v4i cacc[NT];   // int32 PV sums since the last fold into O
+#pragma unroll
+    for (int n = 0; n < NT; ++n) cacc[n] = v4i{0, 0, 0, 0};
+
+    const int nchunks = (t_end - t_begin + kChunk - 1) / kChunk;
+    v4i kf[4][M];
+    v4i vf[NT];
+    load_k(0, kf);
+    load_v(0, vf);
+    for (int c = 0; c < nchunks; ++c) {
+      const int t0 = t_begin + c * kChunk;
+
+      // S^T = K . Q^T : rows = tokens of tile T, columns = (query head, byte)
+      float S[4][4];
+#pragma unroll
+      for (int T = 0; T < 4; ++T) {
+        v4i acc = {0, 0, 0, 0};
+#pragma unroll
+        for (int m = 0; m < M; ++m) acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(kf[T][m], qfrag[m], acc, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) S[T][i] = (float)acc[i] * wq;
+      }
+      if (c + 1 < nchunks) load_k(c + 1, kf);
+#pragma unroll
+      for (int T = 0; T < 4; ++T)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float s = S[T][i];
+          s += quad_xor1(s);
+          s += quad_xor2(s);
+          S[T][i] = s;
+        }
+
+      // token of (T, i) for this lane
+      auto tok_of = [&](int T, int i) -> int {
+        return BS == 64 ? t0 + 16 * T + 4 * j + i : t0 + 16 * j + 4 * T + i;
+      };
+
+      // scores in log2 units, with the segment's (ks, midK) of every token
+      const int t_last = min(t0 + kChunk, t_end) - 1;
+      const int sf = max(__popcll(__ballot(s_start <= t0)) - 1, 0);
+      const int sl = max(__popcll(__ballot(s_start <= t_last)) - 1, 0);
+      const bool uni = sf == sl;
+      if (uni) {
+        const float ks = readlane_f(s_ks, sf), mk = readlane_f(s_midk, sf) * qsum_s;
+#pragma unroll
+        for (int T = 0; T < 4; ++T)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) S[T][i] = fmaf(ks, S[T][i], mk);
+      } else {
+#pragma unroll
+        for (int T = 0; T < 4; ++T)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int idx = seg_of(tok_of(T, i));
+            S[T][i] = fmaf(__shfl(s_ks, idx), S[T][i], __shfl(s_midk, idx) * qsum_s);
+          }
+      }
+      if (t0 + kChunk > t_end) {   // partial last chunk: tokens past the end weigh nothing
+#pragma unroll
+        for (int T = 0; T < 4; ++T)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) S[T][i] = tok_of(T, i) < t_end ? S[T][i] : -INFINITY;
+      }
+
+      // online softmax (base 2)
+      float cmax = -INFINITY;
+#pragma unroll
+      for (int T = 0; T < 4; ++T)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) cmax = fmaxf(cmax, S[T][i]);
+      cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
+      cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
+      const float m_new = fmaxf(m_run, cmax);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      if (__ballot(m_new > m_run) != 0ull) {
+        // some head's maximum moved: fold the int32 sums (relative to the old maximum) into O
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) oacc[4 * n + i][lane] = (oacc[4 * n + i][lane] + (float)cacc[n][i]) * alpha;
+          cacc[n] = v4i{0, 0, 0, 0};
+        }
+      }
+      m_run = m_new;
+      float psum = 0.f, pmv = 0.f;
+      uint32_t pw[4] = {0u, 0u, 0u, 0u};
+      if (uni) {
+        const float wfs = readlane_f(s_wf, sf), mvs = readlane_f(s_midv, sf);
+#pragma unroll
+        for (int T = 0; T < 4; ++T)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float pr = __builtin_amdgcn_exp2f(S[T][i] - m_new);
+            psum += pr;
+            pw[T] |= sel_byte(fmaf(pr, wfs, kMagic), bsel) << (8 * i);
+          }
+        pmv = psum * mvs;
+      } else {
+#pragma unroll
+        for (int T = 0; T < 4; ++T)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int idx = seg_of(tok_of(T, i));
+            const float pr = __builtin_amdgcn_exp2f(S[T][i] - m_new);
+            psum += pr;
+            pmv = fmaf(pr, __shfl(s_midv, idx), pmv);
+            pw[T] |= sel_byte(fmaf(pr, __shfl(s_wf, idx), kMagic), bsel) << (8 * i);
+          }
+      }
+      l_run = fmaf(l_run, alpha, psum);
+      mv_run = fmaf(mv_run, alpha, pmv);
+      const v4i pfrag = v4i{(int)pw[0], (int)pw[1], (int)pw[2], (int)pw[3]};
+
+      // O^T += V^T . P^T : rows = channels of tile n, columns = (query head, byte)
+#pragma unroll
+      for (int n = 0; n < NT; ++n) cacc[n] = __builtin_amdgcn_mfma_i32_16x16x64_i8(vf[n], pfrag, cacc[n], 0, 0, 0);
+      if (c + 1 < nchunks) load_v(c + 1, vf);
+    }
+#pragma unroll
+    for (int n = 0; n < NT; ++n)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) oacc[4 * n + i][lane] += (float)cacc[n][i];
+  }
+
+  // ---- epilogue: combine the byte columns and the mid term per wave, then merge the waves of
+  // the workgroup in LDS and write one partial (m, l, o) per query head ----
+  l_run += __shfl_xor(l_run, 16);
+  l_run += __shfl_xor(l_run, 32);
+  mv_run += __shfl_xor(mv_run, 16);
+  mv_run += __shfl_xor(mv_run, 32);
+#pragma unroll
+  for (int n = 0; n < NT; ++n)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float v = oacc[4 * n + i][lane] * wv;
+      v += quad_xor1(v);
+      v += quad_xor2(v);
+      if (piece == 0 && g < G) sh_o[wave][g][16 * n + 4 * j + i] = active ? v + mv_run : 0.f;
+    }
+  if (j == 0 && piece == 0 && g < G) {
+    sh_m[wave][g] = active ? m_run : -INFINITY;
+    sh_l[wave][g] = active ? l_run : 0.f;
+  }
+  const int done = finish_partition<D, G>(a, b, h, p, L, sh_o, sh_m, sh_l, APPEND && p == P - 1 ? aout.ns : -1);
+  if (APPEND && done != kPartialOnly && threadIdx.x == 0) {
+    // every workgroup of (b, h) has read the old row count: publish the new one
+    const size_t bhs = (size_t)b * a.hkv + h;
+    ap->cache.nseg[bhs] = done == kWroteOutput ? aout.ns
+                                               : __hip_atomic_load(a.pend_nseg + bhs, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+
+template <int D, int G, int BS>
+__global__ __launch_bounds__(64 * kWaves) void append_decode_kernel(DecodeArgs a, AppendArgs ap) {
+  decode_body<D, G, BS, true>(a, &ap);
+}
+
 DecodePlan decode_plan(const dgq_params_t *p, int32_t batch, int32_t max_seq_len, int64_t target_waves) {
   // Each workgroup takes up to kWaves * per consecutive 64-token chunks of one (sequence, kv
   // head) and writes one partial; its waves split them evenly.  Aim at target_waves in all (1024 =
@@ -399,8 +740,10 @@ DecodeArgs make_decode_args(const dgq_params_t *p, const uint16_t *q, const int8
   a.block_table = block_table;
   a.seq_lens = seq_lens;
   char *w = reinterpret_cast<char *>(ws);
+  const size_t ctr_bytes = align_up((size_t)batch * p->num_kv_heads * sizeof(unsigned), 256);
   a.counters = reinterpret_cast<unsigned *>(w);
-  a.part_ml = reinterpret_cast<float *>(w + align_up((size_t)batch * p->num_kv_heads * sizeof(unsigned), 256));
+  a.pend_nseg = reinterpret_cast<int32_t *>(w + ctr_bytes);
+  a.part_ml = reinterpret_cast<float *>(w + 2 * ctr_bytes);
   a.part_o = a.part_ml + align_up((size_t)batch * p->num_q_heads * plan.nparts * 2, 64);
   a.out = out;
   a.status = status;
@@ -431,12 +774,43 @@ dgq_status_t launch_decode(const dgq_params_t *p, const uint16_t *q, const dgq_c
   return check_launch("paged_decode_attn_int8 kernel");
 }
 
+template <int D, int G>
+static void launch_fused_bs(const DecodeArgs &a, const AppendArgs &ap, int bs, int batch, hipStream_t s) {
+  dim3 grid(a.nparts, a.hkv, batch);
+  if (bs == 64) hipLaunchKernelGGL((append_decode_kernel<D, G, 64>), grid, dim3(64 * kWaves), 0, s, a, ap);
+  else hipLaunchKernelGGL((append_decode_kernel<D, G, 16>), grid, dim3(64 * kWaves), 0, s, a, ap);
+}
+
+template <int D>
+static void launch_fused_g(const DecodeArgs &a, const AppendArgs &ap, int G, int bs, int batch, hipStream_t s) {
+  if (G == 1) launch_fused_bs<D, 1>(a, ap, bs, batch, s);
+  else if (G == 2) launch_fused_bs<D, 2>(a, ap, bs, batch, s);
+  else launch_fused_bs<D, 4>(a, ap, bs, batch, s);
+}
+
+dgq_status_t launch_append_decode(const dgq_params_t *p, const uint16_t *k_tok, const uint16_t *v_tok,
+                                  const int32_t *seq_lens, const uint16_t *q, int32_t batch,
+                                  const int32_t *block_table, int32_t max_blocks, int32_t max_seq_len,
+                                  float softmax_scale, const dgq_cache_t *cache, float *out, void *ws,
+                                  hipStream_t stream) {
+  DecodeArgs a = make_decode_args(p, q, cache->k_pool, cache->v_pool, cache->num_blocks, cache->status,
+                                  block_table, max_blocks, seq_lens, batch, max_seq_len, softmax_scale, out, ws,
+                                  kDgqDecodeWaves);
+  a.segs = cache->segs;
+  a.nseg = cache->nseg;
+  AppendArgs ap = make_append_args(p, k_tok, v_tok, seq_lens, block_table, max_blocks, cache);
+  const int D = p->head_dim, G = p->num_q_heads / p->num_kv_heads;
+  if (D == 128) launch_fused_g<128>(a, ap, G, p->block_size, batch, stream);
+  else launch_fused_g<64>(a, ap, G, p->block_size, batch, stream);
+  return check_launch("dgq_append_decode kernel");
+}
+
 size_t decode_workspace_bytes(const dgq_params_t *p, int32_t batch, int32_t max_seq_len) {
   // one size for both decoders: the larger partial count of their two plans
   const int32_t nparts = std::max(decode_plan(p, batch, max_seq_len, kDgqDecodeWaves).nparts,
                                   decode_plan(p, batch, max_seq_len, kG64DecodeWaves).nparts);
   const size_t rows = (size_t)batch * p->num_q_heads * nparts;
-  return align_up((size_t)batch * p->num_kv_heads * sizeof(unsigned), 256) +
+  return 2 * align_up((size_t)batch * p->num_kv_heads * sizeof(unsigned), 256) +
          (align_up(rows * 2, 64) + rows * p->head_dim) * sizeof(float) + 256;
 }
 

@@ -27,6 +27,7 @@ struct DecodeArgs {
   const int32_t *block_table;
   const int32_t *seq_lens;
   unsigned *counters;  // [batch][hkv]: workgroups done; zero between calls
+  int32_t *pend_nseg;  // [batch][hkv]: fused append + decode: row count to publish after the merge
   float *part_ml;   // [batch][hq][nparts][2]
   float *part_o;    // [batch][hq][nparts][D]
   float *out;       // [batch][hq][D]
@@ -147,11 +148,14 @@ typedef float v2f __attribute__((ext_vector_type(2)));
 
 // Merge the kWaves per-wave results of a workgroup (already in sh_o / sh_m / sh_l) into one
 // partial; with one workgroup per (sequence, kv head) write the output directly, otherwise publish
-// the partial and let the last workgroup of (b, h) merge all partials by log-sum-exp.
+// the partial and let the last workgroup of (b, h) merge all partials by log-sum-exp.  A
+// workgroup may also hand over one integer (pend >= 0) that the merging workgroup reads back.
+// Returns kWroteOutput (single workgroup), kMerged (this workgroup merged) or kPartialOnly.
+enum { kPartialOnly = 0, kWroteOutput = 1, kMerged = 2 };
 template <int D, int G>
-__device__ __forceinline__ void finish_partition(const DecodeArgs &a, int b, int h, int p, int L,
-                                                 float (&sh_o)[kWaves][G][D], float (&sh_m)[kWaves][G],
-                                                 float (&sh_l)[kWaves][G]) {
+__device__ __forceinline__ int finish_partition(const DecodeArgs &a, int b, int h, int p, int L,
+                                                float (&sh_o)[kWaves][G][D], float (&sh_m)[kWaves][G],
+                                                float (&sh_l)[kWaves][G], int pend = -1) {
   constexpr int NTH = 64 * kWaves;
   constexpr int NQ = D / 4;                          // float4 columns of a head's output
   static_assert(G * NQ <= NTH, "one float4 column per thread");
@@ -191,7 +195,9 @@ __device__ __forceinline__ void finish_partition(const DecodeArgs &a, int b, int
       }
     }
   }
-  if (P == 1) return;
+  if (P == 1) return kWroteOutput;
+  if (pend >= 0 && tid == 0)
+    __hip_atomic_store(a.pend_nseg + (size_t)b * a.hkv + h, pend, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
   // ---- the last workgroup of (b, h) to finish merges all partials by log-sum-exp ----
   // Publish: wait until this workgroup's device-scope stores have completed, then count it.
@@ -204,7 +210,7 @@ __device__ __forceinline__ void finish_partition(const DecodeArgs &a, int b, int
     sh_last = prev == (unsigned)(P - 1);
   }
   __syncthreads();
-  if (!sh_last) return;
+  if (!sh_last) return kPartialOnly;
 
   // Merge.  Thread (column, part) takes partitions part, part + SPLIT, ... of its head and
   // column; each round issues the (m, l) and output loads of KB partitions at once (device-scope
@@ -275,6 +281,7 @@ __device__ __forceinline__ void finish_partition(const DecodeArgs &a, int b, int
   }
   if (tid == 0)   // ready for the next call
     __hip_atomic_store(a.counters + (size_t)b * a.hkv + h, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return kMerged;
 }
 
 }  // namespace dgq

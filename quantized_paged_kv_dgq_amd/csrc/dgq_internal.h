@@ -76,6 +76,11 @@ dgq_status_t launch_compress(const dgq_params_t *p, const uint16_t *k, const uin
                              const dgq_cache_t *cache, void *ws, hipStream_t stream);
 
 // ---- append ----
+dgq_status_t launch_append_decode(const dgq_params_t *p, const uint16_t *k_tok, const uint16_t *v_tok,
+                                  const int32_t *seq_lens, const uint16_t *q, int32_t batch,
+                                  const int32_t *block_table, int32_t max_blocks, int32_t max_seq_len,
+                                  float softmax_scale, const dgq_cache_t *cache, float *out, void *ws,
+                                  hipStream_t stream);
 dgq_status_t launch_append(const dgq_params_t *p, const uint16_t *k_tok, const uint16_t *v_tok,
                            const int32_t *seq_lens, int32_t batch, const int32_t *block_table,
                            int32_t max_blocks, const dgq_cache_t *cache, hipStream_t stream);
