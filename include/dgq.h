@@ -103,16 +103,17 @@ typedef struct dgq_seg {
   int32_t reserved;
 } dgq_seg_t;
 
-/* Append state of one (sequence, kv head), 208 bytes; written by dgq_compress, advanced by
+/* Append state of one (sequence, kv head), 224 bytes; written by dgq_compress, advanced by
  * dgq_append.  The open span is [r0, length): tokens appended since the tail block was last
  * sealed.  The ring holds the fixed-point moments of the 16 sealed tokens before r0. */
 typedef struct dgq_tail {
   int32_t r0;
   int32_t ring_len;      /* 0..16 */
   int32_t span_own;      /* 1 if the open span has its own segment-table row */
-  int32_t reserved;
+  int32_t window_done;   /* 1 once the span's first-16-token window test came out "no change" */
   int32_t ring_a[16];    /* oldest first */
   int64_t ring_b[16];
+  float span_range[4];   /* K min, K max, V min, V max of the open span (valid while it is not empty) */
 } dgq_tail_t;
 
 /* The compressed cache of one layer: caller-owned device buffers. */

@@ -46,9 +46,10 @@ class Tail(ctypes.Structure):
         ("r0", ctypes.c_int32),
         ("ring_len", ctypes.c_int32),
         ("span_own", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("window_done", ctypes.c_int32),
         ("ring_a", ctypes.c_int32 * 16),
         ("ring_b", ctypes.c_int64 * 16),
+        ("span_range", ctypes.c_float * 4),
     ]
 
 
@@ -84,7 +85,7 @@ DGQ_POLICY_LENGTH_AWARE = 1
 
 assert ctypes.sizeof(Params) == 48
 assert ctypes.sizeof(Seg) == 32
-assert ctypes.sizeof(Tail) == 208
+assert ctypes.sizeof(Tail) == 224
 
 # Every symbol include/dgq.h declares.
 EXPORTS = [

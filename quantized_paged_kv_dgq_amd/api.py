@@ -71,7 +71,7 @@ class DGQCache:
         self.bits = torch.zeros((num_blocks, p.num_kv_heads, p.block_size // 8), dtype=torch.uint8, device=dev)
         self.segs = torch.zeros((batch, p.num_kv_heads, p.seg_capacity, 8), dtype=torch.int32, device=dev)
         self.nseg = torch.zeros((batch, p.num_kv_heads), dtype=torch.int32, device=dev)
-        self.tail = torch.zeros((batch, p.num_kv_heads, 52), dtype=torch.int32, device=dev)
+        self.tail = torch.zeros((batch, p.num_kv_heads, 56), dtype=torch.int32, device=dev)
         self.k_stage = torch.zeros((batch, p.num_kv_heads, p.block_size, p.head_dim), dtype=torch.float16, device=dev)
         self.v_stage = torch.zeros_like(self.k_stage)
         self.status = torch.zeros(4, dtype=torch.int64, device=dev)

@@ -53,6 +53,7 @@ __device__ __forceinline__ void append_one(const AppendArgs &a, int b, int h, bo
   __shared__ long long tail_a[kWin];
   __shared__ long long tail_b[kWin];
   __shared__ dgq_seg_t chosen;
+  __shared__ int reenc_all;                    // 1: every span token's codes change, 0: only the new one
   if (tid == 0) {
     tl = a.cache.tail[bh];
     ns_sh = a.cache.nseg[bh];
@@ -80,30 +81,24 @@ __device__ __forceinline__ void append_one(const AppendArgs &a, int b, int h, bo
   uint16_t *ks = a.cache.k_stage + bh * (size_t)BS * D;
   uint16_t *vs = a.cache.v_stage + bh * (size_t)BS * D;
 
-  // 1. stage the new token
+  // 1. stage the new token, and take its ranges (and a non-finite check) on the way
   const int slot = t % BS;
-  for (int d = tid; d < D; d += 256) {
-    ks[slot * D + d] = a.k_tok[bh * D + d];
-    vs[slot * D + d] = a.v_tok[bh * D + d];
-  }
-  __syncthreads();
-
-  // 2. span ranges (and a non-finite check of the new token)
   float4 r = make_float4(INFINITY, -INFINITY, INFINITY, -INFINITY);
   float bad = 0.f;
-  for (int x = tid; x < span_len * D; x += 256) {
-    const int s = slot0 + x / D, d = x % D;
-    const float kx = half_bits_to_float(ks[s * D + d]);
-    const float vx = half_bits_to_float(vs[s * D + d]);
+  for (int d = tid; d < D; d += 256) {
+    const uint16_t kb = a.k_tok[bh * D + d], vb = a.v_tok[bh * D + d];
+    ks[slot * D + d] = kb;
+    vs[slot * D + d] = vb;
+    const float kx = half_bits_to_float(kb), vx = half_bits_to_float(vb);
     r.x = fminf(r.x, kx);
     r.y = fmaxf(r.y, kx);
     r.z = fminf(r.z, vx);
     r.w = fmaxf(r.w, vx);
-    if (s == slot) {
-      bad = fmaf(kx, 0.f, bad);
-      bad = fmaf(vx, 0.f, bad);
-    }
+    bad = fmaf(kx, 0.f, bad);
+    bad = fmaf(vx, 0.f, bad);
   }
+
+  // 2. span ranges: the stored range of the earlier span tokens, widened by the new token
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
     r.x = fminf(r.x, __shfl_xor(r.x, o));
@@ -125,14 +120,21 @@ __device__ __forceinline__ void append_one(const AppendArgs &a, int b, int h, bo
       q.z = fminf(q.z, red4[w].z);
       q.w = fmaxf(q.w, red4[w].w);
     }
+    if (span_len > 1) {
+      q.x = fminf(q.x, tl.span_range[0]);
+      q.y = fmaxf(q.y, tl.span_range[1]);
+      q.z = fminf(q.z, tl.span_range[2]);
+      q.w = fmaxf(q.w, tl.span_range[3]);
+    }
     rk[0] = q.x + 0.0f;
     rk[1] = q.y + 0.0f;
     rk[2] = q.z + 0.0f;
     rk[3] = q.w + 0.0f;
   }
 
-  // 3. window statistics of the span's first 16 tokens (only needed once it has 16)
-  const bool window_test = span_len >= kWin && tl.ring_len == kWin && !tl.span_own;
+  // 3. window statistics of the span's first 16 tokens: needed once the span has 16 tokens, and
+  // only until the test has said "no change" (the window and the ring stay fixed for the span)
+  const bool window_test = span_len >= kWin && tl.ring_len == kWin && !tl.span_own && !tl.window_done;
   if (window_test) {
     // moments of span token i (i < 16): wave w handles tokens 4w..4w+3, 16 lanes each
     const int w = tid >> 6, lane = tid & 63;
@@ -177,9 +179,11 @@ __device__ __forceinline__ void append_one(const AppendArgs &a, int b, int h, bo
         const long long ql = nel * lb - la * la, qr = nel * rb - ra * ra;
         const long long hi = ql > qr ? ql : qr, lo = ql > qr ? qr : ql;
         want = !((double)hi < a.qfloor) && (double)(hi + 1) / (double)(lo + 1) >= a.tau;
+        if (!want) tl.window_done = 1;
       }
     }
     int clampv = 0;
+    int all = 0;
     if (want && !tl.span_own) {
       if (ns >= a.seg_cap) {
         clampv = 1;
@@ -197,6 +201,7 @@ __device__ __forceinline__ void append_one(const AppendArgs &a, int b, int h, bo
         a.cache.segs[bh * a.seg_cap + ns] = row;
         ns += 1;
         tl.span_own = 1;
+        all = 1;                                 // the span moves to its own range
         if (r0 > 0) {
           const int blk = a.block_table[(size_t)b * a.max_blocks + r0 / BS];
           uint8_t *byte = a.cache.bits + ((size_t)blk * a.hkv + h) * (BS / 8) + (r0 % BS) / 8;
@@ -205,6 +210,7 @@ __device__ __forceinline__ void append_one(const AppendArgs &a, int b, int h, bo
       }
     } else if (want && tl.span_own) {
       dgq_seg_t row = a.cache.segs[bh * a.seg_cap + ns - 1];
+      all = row.kmin != rk[0] || row.kmax != rk[1] || row.vmin != rk[2] || row.vmax != rk[3];
       row.kmin = rk[0];
       row.kmax = rk[1];
       row.vmin = rk[2];
@@ -222,19 +228,22 @@ __device__ __forceinline__ void append_one(const AppendArgs &a, int b, int h, bo
     out.chosen = chosen;
     own_now = tl.span_own;
     clamp_now = clampv;
+    reenc_all = all;
     if (clampv) atomicAdd(a.cache.status + 0, 1ull);
   }
   __syncthreads();
 
-  // 5. re-encode the span with the chosen segment's range
+  // 5. encode with the chosen segment's range: the whole span when that range changed (a new row,
+  // or the span's own row widened), else only the new token (every other span code is unchanged)
   const dgq_seg_t row = chosen;
   const float kinv = dgq_inv(row.kmin, row.kmax), vinv = dgq_inv(row.vmin, row.vmax);
   const int32_t *bt = a.block_table + (size_t)b * a.max_blocks;
   const int blk = bt[r0 / BS];
   int8_t *kt = a.cache.k_pool + ((size_t)blk * a.hkv + h) * (size_t)BS * D;
   int8_t *vt = a.cache.v_pool + ((size_t)blk * a.hkv + h) * (size_t)BS * D;
-  for (int x = tid; x < span_len * D; x += 256) {
-    const int s = slot0 + x / D, d = x % D;
+  const int enc_first = reenc_all ? 0 : span_len - 1;
+  for (int x = tid; x < (span_len - enc_first) * D; x += 256) {
+    const int s = slot0 + enc_first + x / D, d = x % D;
     const float kx = half_bits_to_float(ks[s * D + d]);
     const float vx = half_bits_to_float(vs[s * D + d]);
     kt[k_tile_offset<D, BS>(s, d)] = (int8_t)dgq_encode_value(kx, row.kmin, kinv);
@@ -294,8 +303,10 @@ __device__ __forceinline__ void append_one(const AppendArgs &a, int b, int h, bo
       tl.ring_len = n;
       tl.r0 = t + 1;
       tl.span_own = 0;
+      tl.window_done = 0;
     } else {
       tl.span_own = own_now;
+      for (int i = 0; i < 4; ++i) tl.span_range[i] = rk[i];
     }
     (void)clamp_now;
     a.cache.tail[bh] = tl;

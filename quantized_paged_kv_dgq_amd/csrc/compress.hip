@@ -386,7 +386,8 @@ __global__ __launch_bounds__(256) void select_kernel(CompressArgs a) {
     const int rl = min(kWin, L);
     tl.ring_len = rl;
     tl.span_own = 0;
-    tl.reserved = 0;
+    tl.window_done = 0;
+    for (int i = 0; i < 4; ++i) tl.span_range[i] = 0.f;
     for (int i = 0; i < kWin; ++i) {
       if (i < rl) {
         const size_t idx = (size_t)h * a.total + c0 + (L - rl + i);
@@ -736,7 +737,7 @@ __global__ __launch_bounds__(kSmallThreads) void select_small_kernel(CompressArg
     tl->r0 = L;
     tl->ring_len = rl;
     tl->span_own = 0;
-    tl->reserved = 0;
+    tl->window_done = 0;
   }
 }
 
