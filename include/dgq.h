@@ -14,7 +14,8 @@
  *                         free list; block-granular allocation; paged forward pass with
  *                         block_tables; 64-token blocks for long contexts.
  *   Quantization article  http://cnnetsun.cn/a/2561798 -- section 2.1 asymmetric quantization
- *                         template clamp(round(x / scale) + zero_point, lo, hi).
+ *                         template clamp(round(x / scale) + zero_point, lo, hi); section 3.2
+ *                         page-table entries with a reference count (shared physical pages).
  *
  * Conventions for every entry point
  *   - Device pointers are caller-owned HIP device memory; the library never allocates or frees
@@ -155,11 +156,71 @@ dgq_status_t dgq_pool_destroy(void *pool);
 /* Take n ids into ids (host, n entries).  All or nothing: DGQ_ERR_POOL_EXHAUSTED leaves the pool
  * unchanged.  Ids come from the free list in last-freed-first order. */
 dgq_status_t dgq_block_alloc(void *pool, int32_t n, int32_t *ids);
-/* Return n ids (host).  DGQ_ERR_INVALID_ARG, with the pool unchanged, if any id is out of range,
- * already free, or repeated in the list. */
+/* Drop one reference per entry of ids (host, n entries); a block whose count reaches 0 goes back
+ * on the free list.  An id may be listed as often as it has references.  DGQ_ERR_INVALID_ARG,
+ * with the pool unchanged, if any id is out of range or listed more often than its count. */
 dgq_status_t dgq_block_free(void *pool, int32_t n, const int32_t *ids);
 /* Number of free ids, or -1 for a NULL pool. */
 int32_t dgq_pool_num_free(const void *pool);
+
+/* ---- Block lifecycle: shared blocks, copy-on-write, swap (Quantization article, section 3.2:
+ * reference-counted page-table entries; DGQ article, section 3.1: the cache engine's swap in/out
+ * works on compressed blocks).  A compressed block carries its INT8 codes and its boundary bits;
+ * a sequence's segment table, row count, append state and staging live in its cache row.  Blocks
+ * before the tail block are frozen (dgq_append never writes them), so they can be shared by
+ * several sequences; the tail block is written by every append and must be owned by one. ---- */
+
+/* Add one reference per entry of ids (host, n entries), e.g. when a forked sequence's block table
+ * takes the parent's blocks.  DGQ_ERR_INVALID_ARG, with the pool unchanged, if any id is out of
+ * range or free. */
+dgq_status_t dgq_block_share(void *pool, int32_t n, const int32_t *ids);
+/* References of one block: 0 if free, -1 for a NULL pool or an id out of range. */
+int32_t dgq_block_refcount(const void *pool, int32_t id);
+/* Copy-on-write for a list of blocks about to be written (host, n entries each).  Entries are
+ * served in order: a block with one reference is kept (out_ids[i] = ids[i]); a block with more
+ * takes a fresh block (out_ids[i], one reference) and drops one reference of ids[i].  The caller
+ * then copies every changed pair with dgq_copy_blocks and writes out_ids into its block table.
+ * All or nothing: DGQ_ERR_POOL_EXHAUSTED or DGQ_ERR_INVALID_ARG (an id out of range or free)
+ * leave the pool unchanged. */
+dgq_status_t dgq_block_cow(void *pool, int32_t n, const int32_t *ids, int32_t *out_ids);
+
+/* Copy whole compressed blocks of one layer: for i < n, the K and V codes of every kv head and the
+ * boundary bits of block src_ids[i] are copied to block dst_ids[i].
+ *   src_ids, dst_ids (device) int32 [n].  A dst id must not appear twice nor among the src ids
+ *   (the copies run in parallel).  A pair with an id outside [0, num_blocks) is skipped and
+ *   counted in status[2].  n == 0 queues nothing. */
+dgq_status_t dgq_copy_blocks(const dgq_params_t *p, const dgq_cache_t *cache, const int32_t *src_ids,
+                             const int32_t *dst_ids, int32_t n, hipStream_t stream);
+/* Copy the per-sequence state of one layer from cache row src_rows[i] to row dst_rows[i], i < n:
+ * segment-table rows, row count, append state and the fp16 staging of the open span, for every
+ * kv head.  With dgq_block_share on the block table and dgq_block_cow + dgq_copy_blocks on the
+ * tail block before the next append, this forks a sequence.
+ *   src_rows, dst_rows (device) int32 [n]; the same rules as dgq_copy_blocks' ids, against
+ *   [0, cache->batch).  The cache must have its staging buffers. */
+dgq_status_t dgq_copy_seq_state(const dgq_params_t *p, const dgq_cache_t *cache,
+                                const int32_t *src_rows, const int32_t *dst_rows, int32_t n,
+                                hipStream_t stream);
+
+/* Bytes of the swap image of one sequence with n_blocks blocks (one layer): the cache row's state
+ * (segment-table rows, row counts, append state, staging), then per block its K codes, V codes
+ * and bits, each part padded to 16 bytes.  0 for invalid arguments. */
+size_t dgq_swap_image_bytes(const dgq_params_t *p, int32_t n_blocks);
+/* Swap out one sequence of one layer: its cache row `row` (host int) and blocks ids[0..n_blocks)
+ * (device int32, in logical order) are packed into `staging` (device, >= dgq_swap_image_bytes,
+ * 16-byte aligned); then, if host_dst is not NULL, the image is copied to host_dst (host memory
+ * of the same size, pinned for the copy to be asynchronous) on the same stream.  The cache is not
+ * modified; the caller frees the blocks once the copy has completed.  Block ids outside the pool
+ * are skipped (their part of the image is left as is) and counted in status[2]. */
+dgq_status_t dgq_swap_out(const dgq_params_t *p, const dgq_cache_t *cache, int32_t row,
+                          const int32_t *ids, int32_t n_blocks, void *staging, size_t staging_bytes,
+                          void *host_dst, hipStream_t stream);
+/* Swap in: the inverse.  If host_src is not NULL the image is first copied from host_src to
+ * `staging`; then the state is written to cache row `row` and the blocks to ids[0..n_blocks)
+ * (device int32, freshly allocated by the caller; any ids: the codes do not depend on where a
+ * block lives).  The sequence then decodes and appends exactly as before it was swapped out. */
+dgq_status_t dgq_swap_in(const dgq_params_t *p, const dgq_cache_t *cache, int32_t row,
+                         const int32_t *ids, int32_t n_blocks, void *staging, size_t staging_bytes,
+                         const void *host_src, hipStream_t stream);
 
 /* ---- Workspace sizes (bytes; 0 for invalid arguments) ---- */
 

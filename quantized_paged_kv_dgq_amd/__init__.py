@@ -16,8 +16,13 @@ from .api import (  # noqa: F401
     dgq_append,
     dgq_append_decode,
     dgq_compress,
+    dgq_copy_blocks,
+    dgq_copy_seq_state,
+    dgq_swap_in,
+    dgq_swap_out,
     dgq_g64_quantize,
     paged_decode_attn_g64,
     paged_decode_attn_int8,
+    swap_image_bytes,
     workspace,
 )

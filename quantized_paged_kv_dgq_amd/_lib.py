@@ -91,6 +91,8 @@ assert ctypes.sizeof(Tail) == 224
 EXPORTS = [
     "dgq_status_string", "dgq_last_error",
     "dgq_pool_create", "dgq_pool_destroy", "dgq_block_alloc", "dgq_block_free", "dgq_pool_num_free",
+    "dgq_block_share", "dgq_block_refcount", "dgq_block_cow",
+    "dgq_copy_blocks", "dgq_copy_seq_state", "dgq_swap_image_bytes", "dgq_swap_out", "dgq_swap_in",
     "dgq_compress_workspace_size", "dgq_decode_workspace_size",
     "dgq_compress", "dgq_append", "paged_decode_attn_int8", "dgq_append_decode",
     "dgq_g64_quantize", "paged_decode_attn_g64",
@@ -123,6 +125,22 @@ def load() -> ctypes.CDLL:
     lib.dgq_block_free.restype = i32
     lib.dgq_pool_num_free.argtypes = [vp]
     lib.dgq_pool_num_free.restype = i32
+    lib.dgq_block_share.argtypes = [vp, i32, P(i32)]
+    lib.dgq_block_share.restype = i32
+    lib.dgq_block_refcount.argtypes = [vp, i32]
+    lib.dgq_block_refcount.restype = i32
+    lib.dgq_block_cow.argtypes = [vp, i32, P(i32), P(i32)]
+    lib.dgq_block_cow.restype = i32
+    lib.dgq_copy_blocks.argtypes = [P(Params), P(Cache), vp, vp, i32, vp]
+    lib.dgq_copy_blocks.restype = i32
+    lib.dgq_copy_seq_state.argtypes = [P(Params), P(Cache), vp, vp, i32, vp]
+    lib.dgq_copy_seq_state.restype = i32
+    lib.dgq_swap_image_bytes.argtypes = [P(Params), i32]
+    lib.dgq_swap_image_bytes.restype = sz
+    lib.dgq_swap_out.argtypes = [P(Params), P(Cache), i32, vp, i32, vp, sz, vp, vp]
+    lib.dgq_swap_out.restype = i32
+    lib.dgq_swap_in.argtypes = [P(Params), P(Cache), i32, vp, i32, vp, sz, vp, vp]
+    lib.dgq_swap_in.restype = i32
     lib.dgq_compress_workspace_size.argtypes = [P(Params), i32, i64, i32]
     lib.dgq_compress_workspace_size.restype = sz
     lib.dgq_decode_workspace_size.argtypes = [P(Params), i32, i32]

@@ -120,8 +120,25 @@ class BlockPool:
         return list(ids[:n])
 
     def free(self, ids: Sequence[int]) -> None:
+        """Drop one reference per listed id (dgq_block_free)."""
         arr = (ctypes.c_int32 * max(len(ids), 1))(*ids)
         check(_lib.load().dgq_block_free(self._h, len(ids), arr), "dgq_block_free")
+
+    def share(self, ids: Sequence[int]) -> None:
+        """Add one reference per listed id (dgq_block_share)."""
+        arr = (ctypes.c_int32 * max(len(ids), 1))(*ids)
+        check(_lib.load().dgq_block_share(self._h, len(ids), arr), "dgq_block_share")
+
+    def refcount(self, block_id: int) -> int:
+        return _lib.load().dgq_block_refcount(self._h, block_id)
+
+    def cow(self, ids: Sequence[int]) -> list:
+        """Exclusive ids for blocks about to be written (dgq_block_cow): a changed entry names a
+        fresh block that must receive a copy of the listed one."""
+        arr = (ctypes.c_int32 * max(len(ids), 1))(*ids)
+        out = (ctypes.c_int32 * max(len(ids), 1))()
+        check(_lib.load().dgq_block_cow(self._h, len(ids), arr, out), "dgq_block_cow")
+        return list(out[:len(ids)])
 
     @property
     def num_free(self) -> int:
@@ -226,6 +243,57 @@ def dgq_append_decode(params: DGQParams, k_tok: torch.Tensor, v_tok: torch.Tenso
         ws.numel(), _stream(stream))
     check(st, "dgq_append_decode")
     return out
+
+
+def _ids(t: torch.Tensor, what: str) -> torch.Tensor:
+    _need(t.dtype == torch.int32 and t.is_contiguous() and t.dim() == 1, f"{what}: contiguous int32 vector")
+    return t
+
+
+def dgq_copy_blocks(params: DGQParams, cache: DGQCache, src_ids: torch.Tensor, dst_ids: torch.Tensor,
+                    stream=None) -> None:
+    """Copy whole compressed blocks src_ids[i] -> dst_ids[i] (device int32 vectors)."""
+    _need(src_ids.numel() == dst_ids.numel(), "src_ids and dst_ids differ in length")
+    st = _lib.load().dgq_copy_blocks(ctypes.byref(params.c), ctypes.byref(cache.c), _ptr(_ids(src_ids, "src_ids")),
+                                     _ptr(_ids(dst_ids, "dst_ids")), src_ids.numel(), _stream(stream))
+    check(st, "dgq_copy_blocks")
+
+
+def dgq_copy_seq_state(params: DGQParams, cache: DGQCache, src_rows: torch.Tensor, dst_rows: torch.Tensor,
+                       stream=None) -> None:
+    """Copy cache rows src_rows[i] -> dst_rows[i] (segment table, row count, append state, staging)."""
+    _need(src_rows.numel() == dst_rows.numel(), "src_rows and dst_rows differ in length")
+    st = _lib.load().dgq_copy_seq_state(ctypes.byref(params.c), ctypes.byref(cache.c),
+                                        _ptr(_ids(src_rows, "src_rows")), _ptr(_ids(dst_rows, "dst_rows")),
+                                        src_rows.numel(), _stream(stream))
+    check(st, "dgq_copy_seq_state")
+
+
+def swap_image_bytes(params: DGQParams, n_blocks: int) -> int:
+    return int(_lib.load().dgq_swap_image_bytes(ctypes.byref(params.c), n_blocks))
+
+
+def dgq_swap_out(params: DGQParams, cache: DGQCache, row: int, ids: torch.Tensor, staging: torch.Tensor,
+                 host: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Pack cache row `row` and blocks ids (device int32, logical order) into staging (device
+    uint8), then copy it to `host` (pinned uint8) when given."""
+    _need(staging.dtype == torch.uint8 and staging.is_contiguous(), "staging: contiguous uint8")
+    _need(host is None or (host.dtype == torch.uint8 and host.is_contiguous() and host.numel() >= staging.numel()),
+          "host: contiguous uint8 at least as large as staging")
+    st = _lib.load().dgq_swap_out(ctypes.byref(params.c), ctypes.byref(cache.c), row, _ptr(_ids(ids, "ids")),
+                                  ids.numel(), _ptr(staging), staging.numel(), _ptr(host), _stream(stream))
+    check(st, "dgq_swap_out")
+
+
+def dgq_swap_in(params: DGQParams, cache: DGQCache, row: int, ids: torch.Tensor, staging: torch.Tensor,
+                host: Optional[torch.Tensor] = None, stream=None) -> None:
+    """The inverse of dgq_swap_out: (host ->) staging -> cache row `row` and blocks ids."""
+    _need(staging.dtype == torch.uint8 and staging.is_contiguous(), "staging: contiguous uint8")
+    _need(host is None or (host.dtype == torch.uint8 and host.is_contiguous() and host.numel() >= staging.numel()),
+          "host: contiguous uint8 at least as large as staging")
+    st = _lib.load().dgq_swap_in(ctypes.byref(params.c), ctypes.byref(cache.c), row, _ptr(_ids(ids, "ids")),
+                                 ids.numel(), _ptr(staging), staging.numel(), _ptr(host), _stream(stream))
+    check(st, "dgq_swap_in")
 
 
 def dgq_g64_quantize(params: DGQParams, k: torch.Tensor, v: torch.Tensor, cu_seqlens: torch.Tensor,

@@ -5,6 +5,7 @@
 #include <cstring>
 
 #include "dgq_internal.h"
+#include "lifecycle.h"
 
 namespace dgq {
 
@@ -164,6 +165,64 @@ extern "C" dgq_status_t dgq_append_decode(const dgq_params_t *p, const uint16_t 
   if (ws_bytes < need) return DGQ_ERR_WORKSPACE_TOO_SMALL;
   return launch_append_decode(p, k_tok, v_tok, seq_lens, q, batch, block_table, max_blocks, max_seq_len,
                               softmax_scale, cache, out, ws, stream);
+}
+
+extern "C" dgq_status_t dgq_copy_blocks(const dgq_params_t *p, const dgq_cache_t *cache,
+                                        const int32_t *src_ids, const int32_t *dst_ids, int32_t n,
+                                        hipStream_t stream) {
+  dgq_status_t st = check_params(p);
+  if (st != DGQ_OK) return st;
+  if (n < 0) return DGQ_ERR_INVALID_ARG;
+  if (n == 0) return DGQ_OK;
+  if (!src_ids || !dst_ids) return DGQ_ERR_INVALID_ARG;
+  if ((st = check_cache(cache, 0, false)) != DGQ_OK) return st;
+  return launch_copy_blocks(p, cache, src_ids, dst_ids, n, stream);
+}
+
+extern "C" dgq_status_t dgq_copy_seq_state(const dgq_params_t *p, const dgq_cache_t *cache,
+                                           const int32_t *src_rows, const int32_t *dst_rows, int32_t n,
+                                           hipStream_t stream) {
+  dgq_status_t st = check_params(p);
+  if (st != DGQ_OK) return st;
+  if (n < 0) return DGQ_ERR_INVALID_ARG;
+  if (n == 0) return DGQ_OK;
+  if (!src_rows || !dst_rows) return DGQ_ERR_INVALID_ARG;
+  if ((st = check_cache(cache, 0, true)) != DGQ_OK) return st;
+  return launch_copy_seq_state(p, cache, src_rows, dst_rows, n, stream);
+}
+
+extern "C" size_t dgq_swap_image_bytes(const dgq_params_t *p, int32_t n_blocks) {
+  if (check_params(p) != DGQ_OK || n_blocks < 0) return 0;
+  return swap_image_bytes(p, n_blocks);
+}
+
+static dgq_status_t check_swap(const dgq_params_t *p, const dgq_cache_t *cache, int32_t row,
+                               const int32_t *ids, int32_t n_blocks, const void *staging,
+                               size_t staging_bytes) {
+  dgq_status_t st = check_params(p);
+  if (st != DGQ_OK) return st;
+  if ((st = check_cache(cache, 0, true)) != DGQ_OK) return st;
+  if (row < 0 || row >= cache->batch || n_blocks < 0 || (n_blocks > 0 && ids == nullptr))
+    return DGQ_ERR_INVALID_ARG;
+  if (staging == nullptr || !aligned(staging, 16)) return DGQ_ERR_INVALID_ARG;
+  if (staging_bytes < swap_image_bytes(p, n_blocks)) return DGQ_ERR_WORKSPACE_TOO_SMALL;
+  return DGQ_OK;
+}
+
+extern "C" dgq_status_t dgq_swap_out(const dgq_params_t *p, const dgq_cache_t *cache, int32_t row,
+                                     const int32_t *ids, int32_t n_blocks, void *staging,
+                                     size_t staging_bytes, void *host_dst, hipStream_t stream) {
+  const dgq_status_t st = check_swap(p, cache, row, ids, n_blocks, staging, staging_bytes);
+  if (st != DGQ_OK) return st;
+  return launch_swap(p, cache, row, ids, n_blocks, staging, host_dst, true, stream);
+}
+
+extern "C" dgq_status_t dgq_swap_in(const dgq_params_t *p, const dgq_cache_t *cache, int32_t row,
+                                    const int32_t *ids, int32_t n_blocks, void *staging,
+                                    size_t staging_bytes, const void *host_src, hipStream_t stream) {
+  const dgq_status_t st = check_swap(p, cache, row, ids, n_blocks, staging, staging_bytes);
+  if (st != DGQ_OK) return st;
+  return launch_swap(p, cache, row, ids, n_blocks, staging, const_cast<void *>(host_src), false, stream);
 }
 
 static dgq_status_t check_g64_cache(const dgq_g64_cache_t *c) {

@@ -128,3 +128,94 @@ def test_argument_checks_queue_nothing(lib):
                           None) == _lib.DGQ_ERR_INVALID_ARG
     # an empty batch is a no-op
     assert lib.dgq_append(ctypes.byref(p), None, None, None, 0, None, 0, None, None) == 0
+
+
+def _arr(*v):
+    return (ctypes.c_int32 * max(len(v), 1))(*v)
+
+
+def test_pool_reference_counts(lib):
+    """Shared blocks: a block goes back on the free list when its last reference is dropped."""
+    h = ctypes.c_void_p()
+    assert lib.dgq_pool_create(6, ctypes.byref(h)) == 0
+    ids = (ctypes.c_int32 * 6)()
+    assert lib.dgq_block_alloc(h, 3, ids) == 0 and list(ids[:3]) == [0, 1, 2]
+    assert [lib.dgq_block_refcount(h, i) for i in range(6)] == [1, 1, 1, 0, 0, 0]
+    assert lib.dgq_block_share(h, 3, _arr(0, 1, 1)) == 0
+    assert [lib.dgq_block_refcount(h, i) for i in range(3)] == [2, 3, 1]
+    # sharing a free or out-of-range block fails and changes nothing
+    assert lib.dgq_block_share(h, 2, _arr(0, 4)) == _lib.DGQ_ERR_INVALID_ARG
+    assert lib.dgq_block_share(h, 1, _arr(-1)) == _lib.DGQ_ERR_INVALID_ARG
+    assert [lib.dgq_block_refcount(h, i) for i in range(3)] == [2, 3, 1]
+    # one reference per listed entry; more entries than references is rejected as a whole
+    assert lib.dgq_block_free(h, 4, _arr(1, 1, 1, 1)) == _lib.DGQ_ERR_INVALID_ARG
+    assert lib.dgq_block_free(h, 2, _arr(1, 1)) == 0
+    assert lib.dgq_block_refcount(h, 1) == 1 and lib.dgq_pool_num_free(h) == 3
+    assert lib.dgq_block_free(h, 1, _arr(1)) == 0
+    assert lib.dgq_block_refcount(h, 1) == 0 and lib.dgq_pool_num_free(h) == 4
+    assert lib.dgq_block_refcount(h, 6) == -1 and lib.dgq_block_refcount(None, 0) == -1
+    assert lib.dgq_pool_destroy(h) == 0
+
+
+def test_pool_copy_on_write(lib):
+    h = ctypes.c_void_p()
+    assert lib.dgq_pool_create(4, ctypes.byref(h)) == 0
+    ids = (ctypes.c_int32 * 4)()
+    assert lib.dgq_block_alloc(h, 2, ids) == 0             # 0, 1
+    assert lib.dgq_block_share(h, 2, _arr(0, 0)) == 0      # block 0: three owners
+    out = (ctypes.c_int32 * 4)()
+    # entries in order: the first two owners of block 0 get fresh blocks, the last keeps it;
+    # block 1 has one owner and is kept
+    assert lib.dgq_block_cow(h, 4, _arr(0, 1, 0, 0), out) == 0
+    assert list(out) == [2, 1, 3, 0]
+    assert [lib.dgq_block_refcount(h, i) for i in range(4)] == [1, 1, 1, 1]
+    assert lib.dgq_pool_num_free(h) == 0
+    # a copy that needs a block from an empty pool changes nothing
+    assert lib.dgq_block_share(h, 1, _arr(3)) == 0
+    assert lib.dgq_block_cow(h, 2, _arr(1, 3), out) == _lib.DGQ_ERR_POOL_EXHAUSTED
+    assert lib.dgq_block_refcount(h, 3) == 2
+    # a free block cannot be written through copy-on-write
+    assert lib.dgq_block_free(h, 1, _arr(2)) == 0
+    assert lib.dgq_block_cow(h, 1, _arr(2), out) == _lib.DGQ_ERR_INVALID_ARG
+    assert lib.dgq_block_cow(h, 1, _arr(3), out) == 0 and out[0] == 2
+    assert lib.dgq_block_refcount(h, 3) == 1 and lib.dgq_block_refcount(h, 2) == 1
+    assert lib.dgq_pool_destroy(h) == 0
+
+
+def test_swap_image_bytes(lib):
+    """State (segment rows, row counts, append states, K and V staging) then per block K codes,
+    V codes and bits, each padded to 16 bytes."""
+    for hkv, d, bs, cap in ((8, 128, 64, 16), (2, 64, 16, 5), (3, 64, 16, 7)):
+        p = _params(num_kv_heads=hkv, num_q_heads=hkv, head_dim=d, block_size=bs, seg_capacity=cap,
+                    max_segments=5)
+        pad = lambda x: (x + 15) // 16 * 16
+        state = pad(hkv * cap * 32) + pad(hkv * 4) + pad(hkv * 224) + 2 * pad(hkv * bs * d * 2)
+        block = 2 * pad(hkv * bs * d) + pad(hkv * bs // 8)
+        for n in (0, 1, 37):
+            assert lib.dgq_swap_image_bytes(ctypes.byref(p), n) == state + n * block
+    assert lib.dgq_swap_image_bytes(ctypes.byref(_params()), -1) == 0
+    assert lib.dgq_swap_image_bytes(ctypes.byref(_params(head_dim=96)), 1) == 0
+
+
+def test_lifecycle_argument_checks(lib):
+    p = _params()
+    fake = ctypes.c_void_p(1 << 20)
+    cache = _lib.Cache(fake, fake, fake, fake, fake, fake, fake, fake, fake, 64, 4)
+    nostage = _lib.Cache(fake, fake, fake, fake, fake, fake, None, None, fake, 64, 4)
+    need = lib.dgq_swap_image_bytes(ctypes.byref(p), 3)
+    E = _lib.DGQ_ERR_INVALID_ARG
+    assert lib.dgq_copy_blocks(ctypes.byref(p), ctypes.byref(cache), fake, fake, 0, None) == 0
+    assert lib.dgq_copy_blocks(ctypes.byref(p), ctypes.byref(cache), None, fake, 2, None) == E
+    assert lib.dgq_copy_blocks(ctypes.byref(p), ctypes.byref(cache), fake, fake, -1, None) == E
+    assert lib.dgq_copy_seq_state(ctypes.byref(p), ctypes.byref(nostage), fake, fake, 1, None) == E
+    assert lib.dgq_copy_seq_state(ctypes.byref(_params(block_size=32)), ctypes.byref(cache), fake, fake, 1,
+                                  None) == _lib.DGQ_ERR_UNSUPPORTED
+    for row in (-1, 4):
+        assert lib.dgq_swap_out(ctypes.byref(p), ctypes.byref(cache), row, fake, 3, fake, need, None, None) == E
+        assert lib.dgq_swap_in(ctypes.byref(p), ctypes.byref(cache), row, fake, 3, fake, need, None, None) == E
+    assert lib.dgq_swap_out(ctypes.byref(p), ctypes.byref(cache), 0, fake, 3, fake, need - 16, None,
+                            None) == _lib.DGQ_ERR_WORKSPACE_TOO_SMALL
+    assert lib.dgq_swap_in(ctypes.byref(p), ctypes.byref(cache), 0, None, 3, fake, need, None, None) == E
+    assert lib.dgq_swap_in(ctypes.byref(p), ctypes.byref(cache), 0, fake, 3, ctypes.c_void_p((1 << 20) + 8),
+                           need, None, None) == E
+    assert lib.dgq_swap_out(ctypes.byref(p), ctypes.byref(nostage), 0, fake, 3, fake, need, None, None) == E
