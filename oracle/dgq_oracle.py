@@ -54,6 +54,17 @@ R12 Segment-count policies, both off by default.  Length-aware cap (DGQ article 
     (over the window's 16 x head_dim values, on the fixed-point grid) below min_var, i.e. when
     max(Q_left, Q_right) < min_var * N^2 * 512^2; the append window test obeys the same floor.
     (parity unpinned: "both windows below" is our reading of the floor)
+R13 Marker format (DGQ article 3.2, the variant that keeps the segment identifier inside the
+    INT8 data instead of a separate bit tensor by leaving the two end byte values unused).  Data
+    codes take 254 levels: c = clamp(rint(fp32(fp32(x - min) * inv)), 0, 253) - 127 in
+    [-127, 126], inv = fp32(253 / fp32(max - min)) (0 when max == min), scale =
+    fp32(fp32(max - min) / 253), value (c + 127) * scale + min.  The byte values -128 and 127
+    carry no data: the key byte of channel 0 of the first token of every segment but the first
+    holds a marker, 127 when that element's own code is >= 0 and -128 otherwise, and every byte,
+    marker or not, is dequantized with the same formula (a marker stands for min - scale or
+    max + scale).  The identifier of token t is "its channel-0 key byte is -128 or 127"; segment
+    starts are unchanged, and the segment table still records them.  (parity unpinned: the
+    marker's place, its choice between the two values and its dequantized value are ours)
 """
 
 from __future__ import annotations
@@ -71,6 +82,18 @@ TAU = 2.0           # R5
 MAX_SEGMENTS = 5    # DGQ article section 2.2: 3~5 segments; 2..5 with the forced first cut
 SEG_CAPACITY = 16   # segment-table entries per (sequence, kv head) for appends
 CODE_LEVELS = 255   # INT8: 256 codes, 255 steps between min and max
+MARKER_LEVELS = 253  # R13: 254 data codes, 253 steps; -128 and 127 are markers
+MARK_LOW, MARK_HIGH = -128, 127
+FORMATS = ("bitmap", "marker")
+
+
+def format_levels(fmt: str):
+    """(steps between min and max, code of the minimum) of a storage format (R8 / R13)."""
+    if fmt == "bitmap":
+        return CODE_LEVELS, -128
+    if fmt == "marker":
+        return MARKER_LEVELS, -127
+    raise ValueError(f"unknown format {fmt!r}")
 
 
 # ----------------------------------------------------------------------------------------------
@@ -177,28 +200,29 @@ class SegParams:
     kmax: np.float32
     vmin: np.float32
     vmax: np.float32
+    levels: int = CODE_LEVELS
 
     @property
     def kscale(self) -> np.float32:
-        return quant_scale(self.kmin, self.kmax)
+        return quant_scale(self.kmin, self.kmax, self.levels)
 
     @property
     def vscale(self) -> np.float32:
-        return quant_scale(self.vmin, self.vmax)
+        return quant_scale(self.vmin, self.vmax, self.levels)
 
 
-def quant_scale(mn, mx) -> np.float32:
-    """R8: step between adjacent codes, fp32((max - min) / 255)."""
+def quant_scale(mn, mx, levels: int = CODE_LEVELS) -> np.float32:
+    """R8 (R13): step between adjacent codes, fp32((max - min) / levels)."""
     diff = np.float32(np.float32(mx) - np.float32(mn))
-    return np.float32(diff / np.float32(CODE_LEVELS))
+    return np.float32(diff / np.float32(levels))
 
 
-def quant_inv(mn, mx) -> np.float32:
-    """R8: fp32(255 / (max - min)), or 0 for a constant range."""
+def quant_inv(mn, mx, levels: int = CODE_LEVELS) -> np.float32:
+    """R8 (R13): fp32(levels / (max - min)), or 0 for a constant range."""
     diff = np.float32(np.float32(mx) - np.float32(mn))
     if not diff > 0:
         return np.float32(0.0)
-    return np.float32(np.float32(CODE_LEVELS) / diff)
+    return np.float32(np.float32(levels) / diff)
 
 
 def range_of(x16: np.ndarray):
@@ -207,7 +231,8 @@ def range_of(x16: np.ndarray):
     return np.float32(x.min()), np.float32(x.max())
 
 
-def segment_params(k16: np.ndarray, v16: np.ndarray, starts: List[int]) -> List[SegParams]:
+def segment_params(k16: np.ndarray, v16: np.ndarray, starts: List[int],
+                   levels: int = CODE_LEVELS) -> List[SegParams]:
     """R6: each segment's own key and value min/max (DGQ article section 2.2)."""
     length = k16.shape[0]
     bounds = list(starts) + [length]
@@ -216,23 +241,40 @@ def segment_params(k16: np.ndarray, v16: np.ndarray, starts: List[int]) -> List[
         e = bounds[j + 1]
         kmin, kmax = range_of(k16[s:e])
         vmin, vmax = range_of(v16[s:e])
-        out.append(SegParams(s, kmin, kmax, vmin, vmax))
+        out.append(SegParams(s, kmin, kmax, vmin, vmax, levels))
     return out
 
 
-def encode(x16: np.ndarray, mn, mx) -> np.ndarray:
-    """R8: asymmetric INT8 codes of ``x16`` for the range [mn, mx] (Quantization article 2.1)."""
+def encode(x16: np.ndarray, mn, mx, fmt: str = "bitmap") -> np.ndarray:
+    """R8 (R13): asymmetric INT8 codes of ``x16`` for the range [mn, mx] (Quantization article
+    2.1): 255 steps from -128 in the bitmap format, 253 steps from -127 in the marker format."""
+    levels, low = format_levels(fmt)
     x = canonical_f32(x16)
-    inv = quant_inv(mn, mx)
+    inv = quant_inv(mn, mx, levels)
     d = (x - np.float32(mn)).astype(np.float32)
     u = (d * inv).astype(np.float32)
-    c = np.clip(np.rint(u), 0, CODE_LEVELS).astype(np.int16) - 128
+    c = np.clip(np.rint(u), 0, levels).astype(np.int16) + low
     return c.astype(np.int8)
 
 
-def dequant(codes: np.ndarray, mn, scale) -> np.ndarray:
-    """R9: float64 reconstruction (code + 128) * scale + min."""
-    return (codes.astype(np.float64) + 128.0) * np.float64(scale) + np.float64(mn)
+def dequant(codes: np.ndarray, mn, scale, fmt: str = "bitmap") -> np.ndarray:
+    """R9 (R13): float64 reconstruction (code - low) * scale + min, low = the code of the minimum
+    (-128 bitmap, -127 marker)."""
+    _, low = format_levels(fmt)
+    return (codes.astype(np.float64) - float(low)) * np.float64(scale) + np.float64(mn)
+
+
+def place_marker(code) -> np.int8:
+    """R13: the marker that replaces a segment's first key byte (channel 0): 127 for a code in the
+    upper half of the range, -128 for one in the lower half."""
+    return np.int8(MARK_HIGH if int(code) >= 0 else MARK_LOW)
+
+
+def marker_bits(kcodes: np.ndarray) -> np.ndarray:
+    """R13: the identifier read back from the data: token t starts a segment iff its channel-0 key
+    byte is one of the two marker values."""
+    first = np.asarray(kcodes, np.int8).reshape(len(kcodes), -1)[:, 0]
+    return (first == MARK_LOW) | (first == MARK_HIGH)
 
 
 def boundary_bits(starts: List[int], length: int) -> np.ndarray:
@@ -250,7 +292,9 @@ class HeadCompressed:
     segs: List[SegParams]
     kcodes: np.ndarray      # int8 [L][D]
     vcodes: np.ndarray      # int8 [L][D]
-    bits: np.ndarray        # bool [L]
+    bits: np.ndarray        # bool [L]: the identifier (a bit tensor in the bitmap format; read
+                            # from the marker bytes of kcodes in the marker format)
+    fmt: str = "bitmap"
 
     @property
     def starts(self) -> List[int]:
@@ -264,44 +308,51 @@ class HeadCompressed:
         return idx
 
     def khat(self) -> np.ndarray:
-        return _dequant_by_segment(self.kcodes, self.segs, "k")
+        return _dequant_by_segment(self.kcodes, self.segs, "k", self.fmt)
 
     def vhat(self) -> np.ndarray:
-        return _dequant_by_segment(self.vcodes, self.segs, "v")
+        return _dequant_by_segment(self.vcodes, self.segs, "v", self.fmt)
 
 
-def _dequant_by_segment(codes, segs, which):
+def _dequant_by_segment(codes, segs, which, fmt="bitmap"):
     out = np.empty(codes.shape, dtype=np.float64)
     bounds = [s.start for s in segs] + [codes.shape[0]]
     for j, s in enumerate(segs):
         mn = s.kmin if which == "k" else s.vmin
         sc = s.kscale if which == "k" else s.vscale
-        out[bounds[j]:bounds[j + 1]] = dequant(codes[bounds[j]:bounds[j + 1]], mn, sc)
+        out[bounds[j]:bounds[j + 1]] = dequant(codes[bounds[j]:bounds[j + 1]], mn, sc, fmt)
     return out
 
 
-def encode_by_segment(x16: np.ndarray, segs: List[SegParams], which: str) -> np.ndarray:
-    """Codes of a whole head, each token with its own segment's range."""
+def encode_by_segment(x16: np.ndarray, segs: List[SegParams], which: str, fmt: str = "bitmap") -> np.ndarray:
+    """Codes of a whole head, each token with its own segment's range; in the marker format the
+    first key byte of every segment but the first is its marker (R13)."""
     out = np.empty(x16.shape, dtype=np.int8)
     bounds = [s.start for s in segs] + [x16.shape[0]]
     for j, s in enumerate(segs):
         mn, mx = (s.kmin, s.kmax) if which == "k" else (s.vmin, s.vmax)
-        out[bounds[j]:bounds[j + 1]] = encode(x16[bounds[j]:bounds[j + 1]], mn, mx)
+        out[bounds[j]:bounds[j + 1]] = encode(x16[bounds[j]:bounds[j + 1]], mn, mx, fmt)
+    if fmt == "marker" and which == "k":
+        for s in segs[1:]:
+            if s.start < x16.shape[0]:
+                out[s.start, 0] = place_marker(out[s.start, 0])
     return out
 
 
 def compress_head(k16: np.ndarray, v16: np.ndarray, max_segments: int = MAX_SEGMENTS,
-                  tau: float = TAU, min_var: float = 0.0, length_aware: bool = False) -> HeadCompressed:
-    """The whole DGQ compression of one (sequence, kv head): cuts, params, codes, bits."""
+                  tau: float = TAU, min_var: float = 0.0, length_aware: bool = False,
+                  fmt: str = "bitmap") -> HeadCompressed:
+    """The whole DGQ compression of one (sequence, kv head): cuts, params, codes, identifier."""
     k16 = np.asarray(k16, dtype=np.float16)
     v16 = np.asarray(v16, dtype=np.float16)
     if not (np.isfinite(k16).all() and np.isfinite(v16).all()):
         raise ValueError("DGQ compression needs finite inputs")
     length = k16.shape[0]
+    levels, _ = format_levels(fmt)
     starts = segment_starts(k16, max_segments, tau, min_var, length_aware)
-    segs = segment_params(k16, v16, starts)
-    return HeadCompressed(length, segs, encode_by_segment(k16, segs, "k"),
-                          encode_by_segment(v16, segs, "v"), boundary_bits(starts, length))
+    segs = segment_params(k16, v16, starts, levels)
+    return HeadCompressed(length, segs, encode_by_segment(k16, segs, "k", fmt),
+                          encode_by_segment(v16, segs, "v", fmt), boundary_bits(starts, length), fmt)
 
 
 # ----------------------------------------------------------------------------------------------
@@ -345,6 +396,8 @@ class AppendState:
 
     def __init__(self, comp: HeadCompressed, k16_prefix: np.ndarray, block_size: int,
                  seg_capacity: int = SEG_CAPACITY, tau: float = TAU, min_var: float = 0.0):
+        self.fmt = comp.fmt
+        self.levels, _ = format_levels(comp.fmt)
         self.head_dim = comp.kcodes.shape[1]
         self.floor_q = variance_floor_q(min_var, self.head_dim)
         self.block_size = block_size
@@ -405,18 +458,20 @@ class AppendState:
             else:
                 kmn, kmx = range_of(span_k)
                 vmn, vmx = range_of(span_v)
-                self.segs.append(SegParams(self.r0, kmn, kmx, vmn, vmx))
+                self.segs.append(SegParams(self.r0, kmn, kmx, vmn, vmx, self.levels))
                 self.span_own = True
                 if self.r0 > 0:
                     self.bits[self.r0] = True
         elif want_own and self.span_own:
             kmn, kmx = range_of(span_k)
             vmn, vmx = range_of(span_v)
-            self.segs[-1] = SegParams(self.r0, kmn, kmx, vmn, vmx)
+            self.segs[-1] = SegParams(self.r0, kmn, kmx, vmn, vmx, self.levels)
 
         seg = self.segs[-1] if self.span_own else base
-        kc = encode(span_k, seg.kmin, seg.kmax)
-        vc = encode(span_v, seg.vmin, seg.vmax)
+        kc = encode(span_k, seg.kmin, seg.kmax, self.fmt)
+        vc = encode(span_v, seg.vmin, seg.vmax, self.fmt)
+        if self.fmt == "marker" and self.span_own and self.r0 > 0:
+            kc[0, 0] = place_marker(kc[0, 0])          # R13: the span's segment starts at r0
         for i in range(len(self.stage_k)):
             self.kcodes[self.r0 + i] = kc[i]
             self.vcodes[self.r0 + i] = vc[i]
@@ -433,7 +488,7 @@ class AppendState:
         return HeadCompressed(self.length, [dataclasses.replace(s) for s in self.segs],
                               np.stack(self.kcodes) if self.kcodes else np.zeros((0, self.head_dim), np.int8),
                               np.stack(self.vcodes) if self.vcodes else np.zeros((0, self.head_dim), np.int8),
-                              np.asarray(self.bits, dtype=bool))
+                              np.asarray(self.bits, dtype=bool), self.fmt)
 
 
 # ----------------------------------------------------------------------------------------------
@@ -516,11 +571,13 @@ def page_formula_bytes(num_layers: int, num_heads: int, head_dim: int, seq_len: 
     return fp16, dgq
 
 
-def compressed_bytes(lengths, num_kv_heads: int, head_dim: int, seg_counts=None, entry_bytes: int = 32):
-    """Bytes the compressed cache of one layer uses: codes, bits, and (if given) the segment
-    tables, which the page's formula leaves out."""
+def compressed_bytes(lengths, num_kv_heads: int, head_dim: int, seg_counts=None, entry_bytes: int = 32,
+                     fmt: str = "bitmap"):
+    """Bytes the compressed cache of one layer uses: codes, bits (none in the marker format, R13),
+    and (if given) the segment tables, which the page's formula leaves out."""
+    format_levels(fmt)
     total_tokens = int(np.sum(lengths))
     codes = 2 * total_tokens * num_kv_heads * head_dim
-    bits = total_tokens * num_kv_heads / 8.0
+    bits = total_tokens * num_kv_heads / 8.0 if fmt == "bitmap" else 0.0
     params = 0 if seg_counts is None else int(np.sum(seg_counts)) * entry_bytes
     return {"codes": codes, "bits": bits, "params": params}

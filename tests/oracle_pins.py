@@ -474,11 +474,128 @@ def check_min_var_floor():
         assert (len(st.segs) == 2) == want_cut, (min_var, len(st.segs))
 
 
+# -- marker format (R13) -----------------------------------------------------------------------------
+
+def _is_marker(codes):
+    return (codes == -128) | (codes == 127)
+
+
+def _nearest_code_marker_ok(x16, codes, mn, scale):
+    """Brute force over the 254 data codes of the marker format: the chosen one is (up to fp32
+    rounding) the nearest."""
+    x = np.asarray(x16, np.float64).reshape(-1, 1)
+    allc = np.arange(-127, 127, dtype=np.float64).reshape(1, -1)
+    rec = (allc + 127.0) * np.float64(scale) + np.float64(mn)
+    err = np.abs(x - rec)
+    chosen = err[np.arange(len(x)), codes.reshape(-1).astype(np.int64) + 127]
+    slack = 2.0 ** -20 * max(abs(float(mn)), abs(float(mn) + 253 * float(scale)), float(scale))
+    return np.all(chosen <= err.min(axis=1) + slack)
+
+
+def check_marker_format():
+    """Same cuts and ranges as the bitmap format; data codes are the nearest of 254 levels; the only
+    -128/127 bytes are the markers at (segment start, key channel 0), the identifier read back from
+    them equals the bit tensor of the bitmap format, and each marker names the half of the range
+    its element lies in."""
+    for k, v in _some_heads():
+        hb = O.compress_head(k, v)
+        hm = O.compress_head(k, v, fmt="marker")
+        assert hm.starts == hb.starts
+        for sb, sm in zip(hb.segs, hm.segs):
+            assert (sb.kmin, sb.kmax, sb.vmin, sb.vmax) == (sm.kmin, sm.kmax, sm.vmin, sm.vmax)
+        assert not _is_marker(hm.vcodes).any()
+        assert [tuple(int(i) for i in ix) for ix in zip(*np.nonzero(_is_marker(hm.kcodes)))] == \
+            [(s, 0) for s in hm.starts[1:]]
+        assert np.array_equal(O.marker_bits(hm.kcodes), hb.bits)
+        khat, vhat = hm.khat(), hm.vhat()
+        bounds = hm.starts + [hm.length]
+        for j, s in enumerate(hm.segs):
+            sl = slice(bounds[j], bounds[j + 1])
+            for x16, codes, rec, mn, mx, sc, is_k in ((k[sl], hm.kcodes[sl], khat[sl], s.kmin, s.kmax, s.kscale, True),
+                                                      (v[sl], hm.vcodes[sl], vhat[sl], s.vmin, s.vmax, s.vscale, False)):
+                x = np.asarray(x16, np.float64)
+                data = np.ones(codes.shape, bool)
+                if is_k and j > 0:
+                    data[0, 0] = False
+                assert np.all((codes[data] >= -127) & (codes[data] <= 126))
+                # step = (max - min) / 253 in fp32
+                assert abs(float(sc) * 253 - (float(mx) - float(mn))) <= 253 * 2.0 ** -23 * max(float(sc), 1e-30) + 2.0 ** -23 * abs(float(mx) - float(mn))
+                if not mx > mn:
+                    assert np.all(rec == float(mn))
+                    continue
+                xf = np.asarray(x16, np.float32)
+                assert np.all(codes[data & (xf == mn)] == -127) and np.all(codes[data & (xf == mx)] == 126)
+                assert _nearest_code_marker_ok(x16[data], codes[data], mn, sc)
+                bound = 0.5 * float(sc) * (1 + 2.0 ** -10) + 2.0 ** -22 * max(abs(float(mn)), abs(float(mx)))
+                assert np.max(np.abs(rec[data] - x[data])) <= bound
+                if is_k and j > 0:
+                    frac = (x[0, 0] - float(mn)) / (float(mx) - float(mn))
+                    marker = int(codes[0, 0])
+                    assert (marker == 127 and frac >= 126 / 253) or (marker == -128 and frac <= 127 / 253), (frac, marker)
+                    assert rec[0, 0] == (O.dequant(np.array([marker], np.int8), mn, sc, "marker")[0])
+                    assert abs(rec[0, 0] - x[0, 0]) <= 0.5 * (float(mx) - float(mn)) + 2 * float(sc)
+
+
+def check_marker_constant_segment():
+    """A constant run in the marker format: its codes are the minimum's code -127 except the
+    marker, and every byte, the marker included, reconstructs the constant exactly."""
+    rng = np.random.default_rng(5)
+    k = (rng.standard_normal((160, 16)) * 0.3).astype(np.float16)
+    v = (rng.standard_normal((160, 16)) * 0.3).astype(np.float16)
+    k[64:128] = np.float16(0.0)
+    v[64:128] = np.float16(-0.125)
+    hc = O.compress_head(k, v, max_segments=3, fmt="marker")
+    assert hc.starts == [0, 64, 128], hc.starts
+    assert hc.kcodes[64, 0] == -128 and np.all(hc.kcodes[64:128].reshape(-1)[1:] == -127)
+    assert np.all(hc.vcodes[64:128] == -127)
+    assert np.all(hc.khat()[64:128] == 0.0) and np.all(hc.vhat()[64:128] == -0.125)
+    assert _is_marker(hc.kcodes[128, 0])
+
+
+def check_marker_append(block_size=32):
+    """Appends in the marker format take the same decisions as in the bitmap format; every span
+    that opens a segment carries its marker, a joined span none; the whole sequence equals the
+    direct marker-format encoding with the final segments; frozen codes never change."""
+    for sig_tail, want_new in ((3.0, True), (0.3, False)):
+        k, v = _prefix_and_tail(sig_tail, length=256, tail=3 * block_size)
+        if not want_new:
+            last = O.compress_head(k[:256], v[:256]).segs[-1]
+            k[256:] = np.clip(k[256:].astype(np.float32), 0.6 * last.kmin, 0.6 * last.kmax).astype(np.float16)
+            v[256:] = np.clip(v[256:].astype(np.float32), 0.6 * last.vmin, 0.6 * last.vmax).astype(np.float16)
+        sb = O.AppendState(O.compress_head(k[:256], v[:256]), k[:256], block_size)
+        sm = O.AppendState(O.compress_head(k[:256], v[:256], fmt="marker"), k[:256], block_size)
+        for t in range(256, k.shape[0]):
+            frozen = [c.copy() for c in sm.kcodes[:sm.r0]]
+            sb.append(k[t], v[t])
+            sm.append(k[t], v[t])
+            assert all(np.array_equal(a, b) for a, b in zip(frozen, sm.kcodes[:len(frozen)]))
+            snap = sm.snapshot()
+            assert snap.starts == sb.snapshot().starts
+            assert np.array_equal(O.marker_bits(snap.kcodes), snap.bits)
+        snap = sm.snapshot()
+        n_new = len(snap.segs) - len(O.compress_head(k[:256], v[:256]).segs)
+        assert (n_new == 3) if want_new else (n_new == 0), n_new
+        assert np.array_equal(snap.kcodes, O.encode_by_segment(k, snap.segs, "k", "marker"))
+        assert np.array_equal(snap.vcodes, O.encode_by_segment(v, snap.segs, "v", "marker"))
+        assert not _is_marker(snap.vcodes).any()
+
+
+def check_marker_bytes():
+    """The marker format stores no bit tensor: the cache is exactly 1 byte per element (plus the
+    segment table), 1/8 byte per token per head below the bitmap format."""
+    lens, hkv, d = [8192] * 16, 8, 128
+    b = O.compressed_bytes(lens, hkv, d)
+    m = O.compressed_bytes(lens, hkv, d, fmt="marker")
+    assert m["codes"] == b["codes"] == 2 * 8192 * 16 * hkv * d
+    assert m["bits"] == 0 and b["bits"] == 8192 * 16 * hkv / 8
+
+
 ALL_CHECKS = [
     check_fixed_point, check_window_q_against_variance, check_scores_closed_form,
     check_selection_twin, check_step_change_cut, check_segment_invariants, check_tiny_recovery,
     check_minmax_library, check_bits, check_codes, check_constant_segment_exact,
     check_dequant_closed_form, check_attention, check_append_join, check_append_cut,
     check_append_capacity, check_append_matches_prefix_rule, check_append_from_empty, check_group64,
-    check_length_cap, check_min_var_floor,
+    check_length_cap, check_min_var_floor, check_marker_format, check_marker_constant_segment,
+    check_marker_append, check_marker_bytes,
 ]

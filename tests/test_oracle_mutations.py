@@ -93,28 +93,65 @@ def _select_strict_tau(scores, max_segments=5, tau=2.0):
     return sorted(cuts)
 
 
-def _scale_256(mn, mx):
+def _scale_256(mn, mx, levels=O.CODE_LEVELS):
     return np.float32(np.float32(np.float32(mx) - np.float32(mn)) / np.float32(256))
 
 
-def _inv_256(mn, mx):
+def _inv_256(mn, mx, levels=O.CODE_LEVELS):
     diff = np.float32(np.float32(mx) - np.float32(mn))
     return np.float32(0) if not diff > 0 else np.float32(np.float32(256) / diff)
 
 
-def _encode_floor(x16, mn, mx):
+def _encode_floor(x16, mn, mx, fmt="bitmap"):
+    levels, low = O.format_levels(fmt)
     x = O.canonical_f32(x16)
-    inv = O.quant_inv(mn, mx)
+    inv = O.quant_inv(mn, mx, levels)
     u = ((x - np.float32(mn)) * inv).astype(np.float32)
-    return (np.clip(np.floor(u), 0, 255).astype(np.int16) - 128).astype(np.int8)
+    return (np.clip(np.floor(u), 0, levels).astype(np.int16) + low).astype(np.int8)
 
 
-def _dequant_no_offset(codes, mn, scale):
+def _dequant_no_offset(codes, mn, scale, fmt="bitmap"):
     return codes.astype(np.float64) * np.float64(scale) + np.float64(mn)
 
 
-def _params_swapped(k16, v16, starts):
-    return O.__dict__["_orig_segment_params"](v16, k16, starts)
+def _params_swapped(k16, v16, starts, levels=O.CODE_LEVELS):
+    return O.__dict__["_orig_segment_params"](v16, k16, starts, levels)
+
+
+def _levels_marker_255(fmt):
+    return (O.CODE_LEVELS, -128)
+
+
+def _encode_by_segment_marker_on_v(x16, segs, which, fmt="bitmap"):
+    """Mistake: the markers go into the value bytes instead of the key bytes."""
+    out = O.__dict__["_orig_encode_by_segment"](x16, segs, which, fmt)
+    if fmt != "marker":
+        return out
+    for s in segs[1:]:
+        if which == "k":
+            out[s.start, 0] = O.encode(x16[s.start:s.start + 1, :1], s.kmin, s.kmax, fmt)[0, 0]
+        else:
+            out[s.start, 0] = O.place_marker(out[s.start, 0])
+    return out
+
+
+def _dequant_marker_offset_128(codes, mn, scale, fmt="bitmap"):
+    return (codes.astype(np.float64) + 128.0) * np.float64(scale) + np.float64(mn)
+
+
+def _place_marker_inverted(code):
+    return np.int8(O.MARK_LOW if int(code) >= 0 else O.MARK_HIGH)
+
+
+class _AppendNoMarker(O.AppendState):
+    """Mistake: the span's own segment gets no marker in the marker format."""
+
+    def append(self, k_row, v_row):
+        r0 = self.r0
+        super().append(k_row, v_row)
+        if self.fmt == "marker" and r0 > 0 and self.r0 == r0 and self.span_own:
+            seg = self.segs[-1]
+            self.kcodes[r0] = O.encode(np.asarray(self.stage_k[0]).reshape(1, -1), seg.kmin, seg.kmax, self.fmt)[0]
 
 
 def _attention_no_scale(q16, khat, vhat, softmax_scale=None):
@@ -202,6 +239,11 @@ MUTATIONS = {
     "fixed_point_clamp_16": ("fixed_point", _fixed_point_clamp16, [P.check_fixed_point]),
     "fixed_point_truncates": ("fixed_point", _fixed_point_trunc, [P.check_fixed_point]),
     "append_keeps_stale_codes": ("AppendState", _AppendNoReencode, [P.check_append_cut]),
+    "marker_format_255_levels": ("format_levels", _levels_marker_255, [P.check_marker_format]),
+    "marker_on_value_bytes": ("encode_by_segment", _encode_by_segment_marker_on_v, [P.check_marker_format]),
+    "marker_dequant_offset_128": ("dequant", _dequant_marker_offset_128, [P.check_marker_format]),
+    "marker_choice_inverted": ("place_marker", _place_marker_inverted, [P.check_marker_format]),
+    "append_without_marker": ("AppendState", _AppendNoMarker, [P.check_marker_append]),
 }
 
 
@@ -210,6 +252,7 @@ def test_pins_catch_mutation(name, monkeypatch):
     attr, fake, checks = MUTATIONS[name]
     monkeypatch.setitem(O.__dict__, "_orig_segment_params", O.segment_params)
     monkeypatch.setitem(O.__dict__, "_orig_decode_attention", O.decode_attention)
+    monkeypatch.setitem(O.__dict__, "_orig_encode_by_segment", O.encode_by_segment)
     monkeypatch.setattr(O, attr, fake)
     caught = []
     for check in checks:
