@@ -19,7 +19,8 @@ fp16 keys/values ("group64_baseline", "quality_vs_fp16").
 
 The segment-count policies (segment cap, tau, the length-aware cap, the variance floor) are then
 run on the same batch: segment histogram, compress time and error against fp16 attention
-("segment_policies").  The streaming workload (64 x 2048-token prefixes, 256 append + decode steps) is timed three
+("segment_policies"), and both storage formats of the segment identifier, the bit tensor and the
+marker bytes inside the codes, are compared on it ("identifier_formats").  The streaming workload (64 x 2048-token prefixes, 256 append + decode steps) is timed three
 ways: two launches per step, the fused append + decode, and the group-64 baseline ("streaming").
 Finally the 128K long-context workload (32 layers of one 131,072-token sequence, each layer
 compressed into its own cache, decode looped over the layers) is timed per layer
@@ -225,6 +226,66 @@ def segment_policies(cfg, k, v, cu, dcu, dtable, nblk, q, dev, Q):
                      "compress_us": round(float(np.median([a.elapsed_time(b) for a, b in ts])) * 1e3, 2),
                      "max_rel_err_vs_fp16": round(err[0], 6), "mean_rel_err_vs_fp16": round(err[1], 6)})
         del cache, ws
+    return rows
+
+
+def marker_format(cfg, k, v, cu, dcu, dtable, nblk, q, dev, Q):
+    """The two storage formats of the segment identifier on the same batch (DGQ article 3.2): the
+    bit tensor, and the marker bytes inside the key codes (254 data levels, no bit tensor).
+    Compress and decode time (HIP events, mean of 6; three caches rotate so every decode reads a
+    cache written two compressions earlier), the marker read-back, stored bytes and the error
+    against float32 attention over the unquantized keys/values."""
+    import torch
+
+    B, L, hkv, hq, d, bs = cfg.batch, cfg.seq_len, cfg.hkv, cfg.hq, cfg.head_dim, cfg.block_size
+    total = int(cu[-1])
+    ref = fp16_reference(cfg, k, v, cu, q)
+    lens = torch.full((B,), L, dtype=torch.int32, device=dev)
+    rows = {}
+    for fmt in ("bitmap", "marker"):
+        params = Q.DGQParams(hkv, hq, d, bs, marker=(fmt == "marker"))
+        caches = [Q.DGQCache(params, nblk, B, dev) for _ in range(3)]
+        ws = Q.workspace(Q.compress_workspace_size(params, B, total, L), dev)
+        wsd = Q.workspace(Q.decode_workspace_size(params, B, L), dev)
+        out = torch.empty((B, hq, d), dtype=torch.float32, device=dev)
+        for c in caches:
+            Q.dgq_compress(params, k, v, dcu, dtable, c, L, total, ws=ws)
+        ev = []
+        for i in range(8):
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            e[0].record()
+            Q.dgq_compress(params, k, v, dcu, dtable, caches[i % 3], L, total, ws=ws)
+            e[1].record()
+            Q.paged_decode_attn_int8(params, q, caches[(i + 1) % 3], dtable, lens, L, out=out, ws=wsd)
+            e[2].record()
+            ev.append(e)
+        torch.cuda.synchronize()
+        ev = ev[2:]
+        comp_us = float(np.mean([e[0].elapsed_time(e[1]) for e in ev])) * 1e3
+        dec_us = float(np.mean([e[1].elapsed_time(e[2]) for e in ev])) * 1e3
+        err = rel_err_rows(out, ref)
+        nseg = caches[0].nseg.cpu().numpy().reshape(-1)
+        row = {"compress_us": round(comp_us, 2), "decode_us": round(dec_us, 2),
+               "max_rel_err_vs_fp16": round(err[0], 6), "mean_rel_err_vs_fp16": round(err[1], 6),
+               "code_bytes": int(B * L * hkv * d * 2),
+               "identifier_bytes": int(B * L * hkv // 8) if fmt == "bitmap" else 0,
+               "segment_table_bytes": int(nseg.sum()) * 32}
+        if fmt == "marker":
+            got = torch.zeros_like(rows["bitmap"]["_bits"])
+            Q.dgq_marker_bits(params, caches[0], dtable, lens, L, out=got)     # warm-up
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(5):
+                Q.dgq_marker_bits(params, caches[0], dtable, lens, L, out=got)
+            e1.record()
+            torch.cuda.synchronize()
+            row["marker_readback_us"] = round(e0.elapsed_time(e1) * 1e3 / 5, 2)
+            row["readback_equals_bit_tensor"] = bool(torch.equal(got, rows["bitmap"]["_bits"]))
+        else:
+            row["_bits"] = caches[0].bits.clone()
+        rows[fmt] = row
+        del caches, ws, wsd
+    rows["bitmap"].pop("_bits")
     return rows
 
 
@@ -483,6 +544,7 @@ def main():
     gd_ms = np.array([e[1].elapsed_time(e[2]) for e in gev])
     quality = quality_vs_fp16(cfg, k, v, cu, k_tok, v_tok, q, out, out_g)
     policies = segment_policies(cfg, k, v, cu, dcu, dtable, nblk, q, dev, Q)
+    formats = marker_format(cfg, k, v, cu, dcu, dtable, nblk, q, dev, Q)
 
     # algorithmic bytes
     Ld = L + 1
@@ -555,6 +617,7 @@ def main():
         },
         "quality_vs_fp16": quality,
         "segment_policies": policies,
+        "identifier_formats": formats,
     }
     if not args.no_long_context:
         del caches, g_caches, k, v, ws_c

@@ -50,6 +50,14 @@
  *   bits: uint8 [num_blocks][num_kv_heads][block_size/8]; bit (tau % 8) of byte tau/8 is 1 iff
  *   the token starts a segment other than the first (the 1-bit identifier, kept in its own
  *   tensor as in the DGQ article's original scheme).
+ *
+ * Marker format (flag DGQ_FORMAT_MARKER; DGQ article 3.2, the identifier kept inside the INT8
+ * data): data codes are c in [-127, 126] standing for (c + 127) * scale + min with
+ * scale = fp32((max - min) / 253); the byte values -128 and 127 are markers.  The key byte of
+ * channel 0 of the first token of every segment but the first holds 127 if that element's own
+ * code is >= 0, else -128, and is dequantized with the same formula (min - scale or
+ * max + scale).  There is no bit tensor (dgq_cache_t.bits may be NULL and is never touched);
+ * dgq_marker_bits reads the identifier back from the markers.
  */
 #ifndef DGQ_H
 #define DGQ_H
@@ -72,11 +80,15 @@ typedef enum dgq_status {
   DGQ_ERR_HIP = -5                  /* a HIP call failed; see dgq_last_error() */
 } dgq_status_t;
 
-/* Segment-count policies (dgq_params_t.flags), DGQ article 3.2 and 5.3: */
+/* dgq_params_t.flags: segment-count policies (DGQ article 3.2 and 5.3) and the storage format
+ * of the segment identifier (DGQ article 3.2). */
 enum {
   /* Length-aware cap: a sequence of L tokens gets at most 2 segments below 2048 tokens, 3 below
    * 16384, else min(5, floor(log2(L / 1024)) + 2); the cap only lowers max_segments. */
-  DGQ_POLICY_LENGTH_AWARE = 1u
+  DGQ_POLICY_LENGTH_AWARE = 1u,
+  /* Marker format (see the layout notes above) instead of the bit tensor.  A cache must be
+   * written and read with the same format. */
+  DGQ_FORMAT_MARKER = 2u
 };
 
 /* Shape and method parameters, passed to every call (48 bytes).  Defaults: win 16,
@@ -89,14 +101,15 @@ typedef struct dgq_params {
   int32_t win;           /* sliding-window length of the variance curve; must be 16 (DGQ 2.2) */
   int32_t max_segments;  /* 1..8 segments per (sequence, kv head) from dgq_compress */
   int32_t seg_capacity;  /* segment-table rows per (sequence, kv head): max_segments..64 */
-  uint32_t flags;        /* DGQ_POLICY_* bits; other bits must be 0 */
+  uint32_t flags;        /* DGQ_POLICY_LENGTH_AWARE | DGQ_FORMAT_MARKER; other bits must be 0 */
   double tau;            /* change-point threshold on the window-variance ratio, finite, >= 1 */
   double min_var;        /* variance floor, finite, >= 0 (0 = off): a candidate cut whose two
                             16-token windows both have a population variance below it is not a
                             change point, in dgq_compress and in dgq_append's window test */
 } dgq_params_t;
 
-/* One segment-table row (32 bytes).  kscale = fp32((kmax - kmin) / 255), likewise vscale. */
+/* One segment-table row (32 bytes).  kscale = fp32((kmax - kmin) / 255), likewise vscale (253 in
+ * place of 255 in the marker format). */
 typedef struct dgq_seg {
   int32_t start;         /* first token of the segment */
   float kmin, kmax, vmin, vmax;
@@ -121,7 +134,8 @@ typedef struct dgq_tail {
 typedef struct dgq_cache {
   int8_t *k_pool;        /* [num_blocks][num_kv_heads][block_size*head_dim], 16-byte aligned */
   int8_t *v_pool;        /* same */
-  uint8_t *bits;         /* [num_blocks][num_kv_heads][block_size/8] */
+  uint8_t *bits;         /* [num_blocks][num_kv_heads][block_size/8]; NULL allowed (and unused)
+                            in the marker format */
   dgq_seg_t *segs;       /* [batch][num_kv_heads][seg_capacity] */
   int32_t *nseg;         /* [batch][num_kv_heads] rows in use */
   dgq_tail_t *tail;      /* [batch][num_kv_heads] */
@@ -304,6 +318,21 @@ dgq_status_t dgq_append_decode(const dgq_params_t *p, const uint16_t *k_tok, con
                                const int32_t *block_table, int32_t max_blocks, int32_t max_seq_len,
                                float softmax_scale, const dgq_cache_t *cache, float *out, void *ws,
                                size_t ws_bytes, hipStream_t stream);
+
+/* ---- Identifier read-back in the marker format (DGQ article 3.2: the identifier is taken out
+ * of the INT8 data with a bit mask) ---- */
+
+/* Write the boundary bits of every sequence, in the bit-tensor layout, from the marker bytes of a
+ * marker-format cache: bit tau of block table[b][j] and head h is 1 iff token j*block_size + tau
+ * (< seq_lens[b]) has a marker in its channel-0 key byte.
+ *   block_table (device) int32 [batch][max_blocks]; seq_lens (device) int32 [batch], each
+ *   <= max_seq_len <= max_blocks * block_size; bits_out (device) uint8
+ *   [num_blocks][num_kv_heads][block_size/8]: the blocks of the sequences are overwritten (bits of
+ *   tokens at or past seq_lens[b] are 0), other blocks are not touched.
+ * DGQ_ERR_INVALID_ARG unless p->flags has DGQ_FORMAT_MARKER. */
+dgq_status_t dgq_marker_bits(const dgq_params_t *p, const dgq_cache_t *cache, const int32_t *block_table,
+                             int32_t max_blocks, const int32_t *seq_lens, int32_t batch,
+                             int32_t max_seq_len, uint8_t *bits_out, hipStream_t stream);
 
 /* ---- Fixed 64-channel group INT8 baseline (DGQ article 2.2: the LLM.int8()-style grouping the
  * DGQ design is compared against -- every 64-channel chunk of every token has its own min/max).

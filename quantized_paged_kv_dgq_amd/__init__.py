@@ -18,6 +18,7 @@ from .api import (  # noqa: F401
     dgq_compress,
     dgq_copy_blocks,
     dgq_copy_seq_state,
+    dgq_marker_bits,
     dgq_swap_in,
     dgq_swap_out,
     dgq_g64_quantize,

@@ -82,6 +82,7 @@ class Cache(ctypes.Structure):
 
 
 DGQ_POLICY_LENGTH_AWARE = 1
+DGQ_FORMAT_MARKER = 2
 
 assert ctypes.sizeof(Params) == 48
 assert ctypes.sizeof(Seg) == 32
@@ -93,6 +94,7 @@ EXPORTS = [
     "dgq_pool_create", "dgq_pool_destroy", "dgq_block_alloc", "dgq_block_free", "dgq_pool_num_free",
     "dgq_block_share", "dgq_block_refcount", "dgq_block_cow",
     "dgq_copy_blocks", "dgq_copy_seq_state", "dgq_swap_image_bytes", "dgq_swap_out", "dgq_swap_in",
+    "dgq_marker_bits",
     "dgq_compress_workspace_size", "dgq_decode_workspace_size",
     "dgq_compress", "dgq_append", "paged_decode_attn_int8", "dgq_append_decode",
     "dgq_g64_quantize", "paged_decode_attn_g64",
@@ -141,6 +143,8 @@ def load() -> ctypes.CDLL:
     lib.dgq_swap_out.restype = i32
     lib.dgq_swap_in.argtypes = [P(Params), P(Cache), i32, vp, i32, vp, sz, vp, vp]
     lib.dgq_swap_in.restype = i32
+    lib.dgq_marker_bits.argtypes = [P(Params), P(Cache), vp, i32, vp, i32, i32, vp, vp]
+    lib.dgq_marker_bits.restype = i32
     lib.dgq_compress_workspace_size.argtypes = [P(Params), i32, i64, i32]
     lib.dgq_compress_workspace_size.restype = sz
     lib.dgq_decode_workspace_size.argtypes = [P(Params), i32, i32]

@@ -15,7 +15,7 @@ from typing import Optional, Sequence
 import torch
 
 from . import _lib
-from ._lib import DGQ_POLICY_LENGTH_AWARE, Cache, G64Cache, Params, check
+from ._lib import DGQ_FORMAT_MARKER, DGQ_POLICY_LENGTH_AWARE, Cache, G64Cache, Params, check
 
 
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
@@ -35,12 +35,13 @@ def _need(cond: bool, msg: str) -> None:
 class DGQParams:
     """dgq_params_t: shapes and method constants (window 16; segments 2..max_segments; tau), plus
     the segment-count policies: ``length_aware`` (cap by sequence length) and ``min_var``
-    (variance floor below which a window pair is not a change point)."""
+    (variance floor below which a window pair is not a change point), and the identifier format:
+    ``marker`` keeps it in the codes (no bit tensor) instead of the bit tensor."""
 
     def __init__(self, num_kv_heads: int, num_q_heads: int, head_dim: int, block_size: int,
                  max_segments: int = 5, seg_capacity: int = 16, tau: float = 2.0, win: int = 16,
-                 length_aware: bool = False, min_var: float = 0.0):
-        flags = DGQ_POLICY_LENGTH_AWARE if length_aware else 0
+                 length_aware: bool = False, min_var: float = 0.0, marker: bool = False):
+        flags = (DGQ_POLICY_LENGTH_AWARE if length_aware else 0) | (DGQ_FORMAT_MARKER if marker else 0)
         self.c = Params(num_kv_heads, num_q_heads, head_dim, block_size, win, max_segments,
                         seg_capacity, flags, float(tau), float(min_var))
 
@@ -55,9 +56,14 @@ class DGQParams:
     def length_aware(self) -> bool:
         return bool(self.c.flags & DGQ_POLICY_LENGTH_AWARE)
 
+    @property
+    def marker(self) -> bool:
+        return bool(self.c.flags & DGQ_FORMAT_MARKER)
+
 
 class DGQCache:
-    """The caller-owned device buffers of one layer's compressed cache (dgq_cache_t)."""
+    """The caller-owned device buffers of one layer's compressed cache (dgq_cache_t).  In the
+    marker format there is no bit tensor (``bits`` is None)."""
 
     def __init__(self, params: DGQParams, num_blocks: int, batch: int, device="cuda"):
         p = params.c
@@ -68,7 +74,8 @@ class DGQCache:
         self.batch = batch
         self.k_pool = torch.zeros((num_blocks, p.num_kv_heads, tile), dtype=torch.int8, device=dev)
         self.v_pool = torch.zeros_like(self.k_pool)
-        self.bits = torch.zeros((num_blocks, p.num_kv_heads, p.block_size // 8), dtype=torch.uint8, device=dev)
+        self.bits = None if params.marker else torch.zeros((num_blocks, p.num_kv_heads, p.block_size // 8),
+                                                           dtype=torch.uint8, device=dev)
         self.segs = torch.zeros((batch, p.num_kv_heads, p.seg_capacity, 8), dtype=torch.int32, device=dev)
         self.nseg = torch.zeros((batch, p.num_kv_heads), dtype=torch.int32, device=dev)
         self.tail = torch.zeros((batch, p.num_kv_heads, 56), dtype=torch.int32, device=dev)
@@ -294,6 +301,22 @@ def dgq_swap_in(params: DGQParams, cache: DGQCache, row: int, ids: torch.Tensor,
     st = _lib.load().dgq_swap_in(ctypes.byref(params.c), ctypes.byref(cache.c), row, _ptr(_ids(ids, "ids")),
                                  ids.numel(), _ptr(staging), staging.numel(), _ptr(host), _stream(stream))
     check(st, "dgq_swap_in")
+
+
+def dgq_marker_bits(params: DGQParams, cache: DGQCache, block_table: torch.Tensor, seq_lens: torch.Tensor,
+                    max_seq_len: int, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """The boundary bits of a marker-format cache, read back from its marker bytes, in the
+    bit-tensor layout uint8 [num_blocks][Hkv][block_size/8] (see dgq_marker_bits)."""
+    p = params.c
+    _need(seq_lens.dtype == torch.int32 and block_table.dtype == torch.int32, "int32 index tensors")
+    if out is None:
+        out = torch.zeros((cache.num_blocks, p.num_kv_heads, p.block_size // 8), dtype=torch.uint8,
+                          device=cache.k_pool.device)
+    st = _lib.load().dgq_marker_bits(ctypes.byref(params.c), ctypes.byref(cache.c), _ptr(block_table),
+                                     block_table.shape[1], _ptr(seq_lens), seq_lens.numel(), max_seq_len,
+                                     _ptr(out), _stream(stream))
+    check(st, "dgq_marker_bits")
+    return out
 
 
 def dgq_g64_quantize(params: DGQParams, k: torch.Tensor, v: torch.Tensor, cu_seqlens: torch.Tensor,

@@ -22,7 +22,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libdgq.so")
 ARCH = os.environ.get("DGQ_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["api.hip", "decode.hip", "g64.hip", "compress.hip", "append.hip", "lifecycle.hip", "pool.cpp"]
+SOURCES = ["api.hip", "decode.hip", "g64.hip", "compress.hip", "append.hip", "lifecycle.hip", "markers.hip", "pool.cpp"]
 
 COMMON = ["-O3", "-fPIC", "-std=c++17", "-Wall", "-Werror", "-Wno-unused-function",
           f"-I{INCLUDE}", f"-I{CSRC}"]

@@ -29,15 +29,17 @@ static dgq_status_t check_params(const dgq_params_t *p) {
   if (p->win != kWin) return DGQ_ERR_UNSUPPORTED;
   if (p->max_segments < 1 || p->max_segments > kMaxCuts + 1) return DGQ_ERR_INVALID_ARG;
   if (p->seg_capacity < p->max_segments || p->seg_capacity > kMaxSegCap) return DGQ_ERR_INVALID_ARG;
-  if ((p->flags & ~(uint32_t)DGQ_POLICY_LENGTH_AWARE) != 0) return DGQ_ERR_INVALID_ARG;
+  if ((p->flags & ~(uint32_t)(DGQ_POLICY_LENGTH_AWARE | DGQ_FORMAT_MARKER)) != 0) return DGQ_ERR_INVALID_ARG;
   if (!std::isfinite(p->tau) || p->tau < 1.0) return DGQ_ERR_INVALID_ARG;
   if (!std::isfinite(p->min_var) || p->min_var < 0.0) return DGQ_ERR_INVALID_ARG;
   return DGQ_OK;
 }
 
-static dgq_status_t check_cache(const dgq_cache_t *c, int32_t batch, bool need_stage) {
+// The bit tensor is required in the bitmap format only.
+static dgq_status_t check_cache(const dgq_params_t *p, const dgq_cache_t *c, int32_t batch, bool need_stage) {
   if (c == nullptr) return DGQ_ERR_INVALID_ARG;
-  if (!c->k_pool || !c->v_pool || !c->bits || !c->segs || !c->nseg || !c->tail || !c->status)
+  const bool need_bits = (p->flags & DGQ_FORMAT_MARKER) == 0;
+  if (!c->k_pool || !c->v_pool || (need_bits && !c->bits) || !c->segs || !c->nseg || !c->tail || !c->status)
     return DGQ_ERR_INVALID_ARG;
   if (need_stage && (!c->k_stage || !c->v_stage)) return DGQ_ERR_INVALID_ARG;
   if (!aligned(c->k_pool, 16) || !aligned(c->v_pool, 16) || !aligned(c->segs, 16) ||
@@ -102,7 +104,7 @@ extern "C" dgq_status_t dgq_compress(const dgq_params_t *p, const uint16_t *k, c
   if (p->num_kv_heads > 1 && stride_head < p->head_dim && stride_tok < (int64_t)p->num_kv_heads * p->head_dim)
     return DGQ_ERR_INVALID_ARG;
   if ((st = check_table(p, block_table, max_blocks, max_seq_len)) != DGQ_OK) return st;
-  if ((st = check_cache(cache, batch, false)) != DGQ_OK) return st;
+  if ((st = check_cache(p, cache, batch, false)) != DGQ_OK) return st;
   const size_t need = compress_layout(p, batch, total_tokens, max_seq_len).total;
   if (ws == nullptr || !aligned(ws, 256)) return DGQ_ERR_INVALID_ARG;
   if (ws_bytes < need) return DGQ_ERR_WORKSPACE_TOO_SMALL;
@@ -120,7 +122,7 @@ extern "C" dgq_status_t dgq_append(const dgq_params_t *p, const uint16_t *k_tok,
   if (batch == 0) return DGQ_OK;
   if (!k_tok || !v_tok || !seq_lens || !aligned(k_tok, 16) || !aligned(v_tok, 16)) return DGQ_ERR_INVALID_ARG;
   if (block_table == nullptr || max_blocks < 1) return DGQ_ERR_INVALID_ARG;
-  if ((st = check_cache(cache, batch, true)) != DGQ_OK) return st;
+  if ((st = check_cache(p, cache, batch, true)) != DGQ_OK) return st;
   return launch_append(p, k_tok, v_tok, seq_lens, batch, block_table, max_blocks, cache, stream);
 }
 
@@ -137,7 +139,7 @@ extern "C" dgq_status_t paged_decode_attn_int8(const dgq_params_t *p, const uint
   if (!q || !out || !seq_lens || !aligned(q, 16) || !aligned(out, 16)) return DGQ_ERR_INVALID_ARG;
   if (!std::isfinite(softmax_scale)) return DGQ_ERR_INVALID_ARG;
   if ((st = check_table(p, block_table, max_blocks, max_seq_len)) != DGQ_OK) return st;
-  if ((st = check_cache(cache, batch, false)) != DGQ_OK) return st;
+  if ((st = check_cache(p, cache, batch, false)) != DGQ_OK) return st;
   const size_t need = decode_workspace_bytes(p, batch, max_seq_len);
   if (ws == nullptr || !aligned(ws, 256)) return DGQ_ERR_INVALID_ARG;
   if (ws_bytes < need) return DGQ_ERR_WORKSPACE_TOO_SMALL;
@@ -159,7 +161,7 @@ extern "C" dgq_status_t dgq_append_decode(const dgq_params_t *p, const uint16_t 
   if (!q || !out || !seq_lens || !aligned(q, 16) || !aligned(out, 16)) return DGQ_ERR_INVALID_ARG;
   if (!std::isfinite(softmax_scale)) return DGQ_ERR_INVALID_ARG;
   if ((st = check_table(p, block_table, max_blocks, max_seq_len)) != DGQ_OK) return st;
-  if ((st = check_cache(cache, batch, true)) != DGQ_OK) return st;
+  if ((st = check_cache(p, cache, batch, true)) != DGQ_OK) return st;
   const size_t need = decode_workspace_bytes(p, batch, max_seq_len);
   if (ws == nullptr || !aligned(ws, 256)) return DGQ_ERR_INVALID_ARG;
   if (ws_bytes < need) return DGQ_ERR_WORKSPACE_TOO_SMALL;
@@ -175,7 +177,7 @@ extern "C" dgq_status_t dgq_copy_blocks(const dgq_params_t *p, const dgq_cache_t
   if (n < 0) return DGQ_ERR_INVALID_ARG;
   if (n == 0) return DGQ_OK;
   if (!src_ids || !dst_ids) return DGQ_ERR_INVALID_ARG;
-  if ((st = check_cache(cache, 0, false)) != DGQ_OK) return st;
+  if ((st = check_cache(p, cache, 0, false)) != DGQ_OK) return st;
   return launch_copy_blocks(p, cache, src_ids, dst_ids, n, stream);
 }
 
@@ -187,7 +189,7 @@ extern "C" dgq_status_t dgq_copy_seq_state(const dgq_params_t *p, const dgq_cach
   if (n < 0) return DGQ_ERR_INVALID_ARG;
   if (n == 0) return DGQ_OK;
   if (!src_rows || !dst_rows) return DGQ_ERR_INVALID_ARG;
-  if ((st = check_cache(cache, 0, true)) != DGQ_OK) return st;
+  if ((st = check_cache(p, cache, 0, true)) != DGQ_OK) return st;
   return launch_copy_seq_state(p, cache, src_rows, dst_rows, n, stream);
 }
 
@@ -201,7 +203,7 @@ static dgq_status_t check_swap(const dgq_params_t *p, const dgq_cache_t *cache, 
                                size_t staging_bytes) {
   dgq_status_t st = check_params(p);
   if (st != DGQ_OK) return st;
-  if ((st = check_cache(cache, 0, true)) != DGQ_OK) return st;
+  if ((st = check_cache(p, cache, 0, true)) != DGQ_OK) return st;
   if (row < 0 || row >= cache->batch || n_blocks < 0 || (n_blocks > 0 && ids == nullptr))
     return DGQ_ERR_INVALID_ARG;
   if (staging == nullptr || !aligned(staging, 16)) return DGQ_ERR_INVALID_ARG;
@@ -223,6 +225,21 @@ extern "C" dgq_status_t dgq_swap_in(const dgq_params_t *p, const dgq_cache_t *ca
   const dgq_status_t st = check_swap(p, cache, row, ids, n_blocks, staging, staging_bytes);
   if (st != DGQ_OK) return st;
   return launch_swap(p, cache, row, ids, n_blocks, staging, const_cast<void *>(host_src), false, stream);
+}
+
+extern "C" dgq_status_t dgq_marker_bits(const dgq_params_t *p, const dgq_cache_t *cache,
+                                        const int32_t *block_table, int32_t max_blocks,
+                                        const int32_t *seq_lens, int32_t batch, int32_t max_seq_len,
+                                        uint8_t *bits_out, hipStream_t stream) {
+  dgq_status_t st = check_params(p);
+  if (st != DGQ_OK) return st;
+  if ((p->flags & DGQ_FORMAT_MARKER) == 0) return DGQ_ERR_INVALID_ARG;
+  if (batch < 0 || max_seq_len < 0) return DGQ_ERR_INVALID_ARG;
+  if (batch == 0) return DGQ_OK;
+  if (!seq_lens || !bits_out) return DGQ_ERR_INVALID_ARG;
+  if ((st = check_table(p, block_table, max_blocks, max_seq_len)) != DGQ_OK) return st;
+  if ((st = check_cache(p, cache, batch, false)) != DGQ_OK) return st;
+  return launch_marker_bits(p, cache, block_table, max_blocks, seq_lens, batch, max_seq_len, bits_out, stream);
 }
 
 static dgq_status_t check_g64_cache(const dgq_g64_cache_t *c) {

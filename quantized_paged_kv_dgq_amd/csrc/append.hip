@@ -30,6 +30,7 @@ AppendArgs make_append_args(const dgq_params_t *p, const uint16_t *k_tok, const 
   a.num_blocks = cache->num_blocks;
   a.tau = p->tau;
   a.qfloor = variance_floor_q(p->min_var, p->head_dim);
+  a.fmt = code_format(p);
   a.cache = *cache;
   return a;
 }

@@ -25,6 +25,7 @@ struct AppendArgs {
   int32_t max_blocks, hkv, seg_cap, num_blocks;
   double tau;
   double qfloor;   // variance floor on the Q scale (0 = off)
+  CodeFormat fmt;
   dgq_cache_t cache;
 };
 
@@ -195,14 +196,14 @@ __device__ __forceinline__ void append_one(const AppendArgs &a, int b, int h, bo
         row.kmax = rk[1];
         row.vmin = rk[2];
         row.vmax = rk[3];
-        row.kscale = dgq_scale(row.kmin, row.kmax);
-        row.vscale = dgq_scale(row.vmin, row.vmax);
+        row.kscale = dgq_scale(row.kmin, row.kmax, a.fmt.levels);
+        row.vscale = dgq_scale(row.vmin, row.vmax, a.fmt.levels);
         row.reserved = 0;
         a.cache.segs[bh * a.seg_cap + ns] = row;
         ns += 1;
         tl.span_own = 1;
         all = 1;                                 // the span moves to its own range
-        if (r0 > 0) {
+        if (r0 > 0 && !a.fmt.marker) {
           const int blk = a.block_table[(size_t)b * a.max_blocks + r0 / BS];
           uint8_t *byte = a.cache.bits + ((size_t)blk * a.hkv + h) * (BS / 8) + (r0 % BS) / 8;
           *byte = (uint8_t)(*byte | (1u << (r0 % 8)));
@@ -215,8 +216,8 @@ __device__ __forceinline__ void append_one(const AppendArgs &a, int b, int h, bo
       row.kmax = rk[1];
       row.vmin = rk[2];
       row.vmax = rk[3];
-      row.kscale = dgq_scale(row.kmin, row.kmax);
-      row.vscale = dgq_scale(row.vmin, row.vmax);
+      row.kscale = dgq_scale(row.kmin, row.kmax, a.fmt.levels);
+      row.vscale = dgq_scale(row.vmin, row.vmax, a.fmt.levels);
       a.cache.segs[bh * a.seg_cap + ns - 1] = row;
     }
     ns_sh = ns;
@@ -236,7 +237,11 @@ __device__ __forceinline__ void append_one(const AppendArgs &a, int b, int h, bo
   // 5. encode with the chosen segment's range: the whole span when that range changed (a new row,
   // or the span's own row widened), else only the new token (every other span code is unchanged)
   const dgq_seg_t row = chosen;
-  const float kinv = dgq_inv(row.kmin, row.kmax), vinv = dgq_inv(row.vmin, row.vmax);
+  const float lv = a.fmt.levels;
+  const int low = a.fmt.low;
+  const float kinv = dgq_inv(row.kmin, row.kmax, lv), vinv = dgq_inv(row.vmin, row.vmax, lv);
+  // marker format: the span's own segment starts at r0, whose first key byte is the marker
+  const bool mark = a.fmt.marker && own_now && r0 > 0;
   const int32_t *bt = a.block_table + (size_t)b * a.max_blocks;
   const int blk = bt[r0 / BS];
   int8_t *kt = a.cache.k_pool + ((size_t)blk * a.hkv + h) * (size_t)BS * D;
@@ -246,8 +251,10 @@ __device__ __forceinline__ void append_one(const AppendArgs &a, int b, int h, bo
     const int s = slot0 + enc_first + x / D, d = x % D;
     const float kx = half_bits_to_float(ks[s * D + d]);
     const float vx = half_bits_to_float(vs[s * D + d]);
-    kt[k_tile_offset<D, BS>(s, d)] = (int8_t)dgq_encode_value(kx, row.kmin, kinv);
-    vt[v_tile_offset<D, BS>(s, d)] = (int8_t)dgq_encode_value(vx, row.vmin, vinv);
+    uint32_t kc = (uint32_t)(dgq_encode_value(kx, row.kmin, kinv, lv, low) & 0xFF);
+    if (mark && s == slot0 && d == 0) kc = dgq_marker_byte(kc);
+    kt[k_tile_offset<D, BS>(s, d)] = (int8_t)kc;
+    vt[v_tile_offset<D, BS>(s, d)] = (int8_t)dgq_encode_value(vx, row.vmin, vinv, lv, low);
   }
 
   // 6. seal a full block: the ring keeps the moments of the last 16 sealed tokens

@@ -34,6 +34,7 @@ struct CompressArgs {
   double tau;
   double qfloor;        // variance floor on the Q scale (0 = off)
   int32_t length_aware; // DGQ_POLICY_LENGTH_AWARE: per-sequence segment cap
+  CodeFormat fmt;
   // workspace
   int32_t *ws_a;        // [hkv][total]
   int64_t *ws_b;        // [hkv][total]
@@ -372,8 +373,8 @@ __global__ __launch_bounds__(256) void select_kernel(CompressArgs a) {
       row.kmax = r.y + 0.0f;
       row.vmin = r.z + 0.0f;
       row.vmax = r.w + 0.0f;
-      row.kscale = dgq_scale(row.kmin, row.kmax);
-      row.vscale = dgq_scale(row.vmin, row.vmax);
+      row.kscale = dgq_scale(row.kmin, row.kmax, a.fmt.levels);
+      row.vscale = dgq_scale(row.vmin, row.vmax, a.fmt.levels);
       row.reserved = 0;
       a.cache.segs[bh * a.seg_cap + sgi] = row;
     }
@@ -720,8 +721,8 @@ __global__ __launch_bounds__(kSmallThreads) void select_small_kernel(CompressArg
     row.kmax = r.y + 0.0f;
     row.vmin = r.z + 0.0f;
     row.vmax = r.w + 0.0f;
-    row.kscale = dgq_scale(row.kmin, row.kmax);
-    row.vscale = dgq_scale(row.vmin, row.vmax);
+    row.kscale = dgq_scale(row.kmin, row.kmax, a.fmt.levels);
+    row.vscale = dgq_scale(row.vmin, row.vmax, a.fmt.levels);
     row.reserved = 0;
     a.cache.segs[bh * a.seg_cap + tid] = row;
   }
@@ -764,9 +765,9 @@ __global__ __launch_bounds__(256) void encode_kernel(CompressArgs a) {
     const dgq_seg_t row = a.cache.segs[bh * a.seg_cap + tid];
     s_start[tid] = row.start;
     s_kmin[tid] = row.kmin;
-    s_kinv[tid] = dgq_inv(row.kmin, row.kmax);
+    s_kinv[tid] = dgq_inv(row.kmin, row.kmax, a.fmt.levels);
     s_vmin[tid] = row.vmin;
-    s_vinv[tid] = dgq_inv(row.vmin, row.vmax);
+    s_vinv[tid] = dgq_inv(row.vmin, row.vmax, a.fmt.levels);
   }
   __syncthreads();
   if (tid < kChunk) {
@@ -794,6 +795,8 @@ __global__ __launch_bounds__(256) void encode_kernel(CompressArgs a) {
   const int nblk_seq = (L + BS - 1) / BS;
   const size_t tile_bytes = (size_t)BS * D;
 
+  const float lv = a.fmt.levels;
+  const int low = a.fmt.low;
   // keys: one unit = 16 channels of one token = 16 contiguous bytes of the tile
   constexpr int KU = kChunk * D / 16;
   for (int u = tid; u < KU; u += 256) {
@@ -809,9 +812,12 @@ __global__ __launch_bounds__(256) void encode_kernel(CompressArgs a) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const float x = half_bits_to_float(e & 1 ? ws[e >> 1] >> 16 : ws[e >> 1] & 0xFFFFu);
-      const uint32_t c = (uint32_t)(dgq_encode_value(x, mn, inv) & 0xFF);
+      const uint32_t c = (uint32_t)(dgq_encode_value(x, mn, inv, lv, low) & 0xFF);
       outw[e >> 2] |= c << (8 * (e & 3));
     }
+    // marker format: the first key byte of every segment but the first is its marker
+    if (a.fmt.marker && d0 == 0 && sg > 0 && s_start[sg] == tok)
+      outw[0] = (outw[0] & ~0xFFu) | dgq_marker_byte(outw[0] & 0xFFu);
     bool bad_blk = false;
     const int blk = checked_block(bt[tok / BS], a.cache.num_blocks, bad_blk);
     if (bad_blk) {
@@ -847,7 +853,7 @@ __global__ __launch_bounds__(256) void encode_kernel(CompressArgs a) {
       if (t0 + tau < L) {
         const int sg = segidx[tau];
         const float x = half_bits_to_float(vt[tau * VROW + d]);
-        c = (uint32_t)(dgq_encode_value(x, s_vmin[sg], s_vinv[sg]) & 0xFF);
+        c = (uint32_t)(dgq_encode_value(x, s_vmin[sg], s_vinv[sg], lv, low) & 0xFF);
       }
       outw[e >> 2] |= c << (8 * (e & 3));
     }
@@ -865,8 +871,9 @@ __global__ __launch_bounds__(256) void encode_kernel(CompressArgs a) {
     store_stream(tilep + off, outw);
   }
 
-  // boundary bits: 8 bytes per chunk (one 64-token block, or four 16-token blocks)
-  if (tid < kChunk / 8) {
+  // boundary bits: 8 bytes per chunk (one 64-token block, or four 16-token blocks); none in the
+  // marker format
+  if (!a.fmt.marker && tid < kChunk / 8) {
     const int tok0 = t0 + 8 * tid;
     const int lblk = tok0 / BS;
     if (lblk < nblk_seq) {
@@ -960,6 +967,7 @@ dgq_status_t launch_compress(const dgq_params_t *p, const uint16_t *k, const uin
   a.tau = p->tau;
   a.qfloor = variance_floor_q(p->min_var, p->head_dim);
   a.length_aware = (p->flags & DGQ_POLICY_LENGTH_AWARE) != 0;
+  a.fmt = code_format(p);
   a.ws_a = reinterpret_cast<int32_t *>(w + l.a_off);
   a.ws_b = reinterpret_cast<int64_t *>(w + l.b_off);
   a.ws_score = reinterpret_cast<double *>(w + l.score_off);

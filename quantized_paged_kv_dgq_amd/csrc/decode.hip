@@ -100,9 +100,9 @@ __global__ __launch_bounds__(64 * kWaves) void decode_partition_kernel(DecodeArg
       const dgq_seg_t sg = seg_raw;
       s_start = sg.start;
       s_ks = sg.kscale;
-      s_midk = sg.kmin + 128.0f * sg.kscale;
+      s_midk = sg.kmin + a.code_mid * sg.kscale;
       s_vs = sg.vscale;
-      s_midv = sg.vmin + 128.0f * sg.vscale;
+      s_midv = sg.vmin + a.code_mid * sg.vscale;
     }
     // the largest value scale among the segments this wave's tokens can use (rows starting after
     // its last token cannot apply; leaving them out also keeps the result equal to the fused
@@ -425,9 +425,9 @@ __device__ __forceinline__ void decode_body(const DecodeArgs &a, const AppendArg
       const dgq_seg_t sg = appended && lane == aout.use_row ? aout.chosen : seg_raw;
       s_start = sg.start;
       s_ks = sg.kscale;
-      s_midk = sg.kmin + 128.0f * sg.kscale;
+      s_midk = sg.kmin + a.code_mid * sg.kscale;
       s_vs = sg.vscale;
-      s_midv = sg.vmin + 128.0f * sg.vscale;
+      s_midv = sg.vmin + a.code_mid * sg.vscale;
     }
     // the largest value scale among the segments this wave's tokens can use (rows starting after
     // its last token are left out: they cannot apply, and in the fused step the open span's row
@@ -756,6 +756,7 @@ DecodeArgs make_decode_args(const dgq_params_t *p, const uint16_t *q, const int8
   a.max_seq_len = max_seq_len;
   a.num_blocks = num_blocks;
   a.sm_log2 = softmax_scale * 1.4426950408889634f;
+  a.code_mid = (float)-code_format(p).low;
   return a;
 }
 

@@ -34,6 +34,7 @@ struct DecodeArgs {
   unsigned long long *status;
   int32_t hkv, hq, max_blocks, seg_cap, part_tokens, nparts, max_seq_len, num_blocks;
   float sm_log2;    // softmax_scale * log2(e)
+  float code_mid;   // DGQ: -(code of a segment's minimum): 128, or 127 in the marker format
 };
 
 // x from the lane whose index differs in bit 0 (XOR1) or bit 1 (XOR2), within quads (DPP).

@@ -43,6 +43,19 @@ inline dgq_status_t check_launch(const char *where) {
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// How codes are stored.  Bitmap format: 255 steps between min and max, the minimum at code -128,
+// the identifier in the bit tensor.  Marker format (DGQ article 3.2): 253 steps, the minimum at
+// -127, the two end byte values free for the markers that replace the first key byte of a segment.
+struct CodeFormat {
+  float levels;    // steps between min and max
+  int32_t low;     // code of the minimum
+  int32_t marker;  // 1: marker format
+};
+inline CodeFormat code_format(const dgq_params_t *p) {
+  const bool m = (p->flags & DGQ_FORMAT_MARKER) != 0;
+  return CodeFormat{m ? 253.0f : 255.0f, m ? -127 : -128, m ? 1 : 0};
+}
+
 // ---- decode ----
 struct DecodePlan {
   int part_tokens;  // tokens per workgroup, multiple of kChunk
@@ -133,28 +146,37 @@ __device__ __forceinline__ int v_tile_offset(int tau, int d) {
   }
 }
 
-// DGQ code of one value (exact IEEE steps: subtract, multiply, round to nearest even, clamp).
-__device__ __forceinline__ int dgq_encode_value(float x, float mn, float inv) {
+// DGQ code of one value (exact IEEE steps: subtract, multiply, round to nearest even, clamp to
+// [0, levels], shift by the code of the minimum).
+__device__ __forceinline__ int dgq_encode_value(float x, float mn, float inv, float levels = 255.0f,
+                                                int low = -128) {
 #pragma clang fp contract(off)
   const float dlt = x - mn;
   const float u = dlt * inv;
   float r = __builtin_rintf(u);
-  r = fminf(fmaxf(r, 0.0f), 255.0f);
-  return (int)r - 128;
+  r = fminf(fmaxf(r, 0.0f), levels);
+  return (int)r + low;
 }
 
-// fp32(255 / fp32(mx - mn)), or 0 for an empty range.  The float64 quotient rounded to float32
+// fp32(levels / fp32(mx - mn)), or 0 for an empty range.  The float64 quotient rounded to float32
 // equals the correctly rounded float32 quotient (53 >= 2*24 + 2 bits).
-__device__ __forceinline__ float dgq_inv(float mn, float mx) {
+__device__ __forceinline__ float dgq_inv(float mn, float mx, float levels = 255.0f) {
 #pragma clang fp contract(off)
   const float diff = mx - mn;
-  return diff > 0.0f ? (float)(255.0 / (double)diff) : 0.0f;
+  return diff > 0.0f ? (float)((double)levels / (double)diff) : 0.0f;
 }
 
-__device__ __forceinline__ float dgq_scale(float mn, float mx) {
+// fp32(fp32(mx - mn) / levels), correctly rounded by the same argument.
+__device__ __forceinline__ float dgq_scale(float mn, float mx, float levels = 255.0f) {
 #pragma clang fp contract(off)
   const float diff = mx - mn;
-  return (float)((double)diff / 255.0);
+  return (float)((double)diff / (double)levels);
+}
+
+// Marker byte that replaces the code byte c of a segment's first key element (marker format):
+// 127 (0x7F) for a code in the upper half of the range, -128 (0x80) for one in the lower half.
+__device__ __forceinline__ uint32_t dgq_marker_byte(uint32_t c) {
+  return (c & 0x80u) ? 0x80u : 0x7Fu;
 }
 
 // Bounds of sequence b in the packed input, clamped so that no kernel reads past max_seq_len or

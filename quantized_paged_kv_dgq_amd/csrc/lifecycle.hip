@@ -7,15 +7,13 @@
 
 namespace dgq {
 
-namespace {
-
 constexpr int kThreads = 256;
 constexpr int kParts = 5;
 
 // Sizes of the pieces a state row and a block are made of (bytes, host-computed).
 struct Geometry {
   int64_t tile;       // codes of one block for all kv heads: hkv * block_size * head_dim
-  int64_t bits;       // boundary bits of one block for all kv heads: hkv * block_size / 8
+  int64_t bits;       // boundary bits of one block for all kv heads: hkv * block_size / 8 (or 0)
   int64_t segs;       // segment-table rows of one sequence: hkv * seg_capacity * 32
   int64_t nseg;       // row counts of one sequence: hkv * 4
   int64_t tail;       // append states of one sequence: hkv * 224
@@ -24,11 +22,11 @@ struct Geometry {
   int64_t block_img;  // image bytes of one block
 };
 
-Geometry geometry(const dgq_params_t *p) {
+static Geometry geometry(const dgq_params_t *p) {
   Geometry g;
   const int64_t h = p->num_kv_heads;
   g.tile = h * p->block_size * p->head_dim;
-  g.bits = h * p->block_size / 8;
+  g.bits = (p->flags & DGQ_FORMAT_MARKER) ? 0 : h * p->block_size / 8;   // no bit tensor in the marker format
   g.segs = h * p->seg_capacity * (int64_t)sizeof(dgq_seg_t);
   g.nseg = h * 4;
   g.tail = h * (int64_t)sizeof(dgq_tail_t);
@@ -156,8 +154,6 @@ __global__ __launch_bounds__(kThreads) void swap_kernel(dgq_cache_t c, Geometry 
   if (PACK) move(img_side, cache_side);
   else move(cache_side, img_side);
 }
-
-}  // namespace
 
 size_t swap_image_bytes(const dgq_params_t *p, int32_t n_blocks) {
   const Geometry g = geometry(p);

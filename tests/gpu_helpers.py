@@ -67,6 +67,29 @@ def cache_from_oracle(params: Q.DGQParams, heads, table: np.ndarray, num_blocks:
     return cache
 
 
+def fmt_of(params: Q.DGQParams) -> str:
+    return "marker" if params.marker else "bitmap"
+
+
+def identifier_bits(cache: Q.DGQCache, table: np.ndarray, lens) -> np.ndarray:
+    """The boundary bits of a cache in the bit-tensor layout, on the host: the bit tensor itself,
+    or (marker format) the bits read back from the marker bytes by dgq_marker_bits."""
+    if cache.bits is not None:
+        return cache.bits.cpu().numpy()
+    lens = np.asarray(lens, np.int32)
+    out = Q.dgq_marker_bits(cache.params, cache, torch.from_numpy(np.ascontiguousarray(table, np.int32)).cuda(),
+                            torch.from_numpy(lens).cuda(), int(max(lens.max(initial=0), 0)))
+    return out.cpu().numpy()
+
+
+def compare_markers(got_k: np.ndarray, ref_k: np.ndarray, what: str) -> None:
+    """Marker bytes (-128 / 127) sit at exactly the same places (no 1-LSB slack for them)."""
+    gm = (got_k == -128) | (got_k == 127)
+    rm = (ref_k == -128) | (ref_k == 127)
+    assert np.array_equal(gm, rm), f"{what}: marker positions differ"
+    assert np.array_equal(got_k[gm], ref_k[rm]), f"{what}: marker values differ"
+
+
 def oracle_decode(q16: np.ndarray, heads, lens, hkv: int, group: int) -> np.ndarray:
     """fp64 attention of q [B][Hq][D] over the oracle's dequantized cache."""
     batch, hq, d = q16.shape

@@ -77,7 +77,7 @@ def test_workspace_sizes(lib):
     assert lib.dgq_compress_workspace_size(ctypes.byref(p), 16, 16 * 8192, 8192) > 16 * 8192 * 8 * 20
     assert lib.dgq_decode_workspace_size(ctypes.byref(p), 16, 8192) > 0
     for bad in (_params(head_dim=96), _params(block_size=32), _params(win=8), _params(num_q_heads=20),
-                _params(max_segments=9), _params(seg_capacity=4), _params(tau=0.5), _params(flags=2),
+                _params(max_segments=9), _params(seg_capacity=4), _params(tau=0.5), _params(flags=4),
                 _params(min_var=-1.0), _params(min_var=float("nan"))):
         assert lib.dgq_compress_workspace_size(ctypes.byref(bad), 1, 10, 10) == 0
         assert lib.dgq_decode_workspace_size(ctypes.byref(bad), 1, 10) == 0
@@ -86,7 +86,7 @@ def test_workspace_sizes(lib):
 def test_policy_params_accepted(lib):
     """The length-aware flag and a variance floor are valid parameters."""
     for good in (_params(flags=_lib.DGQ_POLICY_LENGTH_AWARE), _params(min_var=0.01),
-                 _params(flags=1, min_var=1e-4)):
+                 _params(flags=1, min_var=1e-4), _params(flags=_lib.DGQ_FORMAT_MARKER), _params(flags=3)):
         assert lib.dgq_compress_workspace_size(ctypes.byref(good), 1, 10, 10) > 0
 
 
@@ -219,3 +219,25 @@ def test_lifecycle_argument_checks(lib):
     assert lib.dgq_swap_in(ctypes.byref(p), ctypes.byref(cache), 0, fake, 3, ctypes.c_void_p((1 << 20) + 8),
                            need, None, None) == E
     assert lib.dgq_swap_out(ctypes.byref(p), ctypes.byref(nostage), 0, fake, 3, fake, need, None, None) == E
+
+
+def test_marker_format_checks(lib):
+    """The marker format needs no bit tensor; the bitmap format does; the marker read-back is
+    refused for a bitmap-format cache."""
+    fake = ctypes.c_void_p(1 << 20)
+    nobits = _lib.Cache(fake, fake, None, fake, fake, fake, fake, fake, fake, 64, 4)
+    E = _lib.DGQ_ERR_INVALID_ARG
+    bitmap, marker = _params(), _params(flags=_lib.DGQ_FORMAT_MARKER)
+    # bitmap: a missing bit tensor is rejected before anything is queued
+    assert lib.dgq_append(ctypes.byref(bitmap), fake, fake, fake, 1, fake, 4, ctypes.byref(nobits), None) == E
+    assert lib.dgq_marker_bits(ctypes.byref(bitmap), ctypes.byref(nobits), fake, 4, fake, 1, 64, fake, None) == E
+    # marker: the same cache passes the bit-tensor check and fails only on the later ones
+    assert lib.dgq_marker_bits(ctypes.byref(marker), ctypes.byref(nobits), fake, 4, None, 1, 64, fake, None) == E
+    assert lib.dgq_marker_bits(ctypes.byref(marker), ctypes.byref(nobits), fake, 4, fake, 1, 65, fake, None) == E
+    assert lib.dgq_marker_bits(ctypes.byref(marker), ctypes.byref(nobits), fake, 4, fake, 0, 64, None, None) == 0
+    assert lib.paged_decode_attn_int8(ctypes.byref(marker), fake, ctypes.byref(nobits), fake, 4, fake, 1, 64,
+                                      1.0, fake, fake, 16, None) == _lib.DGQ_ERR_WORKSPACE_TOO_SMALL
+    # swap images carry no bits in the marker format
+    pb = lib.dgq_swap_image_bytes(ctypes.byref(bitmap), 10)
+    pm = lib.dgq_swap_image_bytes(ctypes.byref(marker), 10)
+    assert pb - pm == 10 * 16          # 8 heads x 16 tokens / 8 = 16 bytes of bits per block

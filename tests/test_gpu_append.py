@@ -39,7 +39,7 @@ def run_stream(cfg, seed, steps, params=None, check_every=None, k=None, v=None, 
             kk = k[cu[b]:cu[b] + lens[b], h]
             vv = v[cu[b]:cu[b] + lens[b], h]
             states[(b, h)] = O.AppendState(O.compress_head(kk, vv, p.max_segments, p.tau, p.min_var,
-                                                           params.length_aware),
+                                                           params.length_aware, H.fmt_of(params)),
                                            kk, p.block_size, p.seg_capacity, p.tau, p.min_var)
     check_every = check_every or steps
     for s in range(steps):
@@ -61,12 +61,14 @@ def check_state(cfg, params, cache, states, table, cur_lens, qseed):
     p = params.c
     heads = {key: st.snapshot() for key, st in states.items()}
     H.compare_segments(cache, heads, cfg.batch, cfg.hkv)
-    bits = cache.bits.cpu().numpy()
+    bits = H.identifier_bits(cache, table, cur_lens)
     tails = cache.tail.cpu().numpy()
     for (b, h), hc in heads.items():
         kc, vc = H.read_codes(cache, table, b, h, hc.length)
         H.compare_codes(kc, hc.kcodes, f"K codes b{b} h{h}")
         H.compare_codes(vc, hc.vcodes, f"V codes b{b} h{h}")
+        if params.marker:
+            H.compare_markers(kc, hc.kcodes, f"K markers b{b} h{h}")
         assert np.array_equal(PL.gather_bits(bits, table[b], h, hc.length, p.block_size), hc.bits), (b, h)
         st = states[(b, h)]
         tl = tails[b, h]
@@ -133,3 +135,15 @@ def test_stream_table_full_clamps_and_counts():
     H.say("append stream clamp")
     cache, states = run_stream(cfg, 3, 64, params=params, check_every=16, k=k, v=v, cu=cu, lens=lens)
     assert sum(st.clamped for st in states.values()) > 0
+
+
+@pytest.mark.parametrize("cid,over,steps", [
+    (5, dict(batch=3, seq_len=200, append_steps=160), 160),
+    (2, dict(batch=2, seq_len=250, append_steps=90), 90),
+], ids=["bs64", "bs16"])
+def test_stream_marker_format(cid, over, steps):
+    """Appends in the marker format: every span that opens a segment writes its marker at r0,
+    no bit tensor is touched; against the oracle's marker-format AppendState."""
+    cfg = dgq_data.get_config(cid, **over)
+    H.say("append marker format", cid, over)
+    run_stream(cfg, 17, steps, params=H.params_for(cfg, marker=True), check_every=steps // 3)

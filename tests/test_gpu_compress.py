@@ -40,9 +40,10 @@ def compress_and_check(cfg, seed, params=None, k=None, v=None, cu=None, lens=Non
         for h in range(cfg.hkv):
             kk = k[cu[b]:cu[b + 1], h]
             vv = v[cu[b]:cu[b + 1], h]
-            heads[(b, h)] = O.compress_head(kk, vv, p.max_segments, p.tau, p.min_var, params.length_aware)
+            heads[(b, h)] = O.compress_head(kk, vv, p.max_segments, p.tau, p.min_var, params.length_aware,
+                                            H.fmt_of(params))
     H.compare_segments(cache, heads, cfg.batch, cfg.hkv)
-    bits = cache.bits.cpu().numpy()
+    bits = H.identifier_bits(cache, table, lens)
     tails = cache.tail.cpu().numpy()
     for b in range(cfg.batch):
         for h in range(cfg.hkv):
@@ -50,6 +51,9 @@ def compress_and_check(cfg, seed, params=None, k=None, v=None, cu=None, lens=Non
             kc, vc = H.read_codes(cache, table, b, h, hc.length)
             H.compare_codes(kc, hc.kcodes, f"K codes b{b} h{h}")
             H.compare_codes(vc, hc.vcodes, f"V codes b{b} h{h}")
+            if params.marker:
+                H.compare_markers(kc, hc.kcodes, f"K markers b{b} h{h}")
+                H.compare_markers(vc, hc.vcodes, f"V markers b{b} h{h}")
             got_bits = PL.gather_bits(bits, table[b], h, hc.length, p.block_size)
             assert np.array_equal(got_bits, hc.bits), (b, h)
             # append state: r0 = length, ring = moments of the last min(16, L) tokens
@@ -113,6 +117,27 @@ def test_compress_length_cap_and_variance_floor(name, cid, over, length_aware, m
     cache, heads, _ = compress_and_check(cfg, 21, params=params)
     counts = np.bincount([len(hc.segs) for hc in heads.values()], minlength=6)
     print(f"{name}: segments per head {counts.tolist()}")
+
+
+MARKER_CASES = [
+    ("tiny", 1, {}),
+    ("llama_bs16", 2, dict(batch=2, seq_len=1500)),
+    ("long_path_bs64_outliers", 3, dict(seq_len=12000)),
+    ("mha_g1_mixed", 4, dict(batch=5, seq_len=900, min_len=1)),
+    ("d64_g2_bs64", 1, dict(hq=4, block_size=64, seq_len=1111, batch=2)),
+]
+
+
+@pytest.mark.parametrize("name,cid,over", MARKER_CASES, ids=[c[0] for c in MARKER_CASES])
+def test_compress_marker_format(name, cid, over):
+    """The marker format (DGQ article 3.2): 254-level codes with the identifier in the key bytes,
+    no bit tensor; codes, markers, scales and the read-back identifier against the oracle, then
+    decode; on the fused short-sequence and the tiled long-sequence selection paths."""
+    cfg = dgq_data.get_config(cid, **over)
+    H.say("compress marker format", name, over)
+    cache, heads, _ = compress_and_check(cfg, 31, params=H.params_for(cfg, marker=True))
+    assert cache.bits is None
+    assert sum(len(hc.segs) - 1 for hc in heads.values()) > 0
 
 
 def _custom(cfg, seqs):

@@ -21,16 +21,18 @@ def _same_cache(c1, c2, table, lens, p):
     assert torch.equal(c1.segs, c2.segs)
     assert torch.equal(c1.tail, c2.tail)
     assert torch.equal(c1.status, c2.status)
+    assert (c1.bits is None) == (c2.bits is None)
     k1, k2 = c1.k_pool.cpu().numpy(), c2.k_pool.cpu().numpy()
     v1, v2 = c1.v_pool.cpu().numpy(), c2.v_pool.cpu().numpy()
-    b1, b2 = c1.bits.cpu().numpy(), c2.bits.cpu().numpy()
+    b1, b2 = (None, None) if c1.bits is None else (c1.bits.cpu().numpy(), c2.bits.cpu().numpy())
     koff, voff = PL.k_offsets(p.block_size, p.head_dim), PL.v_offsets(p.block_size, p.head_dim)
     for b, n in enumerate(lens):
         for h in range(p.num_kv_heads):
             assert np.array_equal(PL.gather_head(k1, table[b], h, n, koff), PL.gather_head(k2, table[b], h, n, koff))
             assert np.array_equal(PL.gather_head(v1, table[b], h, n, voff), PL.gather_head(v2, table[b], h, n, voff))
-            assert np.array_equal(PL.gather_bits(b1, table[b], h, n, p.block_size),
-                                  PL.gather_bits(b2, table[b], h, n, p.block_size))
+            if b1 is not None:
+                assert np.array_equal(PL.gather_bits(b1, table[b], h, n, p.block_size),
+                                      PL.gather_bits(b2, table[b], h, n, p.block_size))
 
 
 def run_fused(cfg, seed, steps, checks, params=None):
@@ -55,7 +57,7 @@ def run_fused(cfg, seed, steps, checks, params=None):
         for h in range(hkv):
             kk, vv = k[cu[b]:cu[b] + lens[b], h], v[cu[b]:cu[b] + lens[b], h]
             states[(b, h)] = O.AppendState(O.compress_head(kk, vv, p.max_segments, p.tau, p.min_var,
-                                                           params.length_aware),
+                                                           params.length_aware, H.fmt_of(params)),
                                            kk, p.block_size, p.seg_capacity, p.tau, p.min_var)
     for s in range(steps):
         pos = lens + s
@@ -107,3 +109,11 @@ def test_fused_with_policies():
     cfg = dgq_data.get_config(5, batch=2, seq_len=300, append_steps=100)
     H.say("fused with policies")
     run_fused(cfg, 43, 100, (0, 99), params=H.params_for(cfg, length_aware=True, min_var=1e-3))
+
+
+def test_fused_marker_format():
+    """The fused step in the marker format: the appending workgroup writes the marker and the decode
+    uses the marker format's dequantization."""
+    cfg = dgq_data.get_config(5, batch=2, seq_len=260, append_steps=90)
+    H.say("fused marker format")
+    run_fused(cfg, 44, 90, (0, 45, 89), params=H.params_for(cfg, marker=True))

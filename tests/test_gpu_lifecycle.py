@@ -24,14 +24,16 @@ def _oracle_states(params, k, v, c0, length):
     out = {}
     for h in range(p.num_kv_heads):
         kk, vv = k[c0:c0 + length, h], v[c0:c0 + length, h]
-        out[h] = O.AppendState(O.compress_head(kk, vv, p.max_segments, p.tau, p.min_var, params.length_aware),
+        out[h] = O.AppendState(O.compress_head(kk, vv, p.max_segments, p.tau, p.min_var, params.length_aware,
+                                               H.fmt_of(params)),
                                kk, p.block_size, p.seg_capacity, p.tau, p.min_var)
     return out
 
 
 def _block_bytes(cache, ids):
     i = torch.tensor(ids, dtype=torch.long, device=cache.k_pool.device)
-    return (cache.k_pool[i].cpu().numpy(), cache.v_pool[i].cpu().numpy(), cache.bits[i].cpu().numpy())
+    bits = None if cache.bits is None else cache.bits[i].cpu().numpy()
+    return (cache.k_pool[i].cpu().numpy(), cache.v_pool[i].cpu().numpy(), bits)
 
 
 def _check_rows(cache, params, table, states, rows, lens, qseed, cfg):
@@ -39,13 +41,15 @@ def _check_rows(cache, params, table, states, rows, lens, qseed, cfg):
     p = params.c
     heads = {(r, h): states[r][h].snapshot() for r in rows for h in range(p.num_kv_heads)}
     starts, prm, nseg = cache.segment_table()
-    bits = cache.bits.cpu().numpy()
+    bits = H.identifier_bits(cache, table, lens)
     for (r, h), hc in heads.items():
         assert nseg[r, h] == len(hc.segs), (r, h)
         assert list(starts[r, h, :len(hc.segs)]) == [s.start for s in hc.segs], (r, h)
         kc, vc = H.read_codes(cache, table, r, h, hc.length)
         H.compare_codes(kc, hc.kcodes, f"K r{r} h{h}")
         H.compare_codes(vc, hc.vcodes, f"V r{r} h{h}")
+        if params.marker:
+            H.compare_markers(kc, hc.kcodes, f"K markers r{r} h{h}")
         assert np.array_equal(PL.gather_bits(bits, table[r], h, hc.length, p.block_size), hc.bits), (r, h)
     q16 = dgq_data.queries(cfg, qseed)
     dl = torch.from_numpy(np.asarray(lens, np.int32)).cuda()
@@ -57,14 +61,15 @@ def _check_rows(cache, params, table, states, rows, lens, qseed, cfg):
     assert err <= 2e-3
 
 
-@pytest.mark.parametrize("l0,steps", [(1000, 90), (960, 70)], ids=["mid_block", "block_aligned"])
-def test_fork_with_copy_on_write(l0, steps):
+@pytest.mark.parametrize("l0,steps,marker", [(1000, 90, False), (960, 70, False), (1000, 90, True)],
+                         ids=["mid_block", "block_aligned", "mid_block_marker"])
+def test_fork_with_copy_on_write(l0, steps, marker):
     """Row 0 is compressed, row 1 forks from it (shared blocks, copied state row); both then append
     their own tokens.  The first append into the shared tail block copies it for one of them; the
     frozen shared blocks are never written."""
     cfg = dgq_data.get_config(5, batch=2, seq_len=l0 + steps, append_steps=0)
-    H.say("fork with copy-on-write", l0, steps)
-    params = H.params_for(cfg)
+    H.say("fork with copy-on-write", l0, steps, marker)
+    params = H.params_for(cfg, marker=marker)
     p = params.c
     bs = p.block_size
     k, v, cu, lens = dgq_data.batch_kv(cfg, 7)
@@ -125,19 +130,20 @@ def test_fork_with_copy_on_write(l0, steps):
     assert copies == (1 if l0 % bs else 0)
     after = _block_bytes(cache, frozen)
     for a, b in zip(before, after):
-        assert np.array_equal(a, b), "a frozen shared block was written"
+        assert (a is None and b is None) or np.array_equal(a, b), "a frozen shared block was written"
     for i in frozen:
         assert pool.refcount(int(i)) == 2
     assert int(cache.status[2].item()) == 0
 
 
-def test_swap_out_and_in():
+@pytest.mark.parametrize("marker", [False, True], ids=["bitmap", "marker"])
+def test_swap_out_and_in(marker):
     """Row 1 is swapped out to pinned host memory mid-stream, its blocks and state are overwritten,
     and it is swapped back into other block ids; from then on every decode output and the final
     cache equal those of a twin cache that was never swapped."""
     cfg = dgq_data.get_config(5, batch=3, seq_len=300, append_steps=80)
-    H.say("swap out and in", cfg.batch, cfg.seq_len)
-    params = H.params_for(cfg)
+    H.say("swap out and in", cfg.batch, cfg.seq_len, marker)
+    params = H.params_for(cfg, marker=marker)
     p = params.c
     bs = p.block_size
     k, v, cu, lens = dgq_data.batch_kv(cfg, 9)
@@ -176,7 +182,8 @@ def test_swap_out_and_in():
             idx = torch.from_numpy(ids_old.astype(np.int64)).cuda()
             caches[1].k_pool[idx] = 0x5A
             caches[1].v_pool[idx] = -0x21
-            caches[1].bits[idx] = 0xFF
+            if caches[1].bits is not None:
+                caches[1].bits[idx] = 0xFF
             for t in (caches[1].segs, caches[1].nseg, caches[1].tail, caches[1].k_stage, caches[1].v_stage):
                 t[row].zero_()
             staging.zero_()
