@@ -195,7 +195,48 @@ def cpu_baseline(cfg, seed, budget_s):
                   f"decode = dequantize + float64 attention for the {cfg.group} query heads",
         "compress_tokens_per_s": tokens / t_comp,
         "seconds": t_comp + t_dec,
+        "all_cores": cpu_baseline_parallel(cfg, seed, units[:max(done, 1) * 4]),
     }
+
+
+def _oracle_unit(args):
+    """One (sequence, kv head) unit through the oracle on one core: (compress s, decode s)."""
+    cid, seed, b, h = args
+    from threadpoolctl import threadpool_limits
+
+    import dgq_data
+    from oracle import dgq_oracle as O
+
+    cfg = dgq_data.get_config(cid)
+    q16 = dgq_data.queries(cfg, seed)
+    with threadpool_limits(limits=1):
+        k, v = dgq_data.head_kv(cfg, seed, 0, b, h, cfg.seq_len)
+        t0 = time.perf_counter()
+        hc = O.compress_head(k, v)
+        t1 = time.perf_counter()
+        O.decode_attention(q16[b, h * cfg.group:(h + 1) * cfg.group], hc.khat(), hc.vhat())
+        t2 = time.perf_counter()
+    return t1 - t0, t2 - t1
+
+
+def cpu_baseline_parallel(cfg, seed, units):
+    """The same oracle fanned out over (sequence, kv head) units, one process per allowed core
+    (at most 16): the units are independent.  Each process times its own compress and decode
+    while all of them run; throughput = bytes (tokens) / summed seconds x processes, i.e. the
+    rate of that many cores each busy with the oracle."""
+    import multiprocessing as mp
+
+    cores = max(1, min(16, len(os.sched_getaffinity(0))))
+    args = [(cfg.cid, seed, b, h) for b, h in units]
+    t0 = time.perf_counter()
+    with mp.get_context("fork").Pool(cores) as pool:
+        times = pool.map(_oracle_unit, args, chunksize=1)
+    wall = time.perf_counter() - t0
+    t_comp = float(sum(a for a, _ in times))
+    t_dec = float(sum(b for _, b in times))
+    dec_bytes = len(units) * 2 * cfg.seq_len * cfg.head_dim
+    return {"value": dec_bytes / t_dec * cores / 1e9, "unit": "GB/s", "cores": cores, "units": len(units),
+            "compress_tokens_per_s": len(units) * cfg.seq_len / t_comp * cores, "wall_seconds": wall}
 
 
 def fp16_reference(cfg, k, v, cu, q, k_tok=None, v_tok=None):
