@@ -55,6 +55,19 @@ __device__ __forceinline__ void append_one(const AppendArgs &a, int b, int h, bo
   __shared__ long long tail_b[kWin];
   __shared__ dgq_seg_t chosen;
   __shared__ int reenc_all;                    // 1: every span token's codes change, 0: only the new one
+  __shared__ dgq_seg_t srow[kMaxSegCap];       // the segment table as it was before this append
+  // every load that does not depend on the state goes out at once: the state, the segment rows
+  // and the new token (thread d < D holds channel d)
+  static_assert(D <= 256, "one channel per thread");
+  uint16_t kb = 0, vb = 0;
+  if (tid < D) {
+    kb = a.k_tok[bh * D + tid];
+    vb = a.v_tok[bh * D + tid];
+  }
+  if (tid < a.seg_cap) srow[tid] = a.cache.segs[bh * a.seg_cap + tid];
+  // the new token's block: a consistent state has the open span in that same block
+  const bool t_ok = t >= 0 && t / BS < a.max_blocks;
+  const int blk_t = t_ok ? a.block_table[(size_t)b * a.max_blocks + t / BS] : -1;
   if (tid == 0) {
     tl = a.cache.tail[bh];
     ns_sh = a.cache.nseg[bh];
@@ -65,9 +78,10 @@ __device__ __forceinline__ void append_one(const AppendArgs &a, int b, int h, bo
   const int span_len = t + 1 - r0;             // including the new token
   {
     // the state must place the new token inside the open span's block, and the block must exist
-    bool bad = t < 0 || r0 < 0 || r0 > t || slot0 + span_len > BS || t / BS >= a.max_blocks ||
-               ns_sh < 0 || ns_sh > a.seg_cap || tl.ring_len < 0 || tl.ring_len > kWin;
-    if (!bad) checked_block(a.block_table[(size_t)b * a.max_blocks + r0 / BS], a.cache.num_blocks, bad);
+    // (r0 <= t and slot0 + span_len <= BS put r0 and t in the same block)
+    bool bad = !t_ok || r0 < 0 || r0 > t || slot0 + span_len > BS || ns_sh < 0 || ns_sh > a.seg_cap ||
+               tl.ring_len < 0 || tl.ring_len > kWin;
+    if (!bad) checked_block(blk_t, a.cache.num_blocks, bad);
     if (bad) {
       if (tid == 0) {
         atomicAdd(a.cache.status + 2, 1ull);
@@ -86,10 +100,9 @@ __device__ __forceinline__ void append_one(const AppendArgs &a, int b, int h, bo
   const int slot = t % BS;
   float4 r = make_float4(INFINITY, -INFINITY, INFINITY, -INFINITY);
   float bad = 0.f;
-  for (int d = tid; d < D; d += 256) {
-    const uint16_t kb = a.k_tok[bh * D + d], vb = a.v_tok[bh * D + d];
-    ks[slot * D + d] = kb;
-    vs[slot * D + d] = vb;
+  if (tid < D) {
+    ks[slot * D + tid] = kb;
+    vs[slot * D + tid] = vb;
     const float kx = half_bits_to_float(kb), vx = half_bits_to_float(vb);
     r.x = fminf(r.x, kx);
     r.y = fmaxf(r.y, kx);
@@ -166,7 +179,7 @@ __device__ __forceinline__ void append_one(const AppendArgs &a, int b, int h, bo
     const int base = tl.span_own ? ns - 2 : ns - 1;
     bool want = tl.span_own != 0 || base < 0;
     if (!want) {
-      const dgq_seg_t S = a.cache.segs[bh * a.seg_cap + base];
+      const dgq_seg_t S = srow[base];
       want = rk[0] < S.kmin || rk[1] > S.kmax || rk[2] < S.vmin || rk[3] > S.vmax;
       if (!want && window_test) {
         long long la = 0, lb = 0, ra = 0, rb = 0;
@@ -200,17 +213,17 @@ __device__ __forceinline__ void append_one(const AppendArgs &a, int b, int h, bo
         row.vscale = dgq_scale(row.vmin, row.vmax, a.fmt.levels);
         row.reserved = 0;
         a.cache.segs[bh * a.seg_cap + ns] = row;
+        srow[ns] = row;
         ns += 1;
         tl.span_own = 1;
         all = 1;                                 // the span moves to its own range
         if (r0 > 0 && !a.fmt.marker) {
-          const int blk = a.block_table[(size_t)b * a.max_blocks + r0 / BS];
-          uint8_t *byte = a.cache.bits + ((size_t)blk * a.hkv + h) * (BS / 8) + (r0 % BS) / 8;
+          uint8_t *byte = a.cache.bits + ((size_t)blk_t * a.hkv + h) * (BS / 8) + (r0 % BS) / 8;
           *byte = (uint8_t)(*byte | (1u << (r0 % 8)));
         }
       }
     } else if (want && tl.span_own) {
-      dgq_seg_t row = a.cache.segs[bh * a.seg_cap + ns - 1];
+      dgq_seg_t row = srow[ns - 1];
       all = row.kmin != rk[0] || row.kmax != rk[1] || row.vmin != rk[2] || row.vmax != rk[3];
       row.kmin = rk[0];
       row.kmax = rk[1];
@@ -219,10 +232,11 @@ __device__ __forceinline__ void append_one(const AppendArgs &a, int b, int h, bo
       row.kscale = dgq_scale(row.kmin, row.kmax, a.fmt.levels);
       row.vscale = dgq_scale(row.vmin, row.vmax, a.fmt.levels);
       a.cache.segs[bh * a.seg_cap + ns - 1] = row;
+      srow[ns - 1] = row;
     }
     ns_sh = ns;
     use_row = tl.span_own ? ns - 1 : base;
-    chosen = a.cache.segs[bh * a.seg_cap + use_row];
+    chosen = srow[use_row];
     out.ok = 1;
     out.ns = ns;
     out.use_row = use_row;
@@ -242,19 +256,43 @@ __device__ __forceinline__ void append_one(const AppendArgs &a, int b, int h, bo
   const float kinv = dgq_inv(row.kmin, row.kmax, lv), vinv = dgq_inv(row.vmin, row.vmax, lv);
   // marker format: the span's own segment starts at r0, whose first key byte is the marker
   const bool mark = a.fmt.marker && own_now && r0 > 0;
-  const int32_t *bt = a.block_table + (size_t)b * a.max_blocks;
-  const int blk = bt[r0 / BS];
+  const int blk = blk_t;                       // the block of r0 and t (checked above)
   int8_t *kt = a.cache.k_pool + ((size_t)blk * a.hkv + h) * (size_t)BS * D;
   int8_t *vt = a.cache.v_pool + ((size_t)blk * a.hkv + h) * (size_t)BS * D;
   const int enc_first = reenc_all ? 0 : span_len - 1;
-  for (int x = tid; x < (span_len - enc_first) * D; x += 256) {
-    const int s = slot0 + enc_first + x / D, d = x % D;
-    const float kx = half_bits_to_float(ks[s * D + d]);
-    const float vx = half_bits_to_float(vs[s * D + d]);
-    uint32_t kc = (uint32_t)(dgq_encode_value(kx, row.kmin, kinv, lv, low) & 0xFF);
-    if (mark && s == slot0 && d == 0) kc = dgq_marker_byte(kc);
-    kt[k_tile_offset<D, BS>(s, d)] = (int8_t)kc;
-    vt[v_tile_offset<D, BS>(s, d)] = (int8_t)dgq_encode_value(vx, row.vmin, vinv, lv, low);
+  // one unit = 8 channels of one span token: a 16-byte load from the staging copy, 8 key codes
+  // stored as 8 contiguous bytes of the tile; all of a thread's loads go out before any use
+  constexpr int CPU = D / 8;                              // units per token
+  constexpr int UPT = (BS * CPU + 255) / 256;             // units per thread, at most
+  const int nunits = (span_len - enc_first) * CPU;
+  uint4 kw[UPT], vw[UPT];
+#pragma unroll
+  for (int i = 0; i < UPT; ++i) {
+    const int u = tid + 256 * i;
+    if (u < nunits) {
+      const int s = slot0 + enc_first + u / CPU, d0 = 8 * (u % CPU);
+      kw[i] = *reinterpret_cast<const uint4 *>(ks + s * D + d0);
+      vw[i] = *reinterpret_cast<const uint4 *>(vs + s * D + d0);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < UPT; ++i) {
+    const int u = tid + 256 * i;
+    if (u < nunits) {
+      const int s = slot0 + enc_first + u / CPU, d0 = 8 * (u % CPU);
+      const uint32_t kh[4] = {kw[i].x, kw[i].y, kw[i].z, kw[i].w};
+      const uint32_t vh[4] = {vw[i].x, vw[i].y, vw[i].z, vw[i].w};
+      uint32_t kc[2] = {0u, 0u};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float kx = half_bits_to_float(e & 1 ? kh[e >> 1] >> 16 : kh[e >> 1] & 0xFFFFu);
+        const float vx = half_bits_to_float(e & 1 ? vh[e >> 1] >> 16 : vh[e >> 1] & 0xFFFFu);
+        kc[e >> 2] |= (uint32_t)(dgq_encode_value(kx, row.kmin, kinv, lv, low) & 0xFF) << (8 * (e & 3));
+        vt[v_tile_offset<D, BS>(s, d0 + e)] = (int8_t)dgq_encode_value(vx, row.vmin, vinv, lv, low);
+      }
+      if (mark && s == slot0 && d0 == 0) kc[0] = (kc[0] & ~0xFFu) | dgq_marker_byte(kc[0] & 0xFFu);
+      *reinterpret_cast<uint2 *>(kt + k_tile_offset<D, BS>(s, d0)) = make_uint2(kc[0], kc[1]);
+    }
   }
 
   // 6. seal a full block: the ring keeps the moments of the last 16 sealed tokens
