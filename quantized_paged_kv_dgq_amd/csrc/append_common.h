@@ -259,39 +259,49 @@ __device__ __forceinline__ void append_one(const AppendArgs &a, int b, int h, bo
   const int blk = blk_t;                       // the block of r0 and t (checked above)
   int8_t *kt = a.cache.k_pool + ((size_t)blk * a.hkv + h) * (size_t)BS * D;
   int8_t *vt = a.cache.v_pool + ((size_t)blk * a.hkv + h) * (size_t)BS * D;
-  const int enc_first = reenc_all ? 0 : span_len - 1;
-  // one unit = 8 channels of one span token: a 16-byte load from the staging copy, 8 key codes
-  // stored as 8 contiguous bytes of the tile; all of a thread's loads go out before any use
-  constexpr int CPU = D / 8;                              // units per token
-  constexpr int UPT = (BS * CPU + 255) / 256;             // units per thread, at most
-  const int nunits = (span_len - enc_first) * CPU;
-  uint4 kw[UPT], vw[UPT];
-#pragma unroll
-  for (int i = 0; i < UPT; ++i) {
-    const int u = tid + 256 * i;
-    if (u < nunits) {
-      const int s = slot0 + enc_first + u / CPU, d0 = 8 * (u % CPU);
-      kw[i] = *reinterpret_cast<const uint4 *>(ks + s * D + d0);
-      vw[i] = *reinterpret_cast<const uint4 *>(vs + s * D + d0);
+  if (!reenc_all) {
+    // only the new token changes: thread d < D still holds its channel d
+    if (tid < D) {
+      uint32_t kc = (uint32_t)(dgq_encode_value(half_bits_to_float(kb), row.kmin, kinv, lv, low) & 0xFF);
+      if (mark && slot == slot0 && tid == 0) kc = dgq_marker_byte(kc);
+      kt[k_tile_offset<D, BS>(slot, tid)] = (int8_t)kc;
+      vt[v_tile_offset<D, BS>(slot, tid)] = (int8_t)dgq_encode_value(half_bits_to_float(vb), row.vmin, vinv, lv, low);
     }
-  }
+  } else {
+    // the whole span: one unit = 8 channels of one span token, a 16-byte load from the staging
+    // copy and 8 key codes stored as 8 contiguous bytes of the tile; a thread's loads all go out
+    // before any use
+    constexpr int CPU = D / 8;                              // units per token
+    constexpr int UPT = (BS * CPU + 255) / 256;             // units per thread, at most
+    const int nunits = span_len * CPU;
+    uint4 kw[UPT], vw[UPT];
 #pragma unroll
-  for (int i = 0; i < UPT; ++i) {
-    const int u = tid + 256 * i;
-    if (u < nunits) {
-      const int s = slot0 + enc_first + u / CPU, d0 = 8 * (u % CPU);
-      const uint32_t kh[4] = {kw[i].x, kw[i].y, kw[i].z, kw[i].w};
-      const uint32_t vh[4] = {vw[i].x, vw[i].y, vw[i].z, vw[i].w};
-      uint32_t kc[2] = {0u, 0u};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float kx = half_bits_to_float(e & 1 ? kh[e >> 1] >> 16 : kh[e >> 1] & 0xFFFFu);
-        const float vx = half_bits_to_float(e & 1 ? vh[e >> 1] >> 16 : vh[e >> 1] & 0xFFFFu);
-        kc[e >> 2] |= (uint32_t)(dgq_encode_value(kx, row.kmin, kinv, lv, low) & 0xFF) << (8 * (e & 3));
-        vt[v_tile_offset<D, BS>(s, d0 + e)] = (int8_t)dgq_encode_value(vx, row.vmin, vinv, lv, low);
+    for (int i = 0; i < UPT; ++i) {
+      const int u = tid + 256 * i;
+      if (u < nunits) {
+        const int s = slot0 + u / CPU, d0 = 8 * (u % CPU);
+        kw[i] = *reinterpret_cast<const uint4 *>(ks + s * D + d0);
+        vw[i] = *reinterpret_cast<const uint4 *>(vs + s * D + d0);
       }
-      if (mark && s == slot0 && d0 == 0) kc[0] = (kc[0] & ~0xFFu) | dgq_marker_byte(kc[0] & 0xFFu);
-      *reinterpret_cast<uint2 *>(kt + k_tile_offset<D, BS>(s, d0)) = make_uint2(kc[0], kc[1]);
+    }
+#pragma unroll
+    for (int i = 0; i < UPT; ++i) {
+      const int u = tid + 256 * i;
+      if (u < nunits) {
+        const int s = slot0 + u / CPU, d0 = 8 * (u % CPU);
+        const uint32_t kh[4] = {kw[i].x, kw[i].y, kw[i].z, kw[i].w};
+        const uint32_t vh[4] = {vw[i].x, vw[i].y, vw[i].z, vw[i].w};
+        uint32_t kc[2] = {0u, 0u};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float kx = half_bits_to_float(e & 1 ? kh[e >> 1] >> 16 : kh[e >> 1] & 0xFFFFu);
+          const float vx = half_bits_to_float(e & 1 ? vh[e >> 1] >> 16 : vh[e >> 1] & 0xFFFFu);
+          kc[e >> 2] |= (uint32_t)(dgq_encode_value(kx, row.kmin, kinv, lv, low) & 0xFF) << (8 * (e & 3));
+          vt[v_tile_offset<D, BS>(s, d0 + e)] = (int8_t)dgq_encode_value(vx, row.vmin, vinv, lv, low);
+        }
+        if (mark && s == slot0 && d0 == 0) kc[0] = (kc[0] & ~0xFFu) | dgq_marker_byte(kc[0] & 0xFFu);
+        *reinterpret_cast<uint2 *>(kt + k_tile_offset<D, BS>(s, d0)) = make_uint2(kc[0], kc[1]);
+      }
     }
   }
 
