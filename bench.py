@@ -157,6 +157,29 @@ def copy_calibration():
     print(json.dumps({"copy_calibration": {"bytes_read": 512 << 20, "bytes_written": 512 << 20, "launches": 5}}))
 
 
+def achievable_copy(dev):
+    """A plain device copy of 512 MiB (torch's copy kernel), timed like the library's kernels:
+    the bandwidth a simple streaming kernel reaches on this GPU, as a second yardstick beside the
+    8 TB/s data-sheet peak.  Bytes counted: read + written."""
+    import torch
+
+    src = torch.empty(512 << 20, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    ev = []
+    for _ in range(10):
+        e0, e1 = Timer(), Timer()
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        ev.append((e0, e1))
+    torch.cuda.synchronize()
+    us = float(np.median([a.elapsed_time(b) for a, b in ev])) * 1e3
+    del src, dst
+    return {"bytes": 2 * (512 << 20), "us": round(us, 2), "gbs": round(2 * (512 << 20) / us / 1e3, 1)}
+
+
 def cpu_baseline(cfg, seed, budget_s):
     """The oracle as it is, on one host core, on a bounded sample of the same workload: whole
     (sequence, kv head) units of config 2 until the budget is spent."""
@@ -636,6 +659,7 @@ def main():
     gq_ms = np.array([e[0].elapsed_time(e[1]) for e in gev])
     gd_ms = np.array([e[1].elapsed_time(e[2]) for e in gev])
     quality = quality_vs_fp16(cfg, k, v, cu, k_tok, v_tok, q, out, out_g)
+    copy = achievable_copy(dev)
     policies = segment_policies(cfg, k, v, cu, dcu, dtable, nblk, q, dev, Q)
     formats = marker_format(cfg, k, v, cu, dcu, dtable, nblk, q, dev, Q)
 
@@ -688,6 +712,8 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
+            "frac_of_measured_copy": round(dec_gbs / copy["gbs"], 4),
+            "measured_copy": copy,
             "traffic": measured_traffic(),
             "kernel": "decode_partition_kernel<128,4,16> (one launch per paged_decode_attn_int8 call; "
                       "HIP events around the call on its stream)",

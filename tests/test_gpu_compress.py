@@ -152,9 +152,10 @@ def _custom(cfg, seqs):
     return k, v, cu, lens
 
 
-def test_compress_edge_cases():
+@pytest.mark.parametrize("marker", [False, True], ids=["bitmap", "marker"])
+def test_compress_edge_cases(marker):
     """Lengths 0, 1, 31, 32, 33; constant runs (exact reconstruction); subnormals and signed
-    zeros; exact score ties; values beyond the statistics clamp."""
+    zeros; exact score ties; values beyond the statistics clamp; in both identifier formats."""
     cfg = dgq_data.get_config(1, batch=9, hq=2)
     rng = np.random.default_rng(0)
     d = cfg.head_dim
@@ -183,10 +184,15 @@ def test_compress_edge_cases():
     x[50, 0, :4] = np.array([65504, -65504, 1000, -3000], np.float16)
     seqs.append((x, (x / 3).astype(np.float16)))
     k, v, cu, lens = _custom(cfg, seqs)
-    H.say("compress edge cases")
-    cache, heads, _ = compress_and_check(cfg, 13, k=k, v=v, cu=cu, lens=lens)
+    H.say("compress edge cases", marker)
+    cache, heads, table = compress_and_check(cfg, 13, k=k, v=v, cu=cu, lens=lens,
+                                             params=H.params_for(cfg, marker=marker))
     hc = heads[(5, 0)]
     assert hc.starts[1:3] == [64, 128] or 64 in hc.starts
+    if marker:
+        # the constant run is exact on the GPU side too, its marker byte included
+        kc, vc = H.read_codes(cache, table, 5, 0, hc.length)
+        assert np.array_equal(kc[64:128], hc.kcodes[64:128]) and np.array_equal(vc[64:128], hc.vcodes[64:128])
 
 
 def test_compress_repeatable():
