@@ -194,8 +194,8 @@ int32_t dgq_block_refcount(const void *pool, int32_t id);
  * served in order: a block with one reference is kept (out_ids[i] = ids[i]); a block with more
  * takes a fresh block (out_ids[i], one reference) and drops one reference of ids[i].  The caller
  * then copies every changed pair with dgq_copy_blocks and writes out_ids into its block table.
- * All or nothing: DGQ_ERR_POOL_EXHAUSTED or DGQ_ERR_INVALID_ARG (an id out of range or free)
- * leave the pool unchanged. */
+ * All or nothing: DGQ_ERR_POOL_EXHAUSTED, or DGQ_ERR_INVALID_ARG (an id out of range or free, or
+ * listed more often than it has references), leaves the pool unchanged. */
 dgq_status_t dgq_block_cow(void *pool, int32_t n, const int32_t *ids, int32_t *out_ids);
 
 /* Copy whole compressed blocks of one layer: for i < n, the K and V codes of every kv head and the

@@ -106,38 +106,46 @@ extern "C" dgq_status_t dgq_block_share(void *pool, int32_t n, const int32_t *id
 extern "C" dgq_status_t dgq_block_cow(void *pool, int32_t n, const int32_t *ids, int32_t *out_ids) {
   Pool *p = static_cast<Pool *>(pool);
   if (p == nullptr || n < 0 || (n > 0 && (ids == nullptr || out_ids == nullptr))) return DGQ_ERR_INVALID_ARG;
-  // dry run on the counts of the listed ids: entries are served in order, and an entry whose
-  // block still has other owners takes a fresh block and drops one reference
-  std::unordered_map<int32_t, int64_t> refs;
+  // Entries are served in order.  rem[id] = references of id not yet served: an entry that finds
+  // more than one takes a fresh block and drops one; an entry that finds exactly one keeps the
+  // block (rem becomes 0); an entry that finds none (a free block, or one already kept by an
+  // earlier entry) is an error.  A dry run validates everything before the pool changes.
+  std::unordered_map<int32_t, int64_t> rem;
   int64_t fresh = 0;
   try {
     for (int32_t i = 0; i < n; ++i) {
       const int32_t id = ids[i];
       if (id < 0 || (size_t)id >= p->refs.size()) return DGQ_ERR_INVALID_ARG;
-      auto it = refs.find(id);
-      if (it == refs.end()) it = refs.emplace(id, p->refs[(size_t)id]).first;
-      if (it->second == 0) return DGQ_ERR_INVALID_ARG;  // free, or released by an earlier entry
+      auto it = rem.find(id);
+      if (it == rem.end()) it = rem.emplace(id, p->refs[(size_t)id]).first;
+      if (it->second == 0) return DGQ_ERR_INVALID_ARG;
       if (it->second > 1) {
         --it->second;
         ++fresh;
+      } else {
+        it->second = 0;
       }
     }
   } catch (...) {
     return DGQ_ERR_INVALID_ARG;
   }
   if ((size_t)fresh > p->free_list.size()) return DGQ_ERR_POOL_EXHAUSTED;
+  rem.clear();
   for (int32_t i = 0; i < n; ++i) {
     const int32_t id = ids[i];
-    int32_t &r = p->refs[(size_t)id];
-    if (r == 1) {
+    auto it = rem.find(id);
+    if (it == rem.end()) it = rem.emplace(id, p->refs[(size_t)id]).first;
+    if (it->second > 1) {
+      --it->second;
+      --p->refs[(size_t)id];
+      const int32_t nid = p->free_list.back();
+      p->free_list.pop_back();
+      p->refs[(size_t)nid] = 1;
+      out_ids[i] = nid;
+    } else {
+      it->second = 0;
       out_ids[i] = id;
-      continue;
     }
-    --r;
-    const int32_t nid = p->free_list.back();
-    p->free_list.pop_back();
-    p->refs[(size_t)nid] = 1;
-    out_ids[i] = nid;
   }
   return DGQ_OK;
 }

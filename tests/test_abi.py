@@ -179,6 +179,9 @@ def test_pool_copy_on_write(lib):
     assert lib.dgq_block_cow(h, 1, _arr(2), out) == _lib.DGQ_ERR_INVALID_ARG
     assert lib.dgq_block_cow(h, 1, _arr(3), out) == 0 and out[0] == 2
     assert lib.dgq_block_refcount(h, 3) == 1 and lib.dgq_block_refcount(h, 2) == 1
+    # two writers for a block with one owner: refused, nothing changes
+    assert lib.dgq_block_cow(h, 2, _arr(3, 3), out) == _lib.DGQ_ERR_INVALID_ARG
+    assert lib.dgq_block_refcount(h, 3) == 1 and lib.dgq_pool_num_free(h) == 0
     assert lib.dgq_pool_destroy(h) == 0
 
 
