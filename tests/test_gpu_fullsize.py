@@ -23,12 +23,16 @@ pytestmark = pytest.mark.gpu
 
 SEED = 0
 
-# (case id, workload id, overrides, sampled units, decode check steps of a streaming run)
+# (case id, workload id, overrides, sampled units, decode check steps of a streaming run,
+#  marker format, fused append + decode)
 CASES = [
-    ("llama_layer_16x8192_append1", 2, dict(append_steps=1), 6, (0,)),
-    ("long_context_131072_layer0", 3, {}, 2, ()),
-    ("mha_100_mixed_lengths", 4, {}, 6, ()),
-    ("streaming_64x2048_256steps", 5, {}, 4, (0, 63, 64, 255)),
+    ("llama_layer_16x8192_append1", 2, dict(append_steps=1), 6, (0,), False, False),
+    ("long_context_131072_layer0", 3, {}, 2, (), False, False),
+    ("mha_100_mixed_lengths", 4, {}, 6, (), False, False),
+    ("streaming_64x2048_256steps", 5, {}, 4, (0, 63, 64, 255), False, False),
+    ("streaming_64x2048_256steps_fused", 5, {}, 4, (0, 63, 64, 255), False, True),
+    ("llama_layer_16x8192_append1_marker", 2, dict(append_steps=1), 4, (0,), True, False),
+    ("streaming_64x2048_256steps_fused_marker", 5, {}, 3, (0, 127, 255), True, True),
 ]
 
 
@@ -59,8 +63,8 @@ def _check_rows(out, q16, heads, group, what):
     assert worst <= 2e-3, (what, worst)
 
 
-@pytest.mark.parametrize("name,cid,over,nunits,checks", CASES, ids=[c[0] for c in CASES])
-def test_full_size(name, cid, over, nunits, checks):
+@pytest.mark.parametrize("name,cid,over,nunits,checks,marker,fused", CASES, ids=[c[0] for c in CASES])
+def test_full_size(name, cid, over, nunits, checks, marker, fused):
     cfg = dgq_data.get_config(cid, **over)
     steps = cfg.append_steps
     H.say("full-size", name, f"batch {cfg.batch} hkv {cfg.hkv} hq {cfg.hq} bs {cfg.block_size} steps {steps}")
@@ -73,7 +77,7 @@ def test_full_size(name, cid, over, nunits, checks):
     lmax = int(lens.max())
     table, nblk = dgq_data.block_tables(cfg, SEED, lens_total=lens + steps)
     dtable = torch.from_numpy(table).to(dev)
-    params = H.params_for(cfg)
+    params = H.params_for(cfg, marker=marker)
     p = params.c
     cache = Q.DGQCache(params, nblk, cfg.batch, dev)
     ws_c = Q.workspace(Q.compress_workspace_size(params, cfg.batch, total, lmax), dev)
@@ -87,7 +91,7 @@ def test_full_size(name, cid, over, nunits, checks):
     states = {}
     for (b, h), (kk, vv) in host.items():
         n0 = int(lens[b])
-        hc = O.compress_head(kk[:n0], vv[:n0], p.max_segments, p.tau)
+        hc = O.compress_head(kk[:n0], vv[:n0], p.max_segments, p.tau, fmt=H.fmt_of(params))
         states[(b, h)] = O.AppendState(hc, kk[:n0], p.block_size, p.seg_capacity, p.tau)
 
     out = torch.empty((cfg.batch, cfg.hq, cfg.head_dim), dtype=torch.float32, device=dev)
@@ -96,14 +100,17 @@ def test_full_size(name, cid, over, nunits, checks):
     for s in range(steps):
         pos = lens_dev + s
         idx = cu_dev[:-1] + pos
-        Q.dgq_append(params, k.index_select(0, idx).contiguous(), v.index_select(0, idx).contiguous(),
-                     pos.to(torch.int32), dtable, cache)
+        ktok, vtok = k.index_select(0, idx).contiguous(), v.index_select(0, idx).contiguous()
+        q16 = dgq_data.queries(cfg, SEED, 0, s)
+        if fused:
+            Q.dgq_append_decode(params, ktok, vtok, pos.to(torch.int32), torch.from_numpy(q16).to(dev), dtable,
+                                cache, lmax + s + 1, out=out, ws=ws_d)
+        else:
+            Q.dgq_append(params, ktok, vtok, pos.to(torch.int32), dtable, cache)
+            Q.paged_decode_attn_int8(params, torch.from_numpy(q16).to(dev), cache, dtable, (pos + 1).to(torch.int32),
+                                     lmax + s + 1, out=out, ws=ws_d)
         for (b, h), (kk, vv) in host.items():
             states[(b, h)].append(kk[int(lens[b]) + s], vv[int(lens[b]) + s])
-        cur = (pos + 1).to(torch.int32)
-        q16 = dgq_data.queries(cfg, SEED, 0, s)
-        Q.paged_decode_attn_int8(params, torch.from_numpy(q16).to(dev), cache, dtable, cur, lmax + s + 1,
-                                 out=out, ws=ws_d)
         if s in checks:
             torch.cuda.synchronize()
             heads = {u: st.snapshot() for u, st in states.items()}
@@ -121,7 +128,7 @@ def test_full_size(name, cid, over, nunits, checks):
     assert status[0] == 0, "no workload here needs more segment rows than the table holds"
     starts, prm, nseg = cache.segment_table()
     kp, vp = cache.k_pool.cpu().numpy(), cache.v_pool.cpu().numpy()
-    bits = cache.bits.cpu().numpy()
+    bits = H.identifier_bits(cache, table, lens + steps)
     tails = cache.tail.cpu().numpy()
     koff, voff = PL.k_offsets(p.block_size, p.head_dim), PL.v_offsets(p.block_size, p.head_dim)
     for (b, h), st in states.items():
@@ -133,6 +140,8 @@ def test_full_size(name, cid, over, nunits, checks):
                 (b, h, i)
         H.compare_codes(PL.gather_head(kp, table[b], h, hc.length, koff), hc.kcodes, f"{name} K b{b} h{h}")
         H.compare_codes(PL.gather_head(vp, table[b], h, hc.length, voff), hc.vcodes, f"{name} V b{b} h{h}")
+        if marker:
+            H.compare_markers(PL.gather_head(kp, table[b], h, hc.length, koff), hc.kcodes, f"{name} K markers b{b} h{h}")
         assert np.array_equal(PL.gather_bits(bits, table[b], h, hc.length, p.block_size), hc.bits), (b, h)
         tl = tails[b, h]
         assert tl[0] == st.r0 and tl[1] == len(st.ring_a) and tl[2] == int(st.span_own), (b, h, tl[:3])
