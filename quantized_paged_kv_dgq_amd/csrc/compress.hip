@@ -197,231 +197,8 @@ __global__ __launch_bounds__(256) void scores_kernel(CompressArgs a) {
 }
 
 // -------------------------------------------------------------------------------------------
-// 3. select
+// wave reductions with DPP row operations and lane reads (no LDS)
 // -------------------------------------------------------------------------------------------
-__device__ __forceinline__ void block_best(double &s, int &t, double *ss, int *st) {
-  const int tid = threadIdx.x;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const double s2 = __shfl_xor(s, o);
-    const int t2 = __shfl_xor(t, o);
-    if (s2 > s || (s2 == s && t2 < t)) {
-      s = s2;
-      t = t2;
-    }
-  }
-  __syncthreads();
-  if ((tid & 63) == 0) {
-    ss[tid >> 6] = s;
-    st[tid >> 6] = t;
-  }
-  __syncthreads();
-  s = ss[0];
-  t = st[0];
-  for (int w = 1; w < 4; ++w)
-    if (ss[w] > s || (ss[w] == s && st[w] < t)) {
-      s = ss[w];
-      t = st[w];
-    }
-}
-
-__device__ __forceinline__ void block_minmax(float4 &r, float4 *sh) {
-  const int tid = threadIdx.x;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    r.x = fminf(r.x, __shfl_xor(r.x, o));
-    r.y = fmaxf(r.y, __shfl_xor(r.y, o));
-    r.z = fminf(r.z, __shfl_xor(r.z, o));
-    r.w = fmaxf(r.w, __shfl_xor(r.w, o));
-  }
-  __syncthreads();
-  if ((tid & 63) == 0) sh[tid >> 6] = r;
-  __syncthreads();
-  r = sh[0];
-  for (int w = 1; w < 4; ++w) {
-    r.x = fminf(r.x, sh[w].x);
-    r.y = fmaxf(r.y, sh[w].y);
-    r.z = fminf(r.z, sh[w].z);
-    r.w = fmaxf(r.w, sh[w].w);
-  }
-}
-
-template <int D>
-__global__ __launch_bounds__(256) void select_kernel(CompressArgs a) {
-  const int h = blockIdx.x, b = blockIdx.y;
-  int c0, L;
-  bool bad_seq;
-  seq_range(a.cu, b, a.max_seq_len, a.total, c0, L, bad_seq);
-  const int tid = threadIdx.x;
-  const size_t bh = (size_t)b * a.hkv + h;
-  __shared__ int cuts[kMaxCuts + 1];
-  __shared__ int ncuts;
-  __shared__ double ss[4];
-  __shared__ int st[4];
-  __shared__ float4 sh4[4];
-  if (tid == 0) {
-    ncuts = 0;
-    if (bad_seq && h == 0) atomicAdd(a.cache.status + 2, 1ull);
-  }
-  __syncthreads();
-
-  double2 *tiles = a.ws_tile + bh * a.ntile;
-  const int max_seg = a.length_aware ? min(a.max_segments, length_aware_cap(L)) : a.max_segments;
-  if (L >= 2 * kWin && max_seg > 1) {
-    const int ntiles = (L - kWin) / 256 + 1;
-    for (int r = 0; r < max_seg - 1; ++r) {
-      double s = -INFINITY;
-      int t = INT_MAX;
-      for (int c = tid; c < ntiles; c += 256) {
-        const double2 e = tiles[c];
-        const int te = (int)e.y;
-        if (e.x > s || (e.x == s && te < t)) {
-          s = e.x;
-          t = te;
-        }
-      }
-      block_best(s, t, ss, st);
-      if (s == -INFINITY) break;
-      if (r > 0 && !(s >= a.tau)) break;
-      __syncthreads();
-      if (tid == 0) cuts[ncuts] = t;
-      __syncthreads();
-      if (tid == 0) ncuts = ncuts + 1;
-      __syncthreads();
-      const int nc = ncuts;
-      // re-scan the tiles that the suppressed window [t-15, t+15] touches
-      const int lo_tile = max(0, (t - (kWin - 1)) / 256), hi_tile = min(ntiles - 1, (t + kWin - 1) / 256);
-      for (int c = lo_tile; c <= hi_tile; ++c) {
-        const int tc = c * 256 + tid;
-        double sc = -INFINITY;
-        int tt = INT_MAX;
-        if (tc >= kWin && tc <= L - kWin) {
-          bool alive = true;
-          for (int k = 0; k < nc; ++k) alive = alive && abs(tc - cuts[k]) > kWin - 1;
-          if (alive) {
-            sc = a.ws_score[(size_t)h * a.total + c0 + tc];
-            tt = tc;
-          }
-        }
-        block_best(sc, tt, ss, st);
-        if (tid == 0) tiles[c] = make_double2(sc, (double)tt);
-        __syncthreads();
-      }
-    }
-  }
-  __syncthreads();
-  const int nc = ncuts;
-  // starts = [0] + sorted cuts
-  __shared__ int starts[kMaxCuts + 2];
-  if (tid == 0) {
-    int tmp[kMaxCuts + 1];
-    for (int i = 0; i < nc; ++i) tmp[i] = cuts[i];
-    for (int i = 1; i < nc; ++i) {
-      const int x = tmp[i];
-      int k = i - 1;
-      while (k >= 0 && tmp[k] > x) {
-        tmp[k + 1] = tmp[k];
-        --k;
-      }
-      tmp[k + 1] = x;
-    }
-    starts[0] = 0;
-    for (int i = 0; i < nc; ++i) starts[i + 1] = tmp[i];
-    starts[nc + 1] = L;
-  }
-  __syncthreads();
-  const int nseg = L > 0 ? nc + 1 : 0;
-  const float4 *ext = a.ws_ext + bh * a.nsub;
-  for (int sgi = 0; sgi < nseg; ++sgi) {
-    const int s = starts[sgi], e = starts[sgi + 1];
-    float4 r = make_float4(INFINITY, -INFINITY, INFINITY, -INFINITY);
-    const int i0 = s / 16, i1 = (e - 1) / 16;
-    for (int i = i0 + tid; i <= i1; i += 256) {
-      const bool full = (16 * i >= s) && (min(16 * i + 16, L) <= e);
-      if (full) {
-        const float4 x = ext[i];
-        r.x = fminf(r.x, x.x);
-        r.y = fmaxf(r.y, x.y);
-        r.z = fminf(r.z, x.z);
-        r.w = fmaxf(r.w, x.w);
-      }
-    }
-    // raw re-read of the split sub-blocks at either end
-    for (int side = 0; side < 2; ++side) {
-      const int i = side == 0 ? i0 : i1;
-      if (side == 1 && i1 == i0) break;
-      const int ts = max(16 * i, s), te = min(16 * i + 16, e);
-      const bool full = (16 * i >= s) && (min(16 * i + 16, L) <= e);
-      if (full) continue;
-      const int nel = (te - ts) * D;
-      for (int x = tid; x < nel; x += 256) {
-        const int tok = ts + x / D, d = x % D;
-        const size_t off = (size_t)(c0 + tok) * a.stride_tok + (size_t)h * a.stride_head + d;
-        const float kx = half_bits_to_float(a.k[off]);
-        const float vx = half_bits_to_float(a.v[off]);
-        r.x = fminf(r.x, kx);
-        r.y = fmaxf(r.y, kx);
-        r.z = fminf(r.z, vx);
-        r.w = fmaxf(r.w, vx);
-      }
-    }
-    block_minmax(r, sh4);
-    if (tid == 0) {
-      dgq_seg_t row;
-      row.start = s;
-      row.kmin = r.x + 0.0f;
-      row.kmax = r.y + 0.0f;
-      row.vmin = r.z + 0.0f;
-      row.vmax = r.w + 0.0f;
-      row.kscale = dgq_scale(row.kmin, row.kmax, a.fmt.levels);
-      row.vscale = dgq_scale(row.vmin, row.vmax, a.fmt.levels);
-      row.reserved = 0;
-      a.cache.segs[bh * a.seg_cap + sgi] = row;
-    }
-    __syncthreads();
-  }
-  if (tid == 0) {
-    a.cache.nseg[bh] = nseg;
-    dgq_tail_t tl;
-    tl.r0 = L;
-    const int rl = min(kWin, L);
-    tl.ring_len = rl;
-    tl.span_own = 0;
-    tl.window_done = 0;
-    for (int i = 0; i < 4; ++i) tl.span_range[i] = 0.f;
-    for (int i = 0; i < kWin; ++i) {
-      if (i < rl) {
-        const size_t idx = (size_t)h * a.total + c0 + (L - rl + i);
-        tl.ring_a[i] = a.ws_a[idx];
-        tl.ring_b[i] = a.ws_b[idx];
-      } else {
-        tl.ring_a[i] = 0;
-        tl.ring_b[i] = 0;
-      }
-    }
-    a.cache.tail[bh] = tl;
-  }
-}
-
-// -------------------------------------------------------------------------------------------
-// 2+3 fused, for sequences of at most kSmallSeq tokens: one workgroup of 512 threads per
-// (sequence, kv head) holds the key moments in LDS, keeps the scores of its 16 candidates per
-// thread in registers, runs the greedy rounds with no memory traffic, and reduces all segments'
-// min/max in one pass over the sub-block extrema (plus the raw tokens of sub-blocks a cut splits).
-// Wave reductions use DPP row operations and lane reads, not LDS permutes.
-// -------------------------------------------------------------------------------------------
-constexpr int kSmallSeq = 8192;
-constexpr int kSmallThreads = 512;
-constexpr int kSmallWaves = kSmallThreads / 64;
-constexpr int kPerThread = kSmallSeq / kSmallThreads;   // 16 candidates per thread
-static_assert(kPerThread == kWin, "one 16-token sub-block per thread");
-
-// LDS slot of token t, t in [-16, kSmallSeq + 16): one pad slot after every 16 tokens, so that
-// thread i reading token 16 i + u (all i of a wave at once) hits distinct banks; the 16 slots on
-// either side of the sequence hold zeros, so window sums need no bounds tests
-__device__ __forceinline__ int skew(int t) { return (t + kWin) + ((t + kWin) >> 4); }
-constexpr int kSkewed = (kSmallSeq + 2 * kWin) + (kSmallSeq + 2 * kWin) / 16;
-
 template <int C>
 __device__ __forceinline__ int dpp_i(int x) {
   return __builtin_amdgcn_mov_dpp(x, C, 0xF, 0xF, false);
@@ -503,6 +280,272 @@ __device__ __forceinline__ float4 wave_minmax(float4 r) {
   }
   return o;
 }
+
+// -------------------------------------------------------------------------------------------
+// 3. select
+// -------------------------------------------------------------------------------------------
+__device__ __forceinline__ void block_best(double &s, int &t, double *ss, int *st) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const double s2 = __shfl_xor(s, o);
+    const int t2 = __shfl_xor(t, o);
+    if (s2 > s || (s2 == s && t2 < t)) {
+      s = s2;
+      t = t2;
+    }
+  }
+  __syncthreads();
+  if ((tid & 63) == 0) {
+    ss[tid >> 6] = s;
+    st[tid >> 6] = t;
+  }
+  __syncthreads();
+  s = ss[0];
+  t = st[0];
+  for (int w = 1; w < 4; ++w)
+    if (ss[w] > s || (ss[w] == s && st[w] < t)) {
+      s = ss[w];
+      t = st[w];
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void select_kernel(CompressArgs a) {
+  const int h = blockIdx.x, b = blockIdx.y;
+  int c0, L;
+  bool bad_seq;
+  seq_range(a.cu, b, a.max_seq_len, a.total, c0, L, bad_seq);
+  const int tid = threadIdx.x;
+  const size_t bh = (size_t)b * a.hkv + h;
+  __shared__ int cuts[kMaxCuts + 1];
+  __shared__ int ncuts;
+  __shared__ double ss[4];
+  __shared__ int st[4];
+  if (tid == 0) {
+    ncuts = 0;
+    if (bad_seq && h == 0) atomicAdd(a.cache.status + 2, 1ull);
+  }
+  __syncthreads();
+
+  double2 *tiles = a.ws_tile + bh * a.ntile;
+  const int max_seg = a.length_aware ? min(a.max_segments, length_aware_cap(L)) : a.max_segments;
+  if (L >= 2 * kWin && max_seg > 1) {
+    const int ntiles = (L - kWin) / 256 + 1;
+    for (int r = 0; r < max_seg - 1; ++r) {
+      double s = -INFINITY;
+      int t = INT_MAX;
+      for (int c = tid; c < ntiles; c += 256) {
+        const double2 e = tiles[c];
+        const int te = (int)e.y;
+        if (e.x > s || (e.x == s && te < t)) {
+          s = e.x;
+          t = te;
+        }
+      }
+      block_best(s, t, ss, st);
+      if (s == -INFINITY) break;
+      if (r > 0 && !(s >= a.tau)) break;
+      __syncthreads();
+      if (tid == 0) cuts[ncuts] = t;
+      __syncthreads();
+      if (tid == 0) ncuts = ncuts + 1;
+      __syncthreads();
+      const int nc = ncuts;
+      // re-scan the tiles that the suppressed window [t-15, t+15] touches
+      const int lo_tile = max(0, (t - (kWin - 1)) / 256), hi_tile = min(ntiles - 1, (t + kWin - 1) / 256);
+      for (int c = lo_tile; c <= hi_tile; ++c) {
+        const int tc = c * 256 + tid;
+        double sc = -INFINITY;
+        int tt = INT_MAX;
+        if (tc >= kWin && tc <= L - kWin) {
+          bool alive = true;
+          for (int k = 0; k < nc; ++k) alive = alive && abs(tc - cuts[k]) > kWin - 1;
+          if (alive) {
+            sc = a.ws_score[(size_t)h * a.total + c0 + tc];
+            tt = tc;
+          }
+        }
+        block_best(sc, tt, ss, st);
+        if (tid == 0) tiles[c] = make_double2(sc, (double)tt);
+        __syncthreads();
+      }
+    }
+  }
+  __syncthreads();
+  const int nc = ncuts;
+  // starts = [0] + sorted cuts
+  __shared__ int starts[kMaxCuts + 2];
+  if (tid == 0) {
+    int tmp[kMaxCuts + 1];
+    for (int i = 0; i < nc; ++i) tmp[i] = cuts[i];
+    for (int i = 1; i < nc; ++i) {
+      const int x = tmp[i];
+      int k = i - 1;
+      while (k >= 0 && tmp[k] > x) {
+        tmp[k + 1] = tmp[k];
+        --k;
+      }
+      tmp[k + 1] = x;
+    }
+    starts[0] = 0;
+    for (int i = 0; i < nc; ++i) starts[i + 1] = tmp[i];
+    starts[nc + 1] = L;
+  }
+  __syncthreads();
+  const int nseg = L > 0 ? nc + 1 : 0;
+  // ---- every segment's K/V min/max ----
+  // (1) whole sub-blocks, one pass: each thread folds its sub-blocks into the accumulator of the
+  //     segment that holds them, with a batch of loads in flight; then one wave reduction per
+  //     segment.
+  // (2) a sub-block that a cut splits (cuts are >= 16 apart, so one cut per sub-block; a cut at a
+  //     multiple of 16 splits none) is re-read raw by one wave: wave w takes cuts w + 1, w + 5, ...
+  constexpr int MS = kMaxCuts + 1;
+  const int wave = tid >> 6, lane = tid & 63;
+  const float4 ident = make_float4(INFINITY, -INFINITY, INFINITY, -INFINITY);
+  auto fold = [](float4 &r, const float4 x) {
+    r.x = fminf(r.x, x.x);
+    r.y = fmaxf(r.y, x.y);
+    r.z = fminf(r.z, x.z);
+    r.w = fmaxf(r.w, x.w);
+  };
+  __shared__ float4 sred[4][MS];
+  __shared__ float4 sraw[kMaxCuts][2];   // cut c: (left part, right part)
+  {
+    const float4 *ext = a.ws_ext + bh * a.nsub;
+    const int nsub = (L + kWin - 1) / kWin;
+    float4 acc[MS];
+#pragma unroll
+    for (int j = 0; j < MS; ++j) acc[j] = ident;
+    constexpr int U = 8;
+    for (int i0 = tid; i0 < nsub; i0 += 256 * U) {
+      float4 x[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) x[u] = i0 + 256 * u < nsub ? ext[i0 + 256 * u] : ident;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int i = i0 + 256 * u;
+        if (i < nsub) {
+          const int t0 = kWin * i, t1 = min(t0 + kWin, L);
+          int j = 0;
+          for (int k = 1; k < nseg; ++k) j += t0 >= starts[k] ? 1 : 0;
+          if (t1 <= starts[j + 1]) {
+#pragma unroll
+            for (int jj = 0; jj < MS; ++jj)
+              if (jj == j) fold(acc[jj], x[u]);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < MS; ++j) {
+      if (j < nseg) {
+        const float4 r = wave_minmax(acc[j]);
+        if (lane == 0) sred[wave][j] = r;
+      }
+    }
+  }
+  for (int c = wave + 1; c < nseg; c += 4) {
+    const int cut = starts[c];
+    float4 left = ident, right = ident;
+    if (cut % kWin != 0) {
+      const int t0 = cut - cut % kWin;
+      constexpr int PER_LANE = kWin * D / 64;   // halves of the sub-block per lane
+      uint4 kw[PER_LANE / 8], vw[PER_LANE / 8];
+#pragma unroll
+      for (int e = 0; e < PER_LANE / 8; ++e) {
+        const int x = lane * PER_LANE + 8 * e;
+        const int tok = t0 + x / D, d = x % D;
+        if (tok < L) {
+          const size_t off = (size_t)(c0 + tok) * a.stride_tok + (size_t)h * a.stride_head + d;
+          kw[e] = *reinterpret_cast<const uint4 *>(a.k + off);
+          vw[e] = *reinterpret_cast<const uint4 *>(a.v + off);
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < PER_LANE / 8; ++e) {
+        const int x = lane * PER_LANE + 8 * e;
+        const int tok = t0 + x / D;
+        if (tok < L) {
+          const uint32_t kk[4] = {kw[e].x, kw[e].y, kw[e].z, kw[e].w}, vv[4] = {vw[e].x, vw[e].y, vw[e].z, vw[e].w};
+          float4 r = ident;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float k0 = half_bits_to_float(kk[q] & 0xFFFFu), k1 = half_bits_to_float(kk[q] >> 16);
+            const float v0 = half_bits_to_float(vv[q] & 0xFFFFu), v1 = half_bits_to_float(vv[q] >> 16);
+            fold(r, make_float4(fminf(k0, k1), fmaxf(k0, k1), fminf(v0, v1), fmaxf(v0, v1)));
+          }
+          fold(tok < cut ? left : right, r);
+        }
+      }
+    }
+    left = wave_minmax(left);
+    right = wave_minmax(right);
+    if (lane == 0) {
+      sraw[c - 1][0] = left;
+      sraw[c - 1][1] = right;
+    }
+  }
+  __syncthreads();
+  if (tid < nseg) {
+    float4 r = sred[0][tid];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) fold(r, sred[w][tid]);
+    if (tid > 0) fold(r, sraw[tid - 1][1]);        // right of the cut that starts segment tid
+    if (tid + 1 < nseg) fold(r, sraw[tid][0]);      // left of the cut that ends it
+    dgq_seg_t row;
+    row.start = starts[tid];
+    row.kmin = r.x + 0.0f;
+    row.kmax = r.y + 0.0f;
+    row.vmin = r.z + 0.0f;
+    row.vmax = r.w + 0.0f;
+    row.kscale = dgq_scale(row.kmin, row.kmax, a.fmt.levels);
+    row.vscale = dgq_scale(row.vmin, row.vmax, a.fmt.levels);
+    row.reserved = 0;
+    a.cache.segs[bh * a.seg_cap + tid] = row;
+  }
+  if (tid == 0) {
+    a.cache.nseg[bh] = nseg;
+    dgq_tail_t tl;
+    tl.r0 = L;
+    const int rl = min(kWin, L);
+    tl.ring_len = rl;
+    tl.span_own = 0;
+    tl.window_done = 0;
+    for (int i = 0; i < 4; ++i) tl.span_range[i] = 0.f;
+    for (int i = 0; i < kWin; ++i) {
+      if (i < rl) {
+        const size_t idx = (size_t)h * a.total + c0 + (L - rl + i);
+        tl.ring_a[i] = a.ws_a[idx];
+        tl.ring_b[i] = a.ws_b[idx];
+      } else {
+        tl.ring_a[i] = 0;
+        tl.ring_b[i] = 0;
+      }
+    }
+    a.cache.tail[bh] = tl;
+  }
+}
+
+// -------------------------------------------------------------------------------------------
+// 2+3 fused, for sequences of at most kSmallSeq tokens: one workgroup of 512 threads per
+// (sequence, kv head) holds the key moments in LDS, keeps the scores of its 16 candidates per
+// thread in registers, runs the greedy rounds with no memory traffic, and reduces all segments'
+// min/max in one pass over the sub-block extrema (plus the raw tokens of sub-blocks a cut splits).
+// Wave reductions use DPP row operations and lane reads, not LDS permutes.
+// -------------------------------------------------------------------------------------------
+constexpr int kSmallSeq = 8192;
+constexpr int kSmallThreads = 512;
+constexpr int kSmallWaves = kSmallThreads / 64;
+constexpr int kPerThread = kSmallSeq / kSmallThreads;   // 16 candidates per thread
+static_assert(kPerThread == kWin, "one 16-token sub-block per thread");
+
+// LDS slot of token t, t in [-16, kSmallSeq + 16): one pad slot after every 16 tokens, so that
+// thread i reading token 16 i + u (all i of a wave at once) hits distinct banks; the 16 slots on
+// either side of the sequence hold zeros, so window sums need no bounds tests
+__device__ __forceinline__ int skew(int t) { return (t + kWin) + ((t + kWin) >> 4); }
+constexpr int kSkewed = (kSmallSeq + 2 * kWin) + (kSmallSeq + 2 * kWin) / 16;
+
 
 template <int D>
 __global__ __launch_bounds__(kSmallThreads) void select_small_kernel(CompressArgs a) {
