@@ -86,6 +86,13 @@ class DGQCache:
                        _ptr(self.nseg), _ptr(self.tail), _ptr(self.k_stage), _ptr(self.v_stage),
                        _ptr(self.status), num_blocks, batch)
 
+    def read_status(self) -> dict:
+        """The device status words (synchronizes with the device): appends that wanted a new segment
+        but found the table full, groups of inputs with a non-finite value, and device-side
+        inconsistencies that were skipped or clamped (see dgq_cache_t.status)."""
+        v = self.status.cpu().tolist()
+        return {"clamped_appends": v[0], "nonfinite_groups": v[1], "inconsistencies": v[2]}
+
     # host-side views for tests and reports (copies)
     def segment_table(self):
         """(starts int32 [B][H][cap], params float32 [B][H][cap][6], nseg [B][H]) on the host."""

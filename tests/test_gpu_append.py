@@ -135,6 +135,9 @@ def test_stream_table_full_clamps_and_counts():
     H.say("append stream clamp")
     cache, states = run_stream(cfg, 3, 64, params=params, check_every=16, k=k, v=v, cu=cu, lens=lens)
     assert sum(st.clamped for st in states.values()) > 0
+    st = cache.read_status()
+    assert st["clamped_appends"] == sum(s.clamped for s in states.values())
+    assert st["nonfinite_groups"] == 0 and st["inconsistencies"] == 0
 
 
 @pytest.mark.parametrize("cid,over,steps", [
