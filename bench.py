@@ -127,9 +127,21 @@ def kernel_source_digest() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic():
-    """HBM bytes per decode launch from the committed counter profile, if it was taken on the
-    current decode kernel source (else None)."""
+COMPRESS_SOURCES = ("compress.hip", "dgq_internal.h")
+
+
+def compress_source_digest() -> str:
+    """Digest of the sources the compress kernels are compiled from."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in COMPRESS_SOURCES:
+        h.update(open(os.path.join(ROOT, "quantized_paged_kv_dgq_amd", "csrc", name), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(what: str = "decode"):
+    """HBM bytes per decode launch ("decode") or per dgq_compress call ("compress") from the
+    committed counter profile, if it was taken on the current kernel sources (else None)."""
     path = os.path.join(ROOT, "profiles", "decode_llama3_8b_layer_hbm_traffic.txt")
     if not os.path.exists(path):
         return None
@@ -138,10 +150,12 @@ def measured_traffic():
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.split("#", 1)[0].strip()
-    if kv.get("decode_source_sha256_16") != kernel_source_digest():
+    digest = kernel_source_digest() if what == "decode" else compress_source_digest()
+    key = "decode_hbm_bytes_per_launch" if what == "decode" else "compress_hbm_bytes_per_call"
+    if kv.get(f"{what}_source_sha256_16") != digest:
         return None
     try:
-        return int(float(kv["decode_hbm_bytes_per_launch"]))
+        return int(float(kv[key]))
     except (KeyError, ValueError):
         return None
 
@@ -721,6 +735,7 @@ def main():
         "roofline_compress": {
             "bound": "hbm", "achieved": round(comp_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(comp_gbs / HBM_PEAK_GBS, 4),
+            "traffic": measured_traffic("compress"),
             "kernel": "dgq_compress (stats + scores + select + encode, HIP events around the call)",
         },
         "wall_s_timed": round(wall, 4),
