@@ -397,13 +397,64 @@ __device__ __forceinline__ void decode_body(const DecodeArgs &a, const AppendArg
   const int P = parts_of(L, span);
   if (p >= P) return;                              // the whole workgroup has nothing to do
   __shared__ AppendOut aout;
-  if (APPEND && p == P - 1) append_one<D, BS>(*ap, b, h, false, aout);
   const WaveRange wr = wave_range(wg_begin, span, L, wave);
   const int t_begin = wr.t_begin, t_end = wr.t_end;
   const bool active = t_begin < t_end;
   __shared__ int sh_blk[SpanBlocks<BS>::kBlocks];
   span_blk.publish(wblk0, (L + BS - 1) / BS, a.num_blocks, sh_blk, a.status);
   __syncthreads();
+
+  // block ids come from sh_blk: chunk c of the wave is local chunk lc0 + c of the workgroup
+  const int lc0 = (t_begin - wg_begin) / kChunk;
+  const size_t tile_bytes = (size_t)BS * D;
+  const int8_t *kpool = a.k_pool + (size_t)h * tile_bytes;
+  const int8_t *vpool = a.v_pool + (size_t)h * tile_bytes;
+  const size_t blk_stride = (size_t)a.hkv * tile_bytes;
+
+  // Fragment loads of chunk c (64 tokens) of the partition.  Keys: tile T (16 tokens) x slice m
+  // (64 channels) per A operand; values: channel tile n (16 channels) x 64 tokens per A operand.
+  auto load_k = [&](int c, v4i (&kf)[4][M]) {
+    if constexpr (BS == 64) {
+      const int blk = __builtin_amdgcn_readfirstlane(sh_blk[lc0 + c]);
+      const int8_t *kb = kpool + (size_t)blk * blk_stride;
+#pragma unroll
+      for (int T = 0; T < 4; ++T)
+#pragma unroll
+        for (int m = 0; m < M; ++m)
+          kf[T][m] = *reinterpret_cast<const v4i *>(kb + (((T * M + m) * 64) + lane) * 16);
+    } else {
+      const int8_t *kb = kpool + (size_t)sh_blk[4 * (lc0 + c) + ((lane & 15) >> 2)] * blk_stride;
+#pragma unroll
+      for (int T = 0; T < 4; ++T)
+#pragma unroll
+        for (int m = 0; m < M; ++m)
+          kf[T][m] = *reinterpret_cast<const v4i *>(kb + ((((T * M + m) * 4 + j) * 4 + (lane & 3)) * 16));
+    }
+  };
+  auto load_v = [&](int c, v4i (&vf)[NT]) {
+    if constexpr (BS == 64) {
+      const int blk = __builtin_amdgcn_readfirstlane(sh_blk[lc0 + c]);
+      const int8_t *vb = vpool + (size_t)blk * blk_stride;
+#pragma unroll
+      for (int n = 0; n < NT; ++n) vf[n] = *reinterpret_cast<const v4i *>(vb + (n * 64 + lane) * 16);
+    } else {
+      const int8_t *vb = vpool + (size_t)sh_blk[4 * (lc0 + c) + j] * blk_stride;
+#pragma unroll
+      for (int n = 0; n < NT; ++n) vf[n] = *reinterpret_cast<const v4i *>(vb + (16 * n + (lane & 15)) * 16);
+    }
+  };
+  // The workgroup that appends first requests each wave's first chunk when no token of it is in
+  // the tail block (the only block the append writes), so those loads overlap the append.
+  v4i kf[4][M];
+  v4i vf[NT];
+  const int tail_start = (L - 1) / BS * BS;
+  const bool appending = APPEND && p == P - 1;
+  const bool early = appending && active && t_begin + kChunk <= tail_start;
+  if (early) {
+    load_k(0, kf);
+    load_v(0, vf);
+  }
+  if (appending) append_one<D, BS>(*ap, b, h, false, aout);
   __shared__ float sh_o[kWaves][G][D];
   __shared__ float sh_m[kWaves][G], sh_l[kWaves][G];
   // float output of each lane (C layout), folded from the int32 sums only when a maximum moves
@@ -417,7 +468,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs &a, const AppendArg
 
   if (active) {
     // ---- segment table: lane k holds row k (after this step's append, for its workgroup) ----
-    const bool appended = APPEND && p == P - 1;
+    const bool appended = appending;
     const int ns = min(appended ? aout.ns : ns_raw, a.seg_cap);
     int s_start = INT_MAX;
     float s_ks = 0.f, s_midk = 0.f, s_vs = 0.f, s_midv = 0.f;
@@ -480,45 +531,6 @@ __device__ __forceinline__ void decode_body(const DecodeArgs &a, const AppendArg
     const float wq = live ? ldexpf(a.sm_log2, 16 - 8 * piece - qexp) : 0.f;
     const float qsum_s = qsum * a.sm_log2;
 
-    // block ids come from sh_blk: chunk c of the wave is local chunk lc0 + c of the workgroup
-    const int lc0 = (t_begin - wg_begin) / kChunk;
-    const size_t tile_bytes = (size_t)BS * D;
-    const int8_t *kpool = a.k_pool + (size_t)h * tile_bytes;
-    const int8_t *vpool = a.v_pool + (size_t)h * tile_bytes;
-    const size_t blk_stride = (size_t)a.hkv * tile_bytes;
-
-    // Fragment loads of chunk c (64 tokens) of the partition.  Keys: tile T (16 tokens) x slice m
-    // (64 channels) per A operand; values: channel tile n (16 channels) x 64 tokens per A operand.
-    auto load_k = [&](int c, v4i (&kf)[4][M]) {
-      if constexpr (BS == 64) {
-        const int blk = __builtin_amdgcn_readfirstlane(sh_blk[lc0 + c]);
-        const int8_t *kb = kpool + (size_t)blk * blk_stride;
-#pragma unroll
-        for (int T = 0; T < 4; ++T)
-#pragma unroll
-          for (int m = 0; m < M; ++m)
-            kf[T][m] = *reinterpret_cast<const v4i *>(kb + (((T * M + m) * 64) + lane) * 16);
-      } else {
-        const int8_t *kb = kpool + (size_t)sh_blk[4 * (lc0 + c) + ((lane & 15) >> 2)] * blk_stride;
-#pragma unroll
-        for (int T = 0; T < 4; ++T)
-#pragma unroll
-          for (int m = 0; m < M; ++m)
-            kf[T][m] = *reinterpret_cast<const v4i *>(kb + ((((T * M + m) * 4 + j) * 4 + (lane & 3)) * 16));
-      }
-    };
-    auto load_v = [&](int c, v4i (&vf)[NT]) {
-      if constexpr (BS == 64) {
-        const int blk = __builtin_amdgcn_readfirstlane(sh_blk[lc0 + c]);
-        const int8_t *vb = vpool + (size_t)blk * blk_stride;
-#pragma unroll
-        for (int n = 0; n < NT; ++n) vf[n] = *reinterpret_cast<const v4i *>(vb + (n * 64 + lane) * 16);
-      } else {
-        const int8_t *vb = vpool + (size_t)sh_blk[4 * (lc0 + c) + j] * blk_stride;
-#pragma unroll
-        for (int n = 0; n < NT; ++n) vf[n] = *reinterpret_cast<const v4i *>(vb + (16 * n + (lane & 15)) * 16);
-      }
-    };
     // segment index of token t (rows are sorted by start; row 0 starts at 0)
     auto seg_of = [&](int t) -> int {
       int idx = 0;
@@ -531,10 +543,10 @@ __device__ __forceinline__ void decode_body(const DecodeArgs &a, const AppendArg
     for (int n = 0; n < NT; ++n) cacc[n] = v4i{0, 0, 0, 0};
 
     const int nchunks = (t_end - t_begin + kChunk - 1) / kChunk;
-    v4i kf[4][M];
-    v4i vf[NT];
-    load_k(0, kf);
-    load_v(0, vf);
+    if (!early) {
+      load_k(0, kf);
+      load_v(0, vf);
+    }
     for (int c = 0; c < nchunks; ++c) {
       const int t0 = t_begin + c * kChunk;
 
