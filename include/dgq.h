@@ -22,6 +22,8 @@
  *     device memory and never synchronizes a stream.  Work is queued on `stream` in order.
  *   - Host pointers are marked (host).  The block pool handle is owned by the library until
  *     dgq_pool_destroy.
+ *   - Calls that take a batch of sequences accept at most 65535 of them (DGQ_ERR_UNSUPPORTED
+ *     above that: the batch is a launch-grid dimension).
  *   - Every call returns a dgq_status_t.  Arguments are checked on the host before anything is
  *     queued; a failed check queues nothing and writes nothing.  A failed kernel launch returns
  *     DGQ_ERR_HIP; dgq_last_error() gives the HIP error text of the calling thread's last failure.

@@ -16,12 +16,16 @@ dgq_status_t hip_fail(hipError_t err, const char *where) {
   return DGQ_ERR_HIP;
 }
 
+// Sequences are the z (or y) dimension of every launch grid, which holds at most 65535.
+constexpr int32_t kMaxGridBatch = 65535;
+
 static bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 static dgq_status_t check_params(const dgq_params_t *p) {
   if (p == nullptr) return DGQ_ERR_INVALID_ARG;
   if (p->num_kv_heads < 1 || p->num_q_heads < 1 || p->num_q_heads % p->num_kv_heads != 0)
     return DGQ_ERR_INVALID_ARG;
+  if (p->num_kv_heads > kMaxGridBatch) return DGQ_ERR_UNSUPPORTED;   // a launch-grid dimension too
   const int g = p->num_q_heads / p->num_kv_heads;
   if (g != 1 && g != 2 && g != 4) return DGQ_ERR_UNSUPPORTED;
   if (p->head_dim != 64 && p->head_dim != 128) return DGQ_ERR_UNSUPPORTED;
@@ -96,6 +100,7 @@ extern "C" dgq_status_t dgq_compress(const dgq_params_t *p, const uint16_t *k, c
   if (st != DGQ_OK) return st;
   if (batch < 0 || max_seq_len < 0 || total_tokens < 0) return DGQ_ERR_INVALID_ARG;
   if (batch == 0) return DGQ_OK;
+  if (batch > kMaxGridBatch) return DGQ_ERR_UNSUPPORTED;
   if (total_tokens > (int64_t)batch * max_seq_len || total_tokens >= (int64_t)1 << 31)
     return DGQ_ERR_INVALID_ARG;
   if (!k || !v || !cu_seqlens || !aligned(k, 16) || !aligned(v, 16)) return DGQ_ERR_INVALID_ARG;
@@ -120,6 +125,7 @@ extern "C" dgq_status_t dgq_append(const dgq_params_t *p, const uint16_t *k_tok,
   if (st != DGQ_OK) return st;
   if (batch < 0) return DGQ_ERR_INVALID_ARG;
   if (batch == 0) return DGQ_OK;
+  if (batch > kMaxGridBatch) return DGQ_ERR_UNSUPPORTED;
   if (!k_tok || !v_tok || !seq_lens || !aligned(k_tok, 16) || !aligned(v_tok, 16)) return DGQ_ERR_INVALID_ARG;
   if (block_table == nullptr || max_blocks < 1) return DGQ_ERR_INVALID_ARG;
   if ((st = check_cache(p, cache, batch, true)) != DGQ_OK) return st;
@@ -136,6 +142,7 @@ extern "C" dgq_status_t paged_decode_attn_int8(const dgq_params_t *p, const uint
   if (st != DGQ_OK) return st;
   if (batch < 0 || max_seq_len < 0) return DGQ_ERR_INVALID_ARG;
   if (batch == 0) return DGQ_OK;
+  if (batch > kMaxGridBatch) return DGQ_ERR_UNSUPPORTED;
   if (!q || !out || !seq_lens || !aligned(q, 16) || !aligned(out, 16)) return DGQ_ERR_INVALID_ARG;
   if (!std::isfinite(softmax_scale)) return DGQ_ERR_INVALID_ARG;
   if ((st = check_table(p, block_table, max_blocks, max_seq_len)) != DGQ_OK) return st;
@@ -157,6 +164,7 @@ extern "C" dgq_status_t dgq_append_decode(const dgq_params_t *p, const uint16_t 
   if (st != DGQ_OK) return st;
   if (batch < 0 || max_seq_len < 1) return DGQ_ERR_INVALID_ARG;
   if (batch == 0) return DGQ_OK;
+  if (batch > kMaxGridBatch) return DGQ_ERR_UNSUPPORTED;
   if (!k_tok || !v_tok || !aligned(k_tok, 16) || !aligned(v_tok, 16)) return DGQ_ERR_INVALID_ARG;
   if (!q || !out || !seq_lens || !aligned(q, 16) || !aligned(out, 16)) return DGQ_ERR_INVALID_ARG;
   if (!std::isfinite(softmax_scale)) return DGQ_ERR_INVALID_ARG;
@@ -236,6 +244,7 @@ extern "C" dgq_status_t dgq_marker_bits(const dgq_params_t *p, const dgq_cache_t
   if ((p->flags & DGQ_FORMAT_MARKER) == 0) return DGQ_ERR_INVALID_ARG;
   if (batch < 0 || max_seq_len < 0) return DGQ_ERR_INVALID_ARG;
   if (batch == 0) return DGQ_OK;
+  if (batch > kMaxGridBatch) return DGQ_ERR_UNSUPPORTED;
   if (!seq_lens || !bits_out) return DGQ_ERR_INVALID_ARG;
   if ((st = check_table(p, block_table, max_blocks, max_seq_len)) != DGQ_OK) return st;
   if ((st = check_cache(p, cache, batch, false)) != DGQ_OK) return st;
@@ -261,6 +270,7 @@ extern "C" dgq_status_t dgq_g64_quantize(const dgq_params_t *p, const uint16_t *
   if (st != DGQ_OK) return st;
   if (batch < 0 || max_rows < 0 || total_rows < 0 || max_seq_len < 0) return DGQ_ERR_INVALID_ARG;
   if (batch == 0) return DGQ_OK;
+  if (batch > kMaxGridBatch) return DGQ_ERR_UNSUPPORTED;
   if (total_rows > (int64_t)batch * max_rows || total_rows >= (int64_t)1 << 31) return DGQ_ERR_INVALID_ARG;
   if (!k || !v || !cu_seqlens || !aligned(k, 16) || !aligned(v, 16)) return DGQ_ERR_INVALID_ARG;
   if (stride_tok <= 0 || stride_head < 0 || stride_tok % 8 != 0 || stride_head % 8 != 0) return DGQ_ERR_INVALID_ARG;
@@ -279,6 +289,7 @@ extern "C" dgq_status_t paged_decode_attn_g64(const dgq_params_t *p, const uint1
   if (st != DGQ_OK) return st;
   if (batch < 0 || max_seq_len < 0) return DGQ_ERR_INVALID_ARG;
   if (batch == 0) return DGQ_OK;
+  if (batch > kMaxGridBatch) return DGQ_ERR_UNSUPPORTED;
   if (!q || !out || !seq_lens || !aligned(q, 16) || !aligned(out, 16)) return DGQ_ERR_INVALID_ARG;
   if (!std::isfinite(softmax_scale)) return DGQ_ERR_INVALID_ARG;
   if ((st = check_table(p, block_table, max_blocks, max_seq_len)) != DGQ_OK) return st;

@@ -128,6 +128,12 @@ def test_argument_checks_queue_nothing(lib):
                           None) == _lib.DGQ_ERR_INVALID_ARG
     # an empty batch is a no-op
     assert lib.dgq_append(ctypes.byref(p), None, None, None, 0, None, 0, None, None) == 0
+    # a batch beyond the launch grid's 65535 is refused before anything is touched
+    big = _lib.Cache(fake, fake, fake, fake, fake, fake, fake, fake, fake, 64, 70000)
+    assert lib.dgq_append(ctypes.byref(p), fake, fake, fake, 65536, fake, 4, ctypes.byref(big),
+                          None) == _lib.DGQ_ERR_UNSUPPORTED
+    assert lib.paged_decode_attn_int8(ctypes.byref(p), fake, ctypes.byref(big), fake, 4, fake, 65536, 64,
+                                      1.0, fake, fake, 1 << 30, None) == _lib.DGQ_ERR_UNSUPPORTED
 
 
 def _arr(*v):
