@@ -284,124 +284,141 @@ __device__ __forceinline__ float4 wave_minmax(float4 r) {
 // -------------------------------------------------------------------------------------------
 // 3. select
 // -------------------------------------------------------------------------------------------
-__device__ __forceinline__ void block_best(double &s, int &t, double *ss, int *st) {
-  const int tid = threadIdx.x;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const double s2 = __shfl_xor(s, o);
-    const int t2 = __shfl_xor(t, o);
-    if (s2 > s || (s2 == s && t2 < t)) {
-      s = s2;
-      t = t2;
-    }
-  }
-  __syncthreads();
-  if ((tid & 63) == 0) {
-    ss[tid >> 6] = s;
-    st[tid >> 6] = t;
-  }
-  __syncthreads();
-  s = ss[0];
-  t = st[0];
-  for (int w = 1; w < 4; ++w)
-    if (ss[w] > s || (ss[w] == s && st[w] < t)) {
-      s = ss[w];
-      t = st[w];
-    }
-}
+// One 1024-thread workgroup per (sequence, kv head).  The tile maxima are kept in LDS (sequences
+// of up to kSelTiles * 256 tokens; longer ones read them from the workspace), so a greedy round
+// costs one scan of LDS plus one re-read of the (at most two) tiles the new cut's suppression
+// window touches, both re-scanned at once.
+constexpr int kSelThreads = 1024;
+constexpr int kSelWaves = kSelThreads / 64;
+constexpr int kSelTiles = 4096;
 
 template <int D>
-__global__ __launch_bounds__(256) void select_kernel(CompressArgs a) {
+__global__ __launch_bounds__(kSelThreads) void select_kernel(CompressArgs a) {
   const int h = blockIdx.x, b = blockIdx.y;
   int c0, L;
   bool bad_seq;
   seq_range(a.cu, b, a.max_seq_len, a.total, c0, L, bad_seq);
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const size_t bh = (size_t)b * a.hkv + h;
-  __shared__ int cuts[kMaxCuts + 1];
-  __shared__ int ncuts;
-  __shared__ double ss[4];
-  __shared__ int st[4];
-  if (tid == 0) {
-    ncuts = 0;
-    if (bad_seq && h == 0) atomicAdd(a.cache.status + 2, 1ull);
-  }
-  __syncthreads();
+  constexpr int MS = kMaxCuts + 1;
+  __shared__ double2 stile[kSelTiles];
+  __shared__ double wbs[kSelWaves];
+  __shared__ int wbt[kSelWaves];
+  __shared__ int cuts[kMaxCuts];
+  __shared__ int starts[kMaxCuts + 2];
+  if (tid == 0 && bad_seq && h == 0) atomicAdd(a.cache.status + 2, 1ull);
 
-  double2 *tiles = a.ws_tile + bh * a.ntile;
+  // ---- greedy selection over the tile maxima ----
+  double2 *gtiles = a.ws_tile + bh * a.ntile;
+  const int ntiles = L >= 2 * kWin ? (L - kWin) / 256 + 1 : 0;
+  const bool in_lds = ntiles <= kSelTiles;
+  if (in_lds) {
+    constexpr int U = kSelTiles / kSelThreads;
+    double2 x[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = tid + kSelThreads * u;
+      if (c < ntiles) x[u] = gtiles[c];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = tid + kSelThreads * u;
+      if (c < ntiles) stile[c] = x[u];
+    }
+  }
+  double2 *tiles = in_lds ? stile : gtiles;
+  __syncthreads();
   const int max_seg = a.length_aware ? min(a.max_segments, length_aware_cap(L)) : a.max_segments;
-  if (L >= 2 * kWin && max_seg > 1) {
-    const int ntiles = (L - kWin) / 256 + 1;
+  int nc = 0;
+  if (ntiles > 0 && max_seg > 1) {
     for (int r = 0; r < max_seg - 1; ++r) {
       double s = -INFINITY;
       int t = INT_MAX;
-      for (int c = tid; c < ntiles; c += 256) {
+      for (int c = tid; c < ntiles; c += kSelThreads) {
         const double2 e = tiles[c];
-        const int te = (int)e.y;
-        if (e.x > s || (e.x == s && te < t)) {
+        if (better(e.x, (int)e.y, s, t)) {
           s = e.x;
-          t = te;
+          t = (int)e.y;
         }
       }
-      block_best(s, t, ss, st);
+      wave_best(s, t);
+      if (lane == 0) {
+        wbs[wave] = s;
+        wbt[wave] = t;
+      }
+      __syncthreads();
+      s = wbs[0];
+      t = wbt[0];
+      for (int w = 1; w < kSelWaves; ++w)
+        if (better(wbs[w], wbt[w], s, t)) {
+          s = wbs[w];
+          t = wbt[w];
+        }
+      __syncthreads();   // wbs is written again below
       if (s == -INFINITY) break;
       if (r > 0 && !(s >= a.tau)) break;
-      __syncthreads();
-      if (tid == 0) cuts[ncuts] = t;
-      __syncthreads();
-      if (tid == 0) ncuts = ncuts + 1;
-      __syncthreads();
-      const int nc = ncuts;
-      // re-scan the tiles that the suppressed window [t-15, t+15] touches
+      if (tid == 0) cuts[nc] = t;
+      ++nc;
+      // re-scan the tiles the suppressed window [t - 15, t + 15] touches (at most two): threads
+      // 0..255 the first, 256..511 the second
       const int lo_tile = max(0, (t - (kWin - 1)) / 256), hi_tile = min(ntiles - 1, (t + kWin - 1) / 256);
-      for (int c = lo_tile; c <= hi_tile; ++c) {
-        const int tc = c * 256 + tid;
-        double sc = -INFINITY;
-        int tt = INT_MAX;
+      const int c = lo_tile + (tid >> 8);
+      double sc = -INFINITY;
+      int tt = INT_MAX;
+      if (c <= hi_tile) {
+        const int tc = c * 256 + (tid & 255);
         if (tc >= kWin && tc <= L - kWin) {
-          bool alive = true;
-          for (int k = 0; k < nc; ++k) alive = alive && abs(tc - cuts[k]) > kWin - 1;
+          bool alive = abs(tc - t) > kWin - 1;
+          for (int k = 0; k + 1 < nc; ++k) alive = alive && abs(tc - cuts[k]) > kWin - 1;
           if (alive) {
             sc = a.ws_score[(size_t)h * a.total + c0 + tc];
             tt = tc;
           }
         }
-        block_best(sc, tt, ss, st);
-        if (tid == 0) tiles[c] = make_double2(sc, (double)tt);
-        __syncthreads();
       }
+      wave_best(sc, tt);
+      if (lane == 0) {
+        wbs[wave] = sc;
+        wbt[wave] = tt;
+      }
+      __syncthreads();
+      if ((tid & 255) == 0 && c <= hi_tile) {
+        const int w0 = 4 * (tid >> 8);   // the four waves of this tile
+        double bs = wbs[w0];
+        int bt = wbt[w0];
+        for (int w = 1; w < 4; ++w)
+          if (better(wbs[w0 + w], wbt[w0 + w], bs, bt)) {
+            bs = wbs[w0 + w];
+            bt = wbt[w0 + w];
+          }
+        tiles[c] = make_double2(bs, (double)bt);
+      }
+      __syncthreads();
     }
   }
-  __syncthreads();
-  const int nc = ncuts;
-  // starts = [0] + sorted cuts
-  __shared__ int starts[kMaxCuts + 2];
+  // starts = [0] + sorted cuts, then L
   if (tid == 0) {
-    int tmp[kMaxCuts + 1];
-    for (int i = 0; i < nc; ++i) tmp[i] = cuts[i];
-    for (int i = 1; i < nc; ++i) {
-      const int x = tmp[i];
-      int k = i - 1;
-      while (k >= 0 && tmp[k] > x) {
-        tmp[k + 1] = tmp[k];
+    starts[0] = 0;
+    for (int i = 0; i < nc; ++i) {
+      const int x = cuts[i];
+      int k = i;
+      while (k > 0 && starts[k] > x) {
+        starts[k + 1] = starts[k];
         --k;
       }
-      tmp[k + 1] = x;
+      starts[k + 1] = x;
     }
-    starts[0] = 0;
-    for (int i = 0; i < nc; ++i) starts[i + 1] = tmp[i];
     starts[nc + 1] = L;
   }
   __syncthreads();
   const int nseg = L > 0 ? nc + 1 : 0;
+
   // ---- every segment's K/V min/max ----
   // (1) whole sub-blocks, one pass: each thread folds its sub-blocks into the accumulator of the
   //     segment that holds them, with a batch of loads in flight; then one wave reduction per
   //     segment.
   // (2) a sub-block that a cut splits (cuts are >= 16 apart, so one cut per sub-block; a cut at a
-  //     multiple of 16 splits none) is re-read raw by one wave: wave w takes cuts w + 1, w + 5, ...
-  constexpr int MS = kMaxCuts + 1;
-  const int wave = tid >> 6, lane = tid & 63;
+  //     multiple of 16 splits none) is re-read raw by wave c - 1.
   const float4 ident = make_float4(INFINITY, -INFINITY, INFINITY, -INFINITY);
   auto fold = [](float4 &r, const float4 x) {
     r.x = fminf(r.x, x.x);
@@ -409,7 +426,7 @@ __global__ __launch_bounds__(256) void select_kernel(CompressArgs a) {
     r.z = fminf(r.z, x.z);
     r.w = fmaxf(r.w, x.w);
   };
-  __shared__ float4 sred[4][MS];
+  __shared__ float4 sred[kSelWaves][MS];
   __shared__ float4 sraw[kMaxCuts][2];   // cut c: (left part, right part)
   {
     const float4 *ext = a.ws_ext + bh * a.nsub;
@@ -418,13 +435,13 @@ __global__ __launch_bounds__(256) void select_kernel(CompressArgs a) {
 #pragma unroll
     for (int j = 0; j < MS; ++j) acc[j] = ident;
     constexpr int U = 8;
-    for (int i0 = tid; i0 < nsub; i0 += 256 * U) {
+    for (int i0 = tid; i0 < nsub; i0 += kSelThreads * U) {
       float4 x[U];
 #pragma unroll
-      for (int u = 0; u < U; ++u) x[u] = i0 + 256 * u < nsub ? ext[i0 + 256 * u] : ident;
+      for (int u = 0; u < U; ++u) x[u] = i0 + kSelThreads * u < nsub ? ext[i0 + kSelThreads * u] : ident;
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int i = i0 + 256 * u;
+        const int i = i0 + kSelThreads * u;
         if (i < nsub) {
           const int t0 = kWin * i, t1 = min(t0 + kWin, L);
           int j = 0;
@@ -445,8 +462,8 @@ __global__ __launch_bounds__(256) void select_kernel(CompressArgs a) {
       }
     }
   }
-  for (int c = wave + 1; c < nseg; c += 4) {
-    const int cut = starts[c];
+  if (wave + 1 < nseg) {
+    const int cut = starts[wave + 1];
     float4 left = ident, right = ident;
     if (cut % kWin != 0) {
       const int t0 = cut - cut % kWin;
@@ -482,15 +499,14 @@ __global__ __launch_bounds__(256) void select_kernel(CompressArgs a) {
     left = wave_minmax(left);
     right = wave_minmax(right);
     if (lane == 0) {
-      sraw[c - 1][0] = left;
-      sraw[c - 1][1] = right;
+      sraw[wave][0] = left;
+      sraw[wave][1] = right;
     }
   }
   __syncthreads();
   if (tid < nseg) {
     float4 r = sred[0][tid];
-#pragma unroll
-    for (int w = 1; w < 4; ++w) fold(r, sred[w][tid]);
+    for (int w = 1; w < kSelWaves; ++w) fold(r, sred[w][tid]);
     if (tid > 0) fold(r, sraw[tid - 1][1]);        // right of the cut that starts segment tid
     if (tid + 1 < nseg) fold(r, sraw[tid][0]);      // left of the cut that ends it
     dgq_seg_t row;
@@ -504,26 +520,21 @@ __global__ __launch_bounds__(256) void select_kernel(CompressArgs a) {
     row.reserved = 0;
     a.cache.segs[bh * a.seg_cap + tid] = row;
   }
+  // append state: open span starts at L, ring = the last min(16, L) tokens' moments
+  const int rl = min(kWin, L);
+  dgq_tail_t *tl = a.cache.tail + bh;
+  if (tid < kWin) {
+    const size_t idx = (size_t)h * a.total + c0 + (L - rl + tid);
+    tl->ring_a[tid] = tid < rl ? a.ws_a[idx] : 0;
+    tl->ring_b[tid] = tid < rl ? a.ws_b[idx] : 0;
+  }
+  if (tid < 4) tl->span_range[tid] = 0.f;
   if (tid == 0) {
     a.cache.nseg[bh] = nseg;
-    dgq_tail_t tl;
-    tl.r0 = L;
-    const int rl = min(kWin, L);
-    tl.ring_len = rl;
-    tl.span_own = 0;
-    tl.window_done = 0;
-    for (int i = 0; i < 4; ++i) tl.span_range[i] = 0.f;
-    for (int i = 0; i < kWin; ++i) {
-      if (i < rl) {
-        const size_t idx = (size_t)h * a.total + c0 + (L - rl + i);
-        tl.ring_a[i] = a.ws_a[idx];
-        tl.ring_b[i] = a.ws_b[idx];
-      } else {
-        tl.ring_a[i] = 0;
-        tl.ring_b[i] = 0;
-      }
-    }
-    a.cache.tail[bh] = tl;
+    tl->r0 = L;
+    tl->ring_len = rl;
+    tl->span_own = 0;
+    tl->window_done = 0;
   }
 }
 
@@ -975,7 +986,7 @@ static dgq_status_t launch_all(const CompressArgs &a, int bs, int max_seq_len, h
     }
   }
   if (small) hipLaunchKernelGGL(select_small_kernel<D>, dim3(hkv, batch), dim3(kSmallThreads), 0, s, a);
-  else hipLaunchKernelGGL(select_kernel<D>, dim3(hkv, batch), dim3(256), 0, s, a);
+  else hipLaunchKernelGGL(select_kernel<D>, dim3(hkv, batch), dim3(kSelThreads), 0, s, a);
   st = check_launch("dgq_compress select kernel");
   if (st != DGQ_OK) return st;
   if (max_seq_len == 0) return DGQ_OK;
