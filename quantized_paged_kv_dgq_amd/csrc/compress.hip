@@ -53,12 +53,35 @@ __device__ __forceinline__ void store_stream(int8_t *dst, const uint32_t (&w)[4]
   __builtin_nontemporal_store(u32x4{w[0], w[1], w[2], w[3]}, reinterpret_cast<u32x4 *>(dst));
 }
 
+// Workgroup order of the two passes over fp16 K/V (grid: chunks x kv heads x sequences): runs of
+// kRun consecutive 64-token chunks for every kv head in turn, so that the workgroups in flight read
+// whole token rows (all heads' 256-byte pieces of a 2 KB row) of a bounded token range instead of
+// one head's pieces of the whole sequence.  A bijection of (chunk, head); a partial last run keeps
+// the plain order.
+constexpr int kRun = 32;
+__device__ __forceinline__ void run_order(int &chunk, int &h) {
+  const int tiles = gridDim.x, hkv = gridDim.y;
+  const int id = blockIdx.x + tiles * blockIdx.y;
+  const int full = tiles / kRun * kRun;
+  if (id < full * hkv) {
+    const int w = id % (kRun * hkv);
+    h = w / kRun;
+    chunk = id / (kRun * hkv) * kRun + w % kRun;
+  } else {
+    const int r = id - full * hkv, rem = tiles - full;
+    h = r / rem;
+    chunk = full + r % rem;
+  }
+}
+
 // -------------------------------------------------------------------------------------------
 // 1. stats
 // -------------------------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void stats_kernel(CompressArgs a) {
-  const int tile = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  int tile, h;
+  run_order(tile, h);
+  const int b = blockIdx.z;
   int c0, L;
   bool bad_seq;
   seq_range(a.cu, b, a.max_seq_len, a.total, c0, L, bad_seq);
@@ -802,7 +825,9 @@ __global__ __launch_bounds__(kSmallThreads) void select_small_kernel(CompressArg
 template <int D, int BS>
 __global__ __launch_bounds__(256) void encode_kernel(CompressArgs a) {
   constexpr int VROW = D + 8;   // padded LDS row (halves)
-  const int chunk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  int chunk, h;
+  run_order(chunk, h);
+  const int b = blockIdx.z;
   int c0, L;
   bool bad_seq;
   seq_range(a.cu, b, a.max_seq_len, a.total, c0, L, bad_seq);
