@@ -11,7 +11,8 @@
 //    of each (sequence, kv head) to finish merges the partitions by log-sum-exp.
 //  * The dequantization is folded into integer dot products: q . khat_t = ks_t * (q . c_t) +
 //    midK_t * sum(q) and sum_t p_t vhat_t = sum_t (p_t vs_t) c_t + sum_t p_t midV_t, where
-//    (ks, midK, vs, midV) belong to the segment of token t and mid = min + 128 * scale.
+//    (ks, midK, vs, midV) belong to the segment of token t and mid = min + 128 * scale (127 in
+//    the marker format, whose codes start at -127).
 //  * q . c and (p vs) . c run on the int8 matrix cores (v_mfma_i32_16x16x64_i8) with exact int32
 //    sums.  The float operand is split into three signed bytes (24-bit fixed point with a
 //    power-of-two scale), one byte per matrix column: the 16 columns are (query head of the
