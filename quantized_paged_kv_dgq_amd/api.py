@@ -268,8 +268,10 @@ def dgq_copy_blocks(params: DGQParams, cache: DGQCache, src_ids: torch.Tensor, d
                     stream=None) -> None:
     """Copy whole compressed blocks src_ids[i] -> dst_ids[i] (device int32 vectors)."""
     _need(src_ids.numel() == dst_ids.numel(), "src_ids and dst_ids differ in length")
-    st = _lib.load().dgq_copy_blocks(ctypes.byref(params.c), ctypes.byref(cache.c), _ptr(_ids(src_ids, "src_ids")),
-                                     _ptr(_ids(dst_ids, "dst_ids")), src_ids.numel(), _stream(stream))
+    _ids(src_ids, "src_ids")
+    _ids(dst_ids, "dst_ids")
+    st = _lib.load().dgq_copy_blocks(ctypes.byref(params.c), ctypes.byref(cache.c), _ptr(src_ids), _ptr(dst_ids),
+                                     src_ids.numel(), _stream(stream))
     check(st, "dgq_copy_blocks")
 
 
@@ -277,9 +279,10 @@ def dgq_copy_seq_state(params: DGQParams, cache: DGQCache, src_rows: torch.Tenso
                        stream=None) -> None:
     """Copy cache rows src_rows[i] -> dst_rows[i] (segment table, row count, append state, staging)."""
     _need(src_rows.numel() == dst_rows.numel(), "src_rows and dst_rows differ in length")
-    st = _lib.load().dgq_copy_seq_state(ctypes.byref(params.c), ctypes.byref(cache.c),
-                                        _ptr(_ids(src_rows, "src_rows")), _ptr(_ids(dst_rows, "dst_rows")),
-                                        src_rows.numel(), _stream(stream))
+    _ids(src_rows, "src_rows")
+    _ids(dst_rows, "dst_rows")
+    st = _lib.load().dgq_copy_seq_state(ctypes.byref(params.c), ctypes.byref(cache.c), _ptr(src_rows),
+                                        _ptr(dst_rows), src_rows.numel(), _stream(stream))
     check(st, "dgq_copy_seq_state")
 
 
@@ -294,8 +297,9 @@ def dgq_swap_out(params: DGQParams, cache: DGQCache, row: int, ids: torch.Tensor
     _need(staging.dtype == torch.uint8 and staging.is_contiguous(), "staging: contiguous uint8")
     _need(host is None or (host.dtype == torch.uint8 and host.is_contiguous() and host.numel() >= staging.numel()),
           "host: contiguous uint8 at least as large as staging")
-    st = _lib.load().dgq_swap_out(ctypes.byref(params.c), ctypes.byref(cache.c), row, _ptr(_ids(ids, "ids")),
-                                  ids.numel(), _ptr(staging), staging.numel(), _ptr(host), _stream(stream))
+    _ids(ids, "ids")
+    st = _lib.load().dgq_swap_out(ctypes.byref(params.c), ctypes.byref(cache.c), row, _ptr(ids), ids.numel(),
+                                  _ptr(staging), staging.numel(), _ptr(host), _stream(stream))
     check(st, "dgq_swap_out")
 
 
@@ -305,8 +309,9 @@ def dgq_swap_in(params: DGQParams, cache: DGQCache, row: int, ids: torch.Tensor,
     _need(staging.dtype == torch.uint8 and staging.is_contiguous(), "staging: contiguous uint8")
     _need(host is None or (host.dtype == torch.uint8 and host.is_contiguous() and host.numel() >= staging.numel()),
           "host: contiguous uint8 at least as large as staging")
-    st = _lib.load().dgq_swap_in(ctypes.byref(params.c), ctypes.byref(cache.c), row, _ptr(_ids(ids, "ids")),
-                                 ids.numel(), _ptr(staging), staging.numel(), _ptr(host), _stream(stream))
+    _ids(ids, "ids")
+    st = _lib.load().dgq_swap_in(ctypes.byref(params.c), ctypes.byref(cache.c), row, _ptr(ids), ids.numel(),
+                                 _ptr(staging), staging.numel(), _ptr(host), _stream(stream))
     check(st, "dgq_swap_in")
 
 
