@@ -201,7 +201,7 @@ int32_t dgq_block_refcount(const void *pool, int32_t id);
 dgq_status_t dgq_block_cow(void *pool, int32_t n, const int32_t *ids, int32_t *out_ids);
 
 /* Copy whole compressed blocks of one layer: for i < n, the K and V codes of every kv head and the
- * boundary bits of block src_ids[i] are copied to block dst_ids[i].
+ * boundary bits (bit-tensor format) of block src_ids[i] are copied to block dst_ids[i].
  *   src_ids, dst_ids (device) int32 [n].  A dst id must not appear twice nor among the src ids
  *   (the copies run in parallel).  A pair with an id outside [0, num_blocks) is skipped and
  *   counted in status[2].  n == 0 queues nothing. */
@@ -219,7 +219,7 @@ dgq_status_t dgq_copy_seq_state(const dgq_params_t *p, const dgq_cache_t *cache,
 
 /* Bytes of the swap image of one sequence with n_blocks blocks (one layer): the cache row's state
  * (segment-table rows, row counts, append state, staging), then per block its K codes, V codes
- * and bits, each part padded to 16 bytes.  0 for invalid arguments. */
+ * and bits (none in the marker format), each part padded to 16 bytes.  0 for invalid arguments. */
 size_t dgq_swap_image_bytes(const dgq_params_t *p, int32_t n_blocks);
 /* Swap out one sequence of one layer: its cache row `row` (host int) and blocks ids[0..n_blocks)
  * (device int32, in logical order) are packed into `staging` (device, >= dgq_swap_image_bytes,
