@@ -556,7 +556,18 @@ def long_context(seed, dev, Q):
         "compress_us_per_layer": round(c_us, 2),
         "compress_tokens_per_s": round(L / (c_us / 1e6), 1),
         "segments_per_head_hist": np.bincount(nseg.reshape(-1), minlength=6).tolist(),
+        **kv_memory(cfg, caches[0]),
     }
+
+
+def kv_memory(cfg, cache):
+    """KV-cache bytes of all layers of the sequence: fp16 K and V against the DGQ layout (codes,
+    identifier bits and segment-table rows at their allocated capacity)."""
+    fp16 = 2 * cfg.seq_len * cfg.hkv * cfg.head_dim * 2 * cfg.layers
+    per_layer = 2 * cfg.seq_len * cfg.hkv * cfg.head_dim + cfg.seq_len * cfg.hkv // 8
+    per_layer += cache.segs.numel() * cache.segs.element_size() + cache.nseg.numel() * 4
+    return {"kv_bytes_fp16_all_layers": fp16, "kv_bytes_dgq_all_layers": per_layer * cfg.layers,
+            "compression_vs_fp16": round(fp16 / (per_layer * cfg.layers), 4)}
 
 
 def main():
@@ -565,8 +576,8 @@ def main():
         copy_calibration()
         return
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the path has no multi-GPU "
-              "part in this build", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the library has no "
+              "multi-GPU path", file=sys.stderr)
         sys.exit(2)
 
     import dgq_data
