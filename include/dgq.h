@@ -20,6 +20,9 @@
  * Conventions for every entry point
  *   - Device pointers are caller-owned HIP device memory; the library never allocates or frees
  *     device memory and never synchronizes a stream.  Work is queued on `stream` in order.
+ *   - The device entry points other than dgq_swap_out / dgq_swap_in (which copy to or from
+ *     host memory) queue kernel launches only: no memset, copy or event.  They may be captured in
+ *     a HIP graph; a replay reads the buffers' contents at replay time.
  *   - Host pointers are marked (host).  The block pool handle is owned by the library until
  *     dgq_pool_destroy.
  *   - Calls that take a batch of sequences accept at most 65535 of them (DGQ_ERR_UNSUPPORTED
