@@ -37,16 +37,69 @@ struct AppendOut {
   dgq_seg_t chosen;  // that row after the append
 };
 
-// The append of one token to (sequence b, kv head h), by all 256 threads of a workgroup.  With
-// publish_nseg false the new row count is left to the caller (out.ns): a fused decode publishes it
-// only after every workgroup of the same (sequence, head) has read the old count.
-template <int D, int BS>
-__device__ __forceinline__ void append_one(const AppendArgs &a, int b, int h, bool publish_nseg, AppendOut &out) {
+// The loads an append needs, all independent of one another: the new token (thread d < D holds
+// channel d), the segment-table rows (thread k < seg_cap holds row k), the append state (thread i
+// holds its 16-byte word i), and the row count and the new token's block id (thread 0).  A fused
+// decode issues them before its first chunk: loads return in the order they were issued, so an
+// append queued behind a chunk would wait for the whole chunk.  Every value stays with the
+// thread that loaded it until the append passes it through LDS, so no wait is forced before the
+// chunk's loads go out.
+struct AppendLoads {
+  uint16_t kb, vb;
+  uint4 seg[2];
+  uint4 tail;
+  int nseg;
+  int blk;      // the new token's block id (when t_ok)
+  int t;        // position of the new token
+  bool t_ok;
+};
+constexpr int kTailWords = (int)(sizeof(dgq_tail_t) / 16);
+static_assert(sizeof(dgq_tail_t) % 16 == 0 && sizeof(dgq_seg_t) == 32, "16-byte words");
+
+// The loads that depend only on (b, h).
+template <int D>
+__device__ __forceinline__ AppendLoads append_loads_state(const AppendArgs &a, int b, int h) {
+  static_assert(D <= 256, "one channel per thread");
   const int tid = threadIdx.x;
   const size_t bh = (size_t)b * a.hkv + h;
-  const int t = a.seq_lens[b];                 // position of the new token
-  __shared__ dgq_tail_t tl;
-  __shared__ int ns_sh, use_row, own_now, clamp_now;
+  AppendLoads l;
+  l.kb = 0;
+  l.vb = 0;
+  if (tid < D) {
+    l.kb = a.k_tok[bh * D + tid];
+    l.vb = a.v_tok[bh * D + tid];
+  }
+  if (tid < a.seg_cap) {
+    const uint4 *row = reinterpret_cast<const uint4 *>(a.cache.segs + bh * a.seg_cap + tid);
+    l.seg[0] = row[0];
+    l.seg[1] = row[1];
+  }
+  if (tid < kTailWords) l.tail = reinterpret_cast<const uint4 *>(a.cache.tail + bh)[tid];
+  l.nseg = tid == 0 ? a.cache.nseg[bh] : 0;
+  return l;
+}
+
+// The new token's position t and block: a consistent state has the open span in that same block.
+template <int BS>
+__device__ __forceinline__ void append_load_block(const AppendArgs &a, int b, int t, AppendLoads &l) {
+  l.t = t;
+  l.t_ok = t >= 0 && t / BS < a.max_blocks;
+  l.blk = 0;
+  if (threadIdx.x == 0 && l.t_ok) l.blk = a.block_table[(size_t)b * a.max_blocks + t / BS];
+}
+
+// The append of one token to (sequence b, kv head h), by all 256 threads of a workgroup, from the
+// loads of append_loads_state and append_load_block.  With publish_nseg false the new row count
+// is left to the caller (out.ns): a fused decode publishes it only after every workgroup of the
+// same (sequence, head) has read the old count.
+template <int D, int BS>
+__device__ __forceinline__ void append_one(const AppendArgs &a, int b, int h, bool publish_nseg, AppendOut &out,
+                                           const AppendLoads &ld) {
+  const int tid = threadIdx.x;
+  const size_t bh = (size_t)b * a.hkv + h;
+  const int t = ld.t;
+  __shared__ __align__(16) dgq_tail_t tl;
+  __shared__ int ns_sh, blk_sh, use_row, own_now, clamp_now;
   __shared__ float rk[4];                      // span ranges: kmin kmax vmin vmax
   __shared__ float4 red4[4];
   __shared__ long long span_a[kWin];
@@ -55,24 +108,21 @@ __device__ __forceinline__ void append_one(const AppendArgs &a, int b, int h, bo
   __shared__ long long tail_b[kWin];
   __shared__ dgq_seg_t chosen;
   __shared__ int reenc_all;                    // 1: every span token's codes change, 0: only the new one
-  __shared__ dgq_seg_t srow[kMaxSegCap];       // the segment table as it was before this append
-  // every load that does not depend on the state goes out at once: the state, the segment rows
-  // and the new token (thread d < D holds channel d)
-  static_assert(D <= 256, "one channel per thread");
-  uint16_t kb = 0, vb = 0;
-  if (tid < D) {
-    kb = a.k_tok[bh * D + tid];
-    vb = a.v_tok[bh * D + tid];
+  __shared__ __align__(16) dgq_seg_t srow[kMaxSegCap];   // the segment table as it was before this append
+  const uint16_t kb = ld.kb, vb = ld.vb;
+  if (tid < a.seg_cap) {
+    uint4 *row = reinterpret_cast<uint4 *>(&srow[tid]);
+    row[0] = ld.seg[0];
+    row[1] = ld.seg[1];
   }
-  if (tid < a.seg_cap) srow[tid] = a.cache.segs[bh * a.seg_cap + tid];
-  // the new token's block: a consistent state has the open span in that same block
-  const bool t_ok = t >= 0 && t / BS < a.max_blocks;
-  const int blk_t = t_ok ? a.block_table[(size_t)b * a.max_blocks + t / BS] : -1;
+  if (tid < kTailWords) reinterpret_cast<uint4 *>(&tl)[tid] = ld.tail;
   if (tid == 0) {
-    tl = a.cache.tail[bh];
-    ns_sh = a.cache.nseg[bh];
+    ns_sh = ld.nseg;
+    blk_sh = ld.blk;
   }
+  const bool t_ok = ld.t_ok;
   __syncthreads();
+  const int blk_t = t_ok ? blk_sh : -1;
   const int r0 = tl.r0;
   const int slot0 = r0 < 0 ? 0 : r0 % BS;
   const int span_len = t + 1 - r0;             // including the new token
@@ -369,6 +419,15 @@ __device__ __forceinline__ void append_one(const AppendArgs &a, int b, int h, bo
   // the span's codes must have landed before a fused decode in this workgroup loads the block
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+}
+
+// The append kernel's form: the loads, then the append.
+template <int D, int BS>
+__device__ __forceinline__ void append_one(const AppendArgs &a, int b, int h, bool publish_nseg, AppendOut &out) {
+  const int t = a.seq_lens[b];
+  AppendLoads l = append_loads_state<D>(a, b, h);
+  append_load_block<BS>(a, b, t, l);
+  append_one<D, BS>(a, b, h, publish_nseg, out, l);
 }
 
 AppendArgs make_append_args(const dgq_params_t *p, const uint16_t *k_tok, const uint16_t *v_tok,

@@ -369,8 +369,14 @@ __device__ __forceinline__ void decode_body(const DecodeArgs &a, const AppendArg
   const int span = a.part_tokens * kWaves;
   const int wg_begin = p * span;
 
-  // Loads that do not depend on the sequence length go out together with it: the block ids of
-  // the workgroup's span, the segment-table row of this lane and the query slice of this lane.
+  // The sequence length goes out first, then (fused step) the append's loads that depend only on
+  // (b, h), so that they land before the first chunks of all workgroups crowd the memory system;
+  // a workgroup that turns out not to append has spent about a kilobyte on them.  Then the loads
+  // that do not depend on the length: the block ids of the workgroup's span, the segment-table
+  // row of this lane and the query slice of this lane.
+  const int len_raw = a.seq_lens[b];
+  AppendLoads ald;
+  if constexpr (APPEND) ald = append_loads_state<D>(*ap, b, h);
   const int32_t *bt = a.block_table + (size_t)b * a.max_blocks;
   const int wblk0 = wg_begin / BS;
   SpanBlocks<BS> span_blk;
@@ -388,7 +394,8 @@ __device__ __forceinline__ void decode_body(const DecodeArgs &a, const AppendArg
     qraw[m][1] = src[1];
   }
 
-  const int L_raw = a.seq_lens[b] + (APPEND ? 1 : 0);
+  if constexpr (APPEND) append_load_block<BS>(*ap, b, len_raw, ald);
+  const int L_raw = len_raw + (APPEND ? 1 : 0);
   const int L = L_raw < 0 ? 0 : (L_raw > a.max_seq_len ? a.max_seq_len : L_raw);
   if (p == 0 && threadIdx.x == 0 && h == 0 && L != L_raw) atomicAdd(a.status + 2, 1ull);
   if (L == 0 && p == 0) {                          // an empty sequence attends to nothing: zeros
@@ -444,18 +451,20 @@ __device__ __forceinline__ void decode_body(const DecodeArgs &a, const AppendArg
       for (int n = 0; n < NT; ++n) vf[n] = *reinterpret_cast<const v4i *>(vb + (16 * n + (lane & 15)) * 16);
     }
   };
-  // The workgroup that appends first requests each wave's first chunk when no token of it is in
-  // the tail block (the only block the append writes), so those loads overlap the append.
+  // The workgroup that appends requests each wave's first chunk before the append (whose loads
+  // are already out), so the chunk streams in while the append runs and the append does not wait
+  // behind it.  The chunk is kept when none of its tokens is in the tail block (the only block the
+  // append writes); otherwise (or for a wave with no tokens) it is requested again afterwards.
   v4i kf[4][M];
   v4i vf[NT];
   const int tail_start = (L - 1) / BS * BS;
   const bool appending = APPEND && p == P - 1;
   const bool early = appending && active && t_begin + kChunk <= tail_start;
-  if (early) {
+  if (appending) {
     load_k(0, kf);
     load_v(0, vf);
+    append_one<D, BS>(*ap, b, h, false, aout, ald);
   }
-  if (appending) append_one<D, BS>(*ap, b, h, false, aout);
   __shared__ float sh_o[kWaves][G][D];
   __shared__ float sh_m[kWaves][G], sh_l[kWaves][G];
   // float output of each lane (C layout), folded from the int32 sums only when a maximum moves
