@@ -35,7 +35,7 @@
 namespace dgq {
 
 template <int D, int G, int BS>
-__global__ __launch_bounds__(64 * kWaves) void decode_partition_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(64 * kWaves, 2) void decode_partition_kernel(DecodeArgs a) {
   constexpr int M = D / 64;    // 64-channel slices of a key row
   constexpr int NT = D / 16;   // 16-channel tiles of the output
   const int p = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -703,7 +703,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs &a, const AppendArg
 
 
 template <int D, int G, int BS>
-__global__ __launch_bounds__(64 * kWaves) void append_decode_kernel(DecodeArgs a, AppendArgs ap) {
+__global__ __launch_bounds__(64 * kWaves, 2) void append_decode_kernel(DecodeArgs a, AppendArgs ap) {
   decode_body<D, G, BS, true>(a, &ap);
 }
 

@@ -182,7 +182,7 @@ __device__ __forceinline__ float2 unpack_range(uint32_t w) {
 }
 
 template <int D, int G, int BS>
-__global__ __launch_bounds__(64 * kWaves) void g64_decode_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(64 * kWaves, 2) void g64_decode_kernel(DecodeArgs a) {
   constexpr int M = D / 64;    // channel groups = 64-channel slices
   constexpr int NT = D / 16;
   const int p = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
