@@ -211,3 +211,43 @@ def test_compress_repeatable():
         outs.append((cache.k_pool.cpu(), cache.v_pool.cpu(), cache.segs.cpu(), cache.bits.cpu()))
     for a, b in zip(*outs):
         assert torch.equal(a, b)
+
+
+def test_compress_strided_inputs():
+    """The input is addressed through (stride_tok, stride_head): a head-major [H][T][D] tensor
+    (passed as its [T][H][D] view) and the K and V slices of a fused QKV projection output
+    [T][Hq + 2 Hkv][D] compress to the same bytes as contiguous token-major K and V, and the
+    contiguous result matches the oracle's segments."""
+    cfg = dgq_data.get_config(2, batch=3, seq_len=700)
+    k, v, cu, lens, dk, dv = H.upload_batch(cfg, 33)
+    params = H.params_for(cfg)
+    table, nblk = dgq_data.block_tables(cfg, 33)
+    dtable = torch.from_numpy(table).cuda()
+    dcu = torch.from_numpy(cu).cuda()
+    total = int(cu[-1])
+
+    def run(kk, vv):
+        cache = Q.DGQCache(params, nblk, cfg.batch)
+        Q.dgq_compress(params, kk, vv, dcu, dtable, cache, cfg.seq_len, total)
+        torch.cuda.synchronize()
+        assert cache.status.cpu().numpy()[1:3].tolist() == [0, 0]
+        return cache
+
+    ref = run(dk, dv)
+    heads = {(b, h): O.compress_head(k[cu[b]:cu[b + 1], h], v[cu[b]:cu[b + 1], h])
+             for b in range(cfg.batch) for h in range(cfg.hkv)}
+    H.compare_segments(ref, heads, cfg.batch, cfg.hkv)
+
+    # head-major storage, handed over as a [T][H][D] view (stride_tok = D, stride_head = T * D)
+    kh = dk.permute(1, 0, 2).contiguous()
+    vh = dv.permute(1, 0, 2).contiguous()
+    got_hm = run(kh.permute(1, 0, 2), vh.permute(1, 0, 2))
+    # fused QKV output: K and V are head slices of one [T][Hq + 2 Hkv][D] tensor; the query part
+    # holds a large value that would show up in the ranges if it were read
+    qkv = torch.full((total, cfg.hq + 2 * cfg.hkv, cfg.head_dim), 30.0, dtype=torch.float16, device="cuda")
+    qkv[:, cfg.hq:cfg.hq + cfg.hkv] = dk
+    qkv[:, cfg.hq + cfg.hkv:] = dv
+    got_qkv = run(qkv[:, cfg.hq:cfg.hq + cfg.hkv], qkv[:, cfg.hq + cfg.hkv:])
+    for got in (got_hm, got_qkv):
+        for name in ("k_pool", "v_pool", "segs", "nseg", "bits", "tail"):
+            assert torch.equal(getattr(got, name), getattr(ref, name)), name
