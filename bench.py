@@ -108,7 +108,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=20.0,
                     help="time budget of the CPU oracle baseline (0 to skip)")
     ap.add_argument("--no-long-context", action="store_true",
-                    help="skip the streaming and the 32-layer 128K long-context figures")
+                    help="skip the streaming, high-concurrency, tiny and 32-layer 128K long-context figures")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 512 MiB device copy (torch) a few times: the reference "
                          "kernel of known size for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE")
@@ -503,6 +503,96 @@ def streaming(seed, dev, Q):
     }
 
 
+def fixed_batch(cid, seed, dev, Q, ncache, reps):
+    """Compress and decode of one whole configured batch (no append): ``ncache`` caches of the
+    same batch rotate, so each decode reads a cache written ``ncache - 1`` compressions earlier
+    and its codes come from HBM.  Medians of HIP-event times; algorithmic bytes as for the main
+    workload (codes + block table + segment rows + q + out for the decode, 3 B per element +
+    identifier bits + segment rows for the compress); error against float32 attention over the
+    unquantized keys/values."""
+    import torch
+
+    import dgq_data
+
+    cfg = dgq_data.get_config(cid)
+    B, hkv, hq, d, bs = cfg.batch, cfg.hkv, cfg.hq, cfg.head_dim, cfg.block_size
+    k, v, cu, lens = dgq_data.batch_kv_device(cfg, seed, 0, dev)
+    total, L = int(cu[-1]), int(lens.max())
+    dcu = cu.to(dev)
+    table, nblk = dgq_data.block_tables(cfg, seed)
+    dtable = torch.from_numpy(table).to(dev)
+    params = Q.DGQParams(hkv, hq, d, bs)
+    caches = [Q.DGQCache(params, nblk, B, dev) for _ in range(ncache)]
+    ws_c = Q.workspace(Q.compress_workspace_size(params, B, total, L), dev)
+    ws_d = Q.workspace(Q.decode_workspace_size(params, B, L), dev)
+    q = torch.from_numpy(dgq_data.queries(cfg, seed)).to(dev)
+    dl = torch.from_numpy(np.asarray(lens, np.int32)).to(dev)
+    out = torch.empty((B, hq, d), dtype=torch.float32, device=dev)
+    for c in caches:
+        Q.dgq_compress(params, k, v, dcu, dtable, c, L, total, ws=ws_c)
+    ev = []
+    for i in range(reps + 2):
+        e = [Timer() for _ in range(3)]
+        e[0].record()
+        Q.dgq_compress(params, k, v, dcu, dtable, caches[i % ncache], L, total, ws=ws_c)
+        e[1].record()
+        Q.paged_decode_attn_int8(params, q, caches[(i + 1) % ncache], dtable, dl, L, out=out, ws=ws_d)
+        e[2].record()
+        ev.append(e)
+    torch.cuda.synchronize()
+    ev = ev[2:]
+    c_s = float(np.median([e[0].elapsed_time(e[1]) for e in ev])) / 1e3
+    d_s = float(np.median([e[1].elapsed_time(e[2]) for e in ev])) / 1e3
+    G = hq // hkv
+    ref = torch.empty((B, hq, d), dtype=torch.float32, device=dev)
+    cu64 = cu.numpy().astype(np.int64)
+    for b in range(B):
+        kb = k[int(cu64[b]):int(cu64[b + 1])].float().permute(1, 0, 2).contiguous()
+        vb = v[int(cu64[b]):int(cu64[b + 1])].float().permute(1, 0, 2).contiguous()
+        qb = q[b].float().view(hkv, G, d).contiguous()
+        sc = torch.bmm(qb, kb.transpose(1, 2).contiguous()) / math.sqrt(d)
+        ref[b] = torch.bmm(torch.softmax(sc, dim=-1), vb).reshape(hq, d)
+    err = rel_err_rows(out, ref)
+    nseg = caches[0].nseg.cpu().numpy()
+    lens64 = np.asarray(lens, np.int64)
+    seg_bytes = float(nseg.sum()) * 32
+    dec_bytes = float(2 * lens64.sum() * hkv * d + np.ceil(lens64 / bs).sum() * 4 + seg_bytes + B * hq * d * 6)
+    comp_bytes = float(total * hkv * d * 2 * 3 + total * hkv / 8 + seg_bytes)
+    return {
+        "decode_us": round(d_s * 1e6, 2),
+        "decode_gbs_alg": round(dec_bytes / d_s / 1e9, 1),
+        "decode_frac_hbm_peak": round(dec_bytes / d_s / 1e9 / HBM_PEAK_GBS, 4),
+        "decode_kv_tokens_per_s": round(float(lens64.sum()) / d_s, 1),
+        "compress_us": round(c_s * 1e6, 2),
+        "compress_tokens_per_s": round(total / c_s, 1),
+        "compress_gbs_alg": round(comp_bytes / c_s / 1e9, 1),
+        "tokens": total,
+        "decode_bytes": int(dec_bytes),
+        "segments_per_head_hist": np.bincount(nseg.reshape(-1), minlength=6).tolist(),
+        "dgq_max_rel_err_vs_fp16": round(err[0], 6), "dgq_mean_rel_err_vs_fp16": round(err[1], 6),
+    }
+
+
+def high_concurrency(seed, dev, Q):
+    """The high-concurrency MHA workload: 100 sequences with lengths uniform in [512, 4096],
+    32 heads (multi-head, one query head per kv head), head_dim 128, 16-token blocks shuffled in a
+    shared pool; one decode query per sequence."""
+    rec = {"workload": "high-concurrency MHA: 100 seqs, lengths U[512, 4096], 32 KV = 32 q heads, "
+                       "head_dim 128, 16-token blocks shuffled"}
+    rec.update(fixed_batch(4, seed, dev, Q, ncache=3, reps=12))
+    return rec
+
+
+def tiny(seed, dev, Q):
+    """The tiny workload (1 sequence x 256 tokens, 2 heads, head_dim 64): launch-latency bound,
+    reported in microseconds only."""
+    r = fixed_batch(1, seed, dev, Q, ncache=2, reps=20)
+    return {"workload": "tiny: 1 seq x 256 tokens, 2 KV = 2 q heads, head_dim 64, 16-token blocks",
+            "compress_us": r["compress_us"], "decode_us": r["decode_us"],
+            "segments_per_head_hist": r["segments_per_head_hist"],
+            "dgq_max_rel_err_vs_fp16": r["dgq_max_rel_err_vs_fp16"]}
+
+
 def long_context(seed, dev, Q):
     """The 128K long-context workload: 32 layers of one 131,072-token sequence (8 KV / 32 query
     heads, head_dim 128, 64-token blocks, 1% outliers at 8 sigma), each layer compressed into its
@@ -768,6 +858,10 @@ def main():
         del caches, g_caches, k, v, ws_c
         torch.cuda.empty_cache()
         rec["streaming"] = streaming(args.seed, dev, Q)
+        torch.cuda.empty_cache()
+        rec["high_concurrency_mha"] = high_concurrency(args.seed, dev, Q)
+        torch.cuda.empty_cache()
+        rec["tiny"] = tiny(args.seed, dev, Q)
         torch.cuda.empty_cache()
         rec["long_context_128k"] = long_context(args.seed, dev, Q)
     if cpu is not None:

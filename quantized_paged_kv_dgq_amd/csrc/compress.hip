@@ -41,6 +41,7 @@ struct CompressArgs {
   double *ws_score;     // [hkv][total]
   float4 *ws_ext;       // [batch][hkv][nsub]: kmin, kmax, vmin, vmax
   double2 *ws_tile;     // [batch][hkv][ntile]: (score, t as double)
+  int4 *tile_map;       // ragged batches: [map_tiles] {sequence, tile, first token, length}; else null
   dgq_cache_t cache;
 };
 
@@ -75,17 +76,85 @@ __device__ __forceinline__ void run_order(int &chunk, int &h) {
 }
 
 // -------------------------------------------------------------------------------------------
+// 0. tile map (ragged batches)
+// -------------------------------------------------------------------------------------------
+// A grid of max_seq_len / 64 tiles for every sequence leaves most workgroups of a ragged batch
+// with nothing to do, and each still waits on a load of cu_seqlens before it can exit.  For such
+// batches one workgroup first lists the real 64-token tiles, sequence by sequence: entry i is
+// {sequence, tile of the sequence, its first token, its length (clamped as seq_range does)};
+// entries past the last real tile are {-1, 0, 0, 0}.  The two passes over the fp16 input then run
+// on a grid of map_tiles tiles.  One thread per sequence, so batches of up to kMapThreads.
+constexpr int kMapThreads = 1024;
+
+__global__ __launch_bounds__(kMapThreads) void tile_map_kernel(CompressArgs a, int map_tiles) {
+  __shared__ int s_scan[kMapThreads];
+  __shared__ int s_off[kMapThreads], s_c0[kMapThreads], s_len[kMapThreads];
+  const int tid = threadIdx.x;
+  int n = 0;
+  if (tid < a.batch) {
+    int c0, L;
+    bool bad;
+    seq_range(a.cu, tid, a.max_seq_len, a.total, c0, L, bad);
+    s_c0[tid] = c0;
+    s_len[tid] = L;
+    n = (L + kChunk - 1) / kChunk;
+  }
+  s_scan[tid] = n;
+  __syncthreads();
+  for (int o = 1; o < kMapThreads; o <<= 1) {   // inclusive prefix sum of the tile counts
+    const int x = tid >= o ? s_scan[tid - o] : 0;
+    __syncthreads();
+    s_scan[tid] += x;
+    __syncthreads();
+  }
+  if (tid < a.batch) s_off[tid] = s_scan[tid] - n;
+  const int real = min(s_scan[kMapThreads - 1], map_tiles);
+  __syncthreads();
+  for (int i = tid; i < map_tiles; i += kMapThreads) {
+    int4 e = make_int4(-1, 0, 0, 0);
+    if (i < real) {
+      // the last sequence whose first tile is at or before i (empty sequences share their
+      // successor's offset, so the last such sequence is the one that owns tile i)
+      int lo = 0, hi = a.batch - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (s_off[mid] <= i) lo = mid;
+        else hi = mid - 1;
+      }
+      e = make_int4(lo, i - s_off[lo], s_c0[lo], s_len[lo]);
+    }
+    a.tile_map[i] = e;
+  }
+}
+
+// The sequence and 64-token tile of this workgroup, with the sequence's first token and length:
+// from the tile map (grid over the real tiles of a ragged batch), else grid z is the sequence.
+// False when the tile holds no token.
+__device__ __forceinline__ bool compress_tile(const CompressArgs &a, int &tile, int &b, int &c0, int &L) {
+  if (a.tile_map != nullptr) {
+    const int4 e = a.tile_map[tile];
+    if (e.x < 0) return false;
+    b = e.x;
+    tile = e.y;
+    c0 = e.z;
+    L = e.w;
+    return true;
+  }
+  b = blockIdx.z;
+  bool bad;
+  seq_range(a.cu, b, a.max_seq_len, a.total, c0, L, bad);
+  return tile * kChunk < L;
+}
+
+// -------------------------------------------------------------------------------------------
 // 1. stats
 // -------------------------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void stats_kernel(CompressArgs a) {
   int tile, h;
   run_order(tile, h);
-  const int b = blockIdx.z;
-  int c0, L;
-  bool bad_seq;
-  seq_range(a.cu, b, a.max_seq_len, a.total, c0, L, bad_seq);
-  if (tile * 64 >= L) return;
+  int b, c0, L;
+  if (!compress_tile(a, tile, b, c0, L)) return;
   const int tid = threadIdx.x;
   const int t = tile * 64 + (tid >> 2), q = tid & 3;
   const bool valid = t < L;
@@ -562,28 +631,36 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(CompressArgs a) {
 }
 
 // -------------------------------------------------------------------------------------------
-// 2+3 fused, for sequences of at most kSmallSeq tokens: one workgroup of 512 threads per
+// 2+3 fused, for sequences of at most kSmallSeq tokens: one workgroup of 512 (or 256) threads per
 // (sequence, kv head) holds the key moments in LDS, keeps the scores of its 16 candidates per
 // thread in registers, runs the greedy rounds with no memory traffic, and reduces all segments'
 // min/max in one pass over the sub-block extrema (plus the raw tokens of sub-blocks a cut splits).
 // Wave reductions use DPP row operations and lane reads, not LDS permutes.
 // -------------------------------------------------------------------------------------------
-constexpr int kSmallSeq = 8192;
-constexpr int kSmallThreads = 512;
-constexpr int kSmallWaves = kSmallThreads / 64;
-constexpr int kPerThread = kSmallSeq / kSmallThreads;   // 16 candidates per thread
-static_assert(kPerThread == kWin, "one 16-token sub-block per thread");
+constexpr int kSmallSeq = 8192;     // longest sequence of the fused path
+constexpr int kPerThread = kWin;    // 16 candidates (one 16-token sub-block) per thread
 
-// LDS slot of token t, t in [-16, kSmallSeq + 16): one pad slot after every 16 tokens, so that
+// LDS slot of token t, t in [-16, S + 16) for sequences of up to S tokens: one pad slot after every 16 tokens, so that
 // thread i reading token 16 i + u (all i of a wave at once) hits distinct banks; the 16 slots on
 // either side of the sequence hold zeros, so window sums need no bounds tests
 __device__ __forceinline__ int skew(int t) { return (t + kWin) + ((t + kWin) >> 4); }
-constexpr int kSkewed = (kSmallSeq + 2 * kWin) + (kSmallSeq + 2 * kWin) / 16;
+template <int S>
+constexpr int skewed_slots() { return (S + 2 * kWin) + (S + 2 * kWin) / 16; }
 
 
-template <int D>
-__global__ __launch_bounds__(kSmallThreads) void select_small_kernel(CompressArgs a) {
-  constexpr int NW = kSmallWaves;
+// S: the longest sequence the instance handles (8192, or 4096 with half the threads and LDS,
+// so that two workgroups share a compute unit when a batch has many short sequences).  One wave
+// per cut re-reads the sub-block that cut splits, so an instance takes at most NW cuts:
+// small_cuts_ok() is the launch condition.
+template <int S>
+constexpr int small_waves() { return S / kPerThread / 64; }
+constexpr bool small_cuts_ok(int S_waves, int max_segments) { return max_segments - 1 <= S_waves; }
+static_assert(small_waves<kSmallSeq>() >= kMaxCuts, "the 8192-token instance takes every cut count");
+
+template <int D, int S>
+__global__ __launch_bounds__(S / kPerThread) void select_small_kernel(CompressArgs a) {
+  constexpr int NT = S / kPerThread;   // threads
+  constexpr int NW = small_waves<S>();
   constexpr int MS = kMaxCuts + 1;   // segments
   const int h = blockIdx.x, b = blockIdx.y;
   int c0, L;
@@ -591,9 +668,9 @@ __global__ __launch_bounds__(kSmallThreads) void select_small_kernel(CompressArg
   seq_range(a.cu, b, a.max_seq_len, a.total, c0, L, bad_seq);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const size_t bh = (size_t)b * a.hkv + h;
-  __shared__ int sa[kSkewed];
-  __shared__ double sbd[kSkewed];   // key moments b_t (< 2^36, exact in double)
-  __shared__ float4 sext[kSmallSeq / kWin];
+  __shared__ int sa[skewed_slots<S>()];
+  __shared__ double sbd[skewed_slots<S>()];   // key moments b_t (< 2^36, exact in double)
+  __shared__ float4 sext[S / kWin];
   __shared__ double gbs[2 * NW];   // wave bests (score, t) of a round, double-buffered
   __shared__ int gbt[2 * NW];
   __shared__ float4 sred[NW][MS];
@@ -609,20 +686,20 @@ __global__ __launch_bounds__(kSmallThreads) void select_small_kernel(CompressArg
     long long rb[kPerThread];
 #pragma unroll
     for (int i = 0; i < kPerThread; ++i) {
-      const int t = tid + kSmallThreads * i;
+      const int t = tid + NT * i;
       ra[i] = t < L ? a.ws_a[mrow + t] : 0;
       rb[i] = t < L ? a.ws_b[mrow + t] : 0;
     }
 #pragma unroll
     for (int i = 0; i < kPerThread; ++i) {
-      const int t = tid + kSmallThreads * i;
+      const int t = tid + NT * i;
       sa[skew(t)] = ra[i];
       sbd[skew(t)] = (double)rb[i];
       if (t < L && t >= L - kWin) sring_b[t - (L - kWin)] = rb[i];   // kept for the append state
     }
   }
   if (tid < 2 * kWin) {   // the zero pads
-    const int t = tid < kWin ? tid - kWin : kSmallSeq + tid - kWin;
+    const int t = tid < kWin ? tid - kWin : S + tid - kWin;
     sa[skew(t)] = 0;
     sbd[skew(t)] = 0.0;
   }
@@ -827,12 +904,9 @@ __global__ __launch_bounds__(256) void encode_kernel(CompressArgs a) {
   constexpr int VROW = D + 8;   // padded LDS row (halves)
   int chunk, h;
   run_order(chunk, h);
-  const int b = blockIdx.z;
-  int c0, L;
-  bool bad_seq;
-  seq_range(a.cu, b, a.max_seq_len, a.total, c0, L, bad_seq);
+  int b, c0, L;
+  if (!compress_tile(a, chunk, b, c0, L)) return;
   const int t0 = chunk * kChunk;
-  if (t0 >= L) return;
   const int tid = threadIdx.x;
   const size_t bh = (size_t)b * a.hkv + h;
   __shared__ int s_start[kMaxSegCap];
@@ -989,18 +1063,29 @@ CompressLayout compress_layout(const dgq_params_t *p, int32_t batch, int64_t tot
   off = align_up(off + (size_t)batch * hkv * l.nsub * sizeof(float4), 256);
   l.tile_off = off;
   off = align_up(off + (size_t)batch * hkv * l.ntile * sizeof(double2), 256);
+  l.map_tiles = (int64_t)(tot + kChunk - 1) / kChunk + (batch > 0 ? batch : 0);
+  l.map_off = off;
+  off = align_up(off + (size_t)l.map_tiles * sizeof(int4), 256);
   l.total = off;
   return l;
 }
 
 template <int D>
-static dgq_status_t launch_all(const CompressArgs &a, int bs, int max_seq_len, hipStream_t s) {
+static dgq_status_t launch_all(const CompressArgs &a, int bs, int max_seq_len, int64_t map_tiles, hipStream_t s) {
   const int batch = a.batch, hkv = a.hkv;
-  dim3 g64((max_seq_len + 63) / 64, hkv, batch);
+  // the passes over the fp16 input: one workgroup per (64-token tile, kv head) of the padded
+  // batch, or of the real tiles (tile map) for a ragged batch
+  const bool ragged = a.tile_map != nullptr;
+  dim3 g64 = ragged ? dim3((unsigned)map_tiles, hkv, 1) : dim3((max_seq_len + 63) / 64, hkv, batch);
   dim3 g256((max_seq_len + 255) / 256, hkv, batch);
   dgq_status_t st;
   const bool small = max_seq_len <= kSmallSeq && a.max_segments <= kMaxCuts + 1;
   if (max_seq_len > 0) {
+    if (ragged) {
+      hipLaunchKernelGGL(tile_map_kernel, dim3(1), dim3(kMapThreads), 0, s, a, (int)map_tiles);
+      st = check_launch("dgq_compress tile map kernel");
+      if (st != DGQ_OK) return st;
+    }
     hipLaunchKernelGGL(stats_kernel<D>, g64, dim3(256), 0, s, a);
     st = check_launch("dgq_compress stats kernel");
     if (st != DGQ_OK) return st;
@@ -1010,7 +1095,10 @@ static dgq_status_t launch_all(const CompressArgs &a, int bs, int max_seq_len, h
       if (st != DGQ_OK) return st;
     }
   }
-  if (small) hipLaunchKernelGGL(select_small_kernel<D>, dim3(hkv, batch), dim3(kSmallThreads), 0, s, a);
+  if (small && max_seq_len <= kSmallSeq / 2 && small_cuts_ok(small_waves<kSmallSeq / 2>(), a.max_segments))
+    hipLaunchKernelGGL((select_small_kernel<D, kSmallSeq / 2>), dim3(hkv, batch), dim3(kSmallSeq / 2 / kPerThread), 0, s, a);
+  else if (small)
+    hipLaunchKernelGGL((select_small_kernel<D, kSmallSeq>), dim3(hkv, batch), dim3(kSmallSeq / kPerThread), 0, s, a);
   else hipLaunchKernelGGL(select_kernel<D>, dim3(hkv, batch), dim3(kSelThreads), 0, s, a);
   st = check_launch("dgq_compress select kernel");
   if (st != DGQ_OK) return st;
@@ -1052,9 +1140,12 @@ dgq_status_t launch_compress(const dgq_params_t *p, const uint16_t *k, const uin
   a.ws_score = reinterpret_cast<double *>(w + l.score_off);
   a.ws_ext = reinterpret_cast<float4 *>(w + l.ext_off);
   a.ws_tile = reinterpret_cast<double2 *>(w + l.tile_off);
+  const int64_t padded = (int64_t)((max_seq_len + 63) / 64) * batch;
+  const bool ragged = batch <= kMapThreads && l.map_tiles <= INT_MAX && 5 * l.map_tiles < 4 * padded;
+  a.tile_map = ragged ? reinterpret_cast<int4 *>(w + l.map_off) : nullptr;
   a.cache = *cache;
-  if (p->head_dim == 128) return launch_all<128>(a, p->block_size, max_seq_len, stream);
-  return launch_all<64>(a, p->block_size, max_seq_len, stream);
+  if (p->head_dim == 128) return launch_all<128>(a, p->block_size, max_seq_len, l.map_tiles, stream);
+  return launch_all<64>(a, p->block_size, max_seq_len, l.map_tiles, stream);
 }
 
 }  // namespace dgq
