@@ -251,3 +251,23 @@ def test_compress_strided_inputs():
     for got in (got_hm, got_qkv):
         for name in ("k_pool", "v_pool", "segs", "nseg", "bits", "tail"):
             assert torch.equal(getattr(got, name), getattr(ref, name)), name
+
+
+@pytest.mark.parametrize("max_segments", [5, 8])
+def test_compress_ragged_batch_tile_map(max_segments):
+    """A ragged batch whose padded grid (longest sequence's tiles for every sequence) is far above
+    its real tiles, so the two passes over the input run on the list of real tiles: empty, 1-, 63-,
+    64- and 65-token sequences beside 4000-token ones, against the oracle (segments, codes, bits,
+    append state, decode).  max_segments 5 takes the 4096-token selection, 8 the 8192-token one."""
+    lens = np.array([0, 1, 63, 64, 65, 4000, 17, 0, 128, 3999, 2, 640, 33, 0, 4000, 100], np.int64)
+    cfg = dgq_data.get_config(4, batch=len(lens), hkv=2, hq=4, head_dim=64, seq_len=4000, min_len=1)
+    rng = np.random.default_rng(55)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    total = int(cu[-1])
+    sig = rng.choice([0.03, 0.15, 0.47], size=(total, cfg.hkv, 1))
+    k = (rng.standard_normal((total, cfg.hkv, cfg.head_dim)) * sig).astype(np.float16)
+    v = (rng.standard_normal((total, cfg.hkv, cfg.head_dim)) * sig).astype(np.float16)
+    padded = -(-int(lens.max()) // 64) * len(lens)
+    assert 5 * (-(-total // 64) + len(lens)) < 4 * padded      # the tile-list path is the one taken
+    H.say("compress ragged tile map", lens.tolist(), max_segments)
+    compress_and_check(cfg, 56, params=H.params_for(cfg, max_segments=max_segments), k=k, v=v, cu=cu, lens=lens)
