@@ -147,3 +147,30 @@ def test_decode_split_merge_repeatable(cid, over):
         assert H.rel_err_rows(outs[i].cpu().numpy(), ref) <= TOL
     # the merge leaves its completion counters at zero
     assert int(ws[: cfg.batch * cfg.hkv * 4].view(torch.int32).abs().sum().item()) == 0
+
+
+def test_decode_longest_workgroup_span():
+    """The largest launch the plan makes: 65,536 chunks of 64 tokens in all (one kv head of
+    4,194,304 tokens, head_dim 64, 64-token blocks permuted over the pool) gives every wave the
+    most chunks a workgroup stages block ids for (64 per wave, 16,384 tokens per workgroup) and
+    256 partitions to merge.  Random codes under five segments, against the oracle's float64
+    attention over the same codes."""
+    L = 1 << 22
+    cfg = dgq_data.get_config(3, batch=1, hkv=1, hq=1, head_dim=64, block_size=64, seq_len=L, outlier_frac=0.0)
+    rng = np.random.default_rng(91)
+    starts = [0, 70001, 1500000, 2500017, 4000000]
+    bounds = starts + [L]
+    segs = []
+    for j, s in enumerate(starts):
+        lo_k, lo_v = -rng.uniform(0.1, 2.0), -rng.uniform(0.1, 2.0)
+        segs.append(O.SegParams(s, np.float32(lo_k), np.float32(lo_k + rng.uniform(0.2, 4.0)),
+                                np.float32(lo_v), np.float32(lo_v + rng.uniform(0.2, 4.0))))
+    kc = rng.integers(-128, 128, (L, cfg.head_dim)).astype(np.int8)
+    vc = rng.integers(-128, 128, (L, cfg.head_dim)).astype(np.int8)
+    assert all(bounds[j] < bounds[j + 1] for j in range(len(starts)))
+    hc = O.HeadCompressed(L, segs, kc, vc, O.boundary_bits(starts, L))
+    H.say("decode longest span", L)
+    out, ref, _, _ = _run(cfg, 92, [L], heads={(0, 0): hc})
+    err = H.rel_err_rows(out, ref)
+    print(f"4M-token decode: max rel err {err:.3e}")
+    assert err <= 2e-3
