@@ -160,6 +160,27 @@ def measured_traffic(what: str = "decode"):
         return None
 
 
+def kernel_trace_decode_us():
+    """Kernel-trace average duration of the step's decode launches (the Llama-3-8B-shaped layer
+    decodes that follow the step's append) from the committed rocprofv3 summary, if it was taken
+    on the current decode sources (else None).  HIP events recorded around one kernel also count
+    the queue time the start event adds before the kernel (about 2-4 us here)."""
+    path = os.path.join(ROOT, "profiles", "llama3_8b_layer_step_kernel_trace.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#") and not line.startswith(" "):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.split("#", 1)[0].strip()
+    if kv.get("decode_source_sha256_16") != kernel_source_digest():
+        return None
+    try:
+        return float(kv["decode_c2_step_avg_us"])
+    except (KeyError, ValueError):
+        return None
+
+
 def copy_calibration():
     import torch
 
@@ -424,8 +445,9 @@ def streaming(seed, dev, Q):
     (append one token per sequence, decode one query per sequence), 8 KV / 32 query heads,
     head_dim 128, 64-token blocks.  Three copies of the same cache run the step three ways: DGQ
     dgq_append + paged_decode_attn_int8 (two launches), DGQ dgq_append_decode (one launch), and the
-    group-64 baseline (quantize the token, decode).  Per-step medians of HIP-event times, and the
-    last step's error against float32 attention over the unquantized keys/values."""
+    group-64 baseline (quantize the token, decode).  Each way streams on its own cache; per-step
+    times are the mean over the last 248 steps between one pair of HIP events.  Also the last
+    step's error against float32 attention over the unquantized keys/values."""
     import torch
 
     import dgq_data
@@ -450,8 +472,7 @@ def streaming(seed, dev, Q):
     outs = [torch.empty((B, hq, d), dtype=torch.float32, device=dev) for _ in range(3)]
     one = torch.arange(B + 1, dtype=torch.int32, device=dev)
     cu_dev = torch.from_numpy(cu).to(dev)
-    ev = [[Timer() for _ in range(4)] for _ in range(S)]
-    # every step's inputs are on the device before the timed loop, so the GPU never waits for the host
+    # every step's inputs are on the device before the timed loops, so the GPU never waits for the host
     steps = torch.arange(S, device=dev)
     tok_idx = (cu_dev[:-1][None, :] + L + steps[:, None]).reshape(-1)
     k_steps = k.index_select(0, tok_idx).view(S, B, hkv, d)
@@ -460,22 +481,34 @@ def streaming(seed, dev, Q):
     pos_steps = (L + steps[:, None].expand(S, B)).to(torch.int32).contiguous()
     pos1_steps = (pos_steps + 1).contiguous()
     torch.cuda.synchronize()
-    for s in range(S):
+
+    def step(mode, s):
         pos, pos1 = pos_steps[s], pos1_steps[s]
         kt, vt, q = k_steps[s], v_steps[s], q_steps[s]
-        e = ev[s]
-        e[0].record()
-        Q.dgq_append(params, kt, vt, pos, dtable, sep)
-        Q.paged_decode_attn_int8(params, q, sep, dtable, pos1, L + S, out=outs[0], ws=ws[0])
-        e[1].record()
-        Q.dgq_append_decode(params, kt, vt, pos, q, dtable, fused, L + S, out=outs[1], ws=ws[1])
-        e[2].record()
-        Q.dgq_g64_quantize(params, kt, vt, one, dtable, g64, 1, B, L + S, first_pos=pos)
-        Q.paged_decode_attn_g64(params, q, g64, dtable, pos1, L + S, out=outs[2], ws=ws[2])
-        e[3].record()
-    torch.cuda.synchronize()
-    t = np.array([[x[i].elapsed_time(x[i + 1]) for i in range(3)] for x in ev]) * 1e3
-    med = np.median(t[8:], axis=0)
+        if mode == 0:
+            Q.dgq_append(params, kt, vt, pos, dtable, sep)
+            Q.paged_decode_attn_int8(params, q, sep, dtable, pos1, L + S, out=outs[0], ws=ws[0])
+        elif mode == 1:
+            Q.dgq_append_decode(params, kt, vt, pos, q, dtable, fused, L + S, out=outs[1], ws=ws[1])
+        else:
+            Q.dgq_g64_quantize(params, kt, vt, one, dtable, g64, 1, B, L + S, first_pos=pos)
+            Q.paged_decode_attn_g64(params, q, g64, dtable, pos1, L + S, out=outs[2], ws=ws[2])
+
+    # each way runs the whole stream on its own cache: 8 untimed steps, then the other 248 between
+    # one pair of events (no event between steps, whose queue cost would land in every step)
+    warm = 8
+    med = []
+    for mode in range(3):
+        for s in range(warm):
+            step(mode, s)
+        t0, t1 = Timer(), Timer()
+        t0.record()
+        for s in range(warm, S):
+            step(mode, s)
+        t1.record()
+        torch.cuda.synchronize()
+        med.append(t0.elapsed_time(t1) * 1e3 / (S - warm))
+    q = q_steps[S - 1]
     # reference over the L + S tokens of every sequence
     k_all = [k[int(cu[b]):int(cu[b]) + L + S] for b in range(B)]
     v_all = [v[int(cu[b]):int(cu[b]) + L + S] for b in range(B)]
@@ -505,9 +538,9 @@ def streaming(seed, dev, Q):
 
 def fixed_batch(cid, seed, dev, Q, ncache, reps):
     """Compress and decode of one whole configured batch (no append): ``ncache`` caches of the
-    same batch rotate, so each decode reads a cache written ``ncache - 1`` compressions earlier
-    and its codes come from HBM.  Medians of HIP-event times; algorithmic bytes as for the main
-    workload (codes + block table + segment rows + q + out for the decode, 3 B per element +
+    same batch rotate, so consecutive decodes read different caches and their codes come from
+    HBM.  Mean of back-to-back calls between one pair of HIP events; algorithmic bytes as for the
+    main workload (codes + block table + segment rows + q + out for the decode, 3 B per element +
     identifier bits + segment rows for the compress); error against float32 attention over the
     unquantized keys/values."""
     import torch
@@ -530,19 +563,21 @@ def fixed_batch(cid, seed, dev, Q, ncache, reps):
     out = torch.empty((B, hq, d), dtype=torch.float32, device=dev)
     for c in caches:
         Q.dgq_compress(params, k, v, dcu, dtable, c, L, total, ws=ws_c)
-    ev = []
-    for i in range(reps + 2):
-        e = [Timer() for _ in range(3)]
-        e[0].record()
-        Q.dgq_compress(params, k, v, dcu, dtable, caches[i % ncache], L, total, ws=ws_c)
-        e[1].record()
-        Q.paged_decode_attn_int8(params, q, caches[(i + 1) % ncache], dtable, dl, L, out=out, ws=ws_d)
-        e[2].record()
-        ev.append(e)
-    torch.cuda.synchronize()
-    ev = ev[2:]
-    c_s = float(np.median([e[0].elapsed_time(e[1]) for e in ev])) / 1e3
-    d_s = float(np.median([e[1].elapsed_time(e[2]) for e in ev])) / 1e3
+    # compress and decode each timed as `reps` back-to-back calls (rotating caches) between one
+    # pair of events, after two untimed calls
+    def timed(fn):
+        for i in range(2):
+            fn(i)
+        e0, e1 = Timer(), Timer()
+        e0.record()
+        for i in range(reps):
+            fn(i)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / 1e3 / reps
+
+    c_s = timed(lambda i: Q.dgq_compress(params, k, v, dcu, dtable, caches[i % ncache], L, total, ws=ws_c))
+    d_s = timed(lambda i: Q.paged_decode_attn_int8(params, q, caches[i % ncache], dtable, dl, L, out=out, ws=ws_d))
     G = hq // hkv
     ref = torch.empty((B, hq, d), dtype=torch.float32, device=dev)
     cu64 = cu.numpy().astype(np.int64)
@@ -597,7 +632,8 @@ def long_context(seed, dev, Q):
     """The 128K long-context workload: 32 layers of one 131,072-token sequence (8 KV / 32 query
     heads, head_dim 128, 64-token blocks, 1% outliers at 8 sigma), each layer compressed into its
     own cache, then one decode query per layer, looped over the layers.  8 GiB of codes in all, so
-    every layer's decode reads HBM.  Per-layer medians of HIP-event times."""
+    every layer's decode reads HBM.  Compress: median of per-layer HIP-event times; decode: median
+    over three passes of the 32 layers (one event pair per pass) divided by 32."""
     import torch
 
     import dgq_data
@@ -623,18 +659,21 @@ def long_context(seed, dev, Q):
     qs = [torch.from_numpy(dgq_data.queries(cfg, seed, layer)).to(dev) for layer in range(cfg.layers)]
     lens = torch.full((1,), L, dtype=torch.int32, device=dev)
     out = torch.empty((1, hq, d), dtype=torch.float32, device=dev)
+    # one pass = the 32 layers' decodes back to back between one pair of events (an event between
+    # two kernels adds several microseconds of queue time to the interval it opens); the first
+    # pass is untimed
     dec = []
-    for rep in range(3):
+    for rep in range(4):
+        e0, e1 = Timer(), Timer()
+        e0.record()
         for layer in range(cfg.layers):
-            e0, e1 = Timer(), Timer()
-            e0.record()
             Q.paged_decode_attn_int8(params, qs[layer], caches[layer], dtable, lens, L, out=out, ws=ws_d)
-            e1.record()
-            if rep > 0:
-                dec.append((e0, e1))
+        e1.record()
+        if rep > 0:
+            dec.append((e0, e1))
     torch.cuda.synchronize()
     c_us = float(np.median([a.elapsed_time(b) for a, b in comp_ms])) * 1e3
-    d_us = float(np.median([a.elapsed_time(b) for a, b in dec])) * 1e3
+    d_us = float(np.median([a.elapsed_time(b) for a, b in dec])) * 1e3 / cfg.layers
     nseg = torch.stack([c.nseg for c in caches]).cpu().numpy()
     dec_bytes = (2 * L * hkv * d + math.ceil(L / bs) * 4 + float(nseg.mean()) * hkv * 32 + hq * d * 2 + hq * d * 4)
     return {
@@ -795,6 +834,7 @@ def main():
     g_dec_bytes = (B * 2 * Ld * hkv * d + B * Ld * hkv * (d // 64) * 4 * 2 + B * math.ceil(Ld / bs) * 4
                    + B * hq * d * 2 + B * hq * d * 4)
 
+    kt_us = kernel_trace_decode_us()
     rec = {
         "metric": "INT8 paged decode-attn GB/s (% HBM peak) + dgq_compress tokens/s",
         "value": round(dec_gbs, 1),
@@ -832,6 +872,8 @@ def main():
             "traffic": measured_traffic(),
             "kernel": "decode_partition_kernel<128,4,16> (one launch per paged_decode_attn_int8 call; "
                       "HIP events around the call on its stream)",
+            "kernel_trace_avg_us": kt_us,
+            "kernel_trace_frac": round(dec_bytes / (kt_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4) if kt_us else None,
         },
         "roofline_compress": {
             "bound": "hbm", "achieved": round(comp_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",

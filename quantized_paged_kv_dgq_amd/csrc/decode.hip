@@ -173,14 +173,14 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_partition_kernel(Decode
         for (int T = 0; T < 4; ++T)
 #pragma unroll
           for (int m = 0; m < M; ++m)
-            kf[T][m] = *reinterpret_cast<const v4i *>(kb + (((T * M + m) * 64) + lane) * 16);
+            kf[T][m] = load_codes(kb + (((T * M + m) * 64) + lane) * 16);
       } else {
         const int8_t *kb = kpool + (size_t)sh_blk[4 * (lc0 + c) + ((lane & 15) >> 2)] * blk_stride;
 #pragma unroll
         for (int T = 0; T < 4; ++T)
 #pragma unroll
           for (int m = 0; m < M; ++m)
-            kf[T][m] = *reinterpret_cast<const v4i *>(kb + ((((T * M + m) * 4 + j) * 4 + (lane & 3)) * 16));
+            kf[T][m] = load_codes(kb + ((((T * M + m) * 4 + j) * 4 + (lane & 3)) * 16));
       }
     };
     auto load_v = [&](int c, v4i (&vf)[NT]) {
@@ -188,11 +188,11 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_partition_kernel(Decode
         const int blk = __builtin_amdgcn_readfirstlane(sh_blk[lc0 + c]);
         const int8_t *vb = vpool + (size_t)blk * blk_stride;
 #pragma unroll
-        for (int n = 0; n < NT; ++n) vf[n] = *reinterpret_cast<const v4i *>(vb + (n * 64 + lane) * 16);
+        for (int n = 0; n < NT; ++n) vf[n] = load_codes(vb + (n * 64 + lane) * 16);
       } else {
         const int8_t *vb = vpool + (size_t)sh_blk[4 * (lc0 + c) + j] * blk_stride;
 #pragma unroll
-        for (int n = 0; n < NT; ++n) vf[n] = *reinterpret_cast<const v4i *>(vb + (16 * n + (lane & 15)) * 16);
+        for (int n = 0; n < NT; ++n) vf[n] = load_codes(vb + (16 * n + (lane & 15)) * 16);
       }
     };
     // segment index of token t (rows are sorted by start; row 0 starts at 0)
@@ -429,14 +429,14 @@ __device__ __forceinline__ void decode_body(const DecodeArgs &a, const AppendArg
       for (int T = 0; T < 4; ++T)
 #pragma unroll
         for (int m = 0; m < M; ++m)
-          kf[T][m] = *reinterpret_cast<const v4i *>(kb + (((T * M + m) * 64) + lane) * 16);
+          kf[T][m] = load_codes(kb + (((T * M + m) * 64) + lane) * 16);
     } else {
       const int8_t *kb = kpool + (size_t)sh_blk[4 * (lc0 + c) + ((lane & 15) >> 2)] * blk_stride;
 #pragma unroll
       for (int T = 0; T < 4; ++T)
 #pragma unroll
         for (int m = 0; m < M; ++m)
-          kf[T][m] = *reinterpret_cast<const v4i *>(kb + ((((T * M + m) * 4 + j) * 4 + (lane & 3)) * 16));
+          kf[T][m] = load_codes(kb + ((((T * M + m) * 4 + j) * 4 + (lane & 3)) * 16));
     }
   };
   auto load_v = [&](int c, v4i (&vf)[NT]) {
@@ -444,11 +444,11 @@ __device__ __forceinline__ void decode_body(const DecodeArgs &a, const AppendArg
       const int blk = __builtin_amdgcn_readfirstlane(sh_blk[lc0 + c]);
       const int8_t *vb = vpool + (size_t)blk * blk_stride;
 #pragma unroll
-      for (int n = 0; n < NT; ++n) vf[n] = *reinterpret_cast<const v4i *>(vb + (n * 64 + lane) * 16);
+      for (int n = 0; n < NT; ++n) vf[n] = load_codes(vb + (n * 64 + lane) * 16);
     } else {
       const int8_t *vb = vpool + (size_t)sh_blk[4 * (lc0 + c) + j] * blk_stride;
 #pragma unroll
-      for (int n = 0; n < NT; ++n) vf[n] = *reinterpret_cast<const v4i *>(vb + (16 * n + (lane & 15)) * 16);
+      for (int n = 0; n < NT; ++n) vf[n] = load_codes(vb + (16 * n + (lane & 15)) * 16);
     }
   };
   // The workgroup that appends requests each wave's first chunk before the append (whose loads

@@ -49,6 +49,13 @@ __device__ __forceinline__ float readlane_f(float x, int lane) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), lane));
 }
 
+// A 16-byte load of codes, which one call reads exactly once: non-temporal, so the lines are not
+// kept in the L2 or the Infinity Cache.  (Ordinary loads left the paged decode about 9 % slower:
+// 57.3 against 52.5 us for 16 x 8192 tokens, 54.7 against 49.2 us for 131,072.)
+__device__ __forceinline__ v4i load_codes(const int8_t *p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const v4i *>(p));
+}
+
 // Rounding to an integer by adding 1.5 * 2^23: for |v| <= 2^22 the float sum's bit pattern is
 // 0x4B400000 + rint(v) (round to nearest even).
 constexpr float kMagic = 12582912.0f;

@@ -298,9 +298,9 @@ __global__ __launch_bounds__(64 * kWaves, 2) void g64_decode_kernel(DecodeArgs a
 #pragma unroll
         for (int T = 0; T < 4; ++T)
 #pragma unroll
-          for (int m = 0; m < M; ++m) kf[T][m] = *reinterpret_cast<const v4i *>(kb + (((T * M + m) * 64) + lane) * 16);
+          for (int m = 0; m < M; ++m) kf[T][m] = load_codes(kb + (((T * M + m) * 64) + lane) * 16);
 #pragma unroll
-        for (int n = 0; n < NT; ++n) vf[n] = *reinterpret_cast<const v4i *>(vb + (n * 64 + lane) * 16);
+        for (int n = 0; n < NT; ++n) vf[n] = load_codes(vb + (n * 64 + lane) * 16);
       } else {
         const int8_t *kb = kpool + (size_t)sh_blk[4 * (lc0 + c) + ((lane & 15) >> 2)] * blk_stride;
         const int8_t *vb = vpool + (size_t)sh_blk[4 * (lc0 + c) + j] * blk_stride;
@@ -308,9 +308,9 @@ __global__ __launch_bounds__(64 * kWaves, 2) void g64_decode_kernel(DecodeArgs a
         for (int T = 0; T < 4; ++T)
 #pragma unroll
           for (int m = 0; m < M; ++m)
-            kf[T][m] = *reinterpret_cast<const v4i *>(kb + ((((T * M + m) * 4 + j) * 4 + (lane & 3)) * 16));
+            kf[T][m] = load_codes(kb + ((((T * M + m) * 4 + j) * 4 + (lane & 3)) * 16));
 #pragma unroll
-        for (int n = 0; n < NT; ++n) vf[n] = *reinterpret_cast<const v4i *>(vb + (16 * n + (lane & 15)) * 16);
+        for (int n = 0; n < NT; ++n) vf[n] = load_codes(vb + (16 * n + (lane & 15)) * 16);
       }
       auto tau_of = [&](int T, int i) -> int { return BS == 64 ? 16 * T + 4 * j + i : 16 * j + 4 * T + i; };
 
