@@ -27,6 +27,12 @@ struct G64QArgs {
 
 typedef unsigned int u32x4_g __attribute__((ext_vector_type(4)));
 
+// The quantizer reads its fp16 input once: non-temporal 16-byte loads (the lines are not kept).
+__device__ __forceinline__ uint4 load_once(const uint16_t *p) {
+  const u32x4_g v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_g *>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 __device__ __forceinline__ uint32_t pack_range(float mn, float mx) {
   union { _Float16 f; uint16_t u; } a, b;
   a.f = (_Float16)mn;   // exact: both are fp16 values
@@ -62,8 +68,8 @@ __global__ __launch_bounds__(256) void g64_quantize_kernel(G64QArgs a) {
     uint4 wk = make_uint4(0u, 0u, 0u, 0u), wv = wk;
     if (r0 + tau < n) {
       const size_t off = (size_t)(c0 + r0 + tau) * a.stride_tok + (size_t)h * a.stride_head + 8 * cc;
-      wk = *reinterpret_cast<const uint4 *>(a.k + off);
-      wv = *reinterpret_cast<const uint4 *>(a.v + off);
+      wk = load_once(a.k + off);
+      wv = load_once(a.v + off);
     }
     uint32_t *dk = reinterpret_cast<uint32_t *>(kt + tau * ROW + 8 * cc);
     uint32_t *dv = reinterpret_cast<uint32_t *>(vt + tau * ROW + 8 * cc);
