@@ -93,6 +93,51 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_partition_kernel(Decode
   float wv = 0.f;
 
   if (active) {
+    // block ids come from sh_blk: chunk c of the wave is local chunk lc0 + c of the workgroup
+    const int lc0 = (t_begin - wg_begin) / kChunk;
+    const size_t tile_bytes = (size_t)BS * D;
+    const int8_t *kpool = a.k_pool + (size_t)h * tile_bytes;
+    const int8_t *vpool = a.v_pool + (size_t)h * tile_bytes;
+    const size_t blk_stride = (size_t)a.hkv * tile_bytes;
+
+    // Fragment loads of chunk c (64 tokens) of the partition.  Keys: tile T (16 tokens) x slice m
+    // (64 channels) per A operand; values: channel tile n (16 channels) x 64 tokens per A operand.
+    auto load_k = [&](int c, v4i (&kf)[4][M]) {
+      if constexpr (BS == 64) {
+        const int blk = __builtin_amdgcn_readfirstlane(sh_blk[lc0 + c]);
+        const int8_t *kb = kpool + (size_t)blk * blk_stride;
+#pragma unroll
+        for (int T = 0; T < 4; ++T)
+#pragma unroll
+          for (int m = 0; m < M; ++m)
+            kf[T][m] = load_codes(kb + (((T * M + m) * 64) + lane) * 16);
+      } else {
+        const int8_t *kb = kpool + (size_t)sh_blk[4 * (lc0 + c) + ((lane & 15) >> 2)] * blk_stride;
+#pragma unroll
+        for (int T = 0; T < 4; ++T)
+#pragma unroll
+          for (int m = 0; m < M; ++m)
+            kf[T][m] = load_codes(kb + ((((T * M + m) * 4 + j) * 4 + (lane & 3)) * 16));
+      }
+    };
+    auto load_v = [&](int c, v4i (&vf)[NT]) {
+      if constexpr (BS == 64) {
+        const int blk = __builtin_amdgcn_readfirstlane(sh_blk[lc0 + c]);
+        const int8_t *vb = vpool + (size_t)blk * blk_stride;
+#pragma unroll
+        for (int n = 0; n < NT; ++n) vf[n] = load_codes(vb + (n * 64 + lane) * 16);
+      } else {
+        const int8_t *vb = vpool + (size_t)sh_blk[4 * (lc0 + c) + j] * blk_stride;
+#pragma unroll
+        for (int n = 0; n < NT; ++n) vf[n] = load_codes(vb + (16 * n + (lane & 15)) * 16);
+      }
+    };
+    // the first chunk goes out before the segment rows and the query are prepared
+    const int nchunks = (t_end - t_begin + kChunk - 1) / kChunk;
+    v4i kf[4][M];
+    v4i vf[NT];
+    load_k(0, kf);
+    load_v(0, vf);
     // ---- segment table: lane k holds row k ----
     const int ns = min(ns_raw, a.seg_cap);
     int s_start = INT_MAX;
@@ -156,45 +201,6 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_partition_kernel(Decode
     const float wq = live ? ldexpf(a.sm_log2, 16 - 8 * piece - qexp) : 0.f;
     const float qsum_s = qsum * a.sm_log2;
 
-    // block ids come from sh_blk: chunk c of the wave is local chunk lc0 + c of the workgroup
-    const int lc0 = (t_begin - wg_begin) / kChunk;
-    const size_t tile_bytes = (size_t)BS * D;
-    const int8_t *kpool = a.k_pool + (size_t)h * tile_bytes;
-    const int8_t *vpool = a.v_pool + (size_t)h * tile_bytes;
-    const size_t blk_stride = (size_t)a.hkv * tile_bytes;
-
-    // Fragment loads of chunk c (64 tokens) of the partition.  Keys: tile T (16 tokens) x slice m
-    // (64 channels) per A operand; values: channel tile n (16 channels) x 64 tokens per A operand.
-    auto load_k = [&](int c, v4i (&kf)[4][M]) {
-      if constexpr (BS == 64) {
-        const int blk = __builtin_amdgcn_readfirstlane(sh_blk[lc0 + c]);
-        const int8_t *kb = kpool + (size_t)blk * blk_stride;
-#pragma unroll
-        for (int T = 0; T < 4; ++T)
-#pragma unroll
-          for (int m = 0; m < M; ++m)
-            kf[T][m] = load_codes(kb + (((T * M + m) * 64) + lane) * 16);
-      } else {
-        const int8_t *kb = kpool + (size_t)sh_blk[4 * (lc0 + c) + ((lane & 15) >> 2)] * blk_stride;
-#pragma unroll
-        for (int T = 0; T < 4; ++T)
-#pragma unroll
-          for (int m = 0; m < M; ++m)
-            kf[T][m] = load_codes(kb + ((((T * M + m) * 4 + j) * 4 + (lane & 3)) * 16));
-      }
-    };
-    auto load_v = [&](int c, v4i (&vf)[NT]) {
-      if constexpr (BS == 64) {
-        const int blk = __builtin_amdgcn_readfirstlane(sh_blk[lc0 + c]);
-        const int8_t *vb = vpool + (size_t)blk * blk_stride;
-#pragma unroll
-        for (int n = 0; n < NT; ++n) vf[n] = load_codes(vb + (n * 64 + lane) * 16);
-      } else {
-        const int8_t *vb = vpool + (size_t)sh_blk[4 * (lc0 + c) + j] * blk_stride;
-#pragma unroll
-        for (int n = 0; n < NT; ++n) vf[n] = load_codes(vb + (16 * n + (lane & 15)) * 16);
-      }
-    };
     // segment index of token t (rows are sorted by start; row 0 starts at 0)
     auto seg_of = [&](int t) -> int {
       int idx = 0;
@@ -206,11 +212,6 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_partition_kernel(Decode
 #pragma unroll
     for (int n = 0; n < NT; ++n) cacc[n] = v4i{0, 0, 0, 0};
 
-    const int nchunks = (t_end - t_begin + kChunk - 1) / kChunk;
-    v4i kf[4][M];
-    v4i vf[NT];
-    load_k(0, kf);
-    load_v(0, vf);
     for (int c = 0; c < nchunks; ++c) {
       const int t0 = t_begin + c * kChunk;
 
@@ -477,6 +478,12 @@ __device__ __forceinline__ void decode_body(const DecodeArgs &a, const AppendArg
   float wv = 0.f;
 
   if (active) {
+    // the first chunk goes out before the segment rows and the query are prepared
+    const int nchunks = (t_end - t_begin + kChunk - 1) / kChunk;
+    if (!early) {
+      load_k(0, kf);
+      load_v(0, vf);
+    }
     // ---- segment table: lane k holds row k (after this step's append, for its workgroup) ----
     const bool appended = appending;
     const int ns = min(appended ? aout.ns : ns_raw, a.seg_cap);
@@ -552,11 +559,6 @@ __device__ __forceinline__ void decode_body(const DecodeArgs &a, const AppendArg
 #pragma unroll
     for (int n = 0; n < NT; ++n) cacc[n] = v4i{0, 0, 0, 0};
 
-    const int nchunks = (t_end - t_begin + kChunk - 1) / kChunk;
-    if (!early) {
-      load_k(0, kf);
-      load_v(0, vf);
-    }
     for (int c = 0; c < nchunks; ++c) {
       const int t0 = t_begin + c * kChunk;
 
