@@ -293,8 +293,9 @@ __global__ __launch_bounds__(64 * kWaves, 2) void g64_decode_kernel(DecodeArgs a
         const size_t ridx = (((size_t)blk_l * a.hkv + h) * BS + (t0 + lane) % BS) * M;
 #pragma unroll
         for (int m = 0; m < M; ++m) {
-          sh_rng[wave][0][lane][m] = t0 + lane < t_end ? a.k_range[ridx + m] : 0u;
-          sh_rng[wave][1][lane][m] = t0 + lane < t_end ? a.v_range[ridx + m] : 0u;
+          // read once per call, like the codes: non-temporal
+          sh_rng[wave][0][lane][m] = t0 + lane < t_end ? __builtin_nontemporal_load(a.k_range + ridx + m) : 0u;
+          sh_rng[wave][1][lane][m] = t0 + lane < t_end ? __builtin_nontemporal_load(a.v_range + ridx + m) : 0u;
         }
       }
       if constexpr (BS == 64) {
