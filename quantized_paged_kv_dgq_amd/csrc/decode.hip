@@ -83,13 +83,11 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_partition_kernel(Decode
   __syncthreads();
   __shared__ float sh_o[kWaves][G][D];
   __shared__ float sh_m[kWaves][G], sh_l[kWaves][G];
-  // float output of each lane (C layout), folded from the int32 sums only when a maximum moves
-  __shared__ float sh_acc[kWaves][NT * 4][64];
 
   float m_run = -INFINITY, l_run = 0.f, mv_run = 0.f;
-  float (*oacc)[64] = sh_acc[wave];
+  float oacc[NT * 4];   // float output of each lane (C layout), folded from the int32 sums when a maximum moves
 #pragma unroll
-  for (int r = 0; r < NT * 4; ++r) oacc[r][lane] = 0.f;
+  for (int r = 0; r < NT * 4; ++r) oacc[r] = 0.f;
   float wv = 0.f;
 
   if (active) {
@@ -283,7 +281,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_partition_kernel(Decode
 #pragma unroll
         for (int n = 0; n < NT; ++n) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) oacc[4 * n + i][lane] = (oacc[4 * n + i][lane] + (float)cacc[n][i]) * alpha;
+          for (int i = 0; i < 4; ++i) oacc[4 * n + i] = (oacc[4 * n + i] + (float)cacc[n][i]) * alpha;
           cacc[n] = v4i{0, 0, 0, 0};
         }
       }
@@ -325,7 +323,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_partition_kernel(Decode
 #pragma unroll
     for (int n = 0; n < NT; ++n)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) oacc[4 * n + i][lane] += (float)cacc[n][i];
+      for (int i = 0; i < 4; ++i) oacc[4 * n + i] += (float)cacc[n][i];
   }
 
   // ---- epilogue: combine the byte columns and the mid term per wave, then merge the waves of
@@ -338,7 +336,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_partition_kernel(Decode
   for (int n = 0; n < NT; ++n)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      float v = oacc[4 * n + i][lane] * wv;
+      float v = oacc[4 * n + i] * wv;
       v += quad_xor1(v);
       v += quad_xor2(v);
       if (piece == 0 && g < G) sh_o[wave][g][16 * n + 4 * j + i] = active ? v + mv_run : 0.f;
@@ -468,13 +466,11 @@ __device__ __forceinline__ void decode_body(const DecodeArgs &a, const AppendArg
   }
   __shared__ float sh_o[kWaves][G][D];
   __shared__ float sh_m[kWaves][G], sh_l[kWaves][G];
-  // float output of each lane (C layout), folded from the int32 sums only when a maximum moves
-  __shared__ float sh_acc[kWaves][NT * 4][64];
 
   float m_run = -INFINITY, l_run = 0.f, mv_run = 0.f;
-  float (*oacc)[64] = sh_acc[wave];
+  float oacc[NT * 4];   // float output of each lane (C layout), folded from the int32 sums when a maximum moves
 #pragma unroll
-  for (int r = 0; r < NT * 4; ++r) oacc[r][lane] = 0.f;
+  for (int r = 0; r < NT * 4; ++r) oacc[r] = 0.f;
   float wv = 0.f;
 
   if (active) {
@@ -630,7 +626,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs &a, const AppendArg
 #pragma unroll
         for (int n = 0; n < NT; ++n) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) oacc[4 * n + i][lane] = (oacc[4 * n + i][lane] + (float)cacc[n][i]) * alpha;
+          for (int i = 0; i < 4; ++i) oacc[4 * n + i] = (oacc[4 * n + i] + (float)cacc[n][i]) * alpha;
           cacc[n] = v4i{0, 0, 0, 0};
         }
       }
@@ -672,7 +668,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs &a, const AppendArg
 #pragma unroll
     for (int n = 0; n < NT; ++n)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) oacc[4 * n + i][lane] += (float)cacc[n][i];
+      for (int i = 0; i < 4; ++i) oacc[4 * n + i] += (float)cacc[n][i];
   }
 
   // ---- epilogue: combine the byte columns and the mid term per wave, then merge the waves of
@@ -685,7 +681,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs &a, const AppendArg
   for (int n = 0; n < NT; ++n)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      float v = oacc[4 * n + i][lane] * wv;
+      float v = oacc[4 * n + i] * wv;
       v += quad_xor1(v);
       v += quad_xor2(v);
       if (piece == 0 && g < G) sh_o[wave][g][16 * n + 4 * j + i] = active ? v + mv_run : 0.f;
