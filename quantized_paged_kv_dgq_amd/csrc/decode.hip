@@ -272,8 +272,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_partition_kernel(Decode
       for (int T = 0; T < 4; ++T)
 #pragma unroll
         for (int i = 0; i < 4; ++i) cmax = fmaxf(cmax, S[T][i]);
-      cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
-      cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
+      cmax = max_xor32(max_xor16(cmax));
       const float m_new = fmaxf(m_run, cmax);
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       if (__ballot(m_new > m_run) != 0ull) {
@@ -617,8 +616,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs &a, const AppendArg
       for (int T = 0; T < 4; ++T)
 #pragma unroll
         for (int i = 0; i < 4; ++i) cmax = fmaxf(cmax, S[T][i]);
-      cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
-      cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
+      cmax = max_xor32(max_xor16(cmax));
       const float m_new = fmaxf(m_run, cmax);
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       if (__ballot(m_new > m_run) != 0ull) {

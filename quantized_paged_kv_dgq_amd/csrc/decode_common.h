@@ -45,6 +45,18 @@ __device__ __forceinline__ float quad_xor2(float x) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, false));
 }
 
+// Maximum of x over lanes l and l ^ 16, and over lanes l and l ^ 32.  The gfx950 permlane swaps
+// exchange 16-lane rows (or 32-lane halves) of two registers in the VALU, with no LDS round trip;
+// swapping a register with itself leaves {x[l], x[l ^ 16]} (or {x[l], x[l ^ 32]}) in the pair.
+__device__ __forceinline__ float max_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 __device__ __forceinline__ float readlane_f(float x, int lane) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), lane));
 }
