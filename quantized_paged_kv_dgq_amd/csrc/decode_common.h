@@ -57,6 +57,17 @@ __device__ __forceinline__ float max_xor32(float x) {
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
+// Maximum of x over the whole wave with no LDS round trip: the quad exchanges, then the 8-lane and
+// 16-lane mirrors of a row (DPP row_half_mirror, row_mirror) leave every lane of a row with the row's
+// maximum; the two permlane swaps combine the four rows.
+__device__ __forceinline__ float wave_max(float x) {
+  x = fmaxf(x, quad_xor1(x));
+  x = fmaxf(x, quad_xor2(x));
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xF, 0xF, false)));
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x140, 0xF, 0xF, false)));
+  return max_xor32(max_xor16(x));
+}
+
 __device__ __forceinline__ float readlane_f(float x, int lane) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), lane));
 }

@@ -350,8 +350,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void g64_decode_kernel(DecodeArgs a
       for (int T = 0; T < 4; ++T)
 #pragma unroll
         for (int i = 0; i < 4; ++i) cmax = fmaxf(cmax, S[T][i]);
-      cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
-      cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
+      cmax = max_xor32(max_xor16(cmax));
       const float m_new = fmaxf(m_run, cmax);
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       m_run = m_new;
@@ -380,8 +379,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void g64_decode_kernel(DecodeArgs a
         }
 #pragma unroll
       for (int m = 0; m < M; ++m) {
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) wmax[m] = fmaxf(wmax[m], __shfl_xor(wmax[m], o));
+        wmax[m] = wave_max(wmax[m]);
         mv_run[m] = fmaf(mv_run[m], alpha, pmv[m]);
       }
       l_run = fmaf(l_run, alpha, psum);
