@@ -408,10 +408,12 @@ def check_append_from_empty(block_size=16):
 def check_group64():
     """Every (token, 64-channel group) is R8 with its own range: compared with the one-segment
     compression of that group alone (a different route through the oracle) and with numpy's
-    min/max; reconstruction and nearest-code property."""
+    min/max; nearest-code property; the reconstruction's closed forms at the two end codes and
+    its per-element error bound (half a step plus the fp32 rounding of the range)."""
     rng = np.random.default_rng(4)
     x = (rng.standard_normal((40, 128)) * 0.2).astype(np.float16)
     x[3, :64] = np.float16(0.5)                 # a constant group
+    x[7, 64:] = (rng.standard_normal(64) * 0.2 + 3.0).astype(np.float16)   # a group far from 0
     codes, gmin, gmax = O.group64_compress(x)
     for t in range(40):
         for g in range(2):
@@ -421,8 +423,58 @@ def check_group64():
             sc = O.quant_scale(np.float32(gmin[t, g]), np.float32(gmax[t, g]))
             assert _nearest_code_ok(x[t, sl], codes[t, sl], np.float32(gmin[t, g]), sc)
     rec = O.group64_dequant(codes, gmin, gmax)
-    assert np.max(np.abs(rec - x.astype(np.float64))) < 0.01
     assert np.all(rec[3, :64] == 0.5)
+    mn = gmin.astype(np.float64)
+    mx = gmax.astype(np.float64)
+    step = (mx - mn) / 255.0
+    for t in range(40):
+        for g in range(2):
+            sl = slice(64 * g, 64 * g + 64)
+            bound = 0.5 * step[t, g] * (1 + 2.0 ** -10) + 2.0 ** -22 * max(abs(mn[t, g]), abs(mx[t, g]))
+            assert np.max(np.abs(rec[t, sl] - x[t, sl].astype(np.float64))) <= bound, (t, g)
+    # closed forms at the end codes: -128 is the group's minimum exactly, 127 its maximum up to
+    # the fp32 rounding of (max - min) / 255; a code c sits c + 128 steps above the minimum
+    ends = np.zeros((40, 128), np.int8)
+    ends[:, 0::2] = -128
+    ends[:, 1::2] = 127
+    ends[:, 2] = 0
+    rec = O.group64_dequant(ends, gmin, gmax)
+    for t in range(40):
+        for g in range(2):
+            lo, hi = rec[t, 64 * g], rec[t, 64 * g + 1]
+            assert lo == mn[t, g], (t, g, lo, mn[t, g])
+            assert abs(hi - mx[t, g]) <= 2.0 ** -22 * max(abs(mx[t, g] - mn[t, g]), 2.0 ** -126), (t, g, hi, mx[t, g])
+            if g == 0:
+                mid = rec[t, 2]
+                assert abs(mid - (mn[t, 0] + 128.0 * step[t, 0])) <= 2.0 ** -22 * abs(mx[t, 0] - mn[t, 0]) + 1e-300
+
+
+def check_negative_zero():
+    """R1: -0 is stored as +0, so a range is the same bit pattern whatever the order of the values.
+    A segment made only of -0 keys stores +0 (bit pattern 0) as its key min and max; a run of mixed
+    -0 and +0 values gives the same bits in any token order; a group-64 range over -0 is +0."""
+    rng = np.random.default_rng(6)
+    d = 16
+    k = (rng.standard_normal((160, d)) * 0.3).astype(np.float16)
+    v = (rng.standard_normal((160, d)) * 0.3).astype(np.float16)
+    k[64:128] = np.float16(-0.0)
+    v[64:128] = np.where(rng.random((64, d)) < 0.5, np.float16(-0.0), np.float16(0.0)).astype(np.float16)
+    hc = O.compress_head(k, v, max_segments=3)
+    assert hc.starts == [0, 64, 128], hc.starts
+    seg = hc.segs[1]
+    for val in (seg.kmin, seg.kmax, seg.vmin, seg.vmax):
+        assert np.float32(val).view(np.uint32) == 0, (val, hex(int(np.float32(val).view(np.uint32))))
+    perm = rng.permutation(64)
+    v2 = v.copy()
+    v2[64:128] = v[64:128][perm]
+    hc2 = O.compress_head(k, v2, max_segments=3)
+    for a, b in ((seg.vmin, hc2.segs[1].vmin), (seg.vmax, hc2.segs[1].vmax)):
+        assert np.float32(a).view(np.uint32) == np.float32(b).view(np.uint32)
+    assert np.all(hc.kcodes[64:128] == -128)
+    x = np.zeros((2, 128), np.float16)
+    x[:, :64] = np.float16(-0.0)
+    _, gmin, gmax = O.group64_compress(x)
+    assert np.all(gmin.view(np.uint16) == 0) and np.all(gmax.view(np.uint16) == 0), (gmin, gmax)
 
 
 # -- segment-count policies (R12) ------------------------------------------------------------------
@@ -596,6 +648,7 @@ ALL_CHECKS = [
     check_minmax_library, check_bits, check_codes, check_constant_segment_exact,
     check_dequant_closed_form, check_attention, check_append_join, check_append_cut,
     check_append_capacity, check_append_matches_prefix_rule, check_append_from_empty, check_group64,
+    check_negative_zero,
     check_length_cap, check_min_var_floor, check_marker_format, check_marker_constant_segment,
     check_marker_append, check_marker_bytes,
 ]

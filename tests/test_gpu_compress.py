@@ -169,6 +169,12 @@ def test_compress_edge_cases(marker):
     y = x.copy()
     y[64:128] = np.float16(-0.125)
     seqs.append((x, y))
+    # a run of -0 keys and mixed +-0 values: ranges stored as +0 bit patterns
+    x = (rng.standard_normal((200, 2, d)) * 0.3).astype(np.float16)
+    x[64:128] = np.float16(-0.0)
+    y = (rng.standard_normal((200, 2, d)) * 0.3).astype(np.float16)
+    y[64:128] = np.where(rng.random((64, 2, d)) < 0.5, np.float16(-0.0), np.float16(0.0)).astype(np.float16)
+    seqs.append((x, y))
     # subnormals, signed zeros
     x = (rng.standard_normal((150, 2, d)) * 1e-5).astype(np.float16)
     x[::7] = np.float16(-0.0)

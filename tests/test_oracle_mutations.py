@@ -217,6 +217,31 @@ def _cap_inclusive(length):
     return min(5, int(math.floor(math.log2(length / 1024))) + 2)
 
 
+
+def _g64_dequant_offset_127(codes, gmin, gmax):
+    length, head_dim = codes.shape
+    ng = head_dim // O.GROUP
+    mn = np.asarray(gmin, np.float16).astype(np.float32)
+    mx = np.asarray(gmax, np.float16).astype(np.float32)
+    scale = ((mx - mn) / np.float32(O.CODE_LEVELS)).astype(np.float32)
+    c = codes.reshape(length, ng, O.GROUP).astype(np.float64)
+    return ((c + 127.0) * scale[:, :, None] + mn[:, :, None]).reshape(length, head_dim)
+
+
+def _g64_dequant_levels_256(codes, gmin, gmax):
+    length, head_dim = codes.shape
+    ng = head_dim // O.GROUP
+    mn = np.asarray(gmin, np.float16).astype(np.float32)
+    mx = np.asarray(gmax, np.float16).astype(np.float32)
+    scale = ((mx - mn) / np.float32(256)).astype(np.float32)
+    c = codes.reshape(length, ng, O.GROUP).astype(np.float64)
+    return ((c + 128.0) * scale[:, :, None] + mn[:, :, None]).reshape(length, head_dim)
+
+
+def _canonical_keeps_negative_zero(x16):
+    return np.asarray(x16, dtype=np.float16).astype(np.float32)
+
+
 MUTATIONS = {
     "variance_floor_on_min_window": ("change_scores", _scores_floor_on_min, [P.check_min_var_floor]),
     "length_cap_inclusive_edges": ("length_aware_cap", _cap_inclusive, [P.check_length_cap]),
@@ -244,6 +269,9 @@ MUTATIONS = {
     "marker_dequant_offset_128": ("dequant", _dequant_marker_offset_128, [P.check_marker_format]),
     "marker_choice_inverted": ("place_marker", _place_marker_inverted, [P.check_marker_format]),
     "append_without_marker": ("AppendState", _AppendNoMarker, [P.check_marker_append]),
+    "g64_dequant_offset_127": ("group64_dequant", _g64_dequant_offset_127, [P.check_group64]),
+    "g64_dequant_levels_256": ("group64_dequant", _g64_dequant_levels_256, [P.check_group64]),
+    "no_negzero_canonicalization": ("canonical_f32", _canonical_keeps_negative_zero, [P.check_negative_zero]),
 }
 
 
