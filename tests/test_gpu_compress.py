@@ -156,7 +156,7 @@ def _custom(cfg, seqs):
 def test_compress_edge_cases(marker):
     """Lengths 0, 1, 31, 32, 33; constant runs (exact reconstruction); subnormals and signed
     zeros; exact score ties; values beyond the statistics clamp; in both identifier formats."""
-    cfg = dgq_data.get_config(1, batch=9, hq=2)
+    cfg = dgq_data.get_config(1, batch=10, hq=2)
     rng = np.random.default_rng(0)
     d = cfg.head_dim
     seqs = []
