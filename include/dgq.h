@@ -19,7 +19,8 @@
  *
  * Conventions for every entry point
  *   - Device pointers are caller-owned HIP device memory; the library never allocates or frees
- *     device memory and never synchronizes a stream.  Work is queued on `stream` in order.
+ *     device memory and never synchronizes a stream.  Work is queued on `stream` in order.  (The
+ *     one library-owned device buffer is the fixed array of paged_decode_attn_int8_noalloc.)
  *   - The device entry points other than dgq_swap_out / dgq_swap_in (which copy to or from
  *     host memory) queue kernel launches only: no memset, copy or event.  They may be captured in
  *     a HIP graph; a replay reads the buffers' contents at replay time.
@@ -305,6 +306,30 @@ dgq_status_t paged_decode_attn_int8(const dgq_params_t *p, const uint16_t *q,
                                     int32_t max_blocks, const int32_t *seq_lens, int32_t batch,
                                     int32_t max_seq_len, float softmax_scale, float *out,
                                     void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* ---- Allocation-free paged INT8 decode, for callers that cannot allocate device memory or
+ * hand in a workspace (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Same arguments and results as paged_decode_attn_int8, without ws / ws_bytes: the
+ * split-sequence partials and completion counters live in a device array of
+ * DGQ_NOALLOC_SCRATCH_BYTES (16 MiB) inside the library's code object, one copy per GPU, held
+ * until the process ends.  The call allocates nothing (no hipMalloc, no allocating library
+ * routine); its first use on a device (the device of `stream`) looks up that device's copy.
+ * Each call queues a small kernel that zeroes the counters it uses, then the decode (kernel
+ * launches only, so it may be captured).
+ *   Limit: DGQ_ERR_WORKSPACE_TOO_SMALL, queuing nothing, when the call's partials need more than
+ *   the array: each partition of a (sequence, query head) takes (head_dim + 2) * 4 bytes, and
+ *   the launch plan aims at about 256 workgroups.  With head_dim 128 and 32 query heads: 16 x 8192
+ *   tokens or one 131072-token sequence need 0.53 MB, 100 sequences of up to 4096 tokens 1.7 MB;
+ *   about 1000 sequences fit, larger batches are refused.
+ *   Every call on one GPU shares that GPU's array and leaves in it what the last call wrote:
+ *   calls that overlap in time on one GPU (two streams, or two threads) race and give unspecified
+ *   results; serialize them. */
+#define DGQ_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+dgq_status_t paged_decode_attn_int8_noalloc(const dgq_params_t *p, const uint16_t *q,
+                                            const dgq_cache_t *cache, const int32_t *block_table,
+                                            int32_t max_blocks, const int32_t *seq_lens, int32_t batch,
+                                            int32_t max_seq_len, float softmax_scale, float *out,
+                                            hipStream_t stream);
 
 /* ---- Fused decode step: dgq_append followed by paged_decode_attn_int8, in one launch (DGQ
  * article 3.1: the new token's key/value is quantized inside the paged attention step).

@@ -24,6 +24,7 @@ from .api import (  # noqa: F401
     dgq_g64_quantize,
     paged_decode_attn_g64,
     paged_decode_attn_int8,
+    paged_decode_attn_int8_noalloc,
     swap_image_bytes,
     workspace,
 )

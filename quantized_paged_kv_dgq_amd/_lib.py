@@ -83,6 +83,7 @@ class Cache(ctypes.Structure):
 
 DGQ_POLICY_LENGTH_AWARE = 1
 DGQ_FORMAT_MARKER = 2
+DGQ_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 assert ctypes.sizeof(Params) == 48
 assert ctypes.sizeof(Seg) == 32
@@ -96,7 +97,8 @@ EXPORTS = [
     "dgq_copy_blocks", "dgq_copy_seq_state", "dgq_swap_image_bytes", "dgq_swap_out", "dgq_swap_in",
     "dgq_marker_bits",
     "dgq_compress_workspace_size", "dgq_decode_workspace_size",
-    "dgq_compress", "dgq_append", "paged_decode_attn_int8", "dgq_append_decode",
+    "dgq_compress", "dgq_append", "paged_decode_attn_int8", "paged_decode_attn_int8_noalloc",
+    "dgq_append_decode",
     "dgq_g64_quantize", "paged_decode_attn_g64",
 ]
 
@@ -157,6 +159,9 @@ def load() -> ctypes.CDLL:
     lib.paged_decode_attn_int8.argtypes = [P(Params), vp, P(Cache), vp, i32, vp, i32, i32,
                                            ctypes.c_float, vp, vp, sz, vp]
     lib.paged_decode_attn_int8.restype = i32
+    lib.paged_decode_attn_int8_noalloc.argtypes = [P(Params), vp, P(Cache), vp, i32, vp, i32, i32,
+                                                   ctypes.c_float, vp, vp]
+    lib.paged_decode_attn_int8_noalloc.restype = i32
     lib.dgq_append_decode.argtypes = [P(Params), vp, vp, vp, vp, i32, vp, i32, i32, ctypes.c_float,
                                       P(Cache), vp, vp, sz, vp]
     lib.dgq_append_decode.restype = i32

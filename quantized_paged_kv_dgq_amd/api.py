@@ -235,6 +235,25 @@ def paged_decode_attn_int8(params: DGQParams, q: torch.Tensor, cache: DGQCache,
     return out
 
 
+def paged_decode_attn_int8_noalloc(params: DGQParams, q: torch.Tensor, cache: DGQCache,
+                                   block_table: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int,
+                                   out: torch.Tensor, softmax_scale: Optional[float] = None,
+                                   stream=None) -> torch.Tensor:
+    """paged_decode_attn_int8 without a workspace (paged_decode_attn_int8_noalloc): the library's
+    fixed per-device scratch array holds the partials.  ``out`` (fp32 [B][Hq][D]) is required, so
+    that this call allocates nothing either."""
+    _need(q.dtype == torch.float16 and q.is_contiguous(), "q: contiguous float16 [B][Hq][D]")
+    _need(out.dtype == torch.float32 and out.is_contiguous() and out.shape == q.shape, "out: contiguous float32 like q")
+    _need(seq_lens.dtype == torch.int32 and block_table.dtype == torch.int32, "int32 index tensors")
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(params.c.head_dim)
+    st = _lib.load().paged_decode_attn_int8_noalloc(
+        ctypes.byref(params.c), _ptr(q), ctypes.byref(cache.c), _ptr(block_table), block_table.shape[1],
+        _ptr(seq_lens), q.shape[0], max_seq_len, float(softmax_scale), _ptr(out), _stream(stream))
+    check(st, "paged_decode_attn_int8_noalloc")
+    return out
+
+
 def dgq_append_decode(params: DGQParams, k_tok: torch.Tensor, v_tok: torch.Tensor, seq_lens: torch.Tensor,
                       q: torch.Tensor, block_table: torch.Tensor, cache: DGQCache, max_seq_len: int,
                       softmax_scale: Optional[float] = None, out: Optional[torch.Tensor] = None,

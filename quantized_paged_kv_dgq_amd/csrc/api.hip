@@ -3,6 +3,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "dgq_internal.h"
 #include "lifecycle.h"
@@ -150,6 +151,82 @@ extern "C" dgq_status_t paged_decode_attn_int8(const dgq_params_t *p, const uint
   const size_t need = decode_workspace_bytes(p, batch, max_seq_len);
   if (ws == nullptr || !aligned(ws, 256)) return DGQ_ERR_INVALID_ARG;
   if (ws_bytes < need) return DGQ_ERR_WORKSPACE_TOO_SMALL;
+  return launch_decode(p, q, cache, block_table, max_blocks, seq_lens, batch, max_seq_len,
+                       softmax_scale, out, ws, stream);
+}
+
+// ---- Allocation-free decode: the split-sequence partials and completion counters live in a
+// file-scope device array instead of a caller workspace.  Each device that runs the call holds its
+// own copy of the array until the process ends.  In host code `scratch` only names the array's
+// host-side stand-in; its device address comes from hipGetSymbolAddress, once per device. ----
+
+constexpr size_t kNoAllocScratchBytes = size_t(16) << 20;
+static_assert(kNoAllocScratchBytes == DGQ_NOALLOC_SCRATCH_BYTES, "header and library disagree");
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];   // device address of `scratch` per device, set up on first use
+
+// The device address of `scratch` on device `dev`, looked up with `dev` current (the calling
+// thread's current device is restored afterwards).
+dgq_status_t scratch_address(int dev, void **out) {
+  if (dev < 0 || dev >= kMaxDevices) return DGQ_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    int cur = 0;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return hip_fail(e, "hipSetDevice");
+    void *ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    const hipError_t e2 = cur != dev ? hipSetDevice(cur) : hipSuccess;
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (e2 != hipSuccess) return hip_fail(e2, "hipSetDevice");
+    if (ptr == nullptr || !aligned(ptr, 256)) return hip_fail(hipErrorInvalidSymbol, "scratch address");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return DGQ_OK;
+}
+
+// Zero n 32-bit words (the merge's completion counters) with a kernel, so that the clearing is
+// an ordinary stream-ordered launch (also inside a captured graph).
+__global__ void __launch_bounds__(256) zero_words_kernel(unsigned *w, int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) w[i] = 0u;
+}
+
+}  // namespace
+
+extern "C" dgq_status_t paged_decode_attn_int8_noalloc(const dgq_params_t *p, const uint16_t *q,
+                                                       const dgq_cache_t *cache,
+                                                       const int32_t *block_table, int32_t max_blocks,
+                                                       const int32_t *seq_lens, int32_t batch,
+                                                       int32_t max_seq_len, float softmax_scale,
+                                                       float *out, hipStream_t stream) {
+  dgq_status_t st = check_params(p);
+  if (st != DGQ_OK) return st;
+  if (batch < 0 || max_seq_len < 0) return DGQ_ERR_INVALID_ARG;
+  if (batch == 0) return DGQ_OK;
+  if (batch > kMaxGridBatch) return DGQ_ERR_UNSUPPORTED;
+  if (!q || !out || !seq_lens || !aligned(q, 16) || !aligned(out, 16)) return DGQ_ERR_INVALID_ARG;
+  if (!std::isfinite(softmax_scale)) return DGQ_ERR_INVALID_ARG;
+  if ((st = check_table(p, block_table, max_blocks, max_seq_len)) != DGQ_OK) return st;
+  if ((st = check_cache(p, cache, batch, false)) != DGQ_OK) return st;
+  if (decode_workspace_bytes_for(p, batch, max_seq_len, kDgqDecodeWaves) > kNoAllocScratchBytes)
+    return DGQ_ERR_WORKSPACE_TOO_SMALL;
+  int dev = 0;
+  hipError_t e = hipStreamGetDevice(stream, &dev);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamGetDevice");
+  void *ws = nullptr;
+  if ((st = scratch_address(dev, &ws)) != DGQ_OK) return st;
+  const int nctr = batch * p->num_kv_heads;
+  hipLaunchKernelGGL(zero_words_kernel, dim3((nctr + 255) / 256), dim3(256), 0, stream,
+                     reinterpret_cast<unsigned *>(ws), nctr);
+  if ((st = check_launch("paged_decode_attn_int8_noalloc clear")) != DGQ_OK) return st;
   return launch_decode(p, q, cache, block_table, max_blocks, seq_lens, batch, max_seq_len,
                        softmax_scale, out, ws, stream);
 }

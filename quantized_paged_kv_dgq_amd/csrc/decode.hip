@@ -824,13 +824,23 @@ dgq_status_t launch_append_decode(const dgq_params_t *p, const uint16_t *k_tok, 
   return check_launch("dgq_append_decode kernel");
 }
 
+static size_t workspace_bytes_for_parts(const dgq_params_t *p, int32_t batch, int32_t nparts) {
+  // completion counters, handed-over row counts, then (m, l) and the output of every partial
+  const size_t rows = (size_t)batch * p->num_q_heads * nparts;
+  return 2 * align_up((size_t)batch * p->num_kv_heads * sizeof(unsigned), 256) +
+         (align_up(rows * 2, 64) + rows * p->head_dim) * sizeof(float) + 256;
+}
+
 size_t decode_workspace_bytes(const dgq_params_t *p, int32_t batch, int32_t max_seq_len) {
   // one size for both decoders: the larger partial count of their two plans
   const int32_t nparts = std::max(decode_plan(p, batch, max_seq_len, kDgqDecodeWaves).nparts,
                                   decode_plan(p, batch, max_seq_len, kG64DecodeWaves).nparts);
-  const size_t rows = (size_t)batch * p->num_q_heads * nparts;
-  return 2 * align_up((size_t)batch * p->num_kv_heads * sizeof(unsigned), 256) +
-         (align_up(rows * 2, 64) + rows * p->head_dim) * sizeof(float) + 256;
+  return workspace_bytes_for_parts(p, batch, nparts);
+}
+
+size_t decode_workspace_bytes_for(const dgq_params_t *p, int32_t batch, int32_t max_seq_len,
+                                  int64_t target_waves) {
+  return workspace_bytes_for_parts(p, batch, decode_plan(p, batch, max_seq_len, target_waves).nparts);
 }
 
 }  // namespace dgq

@@ -67,6 +67,9 @@ constexpr int64_t kDgqDecodeWaves = 1024;
 constexpr int64_t kG64DecodeWaves = 2048;
 DecodePlan decode_plan(const dgq_params_t *p, int32_t batch, int32_t max_seq_len, int64_t target_waves);
 size_t decode_workspace_bytes(const dgq_params_t *p, int32_t batch, int32_t max_seq_len);
+// Workspace bytes one decoder's launch plan (target_waves) uses.
+size_t decode_workspace_bytes_for(const dgq_params_t *p, int32_t batch, int32_t max_seq_len,
+                                  int64_t target_waves);
 
 dgq_status_t launch_decode(const dgq_params_t *p, const uint16_t *q, const dgq_cache_t *cache,
                            const int32_t *block_table, int32_t max_blocks,

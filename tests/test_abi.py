@@ -250,3 +250,20 @@ def test_marker_format_checks(lib):
     pb = lib.dgq_swap_image_bytes(ctypes.byref(bitmap), 10)
     pm = lib.dgq_swap_image_bytes(ctypes.byref(marker), 10)
     assert pb - pm == 10 * 16          # 8 heads x 16 tokens / 8 = 16 bytes of bits per block
+
+
+def test_noalloc_decode_refuses_beyond_scratch(lib):
+    """The allocation-free decode refuses, on the host and before any HIP call, a batch whose
+    partials exceed its fixed scratch array (DGQ_NOALLOC_SCRATCH_BYTES)."""
+    p = _params(num_kv_heads=32, num_q_heads=32)
+    fake = ctypes.c_void_p(1 << 20)
+    big_batch = 4096                         # 4096 x 32 heads x (128 + 2) x 4 B > 16 MiB
+    cache = _lib.Cache(fake, fake, fake, fake, fake, fake, fake, fake, fake, 64, big_batch)
+    assert lib.paged_decode_attn_int8_noalloc(ctypes.byref(p), fake, ctypes.byref(cache), fake, 4, fake,
+                                              big_batch, 64, 0.1, fake, None) == _lib.DGQ_ERR_WORKSPACE_TOO_SMALL
+    # the usual argument checks come first
+    assert lib.paged_decode_attn_int8_noalloc(ctypes.byref(p), None, ctypes.byref(cache), fake, 4, fake,
+                                              1, 64, 0.1, fake, None) == _lib.DGQ_ERR_INVALID_ARG
+    assert lib.paged_decode_attn_int8_noalloc(ctypes.byref(p), fake, ctypes.byref(cache), fake, 4, fake,
+                                              1, 65, 0.1, fake, None) == _lib.DGQ_ERR_INVALID_ARG
+    assert _lib.DGQ_NOALLOC_SCRATCH_BYTES == 16 << 20
