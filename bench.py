@@ -1,34 +1,33 @@
 """Benchmark of the DGQ hot path on one MI355X.
 
-One step = one pass of the whole path over one batch of the Llama-3-8B-shaped layer workload
-(16 sequences x 8192 tokens, 8 KV / 32 query heads, head_dim 128, 16-token blocks shuffled in
-the pool):
+Headline workload: the 128K long context (one 131,072-token sequence, 32 layers looped on one
+GPU, 8 KV / 32 query heads, head_dim 128, 64-token blocks permuted in the pool, 1 % outliers at
+8 sigma).  The fp16 K/V of all 32 layers (16 GiB) are resident in HBM before the timed region.
+One step = one pass of the whole hot path over that input:
 
-  1. dgq_compress        the batch's fp16 K/V (16 x 8192 tokens) into INT8 DGQ blocks;
-  2. dgq_append          one fp16 token per sequence into that cache;
-  3. paged_decode_attn_int8  one decode query per sequence over a cache of 8193 tokens.
+  1. dgq_compress            every layer's 131,072-token prefix into its own INT8 DGQ cache;
+  2. dgq_append              one fp16 token into every layer's cache;
+  3. paged_decode_attn_int8  one decode query per layer over its 131,073 cached tokens.
 
-Four caches rotate: step i compresses and appends into cache i % 4 and decodes cache (i+2) % 4,
-which was written two steps earlier, so the decode's 256 MiB of codes are read from HBM and not
-from the 256 MB Infinity Cache.  Inputs are resident in HBM before the timed region.
+Each phase runs its 32 launches back to back.  A decode reads a cache written at least 31
+compressions (8 GiB of codes and 24 GiB of fp16 reads) earlier, so its codes come from HBM and
+not from the 256 MB Infinity Cache.  ``ms_per_step`` times K whole steps between one pair of HIP
+events with nothing recorded inside; the per-launch figures come from another K steps with one
+event pair around each phase (32 launches), so no event sits between two decodes.
 
-After the timed DGQ steps, the fixed 64-channel group INT8 baseline runs the same step shape on
-the same data (quantize the batch + the appended token, decode over 8193 tokens; two caches
-rotate), and both decoders' outputs are compared with float32 attention over the unquantized
-fp16 keys/values ("group64_baseline", "quality_vs_fp16").
+``value`` is the decode's throughput in GB/s of algorithmic bytes per launch (INT8 K/V codes +
+block table + segment rows + q + out) over its mean launch time; ``roofline`` compares it with
+the 8 TB/s HBM peak and carries the HBM bytes the committed counter profile measured.
 
-The segment-count policies (segment cap, tau, the length-aware cap, the variance floor) are then
-run on the same batch: segment histogram, compress time and error against fp16 attention
-("segment_policies"), and both storage formats of the segment identifier, the bit tensor and the
-marker bytes inside the codes, are compared on it ("identifier_formats").  The streaming workload (64 x 2048-token prefixes, 256 append + decode steps) is timed three
-ways: two launches per step, the fused append + decode, and the group-64 baseline ("streaming").
-Finally the 128K long-context workload (32 layers of one 131,072-token sequence, each layer
-compressed into its own cache, decode looped over the layers) is timed per layer
-("long_context_128k").
+Sections, each on its own data: the Llama-3-8B-shaped layer (16 x 8192 tokens, 16-token blocks;
+compress + append + decode with rotating caches, the group-64 baseline on the same data, error
+against fp16 attention, the segment-count policies and both identifier formats), the streaming
+workload (64 x 2048-token prefixes, 256 append + decode steps, three ways), the high-concurrency
+MHA batch and the tiny case.  ``cpu_baseline`` times the CPU oracle on the host cores: one core
+on a bounded sample of the headline workload, and every workload fanned out over the allowed
+cores (with the host's CPU model, affinity and thread settings).
 
-Prints one JSON line.  ``value`` is the decode attention's throughput in GB/s of algorithmic
-bytes (INT8 K/V codes + block table + segment tables + q + out), from HIP events recorded around
-every decode call on the stream the kernels run on.
+Prints one JSON line.
 """
 
 from __future__ import annotations
@@ -102,13 +101,13 @@ class Timer:
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--cpu-seconds", type=float, default=20.0,
-                    help="time budget of the CPU oracle baseline (0 to skip)")
-    ap.add_argument("--no-long-context", action="store_true",
-                    help="skip the streaming, high-concurrency, tiny and 32-layer 128K long-context figures")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="time budget of the one-core CPU oracle sample (0 skips the whole CPU baseline)")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="only the 128K long-context step (no Llama-layer, streaming, MHA or tiny sections)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 512 MiB device copy (torch) a few times: the reference "
                          "kernel of known size for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE")
@@ -139,17 +138,27 @@ def compress_source_digest() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(what: str = "decode"):
-    """HBM bytes per decode launch ("decode") or per dgq_compress call ("compress") from the
-    committed counter profile, if it was taken on the current kernel sources (else None)."""
-    path = os.path.join(ROOT, "profiles", "decode_llama3_8b_layer_hbm_traffic.txt")
-    if not os.path.exists(path):
-        return None
+def _profile_kv(name: str) -> dict:
+    """key: value lines of a committed profile summary (comments and indented lines skipped)."""
+    path = os.path.join(ROOT, "profiles", name)
     kv = {}
+    if not os.path.exists(path):
+        return kv
     for line in open(path):
-        if ":" in line and not line.startswith("#"):
+        if ":" in line and not line.startswith("#") and not line.startswith(" "):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.split("#", 1)[0].strip()
+    return kv
+
+
+HEADLINE_PROFILE = "decode_128k_layer_trace_and_traffic.txt"
+LLAMA_PROFILE = "decode_llama3_8b_layer_hbm_traffic.txt"
+
+
+def measured_traffic(what: str = "decode", profile: str = HEADLINE_PROFILE):
+    """HBM bytes per decode launch ("decode") or per dgq_compress call ("compress") from a
+    committed counter profile, if it was taken on the current kernel sources (else None)."""
+    kv = _profile_kv(profile)
     digest = kernel_source_digest() if what == "decode" else compress_source_digest()
     key = "decode_hbm_bytes_per_launch" if what == "decode" else "compress_hbm_bytes_per_call"
     if kv.get(f"{what}_source_sha256_16") != digest:
@@ -160,23 +169,14 @@ def measured_traffic(what: str = "decode"):
         return None
 
 
-def kernel_trace_decode_us():
-    """Kernel-trace average duration of the step's decode launches (the Llama-3-8B-shaped layer
-    decodes that follow the step's append) from the committed rocprofv3 summary, if it was taken
-    on the current decode sources (else None).  HIP events recorded around one kernel also count
-    the queue time the start event adds before the kernel (about 2-4 us here)."""
-    path = os.path.join(ROOT, "profiles", "llama3_8b_layer_step_kernel_trace.txt")
-    if not os.path.exists(path):
-        return None
-    kv = {}
-    for line in open(path):
-        if ":" in line and not line.startswith("#") and not line.startswith(" "):
-            k, v = line.split(":", 1)
-            kv[k.strip()] = v.split("#", 1)[0].strip()
+def kernel_trace_decode_us(profile: str = HEADLINE_PROFILE):
+    """Kernel-trace average duration of the headline decode launches from the committed rocprofv3
+    summary of the same bench command, if it was taken on the current decode sources (else None)."""
+    kv = _profile_kv(profile)
     if kv.get("decode_source_sha256_16") != kernel_source_digest():
         return None
     try:
-        return float(kv["decode_c2_step_avg_us"])
+        return float(kv["decode_avg_us"])
     except (KeyError, ValueError):
         return None
 
@@ -215,86 +215,189 @@ def achievable_copy(dev):
     return {"bytes": 2 * (512 << 20), "us": round(us, 2), "gbs": round(2 * (512 << 20) / us / 1e3, 1)}
 
 
-def cpu_baseline(cfg, seed, budget_s):
-    """The oracle as it is, on one host core, on a bounded sample of the same workload: whole
-    (sequence, kv head) units of config 2 until the budget is spent."""
-    from threadpoolctl import threadpool_limits
-
-    import dgq_data
-    from oracle import dgq_oracle as O
-
-    q16 = dgq_data.queries(cfg, seed)
-    units = [(b, h) for b in range(cfg.batch) for h in range(cfg.hkv)]
-    t_comp = t_dec = 0.0
-    done = 0
-    tokens = 0
-    with threadpool_limits(limits=1):
-        start = time.perf_counter()
-        for b, h in units:
-            k, v = dgq_data.head_kv(cfg, seed, 0, b, h, cfg.seq_len)
-            t0 = time.perf_counter()
-            hc = O.compress_head(k, v)
-            t1 = time.perf_counter()
-            O.decode_attention(q16[b, h * cfg.group:(h + 1) * cfg.group], hc.khat(), hc.vhat())
-            t2 = time.perf_counter()
-            t_comp += t1 - t0
-            t_dec += t2 - t1
-            done += 1
-            tokens += cfg.seq_len
-            if time.perf_counter() - start > budget_s and done >= 2:
+def host_info():
+    """The host the CPU baseline ran on: CPU model, core counts and thread settings."""
+    model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
                 break
-    dec_bytes = done * 2 * cfg.seq_len * cfg.head_dim
-    return {
-        "value": dec_bytes / t_dec / 1e9,
-        "unit": "GB/s",
-        "cores": 1,
-        "kind": "oracle",
-        "sample": f"{done} of {len(units)} (sequence, kv head) units of the {cfg.seq_len}-token layer; "
-                  f"decode = dequantize + float64 attention for the {cfg.group} query heads",
-        "compress_tokens_per_s": tokens / t_comp,
-        "seconds": t_comp + t_dec,
-        "all_cores": cpu_baseline_parallel(cfg, seed, units[:max(done, 1) * 4]),
-    }
+    except OSError:
+        pass
+    info = {"cpu_model": model, "os_cpu_count": os.cpu_count(),
+            "affinity_cores": len(os.sched_getaffinity(0)),
+            "env": {k: os.environ.get(k) for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS",
+                                                    "MKL_NUM_THREADS", "MAX_JOBS")}}
+    try:
+        from threadpoolctl import threadpool_info
+        info["blas_pools"] = [{"api": p.get("internal_api"), "threads": p.get("num_threads")}
+                              for p in threadpool_info()]
+    except Exception:  # pragma: no cover
+        pass
+    info["oracle_threads_per_process"] = 1
+    return info
 
 
-def _oracle_unit(args):
-    """One (sequence, kv head) unit through the oracle on one core: (compress s, decode s)."""
-    cid, seed, b, h = args
+def _oracle_unit(job):
+    """One (layer, sequence, kv head) of a workload through the oracle on one core (BLAS limited
+    to one thread): compress the prefix, then either one decode over it or ``steps`` rounds of
+    (append one token, decode over the cache).  Each timed part is the median of ``reps`` runs
+    (the data is drawn once, untimed)."""
+    cid, seed, layer, b, h, steps, reps, q = job
     from threadpoolctl import threadpool_limits
 
     import dgq_data
     from oracle import dgq_oracle as O
 
     cfg = dgq_data.get_config(cid)
-    q16 = dgq_data.queries(cfg, seed)
+    L = int(dgq_data.seq_lens(cfg, seed)[b])
+    d = cfg.head_dim
+    k, v = dgq_data.head_kv(cfg, seed, layer, b, h, L)
+    comp, dec, app = [], [], []
+    dbytes = 0
     with threadpool_limits(limits=1):
-        k, v = dgq_data.head_kv(cfg, seed, 0, b, h, cfg.seq_len)
-        t0 = time.perf_counter()
-        hc = O.compress_head(k, v)
-        t1 = time.perf_counter()
-        O.decode_attention(q16[b, h * cfg.group:(h + 1) * cfg.group], hc.khat(), hc.vhat())
-        t2 = time.perf_counter()
-    return t1 - t0, t2 - t1
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            hc = O.compress_head(k[:L], v[:L])
+            t1 = time.perf_counter()
+            comp.append(t1 - t0)
+            if steps == 0:
+                O.decode_attention(q, hc.khat(), hc.vhat())
+                dec.append(time.perf_counter() - t1)
+                app.append(0.0)
+                dbytes = 2 * L * d
+                continue
+            st = O.AppendState(hc, k[:L], cfg.block_size)
+            ta = td = 0.0
+            dbytes = 0
+            for s_ in range(steps):
+                a0 = time.perf_counter()
+                st.append(k[L + s_], v[L + s_])
+                a1 = time.perf_counter()
+                snap = st.snapshot()
+                O.decode_attention(q[s_], snap.khat(), snap.vhat())
+                a2 = time.perf_counter()
+                ta += a1 - a0
+                td += a2 - a1
+                dbytes += 2 * (L + s_ + 1) * d
+            app.append(ta)
+            dec.append(td)
+    return {"compress_s": float(np.median(comp)), "decode_s": float(np.median(dec)),
+            "append_s": float(np.median(app)), "tokens": L, "decode_bytes": dbytes, "appended": steps}
 
 
-def cpu_baseline_parallel(cfg, seed, units):
-    """The same oracle fanned out over (sequence, kv head) units, one process per allowed core
-    (at most 16): the units are independent.  Each process times its own compress and decode
-    while all of them run; throughput = bytes (tokens) / summed seconds x processes, i.e. the
-    rate of that many cores each busy with the oracle."""
+def _unit_jobs(cid, seed, units, steps=0, reps=1):
+    """Oracle jobs of (layer, sequence, kv head) units, with their query rows drawn up front."""
+    import dgq_data
+
+    cfg = dgq_data.get_config(cid)
+    g = cfg.group
+    qcache = {}
+    jobs = []
+    for layer, b, h in units:
+        if steps == 0:
+            if layer not in qcache:
+                qcache[layer] = dgq_data.queries(cfg, seed, layer)
+            q = qcache[layer][b, h * g:(h + 1) * g]
+        else:
+            for s_ in range(steps):
+                if (layer, s_) not in qcache:
+                    qcache[(layer, s_)] = dgq_data.queries(cfg, seed, layer, s_)
+            q = np.stack([qcache[(layer, s_)][b, h * g:(h + 1) * g] for s_ in range(steps)])
+        jobs.append((cid, seed, layer, b, h, steps, reps, q))
+    return jobs
+
+
+def _summarize(results, cores, wall, desc):
+    t_c = float(sum(r["compress_s"] for r in results))
+    t_d = float(sum(r["decode_s"] for r in results))
+    t_a = float(sum(r["append_s"] for r in results))
+    tok = float(sum(r["tokens"] for r in results))
+    db = float(sum(r["decode_bytes"] for r in results))
+    out = {"sample": desc, "units": len(results), "cores": cores,
+           "compress_tokens_per_s_per_core": round(tok / t_c, 1),
+           "decode_gbs_per_core": round(db / t_d / 1e9, 4),
+           "compress_tokens_per_s": round(tok / t_c * cores, 1),
+           "decode_gbs": round(db / t_d / 1e9 * cores, 4),
+           "oracle_core_seconds": round(t_c + t_d + t_a, 3), "wall_seconds": round(wall, 3)}
+    appended = float(sum(r["appended"] for r in results))
+    if appended:
+        out["append_tokens_per_s_per_core"] = round(appended / t_a, 1)
+    return out
+
+
+def _fan_out(pool, cores, jobs, desc):
+    t0 = time.perf_counter()
+    res = pool.map(_oracle_unit, jobs, chunksize=1)
+    return _summarize(res, cores, time.perf_counter() - t0, desc)
+
+
+def cpu_baseline(seed, budget_s):
+    """The oracle as it is, on the host cores (run before the GPU is touched: the fan-out forks).
+
+    * ``value``: one core (BLAS limited to one thread) on a bounded sample of the headline
+      workload, whole (layer, kv head) units of the 131,072-token sequence until ``budget_s`` is
+      spent; decode GB/s of codes (the metric's unit) and compress tokens/s.
+    * ``per_workload``: every workload fanned out over (layer, sequence, kv head) units, one
+      process per allowed core (at most 16), each process timing its own units: the tiny case,
+      the Llama-3-8B-shaped layer and the 100-sequence MHA batch whole (each part the median of 3
+      runs per unit), 8 of the 128K long context's 32 layers (8 heads each, one run; the 32-layer
+      time is the per-layer mean x 32), and the streaming workload on one kv head per sequence
+      (64 of 512 units, all 256 append + decode steps).  Rates are per core times the process
+      count."""
     import multiprocessing as mp
 
+    import dgq_data
+
+    cfg3 = dgq_data.get_config(3)
+    units3 = [(layer, 0, h) for layer in range(cfg3.layers) for h in range(cfg3.hkv)]
+    jobs3 = _unit_jobs(3, seed, units3)
+    res1 = []
+    start = time.perf_counter()
+    for job in jobs3:
+        res1.append(_oracle_unit(job))
+        if time.perf_counter() - start > budget_s:
+            break
+    one = _summarize(res1, 1, time.perf_counter() - start,
+                     f"{len(res1)} of {len(units3)} (layer, kv head) units of the 131,072-token sequence "
+                     "(compress + dequantize and float64 attention for the 4 query heads)")
     cores = max(1, min(16, len(os.sched_getaffinity(0))))
-    args = [(cfg.cid, seed, b, h) for b, h in units]
-    t0 = time.perf_counter()
+    per = {}
     with mp.get_context("fork").Pool(cores) as pool:
-        times = pool.map(_oracle_unit, args, chunksize=1)
-    wall = time.perf_counter() - t0
-    t_comp = float(sum(a for a, _ in times))
-    t_dec = float(sum(b for _, b in times))
-    dec_bytes = len(units) * 2 * cfg.seq_len * cfg.head_dim
-    return {"value": dec_bytes / t_dec * cores / 1e9, "unit": "GB/s", "cores": cores, "units": len(units),
-            "compress_tokens_per_s": len(units) * cfg.seq_len / t_comp * cores, "wall_seconds": wall}
+        c1 = dgq_data.get_config(1)
+        per["tiny"] = _fan_out(pool, cores, _unit_jobs(1, seed, [(0, 0, h) for h in range(c1.hkv)], reps=3),
+                               "all 2 heads, median of 3 runs")
+        c2 = dgq_data.get_config(2)
+        per["llama3_8b_layer"] = _fan_out(
+            pool, cores, _unit_jobs(2, seed, [(0, b, h) for b in range(c2.batch) for h in range(c2.hkv)], reps=3),
+            "all 128 (sequence, kv head) units, median of 3 runs each")
+        c4 = dgq_data.get_config(4)
+        per["high_concurrency_mha"] = _fan_out(
+            pool, cores, _unit_jobs(4, seed, [(0, b, h) for b in range(c4.batch) for h in range(c4.hkv)], reps=3),
+            "all 3200 (sequence, head) units, median of 3 runs each")
+        lc = _fan_out(pool, cores, jobs3[:8 * cfg3.hkv],
+                      "8 of the 32 layers x 8 kv heads, one run each; the 32-layer figure scales the "
+                      "per-layer mean by 32 (the layers are drawn alike)")
+        lc["oracle_core_seconds_32_layers"] = round(lc["oracle_core_seconds"] * cfg3.layers / 8, 3)
+        per["long_context_128k"] = lc
+        c5 = dgq_data.get_config(5)
+        per["streaming"] = _fan_out(
+            pool, cores, _unit_jobs(5, seed, [(0, b, b % c5.hkv) for b in range(c5.batch)], steps=c5.append_steps),
+            "64 of 512 units (kv head b % 8 of sequence b): 2048-token prefix compress, then 256 x (append, decode)")
+    lc = per["long_context_128k"]
+    return {
+        "value": one["decode_gbs_per_core"],
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": one["sample"],
+        "compress_tokens_per_s": one["compress_tokens_per_s_per_core"],
+        "seconds": one["oracle_core_seconds"],
+        "long_context_32_layers_core_seconds": lc["oracle_core_seconds_32_layers"],
+        "per_workload": per,
+        "host": host_info(),
+    }
 
 
 def fp16_reference(cfg, k, v, cu, q, k_tok=None, v_tok=None):
@@ -628,67 +731,6 @@ def tiny(seed, dev, Q):
             "dgq_max_rel_err_vs_fp16": r["dgq_max_rel_err_vs_fp16"]}
 
 
-def long_context(seed, dev, Q):
-    """The 128K long-context workload: 32 layers of one 131,072-token sequence (8 KV / 32 query
-    heads, head_dim 128, 64-token blocks, 1% outliers at 8 sigma), each layer compressed into its
-    own cache, then one decode query per layer, looped over the layers.  8 GiB of codes in all, so
-    every layer's decode reads HBM.  Compress: median of per-layer HIP-event times; decode: median
-    over three passes of the 32 layers (one event pair per pass) divided by 32."""
-    import torch
-
-    import dgq_data
-
-    cfg = dgq_data.get_config(3)
-    L, hkv, hq, d, bs = cfg.seq_len, cfg.hkv, cfg.hq, cfg.head_dim, cfg.block_size
-    params = Q.DGQParams(hkv, hq, d, bs)
-    table, nblk = dgq_data.block_tables(cfg, seed)
-    dtable = torch.from_numpy(table).to(dev)
-    caches = [Q.DGQCache(params, nblk, 1, dev) for _ in range(cfg.layers)]
-    ws_c = Q.workspace(Q.compress_workspace_size(params, 1, L, L), dev)
-    ws_d = Q.workspace(Q.decode_workspace_size(params, 1, L), dev)
-    comp_ms = []
-    for layer in range(cfg.layers):
-        k, v, cu, _ = dgq_data.batch_kv_device(cfg, seed, layer, dev)
-        dcu = cu.to(dev)
-        e0, e1 = Timer(), Timer()
-        e0.record()
-        Q.dgq_compress(params, k, v, dcu, dtable, caches[layer], L, L, ws=ws_c)
-        e1.record()
-        comp_ms.append((e0, e1))
-        del k, v
-    qs = [torch.from_numpy(dgq_data.queries(cfg, seed, layer)).to(dev) for layer in range(cfg.layers)]
-    lens = torch.full((1,), L, dtype=torch.int32, device=dev)
-    out = torch.empty((1, hq, d), dtype=torch.float32, device=dev)
-    # one pass = the 32 layers' decodes back to back between one pair of events (an event between
-    # two kernels adds several microseconds of queue time to the interval it opens); the first
-    # pass is untimed
-    dec = []
-    for rep in range(4):
-        e0, e1 = Timer(), Timer()
-        e0.record()
-        for layer in range(cfg.layers):
-            Q.paged_decode_attn_int8(params, qs[layer], caches[layer], dtable, lens, L, out=out, ws=ws_d)
-        e1.record()
-        if rep > 0:
-            dec.append((e0, e1))
-    torch.cuda.synchronize()
-    c_us = float(np.median([a.elapsed_time(b) for a, b in comp_ms])) * 1e3
-    d_us = float(np.median([a.elapsed_time(b) for a, b in dec])) * 1e3 / cfg.layers
-    nseg = torch.stack([c.nseg for c in caches]).cpu().numpy()
-    dec_bytes = (2 * L * hkv * d + math.ceil(L / bs) * 4 + float(nseg.mean()) * hkv * 32 + hq * d * 2 + hq * d * 4)
-    return {
-        "workload": "128K long context: 1 seq x 131072 tokens, 32 layers looped, 8 KV / 32 q heads, "
-                    "head_dim 128, 64-token blocks, 1% outliers at 8 sigma",
-        "decode_us_per_layer": round(d_us, 2),
-        "decode_gbs_alg": round(dec_bytes / d_us / 1e3, 1),
-        "decode_frac_hbm_peak": round(dec_bytes / d_us / 1e3 / HBM_PEAK_GBS, 4),
-        "compress_us_per_layer": round(c_us, 2),
-        "compress_tokens_per_s": round(L / (c_us / 1e6), 1),
-        "segments_per_head_hist": np.bincount(nseg.reshape(-1), minlength=6).tolist(),
-        **kv_memory(cfg, caches[0]),
-    }
-
-
 def kv_memory(cfg, cache):
     """KV-cache bytes of all layers of the sequence: fp16 K and V against the DGQ layout (codes,
     identifier bits and segment-table rows at their allocated capacity)."""
@@ -699,27 +741,166 @@ def kv_memory(cfg, cache):
             "compression_vs_fp16": round(fp16 / (per_layer * cfg.layers), 4)}
 
 
-def main():
-    args = parse()
-    if args.copy_calibration:
-        copy_calibration()
-        return
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the library has no "
-              "multi-GPU path", file=sys.stderr)
-        sys.exit(2)
+def long_context_step(args, dev, Q):
+    """The headline: the 128K long-context workload, one step = compress all 32 layers, append one
+    token to every layer, decode every layer (see the module text)."""
+    import torch
+
+    import dgq_data
+
+    cfg = dgq_data.get_config(3)
+    L, hkv, hq, d, bs, nl = cfg.seq_len, cfg.hkv, cfg.hq, cfg.head_dim, cfg.block_size, cfg.layers
+    params = Q.DGQParams(hkv, hq, d, bs)
+    table, nblk = dgq_data.block_tables(cfg, args.seed, lens_total=np.array([L + 1]))
+    dtable = torch.from_numpy(table).to(dev)
+    kv = []
+    for layer in range(nl):
+        k, v, cu, _ = dgq_data.batch_kv_device(cfg, args.seed, layer, dev)
+        kv.append((k, v))
+    dcu = cu.to(dev)
+    caches = [Q.DGQCache(params, nblk, 1, dev) for _ in range(nl)]
+    ws_c = Q.workspace(Q.compress_workspace_size(params, 1, L, L), dev)
+    ws_d = Q.workspace(Q.decode_workspace_size(params, 1, L + 1), dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(args.seed + 23)
+    toks = [((torch.randn((1, hkv, d), generator=gen, device=dev) * 0.2).half(),
+             (torch.randn((1, hkv, d), generator=gen, device=dev) * 0.2).half()) for _ in range(nl)]
+    qs = [torch.from_numpy(dgq_data.queries(cfg, args.seed, layer)).to(dev) for layer in range(nl)]
+    pos = torch.full((1,), L, dtype=torch.int32, device=dev)
+    dec_lens = torch.full((1,), L + 1, dtype=torch.int32, device=dev)
+    outs = [torch.empty((1, hq, d), dtype=torch.float32, device=dev) for _ in range(nl)]
+
+    def compress_all():
+        for layer in range(nl):
+            Q.dgq_compress(params, kv[layer][0], kv[layer][1], dcu, dtable, caches[layer], L, L, ws=ws_c)
+
+    def append_all():
+        for layer in range(nl):
+            Q.dgq_append(params, toks[layer][0], toks[layer][1], pos, dtable, caches[layer])
+
+    def decode_all():
+        for layer in range(nl):
+            Q.paged_decode_attn_int8(params, qs[layer], caches[layer], dtable, dec_lens, L + 1,
+                                     out=outs[layer], ws=ws_d)
+
+    for _ in range(args.warmup):
+        compress_all()
+        append_all()
+        decode_all()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    # the timed region: K whole steps between one pair of events
+    t_start, t_end = Timer(), Timer()
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record()
+    for _ in range(K):
+        compress_all()
+        append_all()
+        decode_all()
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t_start.elapsed_time(t_end)
+
+    # per-phase times: another K steps, one event pair around each phase of 32 launches
+    ev = [[Timer() for _ in range(4)] for _ in range(K)]
+    for i in range(K):
+        e = ev[i]
+        e[0].record()
+        compress_all()
+        e[1].record()
+        append_all()
+        e[2].record()
+        decode_all()
+        e[3].record()
+    torch.cuda.synchronize()
+    comp_s = float(np.mean([e[0].elapsed_time(e[1]) for e in ev])) / 1e3 / nl
+    app_s = float(np.mean([e[1].elapsed_time(e[2]) for e in ev])) / 1e3 / nl
+    dec_s = float(np.mean([e[2].elapsed_time(e[3]) for e in ev])) / 1e3 / nl
+
+    nseg = torch.stack([c.nseg for c in caches]).cpu().numpy()
+    Ld = L + 1
+    dec_bytes = (2 * Ld * hkv * d + math.ceil(Ld / bs) * 4 + float(nseg.mean()) * hkv * 32
+                 + hq * d * 2 + hq * d * 4)
+    comp_bytes = L * hkv * d * 2 * 3 + L * hkv / 8 + float(nseg.mean()) * hkv * 32
+    dec_gbs = dec_bytes / dec_s / 1e9
+    comp_gbs = comp_bytes / comp_s / 1e9
+    # error of the last decode of every layer against float32 attention over the unquantized fp16 K/V
+    errs = []
+    for layer in range(nl):
+        k, v = kv[layer]
+        kk = torch.cat([k, toks[layer][0]])
+        vv = torch.cat([v, toks[layer][1]])
+        ref = fp16_reference(cfg, kk, vv, np.array([0, Ld]), qs[layer])
+        errs.append(rel_err_rows(outs[layer], ref))
+    kt_us = kernel_trace_decode_us()
+    copy = achievable_copy(dev)
+    rec = {
+        "value": round(dec_gbs, 1),
+        "unit": "GB/s",
+        "ms_per_step": round(total_ms / K, 4),
+        "config": {
+            "workload": "128K long context: 1 seq x 131072 tokens, 32 layers looped on one GPU, 8 KV / 32 q heads, "
+                        "head_dim 128, 64-token blocks permuted, 1% outliers at 8 sigma; step = compress all 32 "
+                        "layers + append 1 token per layer + decode 1 query per layer over 131073 tokens",
+            "global_batch": 1, "seq_len": L, "layers": nl, "block_size": bs, "kv_heads": hkv, "q_heads": hq,
+            "head_dim": d,
+        },
+        "decode_frac_hbm_peak": round(dec_gbs / HBM_PEAK_GBS, 4),
+        "decode_us_per_layer": round(dec_s * 1e6, 2),
+        "decode_kv_tokens_per_s": round(Ld / dec_s, 1),
+        "compress_us_per_layer": round(comp_s * 1e6, 2),
+        "compress_tokens_per_s": round(L / comp_s, 1),
+        "compress_gbs_alg": round(comp_gbs, 1),
+        "append_us_per_layer": round(app_s * 1e6, 2),
+        "step_tokens_per_s": round(nl * L / (total_ms / K / 1e3), 1),
+        "segments_per_head_hist": np.bincount(nseg.reshape(-1), minlength=6).tolist(),
+        "dgq_max_rel_err_vs_fp16": round(max(e[0] for e in errs), 6),
+        "dgq_mean_rel_err_vs_fp16": round(float(np.mean([e[1] for e in errs])), 6),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(dec_gbs, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
+            "traffic": measured_traffic(),
+            "algorithmic_bytes_per_launch": int(dec_bytes),
+            "launch_us": round(dec_s * 1e6, 2),
+            "frac_of_measured_copy": round(dec_gbs / copy["gbs"], 4),
+            "measured_copy": copy,
+            "kernel": "decode_partition_kernel<128,4,64> (one launch per paged_decode_attn_int8 call, 32 x 8 x 1 "
+                      "workgroups; HIP events around the 32 back-to-back decodes of a step on their stream)",
+            "kernel_trace_avg_us": kt_us,
+            "kernel_trace_frac": round(dec_bytes / (kt_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4) if kt_us else None,
+        },
+        "roofline_compress": {
+            "bound": "hbm", "achieved": round(comp_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(comp_gbs / HBM_PEAK_GBS, 4),
+            "traffic": measured_traffic("compress"),
+            "kernel": "dgq_compress per layer (stats + scores + select + encode; HIP events around the 32 "
+                      "compresses of a step)",
+        },
+        "wall_s_timed": round(wall, 4),
+        **kv_memory(cfg, caches[0]),
+    }
+    del kv, caches, ws_c, ws_d
+    return rec
+
+
+def llama_layer(args, dev, Q):
+    """The Llama-3-8B-shaped layer: 16 sequences x 8192 tokens, 8 KV / 32 query heads, head_dim 128,
+    16-token blocks shuffled.  Step = compress the batch + append one token per sequence + decode
+    one query per sequence over 8193 tokens; four caches rotate (step i compresses and appends
+    into cache i % 4 and decodes cache (i + 2) % 4, written two steps earlier).  Also the group-64
+    baseline on the same data, the error of both against fp16 attention, the segment-count
+    policies and the two identifier formats."""
+    import torch
 
     import dgq_data
 
     cfg = dgq_data.get_config(2)
-    cpu = cpu_baseline(cfg, args.seed, args.cpu_seconds) if args.cpu_seconds > 0 else None
-
-    import torch
-
-    import quantized_paged_kv_dgq_amd as Q
-
-    torch.cuda.set_device(0)
-    dev = torch.device("cuda")
     B, L, hkv, hq, d, bs = cfg.batch, cfg.seq_len, cfg.hkv, cfg.hq, cfg.head_dim, cfg.block_size
     k, v, cu, lens = dgq_data.batch_kv_device(cfg, args.seed, 0, dev)
     total = int(cu[-1])
@@ -749,7 +930,6 @@ def main():
     def decode(i):
         Q.paged_decode_attn_int8(params, q, caches[(i + 2) % ncache], dtable, dec_lens, L + 1, out=out, ws=ws_d)
 
-    # fill every cache once (untimed), then warm up
     for i in range(ncache):
         compress(i)
         append(i)
@@ -758,15 +938,8 @@ def main():
         append(i)
         decode(i)
     torch.cuda.synchronize()
-
     K = args.steps
-
-    # The timed region: K whole steps between one pair of events, nothing recorded inside (an
-    # event between two kernels adds queue time on some boxes); then the per-call times from events
-    # recorded around each call, over another K steps.
     t_start, t_end = Timer(), Timer()
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
     t_start.record()
     for i in range(K):
         compress(i)
@@ -774,12 +947,8 @@ def main():
         decode(i)
     t_end.record()
     torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
     total_ms = t_start.elapsed_time(t_end)
-
-    # per-call times from events recorded around each call
     ev = [[Timer() for _ in range(4)] for _ in range(K)]
-    torch.cuda.synchronize()
     for i in range(K):
         e = ev[i]
         e[0].record()
@@ -794,8 +963,6 @@ def main():
     app_ms = np.array([e[1].elapsed_time(e[2]) for e in ev])
     dec_ms = np.array([e[2].elapsed_time(e[3]) for e in ev])
 
-    # the group-64 baseline on the same data, same step shape: quantize the batch, quantize the
-    # appended token, decode over 8193 tokens; two caches rotate so the decoded one is cold
     g_caches = [Q.DGQG64Cache(params, nblk, dev) for _ in range(2)]
     one = torch.arange(B + 1, dtype=torch.int32, device=dev)
     out_g = torch.empty_like(out)
@@ -824,75 +991,39 @@ def main():
     gq_ms = np.array([e[0].elapsed_time(e[1]) for e in gev])
     gd_ms = np.array([e[1].elapsed_time(e[2]) for e in gev])
     quality = quality_vs_fp16(cfg, k, v, cu, k_tok, v_tok, q, out, out_g)
-    copy = achievable_copy(dev)
     policies = segment_policies(cfg, k, v, cu, dcu, dtable, nblk, q, dev, Q)
     formats = marker_format(cfg, k, v, cu, dcu, dtable, nblk, q, dev, Q)
 
-    # algorithmic bytes
     Ld = L + 1
     nseg = torch.stack([c.nseg for c in caches]).cpu().numpy()
     seg_rows = float(nseg.mean()) * B * hkv
     dec_bytes = (B * 2 * Ld * hkv * d + B * math.ceil(Ld / bs) * 4 + seg_rows * 32
                  + B * hq * d * 2 + B * hq * d * 4)
-    comp_elems = total * hkv * d * 2
-    comp_bytes = comp_elems * 3 + total * hkv / 8 + seg_rows * 32
+    comp_bytes = total * hkv * d * 2 * 3 + total * hkv / 8 + seg_rows * 32
     dec_s = float(np.mean(dec_ms)) / 1e3
     comp_s = float(np.mean(comp_ms)) / 1e3
     dec_gbs = dec_bytes / dec_s / 1e9
     comp_gbs = comp_bytes / comp_s / 1e9
-    hist = np.bincount(nseg.reshape(-1), minlength=6).tolist()
     g_dec_s = float(np.mean(gd_ms)) / 1e3
     g_dec_bytes = (B * 2 * Ld * hkv * d + B * Ld * hkv * (d // 64) * 4 * 2 + B * math.ceil(Ld / bs) * 4
                    + B * hq * d * 2 + B * hq * d * 4)
-
-    kt_us = kernel_trace_decode_us()
     rec = {
-        "metric": "INT8 paged decode-attn GB/s (% HBM peak) + dgq_compress tokens/s",
-        "value": round(dec_gbs, 1),
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": K,
-        "warmup": args.warmup,
+        "workload": "Llama-3-8B-shaped layer: 16 seqs x 8192 tokens, 8 KV / 32 q heads, head_dim 128, 16-token "
+                    "blocks shuffled; step = compress + append 1 token + decode 1 query, four caches rotating",
         "ms_per_step": round(total_ms / K, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "i8",
-        "data": "synthetic",
-        "config": {
-            "workload": "Llama-3-8B-shaped layer: 16 seqs x 8192 tokens, 8 KV / 32 q heads, head_dim 128, "
-                        "16-token blocks shuffled; step = compress + append 1 token + decode 1 query",
-            "global_batch": B, "seq_len": L, "block_size": bs, "kv_heads": hkv, "q_heads": hq, "head_dim": d,
-        },
-        "decode_frac_hbm_peak": round(dec_gbs / HBM_PEAK_GBS, 4),
         "decode_us": round(dec_s * 1e6, 2),
+        "decode_gbs_alg": round(dec_gbs, 1),
+        "decode_frac_hbm_peak": round(dec_gbs / HBM_PEAK_GBS, 4),
         "decode_kv_tokens_per_s": round(B * Ld / dec_s, 1),
+        "decode_bytes": int(dec_bytes),
+        "decode_traffic": measured_traffic(profile=LLAMA_PROFILE),
+        "compress_us": round(comp_s * 1e6, 2),
         "compress_tokens_per_s": round(total / comp_s, 1),
         "compress_gbs_alg": round(comp_gbs, 1),
-        "compress_us": round(comp_s * 1e6, 2),
+        "compress_frac_hbm_peak": round(comp_gbs / HBM_PEAK_GBS, 4),
+        "compress_traffic": measured_traffic("compress", profile=LLAMA_PROFILE),
         "append_us": round(float(np.mean(app_ms)) * 1e3, 2),
-        "segments_per_head_hist": hist,
-        "roofline": {
-            "bound": "hbm",
-            "achieved": round(dec_gbs, 1),
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
-            "frac_of_measured_copy": round(dec_gbs / copy["gbs"], 4),
-            "measured_copy": copy,
-            "traffic": measured_traffic(),
-            "kernel": "decode_partition_kernel<128,4,16> (one launch per paged_decode_attn_int8 call; "
-                      "HIP events around the call on its stream)",
-            "kernel_trace_avg_us": kt_us,
-            "kernel_trace_frac": round(dec_bytes / (kt_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4) if kt_us else None,
-        },
-        "roofline_compress": {
-            "bound": "hbm", "achieved": round(comp_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(comp_gbs / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic("compress"),
-            "kernel": "dgq_compress (stats + scores + select + encode, HIP events around the call)",
-        },
-        "wall_s_timed": round(wall, 4),
+        "segments_per_head_hist": np.bincount(nseg.reshape(-1), minlength=6).tolist(),
         "group64_baseline": {
             "decode_us": round(g_dec_s * 1e6, 2),
             "decode_gbs_alg": round(g_dec_bytes / g_dec_s / 1e9, 1),
@@ -900,23 +1031,61 @@ def main():
             "quantize_us": round(float(np.mean(gq_ms)) * 1e3, 2),
             "quantize_tokens_per_s": round((total + B) / (float(np.mean(gq_ms)) / 1e3), 1),
             "decode_bytes": int(g_dec_bytes),
-            "dgq_decode_bytes": int(dec_bytes),
             "dgq_decode_speedup": round(g_dec_s / dec_s, 4),
         },
         "quality_vs_fp16": quality,
         "segment_policies": policies,
         "identifier_formats": formats,
     }
-    if not args.no_long_context:
-        del caches, g_caches, k, v, ws_c
+    del caches, g_caches, k, v, ws_c, ws_d
+    return rec
+
+
+def main():
+    args = parse()
+    if args.copy_calibration:
+        copy_calibration()
+        return
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the library has no "
+              "multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+
+    # the CPU oracle first: its fan-out forks, which must happen before the GPU is touched
+    cpu = cpu_baseline(args.seed, args.cpu_seconds) if args.cpu_seconds > 0 else None
+
+    import torch
+
+    import quantized_paged_kv_dgq_amd as Q
+
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda")
+    head = long_context_step(args, dev, Q)
+    torch.cuda.empty_cache()
+    rec = {
+        "metric": "INT8 paged decode-attn GB/s (% HBM peak) + dgq_compress tokens/s",
+        "value": head.pop("value"),
+        "unit": head.pop("unit"),
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head.pop("ms_per_step"),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i8",
+        "data": "synthetic",
+        "config": head.pop("config"),
+    }
+    rec.update(head)
+    if not args.headline_only:
+        rec["llama3_8b_layer"] = llama_layer(args, dev, Q)
         torch.cuda.empty_cache()
         rec["streaming"] = streaming(args.seed, dev, Q)
         torch.cuda.empty_cache()
         rec["high_concurrency_mha"] = high_concurrency(args.seed, dev, Q)
         torch.cuda.empty_cache()
         rec["tiny"] = tiny(args.seed, dev, Q)
-        torch.cuda.empty_cache()
-        rec["long_context_128k"] = long_context(args.seed, dev, Q)
     if cpu is not None:
         rec["cpu_baseline"] = cpu
     print(json.dumps(rec))
