@@ -94,7 +94,12 @@ enum {
   DGQ_POLICY_LENGTH_AWARE = 1u,
   /* Marker format (see the layout notes above) instead of the bit tensor.  A cache must be
    * written and read with the same format. */
-  DGQ_FORMAT_MARKER = 2u
+  DGQ_FORMAT_MARKER = 2u,
+  /* dgq_compress only: run the separate stats / selection / encode launches even where the
+   * one-launch path for short sequences (at most 256 tokens at head_dim 128, 512 at 64) applies.
+   * Both paths write bit-identical results; the flag is for comparing them.  Other calls ignore
+   * it. */
+  DGQ_COMPRESS_MULTIPASS = 4u
 };
 
 /* Shape and method parameters, passed to every call (48 bytes).  Defaults: win 16,
@@ -107,7 +112,8 @@ typedef struct dgq_params {
   int32_t win;           /* sliding-window length of the variance curve; must be 16 (DGQ 2.2) */
   int32_t max_segments;  /* 1..8 segments per (sequence, kv head) from dgq_compress */
   int32_t seg_capacity;  /* segment-table rows per (sequence, kv head): max_segments..64 */
-  uint32_t flags;        /* DGQ_POLICY_LENGTH_AWARE | DGQ_FORMAT_MARKER; other bits must be 0 */
+  uint32_t flags;        /* DGQ_POLICY_LENGTH_AWARE | DGQ_FORMAT_MARKER | DGQ_COMPRESS_MULTIPASS;
+                            other bits must be 0 */
   double tau;            /* change-point threshold on the window-variance ratio, finite, >= 1 */
   double min_var;        /* variance floor, finite, >= 0 (0 = off): a candidate cut whose two
                             16-token windows both have a population variance below it is not a

@@ -83,6 +83,7 @@ class Cache(ctypes.Structure):
 
 DGQ_POLICY_LENGTH_AWARE = 1
 DGQ_FORMAT_MARKER = 2
+DGQ_COMPRESS_MULTIPASS = 4
 DGQ_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 assert ctypes.sizeof(Params) == 48

@@ -15,7 +15,8 @@ from typing import Optional, Sequence
 import torch
 
 from . import _lib
-from ._lib import DGQ_FORMAT_MARKER, DGQ_POLICY_LENGTH_AWARE, Cache, G64Cache, Params, check
+from ._lib import (DGQ_COMPRESS_MULTIPASS, DGQ_FORMAT_MARKER, DGQ_POLICY_LENGTH_AWARE, Cache, G64Cache, Params,
+                   check)
 
 
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
@@ -36,12 +37,15 @@ class DGQParams:
     """dgq_params_t: shapes and method constants (window 16; segments 2..max_segments; tau), plus
     the segment-count policies: ``length_aware`` (cap by sequence length) and ``min_var``
     (variance floor below which a window pair is not a change point), and the identifier format:
-    ``marker`` keeps it in the codes (no bit tensor) instead of the bit tensor."""
+    ``marker`` keeps it in the codes (no bit tensor) instead of the bit tensor.  ``multipass``
+    makes dgq_compress use its separate launches also for short sequences (same results)."""
 
     def __init__(self, num_kv_heads: int, num_q_heads: int, head_dim: int, block_size: int,
                  max_segments: int = 5, seg_capacity: int = 16, tau: float = 2.0, win: int = 16,
-                 length_aware: bool = False, min_var: float = 0.0, marker: bool = False):
-        flags = (DGQ_POLICY_LENGTH_AWARE if length_aware else 0) | (DGQ_FORMAT_MARKER if marker else 0)
+                 length_aware: bool = False, min_var: float = 0.0, marker: bool = False,
+                 multipass: bool = False):
+        flags = ((DGQ_POLICY_LENGTH_AWARE if length_aware else 0) | (DGQ_FORMAT_MARKER if marker else 0)
+                 | (DGQ_COMPRESS_MULTIPASS if multipass else 0))
         self.c = Params(num_kv_heads, num_q_heads, head_dim, block_size, win, max_segments,
                         seg_capacity, flags, float(tau), float(min_var))
 
@@ -59,6 +63,10 @@ class DGQParams:
     @property
     def marker(self) -> bool:
         return bool(self.c.flags & DGQ_FORMAT_MARKER)
+
+    @property
+    def multipass(self) -> bool:
+        return bool(self.c.flags & DGQ_COMPRESS_MULTIPASS)
 
 
 class DGQCache:

@@ -34,7 +34,8 @@ static dgq_status_t check_params(const dgq_params_t *p) {
   if (p->win != kWin) return DGQ_ERR_UNSUPPORTED;
   if (p->max_segments < 1 || p->max_segments > kMaxCuts + 1) return DGQ_ERR_INVALID_ARG;
   if (p->seg_capacity < p->max_segments || p->seg_capacity > kMaxSegCap) return DGQ_ERR_INVALID_ARG;
-  if ((p->flags & ~(uint32_t)(DGQ_POLICY_LENGTH_AWARE | DGQ_FORMAT_MARKER)) != 0) return DGQ_ERR_INVALID_ARG;
+  if ((p->flags & ~(uint32_t)(DGQ_POLICY_LENGTH_AWARE | DGQ_FORMAT_MARKER | DGQ_COMPRESS_MULTIPASS)) != 0)
+    return DGQ_ERR_INVALID_ARG;
   if (!std::isfinite(p->tau) || p->tau < 1.0) return DGQ_ERR_INVALID_ARG;
   if (!std::isfinite(p->min_var) || p->min_var < 0.0) return DGQ_ERR_INVALID_ARG;
   return DGQ_OK;

@@ -14,6 +14,9 @@
 //  4. encode  -- second read of fp16 K/V; writes INT8 codes into the paged pool in the tile order
 //                of the decode kernel (values through LDS, since their tiles are channel-major),
 //                and the boundary bits.
+//
+// Sequences of at most 256 tokens (head_dim 128) or 512 (head_dim 64) take one launch instead,
+// one workgroup per (sequence, kv head) doing all four steps on one read of the input.
 #include <climits>
 #include <type_traits>
 #include <cmath>
@@ -34,6 +37,7 @@ struct CompressArgs {
   double tau;
   double qfloor;        // variance floor on the Q scale (0 = off)
   int32_t length_aware; // DGQ_POLICY_LENGTH_AWARE: per-sequence segment cap
+  int32_t multipass;    // DGQ_COMPRESS_MULTIPASS: no one-launch path for short sequences
   CodeFormat fmt;
   // workspace
   int32_t *ws_a;        // [hkv][total]
@@ -1053,6 +1057,408 @@ __global__ __launch_bounds__(256) void encode_kernel(CompressArgs a) {
   }
 }
 
+// -------------------------------------------------------------------------------------------
+// one launch for short sequences: stats, scores, selection and encode of one (sequence, kv head)
+// in one workgroup, for sequences whose fp16 values fit in LDS (L * head_dim <= kShortElems)
+// -------------------------------------------------------------------------------------------
+// The four passes above cost four launches and a round trip of the moments through the
+// workspace; for a short sequence that is most of the time.  Here 1024 threads read the
+// sequence's fp16 K and V once (lanes_per_token lanes per token, 32 channels per lane), keep the
+// keys in registers and the values in LDS, and compute the same quantities in the same
+// precision: exact integer moments, the window statistic as an exact double, the greedy cuts
+// with the same tie rule, min/max folds (order-free once -0 is stored as +0), the same encoding
+// steps and the same tile layout.  The results are bit-identical to the four-pass path.
+// One workgroup does all of a head's element work on one compute unit, so the per-element
+// arithmetic is kept short: packed fp16 min/max and non-finite tests, the fixed-point image by
+// one fused multiply-add into the round-to-integer range of float32, 24-bit integer squares, and
+// the hardware float-to-byte conversion for the codes.
+constexpr int kShortThreads = 1024;
+constexpr int kShortElems = 32768;   // longest sequence * head_dim: 256 tokens at 128, 512 at 64
+template <int D>
+constexpr int short_tokens() { return kShortElems / D; }
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ half2_t as_half2(uint32_t w) { return __builtin_bit_cast(half2_t, w); }
+
+// dgq_fixed_point(x) for every x: the clamped value times 512 is exact, and adding 1.5 * 2^23
+// rounds it to the nearest integer (ties to even) in one step, that integer then being the low
+// bits of the sum (|x * 512| <= 2^14 < 2^22).
+__device__ __forceinline__ int fixed_point_fma(float x) {
+  const float c = fminf(fmaxf(x, -32.0f), 32.0f);
+  return __float_as_int(fmaf(c, 512.0f, 12582912.0f)) - 0x4B400000;
+}
+
+// The code bytes of four values (byte e from x[e], with its segment's min and 1 / scale), equal to
+// dgq_encode_value's for every input of dgq_compress: subtract and multiply as there, then the
+// float-to-byte conversion, which rounds to nearest even, saturates to [0, 255] and takes NaN to 0.
+// The clamp to [0, levels] never binds here: a segment's min and max are those of its own values,
+// so 0 <= x - mn <= mx - mn and u <= levels * (1 + 2^-22) < levels + 1/2, and a NaN gives 0 in both.
+// The byte is then shifted by the code of the minimum: -128 flips its top bit, -127 adds 129
+// modulo 256.
+__device__ __forceinline__ uint32_t encode4(const float (&x)[4], const float (&mn)[4], const float (&inv)[4],
+                                            bool marker) {
+#pragma clang fp contract(off)
+  uint32_t w = 0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float dlt = x[e] - mn[e];
+    const float u = dlt * inv[e];
+    w = __builtin_amdgcn_cvt_pk_u8_f32(u, e, w);
+  }
+  return marker ? (((w & 0x7F7F7F7Fu) + 0x01010101u) ^ ((w ^ 0x81818181u) & 0x80808080u)) : (w ^ 0x80808080u);
+}
+
+template <int D, int BS>
+__global__ __launch_bounds__(kShortThreads) void compress_short_kernel(CompressArgs a) {
+  constexpr int S = short_tokens<D>();
+  constexpr int LPT = kShortThreads / S;   // lanes per token: 4 at head_dim 128, 2 at 64
+  constexpr int PER = D / LPT;             // channels per lane
+  static_assert(PER == 32, "each lane holds 32 channels of K and of V");
+  constexpr int P = S / 64;                // candidates per lane of the selecting wave
+  constexpr int MS = kMaxCuts + 1;
+  static_assert(MS <= kShortThreads / 64 - 1, "one wave per segment plus one for the append state");
+  const int h = blockIdx.x, b = blockIdx.y;
+  int c0, L;
+  bool bad_seq;
+  seq_range(a.cu, b, a.max_seq_len, a.total, c0, L, bad_seq);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const size_t bh = (size_t)b * a.hkv + h;
+  dgq_tail_t *tl = a.cache.tail + bh;
+  if (tid == 0 && bad_seq && h == 0) atomicAdd(a.cache.status + 2, 1ull);
+  if (L == 0) {   // empty: no segments, empty append state
+    if (tid < kWin) {
+      tl->ring_a[tid] = 0;
+      tl->ring_b[tid] = 0;
+    }
+    if (tid == 0) {
+      a.cache.nseg[bh] = 0;
+      tl->r0 = 0;
+      tl->ring_len = 0;
+      tl->span_own = 0;
+      tl->window_done = 0;
+    }
+    return;
+  }
+  __shared__ __align__(16) uint32_t ct[S * D / 4];   // value codes, token-major (4 channels a word)
+  __shared__ int ta[S];
+  __shared__ long long tb[S];
+  __shared__ float4 text[S];             // per-token K min, K max, V min, V max
+  __shared__ int wa[S];                  // window sums over tokens [t, t + 16)
+  __shared__ long long wb[S];
+  __shared__ double scs[S];              // score of candidate cut t
+  __shared__ float2 kprm[S], vprm[S];    // per-token segment (min, 1 / scale) of K and V
+  __shared__ int segid[S];               // per-token segment index
+  __shared__ int sstart[MS + 1];
+  __shared__ int s_nseg;
+
+  // ---- one read of the sequence: token t, channels [32 q, 32 q + 32) ----
+  const int t = tid / LPT, q = tid % LPT;
+  const bool valid = t < L;
+  uint32_t kw[16], vw[16];
+  float kmn = INFINITY, kmx = -INFINITY, vmn, vmx;
+  bool bad;
+  int asum = 0;
+  long long bsum = 0;
+  {
+    uint4 kr[4], vr[4];
+    const size_t row = (size_t)(c0 + (valid ? t : 0)) * a.stride_tok + (size_t)h * a.stride_head + PER * q;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      kr[i] = valid ? *reinterpret_cast<const uint4 *>(a.k + row + 8 * i) : make_uint4(0u, 0u, 0u, 0u);
+      vr[i] = valid ? *reinterpret_cast<const uint4 *>(a.v + row + 8 * i) : make_uint4(0u, 0u, 0u, 0u);
+    }
+    const half2_t zero2 = {(_Float16)0.0f, (_Float16)0.0f};
+    half2_t vmn2 = {(_Float16)INFINITY, (_Float16)INFINITY}, vmx2 = -vmn2, bad2 = zero2;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t ks[4] = {kr[i].x, kr[i].y, kr[i].z, kr[i].w};
+      const uint32_t vs[4] = {vr[i].x, vr[i].y, vr[i].z, vr[i].w};
+      unsigned int bpart = 0;   // <= 8 * 2^28 < 2^32
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const half2_t kx = as_half2(ks[e]), vx = as_half2(vs[e]);
+        vmn2 = __builtin_elementwise_min(vmn2, vx);
+        vmx2 = __builtin_elementwise_max(vmx2, vx);
+        bad2 = __builtin_elementwise_fma(kx, zero2, bad2);   // NaN once any value is not finite
+        bad2 = __builtin_elementwise_fma(vx, zero2, bad2);
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          const float x = (float)kx[hf];
+          kmn = fminf(kmn, x);
+          kmx = fmaxf(kmx, x);
+          const int n = fixed_point_fma(x);
+          asum += n;
+          bpart += (unsigned int)__mul24(n, n);
+        }
+      }
+      bsum += bpart;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        kw[4 * i + e] = ks[e];
+        vw[4 * i + e] = vs[e];
+      }
+    }
+    vmn = fminf((float)vmn2[0], (float)vmn2[1]);
+    vmx = fmaxf((float)vmx2[0], (float)vmx2[1]);
+    bad = !(bad2[0] == (_Float16)0.0f && bad2[1] == (_Float16)0.0f);
+  }
+#pragma unroll
+  for (int o = 1; o < LPT; o <<= 1) {
+    asum += __shfl_xor(asum, o);
+    bsum += __shfl_xor(bsum, o);
+    kmn = fminf(kmn, __shfl_xor(kmn, o));
+    kmx = fmaxf(kmx, __shfl_xor(kmx, o));
+    vmn = fminf(vmn, __shfl_xor(vmn, o));
+    vmx = fmaxf(vmx, __shfl_xor(vmx, o));
+  }
+  if (q == 0) {
+    ta[t] = valid ? asum : 0;
+    tb[t] = valid ? bsum : 0;
+    text[t] = make_float4(kmn, kmx, vmn, vmx);
+  }
+  {
+    // one count per 16-token group that holds a non-finite value (a group is 16 * LPT lanes)
+    const unsigned long long m = __ballot(bad);
+    constexpr int GL = kWin * LPT;
+    if (lane == 0) {
+      unsigned int n = 0;
+#pragma unroll
+      for (int g = 0; g < 64 / GL; ++g) n += ((m >> (GL * g)) & ((GL == 64) ? ~0ull : ((1ull << GL) - 1))) != 0ull;
+      if (n) atomicAdd(a.cache.status + 1, (unsigned long long)n);
+    }
+  }
+  __syncthreads();
+
+  // ---- window sums, then the score of every candidate cut (both windows inside the sequence) ----
+  if (tid < S && tid + kWin <= L) {
+    int A = 0;
+    long long B = 0;
+#pragma unroll
+    for (int u = 0; u < kWin; ++u) {
+      A += ta[tid + u];
+      B += tb[tid + u];
+    }
+    wa[tid] = A;
+    wb[tid] = B;
+  }
+  __syncthreads();
+  if (tid < S) {
+    double sc = -INFINITY;
+    if (tid >= kWin && tid <= L - kWin) {
+      // Q = N * sum b - (sum a)^2, exact in double (|sum a| <= 2^25, N * sum b <= 2^51)
+      const double nel = (double)(kWin * D);
+      const double Al = (double)wa[tid - kWin], Ar = (double)wa[tid];
+      const double ql = fma(-Al, Al, nel * (double)wb[tid - kWin]);
+      const double qr = fma(-Ar, Ar, nel * (double)wb[tid]);
+      sc = fmax(ql, qr) < a.qfloor ? -INFINITY : (fmax(ql, qr) + 1.0) / (fmin(ql, qr) + 1.0);
+    }
+    scs[tid] = sc;
+  }
+  __syncthreads();
+
+  // ---- greedy selection in wave 0 alone: lane l holds candidates P l .. P l + P - 1 ----
+  if (wave == 0) {
+    double sc[P];
+#pragma unroll
+    for (int i = 0; i < P; ++i) sc[i] = scs[P * lane + i];
+    int cut[kMaxCuts];
+    int nc = 0;
+    const int max_seg = a.length_aware ? min(a.max_segments, length_aware_cap(L)) : a.max_segments;
+    if (L >= 2 * kWin) {
+      for (int r = 0; r < max_seg - 1; ++r) {
+        double s = -INFINITY;
+        int tt = INT_MAX;
+#pragma unroll
+        for (int i = 0; i < P; ++i)
+          if (sc[i] > s) {   // ascending t: the first maximum is the smallest t
+            s = sc[i];
+            tt = P * lane + i;
+          }
+        wave_best(s, tt);
+        if (s == -INFINITY) break;
+        if (r > 0 && !(s >= a.tau)) break;
+        cut[nc++] = tt;
+#pragma unroll
+        for (int i = 0; i < P; ++i)
+          if (abs(P * lane + i - tt) <= kWin - 1) sc[i] = -INFINITY;
+      }
+    }
+    // starts = [0] + sorted cuts, then L (the cuts are wave-uniform)
+    for (int i = 1; i < nc; ++i) {
+      const int x = cut[i];
+      int k = i;
+      while (k > 0 && cut[k - 1] > x) {
+        cut[k] = cut[k - 1];
+        --k;
+      }
+      cut[k] = x;
+    }
+    if (lane == 0) {
+      sstart[0] = 0;
+      for (int i = 0; i < nc; ++i) sstart[i + 1] = cut[i];
+      sstart[nc + 1] = L;
+      s_nseg = nc + 1;
+    }
+  }
+  __syncthreads();
+  const int nseg = s_nseg;
+
+  // ---- segment j's K/V min/max in wave j, the segment row, and its tokens' parameters; the
+  // append state in the last wave ----
+  if (wave < nseg) {
+    const int s0 = sstart[wave], s1 = sstart[wave + 1];
+    float4 r = make_float4(INFINITY, -INFINITY, INFINITY, -INFINITY);
+    for (int tok = s0 + lane; tok < s1; tok += 64) {
+      const float4 x = text[tok];
+      r.x = fminf(r.x, x.x);
+      r.y = fmaxf(r.y, x.y);
+      r.z = fminf(r.z, x.z);
+      r.w = fmaxf(r.w, x.w);
+    }
+    r = wave_minmax(r);
+    dgq_seg_t row;
+    row.start = s0;
+    row.kmin = r.x + 0.0f;
+    row.kmax = r.y + 0.0f;
+    row.vmin = r.z + 0.0f;
+    row.vmax = r.w + 0.0f;
+    row.kscale = dgq_scale(row.kmin, row.kmax, a.fmt.levels);
+    row.vscale = dgq_scale(row.vmin, row.vmax, a.fmt.levels);
+    row.reserved = 0;
+    if (lane == 0) a.cache.segs[bh * a.seg_cap + wave] = row;
+    const float2 kp = make_float2(row.kmin, dgq_inv(row.kmin, row.kmax, a.fmt.levels));
+    const float2 vp = make_float2(row.vmin, dgq_inv(row.vmin, row.vmax, a.fmt.levels));
+    for (int tok = s0 + lane; tok < s1; tok += 64) {
+      kprm[tok] = kp;
+      vprm[tok] = vp;
+      segid[tok] = wave;
+    }
+  } else if (wave == kShortThreads / 64 - 1) {
+    // append state: open span starts at L, ring = the last min(16, L) tokens' moments
+    const int rl = min(kWin, L);
+    if (lane < kWin) {
+      tl->ring_a[lane] = lane < rl ? ta[L - rl + lane] : 0;
+      tl->ring_b[lane] = lane < rl ? tb[L - rl + lane] : 0;
+    }
+    if (lane == 0) {
+      a.cache.nseg[bh] = nseg;
+      tl->r0 = L;
+      tl->ring_len = rl;
+      tl->span_own = 0;
+      tl->window_done = 0;
+    }
+  }
+  __syncthreads();
+
+  const int32_t *bt = a.block_table + (size_t)b * a.max_blocks;
+  const int nblk_seq = (L + BS - 1) / BS;
+  const size_t tile_bytes = (size_t)BS * D;
+  const bool marker = a.fmt.marker != 0;
+
+  // ---- keys, from the registers: two 16-channel units of token t per lane; values, from the
+  // registers into the token-major code array (zeros past L) ----
+  {
+    uint4 *dst = reinterpret_cast<uint4 *>(ct + (t * D + PER * q) / 4);
+    if (valid) {
+      const float2 vp = vprm[t];
+      const float mn[4] = {vp.x, vp.x, vp.x, vp.x};
+      const float inv[4] = {vp.y, vp.y, vp.y, vp.y};
+      uint32_t cw[8];
+#pragma unroll
+      for (int g = 0; g < 8; ++g) {
+        const half2_t x01 = as_half2(vw[2 * g]), x23 = as_half2(vw[2 * g + 1]);
+        const float x[4] = {(float)x01[0], (float)x01[1], (float)x23[0], (float)x23[1]};
+        cw[g] = encode4(x, mn, inv, marker);
+      }
+      dst[0] = make_uint4(cw[0], cw[1], cw[2], cw[3]);
+      dst[1] = make_uint4(cw[4], cw[5], cw[6], cw[7]);
+    } else {
+      dst[0] = make_uint4(0u, 0u, 0u, 0u);
+      dst[1] = make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
+  if (valid) {
+    const float2 kp = kprm[t];
+    const float mn[4] = {kp.x, kp.x, kp.x, kp.x};
+    const float inv[4] = {kp.y, kp.y, kp.y, kp.y};
+    const bool first = t > 0 && segid[t] != segid[t - 1];   // first token of a segment but the first
+    bool bad_blk = false;
+    const int blk = checked_block(bt[t / BS], a.cache.num_blocks, bad_blk);
+#pragma unroll
+    for (int hu = 0; hu < 2; ++hu) {
+      const int d0 = PER * q + 16 * hu;
+      uint32_t outw[4];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const half2_t x01 = as_half2(kw[8 * hu + 2 * g]), x23 = as_half2(kw[8 * hu + 2 * g + 1]);
+        const float x[4] = {(float)x01[0], (float)x01[1], (float)x23[0], (float)x23[1]};
+        outw[g] = encode4(x, mn, inv, marker);
+      }
+      if (marker && d0 == 0 && first) outw[0] = (outw[0] & ~0xFFu) | dgq_marker_byte(outw[0] & 0xFFu);
+      if (bad_blk) {
+        atomicAdd(a.cache.status + 2, 1ull);
+        continue;
+      }
+      int8_t *dst = a.cache.k_pool + ((size_t)blk * a.hkv + h) * tile_bytes + k_tile_offset<D, BS>(t % BS, d0);
+      store_stream(dst, outw);
+    }
+  }
+
+  __syncthreads();
+
+  // ---- values: one quad = 4 channels x the 16 tokens of a value unit; its four units are 64
+  // contiguous bytes of a tile.  Word g of a unit holds 4 consecutive tokens (byte e = token
+  // base_g + e), so each 4 x 4 byte block of the token-major codes is transposed with byte
+  // permutes ----
+  {
+    constexpr int QD = D / 4;                          // channel quads per token row
+    const int sets = nblk_seq * (BS / 16);             // 16-token sets of the sequence's blocks
+    for (int qi = tid; qi < sets * QD; qi += kShortThreads) {
+      const int set = qi / QD, c = qi % QD;
+      const int lblk = set / (BS / 16);
+      uint32_t out[4][4];                              // [channel j][word g]
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        // BS 16: the set is block lblk, word g = tokens 4 g ..; BS 64: the set is (lblk, jj),
+        // word g = tokens 16 g + 4 jj ..
+        const int base = BS == 16 ? 16 * lblk + 4 * g : 64 * lblk + 16 * g + 4 * (set % 4);
+        const uint32_t w0 = ct[(base + 0) * QD + c], w1 = ct[(base + 1) * QD + c];
+        const uint32_t w2 = ct[(base + 2) * QD + c], w3 = ct[(base + 3) * QD + c];
+        const uint32_t lo01 = __builtin_amdgcn_perm(w1, w0, 0x05010400u), hi01 = __builtin_amdgcn_perm(w1, w0, 0x07030602u);
+        const uint32_t lo23 = __builtin_amdgcn_perm(w3, w2, 0x05010400u), hi23 = __builtin_amdgcn_perm(w3, w2, 0x07030602u);
+        out[0][g] = __builtin_amdgcn_perm(lo23, lo01, 0x05040100u);
+        out[1][g] = __builtin_amdgcn_perm(lo23, lo01, 0x07060302u);
+        out[2][g] = __builtin_amdgcn_perm(hi23, hi01, 0x05040100u);
+        out[3][g] = __builtin_amdgcn_perm(hi23, hi01, 0x07060302u);
+      }
+      bool bad_blk = false;
+      const int blk = checked_block(bt[lblk], a.cache.num_blocks, bad_blk);
+      if (bad_blk) continue;   // counted by the key loop
+      int8_t *tilep = a.cache.v_pool + ((size_t)blk * a.hkv + h) * tile_bytes;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int d = 4 * c + j;
+        const int off = BS == 16 ? v_tile_offset<D, BS>(0, d) : v_tile_offset<D, BS>(4 * (set % 4), d);
+        store_stream(tilep + off, out[j]);
+      }
+    }
+  }
+
+  // ---- boundary bits: one byte per 8 tokens of every block of the sequence (bitmap format) ----
+  if (!marker && tid < nblk_seq * (BS / 8)) {
+    const int tok0 = 8 * tid;
+    uint32_t byte = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int tok = tok0 + i;
+      if (tok > 0 && tok < L && segid[tok] != segid[tok - 1]) byte |= 1u << i;
+    }
+    bool bad_blk = false;
+    const int blk = checked_block(bt[tok0 / BS], a.cache.num_blocks, bad_blk);
+    if (!bad_blk) a.cache.bits[((size_t)blk * a.hkv + h) * (BS / 8) + (tok0 % BS) / 8] = (uint8_t)byte;
+  }
+}
+
 CompressLayout compress_layout(const dgq_params_t *p, int32_t batch, int64_t total_tokens,
                                int32_t max_seq_len) {
   CompressLayout l;
@@ -1088,6 +1494,11 @@ static dgq_status_t launch_all(const CompressArgs &a, int bs, int max_seq_len, i
   dim3 g64 = ragged ? dim3((unsigned)map_tiles, hkv, 1) : dim3((max_seq_len + 63) / 64, hkv, batch);
   dim3 g256((max_seq_len + 255) / 256, hkv, batch);
   dgq_status_t st;
+  if (!a.multipass && max_seq_len <= short_tokens<D>()) {
+    if (bs == 64) hipLaunchKernelGGL((compress_short_kernel<D, 64>), dim3(hkv, batch), dim3(kShortThreads), 0, s, a);
+    else hipLaunchKernelGGL((compress_short_kernel<D, 16>), dim3(hkv, batch), dim3(kShortThreads), 0, s, a);
+    return check_launch("dgq_compress one-launch kernel");
+  }
   const bool small = max_seq_len <= kSmallSeq && a.max_segments <= kMaxCuts + 1;
   if (max_seq_len > 0) {
     if (ragged) {
@@ -1143,6 +1554,7 @@ dgq_status_t launch_compress(const dgq_params_t *p, const uint16_t *k, const uin
   a.tau = p->tau;
   a.qfloor = variance_floor_q(p->min_var, p->head_dim);
   a.length_aware = (p->flags & DGQ_POLICY_LENGTH_AWARE) != 0;
+  a.multipass = (p->flags & DGQ_COMPRESS_MULTIPASS) != 0;
   a.fmt = code_format(p);
   a.ws_a = reinterpret_cast<int32_t *>(w + l.a_off);
   a.ws_b = reinterpret_cast<int64_t *>(w + l.b_off);

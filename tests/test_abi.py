@@ -77,16 +77,18 @@ def test_workspace_sizes(lib):
     assert lib.dgq_compress_workspace_size(ctypes.byref(p), 16, 16 * 8192, 8192) > 16 * 8192 * 8 * 20
     assert lib.dgq_decode_workspace_size(ctypes.byref(p), 16, 8192) > 0
     for bad in (_params(head_dim=96), _params(block_size=32), _params(win=8), _params(num_q_heads=20),
-                _params(max_segments=9), _params(seg_capacity=4), _params(tau=0.5), _params(flags=4),
+                _params(max_segments=9), _params(seg_capacity=4), _params(tau=0.5), _params(flags=8),
                 _params(min_var=-1.0), _params(min_var=float("nan"))):
         assert lib.dgq_compress_workspace_size(ctypes.byref(bad), 1, 10, 10) == 0
         assert lib.dgq_decode_workspace_size(ctypes.byref(bad), 1, 10) == 0
 
 
 def test_policy_params_accepted(lib):
-    """The length-aware flag and a variance floor are valid parameters."""
+    """The length-aware flag, a variance floor, the marker format and the multi-pass compress
+    switch are valid parameters."""
     for good in (_params(flags=_lib.DGQ_POLICY_LENGTH_AWARE), _params(min_var=0.01),
-                 _params(flags=1, min_var=1e-4), _params(flags=_lib.DGQ_FORMAT_MARKER), _params(flags=3)):
+                 _params(flags=1, min_var=1e-4), _params(flags=_lib.DGQ_FORMAT_MARKER), _params(flags=3),
+                 _params(flags=_lib.DGQ_COMPRESS_MULTIPASS), _params(flags=7)):
         assert lib.dgq_compress_workspace_size(ctypes.byref(good), 1, 10, 10) > 0
 
 
