@@ -23,9 +23,17 @@ def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
 
-def _stream(stream) -> ctypes.c_void_p:
-    s = torch.cuda.current_stream() if stream is None else stream
-    return ctypes.c_void_p(s.cuda_stream)
+# torch's current-stream handle of a device as a plain integer, without building a Stream object
+# (that costs a few microseconds per call, as much as a small kernel).
+_raw_current_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
+def _stream(stream) -> int:
+    if stream is not None:
+        return stream.cuda_stream
+    if _raw_current_stream is not None:
+        return _raw_current_stream(torch.cuda.current_device())
+    return torch.cuda.current_stream().cuda_stream
 
 
 def _need(cond: bool, msg: str) -> None:

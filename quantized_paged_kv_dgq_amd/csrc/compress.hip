@@ -1078,6 +1078,8 @@ template <int D>
 constexpr int short_tokens() { return kShortElems / D; }
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef short short2_t __attribute__((ext_vector_type(2)));
+constexpr short2_t kOnes2 = {1, 1};
 __device__ __forceinline__ half2_t as_half2(uint32_t w) { return __builtin_bit_cast(half2_t, w); }
 
 // dgq_fixed_point(x) for every x: the clamped value times 512 is exact, and adding 1.5 * 2^23
@@ -1173,7 +1175,7 @@ __global__ __launch_bounds__(kShortThreads) void compress_short_kernel(CompressA
     for (int i = 0; i < 4; ++i) {
       const uint32_t ks[4] = {kr[i].x, kr[i].y, kr[i].z, kr[i].w};
       const uint32_t vs[4] = {vr[i].x, vr[i].y, vr[i].z, vr[i].w};
-      unsigned int bpart = 0;   // <= 8 * 2^28 < 2^32
+      int bpart = 0;   // sum of 8 squares <= 2^31: wraps as int32, exact read as uint32
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const half2_t kx = as_half2(ks[e]), vx = as_half2(vs[e]);
@@ -1181,17 +1183,18 @@ __global__ __launch_bounds__(kShortThreads) void compress_short_kernel(CompressA
         vmx2 = __builtin_elementwise_max(vmx2, vx);
         bad2 = __builtin_elementwise_fma(kx, zero2, bad2);   // NaN once any value is not finite
         bad2 = __builtin_elementwise_fma(vx, zero2, bad2);
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          const float x = (float)kx[hf];
-          kmn = fminf(kmn, x);
-          kmx = fmaxf(kmx, x);
-          const int n = fixed_point_fma(x);
-          asum += n;
-          bpart += (unsigned int)__mul24(n, n);
-        }
+        const float x0 = (float)kx[0], x1 = (float)kx[1];
+        kmn = fminf(kmn, fminf(x0, x1));
+        kmx = fmaxf(kmx, fmaxf(x0, x1));
+        // the two fixed-point images as int16 halves of one word (|n| <= 2^14), then the sums of
+        // n and n^2 by 16-bit dot products
+        const uint32_t n01 = __builtin_amdgcn_perm((uint32_t)fixed_point_fma(x1), (uint32_t)fixed_point_fma(x0),
+                                                   0x05040100u);
+        const short2_t n2 = __builtin_bit_cast(short2_t, n01);
+        asum = __builtin_amdgcn_sdot2(n2, kOnes2, asum, false);
+        bpart = __builtin_amdgcn_sdot2(n2, n2, bpart, false);
       }
-      bsum += bpart;
+      bsum += (unsigned int)bpart;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         kw[4 * i + e] = ks[e];
@@ -1202,15 +1205,18 @@ __global__ __launch_bounds__(kShortThreads) void compress_short_kernel(CompressA
     vmx = fmaxf((float)vmx2[0], (float)vmx2[1]);
     bad = !(bad2[0] == (_Float16)0.0f && bad2[1] == (_Float16)0.0f);
   }
-#pragma unroll
-  for (int o = 1; o < LPT; o <<= 1) {
-    asum += __shfl_xor(asum, o);
-    bsum += __shfl_xor(bsum, o);
-    kmn = fminf(kmn, __shfl_xor(kmn, o));
-    kmx = fmaxf(kmx, __shfl_xor(kmx, o));
-    vmn = fminf(vmn, __shfl_xor(vmn, o));
-    vmx = fmaxf(vmx, __shfl_xor(vmx, o));
-  }
+  // combine the LPT lanes of a token (adjacent lanes of one quad) with DPP quad swaps
+  auto quad_combine = [&](auto tag) {
+    constexpr int C = decltype(tag)::value;
+    asum += dpp_i<C>(asum);
+    bsum += (long long)(unsigned)dpp_i<C>((int)bsum) | ((long long)dpp_i<C>((int)(bsum >> 32)) << 32);
+    kmn = fminf(kmn, dpp_f<C>(kmn));
+    kmx = fmaxf(kmx, dpp_f<C>(kmx));
+    vmn = fminf(vmn, dpp_f<C>(vmn));
+    vmx = fmaxf(vmx, dpp_f<C>(vmx));
+  };
+  quad_combine(std::integral_constant<int, kQuadSwap1>{});
+  if constexpr (LPT == 4) quad_combine(std::integral_constant<int, kQuadSwap2>{});
   if (q == 0) {
     ta[t] = valid ? asum : 0;
     tb[t] = valid ? bsum : 0;
