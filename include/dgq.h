@@ -256,6 +256,26 @@ size_t dgq_compress_workspace_size(const dgq_params_t *p, int32_t batch, int64_t
 /* paged_decode_attn_int8 scratch (split-sequence partial results). */
 size_t dgq_decode_workspace_size(const dgq_params_t *p, int32_t batch, int32_t max_seq_len);
 
+/* The operations of dgq_workspace_size. */
+enum {
+  DGQ_OP_COMPRESS = 0,       /* dgq_compress */
+  DGQ_OP_APPEND = 1,         /* dgq_append: takes no workspace (size 0) */
+  DGQ_OP_DECODE = 2,         /* paged_decode_attn_int8 */
+  DGQ_OP_APPEND_DECODE = 3,  /* dgq_append_decode */
+  DGQ_OP_G64_DECODE = 4      /* paged_decode_attn_g64 */
+};
+/* Workspace bytes of operation `op` for `batch` sequences of at most max_seq_len tokens
+ * (total_tokens in all; read for DGQ_OP_COMPRESS only): one entry for every operation, equal to
+ * the per-operation functions above.  0 for invalid arguments or an unknown op. */
+size_t dgq_workspace_size(const dgq_params_t *p, int32_t op, int32_t batch, int64_t total_tokens,
+                          int32_t max_seq_len);
+
+/* Copy the cache's four device status words (see dgq_cache_t.status) to host memory out[0..3],
+ * after everything queued on `stream` before this call: enqueues the copy on `stream` and then
+ * synchronizes that stream (the one library call that waits).  out: host, 4 elements.  The words
+ * are not reset.  DGQ_ERR_INVALID_ARG for a null cache, status pointer or out. */
+dgq_status_t dgq_read_device_status(const dgq_cache_t *cache, unsigned long long *out, hipStream_t stream);
+
 /* ---- DGQ compression (DGQ article 2.2) ----
  * For every (sequence b, kv head h): the variance curve of the keys over a sliding 16-token
  * window, cuts at its change points (2..max_segments segments when the sequence has >= 32

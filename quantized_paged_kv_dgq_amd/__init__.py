@@ -5,7 +5,8 @@ this package is its Python binding.  Importing it does not load the library; the
 does, and fails loudly if it is not built.
 """
 
-from ._lib import DGQError, EXPORTS, LIB_PATH, load  # noqa: F401
+from ._lib import (DGQ_OP_APPEND, DGQ_OP_APPEND_DECODE, DGQ_OP_COMPRESS, DGQ_OP_DECODE,  # noqa: F401
+                   DGQ_OP_G64_DECODE, DGQError, EXPORTS, LIB_PATH, load)
 from .api import (  # noqa: F401
     BlockPool,
     DGQCache,
@@ -27,4 +28,5 @@ from .api import (  # noqa: F401
     paged_decode_attn_int8_noalloc,
     swap_image_bytes,
     workspace,
+    workspace_size,
 )

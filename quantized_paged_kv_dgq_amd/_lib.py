@@ -85,6 +85,7 @@ DGQ_POLICY_LENGTH_AWARE = 1
 DGQ_FORMAT_MARKER = 2
 DGQ_COMPRESS_MULTIPASS = 4
 DGQ_NOALLOC_SCRATCH_BYTES = 16 << 20
+DGQ_OP_COMPRESS, DGQ_OP_APPEND, DGQ_OP_DECODE, DGQ_OP_APPEND_DECODE, DGQ_OP_G64_DECODE = range(5)
 
 assert ctypes.sizeof(Params) == 48
 assert ctypes.sizeof(Seg) == 32
@@ -97,7 +98,7 @@ EXPORTS = [
     "dgq_block_share", "dgq_block_refcount", "dgq_block_cow",
     "dgq_copy_blocks", "dgq_copy_seq_state", "dgq_swap_image_bytes", "dgq_swap_out", "dgq_swap_in",
     "dgq_marker_bits",
-    "dgq_compress_workspace_size", "dgq_decode_workspace_size",
+    "dgq_compress_workspace_size", "dgq_decode_workspace_size", "dgq_workspace_size", "dgq_read_device_status",
     "dgq_compress", "dgq_append", "paged_decode_attn_int8", "paged_decode_attn_int8_noalloc",
     "dgq_append_decode",
     "dgq_g64_quantize", "paged_decode_attn_g64",
@@ -152,6 +153,10 @@ def load() -> ctypes.CDLL:
     lib.dgq_compress_workspace_size.restype = sz
     lib.dgq_decode_workspace_size.argtypes = [P(Params), i32, i32]
     lib.dgq_decode_workspace_size.restype = sz
+    lib.dgq_workspace_size.argtypes = [P(Params), i32, i32, i64, i32]
+    lib.dgq_workspace_size.restype = sz
+    lib.dgq_read_device_status.argtypes = [P(Cache), P(ctypes.c_ulonglong), vp]
+    lib.dgq_read_device_status.restype = i32
     lib.dgq_compress.argtypes = [P(Params), vp, vp, i64, i64, vp, i32, i32, i64, vp, i32,
                                  P(Cache), vp, sz, vp]
     lib.dgq_compress.restype = i32

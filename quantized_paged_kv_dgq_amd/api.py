@@ -102,11 +102,13 @@ class DGQCache:
                        _ptr(self.nseg), _ptr(self.tail), _ptr(self.k_stage), _ptr(self.v_stage),
                        _ptr(self.status), num_blocks, batch)
 
-    def read_status(self) -> dict:
-        """The device status words (synchronizes with the device): appends that wanted a new segment
-        but found the table full, groups of inputs with a non-finite value, and device-side
-        inconsistencies that were skipped or clamped (see dgq_cache_t.status)."""
-        v = self.status.cpu().tolist()
+    def read_status(self, stream=None) -> dict:
+        """The device status words through dgq_read_device_status (waits for the stream): appends
+        that wanted a new segment but found the table full, groups of inputs with a non-finite
+        value, and device-side inconsistencies that were skipped or clamped (see
+        dgq_cache_t.status)."""
+        v = (ctypes.c_ulonglong * 4)()
+        check(_lib.load().dgq_read_device_status(ctypes.byref(self.c), v, _stream(stream)), "dgq_read_device_status")
         return {"clamped_appends": v[0], "nonfinite_groups": v[1], "inconsistencies": v[2]}
 
     # host-side views for tests and reports (copies)
@@ -192,6 +194,11 @@ def compress_workspace_size(params: DGQParams, batch: int, total_tokens: int, ma
 
 def decode_workspace_size(params: DGQParams, batch: int, max_seq_len: int) -> int:
     return int(_lib.load().dgq_decode_workspace_size(ctypes.byref(params.c), batch, max_seq_len))
+
+
+def workspace_size(params: DGQParams, op: int, batch: int, total_tokens: int, max_seq_len: int) -> int:
+    """dgq_workspace_size: workspace bytes of operation ``op`` (DGQ_OP_*)."""
+    return int(_lib.load().dgq_workspace_size(ctypes.byref(params.c), op, batch, total_tokens, max_seq_len))
 
 
 def workspace(nbytes: int, device="cuda") -> torch.Tensor:

@@ -92,6 +92,28 @@ extern "C" size_t dgq_decode_workspace_size(const dgq_params_t *p, int32_t batch
   return decode_workspace_bytes(p, batch, max_seq_len);
 }
 
+extern "C" size_t dgq_workspace_size(const dgq_params_t *p, int32_t op, int32_t batch, int64_t total_tokens,
+                                     int32_t max_seq_len) {
+  switch (op) {
+    case DGQ_OP_COMPRESS: return dgq_compress_workspace_size(p, batch, total_tokens, max_seq_len);
+    case DGQ_OP_APPEND: return 0;
+    case DGQ_OP_DECODE:
+    case DGQ_OP_APPEND_DECODE:
+    case DGQ_OP_G64_DECODE: return dgq_decode_workspace_size(p, batch, max_seq_len);
+    default: return 0;
+  }
+}
+
+extern "C" dgq_status_t dgq_read_device_status(const dgq_cache_t *cache, unsigned long long *out,
+                                               hipStream_t stream) {
+  if (cache == nullptr || cache->status == nullptr || out == nullptr) return DGQ_ERR_INVALID_ARG;
+  hipError_t e = hipMemcpyAsync(out, cache->status, 4 * sizeof(unsigned long long), hipMemcpyDeviceToHost, stream);
+  if (e != hipSuccess) return hip_fail(e, "dgq_read_device_status copy");
+  e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return hip_fail(e, "dgq_read_device_status synchronize");
+  return DGQ_OK;
+}
+
 extern "C" dgq_status_t dgq_compress(const dgq_params_t *p, const uint16_t *k, const uint16_t *v,
                                      int64_t stride_tok, int64_t stride_head,
                                      const int32_t *cu_seqlens, int32_t batch, int32_t max_seq_len,

@@ -83,6 +83,35 @@ def test_workspace_sizes(lib):
         assert lib.dgq_decode_workspace_size(ctypes.byref(bad), 1, 10) == 0
 
 
+def test_workspace_size_by_operation(lib):
+    """dgq_workspace_size(op) equals the per-operation functions; append takes none; an unknown op
+    or invalid parameters give 0."""
+    for p in (_params(), _params(head_dim=64, block_size=64, num_q_heads=8), _params(flags=7)):
+        for batch, total, L in ((16, 16 * 8192, 8192), (1, 131072, 131072), (100, 234194, 4096), (1, 256, 256)):
+            comp = lib.dgq_compress_workspace_size(ctypes.byref(p), batch, total, L)
+            dec = lib.dgq_decode_workspace_size(ctypes.byref(p), batch, L)
+            assert comp > 0 and dec > 0
+            ws = lambda op: lib.dgq_workspace_size(ctypes.byref(p), op, batch, total, L)  # noqa: E731
+            assert ws(_lib.DGQ_OP_COMPRESS) == comp
+            assert ws(_lib.DGQ_OP_APPEND) == 0
+            assert ws(_lib.DGQ_OP_DECODE) == dec
+            assert ws(_lib.DGQ_OP_APPEND_DECODE) == dec
+            assert ws(_lib.DGQ_OP_G64_DECODE) == dec
+            assert ws(5) == 0 and ws(-1) == 0
+    bad = _params(head_dim=96)
+    assert lib.dgq_workspace_size(ctypes.byref(bad), _lib.DGQ_OP_DECODE, 1, 10, 10) == 0
+
+
+def test_read_device_status_argument_checks(lib):
+    """Null cache, status pointer or output: refused before any HIP call."""
+    out = (ctypes.c_ulonglong * 4)()
+    assert lib.dgq_read_device_status(None, out, None) == _lib.DGQ_ERR_INVALID_ARG
+    cache = _lib.Cache()
+    assert lib.dgq_read_device_status(ctypes.byref(cache), out, None) == _lib.DGQ_ERR_INVALID_ARG
+    cache.status = 1 << 20                  # never dereferenced: the null output fails first
+    assert lib.dgq_read_device_status(ctypes.byref(cache), None, None) == _lib.DGQ_ERR_INVALID_ARG
+
+
 def test_policy_params_accepted(lib):
     """The length-aware flag, a variance floor, the marker format and the multi-pass compress
     switch are valid parameters."""
