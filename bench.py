@@ -153,14 +153,16 @@ def _profile_kv(name: str) -> dict:
 
 HEADLINE_PROFILE = "decode_128k_layer_trace_and_traffic.txt"
 LLAMA_PROFILE = "decode_llama3_8b_layer_hbm_traffic.txt"
+WORKLOADS_PROFILE = "workloads_hbm_traffic.txt"
 
 
-def measured_traffic(what: str = "decode", profile: str = HEADLINE_PROFILE):
+def measured_traffic(what: str = "decode", profile: str = HEADLINE_PROFILE, prefix: str = ""):
     """HBM bytes per decode launch ("decode") or per dgq_compress call ("compress") from a
-    committed counter profile, if it was taken on the current kernel sources (else None)."""
+    committed counter profile (keys with an optional section prefix, e.g. "mha_"), if it was taken
+    on the current kernel sources (else None)."""
     kv = _profile_kv(profile)
     digest = kernel_source_digest() if what == "decode" else compress_source_digest()
-    key = "decode_hbm_bytes_per_launch" if what == "decode" else "compress_hbm_bytes_per_call"
+    key = prefix + ("decode_hbm_bytes_per_launch" if what == "decode" else "compress_hbm_bytes_per_call")
     if kv.get(f"{what}_source_sha256_16") != digest:
         return None
     try:
@@ -718,13 +720,21 @@ def high_concurrency(seed, dev, Q):
     rec = {"workload": "high-concurrency MHA: 100 seqs, lengths U[512, 4096], 32 KV = 32 q heads, "
                        "head_dim 128, 16-token blocks shuffled"}
     rec.update(fixed_batch(4, seed, dev, Q, ncache=3, reps=12))
+    rec["decode_traffic"] = measured_traffic(profile=WORKLOADS_PROFILE, prefix="mha_")
+    rec["roofline_compress"] = {
+        "bound": "hbm", "achieved": rec["compress_gbs_alg"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+        "frac": round(rec["compress_gbs_alg"] / HBM_PEAK_GBS, 4),
+        "traffic": measured_traffic("compress", profile=WORKLOADS_PROFILE, prefix="mha_"),
+        "kernel": "dgq_compress of the batch (tile map + stats + select + encode; HIP events around "
+                  "back-to-back calls)",
+    }
     return rec
 
 
 def tiny(seed, dev, Q):
     """The tiny workload (1 sequence x 256 tokens, 2 heads, head_dim 64): launch-latency bound,
     reported in microseconds only."""
-    r = fixed_batch(1, seed, dev, Q, ncache=2, reps=20)
+    r = fixed_batch(1, seed, dev, Q, ncache=2, reps=200)
     return {"workload": "tiny: 1 seq x 256 tokens, 2 KV = 2 q heads, head_dim 64, 16-token blocks",
             "compress_us": r["compress_us"], "decode_us": r["decode_us"],
             "segments_per_head_hist": r["segments_per_head_hist"],

@@ -362,6 +362,32 @@ __device__ __forceinline__ void wave_best(double &s, int &t) {
   s = bs;
   t = bt;
 }
+// maximum of an unsigned 64-bit value over the wave, returned uniform
+template <int C>
+__device__ __forceinline__ unsigned long long dpp_u64(unsigned long long x) {
+  const int lo = dpp_i<C>((int)x), hi = dpp_i<C>((int)(x >> 32));
+  return (unsigned long long)(unsigned)lo | ((unsigned long long)(unsigned)hi << 32);
+}
+__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long x) {
+  auto step = [&](auto tag) {
+    constexpr int C = decltype(tag)::value;
+    const unsigned long long y = dpp_u64<C>(x);
+    x = y > x ? y : x;
+  };
+  step(std::integral_constant<int, kQuadSwap1>{});
+  step(std::integral_constant<int, kQuadSwap2>{});
+  step(std::integral_constant<int, kRowRor4>{});
+  step(std::integral_constant<int, kRowRor8>{});   // every lane holds its row's maximum
+  unsigned long long m = 0ull;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const unsigned lo = (unsigned)__builtin_amdgcn_readlane((int)x, 16 * r);
+    const unsigned hi = (unsigned)__builtin_amdgcn_readlane((int)(x >> 32), 16 * r);
+    const unsigned long long y = (unsigned long long)lo | ((unsigned long long)hi << 32);
+    m = y > m ? y : m;
+  }
+  return m;
+}
 // (min, max, min, max) over the wave, returned uniform
 __device__ __forceinline__ float4 wave_minmax(float4 r) {
   auto step = [&](auto tag) {
@@ -1262,31 +1288,39 @@ __global__ __launch_bounds__(kShortThreads) void compress_short_kernel(CompressA
   }
   __syncthreads();
 
-  // ---- greedy selection in wave 0 alone: lane l holds candidates P l .. P l + P - 1 ----
+  // ---- greedy selection in wave 0 alone: lane l holds candidates P l .. P l + P - 1.  A score is
+  // compared through its bit pattern as a 64-bit integer (scores are finite and >= 1, and positive
+  // doubles order like their bit patterns; 0 = no candidate), so the wave maximum is an integer
+  // reduction; among equal maxima the smallest t is the first lane's first one ----
   if (wave == 0) {
-    double sc[P];
+    unsigned long long key[P];
 #pragma unroll
-    for (int i = 0; i < P; ++i) sc[i] = scs[P * lane + i];
+    for (int i = 0; i < P; ++i) {
+      const double v = scs[P * lane + i];
+      key[i] = v > -INFINITY ? (unsigned long long)__double_as_longlong(v) : 0ull;
+    }
     int cut[kMaxCuts];
     int nc = 0;
     const int max_seg = a.length_aware ? min(a.max_segments, length_aware_cap(L)) : a.max_segments;
     if (L >= 2 * kWin) {
       for (int r = 0; r < max_seg - 1; ++r) {
-        double s = -INFINITY;
-        int tt = INT_MAX;
+        unsigned long long kb = 0ull;
+        int ib = 0;
 #pragma unroll
         for (int i = 0; i < P; ++i)
-          if (sc[i] > s) {   // ascending t: the first maximum is the smallest t
-            s = sc[i];
-            tt = P * lane + i;
+          if (key[i] > kb) {   // ascending t: the first maximum is the smallest t
+            kb = key[i];
+            ib = i;
           }
-        wave_best(s, tt);
-        if (s == -INFINITY) break;
-        if (r > 0 && !(s >= a.tau)) break;
+        const unsigned long long wm = wave_max_u64(kb);
+        if (wm == 0ull) break;
+        if (r > 0 && !(__longlong_as_double((long long)wm) >= a.tau)) break;
+        const int wl = __builtin_ctzll(__ballot(kb == wm));
+        const int tt = P * wl + __builtin_amdgcn_readlane(ib, wl);
         cut[nc++] = tt;
 #pragma unroll
         for (int i = 0; i < P; ++i)
-          if (abs(P * lane + i - tt) <= kWin - 1) sc[i] = -INFINITY;
+          if (abs(P * lane + i - tt) <= kWin - 1) key[i] = 0ull;
       }
     }
     // starts = [0] + sorted cuts, then L (the cuts are wave-uniform)
