@@ -160,148 +160,6 @@ __device__ __forceinline__ bool compress_tile(const CompressArgs &a, int &tile, 
 }
 
 // -------------------------------------------------------------------------------------------
-// 1. stats
-// -------------------------------------------------------------------------------------------
-template <int D>
-__global__ __launch_bounds__(256) void stats_kernel(CompressArgs a) {
-  int tile, h;
-  run_order(tile, h);
-  int b, c0, L;
-  if (!compress_tile(a, tile, b, c0, L)) return;
-  const int tid = threadIdx.x;
-  const int t = tile * 64 + (tid >> 2), q = tid & 3;
-  const bool valid = t < L;
-  float kmn = INFINITY, kmx = -INFINITY, vmn = INFINITY, vmx = -INFINITY, bad = 0.f;
-  int asum = 0;
-  long long bsum = 0;
-  if (valid) {
-    const size_t row = (size_t)(c0 + t) * a.stride_tok + (size_t)h * a.stride_head;
-    const uint4 *kr = reinterpret_cast<const uint4 *>(a.k + row);
-    const uint4 *vr = reinterpret_cast<const uint4 *>(a.v + row);
-#pragma unroll
-    for (int c = 0; c < D / 32; ++c) {
-      const uint4 kw = kr[q + 4 * c], vw = vr[q + 4 * c];
-      const uint32_t ks[4] = {kw.x, kw.y, kw.z, kw.w};
-      const uint32_t vs[4] = {vw.x, vw.y, vw.z, vw.w};
-      unsigned int bpart = 0;   // <= 8 * 2^28 < 2^32
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float x = half_bits_to_float(e & 1 ? ks[e >> 1] >> 16 : ks[e >> 1] & 0xFFFFu);
-        const float y = half_bits_to_float(e & 1 ? vs[e >> 1] >> 16 : vs[e >> 1] & 0xFFFFu);
-        kmn = fminf(kmn, x);
-        kmx = fmaxf(kmx, x);
-        vmn = fminf(vmn, y);
-        vmx = fmaxf(vmx, y);
-        bad = fmaf(x, 0.f, bad);
-        bad = fmaf(y, 0.f, bad);
-        const int n = dgq_fixed_point(x);
-        asum += n;
-        bpart += (unsigned int)(n * n);
-      }
-      bsum += bpart;
-    }
-  }
-#pragma unroll
-  for (int o = 1; o <= 2; o <<= 1) {
-    asum += __shfl_xor(asum, o);
-    bsum += __shfl_xor(bsum, o);
-  }
-  if (valid && q == 0) {
-    const size_t idx = (size_t)h * a.total + c0 + t;
-    a.ws_a[idx] = asum;
-    a.ws_b[idx] = bsum;
-  }
-  // sub-block extrema: wave w covers tokens tile*64 + 16w .. +15
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    kmn = fminf(kmn, __shfl_xor(kmn, o));
-    kmx = fmaxf(kmx, __shfl_xor(kmx, o));
-    vmn = fminf(vmn, __shfl_xor(vmn, o));
-    vmx = fmaxf(vmx, __shfl_xor(vmx, o));
-  }
-  const int w = tid >> 6;
-  const int sb = tile * 4 + w;
-  if ((tid & 63) == 0 && sb * 16 < L) a.ws_ext[((size_t)b * a.hkv + h) * a.nsub + sb] = make_float4(kmn, kmx, vmn, vmx);
-  const bool any_bad = __ballot(!(bad == 0.f)) != 0ull;
-  if (any_bad && (tid & 63) == 0) atomicAdd(a.cache.status + 1, 1ull);
-}
-
-// -------------------------------------------------------------------------------------------
-// 2. scores
-// -------------------------------------------------------------------------------------------
-template <int D>
-__global__ __launch_bounds__(256) void scores_kernel(CompressArgs a) {
-  const int tile = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  int c0, L;
-  bool bad_seq;
-  seq_range(a.cu, b, a.max_seq_len, a.total, c0, L, bad_seq);
-  if (L < 2 * kWin || tile * 256 > L - kWin) return;
-  __shared__ int sa[256 + 2 * kWin];
-  __shared__ long long sbm[256 + 2 * kWin];
-  __shared__ double best_s[4];
-  __shared__ int best_t[4];
-  const int tid = threadIdx.x;
-  const int base = tile * 256 - kWin;
-  for (int i = tid; i < 256 + 2 * kWin; i += 256) {
-    const int tok = base + i;
-    if (tok >= 0 && tok < L) {
-      const size_t idx = (size_t)h * a.total + c0 + tok;
-      sa[i] = a.ws_a[idx];
-      sbm[i] = a.ws_b[idx];
-    } else {
-      sa[i] = 0;
-      sbm[i] = 0;
-    }
-  }
-  __syncthreads();
-  const int t = tile * 256 + tid;
-  double score = -INFINITY;
-  int tb = INT_MAX;
-  if (t >= kWin && t <= L - kWin) {
-    long long al = 0, ar = 0, bl = 0, br = 0;
-#pragma unroll
-    for (int i = 0; i < kWin; ++i) {
-      al += sa[tid + i];
-      bl += sbm[tid + i];
-      ar += sa[tid + kWin + i];
-      br += sbm[tid + kWin + i];
-    }
-    const long long nel = (long long)kWin * D;
-    const long long ql = nel * bl - al * al;
-    const long long qr = nel * br - ar * ar;
-    const long long hi = ql > qr ? ql : qr, lo = ql > qr ? qr : ql;
-    score = (double)hi < a.qfloor ? -INFINITY : (double)(hi + 1) / (double)(lo + 1);
-    a.ws_score[(size_t)h * a.total + c0 + t] = score;
-    tb = t;
-  }
-  // best (score, smallest t) of the tile
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const double s2 = __shfl_xor(score, o);
-    const int t2 = __shfl_xor(tb, o);
-    if (s2 > score || (s2 == score && t2 < tb)) {
-      score = s2;
-      tb = t2;
-    }
-  }
-  if ((tid & 63) == 0) {
-    best_s[tid >> 6] = score;
-    best_t[tid >> 6] = tb;
-  }
-  __syncthreads();
-  if (tid == 0) {
-    double s = best_s[0];
-    int tt = best_t[0];
-    for (int w = 1; w < 4; ++w)
-      if (best_s[w] > s || (best_s[w] == s && best_t[w] < tt)) {
-        s = best_s[w];
-        tt = best_t[w];
-      }
-    a.ws_tile[((size_t)b * a.hkv + h) * a.ntile + tile] = make_double2(s, (double)tt);
-  }
-}
-
-// -------------------------------------------------------------------------------------------
 // wave reductions with DPP row operations and lane reads (no LDS)
 // -------------------------------------------------------------------------------------------
 template <int C>
@@ -410,6 +268,190 @@ __device__ __forceinline__ float4 wave_minmax(float4 r) {
     o.w = fmaxf(o.w, readlane_f(r.w, 16 * q));
   }
   return o;
+}
+
+// -------------------------------------------------------------------------------------------
+// exact per-element arithmetic shared by the passes over the fp16 input
+// -------------------------------------------------------------------------------------------
+// A pass over the input spends most of its instructions on each element, so each step is kept to
+// a few instructions while staying exact: packed fp16 min/max and non-finite tests, the
+// fixed-point image by one fused multiply-add into float32's round-to-integer range, sums of n and
+// n^2 by 16-bit dot products, and the codes by the float-to-byte conversion.
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef short short2_t __attribute__((ext_vector_type(2)));
+constexpr short2_t kOnes2 = {1, 1};
+__device__ __forceinline__ half2_t as_half2(uint32_t w) { return __builtin_bit_cast(half2_t, w); }
+
+// dgq_fixed_point(x) for every x: the clamped value times 512 is exact, and adding 1.5 * 2^23
+// rounds it to the nearest integer (ties to even) in one step, that integer then being the low
+// bits of the sum (|x * 512| <= 2^14 < 2^22).
+__device__ __forceinline__ int fixed_point_fma(float x) {
+  const float c = fminf(fmaxf(x, -32.0f), 32.0f);
+  return __float_as_int(fmaf(c, 512.0f, 12582912.0f)) - 0x4B400000;
+}
+
+// The code bytes of four values (byte e from x[e], with its segment's min and 1 / scale), equal to
+// dgq_encode_value's for every input of dgq_compress: subtract and multiply as there, then the
+// float-to-byte conversion, which rounds to nearest even, saturates to [0, 255] and takes NaN to 0.
+// The clamp to [0, levels] never binds here: a segment's min and max are those of its own values,
+// so 0 <= x - mn <= mx - mn and u <= levels * (1 + 2^-22) < levels + 1/2, and a NaN gives 0 in both.
+// The byte is then shifted by the code of the minimum: -128 flips its top bit, -127 adds 129
+// modulo 256.
+__device__ __forceinline__ uint32_t encode4(const float (&x)[4], const float (&mn)[4], const float (&inv)[4],
+                                            bool marker) {
+#pragma clang fp contract(off)
+  uint32_t w = 0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float dlt = x[e] - mn[e];
+    const float u = dlt * inv[e];
+    w = __builtin_amdgcn_cvt_pk_u8_f32(u, e, w);
+  }
+  return marker ? (((w & 0x7F7F7F7Fu) + 0x01010101u) ^ ((w ^ 0x81818181u) & 0x80808080u)) : (w ^ 0x80808080u);
+}
+
+// -------------------------------------------------------------------------------------------
+// 1. stats
+// -------------------------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void stats_kernel(CompressArgs a) {
+  int tile, h;
+  run_order(tile, h);
+  int b, c0, L;
+  if (!compress_tile(a, tile, b, c0, L)) return;
+  const int tid = threadIdx.x;
+  const int t = tile * 64 + (tid >> 2), q = tid & 3;
+  const bool valid = t < L;
+  float kmn = INFINITY, kmx = -INFINITY, vmn = INFINITY, vmx = -INFINITY;
+  bool bad = false;
+  int asum = 0;
+  long long bsum = 0;
+  if (valid) {
+    const size_t row = (size_t)(c0 + t) * a.stride_tok + (size_t)h * a.stride_head;
+    const uint4 *kr = reinterpret_cast<const uint4 *>(a.k + row);
+    const uint4 *vr = reinterpret_cast<const uint4 *>(a.v + row);
+    const half2_t zero2 = {(_Float16)0.0f, (_Float16)0.0f};
+    half2_t vmn2 = {(_Float16)INFINITY, (_Float16)INFINITY}, vmx2 = -vmn2, bad2 = zero2;
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c) {
+      const uint4 kw = kr[q + 4 * c], vw = vr[q + 4 * c];
+      const uint32_t ks[4] = {kw.x, kw.y, kw.z, kw.w};
+      const uint32_t vs[4] = {vw.x, vw.y, vw.z, vw.w};
+      int bpart = 0;   // sum of 8 squares <= 2^31: wraps as int32, exact read as uint32
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const half2_t kx = as_half2(ks[e]), vx = as_half2(vs[e]);
+        vmn2 = __builtin_elementwise_min(vmn2, vx);
+        vmx2 = __builtin_elementwise_max(vmx2, vx);
+        bad2 = __builtin_elementwise_fma(kx, zero2, bad2);   // NaN once any value is not finite
+        bad2 = __builtin_elementwise_fma(vx, zero2, bad2);
+        const float x0 = (float)kx[0], x1 = (float)kx[1];
+        kmn = fminf(kmn, fminf(x0, x1));
+        kmx = fmaxf(kmx, fmaxf(x0, x1));
+        const uint32_t n01 = __builtin_amdgcn_perm((uint32_t)fixed_point_fma(x1), (uint32_t)fixed_point_fma(x0),
+                                                   0x05040100u);
+        const short2_t n2 = __builtin_bit_cast(short2_t, n01);
+        asum = __builtin_amdgcn_sdot2(n2, kOnes2, asum, false);
+        bpart = __builtin_amdgcn_sdot2(n2, n2, bpart, false);
+      }
+      bsum += (unsigned int)bpart;
+    }
+    vmn = fminf((float)vmn2[0], (float)vmn2[1]);
+    vmx = fmaxf((float)vmx2[0], (float)vmx2[1]);
+    bad = !(bad2[0] == (_Float16)0.0f && bad2[1] == (_Float16)0.0f);
+  }
+  // the four lanes of a token (one quad) by DPP quad swaps
+  asum += dpp_i<kQuadSwap1>(asum);
+  bsum += (long long)dpp_u64<kQuadSwap1>((unsigned long long)bsum);
+  asum += dpp_i<kQuadSwap2>(asum);
+  bsum += (long long)dpp_u64<kQuadSwap2>((unsigned long long)bsum);
+  if (valid && q == 0) {
+    const size_t idx = (size_t)h * a.total + c0 + t;
+    a.ws_a[idx] = asum;
+    a.ws_b[idx] = bsum;
+  }
+  // sub-block extrema: wave w covers tokens tile*64 + 16w .. +15
+  const float4 ext = wave_minmax(make_float4(kmn, kmx, vmn, vmx));
+  const int w = tid >> 6;
+  const int sb = tile * 4 + w;
+  if ((tid & 63) == 0 && sb * 16 < L) a.ws_ext[((size_t)b * a.hkv + h) * a.nsub + sb] = ext;
+  const bool any_bad = __ballot(bad) != 0ull;
+  if (any_bad && (tid & 63) == 0) atomicAdd(a.cache.status + 1, 1ull);
+}
+
+// -------------------------------------------------------------------------------------------
+// 2. scores
+// -------------------------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void scores_kernel(CompressArgs a) {
+  const int tile = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  int c0, L;
+  bool bad_seq;
+  seq_range(a.cu, b, a.max_seq_len, a.total, c0, L, bad_seq);
+  if (L < 2 * kWin || tile * 256 > L - kWin) return;
+  __shared__ int sa[256 + 2 * kWin];
+  __shared__ long long sbm[256 + 2 * kWin];
+  __shared__ double best_s[4];
+  __shared__ int best_t[4];
+  const int tid = threadIdx.x;
+  const int base = tile * 256 - kWin;
+  for (int i = tid; i < 256 + 2 * kWin; i += 256) {
+    const int tok = base + i;
+    if (tok >= 0 && tok < L) {
+      const size_t idx = (size_t)h * a.total + c0 + tok;
+      sa[i] = a.ws_a[idx];
+      sbm[i] = a.ws_b[idx];
+    } else {
+      sa[i] = 0;
+      sbm[i] = 0;
+    }
+  }
+  __syncthreads();
+  const int t = tile * 256 + tid;
+  double score = -INFINITY;
+  int tb = INT_MAX;
+  if (t >= kWin && t <= L - kWin) {
+    long long al = 0, ar = 0, bl = 0, br = 0;
+#pragma unroll
+    for (int i = 0; i < kWin; ++i) {
+      al += sa[tid + i];
+      bl += sbm[tid + i];
+      ar += sa[tid + kWin + i];
+      br += sbm[tid + kWin + i];
+    }
+    const long long nel = (long long)kWin * D;
+    const long long ql = nel * bl - al * al;
+    const long long qr = nel * br - ar * ar;
+    const long long hi = ql > qr ? ql : qr, lo = ql > qr ? qr : ql;
+    score = (double)hi < a.qfloor ? -INFINITY : (double)(hi + 1) / (double)(lo + 1);
+    a.ws_score[(size_t)h * a.total + c0 + t] = score;
+    tb = t;
+  }
+  // best (score, smallest t) of the tile
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const double s2 = __shfl_xor(score, o);
+    const int t2 = __shfl_xor(tb, o);
+    if (s2 > score || (s2 == score && t2 < tb)) {
+      score = s2;
+      tb = t2;
+    }
+  }
+  if ((tid & 63) == 0) {
+    best_s[tid >> 6] = score;
+    best_t[tid >> 6] = tb;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    double s = best_s[0];
+    int tt = best_t[0];
+    for (int w = 1; w < 4; ++w)
+      if (best_s[w] > s || (best_s[w] == s && best_t[w] < tt)) {
+        s = best_s[w];
+        tt = best_t[w];
+      }
+    a.ws_tile[((size_t)b * a.hkv + h) * a.ntile + tile] = make_double2(s, (double)tt);
+  }
 }
 
 // -------------------------------------------------------------------------------------------
@@ -951,6 +993,7 @@ __global__ __launch_bounds__(256) void encode_kernel(CompressArgs a) {
   __shared__ int s_start[kMaxSegCap];
   __shared__ float s_kmin[kMaxSegCap], s_kinv[kMaxSegCap], s_vmin[kMaxSegCap], s_vinv[kMaxSegCap];
   __shared__ int segidx[kChunk];
+  __shared__ float2 kprm[kChunk], vprm[kChunk];   // per-token segment (min, 1 / scale) of K and V
   __shared__ uint16_t vt[kChunk * VROW];
   const int ns = a.cache.nseg[bh];
   if (tid < ns) {
@@ -967,6 +1010,8 @@ __global__ __launch_bounds__(256) void encode_kernel(CompressArgs a) {
     int idx = 0;
     for (int k = 1; k < ns; ++k) idx += tok >= s_start[k] ? 1 : 0;
     segidx[tid] = idx;
+    kprm[tid] = make_float2(s_kmin[idx], s_kinv[idx]);
+    vprm[tid] = make_float2(s_vmin[idx], s_vinv[idx]);
   }
   // stage the value rows of the chunk
   constexpr int VPR = D / 8;   // uint4 per row
@@ -986,30 +1031,32 @@ __global__ __launch_bounds__(256) void encode_kernel(CompressArgs a) {
   const int32_t *bt = a.block_table + (size_t)b * a.max_blocks;
   const int nblk_seq = (L + BS - 1) / BS;
   const size_t tile_bytes = (size_t)BS * D;
+  const bool marker = a.fmt.marker != 0;
 
-  const float lv = a.fmt.levels;
-  const int low = a.fmt.low;
   // keys: one unit = 16 channels of one token = 16 contiguous bytes of the tile
   constexpr int KU = kChunk * D / 16;
   for (int u = tid; u < KU; u += 256) {
     const int tau = u / (D / 16), d0 = 16 * (u % (D / 16));
     const int tok = t0 + tau;
     if (tok >= L) continue;
-    const int sg = segidx[tau];
-    const float mn = s_kmin[sg], inv = s_kinv[sg];
+    const float2 kp = kprm[tau];
+    const float mn[4] = {kp.x, kp.x, kp.x, kp.x};
+    const float inv[4] = {kp.y, kp.y, kp.y, kp.y};
     const uint16_t *src = a.k + (size_t)(c0 + tok) * a.stride_tok + (size_t)h * a.stride_head + d0;
     const uint4 w0 = load_last_use(src), w1 = load_last_use(src + 8);
     const uint32_t ws[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-    uint32_t outw[4] = {0u, 0u, 0u, 0u};
+    uint32_t outw[4];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const float x = half_bits_to_float(e & 1 ? ws[e >> 1] >> 16 : ws[e >> 1] & 0xFFFFu);
-      const uint32_t c = (uint32_t)(dgq_encode_value(x, mn, inv, lv, low) & 0xFF);
-      outw[e >> 2] |= c << (8 * (e & 3));
+    for (int g = 0; g < 4; ++g) {
+      const half2_t x01 = as_half2(ws[2 * g]), x23 = as_half2(ws[2 * g + 1]);
+      const float x[4] = {(float)x01[0], (float)x01[1], (float)x23[0], (float)x23[1]};
+      outw[g] = encode4(x, mn, inv, marker);
     }
     // marker format: the first key byte of every segment but the first is its marker
-    if (a.fmt.marker && d0 == 0 && sg > 0 && s_start[sg] == tok)
-      outw[0] = (outw[0] & ~0xFFu) | dgq_marker_byte(outw[0] & 0xFFu);
+    if (marker && d0 == 0) {
+      const int sg = segidx[tau];
+      if (sg > 0 && s_start[sg] == tok) outw[0] = (outw[0] & ~0xFFu) | dgq_marker_byte(outw[0] & 0xFFu);
+    }
     bool bad_blk = false;
     const int blk = checked_block(bt[tok / BS], a.cache.num_blocks, bad_blk);
     if (bad_blk) {
@@ -1020,7 +1067,9 @@ __global__ __launch_bounds__(256) void encode_kernel(CompressArgs a) {
     store_stream(dst, outw);
   }
 
-  // values: one unit = 16 tokens of one channel = 16 contiguous bytes of the tile
+  // values: one unit = 16 tokens of one channel = 16 contiguous bytes of the tile; the code of a
+  // token past L is 0
+  const int last = L - 1 - t0;   // last token of the sequence in this chunk (>= 0)
   for (int u = tid; u < KU; u += 256) {
     int d, blk_local, taus[16];
     if constexpr (BS == 64) {
@@ -1037,17 +1086,22 @@ __global__ __launch_bounds__(256) void encode_kernel(CompressArgs a) {
     }
     const int lblk = (t0 + (BS == 64 ? 0 : 16 * blk_local)) / BS;
     if (lblk >= nblk_seq) continue;
-    uint32_t outw[4] = {0u, 0u, 0u, 0u};
+    uint32_t outw[4];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int tau = taus[e];
-      uint32_t c = 0u;
-      if (t0 + tau < L) {
-        const int sg = segidx[tau];
-        const float x = half_bits_to_float(vt[tau * VROW + d]);
-        c = (uint32_t)(dgq_encode_value(x, s_vmin[sg], s_vinv[sg], lv, low) & 0xFF);
+    for (int g = 0; g < 4; ++g) {
+      float x[4], mn[4], inv[4];
+      uint32_t past = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int tau = taus[4 * g + e];
+        const int tc = min(tau, last);
+        const float2 pr = vprm[tc];
+        x[e] = half_bits_to_float(vt[tc * VROW + d]);
+        mn[e] = pr.x;
+        inv[e] = pr.y;
+        past |= tau <= last ? 0u : 0xFFu << (8 * e);
       }
-      outw[e >> 2] |= c << (8 * (e & 3));
+      outw[g] = encode4(x, mn, inv, marker) & ~past;
     }
     bool bad_blk = false;
     const int blk = checked_block(bt[lblk], a.cache.num_blocks, bad_blk);
@@ -1065,7 +1119,7 @@ __global__ __launch_bounds__(256) void encode_kernel(CompressArgs a) {
 
   // boundary bits: 8 bytes per chunk (one 64-token block, or four 16-token blocks); none in the
   // marker format
-  if (!a.fmt.marker && tid < kChunk / 8) {
+  if (!marker && tid < kChunk / 8) {
     const int tok0 = t0 + 8 * tid;
     const int lblk = tok0 / BS;
     if (lblk < nblk_seq) {
@@ -1094,47 +1148,10 @@ __global__ __launch_bounds__(256) void encode_kernel(CompressArgs a) {
 // precision: exact integer moments, the window statistic as an exact double, the greedy cuts
 // with the same tie rule, min/max folds (order-free once -0 is stored as +0), the same encoding
 // steps and the same tile layout.  The results are bit-identical to the four-pass path.
-// One workgroup does all of a head's element work on one compute unit, so the per-element
-// arithmetic is kept short: packed fp16 min/max and non-finite tests, the fixed-point image by
-// one fused multiply-add into the round-to-integer range of float32, 24-bit integer squares, and
-// the hardware float-to-byte conversion for the codes.
 constexpr int kShortThreads = 1024;
 constexpr int kShortElems = 32768;   // longest sequence * head_dim: 256 tokens at 128, 512 at 64
 template <int D>
 constexpr int short_tokens() { return kShortElems / D; }
-
-typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
-typedef short short2_t __attribute__((ext_vector_type(2)));
-constexpr short2_t kOnes2 = {1, 1};
-__device__ __forceinline__ half2_t as_half2(uint32_t w) { return __builtin_bit_cast(half2_t, w); }
-
-// dgq_fixed_point(x) for every x: the clamped value times 512 is exact, and adding 1.5 * 2^23
-// rounds it to the nearest integer (ties to even) in one step, that integer then being the low
-// bits of the sum (|x * 512| <= 2^14 < 2^22).
-__device__ __forceinline__ int fixed_point_fma(float x) {
-  const float c = fminf(fmaxf(x, -32.0f), 32.0f);
-  return __float_as_int(fmaf(c, 512.0f, 12582912.0f)) - 0x4B400000;
-}
-
-// The code bytes of four values (byte e from x[e], with its segment's min and 1 / scale), equal to
-// dgq_encode_value's for every input of dgq_compress: subtract and multiply as there, then the
-// float-to-byte conversion, which rounds to nearest even, saturates to [0, 255] and takes NaN to 0.
-// The clamp to [0, levels] never binds here: a segment's min and max are those of its own values,
-// so 0 <= x - mn <= mx - mn and u <= levels * (1 + 2^-22) < levels + 1/2, and a NaN gives 0 in both.
-// The byte is then shifted by the code of the minimum: -128 flips its top bit, -127 adds 129
-// modulo 256.
-__device__ __forceinline__ uint32_t encode4(const float (&x)[4], const float (&mn)[4], const float (&inv)[4],
-                                            bool marker) {
-#pragma clang fp contract(off)
-  uint32_t w = 0;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const float dlt = x[e] - mn[e];
-    const float u = dlt * inv[e];
-    w = __builtin_amdgcn_cvt_pk_u8_f32(u, e, w);
-  }
-  return marker ? (((w & 0x7F7F7F7Fu) + 0x01010101u) ^ ((w ^ 0x81818181u) & 0x80808080u)) : (w ^ 0x80808080u);
-}
 
 template <int D, int BS>
 __global__ __launch_bounds__(kShortThreads) void compress_short_kernel(CompressArgs a) {
