@@ -186,6 +186,8 @@ __device__ __forceinline__ double readlane_d(double x, int l) {
 }
 // DPP controls: swap neighbours, swap pairs (within quads), rotate a 16-lane row by 4 and by 8
 constexpr int kQuadSwap1 = 0xB1, kQuadSwap2 = 0x4E, kRowRor4 = 0x124, kRowRor8 = 0x128;
+// mirror each half row of 8 lanes (lane i <-> 7 - i): after the quad swaps, the other quad's value
+constexpr int kHalfMirror = 0x141;
 
 // (score desc, t asc): true if (s2, t2) comes first
 __device__ __forceinline__ bool better(double s2, int t2, double s, int t) {
@@ -313,70 +315,92 @@ __device__ __forceinline__ uint32_t encode4(const float (&x)[4], const float (&m
 // -------------------------------------------------------------------------------------------
 // 1. stats
 // -------------------------------------------------------------------------------------------
+// Each load instruction of a wave reads whole 2 D-byte rows: LPR = D / 8 lanes per token row (16 B
+// each), TPI = 64 / LPR tokens per instruction, NI = 16 / TPI instructions for the wave's 16
+// tokens (one 16-token sub-block).  A lane keeps per-token moment sums for its NI tokens; the LPR
+// lanes of a row are combined by DPP, and the extrema and the non-finite test cover the wave.
 template <int D>
 __global__ __launch_bounds__(256) void stats_kernel(CompressArgs a) {
+  constexpr int LPR = D / 8, TPI = 64 / LPR, NI = kWin / TPI;
   int tile, h;
   run_order(tile, h);
   int b, c0, L;
   if (!compress_tile(a, tile, b, c0, L)) return;
-  const int tid = threadIdx.x;
-  const int t = tile * 64 + (tid >> 2), q = tid & 3;
-  const bool valid = t < L;
-  float kmn = INFINITY, kmx = -INFINITY, vmn = INFINITY, vmx = -INFINITY;
-  bool bad = false;
-  int asum = 0;
-  long long bsum = 0;
-  if (valid) {
-    const size_t row = (size_t)(c0 + t) * a.stride_tok + (size_t)h * a.stride_head;
-    const uint4 *kr = reinterpret_cast<const uint4 *>(a.k + row);
-    const uint4 *vr = reinterpret_cast<const uint4 *>(a.v + row);
-    const half2_t zero2 = {(_Float16)0.0f, (_Float16)0.0f};
-    half2_t vmn2 = {(_Float16)INFINITY, (_Float16)INFINITY}, vmx2 = -vmn2, bad2 = zero2;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int r = lane / LPR, col = lane % LPR;
+  float kmn = INFINITY, kmx = -INFINITY;
+  int asum[NI];
+  long long bsum[NI];
+  const half2_t zero2 = {(_Float16)0.0f, (_Float16)0.0f};
+  half2_t vmn2 = {(_Float16)INFINITY, (_Float16)INFINITY}, vmx2 = -vmn2, bad2 = zero2;
+  {
+    uint4 kr[NI], vr[NI];
 #pragma unroll
-    for (int c = 0; c < D / 32; ++c) {
-      const uint4 kw = kr[q + 4 * c], vw = vr[q + 4 * c];
-      const uint32_t ks[4] = {kw.x, kw.y, kw.z, kw.w};
-      const uint32_t vs[4] = {vw.x, vw.y, vw.z, vw.w};
-      int bpart = 0;   // sum of 8 squares <= 2^31: wraps as int32, exact read as uint32
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const half2_t kx = as_half2(ks[e]), vx = as_half2(vs[e]);
-        vmn2 = __builtin_elementwise_min(vmn2, vx);
-        vmx2 = __builtin_elementwise_max(vmx2, vx);
-        bad2 = __builtin_elementwise_fma(kx, zero2, bad2);   // NaN once any value is not finite
-        bad2 = __builtin_elementwise_fma(vx, zero2, bad2);
-        const float x0 = (float)kx[0], x1 = (float)kx[1];
-        kmn = fminf(kmn, fminf(x0, x1));
-        kmx = fmaxf(kmx, fmaxf(x0, x1));
-        const uint32_t n01 = __builtin_amdgcn_perm((uint32_t)fixed_point_fma(x1), (uint32_t)fixed_point_fma(x0),
-                                                   0x05040100u);
-        const short2_t n2 = __builtin_bit_cast(short2_t, n01);
-        asum = __builtin_amdgcn_sdot2(n2, kOnes2, asum, false);
-        bpart = __builtin_amdgcn_sdot2(n2, n2, bpart, false);
+    for (int c = 0; c < NI; ++c) {
+      const int t = tile * 64 + kWin * w + TPI * c + r;
+      kr[c] = vr[c] = make_uint4(0u, 0u, 0u, 0u);
+      if (t < L) {
+        const size_t off = (size_t)(c0 + t) * a.stride_tok + (size_t)h * a.stride_head + 8 * col;
+        kr[c] = *reinterpret_cast<const uint4 *>(a.k + off);
+        vr[c] = *reinterpret_cast<const uint4 *>(a.v + off);
       }
-      bsum += (unsigned int)bpart;
     }
-    vmn = fminf((float)vmn2[0], (float)vmn2[1]);
-    vmx = fmaxf((float)vmx2[0], (float)vmx2[1]);
-    bad = !(bad2[0] == (_Float16)0.0f && bad2[1] == (_Float16)0.0f);
+#pragma unroll
+    for (int c = 0; c < NI; ++c) {
+      const int t = tile * 64 + kWin * w + TPI * c + r;
+      const uint32_t ks[4] = {kr[c].x, kr[c].y, kr[c].z, kr[c].w};
+      const uint32_t vs[4] = {vr[c].x, vr[c].y, vr[c].z, vr[c].w};
+      int as = 0, bpart = 0;   // sum of 8 squares <= 2^31: wraps as int32, exact read as uint32
+      if (t < L) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const half2_t kx = as_half2(ks[e]), vx = as_half2(vs[e]);
+          vmn2 = __builtin_elementwise_min(vmn2, vx);
+          vmx2 = __builtin_elementwise_max(vmx2, vx);
+          bad2 = __builtin_elementwise_fma(kx, zero2, bad2);   // NaN once any value is not finite
+          bad2 = __builtin_elementwise_fma(vx, zero2, bad2);
+          const float x0 = (float)kx[0], x1 = (float)kx[1];
+          kmn = fminf(kmn, fminf(x0, x1));
+          kmx = fmaxf(kmx, fmaxf(x0, x1));
+          const uint32_t n01 = __builtin_amdgcn_perm((uint32_t)fixed_point_fma(x1), (uint32_t)fixed_point_fma(x0),
+                                                     0x05040100u);
+          const short2_t n2 = __builtin_bit_cast(short2_t, n01);
+          as = __builtin_amdgcn_sdot2(n2, kOnes2, as, false);
+          bpart = __builtin_amdgcn_sdot2(n2, n2, bpart, false);
+        }
+      }
+      asum[c] = as;
+      bsum[c] = (long long)(unsigned int)bpart;
+    }
   }
-  // the four lanes of a token (one quad) by DPP quad swaps
-  asum += dpp_i<kQuadSwap1>(asum);
-  bsum += (long long)dpp_u64<kQuadSwap1>((unsigned long long)bsum);
-  asum += dpp_i<kQuadSwap2>(asum);
-  bsum += (long long)dpp_u64<kQuadSwap2>((unsigned long long)bsum);
-  if (valid && q == 0) {
-    const size_t idx = (size_t)h * a.total + c0 + t;
-    a.ws_a[idx] = asum;
-    a.ws_b[idx] = bsum;
+  // the LPR lanes of a row: quads, then half rows, then (LPR 16) whole rows
+#pragma unroll
+  for (int c = 0; c < NI; ++c) {
+    asum[c] += dpp_i<kQuadSwap1>(asum[c]);
+    bsum[c] += (long long)dpp_u64<kQuadSwap1>((unsigned long long)bsum[c]);
+    asum[c] += dpp_i<kQuadSwap2>(asum[c]);
+    bsum[c] += (long long)dpp_u64<kQuadSwap2>((unsigned long long)bsum[c]);
+    asum[c] += dpp_i<kHalfMirror>(asum[c]);
+    bsum[c] += (long long)dpp_u64<kHalfMirror>((unsigned long long)bsum[c]);
+    if constexpr (LPR == 16) {
+      asum[c] += dpp_i<kRowRor8>(asum[c]);
+      bsum[c] += (long long)dpp_u64<kRowRor8>((unsigned long long)bsum[c]);
+    }
+    const int t = tile * 64 + kWin * w + TPI * c + r;
+    if (col == 0 && t < L) {
+      const size_t idx = (size_t)h * a.total + c0 + t;
+      a.ws_a[idx] = asum[c];
+      a.ws_b[idx] = bsum[c];
+    }
   }
   // sub-block extrema: wave w covers tokens tile*64 + 16w .. +15
+  const float vmn = fminf((float)vmn2[0], (float)vmn2[1]);
+  const float vmx = fmaxf((float)vmx2[0], (float)vmx2[1]);
   const float4 ext = wave_minmax(make_float4(kmn, kmx, vmn, vmx));
-  const int w = tid >> 6;
   const int sb = tile * 4 + w;
-  if ((tid & 63) == 0 && sb * 16 < L) a.ws_ext[((size_t)b * a.hkv + h) * a.nsub + sb] = ext;
-  const bool any_bad = __ballot(bad) != 0ull;
-  if (any_bad && (tid & 63) == 0) atomicAdd(a.cache.status + 1, 1ull);
+  if (lane == 0 && sb * 16 < L) a.ws_ext[((size_t)b * a.hkv + h) * a.nsub + sb] = ext;
+  const bool bad = !(bad2[0] == (_Float16)0.0f && bad2[1] == (_Float16)0.0f);
+  if (__ballot(bad) != 0ull && lane == 0) atomicAdd(a.cache.status + 1, 1ull);
 }
 
 // -------------------------------------------------------------------------------------------
