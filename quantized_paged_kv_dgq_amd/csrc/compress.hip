@@ -45,6 +45,7 @@ struct CompressArgs {
   double *ws_score;     // [hkv][total]
   float4 *ws_ext;       // [batch][hkv][nsub]: kmin, kmax, vmin, vmax
   double2 *ws_tile;     // [batch][hkv][ntile]: (score, t as double)
+  float4 *ws_text;      // [batch][hkv][ntile]: K min, K max, V min, V max of each 256-token tile
   int4 *tile_map;       // ragged batches: [map_tiles] {sequence, tile, first token, length}; else null
   dgq_cache_t cache;
 };
@@ -412,12 +413,25 @@ __global__ __launch_bounds__(256) void scores_kernel(CompressArgs a) {
   int c0, L;
   bool bad_seq;
   seq_range(a.cu, b, a.max_seq_len, a.total, c0, L, bad_seq);
+  if (tile * 256 >= L) return;
+  const int tid = threadIdx.x;
+  const size_t bh = (size_t)b * a.hkv + h;
+  // the tile's K/V extrema from its sub-blocks (for the segment ranges of the selection)
+  if (tid < 64) {
+    const int sb = 16 * tile + (tid & 15);
+    const float4 ident = make_float4(INFINITY, -INFINITY, INFINITY, -INFINITY);
+    float4 x = ident;
+    if (tid < 16 && kWin * sb < L) x = a.ws_ext[bh * a.nsub + sb];
+    const float4 r = wave_minmax(x);
+    if (tid == 0) a.ws_text[bh * a.ntile + tile] = r;
+  }
   if (L < 2 * kWin || tile * 256 > L - kWin) return;
   __shared__ int sa[256 + 2 * kWin];
   __shared__ long long sbm[256 + 2 * kWin];
+  __shared__ int wa[256 + kWin];           // window sums: wa[i] = sa[i] + ... + sa[i + 15]
+  __shared__ long long wbm[256 + kWin];
   __shared__ double best_s[4];
   __shared__ int best_t[4];
-  const int tid = threadIdx.x;
   const int base = tile * 256 - kWin;
   for (int i = tid; i < 256 + 2 * kWin; i += 256) {
     const int tok = base + i;
@@ -431,36 +445,35 @@ __global__ __launch_bounds__(256) void scores_kernel(CompressArgs a) {
     }
   }
   __syncthreads();
+  for (int i = tid; i < 256 + kWin; i += 256) {
+    int A = 0;
+    long long B = 0;
+#pragma unroll
+    for (int u = 0; u < kWin; ++u) {
+      A += sa[i + u];
+      B += sbm[i + u];
+    }
+    wa[i] = A;
+    wbm[i] = B;
+  }
+  __syncthreads();
   const int t = tile * 256 + tid;
   double score = -INFINITY;
   int tb = INT_MAX;
   if (t >= kWin && t <= L - kWin) {
-    long long al = 0, ar = 0, bl = 0, br = 0;
-#pragma unroll
-    for (int i = 0; i < kWin; ++i) {
-      al += sa[tid + i];
-      bl += sbm[tid + i];
-      ar += sa[tid + kWin + i];
-      br += sbm[tid + kWin + i];
-    }
-    const long long nel = (long long)kWin * D;
-    const long long ql = nel * bl - al * al;
-    const long long qr = nel * br - ar * ar;
-    const long long hi = ql > qr ? ql : qr, lo = ql > qr ? qr : ql;
-    score = (double)hi < a.qfloor ? -INFINITY : (double)(hi + 1) / (double)(lo + 1);
+    // Q = N * sum b - (sum a)^2 of the windows [t - 16, t) and [t, t + 16), exact in double
+    // (|sum a| <= 2^25, N * sum b <= 2^51, the fused result is an integer below 2^51)
+    const double nel = (double)(kWin * D);
+    const double Al = (double)wa[tid], Ar = (double)wa[tid + kWin];
+    const double ql = fma(-Al, Al, nel * (double)wbm[tid]);
+    const double qr = fma(-Ar, Ar, nel * (double)wbm[tid + kWin]);
+    const double hi = fmax(ql, qr), lo = fmin(ql, qr);
+    score = hi < a.qfloor ? -INFINITY : (hi + 1.0) / (lo + 1.0);
     a.ws_score[(size_t)h * a.total + c0 + t] = score;
     tb = t;
   }
   // best (score, smallest t) of the tile
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const double s2 = __shfl_xor(score, o);
-    const int t2 = __shfl_xor(tb, o);
-    if (s2 > score || (s2 == score && t2 < tb)) {
-      score = s2;
-      tb = t2;
-    }
-  }
+  wave_best(score, tb);
   if ((tid & 63) == 0) {
     best_s[tid >> 6] = score;
     best_t[tid >> 6] = tb;
@@ -470,11 +483,11 @@ __global__ __launch_bounds__(256) void scores_kernel(CompressArgs a) {
     double s = best_s[0];
     int tt = best_t[0];
     for (int w = 1; w < 4; ++w)
-      if (best_s[w] > s || (best_s[w] == s && best_t[w] < tt)) {
+      if (better(best_s[w], best_t[w], s, tt)) {
         s = best_s[w];
         tt = best_t[w];
       }
-    a.ws_tile[((size_t)b * a.hkv + h) * a.ntile + tile] = make_double2(s, (double)tt);
+    a.ws_tile[bh * a.ntile + tile] = make_double2(s, (double)tt);
   }
 }
 
@@ -509,14 +522,12 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(CompressArgs a) {
   double2 *gtiles = a.ws_tile + bh * a.ntile;
   const int ntiles = L >= 2 * kWin ? (L - kWin) / 256 + 1 : 0;
   const bool in_lds = ntiles <= kSelTiles;
-  if (in_lds) {
+  if (in_lds && ntiles > 0) {
+    // all loads in flight at once (clamped indices, so every load is in bounds and unconditional)
     constexpr int U = kSelTiles / kSelThreads;
     double2 x[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int c = tid + kSelThreads * u;
-      if (c < ntiles) x[u] = gtiles[c];
-    }
+    for (int u = 0; u < U; ++u) x[u] = gtiles[min(tid + kSelThreads * u, ntiles - 1)];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int c = tid + kSelThreads * u;
@@ -611,9 +622,9 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(CompressArgs a) {
   const int nseg = L > 0 ? nc + 1 : 0;
 
   // ---- every segment's K/V min/max ----
-  // (1) whole sub-blocks, one pass: each thread folds its sub-blocks into the accumulator of the
-  //     segment that holds them, with a batch of loads in flight; then one wave reduction per
-  //     segment.
+  // (1) thread i takes 256-token tile i: a tile inside one segment folds the tile's extrema (from
+  //     the scores pass); a tile that holds a cut folds its whole sub-blocks one by one into the
+  //     accumulator of the segment that holds each; then one wave reduction per segment.
   // (2) a sub-block that a cut splits (cuts are >= 16 apart, so one cut per sub-block; a cut at a
   //     multiple of 16 splits none) is re-read raw by wave c - 1.
   const float4 ident = make_float4(INFINITY, -INFINITY, INFINITY, -INFINITY);
@@ -627,26 +638,42 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(CompressArgs a) {
   __shared__ float4 sraw[kMaxCuts][2];   // cut c: (left part, right part)
   {
     const float4 *ext = a.ws_ext + bh * a.nsub;
-    const int nsub = (L + kWin - 1) / kWin;
+    const float4 *text = a.ws_text + bh * a.ntile;
+    const int ntl = (L + 255) / 256;
     float4 acc[MS];
 #pragma unroll
     for (int j = 0; j < MS; ++j) acc[j] = ident;
-    constexpr int U = 8;
-    for (int i0 = tid; i0 < nsub; i0 += kSelThreads * U) {
-      float4 x[U];
+    auto seg_of = [&](int t) {
+      int j = 0;
+      for (int k = 1; k < nseg; ++k) j += t >= starts[k] ? 1 : 0;
+      return j;
+    };
+    for (int i = tid; i < ntl; i += kSelThreads) {
+      const int t0 = 256 * i, t1 = min(t0 + 256, L);
+      const int j0 = seg_of(t0);
+      if (seg_of(t1 - 1) == j0) {
+        const float4 x = text[i];
 #pragma unroll
-      for (int u = 0; u < U; ++u) x[u] = i0 + kSelThreads * u < nsub ? ext[i0 + kSelThreads * u] : ident;
+        for (int jj = 0; jj < MS; ++jj)
+          if (jj == j0) fold(acc[jj], x);
+      } else {
+        const int nsb = (t1 - t0 + kWin - 1) / kWin;
+        float4 x[16];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int i = i0 + kSelThreads * u;
-        if (i < nsub) {
-          const int t0 = kWin * i, t1 = min(t0 + kWin, L);
-          int j = 0;
-          for (int k = 1; k < nseg; ++k) j += t0 >= starts[k] ? 1 : 0;
-          if (t1 <= starts[j + 1]) {
+        for (int u = 0; u < 16; ++u) {
+          x[u] = ident;
+          if (u < nsb) x[u] = ext[16 * i + u];
+        }
 #pragma unroll
-            for (int jj = 0; jj < MS; ++jj)
-              if (jj == j) fold(acc[jj], x[u]);
+        for (int u = 0; u < 16; ++u) {
+          if (u < nsb) {
+            const int s0 = t0 + kWin * u, s1 = min(s0 + kWin, L);
+            const int j = seg_of(s0);
+            if (s1 <= starts[j + 1]) {
+#pragma unroll
+              for (int jj = 0; jj < MS; ++jj)
+                if (jj == j) fold(acc[jj], x[u]);
+            }
           }
         }
       }
@@ -1559,6 +1586,8 @@ CompressLayout compress_layout(const dgq_params_t *p, int32_t batch, int64_t tot
   off = align_up(off + (size_t)batch * hkv * l.nsub * sizeof(float4), 256);
   l.tile_off = off;
   off = align_up(off + (size_t)batch * hkv * l.ntile * sizeof(double2), 256);
+  l.text_off = off;
+  off = align_up(off + (size_t)batch * hkv * l.ntile * sizeof(float4), 256);
   l.map_tiles = (int64_t)(tot + kChunk - 1) / kChunk + (batch > 0 ? batch : 0);
   l.map_off = off;
   off = align_up(off + (size_t)l.map_tiles * sizeof(int4), 256);
@@ -1642,6 +1671,7 @@ dgq_status_t launch_compress(const dgq_params_t *p, const uint16_t *k, const uin
   a.ws_score = reinterpret_cast<double *>(w + l.score_off);
   a.ws_ext = reinterpret_cast<float4 *>(w + l.ext_off);
   a.ws_tile = reinterpret_cast<double2 *>(w + l.tile_off);
+  a.ws_text = reinterpret_cast<float4 *>(w + l.text_off);
   const int64_t padded = (int64_t)((max_seq_len + 63) / 64) * batch;
   const bool ragged = batch <= kMapThreads && l.map_tiles <= INT_MAX && 5 * l.map_tiles < 4 * padded;
   a.tile_map = ragged ? reinterpret_cast<int4 *>(w + l.map_off) : nullptr;

@@ -78,7 +78,7 @@ dgq_status_t launch_decode(const dgq_params_t *p, const uint16_t *q, const dgq_c
 
 // ---- compress ----
 struct CompressLayout {
-  size_t a_off, b_off, score_off, ext_off, tile_off, map_off, total;
+  size_t a_off, b_off, score_off, ext_off, tile_off, text_off, map_off, total;
   int nsub;    // 16-token sub-blocks per sequence at max_seq_len
   int ntile;   // 256-candidate tiles per sequence at max_seq_len
   int64_t map_tiles;   // bound on the batch's real 64-token tiles: total_tokens / 64 + batch
