@@ -51,6 +51,9 @@
  *     V, block_size 64: n = d/16, r = d%16, j = (tau%16)/4, e = 4*(tau/16) + tau%4
  *                       offset = ((n*4 + j)*16 + r)*16 + e
  *     V, block_size 16: offset = d*16 + tau
+ *     block_size 32: two 16-token tiles one after the other (tokens 0..15, then 16..31), each in
+ *                    the block_size 16 order: offset = (tau/16)*16*head_dim + the 16-token offset
+ *                    of (tau%16, d), for K and for V
  *   A code is the signed byte c in [-128, 127]; the value it stands for is (c + 128) * scale + min
  *   with the (scale, min) of the token's segment.
  *   bits: uint8 [num_blocks][num_kv_heads][block_size/8]; bit (tau % 8) of byte tau/8 is 1 iff
@@ -108,7 +111,8 @@ typedef struct dgq_params {
   int32_t num_kv_heads;  /* >= 1 */
   int32_t num_q_heads;   /* num_kv_heads * G with G in {1, 2, 4}; query head g uses kv head g / G */
   int32_t head_dim;      /* 64 or 128 */
-  int32_t block_size;    /* tokens per physical block: 16 or 64 */
+  int32_t block_size;    /* tokens per physical block: 16, 32 or 64 (the group-64 baseline: 16
+                            or 64) */
   int32_t win;           /* sliding-window length of the variance curve; must be 16 (DGQ 2.2) */
   int32_t max_segments;  /* 1..8 segments per (sequence, kv head) from dgq_compress */
   int32_t seg_capacity;  /* segment-table rows per (sequence, kv head): max_segments..64 */
@@ -417,7 +421,8 @@ dgq_status_t dgq_g64_quantize(const dgq_params_t *p, const uint16_t *k, const ui
                               int32_t max_seq_len, const dgq_g64_cache_t *cache, hipStream_t stream);
 
 /* Paged decode attention over a group-64 cache; arguments and workspace (including its zeroed
- * counters, dgq_decode_workspace_size) as paged_decode_attn_int8. */
+ * counters, dgq_decode_workspace_size) as paged_decode_attn_int8.  The group-64 calls take block
+ * sizes 16 and 64 (DGQ_ERR_UNSUPPORTED for 32). */
 dgq_status_t paged_decode_attn_g64(const dgq_params_t *p, const uint16_t *q,
                                    const dgq_g64_cache_t *cache, const int32_t *block_table,
                                    int32_t max_blocks, const int32_t *seq_lens, int32_t batch,

@@ -30,7 +30,7 @@ static dgq_status_t check_params(const dgq_params_t *p) {
   const int g = p->num_q_heads / p->num_kv_heads;
   if (g != 1 && g != 2 && g != 4) return DGQ_ERR_UNSUPPORTED;
   if (p->head_dim != 64 && p->head_dim != 128) return DGQ_ERR_UNSUPPORTED;
-  if (p->block_size != 16 && p->block_size != 64) return DGQ_ERR_UNSUPPORTED;
+  if (p->block_size != 16 && p->block_size != 32 && p->block_size != 64) return DGQ_ERR_UNSUPPORTED;
   if (p->win != kWin) return DGQ_ERR_UNSUPPORTED;
   if (p->max_segments < 1 || p->max_segments > kMaxCuts + 1) return DGQ_ERR_INVALID_ARG;
   if (p->seg_capacity < p->max_segments || p->seg_capacity > kMaxSegCap) return DGQ_ERR_INVALID_ARG;
@@ -368,6 +368,7 @@ extern "C" dgq_status_t dgq_g64_quantize(const dgq_params_t *p, const uint16_t *
                                          hipStream_t stream) {
   dgq_status_t st = check_params(p);
   if (st != DGQ_OK) return st;
+  if (p->block_size == 32) return DGQ_ERR_UNSUPPORTED;   // the group-64 baseline keeps 16 and 64
   if (batch < 0 || max_rows < 0 || total_rows < 0 || max_seq_len < 0) return DGQ_ERR_INVALID_ARG;
   if (batch == 0) return DGQ_OK;
   if (batch > kMaxGridBatch) return DGQ_ERR_UNSUPPORTED;
@@ -387,6 +388,7 @@ extern "C" dgq_status_t paged_decode_attn_g64(const dgq_params_t *p, const uint1
                                               void *ws, size_t ws_bytes, hipStream_t stream) {
   dgq_status_t st = check_params(p);
   if (st != DGQ_OK) return st;
+  if (p->block_size == 32) return DGQ_ERR_UNSUPPORTED;   // the group-64 baseline keeps 16 and 64
   if (batch < 0 || max_seq_len < 0) return DGQ_ERR_INVALID_ARG;
   if (batch == 0) return DGQ_OK;
   if (batch > kMaxGridBatch) return DGQ_ERR_UNSUPPORTED;

@@ -13,6 +13,7 @@ template <int D>
 static void launch_bs(const AppendArgs &a, int bs, int batch, hipStream_t s) {
   dim3 grid(a.hkv, batch);
   if (bs == 64) hipLaunchKernelGGL((append_kernel<D, 64>), grid, dim3(256), 0, s, a);
+  else if (bs == 32) hipLaunchKernelGGL((append_kernel<D, 32>), grid, dim3(256), 0, s, a);
   else hipLaunchKernelGGL((append_kernel<D, 16>), grid, dim3(256), 0, s, a);
 }
 

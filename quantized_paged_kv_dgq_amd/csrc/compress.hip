@@ -1163,7 +1163,7 @@ __global__ __launch_bounds__(256) void encode_kernel(CompressArgs a) {
       const int n = u / 64, jj = (u / 16) % 4, r = u % 16;
       off = ((n * 4 + jj) * 16 + r) * 16;
     } else {
-      off = d * 16;
+      off = v_tile_offset<D, BS>((t0 + 16 * blk_local) % BS, d);   // the unit's 16-token tile
     }
     store_stream(tilep + off, outw);
   }
@@ -1527,9 +1527,9 @@ __global__ __launch_bounds__(kShortThreads) void compress_short_kernel(CompressA
       uint32_t out[4][4];                              // [channel j][word g]
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        // BS 16: the set is block lblk, word g = tokens 4 g ..; BS 64: the set is (lblk, jj),
-        // word g = tokens 16 g + 4 jj ..
-        const int base = BS == 16 ? 16 * lblk + 4 * g : 64 * lblk + 16 * g + 4 * (set % 4);
+        // BS 16 and 32: the set is the 16 tokens 16 set ..; word g = tokens 4 g ..; BS 64: the set
+        // is (lblk, jj), word g = tokens 16 g + 4 jj ..
+        const int base = BS == 64 ? 64 * lblk + 16 * g + 4 * (set % 4) : 16 * set + 4 * g;
         const uint32_t w0 = ct[(base + 0) * QD + c], w1 = ct[(base + 1) * QD + c];
         const uint32_t w2 = ct[(base + 2) * QD + c], w3 = ct[(base + 3) * QD + c];
         const uint32_t lo01 = __builtin_amdgcn_perm(w1, w0, 0x05010400u), hi01 = __builtin_amdgcn_perm(w1, w0, 0x07030602u);
@@ -1546,7 +1546,7 @@ __global__ __launch_bounds__(kShortThreads) void compress_short_kernel(CompressA
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int d = 4 * c + j;
-        const int off = BS == 16 ? v_tile_offset<D, BS>(0, d) : v_tile_offset<D, BS>(4 * (set % 4), d);
+        const int off = BS == 64 ? v_tile_offset<D, BS>(4 * (set % 4), d) : v_tile_offset<D, BS>((16 * set) % BS, d);
         store_stream(tilep + off, out[j]);
       }
     }
@@ -1606,6 +1606,7 @@ static dgq_status_t launch_all(const CompressArgs &a, int bs, int max_seq_len, i
   dgq_status_t st;
   if (!a.multipass && max_seq_len <= short_tokens<D>()) {
     if (bs == 64) hipLaunchKernelGGL((compress_short_kernel<D, 64>), dim3(hkv, batch), dim3(kShortThreads), 0, s, a);
+    else if (bs == 32) hipLaunchKernelGGL((compress_short_kernel<D, 32>), dim3(hkv, batch), dim3(kShortThreads), 0, s, a);
     else hipLaunchKernelGGL((compress_short_kernel<D, 16>), dim3(hkv, batch), dim3(kShortThreads), 0, s, a);
     return check_launch("dgq_compress one-launch kernel");
   }
@@ -1634,6 +1635,7 @@ static dgq_status_t launch_all(const CompressArgs &a, int bs, int max_seq_len, i
   if (st != DGQ_OK) return st;
   if (max_seq_len == 0) return DGQ_OK;
   if (bs == 64) hipLaunchKernelGGL((encode_kernel<D, 64>), g64, dim3(256), 0, s, a);
+  else if (bs == 32) hipLaunchKernelGGL((encode_kernel<D, 32>), g64, dim3(256), 0, s, a);
   else hipLaunchKernelGGL((encode_kernel<D, 16>), g64, dim3(256), 0, s, a);
   return check_launch("dgq_compress encode kernel");
 }

@@ -110,7 +110,10 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_partition_kernel(Decode
           for (int m = 0; m < M; ++m)
             kf[T][m] = load_codes(kb + (((T * M + m) * 64) + lane) * 16);
       } else {
-        const int8_t *kb = kpool + (size_t)sh_blk[4 * (lc0 + c) + ((lane & 15) >> 2)] * blk_stride;
+        // 16-token blocks, or 32-token blocks made of two 16-token tiles
+        const int g4 = (lane & 15) >> 2;
+        const int8_t *kb = BS == 16 ? kpool + (size_t)sh_blk[4 * (lc0 + c) + g4] * blk_stride
+                                     : kpool + (size_t)sh_blk[2 * (lc0 + c) + (g4 >> 1)] * blk_stride + (g4 & 1) * 16 * D;
 #pragma unroll
         for (int T = 0; T < 4; ++T)
 #pragma unroll
@@ -125,7 +128,8 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_partition_kernel(Decode
 #pragma unroll
         for (int n = 0; n < NT; ++n) vf[n] = load_codes(vb + (n * 64 + lane) * 16);
       } else {
-        const int8_t *vb = vpool + (size_t)sh_blk[4 * (lc0 + c) + j] * blk_stride;
+        const int8_t *vb = BS == 16 ? vpool + (size_t)sh_blk[4 * (lc0 + c) + j] * blk_stride
+                                     : vpool + (size_t)sh_blk[2 * (lc0 + c) + (j >> 1)] * blk_stride + (j & 1) * 16 * D;
 #pragma unroll
         for (int n = 0; n < NT; ++n) vf[n] = load_codes(vb + (16 * n + (lane & 15)) * 16);
       }
@@ -429,7 +433,10 @@ __device__ __forceinline__ void decode_body(const DecodeArgs &a, const AppendArg
         for (int m = 0; m < M; ++m)
           kf[T][m] = load_codes(kb + (((T * M + m) * 64) + lane) * 16);
     } else {
-      const int8_t *kb = kpool + (size_t)sh_blk[4 * (lc0 + c) + ((lane & 15) >> 2)] * blk_stride;
+      // 16-token blocks, or 32-token blocks made of two 16-token tiles
+      const int g4 = (lane & 15) >> 2;
+      const int8_t *kb = BS == 16 ? kpool + (size_t)sh_blk[4 * (lc0 + c) + g4] * blk_stride
+                                   : kpool + (size_t)sh_blk[2 * (lc0 + c) + (g4 >> 1)] * blk_stride + (g4 & 1) * 16 * D;
 #pragma unroll
       for (int T = 0; T < 4; ++T)
 #pragma unroll
@@ -444,7 +451,8 @@ __device__ __forceinline__ void decode_body(const DecodeArgs &a, const AppendArg
 #pragma unroll
       for (int n = 0; n < NT; ++n) vf[n] = load_codes(vb + (n * 64 + lane) * 16);
     } else {
-      const int8_t *vb = vpool + (size_t)sh_blk[4 * (lc0 + c) + j] * blk_stride;
+      const int8_t *vb = BS == 16 ? vpool + (size_t)sh_blk[4 * (lc0 + c) + j] * blk_stride
+                                   : vpool + (size_t)sh_blk[2 * (lc0 + c) + (j >> 1)] * blk_stride + (j & 1) * 16 * D;
 #pragma unroll
       for (int n = 0; n < NT; ++n) vf[n] = load_codes(vb + (16 * n + (lane & 15)) * 16);
     }
@@ -735,6 +743,7 @@ static void launch_part(const DecodeArgs &a, int batch, hipStream_t s) {
 template <int D, int G>
 static void launch_part_bs(const DecodeArgs &a, int bs, int batch, hipStream_t s) {
   if (bs == 64) launch_part<D, G, 64>(a, batch, s);
+  else if (bs == 32) launch_part<D, G, 32>(a, batch, s);
   else launch_part<D, G, 16>(a, batch, s);
 }
 
@@ -797,6 +806,7 @@ template <int D, int G>
 static void launch_fused_bs(const DecodeArgs &a, const AppendArgs &ap, int bs, int batch, hipStream_t s) {
   dim3 grid(a.nparts, a.hkv, batch);
   if (bs == 64) hipLaunchKernelGGL((append_decode_kernel<D, G, 64>), grid, dim3(64 * kWaves), 0, s, a, ap);
+  else if (bs == 32) hipLaunchKernelGGL((append_decode_kernel<D, G, 32>), grid, dim3(64 * kWaves), 0, s, a, ap);
   else hipLaunchKernelGGL((append_decode_kernel<D, G, 16>), grid, dim3(64 * kWaves), 0, s, a, ap);
 }
 

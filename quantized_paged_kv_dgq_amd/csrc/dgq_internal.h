@@ -125,12 +125,15 @@ __device__ __forceinline__ float half_bits_to_float(uint32_t h) {
   return (float)c.f;
 }
 
-// Byte offset of (token tau of its block, channel d) inside one (block, head) K tile.
+// Byte offset of (token tau of its block, channel d) inside one (block, head) K tile.  A 32-token
+// block is two 16-token tiles one after the other.
 template <int D, int BS>
 __device__ __forceinline__ int k_tile_offset(int tau, int d) {
   constexpr int M = D / 64;
   const int m = d >> 6, j = (d & 63) >> 4, e = d & 15;
-  if constexpr (BS == 64) {
+  if constexpr (BS == 32) {
+    return (tau >> 4) * (16 * D) + k_tile_offset<D, 16>(tau & 15, d);
+  } else if constexpr (BS == 64) {
     const int T = tau >> 4, r = tau & 15;
     return (((T * M + m) * 4 + j) * 16 + r) * 16 + e;
   } else {
@@ -139,10 +142,13 @@ __device__ __forceinline__ int k_tile_offset(int tau, int d) {
   }
 }
 
-// Byte offset of (token tau, channel d) inside one (block, head) V tile.
+// Byte offset of (token tau, channel d) inside one (block, head) V tile (32-token blocks: two
+// 16-token tiles).
 template <int D, int BS>
 __device__ __forceinline__ int v_tile_offset(int tau, int d) {
-  if constexpr (BS == 64) {
+  if constexpr (BS == 32) {
+    return (tau >> 4) * (16 * D) + v_tile_offset<D, 16>(tau & 15, d);
+  } else if constexpr (BS == 64) {
     const int n = d >> 4, r = d & 15, j = (tau & 15) >> 2, e = ((tau >> 4) << 2) | (tau & 3);
     return ((n * 4 + j) * 16 + r) * 16 + e;
   } else {

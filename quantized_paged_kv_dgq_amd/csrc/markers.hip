@@ -53,6 +53,7 @@ void launch_bs(const MarkerArgs &a, int bs, int batch, hipStream_t s) {
   const int nx = (a.max_seq_len + 255) / 256;
   const dim3 grid(nx > 0 ? nx : 1, a.hkv, batch);
   if (bs == 64) hipLaunchKernelGGL((marker_bits_kernel<D, 64>), grid, dim3(256), 0, s, a);
+  else if (bs == 32) hipLaunchKernelGGL((marker_bits_kernel<D, 32>), grid, dim3(256), 0, s, a);
   else hipLaunchKernelGGL((marker_bits_kernel<D, 16>), grid, dim3(256), 0, s, a);
 }
 

@@ -20,6 +20,8 @@ def k_offsets(block_size: int, head_dim: int) -> np.ndarray:
     if block_size == 16:
         T, i = tau // 4, tau % 4
         return ((((T * m_count + m) * 4 + j) * 4 + i) * 16) + e
+    if block_size == 32:   # two 16-token tiles one after the other
+        return np.concatenate([k_offsets(16, head_dim), 16 * head_dim + k_offsets(16, head_dim)])
     raise ValueError(block_size)
 
 
@@ -33,6 +35,8 @@ def v_offsets(block_size: int, head_dim: int) -> np.ndarray:
         return ((n * 4 + j) * 16 + r) * 16 + e
     if block_size == 16:
         return d * 16 + tau
+    if block_size == 32:   # two 16-token tiles one after the other
+        return np.concatenate([v_offsets(16, head_dim), 16 * head_dim + v_offsets(16, head_dim)])
     raise ValueError(block_size)
 
 

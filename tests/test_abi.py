@@ -76,7 +76,7 @@ def test_workspace_sizes(lib):
     p = _params()
     assert lib.dgq_compress_workspace_size(ctypes.byref(p), 16, 16 * 8192, 8192) > 16 * 8192 * 8 * 20
     assert lib.dgq_decode_workspace_size(ctypes.byref(p), 16, 8192) > 0
-    for bad in (_params(head_dim=96), _params(block_size=32), _params(win=8), _params(num_q_heads=20),
+    for bad in (_params(head_dim=96), _params(block_size=48), _params(win=8), _params(num_q_heads=20),
                 _params(max_segments=9), _params(seg_capacity=4), _params(tau=0.5), _params(flags=8),
                 _params(min_var=-1.0), _params(min_var=float("nan"))):
         assert lib.dgq_compress_workspace_size(ctypes.byref(bad), 1, 10, 10) == 0
@@ -248,7 +248,7 @@ def test_lifecycle_argument_checks(lib):
     assert lib.dgq_copy_blocks(ctypes.byref(p), ctypes.byref(cache), None, fake, 2, None) == E
     assert lib.dgq_copy_blocks(ctypes.byref(p), ctypes.byref(cache), fake, fake, -1, None) == E
     assert lib.dgq_copy_seq_state(ctypes.byref(p), ctypes.byref(nostage), fake, fake, 1, None) == E
-    assert lib.dgq_copy_seq_state(ctypes.byref(_params(block_size=32)), ctypes.byref(cache), fake, fake, 1,
+    assert lib.dgq_copy_seq_state(ctypes.byref(_params(block_size=48)), ctypes.byref(cache), fake, fake, 1,
                                   None) == _lib.DGQ_ERR_UNSUPPORTED
     for row in (-1, 4):
         assert lib.dgq_swap_out(ctypes.byref(p), ctypes.byref(cache), row, fake, 3, fake, need, None, None) == E
@@ -259,6 +259,22 @@ def test_lifecycle_argument_checks(lib):
     assert lib.dgq_swap_in(ctypes.byref(p), ctypes.byref(cache), 0, fake, 3, ctypes.c_void_p((1 << 20) + 8),
                            need, None, None) == E
     assert lib.dgq_swap_out(ctypes.byref(p), ctypes.byref(nostage), 0, fake, 3, fake, need, None, None) == E
+
+
+def test_block_size_32_accepted_except_group64(lib):
+    """32-token blocks are valid for the DGQ calls; the group-64 baseline refuses them before any
+    HIP call."""
+    p = _params(block_size=32)
+    assert lib.dgq_compress_workspace_size(ctypes.byref(p), 1, 100, 100) > 0
+    assert lib.dgq_decode_workspace_size(ctypes.byref(p), 1, 100) > 0
+    fake = ctypes.c_void_p(1 << 20)
+    g = _lib.G64Cache(fake, fake, fake, fake, fake, 64, 0)
+    U = _lib.DGQ_ERR_UNSUPPORTED
+    assert lib.dgq_g64_quantize(ctypes.byref(p), fake, fake, 1024, 128, fake, None, 1, 64, 64, fake, 4, 128,
+                                ctypes.byref(g), None) == U
+    assert lib.paged_decode_attn_g64(ctypes.byref(p), fake, ctypes.byref(g), fake, 4, fake, 1, 128, 1.0, fake,
+                                     fake, 1 << 20, None) == U
+    assert lib.dgq_swap_image_bytes(ctypes.byref(p), 10) > 0
 
 
 def test_marker_format_checks(lib):

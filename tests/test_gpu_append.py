@@ -97,6 +97,13 @@ def test_stream_bs16_block_aligned_prefix():
     run_stream(cfg, 1, 80, check_every=16)
 
 
+def test_stream_bs32():
+    """32-token blocks (two 16-token tiles each): prefix 300 + 100 appends, crossing blocks."""
+    cfg = dgq_data.get_config(2, batch=2, seq_len=300, append_steps=100, block_size=32)
+    H.say("append stream bs32 prefix 300 + 100")
+    run_stream(cfg, 5, 100, check_every=25)
+
+
 def test_stream_from_empty_and_short_prefixes():
     """Prefixes of 0, 5 and 40 tokens (no full window in the ring at first)."""
     cfg = dgq_data.get_config(1, batch=3, append_steps=100, block_size=16)

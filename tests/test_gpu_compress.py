@@ -81,6 +81,8 @@ CASES = [
     ("mha_g1_mixed", 4, dict(batch=6, seq_len=900, min_len=1), 3),
     ("stream_prefix_bs64", 5, dict(batch=3, seq_len=200, append_steps=0), 4),
     ("d64_g2", 1, dict(hq=4, block_size=64, seq_len=1111, batch=2), 5),
+    ("llama_bs32", 2, dict(batch=2, seq_len=1300, block_size=32), 6),
+    ("d64_g2_bs32_ragged", 4, dict(batch=5, hkv=2, hq=4, head_dim=64, block_size=32, seq_len=1500, min_len=1), 7),
 ]
 
 
@@ -125,6 +127,8 @@ MARKER_CASES = [
     ("long_path_bs64_outliers", 3, dict(seq_len=12000)),
     ("mha_g1_mixed", 4, dict(batch=5, seq_len=900, min_len=1)),
     ("d64_g2_bs64", 1, dict(hq=4, block_size=64, seq_len=1111, batch=2)),
+    ("llama_bs32", 2, dict(batch=2, seq_len=900, block_size=32)),
+    ("long_path_bs32", 3, dict(seq_len=9000, block_size=32)),
 ]
 
 

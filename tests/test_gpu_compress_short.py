@@ -1,7 +1,7 @@
 """The one-launch compress for short sequences (at most 256 tokens at head_dim 128, 512 at 64)
 against the oracle and, byte for byte, against the separate stats / selection / encode launches
 (DGQ_COMPRESS_MULTIPASS) on the same input: pools, boundary bits, segment table, nseg, append
-state and status words, in both identifier formats and both block sizes, for ragged batches that
+state and status words, in both identifier formats and all three block sizes, for ragged batches that
 reach the length limit, with the segment-count policies, non-finite inputs, an out-of-range
 block id and a sequence longer than max_seq_len (DGQ article 2.2 for the method; 3.2 for
 short-context compress latency)."""
@@ -83,7 +83,7 @@ def _same(a, b, what):
         assert torch.equal(x, y), (what, f)
 
 
-@pytest.mark.parametrize("d,bs", [(64, 16), (64, 64), (128, 16), (128, 64)])
+@pytest.mark.parametrize("d,bs", [(64, 16), (64, 32), (64, 64), (128, 16), (128, 32), (128, 64)])
 @pytest.mark.parametrize("marker", [False, True], ids=["bitmap", "marker"])
 def test_short_path_equals_multipass_and_oracle(d, bs, marker):
     lens = _lens(d)

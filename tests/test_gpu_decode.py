@@ -51,6 +51,8 @@ CASES = [
     ("mha_g1_bs16_mixed", 4, dict(batch=5, seq_len=700, min_len=1), 3, None),
     ("stream_bs64_g4", 5, dict(batch=3, seq_len=300, append_steps=0), 4, None),
     ("d64_g2_bs64", 1, dict(hq=4, block_size=64, seq_len=333), 5, None),
+    ("llama_bs32_g4", 2, dict(batch=3, seq_len=1111, block_size=32), 7, None),
+    ("mha_g1_bs32_mixed", 4, dict(batch=4, seq_len=600, min_len=1, block_size=32, hkv=4, hq=4), 8, None),
     ("short_and_empty", 2, dict(batch=4, seq_len=70), 6, [70, 1, 0, 17]),
 ]
 

@@ -90,7 +90,8 @@ def run_fused(cfg, seed, steps, checks, params=None):
     (5, dict(batch=3, seq_len=200, append_steps=150), 150, (0, 55, 64, 149)),
     (2, dict(batch=2, seq_len=256, append_steps=80), 80, (0, 15, 16, 79)),
     (1, dict(hq=4, block_size=64, seq_len=100, append_steps=60, batch=2), 60, (0, 59)),
-], ids=["bs64_stream", "bs16_block_aligned", "d64_g2"])
+    (2, dict(batch=2, seq_len=250, append_steps=70, block_size=32), 70, (0, 5, 6, 69)),
+], ids=["bs64_stream", "bs16_block_aligned", "d64_g2", "bs32"])
 def test_fused_matches_separate_and_oracle(cid, over, steps, checks):
     cfg = dgq_data.get_config(cid, **over)
     H.say("fused append+decode", cid, over)

@@ -136,13 +136,13 @@ def test_fork_with_copy_on_write(l0, steps, marker):
     assert int(cache.status[2].item()) == 0
 
 
-@pytest.mark.parametrize("marker", [False, True], ids=["bitmap", "marker"])
-def test_swap_out_and_in(marker):
+@pytest.mark.parametrize("marker,bs", [(False, 64), (True, 64), (False, 32)], ids=["bitmap", "marker", "bitmap_bs32"])
+def test_swap_out_and_in(marker, bs):
     """Row 1 is swapped out to pinned host memory mid-stream, its blocks and state are overwritten,
     and it is swapped back into other block ids; from then on every decode output and the final
     cache equal those of a twin cache that was never swapped."""
-    cfg = dgq_data.get_config(5, batch=3, seq_len=300, append_steps=80)
-    H.say("swap out and in", cfg.batch, cfg.seq_len, marker)
+    cfg = dgq_data.get_config(5, batch=3, seq_len=300, append_steps=80, block_size=bs)
+    H.say("swap out and in", cfg.batch, cfg.seq_len, marker, bs)
     params = H.params_for(cfg, marker=marker)
     p = params.c
     bs = p.block_size
@@ -187,7 +187,7 @@ def test_swap_out_and_in(marker):
             for t in (caches[1].segs, caches[1].nseg, caches[1].tail, caches[1].k_stage, caches[1].v_stage):
                 t[row].zero_()
             staging.zero_()
-            pool.alloc(7)
+            pool.alloc(len(ids_old))   # the other owner takes the freed blocks (last freed first)
             ids_new = np.asarray(pool.alloc(max_blocks), np.int32)
             assert not set(ids_new) & set(ids_old)
             Q.dgq_swap_in(params, caches[1], row, torch.from_numpy(ids_new).cuda(), staging, host)

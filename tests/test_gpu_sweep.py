@@ -24,7 +24,7 @@ def draw_case(idx: int, streaming: bool):
     hkv = int(rng.choice([1, 2, 4, 8]))
     group = int(rng.choice([1, 2, 4]))
     head_dim = int(rng.choice([64, 128]))
-    block_size = int(rng.choice([16, 64]))
+    block_size = int(rng.choice([16, 32, 64]))
     batch = int(rng.integers(1, 5))
     if streaming:
         seq_len = int(rng.integers(1, 500))

@@ -7,7 +7,7 @@ import pytest
 import paged_layout as PL
 
 
-@pytest.mark.parametrize("bs", [16, 64])
+@pytest.mark.parametrize("bs", [16, 32, 64])
 @pytest.mark.parametrize("d", [64, 128])
 def test_offsets_are_bijections(bs, d):
     PL._check_bijection(PL.k_offsets(bs, d))
@@ -17,7 +17,7 @@ def test_offsets_are_bijections(bs, d):
 @pytest.mark.parametrize("d", [64, 128])
 def test_scatter_gather_roundtrip(d):
     rng = np.random.default_rng(0)
-    for bs in (16, 64):
+    for bs in (16, 32, 64):
         L = 3 * bs + 5
         table = rng.permutation(8)
         pool = np.zeros((8, 2, bs * d), np.int8)
