@@ -2,8 +2,9 @@
 
 Every workload runs whole on the GPU: the full batch is compressed in one call, the streaming
 workload then appends and decodes step by step, and every decode covers the whole batch with
-the same launch configuration the benchmark uses.  The oracle then checks a seeded sample of
-(sequence, kv head) units one at a time: segment table bit-exact, codes (acceptance bound),
+the same launch configuration the benchmark uses.  The oracle then checks (sequence, kv head)
+units one at a time, every unit of the Llama-shaped layer, the 128K layer and the MHA batch and a
+seeded sample of the streaming runs: segment table bit-exact, codes (acceptance bound),
 boundary bits and tail state, and the decode outputs of that unit's query heads (max rel err
 2e-3).  Inputs come from the device generator in dgq_data, and each sampled unit is copied back
 to the host as the oracle's input, so both sides see the same fp16 values.
@@ -26,13 +27,13 @@ SEED = 0
 # (case id, workload id, overrides, sampled units, decode check steps of a streaming run,
 #  marker format, fused append + decode)
 CASES = [
-    ("llama_layer_16x8192_append1", 2, dict(append_steps=1), 6, (0,), False, False),
-    ("long_context_131072_layer0", 3, {}, 2, (), False, False),
-    ("mha_100_mixed_lengths", 4, {}, 6, (), False, False),
-    ("streaming_64x2048_256steps", 5, {}, 4, (0, 63, 64, 255), False, False),
-    ("streaming_64x2048_256steps_fused", 5, {}, 4, (0, 63, 64, 255), False, True),
-    ("llama_layer_16x8192_append1_marker", 2, dict(append_steps=1), 4, (0,), True, False),
-    ("streaming_64x2048_256steps_fused_marker", 5, {}, 3, (0, 127, 255), True, True),
+    ("llama_layer_16x8192_append1", 2, dict(append_steps=1), 128, (0,), False, False),   # every unit
+    ("long_context_131072_layer0", 3, {}, 8, (), False, False),   # every kv head of the layer
+    ("mha_100_mixed_lengths", 4, {}, 3200, (), False, False),   # every unit
+    ("streaming_64x2048_256steps", 5, {}, 128, (0, 63, 64, 255), False, False),
+    ("streaming_64x2048_256steps_fused", 5, {}, 128, (0, 63, 64, 255), False, True),
+    ("llama_layer_16x8192_append1_marker", 2, dict(append_steps=1), 128, (0,), True, False),
+    ("streaming_64x2048_256steps_fused_marker", 5, {}, 32, (0, 127, 255), True, True),
 ]
 
 
