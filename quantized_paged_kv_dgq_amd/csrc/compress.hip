@@ -534,7 +534,18 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(CompressArgs a) {
       if (c < ntiles) stile[c] = x[u];
     }
   }
-  double2 *tiles = in_lds ? stile : gtiles;
+  // tile c: LDS when the tiles fit, else the workspace through a buffer resource (two kinds of
+  // access, so that the compiler does not merge them into one generic-pointer access, which would
+  // make every wait cover both the LDS and the memory counters)
+  const __amdgpu_buffer_rsrc_t rtiles = raw_rsrc(gtiles, (uint32_t)(ntiles * sizeof(double2)));
+  auto tile_get = [&](int c) -> double2 {
+    if (in_lds) return stile[c];
+    return __builtin_bit_cast(double2, __builtin_amdgcn_raw_buffer_load_b128(rtiles, (uint32_t)c * 16u, 0, 0));
+  };
+  auto tile_put = [&](int c, double2 v) {
+    if (in_lds) stile[c] = v;
+    else __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rtiles, (uint32_t)c * 16u, 0, 0);
+  };
   __syncthreads();
   const int max_seg = a.length_aware ? min(a.max_segments, length_aware_cap(L)) : a.max_segments;
   int nc = 0;
@@ -543,7 +554,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(CompressArgs a) {
       double s = -INFINITY;
       int t = INT_MAX;
       for (int c = tid; c < ntiles; c += kSelThreads) {
-        const double2 e = tiles[c];
+        const double2 e = tile_get(c);
         if (better(e.x, (int)e.y, s, t)) {
           s = e.x;
           t = (int)e.y;
@@ -599,7 +610,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(CompressArgs a) {
             bs = wbs[w0 + w];
             bt = wbt[w0 + w];
           }
-        tiles[c] = make_double2(bs, (double)bt);
+        tile_put(c, make_double2(bs, (double)bt));
       }
       __syncthreads();
     }

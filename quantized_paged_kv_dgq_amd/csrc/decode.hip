@@ -396,7 +396,6 @@ __device__ __forceinline__ void decode_body(const DecodeArgs &a, const AppendArg
     qraw[m][1] = src[1];
   }
 
-  if constexpr (APPEND) append_load_block<BS>(*ap, b, len_raw, ald);
   const int L_raw = len_raw + (APPEND ? 1 : 0);
   const int L = L_raw < 0 ? 0 : (L_raw > a.max_seq_len ? a.max_seq_len : L_raw);
   if (p == 0 && threadIdx.x == 0 && h == 0 && L != L_raw) atomicAdd(a.status + 2, 1ull);
@@ -410,9 +409,26 @@ __device__ __forceinline__ void decode_body(const DecodeArgs &a, const AppendArg
   const WaveRange wr = wave_range(wg_begin, span, L, wave);
   const int t_begin = wr.t_begin, t_end = wr.t_end;
   const bool active = t_begin < t_end;
+  const bool appending = APPEND && p == P - 1;
+  // the appended token's block id is one of the span's (a length clamped to max_seq_len aside)
   __shared__ int sh_blk[SpanBlocks<BS>::kBlocks];
-  span_blk.publish(wblk0, (L + BS - 1) / BS, a.num_blocks, sh_blk, a.status);
+  __shared__ int sh_tail_raw;
+  int tail_slot = -1;
+  if constexpr (APPEND) {
+    ald.t = len_raw;
+    ald.t_ok = len_raw >= 0 && len_raw / BS < ap->max_blocks;
+    ald.blk = 0;
+    const int rs = len_raw / BS - wblk0;
+    if (appending && ald.t_ok && rs >= 0 && rs < SpanBlocks<BS>::kBlocks) tail_slot = rs;
+  }
+  span_blk.publish(wblk0, (L + BS - 1) / BS, a.num_blocks, sh_blk, a.status, tail_slot, &sh_tail_raw);
   __syncthreads();
+  if constexpr (APPEND) {
+    if (appending && threadIdx.x == 0 && ald.t_ok) {
+      ald.blk = sh_tail_raw;
+      if (tail_slot < 0) ald.blk = ap->block_table[(size_t)b * ap->max_blocks + len_raw / BS];
+    }
+  }
 
   // block ids come from sh_blk: chunk c of the wave is local chunk lc0 + c of the workgroup
   const int lc0 = (t_begin - wg_begin) / kChunk;
@@ -457,19 +473,67 @@ __device__ __forceinline__ void decode_body(const DecodeArgs &a, const AppendArg
       for (int n = 0; n < NT; ++n) vf[n] = load_codes(vb + (16 * n + (lane & 15)) * 16);
     }
   };
-  // The workgroup that appends requests each wave's first chunk before the append (whose loads
-  // are already out), so the chunk streams in while the append runs and the append does not wait
-  // behind it.  The chunk is kept when none of its tokens is in the tail block (the only block the
-  // append writes); otherwise (or for a wave with no tokens) it is requested again afterwards.
+  // The workgroup that appends requests each wave's first chunk between the two halves of the
+  // append: after the loads of the append state and of the staging copy it may need (loads
+  // return in issue order, so the append does not wait behind the chunk), before the decision and
+  // the encode, so that the chunk streams in while they run.  The query is prepared meanwhile,
+  // while the staging copy is on its way.  The chunk is kept when none of its tokens is in the
+  // tail block (the only block the append writes); otherwise (or for a wave with no tokens) it is
+  // requested again afterwards.  Other workgroups request the chunk first, then prepare the query.
   v4i kf[4][M];
   v4i vf[NT];
   const int tail_start = (L - 1) / BS * BS;
-  const bool appending = APPEND && p == P - 1;
   const bool early = appending && active && t_begin + kChunk <= tail_start;
-  if (appending) {
-    load_k(0, kf);
-    load_v(0, vf);
-    append_one<D, BS>(*ap, b, h, false, aout, ald);
+  // ---- query: three signed bytes per channel, one per column of the B operand (its fp16 values
+  // are read here, before any load the append adds) ----
+  float qv[M][16];
+  float amax = 0.f, qsum = 0.f;
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    const uint4 w0 = qraw[m][0], w1 = qraw[m][1];
+    const uint32_t ws[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      qv[m][2 * e] = half_bits_to_float(ws[e] & 0xFFFFu);
+      qv[m][2 * e + 1] = half_bits_to_float(ws[e] >> 16);
+    }
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      amax = fmaxf(amax, fabsf(qv[m][e]));
+      qsum += qv[m][e];
+    }
+  }
+  amax = fmaxf(amax, __shfl_xor(amax, 16));
+  amax = fmaxf(amax, __shfl_xor(amax, 32));
+  qsum += __shfl_xor(qsum, 16);
+  qsum += __shfl_xor(qsum, 32);
+  AppendStage<D, BS> st;
+  if constexpr (APPEND) {
+    if (appending) append_begin<D, BS>(*ap, b, h, aout, ald, st);
+  }
+  load_k(0, kf);   // every wave (a wave with no tokens reads a valid block it does not use): a
+  load_v(0, vf);   // branch here would make the waits below count only the loads before it
+  int qexp = 0;
+  if (amax > 0.f) {
+    int ex;
+    frexpf(amax, &ex);
+    qexp = 22 - ex;   // amax * 2^qexp in [2^21, 2^22)
+  }
+  const float qmul = ldexpf(1.0f, qexp);
+  v4i qfrag[M];
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    uint32_t wq4[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int e = 0; e < 16; ++e) wq4[e >> 2] |= sel_byte(fmaf(qv[m][e], qmul, kMagic), bsel) << (8 * (e & 3));
+    qfrag[m] = v4i{(int)wq4[0], (int)wq4[1], (int)wq4[2], (int)wq4[3]};
+  }
+  // per-lane weight of this byte's partial dot product, in log2 units of the softmax
+  const float wq = live ? ldexpf(a.sm_log2, 16 - 8 * piece - qexp) : 0.f;
+  const float qsum_s = qsum * a.sm_log2;
+
+  if constexpr (APPEND) {
+    if (appending) append_end<D, BS>(*ap, b, h, false, aout, ald, st);
   }
   __shared__ float sh_o[kWaves][G][D];
   __shared__ float sh_m[kWaves][G], sh_l[kWaves][G];
@@ -481,9 +545,8 @@ __device__ __forceinline__ void decode_body(const DecodeArgs &a, const AppendArg
   float wv = 0.f;
 
   if (active) {
-    // the first chunk goes out before the segment rows and the query are prepared
     const int nchunks = (t_end - t_begin + kChunk - 1) / kChunk;
-    if (!early) {
+    if (appending && !early) {   // the chunk holds the tail block: read it after the append
       load_k(0, kf);
       load_v(0, vf);
     }
@@ -509,47 +572,6 @@ __device__ __forceinline__ void decode_body(const DecodeArgs &a, const AppendArg
     const float wfac_unit = vsmax > 0.f ? 4194304.0f / vsmax : 0.f;   // 2^22 / vsmax
     const float s_wf = s_vs * wfac_unit;
     wv = live ? ldexpf(vsmax, -6 - 8 * piece) : 0.f;                // 2^(16-8*piece) * vsmax / 2^22
-
-    // ---- query: three signed bytes per channel, one per column of the B operand ----
-    float qv[M][16];
-    float amax = 0.f, qsum = 0.f;
-#pragma unroll
-    for (int m = 0; m < M; ++m) {
-      const uint4 w0 = qraw[m][0], w1 = qraw[m][1];
-      const uint32_t ws[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        qv[m][2 * e] = half_bits_to_float(ws[e] & 0xFFFFu);
-        qv[m][2 * e + 1] = half_bits_to_float(ws[e] >> 16);
-      }
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        amax = fmaxf(amax, fabsf(qv[m][e]));
-        qsum += qv[m][e];
-      }
-    }
-    amax = fmaxf(amax, __shfl_xor(amax, 16));
-    amax = fmaxf(amax, __shfl_xor(amax, 32));
-    qsum += __shfl_xor(qsum, 16);
-    qsum += __shfl_xor(qsum, 32);
-    int qexp = 0;
-    if (amax > 0.f) {
-      int ex;
-      frexpf(amax, &ex);
-      qexp = 22 - ex;   // amax * 2^qexp in [2^21, 2^22)
-    }
-    const float qmul = ldexpf(1.0f, qexp);
-    v4i qfrag[M];
-#pragma unroll
-    for (int m = 0; m < M; ++m) {
-      uint32_t wq4[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-      for (int e = 0; e < 16; ++e) wq4[e >> 2] |= sel_byte(fmaf(qv[m][e], qmul, kMagic), bsel) << (8 * (e & 3));
-      qfrag[m] = v4i{(int)wq4[0], (int)wq4[1], (int)wq4[2], (int)wq4[3]};
-    }
-    // per-lane weight of this byte's partial dot product, in log2 units of the softmax
-    const float wq = live ? ldexpf(a.sm_log2, 16 - 8 * piece - qexp) : 0.f;
-    const float qsum_s = qsum * a.sm_log2;
 
     // segment index of token t (rows are sorted by start; row 0 starts at 0)
     auto seg_of = [&](int t) -> int {
@@ -697,6 +719,9 @@ __device__ __forceinline__ void decode_body(const DecodeArgs &a, const AppendArg
     sh_l[wave][g] = active ? l_run : 0.f;
   }
   const int done = finish_partition<D, G>(a, b, h, p, L, sh_o, sh_m, sh_l, APPEND && p == P - 1 ? aout.ns : -1);
+  // an append whose state did not fit the new position is counted here, after the decode: an
+  // atomic in flight earlier would make the compiler wait for every load outstanding at each wait
+  if (appending && threadIdx.x == 0 && !aout.ok) atomicAdd(ap->cache.status + 2, 1ull);
   if (APPEND && done != kPartialOnly && threadIdx.x == 0) {
     // every workgroup of (b, h) has read the old row count: publish the new one
     const size_t bhs = (size_t)b * a.hkv + h;

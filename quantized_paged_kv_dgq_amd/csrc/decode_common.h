@@ -153,23 +153,22 @@ struct SpanBlocks {
       raw[i] = slot < kBlocks && wblk0 + slot < max_blocks ? bt[wblk0 + slot] : 0;
     }
   }
+  // (raw_slot >= 0: the unchecked id of that slot is also left in *sh_raw, for the append of a
+  // fused decode, which checks it itself)
   __device__ __forceinline__ void publish(int wblk0, int nblk_seq, int num_blocks, int *sh_blk,
-                                          unsigned long long *status) const {
+                                          unsigned long long *status, int raw_slot = -1,
+                                          int *sh_raw = nullptr) const {
     bool bad = false;
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
       const int slot = (int)threadIdx.x + 64 * kWaves * i;
       if (slot < kBlocks) sh_blk[slot] = wblk0 + slot < nblk_seq ? checked_block(raw[i], num_blocks, bad) : 0;
+      if (slot == raw_slot) *sh_raw = raw[i];
     }
     if (__ballot(bad) != 0ull && (threadIdx.x & 63) == 0) atomicAdd(status + 2, 1ull);
   }
 };
 
-// Buffer resource over `bytes` bytes at `base` (raw, untyped, 32-bit data format): loads past the
-// end return zero, stores past the end are dropped.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void *base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
-}
 // Cache policy of the partials: agent (device) scope, i.e. coherent across the XCDs' L2 caches,
 // the same policy as relaxed device-scope atomic loads and stores.
 constexpr int kAgentScope = 16;

@@ -216,6 +216,13 @@ __device__ __forceinline__ int checked_block(int id, int num_blocks, bool &bad) 
   return id;
 }
 
+// Buffer resource over `bytes` bytes at `base` (raw, untyped, 32-bit data format): loads past the
+// end return zero without touching memory, stores past the end are dropped.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+constexpr uint32_t kOutOfRange = 0x80000000u;   // a buffer offset past any resource used here
+
 // Fixed-point image for the variance statistics: rint(clamp(x, -32, 32) * 512).
 __device__ __forceinline__ int dgq_fixed_point(float x) {
   const float c = fminf(fmaxf(x, -32.0f), 32.0f);
