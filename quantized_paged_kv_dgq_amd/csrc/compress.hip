@@ -189,6 +189,8 @@ __device__ __forceinline__ double readlane_d(double x, int l) {
 constexpr int kQuadSwap1 = 0xB1, kQuadSwap2 = 0x4E, kRowRor4 = 0x124, kRowRor8 = 0x128;
 // mirror each half row of 8 lanes (lane i <-> 7 - i): after the quad swaps, the other quad's value
 constexpr int kHalfMirror = 0x141;
+// mirror a 16-lane row (lane i <-> 15 - i): after the quad swaps and the half mirror, the row's value
+constexpr int kRowMirror = 0x140;
 
 // (score desc, t asc): true if (s2, t2) comes first
 __device__ __forceinline__ bool better(double s2, int t2, double s, int t) {
@@ -512,8 +514,8 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(CompressArgs a) {
   const size_t bh = (size_t)b * a.hkv + h;
   constexpr int MS = kMaxCuts + 1;
   __shared__ double2 stile[kSelTiles];
-  __shared__ double wbs[kSelWaves];
-  __shared__ int wbt[kSelWaves];
+  __shared__ double wbs[2][kSelWaves];   // per wave: best of the scan (0) and of the re-scan (1)
+  __shared__ int wbt[2][kSelWaves];
   __shared__ int cuts[kMaxCuts];
   __shared__ int starts[kMaxCuts + 2];
   if (tid == 0 && bad_seq && h == 0) atomicAdd(a.cache.status + 2, 1ull);
@@ -562,18 +564,17 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(CompressArgs a) {
       }
       wave_best(s, t);
       if (lane == 0) {
-        wbs[wave] = s;
-        wbt[wave] = t;
+        wbs[0][wave] = s;
+        wbt[0][wave] = t;
       }
       __syncthreads();
-      s = wbs[0];
-      t = wbt[0];
+      s = wbs[0][0];
+      t = wbt[0][0];
       for (int w = 1; w < kSelWaves; ++w)
-        if (better(wbs[w], wbt[w], s, t)) {
-          s = wbs[w];
-          t = wbt[w];
+        if (better(wbs[0][w], wbt[0][w], s, t)) {
+          s = wbs[0][w];
+          t = wbt[0][w];
         }
-      __syncthreads();   // wbs is written again below
       if (s == -INFINITY) break;
       if (r > 0 && !(s >= a.tau)) break;
       if (tid == 0) cuts[nc] = t;
@@ -597,22 +598,28 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(CompressArgs a) {
       }
       wave_best(sc, tt);
       if (lane == 0) {
-        wbs[wave] = sc;
-        wbt[wave] = tt;
+        wbs[1][wave] = sc;
+        wbt[1][wave] = tt;
       }
       __syncthreads();
-      if ((tid & 255) == 0 && c <= hi_tile) {
-        const int w0 = 4 * (tid >> 8);   // the four waves of this tile
-        double bs = wbs[w0];
-        int bt = wbt[w0];
-        for (int w = 1; w < 4; ++w)
-          if (better(wbs[w0 + w], wbt[w0 + w], bs, bt)) {
-            bs = wbs[w0 + w];
-            bt = wbt[w0 + w];
-          }
-        tile_put(c, make_double2(bs, (double)bt));
+      // the thread that scans a re-scanned tile folds the four waves of its group and stores the
+      // tile's new best itself, so its next scan reads it without another barrier (the scan's
+      // results sit in the other half of wbs, so no barrier is needed between reading them and the
+      // re-scan either)
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int cq = lo_tile + q;
+        if (cq <= hi_tile && cq % kSelThreads == tid) {
+          double bs = wbs[1][4 * q];
+          int bt = wbt[1][4 * q];
+          for (int w = 1; w < 4; ++w)
+            if (better(wbs[1][4 * q + w], wbt[1][4 * q + w], bs, bt)) {
+              bs = wbs[1][4 * q + w];
+              bt = wbt[1][4 * q + w];
+            }
+          tile_put(cq, make_double2(bs, (double)bt));
+        }
       }
-      __syncthreads();
     }
   }
   // starts = [0] + sorted cuts, then L
@@ -633,11 +640,15 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(CompressArgs a) {
   const int nseg = L > 0 ? nc + 1 : 0;
 
   // ---- every segment's K/V min/max ----
-  // (1) thread i takes 256-token tile i: a tile inside one segment folds the tile's extrema (from
-  //     the scores pass); a tile that holds a cut folds its whole sub-blocks one by one into the
-  //     accumulator of the segment that holds each; then one wave reduction per segment.
-  // (2) a sub-block that a cut splits (cuts are >= 16 apart, so one cut per sub-block; a cut at a
+  // (1) tiles inside one segment: the tile extrema of the scores pass, one tile per thread and
+  //     pass, folded per segment by one wave reduction each (segments in a plain loop, partial
+  //     results in the wave's LDS slot);
+  // (2) a tile that holds a cut: its 16 sub-blocks, one per lane of a 16-lane group (group c takes
+  //     the tile of cut c, unless cut c - 1 took it), folded per segment by a row reduction;
+  // (3) a sub-block that a cut splits (cuts are >= 16 apart, so one cut per sub-block; a cut at a
   //     multiple of 16 splits none) is re-read raw by wave c - 1.
+  // (Short loops and no per-segment register arrays: this part runs once per head, so its code
+  // is fetched cold, and its length is what it costs.)
   const float4 ident = make_float4(INFINITY, -INFINITY, INFINITY, -INFINITY);
   auto fold = [](float4 &r, const float4 x) {
     r.x = fminf(r.x, x.x);
@@ -645,56 +656,66 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(CompressArgs a) {
     r.z = fminf(r.z, x.z);
     r.w = fmaxf(r.w, x.w);
   };
+  auto seg_of = [&](int t) {
+    int j = 0;
+    for (int k = 1; k < nseg; ++k) j += t >= starts[k] ? 1 : 0;
+    return j;
+  };
   __shared__ float4 sred[kSelWaves][MS];
+  __shared__ float4 scut[kMaxCuts][MS];
   __shared__ float4 sraw[kMaxCuts][2];   // cut c: (left part, right part)
+  if (lane == 0)
+    for (int j = 0; j < MS; ++j) sred[wave][j] = ident;
+  if (tid < kMaxCuts * MS) scut[tid / MS][tid % MS] = ident;
+  __syncthreads();
   {
-    const float4 *ext = a.ws_ext + bh * a.nsub;
     const float4 *text = a.ws_text + bh * a.ntile;
     const int ntl = (L + 255) / 256;
-    float4 acc[MS];
-#pragma unroll
-    for (int j = 0; j < MS; ++j) acc[j] = ident;
-    auto seg_of = [&](int t) {
-      int j = 0;
-      for (int k = 1; k < nseg; ++k) j += t >= starts[k] ? 1 : 0;
-      return j;
-    };
-    for (int i = tid; i < ntl; i += kSelThreads) {
-      const int t0 = 256 * i, t1 = min(t0 + 256, L);
-      const int j0 = seg_of(t0);
-      if (seg_of(t1 - 1) == j0) {
-        const float4 x = text[i];
-#pragma unroll
-        for (int jj = 0; jj < MS; ++jj)
-          if (jj == j0) fold(acc[jj], x);
-      } else {
-        const int nsb = (t1 - t0 + kWin - 1) / kWin;
-        float4 x[16];
-#pragma unroll
-        for (int u = 0; u < 16; ++u) {
-          x[u] = ident;
-          if (u < nsb) x[u] = ext[16 * i + u];
-        }
-#pragma unroll
-        for (int u = 0; u < 16; ++u) {
-          if (u < nsb) {
-            const int s0 = t0 + kWin * u, s1 = min(s0 + kWin, L);
-            const int j = seg_of(s0);
-            if (s1 <= starts[j + 1]) {
-#pragma unroll
-              for (int jj = 0; jj < MS; ++jj)
-                if (jj == j) fold(acc[jj], x[u]);
-            }
-          }
-        }
+    for (int i0 = 0; i0 < ntl; i0 += kSelThreads) {
+      const int i = i0 + tid;
+      float4 x = ident;
+      int j0 = -1;
+      if (i < ntl) {
+        const int t0 = 256 * i, t1 = min(t0 + 256, L);
+        j0 = seg_of(t0);
+        if (seg_of(t1 - 1) == j0) x = text[i];
+        else j0 = -1;                                // (2)
+      }
+      for (int j = 0; j < nseg; ++j) {
+        const float4 r = wave_minmax(j0 == j ? x : ident);
+        if (lane == 0) fold(sred[wave][j], r);
       }
     }
-#pragma unroll
-    for (int j = 0; j < MS; ++j) {
-      if (j < nseg) {
-        const float4 r = wave_minmax(acc[j]);
-        if (lane == 0) sred[wave][j] = r;
+  }
+  if (wave < (kMaxCuts + 3) / 4) {
+    const float4 *ext = a.ws_ext + bh * a.nsub;
+    const int g = tid >> 4, k = tid & 15;
+    const bool on = g < nc && !(g > 0 && starts[g] / 256 == starts[g + 1] / 256);
+    float4 x = ident;
+    int j = -1;
+    if (on) {
+      const int sb = 16 * (starts[g + 1] / 256) + k;
+      const int s0 = kWin * sb, s1 = min(s0 + kWin, L);
+      if (s0 < L) {
+        j = seg_of(s0);
+        if (s1 <= starts[j + 1]) x = ext[sb];
+        else j = -1;                                 // (3)
       }
+    }
+    for (int jj = 0; jj < nseg; ++jj) {
+      float4 r = j == jj ? x : ident;
+      auto step = [&](auto tag) {
+        constexpr int C = decltype(tag)::value;
+        r.x = fminf(r.x, dpp_f<C>(r.x));
+        r.y = fmaxf(r.y, dpp_f<C>(r.y));
+        r.z = fminf(r.z, dpp_f<C>(r.z));
+        r.w = fmaxf(r.w, dpp_f<C>(r.w));
+      };
+      step(std::integral_constant<int, kQuadSwap1>{});
+      step(std::integral_constant<int, kQuadSwap2>{});
+      step(std::integral_constant<int, kHalfMirror>{});
+      step(std::integral_constant<int, kRowMirror>{});   // every lane of the row holds its result
+      if (on && k == 0) scut[g][jj] = r;
     }
   }
   if (wave + 1 < nseg) {
@@ -742,6 +763,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(CompressArgs a) {
   if (tid < nseg) {
     float4 r = sred[0][tid];
     for (int w = 1; w < kSelWaves; ++w) fold(r, sred[w][tid]);
+    for (int c = 0; c < nc; ++c) fold(r, scut[c][tid]);
     if (tid > 0) fold(r, sraw[tid - 1][1]);        // right of the cut that starts segment tid
     if (tid + 1 < nseg) fold(r, sraw[tid][0]);      // left of the cut that ends it
     dgq_seg_t row;
