@@ -409,33 +409,40 @@ __global__ __launch_bounds__(256) void stats_kernel(CompressArgs a) {
 // -------------------------------------------------------------------------------------------
 // 2. scores
 // -------------------------------------------------------------------------------------------
+// Two 256-token tiles per workgroup: the launch then fits the compute units in one round of
+// workgroups (each is short and mostly waits for its loads).
+constexpr int kScoreTiles = 2;
+
 template <int D>
 __global__ __launch_bounds__(256) void scores_kernel(CompressArgs a) {
-  const int tile = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  constexpr int TW = kScoreTiles;
+  const int tile0 = TW * blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   int c0, L;
   bool bad_seq;
   seq_range(a.cu, b, a.max_seq_len, a.total, c0, L, bad_seq);
-  if (tile * 256 >= L) return;
+  if (tile0 * 256 >= L) return;
   const int tid = threadIdx.x;
   const size_t bh = (size_t)b * a.hkv + h;
-  // the tile's K/V extrema from its sub-blocks (for the segment ranges of the selection)
-  if (tid < 64) {
-    const int sb = 16 * tile + (tid & 15);
+  // each tile's K/V extrema from its sub-blocks (for the segment ranges of the selection): wave q
+  // takes tile tile0 + q
+  if (tid < 64 * TW) {
+    const int tile = tile0 + (tid >> 6), k = tid & 63;
+    const int sb = 16 * tile + (k & 15);
     const float4 ident = make_float4(INFINITY, -INFINITY, INFINITY, -INFINITY);
     float4 x = ident;
-    if (tid < 16 && kWin * sb < L) x = a.ws_ext[bh * a.nsub + sb];
+    if (k < 16 && kWin * sb < L) x = a.ws_ext[bh * a.nsub + sb];
     const float4 r = wave_minmax(x);
-    if (tid == 0) a.ws_text[bh * a.ntile + tile] = r;
+    if (k == 0 && tile * 256 < L) a.ws_text[bh * a.ntile + tile] = r;
   }
-  if (L < 2 * kWin || tile * 256 > L - kWin) return;
-  __shared__ int sa[256 + 2 * kWin];
-  __shared__ long long sbm[256 + 2 * kWin];
-  __shared__ int wa[256 + kWin];           // window sums: wa[i] = sa[i] + ... + sa[i + 15]
-  __shared__ long long wbm[256 + kWin];
-  __shared__ double best_s[4];
-  __shared__ int best_t[4];
-  const int base = tile * 256 - kWin;
-  for (int i = tid; i < 256 + 2 * kWin; i += 256) {
+  if (L < 2 * kWin || tile0 * 256 > L - kWin) return;
+  __shared__ int sa[TW * 256 + 2 * kWin];
+  __shared__ long long sbm[TW * 256 + 2 * kWin];
+  __shared__ int wa[TW * 256 + kWin];           // window sums: wa[i] = sa[i] + ... + sa[i + 15]
+  __shared__ long long wbm[TW * 256 + kWin];
+  __shared__ double best_s[TW][4];
+  __shared__ int best_t[TW][4];
+  const int base = tile0 * 256 - kWin;
+  for (int i = tid; i < TW * 256 + 2 * kWin; i += 256) {
     const int tok = base + i;
     if (tok >= 0 && tok < L) {
       const size_t idx = (size_t)h * a.total + c0 + tok;
@@ -447,7 +454,7 @@ __global__ __launch_bounds__(256) void scores_kernel(CompressArgs a) {
     }
   }
   __syncthreads();
-  for (int i = tid; i < 256 + kWin; i += 256) {
+  for (int i = tid; i < TW * 256 + kWin; i += 256) {
     int A = 0;
     long long B = 0;
 #pragma unroll
@@ -459,37 +466,43 @@ __global__ __launch_bounds__(256) void scores_kernel(CompressArgs a) {
     wbm[i] = B;
   }
   __syncthreads();
-  const int t = tile * 256 + tid;
-  double score = -INFINITY;
-  int tb = INT_MAX;
-  if (t >= kWin && t <= L - kWin) {
-    // Q = N * sum b - (sum a)^2 of the windows [t - 16, t) and [t, t + 16), exact in double
-    // (|sum a| <= 2^25, N * sum b <= 2^51, the fused result is an integer below 2^51)
-    const double nel = (double)(kWin * D);
-    const double Al = (double)wa[tid], Ar = (double)wa[tid + kWin];
-    const double ql = fma(-Al, Al, nel * (double)wbm[tid]);
-    const double qr = fma(-Ar, Ar, nel * (double)wbm[tid + kWin]);
-    const double hi = fmax(ql, qr), lo = fmin(ql, qr);
-    score = hi < a.qfloor ? -INFINITY : (hi + 1.0) / (lo + 1.0);
-    a.ws_score[(size_t)h * a.total + c0 + t] = score;
-    tb = t;
-  }
-  // best (score, smallest t) of the tile
-  wave_best(score, tb);
-  if ((tid & 63) == 0) {
-    best_s[tid >> 6] = score;
-    best_t[tid >> 6] = tb;
+#pragma unroll
+  for (int q = 0; q < TW; ++q) {
+    const int li = 256 * q + tid, t = tile0 * 256 + li;
+    double score = -INFINITY;
+    int tb = INT_MAX;
+    if (t >= kWin && t <= L - kWin) {
+      // Q = N * sum b - (sum a)^2 of the windows [t - 16, t) and [t, t + 16), exact in double
+      // (|sum a| <= 2^25, N * sum b <= 2^51, the fused result is an integer below 2^51)
+      const double nel = (double)(kWin * D);
+      const double Al = (double)wa[li], Ar = (double)wa[li + kWin];
+      const double ql = fma(-Al, Al, nel * (double)wbm[li]);
+      const double qr = fma(-Ar, Ar, nel * (double)wbm[li + kWin]);
+      const double hi = fmax(ql, qr), lo = fmin(ql, qr);
+      score = hi < a.qfloor ? -INFINITY : (hi + 1.0) / (lo + 1.0);
+      a.ws_score[(size_t)h * a.total + c0 + t] = score;
+      tb = t;
+    }
+    // best (score, smallest t) of the tile
+    wave_best(score, tb);
+    if ((tid & 63) == 0) {
+      best_s[q][tid >> 6] = score;
+      best_t[q][tid >> 6] = tb;
+    }
   }
   __syncthreads();
-  if (tid == 0) {
-    double s = best_s[0];
-    int tt = best_t[0];
-    for (int w = 1; w < 4; ++w)
-      if (better(best_s[w], best_t[w], s, tt)) {
-        s = best_s[w];
-        tt = best_t[w];
-      }
-    a.ws_tile[bh * a.ntile + tile] = make_double2(s, (double)tt);
+  if (tid < TW) {
+    const int tile = tile0 + tid;
+    if (tile * 256 <= L - kWin) {   // the tiles the selection scans
+      double s = best_s[tid][0];
+      int tt = best_t[tid][0];
+      for (int w = 1; w < 4; ++w)
+        if (better(best_s[tid][w], best_t[tid][w], s, tt)) {
+          s = best_s[tid][w];
+          tt = best_t[tid][w];
+        }
+      a.ws_tile[bh * a.ntile + tile] = make_double2(s, (double)tt);
+    }
   }
 }
 
@@ -1635,7 +1648,6 @@ static dgq_status_t launch_all(const CompressArgs &a, int bs, int max_seq_len, i
   // batch, or of the real tiles (tile map) for a ragged batch
   const bool ragged = a.tile_map != nullptr;
   dim3 g64 = ragged ? dim3((unsigned)map_tiles, hkv, 1) : dim3((max_seq_len + 63) / 64, hkv, batch);
-  dim3 g256((max_seq_len + 255) / 256, hkv, batch);
   dgq_status_t st;
   if (!a.multipass && max_seq_len <= short_tokens<D>()) {
     if (bs == 64) hipLaunchKernelGGL((compress_short_kernel<D, 64>), dim3(hkv, batch), dim3(kShortThreads), 0, s, a);
@@ -1654,7 +1666,8 @@ static dgq_status_t launch_all(const CompressArgs &a, int bs, int max_seq_len, i
     st = check_launch("dgq_compress stats kernel");
     if (st != DGQ_OK) return st;
     if (!small) {
-      hipLaunchKernelGGL(scores_kernel<D>, g256, dim3(256), 0, s, a);
+      const dim3 gs(((max_seq_len + 255) / 256 + kScoreTiles - 1) / kScoreTiles, hkv, batch);
+      hipLaunchKernelGGL(scores_kernel<D>, gs, dim3(256), 0, s, a);
       st = check_launch("dgq_compress scores kernel");
       if (st != DGQ_OK) return st;
     }
