@@ -136,9 +136,8 @@ __device__ __forceinline__ void append_load_block(const AppendArgs &a, int b, in
 //    part of the decision that needs no more data; then, only when the span's codes may be
 //    rewritten, its first-16-token window is tested or the block seals, the requests for the
 //    span's fp16 staging copy (one 16-byte unit per thread and pass), and the bitmap byte a new
-//    row would mark.  It stores nothing to global memory: with a store in flight, the compiler
-//    cannot count the outstanding loads (stores and loads may complete out of order) and every
-//    wait for the staged data would also wait for the caller's chunk.
+//    row would mark.  It stores nothing to global memory: every store of the append comes in
+//    append_end, after the decision.
 //  * append_end: the window and ring moments from the staged keys, the decision, the encode and
 //    all the stores (the new token's staging copy included).  Nothing waits for a store: the
 //    closing barrier orders the code stores before any later load by the same workgroup (a

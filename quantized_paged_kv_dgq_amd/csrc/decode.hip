@@ -719,8 +719,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs &a, const AppendArg
     sh_l[wave][g] = active ? l_run : 0.f;
   }
   const int done = finish_partition<D, G>(a, b, h, p, L, sh_o, sh_m, sh_l, APPEND && p == P - 1 ? aout.ns : -1);
-  // an append whose state did not fit the new position is counted here, after the decode: an
-  // atomic in flight earlier would make the compiler wait for every load outstanding at each wait
+  // an append whose state did not fit the new position (nothing was appended) is counted once
   if (appending && threadIdx.x == 0 && !aout.ok) atomicAdd(ap->cache.status + 2, 1ull);
   if (APPEND && done != kPartialOnly && threadIdx.x == 0) {
     // every workgroup of (b, h) has read the old row count: publish the new one
