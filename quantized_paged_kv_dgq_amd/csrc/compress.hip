@@ -660,8 +660,8 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(CompressArgs a) {
   //     the tile of cut c, unless cut c - 1 took it), folded per segment by a row reduction;
   // (3) a sub-block that a cut splits (cuts are >= 16 apart, so one cut per sub-block; a cut at a
   //     multiple of 16 splits none) is re-read raw by wave c - 1.
-  // (Short loops and no per-segment register arrays: this part runs once per head, so its code
-  // is fetched cold, and its length is what it costs.)
+  // (Short loops and no per-segment register arrays: this part runs once per head, mostly in
+  // one or two waves, so the length of its code is what it costs.)
   const float4 ident = make_float4(INFINITY, -INFINITY, INFINITY, -INFINITY);
   auto fold = [](float4 &r, const float4 x) {
     r.x = fminf(r.x, x.x);
