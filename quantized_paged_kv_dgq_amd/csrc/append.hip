@@ -5,7 +5,7 @@ namespace dgq {
 
 template <int D, int BS>
 __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
-  __shared__ AppendOut out;
+  AppendOut out;
   append_one<D, BS>(a, blockIdx.y, blockIdx.x, true, out);
 }
 

@@ -30,7 +30,8 @@ struct AppendArgs {
   dgq_cache_t cache;
 };
 
-// What one append left for a decode that follows it in the same workgroup.
+// What one append left for a decode that follows it in the same workgroup (every thread holds
+// the same values).
 struct AppendOut {
   int ok;            // 0: the state was inconsistent and nothing was appended (status[2] counted)
   int ns;            // segment-table rows after the append
@@ -38,25 +39,27 @@ struct AppendOut {
   dgq_seg_t chosen;  // that row after the append
 };
 
-// The loads an append needs, all independent of one another: the new token (thread d < D holds
-// channel d), the segment-table rows (thread k < seg_cap holds row k), the append state (thread i
-// holds its 16-byte word i), and the row count and the new token's block id (thread 0).  A fused
-// decode issues them before its first chunk: loads return in the order they were issued, so an
-// append queued behind a chunk would wait for the whole chunk.  Every value stays with the
-// thread that loaded it until the append passes it through LDS, so no wait is forced before the
-// chunk's loads go out.  (The fused decode takes the block id from the block ids it reads for its
-// own span, which go out with these loads, instead of a second dependent load.)
+// The loads an append needs, all independent of one another and all made by every wave: the new
+// token (lane l < D/2 holds channels 2l and 2l+1), the segment-table rows (lane k < seg_cap holds
+// row k), the append state (lane i holds its 16-byte word i) and the row count.  Every wave can
+// then take the whole decision from its own registers.  A fused decode issues them before its
+// first chunk: loads return in the order they were issued, so an append queued behind a chunk
+// would wait for the whole chunk.  (The fused decode takes the new token's block id from the
+// block ids it reads for its own span instead of a second dependent load.)
 struct AppendLoads {
-  uint16_t kb, vb;
+  uint32_t kp, vp;
   uint4 seg[2];
   uint4 tail;
   int nseg;
-  int blk;      // the new token's block id (when t_ok)
+  int blk;      // the new token's block id (when t_ok), the same in every thread
   int t;        // position of the new token
   bool t_ok;
 };
 constexpr int kTailWords = (int)(sizeof(dgq_tail_t) / 16);
 static_assert(sizeof(dgq_tail_t) % 16 == 0 && sizeof(dgq_seg_t) == 32, "16-byte words");
+// word 0: r0, ring_len, span_own, window_done; words 1-4: ring_a; words 5-12: ring_b; word 13: span_range
+static_assert(offsetof(dgq_tail_t, ring_a) == 16 && offsetof(dgq_tail_t, ring_b) == 80 &&
+              offsetof(dgq_tail_t, span_range) == 208 && kTailWords == 14, "append state words");
 
 // (min, max, min, max) of r over the wave, in every lane, without an LDS round trip: neighbour and
 // pair exchanges within quads, the 8- and 16-lane mirrors of a row (DPP), then the permlane swaps
@@ -97,26 +100,25 @@ __device__ __forceinline__ float4 span_wave_minmax(float4 r) {
   return r;
 }
 
-// The loads that depend only on (b, h).
+// The loads that depend only on (b, h).  Buffer loads: a lane past the end of its resource reads
+// zeros without touching memory, so no branch separates these loads from the caller's next ones.
 template <int D>
 __device__ __forceinline__ AppendLoads append_loads_state(const AppendArgs &a, int b, int h) {
-  static_assert(D <= 256, "one channel per thread");
-  const int tid = threadIdx.x;
+  static_assert(D % 2 == 0 && D / 2 <= 64, "two channels per lane");
+  const uint32_t lane = threadIdx.x & 63;
   const size_t bh = (size_t)b * a.hkv + h;
   AppendLoads l;
-  l.kb = 0;
-  l.vb = 0;
-  if (tid < D) {
-    l.kb = a.k_tok[bh * D + tid];
-    l.vb = a.v_tok[bh * D + tid];
-  }
-  if (tid < a.seg_cap) {
-    const uint4 *row = reinterpret_cast<const uint4 *>(a.cache.segs + bh * a.seg_cap + tid);
-    l.seg[0] = row[0];
-    l.seg[1] = row[1];
-  }
-  if (tid < kTailWords) l.tail = reinterpret_cast<const uint4 *>(a.cache.tail + bh)[tid];
-  l.nseg = tid == 0 ? a.cache.nseg[bh] : 0;
+  l.kp = __builtin_amdgcn_raw_buffer_load_b32(raw_rsrc(a.k_tok + bh * D, D * 2), lane * 4, 0, 0);
+  l.vp = __builtin_amdgcn_raw_buffer_load_b32(raw_rsrc(a.v_tok + bh * D, D * 2), lane * 4, 0, 0);
+  const __amdgpu_buffer_rsrc_t rs = raw_rsrc(a.cache.segs + bh * a.seg_cap, (uint32_t)a.seg_cap * 32u);
+  l.seg[0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, lane * 32, 0, 0));
+  l.seg[1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, lane * 32 + 16, 0, 0));
+  l.tail = __builtin_bit_cast(
+      uint4, __builtin_amdgcn_raw_buffer_load_b128(raw_rsrc(a.cache.tail + bh, sizeof(dgq_tail_t)), lane * 16, 0, 0));
+  l.nseg = a.cache.nseg[bh];
+  l.blk = 0;
+  l.t = 0;
+  l.t_ok = false;
   return l;
 }
 
@@ -125,35 +127,95 @@ template <int BS>
 __device__ __forceinline__ void append_load_block(const AppendArgs &a, int b, int t, AppendLoads &l) {
   l.t = t;
   l.t_ok = t >= 0 && t / BS < a.max_blocks;
-  l.blk = 0;
-  if (threadIdx.x == 0 && l.t_ok) l.blk = a.block_table[(size_t)b * a.max_blocks + t / BS];
+  l.blk = (int)__builtin_amdgcn_raw_buffer_load_b32(raw_rsrc(a.block_table + (size_t)b * a.max_blocks, (uint32_t)a.max_blocks * 4u),
+                                                    l.t_ok ? (uint32_t)(t / BS) * 4u : kOutOfRange, 0, 0);
+}
+
+// The outcome of the join-or-own decision.
+struct AppendDecision {
+  dgq_seg_t chosen;   // the row the span is encoded with, after the append
+  int ns;             // rows after the append
+  int use_row;        // index of that row
+  int write_row;      // row this append stores (-1: none)
+  bool new_row;       // the span gets a row of its own now
+  bool own_now;       // the span has its own row after the append
+  bool all;           // the span's range changed: every span code is rewritten
+  bool full;          // a row of its own was wanted but the table is full (the span joins)
+};
+
+// want: the span should have its own row (it has one, its range left the row before it, or the
+// window test says so).  R is row ns - 1: the span's own row, or the row it would join.
+__device__ __forceinline__ AppendDecision append_decide(bool want, bool own, int ns, int seg_cap, int r0,
+                                                        const dgq_seg_t &R, float4 rk, float levels) {
+  AppendDecision d;
+  d.chosen = R;
+  d.ns = ns;
+  d.use_row = ns - 1;
+  d.write_row = -1;
+  d.new_row = false;
+  d.own_now = own;
+  d.all = false;
+  d.full = false;
+  if (want && !own) {
+    if (ns >= seg_cap) {
+      d.full = true;
+    } else {
+      d.chosen.start = r0;
+      d.chosen.kmin = rk.x;
+      d.chosen.kmax = rk.y;
+      d.chosen.vmin = rk.z;
+      d.chosen.vmax = rk.w;
+      d.chosen.kscale = dgq_scale(rk.x, rk.y, levels);
+      d.chosen.vscale = dgq_scale(rk.z, rk.w, levels);
+      d.chosen.reserved = 0;
+      d.ns = ns + 1;
+      d.use_row = ns;
+      d.write_row = ns;
+      d.new_row = true;
+      d.own_now = true;
+      d.all = true;   // the span moves to its own range
+    }
+  } else if (want) {
+    // its own row, widened (or rewritten unchanged)
+    d.all = (R.kmin != rk.x) | (R.kmax != rk.y) | (R.vmin != rk.z) | (R.vmax != rk.w);
+    d.chosen.kmin = rk.x;
+    d.chosen.kmax = rk.y;
+    d.chosen.vmin = rk.z;
+    d.chosen.vmax = rk.w;
+    d.chosen.kscale = dgq_scale(rk.x, rk.y, levels);
+    d.chosen.vscale = dgq_scale(rk.z, rk.w, levels);
+    d.write_row = ns - 1;
+  }
+  return d;
 }
 
 // The append of one token to (sequence b, kv head h), by all 256 threads of a workgroup, in two
 // halves so that a fused decode can put its first chunk's loads between them:
 //
-//  * append_begin: from the loads above (one memory round trip), the span's new ranges and every
-//    part of the decision that needs no more data; then, only when the span's codes may be
-//    rewritten, its first-16-token window is tested or the block seals, the requests for the
-//    span's fp16 staging copy (one 16-byte unit per thread and pass), and the bitmap byte a new
-//    row would mark.  It stores nothing to global memory: every store of the append comes in
-//    append_end, after the decision.
-//  * append_end: the window and ring moments from the staged keys, the decision, the encode and
-//    all the stores (the new token's staging copy included).  Nothing waits for a store: the
-//    closing barrier orders the code stores before any later load by the same workgroup (a
-//    decode of the tail block), and other workgroups or kernels only read them after this launch.
+//  * append_begin: every wave, from its own registers (no barrier): the state, the span's new
+//    ranges (DPP and permlane reductions), and the decision unless the window test is due; then,
+//    only when the span's codes may be rewritten, its first-16-token window is tested or the block
+//    seals, the requests for the span's fp16 staging copy (one 16-byte unit per thread and pass),
+//    the value-tile words that hold frozen tokens of the same block, and the bitmap byte a new row
+//    would mark.  It stores nothing.
+//  * append_end: the window and ring moments (window test or seal only, with one barrier), the
+//    encode and the code stores; a barrier; then the segment row, bitmap byte, row count and state
+//    stores (after the barrier, so that every wave has read the state they replace).  The code
+//    stores come before that barrier, which orders them before any later load of the tail block
+//    by the same workgroup (a decode of the tail block); other workgroups or kernels only read
+//    them after this launch.
+//
+// A re-encoded span's value codes go through an LDS image of the value tile and out as whole
+// 16-byte words: a value tile interleaves the tokens of a block inside each word, so the codes of
+// one token are single bytes 16 bytes apart, and storing them one by one costs a memory
+// transaction per byte.
 //
 // With publish_nseg false the new row count is left to the caller (out.ns): a fused decode
 // publishes it only after every workgroup of the same (sequence, head) has read the old count.
 template <int D, int BS>
 struct AppendShared {
-  dgq_tail_t tl;
-  uint16_t newk[D], newv[D];     // the new token
-  int wbad[4];                   // per wave: the new token held a non-finite value
-  dgq_seg_t srow[kMaxSegCap];   // the segment table as it was before this append
-  dgq_seg_t chosen;
-  int ns, blk, use_row, own_now, reenc_all;
-  float4 red4[4];
+  uint8_t vimg[BS * D];          // value codes of the tail block (re-encoded spans), words swizzled
+  uint4 tw[kTailWords];          // the state words (window test and seal)
   int mom_a[BS];                 // fixed-point moments of the span's tokens (span-relative index)
   long long mom_b[BS];
 };
@@ -164,128 +226,135 @@ __device__ __forceinline__ AppendShared<D, BS> &append_shared() {
   return sm;
 }
 
-// What append_begin hands to append_end (uniform across the workgroup, except the staged units
-// and the bitmap byte, which stay with the thread that loaded them).
+// Word W of a value tile sits at LDS word vimg_word(W): the low three bits of W are XORed with
+// the channel-tile bits above them, so the bytes that one pass of units writes (16 channels of 4
+// tokens) fall into different banks.  A bijection within each group of 8 words.
+template <int BS>
+__device__ __forceinline__ int vimg_word(int W) {
+  if constexpr (BS == 64) return W ^ ((W >> 6) & 7);
+  else return W ^ ((W >> 4) & 7);
+}
+template <int D, int BS>
+__device__ __forceinline__ int vimg_byte(int tau, int d) {
+  const int off = v_tile_offset<D, BS>(tau, d);
+  return (vimg_word<BS>(off >> 4) << 4) | (off & 15);
+}
+// The token (of its block) whose code is byte e of value-tile word W.
+template <int D, int BS>
+__device__ __forceinline__ int vword_token(int W, int e) {
+  if constexpr (BS == 64) return 16 * (e >> 2) + 4 * ((W >> 4) & 3) + (e & 3);
+  else if constexpr (BS == 32) return 16 * (W / D) + e;
+  else return e;
+}
+
+// What append_begin hands to append_end (uniform across the workgroup, except the staged units,
+// the old value words and the bitmap byte, which stay with the thread that loaded them).
 template <int D, int BS>
 struct AppendStage {
   static constexpr int CPU = D / 8;                   // 16-byte units per token
   static constexpr int UPT = (BS * CPU + 255) / 256;  // units per thread, at most
+  static constexpr int VWORDS = BS * D / 16;          // 16-byte words of a value tile
+  static constexpr int VW = (VWORDS + 255) / 256;     // value-tile words per thread, at most
   uint4 kw[UPT], vw[UPT];   // staged unit tid + 256 i: 8 channels of span token u / CPU
+  uint4 vold[VW];           // value-tile word tid + 256 k as it was (only after frozen tokens)
   uint32_t bits_old;        // thread 0: the bitmap byte holding r0's bit
   float4 rk;                // the span's K min, K max, V min, V max with the new token
-  int t, r0, slot0, span_len, nunits, blk;
+  dgq_seg_t R;              // row ns - 1 before the append
+  int t, r0, slot0, span_len, nunits, blk, ns, ring_len, nbad;
   bool go;                  // false: the state did not fit, nothing was appended
-  bool window_test, seal, staged;
+  bool own, wdone, window_test, seal;
 };
 
 template <int D, int BS>
-__device__ __forceinline__ void append_begin(const AppendArgs &a, int b, int h, AppendOut &out, const AppendLoads &ld,
-                                             AppendStage<D, BS> &st) {
-  const int tid = threadIdx.x;
+__device__ __forceinline__ void append_begin(const AppendArgs &a, int b, int h, AppendOut &out, AppendDecision &dec,
+                                             const AppendLoads &ld, AppendStage<D, BS> &st) {
+  constexpr int CPU = AppendStage<D, BS>::CPU;
+  const int tid = threadIdx.x, lane = tid & 63;
   const size_t bh = (size_t)b * a.hkv + h;
   const int t = ld.t;
-  AppendShared<D, BS> &sm = append_shared<D, BS>();
-  if (tid < a.seg_cap) {
-    uint4 *row = reinterpret_cast<uint4 *>(&sm.srow[tid]);
-    row[0] = ld.seg[0];
-    row[1] = ld.seg[1];
-  }
-  if (tid < kTailWords) reinterpret_cast<uint4 *>(&sm.tl)[tid] = ld.tail;
-  if (tid < D) {
-    sm.newk[tid] = ld.kb;
-    sm.newv[tid] = ld.vb;
-  }
-  if (tid == 0) {
-    sm.ns = ld.nseg;
-    sm.blk = ld.blk;
-  }
-  const bool t_ok = ld.t_ok;
-  __syncthreads();
-  const int blk_t = t_ok ? sm.blk : -1;
-  const int r0 = sm.tl.r0;
-  const int ns = sm.ns;
+  auto lane_i = [](uint32_t v, int l) { return __builtin_amdgcn_readlane((int)v, l); };
+  auto lane_f = [](uint32_t v, int l) { return __int_as_float(__builtin_amdgcn_readlane((int)v, l)); };
+  // the state: words 0 and 13 of the append state, from the lanes that loaded them
+  const int r0 = lane_i(ld.tail.x, 0), ring_len = lane_i(ld.tail.y, 0);
+  const bool own = lane_i(ld.tail.z, 0) != 0;
+  const bool wdone = lane_i(ld.tail.w, 0) != 0;
+  const float4 srange = make_float4(lane_f(ld.tail.x, 13), lane_f(ld.tail.y, 13), lane_f(ld.tail.z, 13), lane_f(ld.tail.w, 13));
+  const int ns = __builtin_amdgcn_readfirstlane(ld.nseg);
+  const int blk_raw = __builtin_amdgcn_readfirstlane(ld.blk);
   const int slot0 = r0 < 0 ? 0 : r0 % BS;
   const int span_len = t + 1 - r0;             // including the new token
-  st.go = true;
-  {
-    // the state must place the new token inside the open span's block, and the block must exist
-    // (r0 <= t and slot0 + span_len <= BS put r0 and t in the same block)
-    bool bad = !t_ok || r0 < 0 || r0 > t || slot0 + span_len > BS || ns < 0 || ns > a.seg_cap ||
-               (sm.tl.span_own != 0 && ns < 1) || sm.tl.ring_len < 0 || sm.tl.ring_len > kWin;
-    if (!bad) checked_block(blk_t, a.cache.num_blocks, bad);
-    if (bad) {
-      if (tid == 0) {
-        out.ok = 0;
-        out.ns = ns;
-        out.use_row = -1;
-      }
-      st.go = false;           // the caller counts it (out.ok == 0)
-      return;
-    }
-  }
-  const uint16_t *ks = a.cache.k_stage + bh * (size_t)BS * D;
-  const uint16_t *vs = a.cache.v_stage + bh * (size_t)BS * D;
+  // the state must place the new token inside the open span's block, and the block must exist
+  // (r0 <= t and slot0 + span_len <= BS put r0 and t in the same block)
+  bool bad = !ld.t_ok || r0 < 0 || r0 > t || slot0 + span_len > BS || ns < 0 || ns > a.seg_cap ||
+             (own && ns < 1) || ring_len < 0 || ring_len > kWin;
+  const int blk_t = checked_block(blk_raw, a.cache.num_blocks, bad);
+  const bool go = !bad;
+  st.go = go;
+  out.ok = go ? 1 : 0;
+  out.ns = ns;
+  out.use_row = -1;
 
-  // 1. the new token's ranges (and a non-finite check)
+  // 1. the new token's ranges over all its channels (every wave), and the 64-channel groups that
+  // hold a non-finite value
   float4 r = make_float4(INFINITY, -INFINITY, INFINITY, -INFINITY);
-  float bad = 0.f;
-  if (tid < D) {
-    const float kx = half_bits_to_float(ld.kb), vx = half_bits_to_float(ld.vb);
-    r.x = fminf(r.x, kx);
-    r.y = fmaxf(r.y, kx);
-    r.z = fminf(r.z, vx);
-    r.w = fmaxf(r.w, vx);
-    bad = fmaf(kx, 0.f, bad);
-    bad = fmaf(vx, 0.f, bad);
+  float badv = 0.f;
+  if (lane < D / 2) {
+    const float k0 = half_bits_to_float(ld.kp & 0xFFFFu), k1 = half_bits_to_float(ld.kp >> 16);
+    const float v0 = half_bits_to_float(ld.vp & 0xFFFFu), v1 = half_bits_to_float(ld.vp >> 16);
+    r.x = fminf(fminf(r.x, k0), k1);
+    r.y = fmaxf(fmaxf(r.y, k0), k1);
+    r.z = fminf(fminf(r.z, v0), v1);
+    r.w = fmaxf(fmaxf(r.w, v0), v1);
+    badv = fmaf(k0, 0.f, badv);
+    badv = fmaf(k1, 0.f, badv);
+    badv = fmaf(v0, 0.f, badv);
+    badv = fmaf(v1, 0.f, badv);
   }
   r = span_wave_minmax(r);
-  const bool wave_bad = __ballot(!(bad == 0.f)) != 0ull;
-  if ((tid & 63) == 0) {
-    sm.red4[tid >> 6] = r;
-    sm.wbad[tid >> 6] = wave_bad ? 1 : 0;
-  }
-  __syncthreads();
+  const unsigned long long badm = __ballot(!(badv == 0.f));
+  st.nbad = ((badm & 0xFFFFFFFFull) != 0ull ? 1 : 0) + ((badm >> 32) != 0ull ? 1 : 0);
 
   // 2. the span's ranges: the stored range of the earlier span tokens, widened by the new token
-  // (every thread computes the same values in the same order)
-  float4 q = sm.red4[0];
-#pragma unroll
-  for (int w = 1; w < 4; ++w) {
-    q.x = fminf(q.x, sm.red4[w].x);
-    q.y = fmaxf(q.y, sm.red4[w].y);
-    q.z = fminf(q.z, sm.red4[w].z);
-    q.w = fmaxf(q.w, sm.red4[w].w);
-  }
   if (span_len > 1) {
-    q.x = fminf(q.x, sm.tl.span_range[0]);
-    q.y = fmaxf(q.y, sm.tl.span_range[1]);
-    q.z = fminf(q.z, sm.tl.span_range[2]);
-    q.w = fmaxf(q.w, sm.tl.span_range[3]);
+    r.x = fminf(r.x, srange.x);
+    r.y = fmaxf(r.y, srange.y);
+    r.z = fminf(r.z, srange.z);
+    r.w = fmaxf(r.w, srange.w);
   }
-  const float4 rk = make_float4(q.x + 0.0f, q.y + 0.0f, q.z + 0.0f, q.w + 0.0f);
+  // (every lane holds the same ranges; taking them from the first lane tells the compiler so, and
+  // keeps the decision and the row count that the decode loops on in scalar registers)
+  auto uni = [](float x) { return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(x))); };
+  const float4 rk = make_float4(uni(r.x + 0.0f), uni(r.y + 0.0f), uni(r.z + 0.0f), uni(r.w + 0.0f));
 
-  // 3. what the decision can still need: the window test runs once the span has 16 tokens (until
-  // it has said "no change": window and ring stay fixed for the span); the span's codes are
-  // rewritten when it gets its own row (its range leaves the row before it, or the window test
-  // says so) or its own row widens; a full block seals
-  const bool own = sm.tl.span_own != 0;
-  const int base = own ? ns - 2 : ns - 1;
+  // 3. row ns - 1, the one row the decision can need (its own row, or the row the span would
+  // join), from the lane that loaded it; then the decision, unless the window test is due (once
+  // the span has 16 tokens and until it has said "no change": window and ring stay fixed for the
+  // span).  The span's codes are rewritten when it gets its own row or its own row widens; a
+  // full block seals.
+  const int rr = ns >= 1 && ns <= a.seg_cap ? ns - 1 : 0;
+  dgq_seg_t R;
+  R.start = lane_i(ld.seg[0].x, rr);
+  R.kmin = lane_f(ld.seg[0].y, rr);
+  R.kmax = lane_f(ld.seg[0].z, rr);
+  R.vmin = lane_f(ld.seg[0].w, rr);
+  R.vmax = lane_f(ld.seg[1].x, rr);
+  R.kscale = lane_f(ld.seg[1].y, rr);
+  R.vscale = lane_f(ld.seg[1].z, rr);
+  R.reserved = lane_i(ld.seg[1].w, rr);
   bool may_reenc;
-  if (own) {
-    const dgq_seg_t &R = sm.srow[ns - 1];
-    may_reenc = R.kmin != rk.x || R.kmax != rk.y || R.vmin != rk.z || R.vmax != rk.w;
-  } else {
-    may_reenc = base < 0 || rk.x < sm.srow[base].kmin || rk.y > sm.srow[base].kmax || rk.z < sm.srow[base].vmin ||
-                rk.w > sm.srow[base].vmax;
-  }
-  const bool window_test = !own && !may_reenc && span_len >= kWin && sm.tl.ring_len == kWin && !sm.tl.window_done;
-  const bool seal = (t + 1) % BS == 0;
-  const bool staged = may_reenc || window_test || seal;
-  constexpr int CPU = AppendStage<D, BS>::CPU;
+  if (own) may_reenc = (R.kmin != rk.x) | (R.kmax != rk.y) | (R.vmin != rk.z) | (R.vmax != rk.w);
+  else may_reenc = (ns < 1) | (rk.x < R.kmin) | (rk.y > R.kmax) | (rk.z < R.vmin) | (rk.w > R.vmax);
+  const bool window_test = go && !own && !may_reenc && span_len >= kWin && ring_len == kWin && !wdone;
+  const bool seal = go && (t + 1) % BS == 0;
+  const bool staged = go && (may_reenc || window_test || seal);
+  dec = append_decide(own || may_reenc, own, ns, a.seg_cap, r0, R, rk, a.fmt.levels);
+
+  // 4. buffer loads of the earlier span tokens (the new one comes from the registers of wave 0),
+  // every one issued: a unit that is not needed gets an offset past the resource (zero, no memory
+  // access), so no branch separates these loads from the caller's next ones
   const int nunits = span_len * CPU;
-  // buffer loads of the earlier span tokens (the new one comes from LDS in append_end), every one
-  // issued: a unit that is not needed gets an offset past the resource (zero, no memory access),
-  // so no branch separates these loads from the caller's next ones
+  const uint16_t *ks = a.cache.k_stage + bh * (size_t)BS * D;
+  const uint16_t *vs = a.cache.v_stage + bh * (size_t)BS * D;
   const __amdgpu_buffer_rsrc_t rks = raw_rsrc(ks, BS * D * 2), rvs = raw_rsrc(vs, BS * D * 2);
 #pragma unroll
   for (int i = 0; i < AppendStage<D, BS>::UPT; ++i) {
@@ -294,57 +363,61 @@ __device__ __forceinline__ void append_begin(const AppendArgs &a, int b, int h, 
     st.kw[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rks, off, 0, 0));
     st.vw[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rvs, off, 0, 0));
   }
+  // the value-tile words as they are, where frozen tokens of the block precede the span (they
+  // keep their bytes when a re-encoded span's words are written)
+  const int8_t *vt = a.cache.v_pool + ((size_t)blk_t * a.hkv + h) * (size_t)BS * D;
+  const __amdgpu_buffer_rsrc_t rvt = raw_rsrc(vt, BS * D);
+#pragma unroll
+  for (int k = 0; k < AppendStage<D, BS>::VW; ++k) {
+    const int W = tid + 256 * k;
+    const uint32_t off = staged && slot0 > 0 && W < AppendStage<D, BS>::VWORDS ? (uint32_t)W * 16u : kOutOfRange;
+    st.vold[k] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rvt, off, 0, 0));
+  }
   // the bitmap byte holding r0's bit, for a new row (thread 0)
-  const bool want_bits = tid == 0 && !own && r0 > 0 && !a.fmt.marker && (may_reenc || window_test);
+  const bool want_bits = tid == 0 && go && !own && r0 > 0 && !a.fmt.marker && (may_reenc || window_test);
   const uint8_t *bits_blk = a.fmt.marker ? nullptr : a.cache.bits + ((size_t)blk_t * a.hkv + h) * (BS / 8);
   st.bits_old = __builtin_amdgcn_raw_buffer_load_b8(raw_rsrc(bits_blk, BS / 8), want_bits ? (uint32_t)((r0 % BS) / 8) : kOutOfRange,
                                                      0, 0);
   st.rk = rk;
+  st.R = R;
   st.t = t;
   st.r0 = r0;
   st.slot0 = slot0;
   st.span_len = span_len;
   st.nunits = nunits;
   st.blk = blk_t;
+  st.ns = ns;
+  st.ring_len = ring_len;
+  st.own = own;
+  st.wdone = wdone;
   st.window_test = window_test;
   st.seal = seal;
-  st.staged = staged;
 }
 
 template <int D, int BS>
 __device__ __forceinline__ void append_end(const AppendArgs &a, int b, int h, bool publish_nseg, AppendOut &out,
-                                           const AppendLoads &ld, const AppendStage<D, BS> &st) {
-  if (!st.go) {
-    __syncthreads();
-    return;
-  }
+                                           AppendDecision &dec, const AppendLoads &ld, const AppendStage<D, BS> &st) {
+  if (!st.go) return;
   constexpr int CPU = AppendStage<D, BS>::CPU;
   constexpr int UPT = AppendStage<D, BS>::UPT;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const size_t bh = (size_t)b * a.hkv + h;
   AppendShared<D, BS> &sm = append_shared<D, BS>();
   const int t = st.t, r0 = st.r0, slot0 = st.slot0, span_len = st.span_len;
   const int slot = t % BS;
-  // the new token's units come from LDS (a select, so that the staged loads are waited for here,
-  // before any store: see append_begin)
-  uint4 kw[UPT], vw[UPT];
-#pragma unroll
-  for (int i = 0; i < UPT; ++i) {
-    const int u = tid + 256 * i;
-    const bool mine = u >= st.nunits - CPU && u < st.nunits;
-    const uint4 nk = *reinterpret_cast<const uint4 *>(&sm.newk[8 * (u % CPU)]);
-    const uint4 nv = *reinterpret_cast<const uint4 *>(&sm.newv[8 * (u % CPU)]);
-    kw[i] = mine ? nk : st.kw[i];
-    vw[i] = mine ? nv : st.vw[i];
-  }
+  const int nold = st.nunits - CPU;   // staged units (the span tokens before the new one)
+  // the new token's channels 2 lane and 2 lane + 1 (lanes < D/2 of every wave)
+  const float k0 = half_bits_to_float(ld.kp & 0xFFFFu), k1 = half_bits_to_float(ld.kp >> 16);
+  const float v0 = half_bits_to_float(ld.vp & 0xFFFFu), v1 = half_bits_to_float(ld.vp >> 16);
+  bool wdone = st.wdone;
 
-  // 4. fixed-point moments of the staged span tokens, for the window test and the ring: the CPU
-  // units of a token sit in CPU consecutive lanes of one pass
+  // 1. window test and seal: the fixed-point moments of the span's tokens (the CPU units of a
+  // token sit in CPU consecutive lanes of one pass; the new token's from wave 0's channel pairs)
   if (st.window_test || st.seal) {
 #pragma unroll
     for (int i = 0; i < UPT; ++i) {
       const int u = tid + 256 * i;
-      const uint32_t kh[4] = {kw[i].x, kw[i].y, kw[i].z, kw[i].w};
+      const uint32_t kh[4] = {st.kw[i].x, st.kw[i].y, st.kw[i].z, st.kw[i].w};
       int as = 0;
       long long bs2 = 0;
 #pragma unroll
@@ -353,184 +426,196 @@ __device__ __forceinline__ void append_end(const AppendArgs &a, int b, int h, bo
         as += n;
         bs2 += (long long)(n * n);
       }
-      if (u >= st.nunits) {
-        as = 0;
-        bs2 = 0;
-      }
 #pragma unroll
       for (int o = 1; o < CPU; o <<= 1) {
         as += __shfl_xor(as, o);
         bs2 += __shfl_xor(bs2, o);
       }
-      if (u < st.nunits && u % CPU == 0) {
+      if (u < nold && u % CPU == 0) {
         sm.mom_a[u / CPU] = as;
         sm.mom_b[u / CPU] = bs2;
       }
     }
-  }
-  __syncthreads();
-
-  // 5. decision (one thread)
-  if (tid == 0) {
-    const int nbad = sm.wbad[0] + sm.wbad[1] + sm.wbad[2] + sm.wbad[3];
-    if (nbad > 0) atomicAdd(a.cache.status + 1, (unsigned long long)nbad);
-    dgq_tail_t &tl = sm.tl;
-    int ns = sm.ns;
-    const int base = tl.span_own ? ns - 2 : ns - 1;
-    const float4 rk = st.rk;
-    bool want = tl.span_own != 0 || base < 0;
-    if (!want) {
-      const dgq_seg_t S = sm.srow[base];
-      want = rk.x < S.kmin || rk.y > S.kmax || rk.z < S.vmin || rk.w > S.vmax;
-      if (!want && st.window_test) {
-        long long la = 0, lb = 0, ra = 0, rb = 0;
-        for (int i = 0; i < kWin; ++i) {
-          la += tl.ring_a[i];
-          lb += tl.ring_b[i];
-          ra += sm.mom_a[i];
-          rb += sm.mom_b[i];
-        }
-        const long long nel = (long long)kWin * D;
-        const long long ql = nel * lb - la * la, qr = nel * rb - ra * ra;
-        const long long hi = ql > qr ? ql : qr, lo = ql > qr ? qr : ql;
-        want = !((double)hi < a.qfloor) && (double)(hi + 1) / (double)(lo + 1) >= a.tau;
-        if (!want) tl.window_done = 1;
+    if (wave == 0) {
+      int as = 0;
+      long long bs2 = 0;
+      if (lane < D / 2) {
+        const int n0 = dgq_fixed_point(k0), n1 = dgq_fixed_point(k1);
+        as = n0 + n1;
+        bs2 = (long long)(n0 * n0) + (long long)(n1 * n1);
       }
-    }
-    int all = 0;
-    if (want && !tl.span_own) {
-      if (ns >= a.seg_cap) {
-        atomicAdd(a.cache.status + 0, 1ull);   // the table is full: the span joins the row before it
-      } else {
-        dgq_seg_t row;
-        row.start = r0;
-        row.kmin = rk.x;
-        row.kmax = rk.y;
-        row.vmin = rk.z;
-        row.vmax = rk.w;
-        row.kscale = dgq_scale(row.kmin, row.kmax, a.fmt.levels);
-        row.vscale = dgq_scale(row.vmin, row.vmax, a.fmt.levels);
-        row.reserved = 0;
-        a.cache.segs[bh * a.seg_cap + ns] = row;
-        sm.srow[ns] = row;
-        ns += 1;
-        tl.span_own = 1;
-        all = 1;                                 // the span moves to its own range
-        if (r0 > 0 && !a.fmt.marker)
-          a.cache.bits[((size_t)st.blk * a.hkv + h) * (BS / 8) + (r0 % BS) / 8] =
-              (uint8_t)((st.bits_old & 0xFFu) | (1u << (r0 % 8)));
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        as += __shfl_xor(as, o);
+        bs2 += __shfl_xor(bs2, o);
       }
-    } else if (want && tl.span_own) {
-      dgq_seg_t row = sm.srow[ns - 1];
-      all = row.kmin != rk.x || row.kmax != rk.y || row.vmin != rk.z || row.vmax != rk.w;
-      row.kmin = rk.x;
-      row.kmax = rk.y;
-      row.vmin = rk.z;
-      row.vmax = rk.w;
-      row.kscale = dgq_scale(row.kmin, row.kmax, a.fmt.levels);
-      row.vscale = dgq_scale(row.vmin, row.vmax, a.fmt.levels);
-      a.cache.segs[bh * a.seg_cap + ns - 1] = row;
-      sm.srow[ns - 1] = row;
+      if (lane == 0) {
+        sm.mom_a[span_len - 1] = as;
+        sm.mom_b[span_len - 1] = bs2;
+      }
+      if (lane < kTailWords) sm.tw[lane] = ld.tail;
     }
-    sm.ns = ns;
-    sm.use_row = tl.span_own ? ns - 1 : base;
-    sm.chosen = sm.srow[sm.use_row];
-    sm.own_now = tl.span_own;
-    sm.reenc_all = all;
-    out.ok = 1;
-    out.ns = ns;
-    out.use_row = sm.use_row;
-    out.chosen = sm.chosen;
+    __syncthreads();
+    if (st.window_test) {
+      // every lane sums the ring and the span's first 16 tokens over lanes (l & 15) of its row,
+      // so every lane holds the same totals
+      const dgq_tail_t &tl = *reinterpret_cast<const dgq_tail_t *>(sm.tw);
+      const int i = lane & 15;
+      long long la = tl.ring_a[i], lb = tl.ring_b[i], ra = sm.mom_a[i], rb = sm.mom_b[i];
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) {
+        la += __shfl_xor(la, o);
+        lb += __shfl_xor(lb, o);
+        ra += __shfl_xor(ra, o);
+        rb += __shfl_xor(rb, o);
+      }
+      const long long nel = (long long)kWin * D;
+      const long long ql = nel * lb - la * la, qr = nel * rb - ra * ra;
+      const long long hi = ql > qr ? ql : qr, lo = ql > qr ? qr : ql;
+      const bool want = __builtin_amdgcn_readfirstlane(
+                            (!((double)hi < a.qfloor) && (double)(hi + 1) / (double)(lo + 1) >= a.tau) ? 1 : 0) != 0;
+      if (!want) wdone = true;
+      dec = append_decide(want, false, st.ns, a.seg_cap, r0, st.R, st.rk, a.fmt.levels);
+    }
   }
-  __syncthreads();
 
-  // 6. encode with the chosen segment's range: the whole span when that range changed (a new row,
-  // or the span's own row widened), else only the new token (every other span code is unchanged)
-  const dgq_seg_t row = sm.chosen;
+  // 2. encode with the chosen row: the whole span when that range changed (a new row, or the
+  // span's own row widened), else only the new token (every other span code is unchanged)
+  const dgq_seg_t row = dec.chosen;
   const float lv = a.fmt.levels;
   const int low = a.fmt.low;
   const float kinv = dgq_inv(row.kmin, row.kmax, lv), vinv = dgq_inv(row.vmin, row.vmax, lv);
   // marker format: the span's own segment starts at r0, whose first key byte is the marker
-  const bool mark = a.fmt.marker && sm.own_now && r0 > 0;
+  const bool mark = a.fmt.marker && dec.own_now && r0 > 0;
   int8_t *kt = a.cache.k_pool + ((size_t)st.blk * a.hkv + h) * (size_t)BS * D;
   int8_t *vt = a.cache.v_pool + ((size_t)st.blk * a.hkv + h) * (size_t)BS * D;
-  if (tid < D) {
-    // the new token's staging copy
-    a.cache.k_stage[(bh * BS + slot) * D + tid] = ld.kb;
-    a.cache.v_stage[(bh * BS + slot) * D + tid] = ld.vb;
-  }
-  if (!sm.reenc_all) {
-    // only the new token changes: thread d < D still holds its channel d
-    if (tid < D) {
-      uint32_t kc = (uint32_t)(dgq_encode_value(half_bits_to_float(ld.kb), row.kmin, kinv, lv, low) & 0xFF);
-      if (mark && slot == slot0 && tid == 0) kc = dgq_marker_byte(kc);
-      kt[k_tile_offset<D, BS>(slot, tid)] = (int8_t)kc;
-      vt[v_tile_offset<D, BS>(slot, tid)] = (int8_t)dgq_encode_value(half_bits_to_float(ld.vb), row.vmin, vinv, lv, low);
+  if (wave == 0 && lane < D / 2) {
+    // the new token, channels 2 lane and 2 lane + 1, and its staging copy
+    *reinterpret_cast<uint32_t *>(a.cache.k_stage + (bh * BS + slot) * D + 2 * lane) = ld.kp;
+    *reinterpret_cast<uint32_t *>(a.cache.v_stage + (bh * BS + slot) * D + 2 * lane) = ld.vp;
+    uint32_t kc = (uint32_t)(dgq_encode_value(k0, row.kmin, kinv, lv, low) & 0xFF) |
+                  ((uint32_t)(dgq_encode_value(k1, row.kmin, kinv, lv, low) & 0xFF) << 8);
+    if (mark && slot == slot0 && lane == 0) kc = (kc & ~0xFFu) | dgq_marker_byte(kc & 0xFFu);
+    *reinterpret_cast<uint16_t *>(kt + k_tile_offset<D, BS>(slot, 2 * lane)) = (uint16_t)kc;
+    const int8_t vc0 = (int8_t)dgq_encode_value(v0, row.vmin, vinv, lv, low);
+    const int8_t vc1 = (int8_t)dgq_encode_value(v1, row.vmin, vinv, lv, low);
+    if (dec.all) {
+      sm.vimg[vimg_byte<D, BS>(slot, 2 * lane)] = (uint8_t)vc0;
+      sm.vimg[vimg_byte<D, BS>(slot, 2 * lane + 1)] = (uint8_t)vc1;
+    } else {
+      vt[v_tile_offset<D, BS>(slot, 2 * lane)] = vc0;
+      vt[v_tile_offset<D, BS>(slot, 2 * lane + 1)] = vc1;
     }
-  } else {
-    // the whole span, from the staged units: 8 key codes stored as 8 contiguous bytes of the tile
+  }
+  if (dec.all) {
+    // the earlier span tokens, from the staged units: 8 key codes stored as 8 contiguous bytes of
+    // the tile, 8 value codes into the image
 #pragma unroll
     for (int i = 0; i < UPT; ++i) {
       const int u = tid + 256 * i;
-      if (u < st.nunits) {
+      if (u < nold) {
         const int s = slot0 + u / CPU, d0 = 8 * (u % CPU);
-        const uint32_t kh[4] = {kw[i].x, kw[i].y, kw[i].z, kw[i].w};
-        const uint32_t vh[4] = {vw[i].x, vw[i].y, vw[i].z, vw[i].w};
+        const uint32_t kh[4] = {st.kw[i].x, st.kw[i].y, st.kw[i].z, st.kw[i].w};
+        const uint32_t vh[4] = {st.vw[i].x, st.vw[i].y, st.vw[i].z, st.vw[i].w};
         uint32_t kc[2] = {0u, 0u};
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const float kx = half_bits_to_float(e & 1 ? kh[e >> 1] >> 16 : kh[e >> 1] & 0xFFFFu);
           const float vx = half_bits_to_float(e & 1 ? vh[e >> 1] >> 16 : vh[e >> 1] & 0xFFFFu);
           kc[e >> 2] |= (uint32_t)(dgq_encode_value(kx, row.kmin, kinv, lv, low) & 0xFF) << (8 * (e & 3));
-          vt[v_tile_offset<D, BS>(s, d0 + e)] = (int8_t)dgq_encode_value(vx, row.vmin, vinv, lv, low);
+          sm.vimg[vimg_byte<D, BS>(s, d0 + e)] = (uint8_t)dgq_encode_value(vx, row.vmin, vinv, lv, low);
         }
         if (mark && s == slot0 && d0 == 0) kc[0] = (kc[0] & ~0xFFu) | dgq_marker_byte(kc[0] & 0xFFu);
         *reinterpret_cast<uint2 *>(kt + k_tile_offset<D, BS>(s, d0)) = make_uint2(kc[0], kc[1]);
       }
     }
+    __syncthreads();
+    // the value-tile words that hold a span token, whole from the image: bytes of frozen tokens
+    // (before the span) from the word as it was, bytes of tokens after the new one are never read
+    // before their own append writes them
+#pragma unroll
+    for (int k = 0; k < AppendStage<D, BS>::VW; ++k) {
+      const int W = tid + 256 * k;
+      if (W < AppendStage<D, BS>::VWORDS) {
+        uint32_t span_m = 0u, frozen_m = 0u;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int tau = vword_token<D, BS>(W, e);
+          span_m |= (uint32_t)(tau >= slot0 && tau <= slot) << e;
+          frozen_m |= (uint32_t)(tau < slot0) << e;
+        }
+        if (span_m != 0u) {
+          uint4 w = *reinterpret_cast<const uint4 *>(&sm.vimg[vimg_word<BS>(W) << 4]);
+          if (frozen_m != 0u) {
+            uint32_t wv[4] = {w.x, w.y, w.z, w.w};
+            const uint32_t ov[4] = {st.vold[k].x, st.vold[k].y, st.vold[k].z, st.vold[k].w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              uint32_t m = 0u;
+#pragma unroll
+              for (int e = 0; e < 4; ++e) m |= ((frozen_m >> (4 * q + e)) & 1u) * (0xFFu << (8 * e));
+              wv[q] = (wv[q] & ~m) | (ov[q] & m);
+            }
+            w = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+          }
+          *reinterpret_cast<uint4 *>(vt + W * 16) = w;
+        }
+      }
+    }
   }
 
-  // 7. the state: seal a full block (the ring keeps the moments of the last 16 sealed tokens), or
-  // keep the span's ranges
-  if (tid == 0) {
-    dgq_tail_t &tl = sm.tl;
-    if (publish_nseg) a.cache.nseg[bh] = sm.ns;
-    if (st.seal) {
-      // new ring = last 16 of (old ring, span tokens)
-      const int m_tail = span_len < kWin ? span_len : kWin;   // span tokens that enter the ring
-      const int old_keep = m_tail < kWin ? (tl.ring_len < kWin - m_tail ? tl.ring_len : kWin - m_tail) : 0;
-      int32_t na[kWin];
-      long long nb[kWin];
-      int n = 0;
-      for (int i = tl.ring_len - old_keep; i < tl.ring_len; ++i) {
-        na[n] = tl.ring_a[i];
-        nb[n] = tl.ring_b[i];
-        ++n;
-      }
-      for (int i = 0; i < m_tail; ++i) {
-        na[n] = sm.mom_a[span_len - m_tail + i];
-        nb[n] = sm.mom_b[span_len - m_tail + i];
-        ++n;
-      }
-      for (int i = 0; i < kWin; ++i) {
-        tl.ring_a[i] = i < n ? na[i] : 0;
-        tl.ring_b[i] = i < n ? nb[i] : 0;
-      }
-      tl.ring_len = n;
-      tl.r0 = t + 1;
-      tl.span_own = 0;
-      tl.window_done = 0;
-    } else {
-      tl.span_range[0] = st.rk.x;
-      tl.span_range[1] = st.rk.y;
-      tl.span_range[2] = st.rk.z;
-      tl.span_range[3] = st.rk.w;
-    }
-    a.cache.tail[bh] = tl;
-  }
-  // the code stores above come before any load of the tail block by this workgroup after this
-  // barrier (workgroup scope: one compute unit, in-order vector memory)
+  // 3. the code stores above come before any load of the tail block by this workgroup after this
+  // barrier (workgroup scope: one compute unit, in-order vector memory), and every wave has read
+  // the state that the stores below replace
   __syncthreads();
+  out.ok = 1;
+  out.ns = dec.ns;
+  out.use_row = dec.use_row;
+  out.chosen = dec.chosen;
+  if (wave == 0) {
+    if (lane == 0) {
+      if (st.nbad > 0) atomicAdd(a.cache.status + 1, (unsigned long long)st.nbad);
+      if (dec.full) atomicAdd(a.cache.status + 0, 1ull);   // the table is full: the span joins the row before it
+      if (dec.new_row && r0 > 0 && !a.fmt.marker)
+        a.cache.bits[((size_t)st.blk * a.hkv + h) * (BS / 8) + (r0 % BS) / 8] =
+            (uint8_t)((st.bits_old & 0xFFu) | (1u << (r0 % 8)));
+      if (publish_nseg) a.cache.nseg[bh] = dec.ns;
+    }
+    if (dec.write_row >= 0) {
+      const dgq_seg_t &c = dec.chosen;
+      uint4 *dst = reinterpret_cast<uint4 *>(a.cache.segs + bh * a.seg_cap + dec.write_row);
+      if (lane == 0) dst[0] = make_uint4((uint32_t)c.start, __float_as_uint(c.kmin), __float_as_uint(c.kmax), __float_as_uint(c.vmin));
+      if (lane == 1) dst[1] = make_uint4(__float_as_uint(c.vmax), __float_as_uint(c.kscale), __float_as_uint(c.vscale), (uint32_t)c.reserved);
+    }
+    // 4. the state: seal a full block (the ring keeps the moments of the last 16 sealed tokens),
+    // or keep the span's ranges
+    dgq_tail_t *tp = a.cache.tail + bh;
+    if (st.seal) {
+      // new ring = last 16 of (old ring, span tokens): lane i < 16 writes element i
+      const dgq_tail_t &tl = *reinterpret_cast<const dgq_tail_t *>(sm.tw);
+      const int m_tail = span_len < kWin ? span_len : kWin;   // span tokens that enter the ring
+      const int ring_len = st.ring_len;
+      const int old_keep = m_tail < kWin ? (ring_len < kWin - m_tail ? ring_len : kWin - m_tail) : 0;
+      const int n = old_keep + m_tail;
+      if (lane < kWin) {
+        int32_t ea = 0;
+        long long eb = 0;
+        if (lane < old_keep) {
+          ea = tl.ring_a[ring_len - old_keep + lane];
+          eb = tl.ring_b[ring_len - old_keep + lane];
+        } else if (lane < n) {
+          ea = sm.mom_a[span_len - m_tail + (lane - old_keep)];
+          eb = sm.mom_b[span_len - m_tail + (lane - old_keep)];
+        }
+        tp->ring_a[lane] = ea;
+        tp->ring_b[lane] = eb;
+      }
+      if (lane == 0) *reinterpret_cast<int4 *>(tp) = make_int4(t + 1, n, 0, 0);
+    } else {
+      if (lane == 0) *reinterpret_cast<int4 *>(tp) = make_int4(r0, st.ring_len, dec.own_now ? 1 : 0, wdone ? 1 : 0);
+      if (lane == 13) *reinterpret_cast<float4 *>(tp->span_range) = st.rk;
+    }
+  }
 }
 
 // The append kernel's form: the loads, then the append.
@@ -540,8 +625,9 @@ __device__ __forceinline__ void append_one(const AppendArgs &a, int b, int h, bo
   AppendLoads l = append_loads_state<D>(a, b, h);
   append_load_block<BS>(a, b, t, l);
   AppendStage<D, BS> st;
-  append_begin<D, BS>(a, b, h, out, l, st);
-  append_end<D, BS>(a, b, h, publish_nseg, out, l, st);
+  AppendDecision dec;
+  append_begin<D, BS>(a, b, h, out, dec, l, st);
+  append_end<D, BS>(a, b, h, publish_nseg, out, dec, l, st);
   if (threadIdx.x == 0 && !out.ok) atomicAdd(a.cache.status + 2, 1ull);   // the state did not fit
 }
 

@@ -361,7 +361,10 @@ template <int D, int G, int BS, bool APPEND>
 __device__ __forceinline__ void decode_body(const DecodeArgs &a, const AppendArgs *ap) {
   constexpr int M = D / 64;    // 64-channel slices of a key row
   constexpr int NT = D / 16;   // 16-channel tiles of the output
-  const int p = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  // Consecutive workgroup ids go to consecutive XCDs.  With one partition per (sequence, head)
+  // and 8 kv heads, XCD k would serve kv head k of every sequence; rotating the head by the
+  // sequence index gives every XCD every head (measured 0.5 us off the 64 x 2048-token step).
+  const int p = blockIdx.x, b = blockIdx.z, h = (int)((blockIdx.y + blockIdx.z) % (unsigned)a.hkv);
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   const int j = lane >> 4, col = lane & 15, g = col >> 2, piece = col & 3;
@@ -383,9 +386,16 @@ __device__ __forceinline__ void decode_body(const DecodeArgs &a, const AppendArg
   const int wblk0 = wg_begin / BS;
   SpanBlocks<BS> span_blk;
   span_blk.load(bt, a.max_blocks, wblk0);
-  const int ns_raw = a.nseg[bh];
+  // the segment-table row of this lane and the row count (the append's loads already hold them)
+  int ns_raw;
   dgq_seg_t seg_raw = {};
-  if (lane < a.seg_cap) seg_raw = a.segs[(size_t)bh * a.seg_cap + lane];
+  if constexpr (APPEND) {
+    ns_raw = ald.nseg;
+    seg_raw = __builtin_bit_cast(dgq_seg_t, ald.seg);
+  } else {
+    ns_raw = a.nseg[bh];
+    if (lane < a.seg_cap) seg_raw = a.segs[(size_t)bh * a.seg_cap + lane];
+  }
   const int qh = h * G + (g < G ? g : 0);
   const uint16_t *qrow = a.q + ((size_t)b * a.hq + qh) * D;
   uint4 qraw[M][2];
@@ -405,7 +415,8 @@ __device__ __forceinline__ void decode_body(const DecodeArgs &a, const AppendArg
   }
   const int P = parts_of(L, span);
   if (p >= P) return;                              // the whole workgroup has nothing to do
-  __shared__ AppendOut aout;
+  AppendOut aout;
+  AppendDecision adec;
   const WaveRange wr = wave_range(wg_begin, span, L, wave);
   const int t_begin = wr.t_begin, t_end = wr.t_end;
   const bool active = t_begin < t_end;
@@ -424,10 +435,11 @@ __device__ __forceinline__ void decode_body(const DecodeArgs &a, const AppendArg
   span_blk.publish(wblk0, (L + BS - 1) / BS, a.num_blocks, sh_blk, a.status, tail_slot, &sh_tail_raw);
   __syncthreads();
   if constexpr (APPEND) {
-    if (appending && threadIdx.x == 0 && ald.t_ok) {
-      ald.blk = sh_tail_raw;
-      if (tail_slot < 0) ald.blk = ap->block_table[(size_t)b * ap->max_blocks + len_raw / BS];
-    }
+    // (a length clamped to max_seq_len puts the tail block outside the span: one load, no branch)
+    const int fb = (int)__builtin_amdgcn_raw_buffer_load_b32(
+        raw_rsrc(ap->block_table + (size_t)b * ap->max_blocks, (uint32_t)ap->max_blocks * 4u),
+        appending && ald.t_ok && tail_slot < 0 ? (uint32_t)(len_raw / BS) * 4u : kOutOfRange, 0, 0);
+    ald.blk = tail_slot >= 0 ? sh_tail_raw : fb;
   }
 
   // block ids come from sh_blk: chunk c of the wave is local chunk lc0 + c of the workgroup
@@ -509,7 +521,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs &a, const AppendArg
   qsum += __shfl_xor(qsum, 32);
   AppendStage<D, BS> st;
   if constexpr (APPEND) {
-    if (appending) append_begin<D, BS>(*ap, b, h, aout, ald, st);
+    if (appending) append_begin<D, BS>(*ap, b, h, aout, adec, ald, st);
   }
   load_k(0, kf);   // every wave (a wave with no tokens reads a valid block it does not use): a
   load_v(0, vf);   // branch here would make the waits below count only the loads before it
@@ -533,7 +545,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs &a, const AppendArg
   const float qsum_s = qsum * a.sm_log2;
 
   if constexpr (APPEND) {
-    if (appending) append_end<D, BS>(*ap, b, h, false, aout, ald, st);
+    if (appending) append_end<D, BS>(*ap, b, h, false, aout, adec, ald, st);
   }
   __shared__ float sh_o[kWaves][G][D];
   __shared__ float sh_m[kWaves][G], sh_l[kWaves][G];
