@@ -212,6 +212,8 @@ __device__ __forceinline__ AppendDecision append_decide(bool want, bool own, int
 //
 // With publish_nseg false the new row count is left to the caller (out.ns): a fused decode
 // publishes it only after every workgroup of the same (sequence, head) has read the old count.
+constexpr int kNewTokenWave = 3;   // the last of the workgroup's four waves
+
 template <int D, int BS>
 struct AppendShared {
   uint8_t vimg[BS * D];          // value codes of the tail block (re-encoded spans), words swizzled
@@ -245,6 +247,28 @@ __device__ __forceinline__ int vword_token(int W, int e) {
   if constexpr (BS == 64) return 16 * (e >> 2) + 4 * ((W >> 4) & 3) + (e & 3);
   else if constexpr (BS == 32) return 16 * (W / D) + e;
   else return e;
+}
+
+// Codes of up to four values packed into the bytes of one word (byte e = value e), the same steps
+// as dgq_encode_value: the difference and the product in float32, the clamp to [0, levels], then
+// the packing conversion, which rounds to nearest even (and clamps to [0, 255]); a NaN gives 0, as
+// there.  code_bytes then adds the code of the minimum to every byte, modulo 256, without carries.
+template <int N>
+__device__ __forceinline__ uint32_t encode_packed(const float (&x)[N], float mn, float inv, float levels) {
+#pragma clang fp contract(off)
+  static_assert(N >= 1 && N <= 4, "one word");
+  uint32_t w = 0u;
+#pragma unroll
+  for (int e = 0; e < N; ++e) {
+    const float dlt = x[e] - mn;
+    const float u = fminf(fmaxf(dlt * inv, 0.0f), levels);
+    w = __builtin_amdgcn_cvt_pk_u8_f32(u, (uint32_t)e, w);
+  }
+  return w;
+}
+__device__ __forceinline__ uint32_t code_bytes(uint32_t w, int low) {
+  const uint32_t c = ((uint32_t)low & 0xFFu) * 0x01010101u;
+  return ((w & 0x7F7F7F7Fu) + (c & 0x7F7F7F7Fu)) ^ ((w ^ c) & 0x80808080u);
 }
 
 // What append_begin hands to append_end (uniform across the workgroup, except the staged units,
@@ -489,22 +513,22 @@ __device__ __forceinline__ void append_end(const AppendArgs &a, int b, int h, bo
   const bool mark = a.fmt.marker && dec.own_now && r0 > 0;
   int8_t *kt = a.cache.k_pool + ((size_t)st.blk * a.hkv + h) * (size_t)BS * D;
   int8_t *vt = a.cache.v_pool + ((size_t)st.blk * a.hkv + h) * (size_t)BS * D;
-  if (wave == 0 && lane < D / 2) {
+  // (by the last wave: it has the fewest span units, as units go to threads in order)
+  if (wave == kNewTokenWave && lane < D / 2) {
     // the new token, channels 2 lane and 2 lane + 1, and its staging copy
     *reinterpret_cast<uint32_t *>(a.cache.k_stage + (bh * BS + slot) * D + 2 * lane) = ld.kp;
     *reinterpret_cast<uint32_t *>(a.cache.v_stage + (bh * BS + slot) * D + 2 * lane) = ld.vp;
-    uint32_t kc = (uint32_t)(dgq_encode_value(k0, row.kmin, kinv, lv, low) & 0xFF) |
-                  ((uint32_t)(dgq_encode_value(k1, row.kmin, kinv, lv, low) & 0xFF) << 8);
+    const float kx[2] = {k0, k1}, vx[2] = {v0, v1};
+    uint32_t kc = code_bytes(encode_packed(kx, row.kmin, kinv, lv), low);
     if (mark && slot == slot0 && lane == 0) kc = (kc & ~0xFFu) | dgq_marker_byte(kc & 0xFFu);
     *reinterpret_cast<uint16_t *>(kt + k_tile_offset<D, BS>(slot, 2 * lane)) = (uint16_t)kc;
-    const int8_t vc0 = (int8_t)dgq_encode_value(v0, row.vmin, vinv, lv, low);
-    const int8_t vc1 = (int8_t)dgq_encode_value(v1, row.vmin, vinv, lv, low);
+    const uint32_t vc = code_bytes(encode_packed(vx, row.vmin, vinv, lv), low);
     if (dec.all) {
-      sm.vimg[vimg_byte<D, BS>(slot, 2 * lane)] = (uint8_t)vc0;
-      sm.vimg[vimg_byte<D, BS>(slot, 2 * lane + 1)] = (uint8_t)vc1;
+      sm.vimg[vimg_byte<D, BS>(slot, 2 * lane)] = (uint8_t)vc;
+      sm.vimg[vimg_byte<D, BS>(slot, 2 * lane + 1)] = (uint8_t)(vc >> 8);
     } else {
-      vt[v_tile_offset<D, BS>(slot, 2 * lane)] = vc0;
-      vt[v_tile_offset<D, BS>(slot, 2 * lane + 1)] = vc1;
+      vt[v_tile_offset<D, BS>(slot, 2 * lane)] = (int8_t)vc;
+      vt[v_tile_offset<D, BS>(slot, 2 * lane + 1)] = (int8_t)(vc >> 8);
     }
   }
   if (dec.all) {
@@ -517,14 +541,18 @@ __device__ __forceinline__ void append_end(const AppendArgs &a, int b, int h, bo
         const int s = slot0 + u / CPU, d0 = 8 * (u % CPU);
         const uint32_t kh[4] = {st.kw[i].x, st.kw[i].y, st.kw[i].z, st.kw[i].w};
         const uint32_t vh[4] = {st.vw[i].x, st.vw[i].y, st.vw[i].z, st.vw[i].w};
-        uint32_t kc[2] = {0u, 0u};
+        uint32_t kc[2], vc[2];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float kx = half_bits_to_float(e & 1 ? kh[e >> 1] >> 16 : kh[e >> 1] & 0xFFFFu);
-          const float vx = half_bits_to_float(e & 1 ? vh[e >> 1] >> 16 : vh[e >> 1] & 0xFFFFu);
-          kc[e >> 2] |= (uint32_t)(dgq_encode_value(kx, row.kmin, kinv, lv, low) & 0xFF) << (8 * (e & 3));
-          sm.vimg[vimg_byte<D, BS>(s, d0 + e)] = (uint8_t)dgq_encode_value(vx, row.vmin, vinv, lv, low);
+        for (int hw = 0; hw < 2; ++hw) {
+          const float kx[4] = {half_bits_to_float(kh[2 * hw] & 0xFFFFu), half_bits_to_float(kh[2 * hw] >> 16),
+                               half_bits_to_float(kh[2 * hw + 1] & 0xFFFFu), half_bits_to_float(kh[2 * hw + 1] >> 16)};
+          const float vx[4] = {half_bits_to_float(vh[2 * hw] & 0xFFFFu), half_bits_to_float(vh[2 * hw] >> 16),
+                               half_bits_to_float(vh[2 * hw + 1] & 0xFFFFu), half_bits_to_float(vh[2 * hw + 1] >> 16)};
+          kc[hw] = code_bytes(encode_packed(kx, row.kmin, kinv, lv), low);
+          vc[hw] = code_bytes(encode_packed(vx, row.vmin, vinv, lv), low);
         }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sm.vimg[vimg_byte<D, BS>(s, d0 + e)] = (uint8_t)(vc[e >> 2] >> (8 * (e & 3)));
         if (mark && s == slot0 && d0 == 0) kc[0] = (kc[0] & ~0xFFu) | dgq_marker_byte(kc[0] & 0xFFu);
         *reinterpret_cast<uint2 *>(kt + k_tile_offset<D, BS>(s, d0)) = make_uint2(kc[0], kc[1]);
       }
@@ -536,7 +564,11 @@ __device__ __forceinline__ void append_end(const AppendArgs &a, int b, int h, bo
 #pragma unroll
     for (int k = 0; k < AppendStage<D, BS>::VW; ++k) {
       const int W = tid + 256 * k;
-      if (W < AppendStage<D, BS>::VWORDS) {
+      if (W < AppendStage<D, BS>::VWORDS && slot0 == 0) {
+        // the span starts the block: a word holds a span token iff its first byte's token does
+        if (vword_token<D, BS>(W, 0) <= slot)
+          *reinterpret_cast<uint4 *>(vt + W * 16) = *reinterpret_cast<const uint4 *>(&sm.vimg[vimg_word<BS>(W) << 4]);
+      } else if (W < AppendStage<D, BS>::VWORDS) {
         uint32_t span_m = 0u, frozen_m = 0u;
 #pragma unroll
         for (int e = 0; e < 16; ++e) {

@@ -38,7 +38,9 @@ template <int D, int G, int BS>
 __global__ __launch_bounds__(64 * kWaves, 2) void decode_partition_kernel(DecodeArgs a) {
   constexpr int M = D / 64;    // 64-channel slices of a key row
   constexpr int NT = D / 16;   // 16-channel tiles of the output
-  const int p = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  // the kv head is rotated by the sequence index, so that every XCD serves every head (see
+  // decode_body)
+  const int p = blockIdx.x, b = blockIdx.z, h = (int)((blockIdx.y + blockIdx.z) % (unsigned)a.hkv);
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   const int j = lane >> 4, col = lane & 15, g = col >> 2, piece = col & 3;

@@ -191,7 +191,9 @@ template <int D, int G, int BS>
 __global__ __launch_bounds__(64 * kWaves, 2) void g64_decode_kernel(DecodeArgs a) {
   constexpr int M = D / 64;    // channel groups = 64-channel slices
   constexpr int NT = D / 16;
-  const int p = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  // the kv head is rotated by the sequence index, as in the DGQ decode, so that every XCD serves
+  // every head
+  const int p = blockIdx.x, b = blockIdx.z, h = (int)((blockIdx.y + blockIdx.z) % (unsigned)a.hkv);
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   const int j = lane >> 4, col = lane & 15, g = col >> 2, piece = col & 3;
