@@ -141,6 +141,7 @@ struct AppendDecision {
   bool own_now;       // the span has its own row after the append
   bool all;           // the span's range changed: every span code is rewritten
   bool full;          // a row of its own was wanted but the table is full (the span joins)
+  bool wdone;         // the window test has said "no change" for this span
 };
 
 // want: the span should have its own row (it has one, its range left the row before it, or the
@@ -156,6 +157,7 @@ __device__ __forceinline__ AppendDecision append_decide(bool want, bool own, int
   d.own_now = own;
   d.all = false;
   d.full = false;
+  d.wdone = false;
   if (want && !own) {
     if (ns >= seg_cap) {
       d.full = true;
@@ -214,8 +216,19 @@ __device__ __forceinline__ AppendDecision append_decide(bool want, bool own, int
 // publishes it only after every workgroup of the same (sequence, head) has read the old count.
 constexpr int kNewTokenWave = 3;   // the last of the workgroup's four waves
 
+// What the state stores need, kept in LDS from the decision to the stores (a fused decode makes
+// them after its chunks, and registers held that long would crowd the decode loop).
+struct AppendPending {
+  dgq_seg_t chosen;
+  float4 rk;
+  int t, r0, span_len, ring_len, blk, ns, write_row, nbad;
+  uint32_t bits_old;
+  int go, full, new_row, own_now, wdone, seal;
+};
+
 template <int D, int BS>
 struct AppendShared {
+  AppendPending pend;
   uint8_t vimg[BS * D];          // value codes of the tail block (re-encoded spans), words swizzled
   uint4 tw[kTailWords];          // the state words (window test and seal)
   int mom_a[BS];                 // fixed-point moments of the span's tokens (span-relative index)
@@ -372,6 +385,12 @@ __device__ __forceinline__ void append_begin(const AppendArgs &a, int b, int h, 
   const bool seal = go && (t + 1) % BS == 0;
   const bool staged = go && (may_reenc || window_test || seal);
   dec = append_decide(own || may_reenc, own, ns, a.seg_cap, r0, R, rk, a.fmt.levels);
+  dec.wdone = wdone;
+  if (go) {
+    out.ns = dec.ns;
+    out.use_row = dec.use_row;
+    out.chosen = dec.chosen;
+  }
 
   // 4. buffer loads of the earlier span tokens (the new one comes from the registers of wave 0),
   // every one issued: a unit that is not needed gets an offset past the resource (zero, no memory
@@ -418,22 +437,73 @@ __device__ __forceinline__ void append_begin(const AppendArgs &a, int b, int h, 
   st.seal = seal;
 }
 
+// The row the span is encoded with, and where its codes go.
 template <int D, int BS>
-__device__ __forceinline__ void append_end(const AppendArgs &a, int b, int h, bool publish_nseg, AppendOut &out,
-                                           AppendDecision &dec, const AppendLoads &ld, const AppendStage<D, BS> &st) {
-  if (!st.go) return;
+struct AppendCoder {
+  dgq_seg_t row;
+  float kinv, vinv, lv;
+  int low;
+  bool mark;   // marker format: the span's own segment starts at r0, whose first key byte is the marker
+  int8_t *kt, *vt;
+  __device__ __forceinline__ AppendCoder(const AppendArgs &a, int h, const AppendDecision &dec, const AppendStage<D, BS> &st)
+      : row(dec.chosen), lv(a.fmt.levels), low(a.fmt.low) {
+    kinv = dgq_inv(row.kmin, row.kmax, lv);
+    vinv = dgq_inv(row.vmin, row.vmax, lv);
+    mark = a.fmt.marker && dec.own_now && st.r0 > 0;
+    kt = a.cache.k_pool + ((size_t)st.blk * a.hkv + h) * (size_t)BS * D;
+    vt = a.cache.v_pool + ((size_t)st.blk * a.hkv + h) * (size_t)BS * D;
+  }
+};
+
+// The new token's codes and staging copy, by one wave (lane l < D/2: channels 2l and 2l + 1); its
+// value codes go into the value image when the whole span is re-encoded.
+template <int D, int BS>
+__device__ __forceinline__ void append_new_token(const AppendArgs &a, int b, int h, const AppendDecision &dec,
+                                                 const AppendLoads &ld, const AppendStage<D, BS> &st) {
+  const int lane = threadIdx.x & 63;
+  if (lane >= D / 2) return;
+  const size_t bh = (size_t)b * a.hkv + h;
+  const int slot = st.t % BS;
+  const AppendCoder<D, BS> cd(a, h, dec, st);
+  *reinterpret_cast<uint32_t *>(a.cache.k_stage + (bh * BS + slot) * D + 2 * lane) = ld.kp;
+  *reinterpret_cast<uint32_t *>(a.cache.v_stage + (bh * BS + slot) * D + 2 * lane) = ld.vp;
+  const float kx[2] = {half_bits_to_float(ld.kp & 0xFFFFu), half_bits_to_float(ld.kp >> 16)};
+  const float vx[2] = {half_bits_to_float(ld.vp & 0xFFFFu), half_bits_to_float(ld.vp >> 16)};
+  uint32_t kc = code_bytes(encode_packed(kx, cd.row.kmin, cd.kinv, cd.lv), cd.low);
+  if (cd.mark && slot == st.slot0 && lane == 0) kc = (kc & ~0xFFu) | dgq_marker_byte(kc & 0xFFu);
+  *reinterpret_cast<uint16_t *>(cd.kt + k_tile_offset<D, BS>(slot, 2 * lane)) = (uint16_t)kc;
+  const uint32_t vc = code_bytes(encode_packed(vx, cd.row.vmin, cd.vinv, cd.lv), cd.low);
+  if (dec.all) {
+    AppendShared<D, BS> &sm = append_shared<D, BS>();
+    sm.vimg[vimg_byte<D, BS>(slot, 2 * lane)] = (uint8_t)vc;
+    sm.vimg[vimg_byte<D, BS>(slot, 2 * lane + 1)] = (uint8_t)(vc >> 8);
+  } else {
+    cd.vt[v_tile_offset<D, BS>(slot, 2 * lane)] = (int8_t)vc;
+    cd.vt[v_tile_offset<D, BS>(slot, 2 * lane + 1)] = (int8_t)(vc >> 8);
+  }
+}
+
+// Whether the step needs the whole workgroup (the window test, a seal or a re-encoded span); the
+// other steps write only the new token's codes, which one wave does without a barrier.
+template <int D, int BS>
+__device__ __forceinline__ bool append_needs_span(const AppendDecision &dec, const AppendStage<D, BS> &st) {
+  return st.go && (dec.all || st.window_test || st.seal);
+}
+
+// The whole-workgroup part of a step: the window test and the ring moments, the span's encode and
+// the new token's codes, then a barrier, which orders the code stores before any later load of
+// the tail block by the same workgroup (workgroup scope: one compute unit, in-order vector memory).
+template <int D, int BS>
+__device__ __forceinline__ void append_span(const AppendArgs &a, int b, int h, AppendOut &out, AppendDecision &dec,
+                                            const AppendLoads &ld, const AppendStage<D, BS> &st) {
   constexpr int CPU = AppendStage<D, BS>::CPU;
   constexpr int UPT = AppendStage<D, BS>::UPT;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const size_t bh = (size_t)b * a.hkv + h;
   AppendShared<D, BS> &sm = append_shared<D, BS>();
   const int t = st.t, r0 = st.r0, slot0 = st.slot0, span_len = st.span_len;
   const int slot = t % BS;
   const int nold = st.nunits - CPU;   // staged units (the span tokens before the new one)
-  // the new token's channels 2 lane and 2 lane + 1 (lanes < D/2 of every wave)
   const float k0 = half_bits_to_float(ld.kp & 0xFFFFu), k1 = half_bits_to_float(ld.kp >> 16);
-  const float v0 = half_bits_to_float(ld.vp & 0xFFFFu), v1 = half_bits_to_float(ld.vp >> 16);
-  bool wdone = st.wdone;
 
   // 1. window test and seal: the fixed-point moments of the span's tokens (the CPU units of a
   // token sit in CPU consecutive lanes of one pass; the new token's from wave 0's channel pairs)
@@ -498,40 +568,25 @@ __device__ __forceinline__ void append_end(const AppendArgs &a, int b, int h, bo
       const long long hi = ql > qr ? ql : qr, lo = ql > qr ? qr : ql;
       const bool want = __builtin_amdgcn_readfirstlane(
                             (!((double)hi < a.qfloor) && (double)(hi + 1) / (double)(lo + 1) >= a.tau) ? 1 : 0) != 0;
-      if (!want) wdone = true;
       dec = append_decide(want, false, st.ns, a.seg_cap, r0, st.R, st.rk, a.fmt.levels);
+      dec.wdone = !want;
+      out.ns = dec.ns;
+      out.use_row = dec.use_row;
+      out.chosen = dec.chosen;
     }
   }
 
   // 2. encode with the chosen row: the whole span when that range changed (a new row, or the
-  // span's own row widened), else only the new token (every other span code is unchanged)
-  const dgq_seg_t row = dec.chosen;
-  const float lv = a.fmt.levels;
-  const int low = a.fmt.low;
-  const float kinv = dgq_inv(row.kmin, row.kmax, lv), vinv = dgq_inv(row.vmin, row.vmax, lv);
-  // marker format: the span's own segment starts at r0, whose first key byte is the marker
-  const bool mark = a.fmt.marker && dec.own_now && r0 > 0;
-  int8_t *kt = a.cache.k_pool + ((size_t)st.blk * a.hkv + h) * (size_t)BS * D;
-  int8_t *vt = a.cache.v_pool + ((size_t)st.blk * a.hkv + h) * (size_t)BS * D;
-  // (by the last wave: it has the fewest span units, as units go to threads in order)
-  if (wave == kNewTokenWave && lane < D / 2) {
-    // the new token, channels 2 lane and 2 lane + 1, and its staging copy
-    *reinterpret_cast<uint32_t *>(a.cache.k_stage + (bh * BS + slot) * D + 2 * lane) = ld.kp;
-    *reinterpret_cast<uint32_t *>(a.cache.v_stage + (bh * BS + slot) * D + 2 * lane) = ld.vp;
-    const float kx[2] = {k0, k1}, vx[2] = {v0, v1};
-    uint32_t kc = code_bytes(encode_packed(kx, row.kmin, kinv, lv), low);
-    if (mark && slot == slot0 && lane == 0) kc = (kc & ~0xFFu) | dgq_marker_byte(kc & 0xFFu);
-    *reinterpret_cast<uint16_t *>(kt + k_tile_offset<D, BS>(slot, 2 * lane)) = (uint16_t)kc;
-    const uint32_t vc = code_bytes(encode_packed(vx, row.vmin, vinv, lv), low);
-    if (dec.all) {
-      sm.vimg[vimg_byte<D, BS>(slot, 2 * lane)] = (uint8_t)vc;
-      sm.vimg[vimg_byte<D, BS>(slot, 2 * lane + 1)] = (uint8_t)(vc >> 8);
-    } else {
-      vt[v_tile_offset<D, BS>(slot, 2 * lane)] = (int8_t)vc;
-      vt[v_tile_offset<D, BS>(slot, 2 * lane + 1)] = (int8_t)(vc >> 8);
-    }
-  }
+  // span's own row widened), else only the new token (every other span code is unchanged); the
+  // new token by the last wave, which has the fewest span units (units go to threads in order)
+  if (wave == kNewTokenWave) append_new_token<D, BS>(a, b, h, dec, ld, st);
   if (dec.all) {
+    const AppendCoder<D, BS> cd(a, h, dec, st);
+    const dgq_seg_t &row = cd.row;
+    const float kinv = cd.kinv, vinv = cd.vinv, lv = cd.lv;
+    const int low = cd.low;
+    const bool mark = cd.mark;
+    int8_t *kt = cd.kt, *vt = cd.vt;
     // the earlier span tokens, from the staged units: 8 key codes stored as 8 contiguous bytes of
     // the tile, 8 value codes into the image
 #pragma unroll
@@ -596,57 +651,85 @@ __device__ __forceinline__ void append_end(const AppendArgs &a, int b, int h, bo
     }
   }
 
-  // 3. the code stores above come before any load of the tail block by this workgroup after this
-  // barrier (workgroup scope: one compute unit, in-order vector memory), and every wave has read
-  // the state that the stores below replace
   __syncthreads();
-  out.ok = 1;
-  out.ns = dec.ns;
-  out.use_row = dec.use_row;
-  out.chosen = dec.chosen;
-  if (wave == 0) {
-    if (lane == 0) {
-      if (st.nbad > 0) atomicAdd(a.cache.status + 1, (unsigned long long)st.nbad);
-      if (dec.full) atomicAdd(a.cache.status + 0, 1ull);   // the table is full: the span joins the row before it
-      if (dec.new_row && r0 > 0 && !a.fmt.marker)
-        a.cache.bits[((size_t)st.blk * a.hkv + h) * (BS / 8) + (r0 % BS) / 8] =
-            (uint8_t)((st.bits_old & 0xFFu) | (1u << (r0 % 8)));
-      if (publish_nseg) a.cache.nseg[bh] = dec.ns;
-    }
-    if (dec.write_row >= 0) {
-      const dgq_seg_t &c = dec.chosen;
-      uint4 *dst = reinterpret_cast<uint4 *>(a.cache.segs + bh * a.seg_cap + dec.write_row);
-      if (lane == 0) dst[0] = make_uint4((uint32_t)c.start, __float_as_uint(c.kmin), __float_as_uint(c.kmax), __float_as_uint(c.vmin));
-      if (lane == 1) dst[1] = make_uint4(__float_as_uint(c.vmax), __float_as_uint(c.kscale), __float_as_uint(c.vscale), (uint32_t)c.reserved);
-    }
-    // 4. the state: seal a full block (the ring keeps the moments of the last 16 sealed tokens),
-    // or keep the span's ranges
-    dgq_tail_t *tp = a.cache.tail + bh;
-    if (st.seal) {
-      // new ring = last 16 of (old ring, span tokens): lane i < 16 writes element i
-      const dgq_tail_t &tl = *reinterpret_cast<const dgq_tail_t *>(sm.tw);
-      const int m_tail = span_len < kWin ? span_len : kWin;   // span tokens that enter the ring
-      const int ring_len = st.ring_len;
-      const int old_keep = m_tail < kWin ? (ring_len < kWin - m_tail ? ring_len : kWin - m_tail) : 0;
-      const int n = old_keep + m_tail;
-      if (lane < kWin) {
-        int32_t ea = 0;
-        long long eb = 0;
-        if (lane < old_keep) {
-          ea = tl.ring_a[ring_len - old_keep + lane];
-          eb = tl.ring_b[ring_len - old_keep + lane];
-        } else if (lane < n) {
-          ea = sm.mom_a[span_len - m_tail + (lane - old_keep)];
-          eb = sm.mom_b[span_len - m_tail + (lane - old_keep)];
-        }
-        tp->ring_a[lane] = ea;
-        tp->ring_b[lane] = eb;
+}
+
+// The decision as the state stores need it, into LDS (thread 0).
+template <int D, int BS>
+__device__ __forceinline__ void append_stash(const AppendDecision &dec, const AppendStage<D, BS> &st) {
+  if (threadIdx.x != 0) return;
+  AppendPending &pd = append_shared<D, BS>().pend;
+  pd.chosen = dec.chosen;
+  pd.rk = st.rk;
+  pd.t = st.t;
+  pd.r0 = st.r0;
+  pd.span_len = st.span_len;
+  pd.ring_len = st.ring_len;
+  pd.blk = st.blk;
+  pd.ns = dec.ns;
+  pd.write_row = dec.write_row;
+  pd.nbad = st.nbad;
+  pd.bits_old = st.bits_old;
+  pd.go = st.go;
+  pd.full = dec.full;
+  pd.new_row = dec.new_row;
+  pd.own_now = dec.own_now;
+  pd.wdone = dec.wdone;
+  pd.seal = st.seal;
+}
+
+// The state an append leaves (by wave 0, from what append_stash kept; every wave must have read
+// the state first): the status counts, the segment row, the bitmap byte, the row count
+// (publish_nseg) and the append state.
+template <int D, int BS>
+__device__ __forceinline__ void append_store_state(const AppendArgs &a, int b, int h, bool publish_nseg) {
+  const int lane = threadIdx.x & 63;
+  if ((threadIdx.x >> 6) != 0) return;
+  AppendShared<D, BS> &sm = append_shared<D, BS>();
+  const AppendPending &pd = sm.pend;
+  if (!pd.go) return;
+  const size_t bh = (size_t)b * a.hkv + h;
+  const int t = pd.t, r0 = pd.r0, span_len = pd.span_len, ring_len = pd.ring_len;
+  if (lane == 0) {
+    if (pd.nbad > 0) atomicAdd(a.cache.status + 1, (unsigned long long)pd.nbad);
+    if (pd.full) atomicAdd(a.cache.status + 0, 1ull);   // the table is full: the span joins the row before it
+    if (pd.new_row && r0 > 0 && !a.fmt.marker)
+      a.cache.bits[((size_t)pd.blk * a.hkv + h) * (BS / 8) + (r0 % BS) / 8] =
+          (uint8_t)((pd.bits_old & 0xFFu) | (1u << (r0 % 8)));
+    if (publish_nseg) a.cache.nseg[bh] = pd.ns;
+  }
+  if (pd.write_row >= 0) {
+    const dgq_seg_t &c = pd.chosen;
+    uint4 *dst = reinterpret_cast<uint4 *>(a.cache.segs + bh * a.seg_cap + pd.write_row);
+    if (lane == 0) dst[0] = make_uint4((uint32_t)c.start, __float_as_uint(c.kmin), __float_as_uint(c.kmax), __float_as_uint(c.vmin));
+    if (lane == 1) dst[1] = make_uint4(__float_as_uint(c.vmax), __float_as_uint(c.kscale), __float_as_uint(c.vscale), (uint32_t)c.reserved);
+  }
+  // the state: seal a full block (the ring keeps the moments of the last 16 sealed tokens), or
+  // keep the span's ranges
+  dgq_tail_t *tp = a.cache.tail + bh;
+  if (pd.seal) {
+    // new ring = last 16 of (old ring, span tokens): lane i < 16 writes element i
+    const dgq_tail_t &tl = *reinterpret_cast<const dgq_tail_t *>(sm.tw);
+    const int m_tail = span_len < kWin ? span_len : kWin;   // span tokens that enter the ring
+    const int old_keep = m_tail < kWin ? (ring_len < kWin - m_tail ? ring_len : kWin - m_tail) : 0;
+    const int n = old_keep + m_tail;
+    if (lane < kWin) {
+      int32_t ea = 0;
+      long long eb = 0;
+      if (lane < old_keep) {
+        ea = tl.ring_a[ring_len - old_keep + lane];
+        eb = tl.ring_b[ring_len - old_keep + lane];
+      } else if (lane < n) {
+        ea = sm.mom_a[span_len - m_tail + (lane - old_keep)];
+        eb = sm.mom_b[span_len - m_tail + (lane - old_keep)];
       }
-      if (lane == 0) *reinterpret_cast<int4 *>(tp) = make_int4(t + 1, n, 0, 0);
-    } else {
-      if (lane == 0) *reinterpret_cast<int4 *>(tp) = make_int4(r0, st.ring_len, dec.own_now ? 1 : 0, wdone ? 1 : 0);
-      if (lane == 13) *reinterpret_cast<float4 *>(tp->span_range) = st.rk;
+      tp->ring_a[lane] = ea;
+      tp->ring_b[lane] = eb;
     }
+    if (lane == 0) *reinterpret_cast<int4 *>(tp) = make_int4(t + 1, n, 0, 0);
+  } else {
+    if (lane == 0) *reinterpret_cast<int4 *>(tp) = make_int4(r0, ring_len, pd.own_now, pd.wdone);
+    if (lane == 13) *reinterpret_cast<float4 *>(tp->span_range) = pd.rk;
   }
 }
 
@@ -659,7 +742,11 @@ __device__ __forceinline__ void append_one(const AppendArgs &a, int b, int h, bo
   AppendStage<D, BS> st;
   AppendDecision dec;
   append_begin<D, BS>(a, b, h, out, dec, l, st);
-  append_end<D, BS>(a, b, h, publish_nseg, out, dec, l, st);
+  if (append_needs_span(dec, st)) append_span<D, BS>(a, b, h, out, dec, l, st);
+  else if (st.go && (threadIdx.x >> 6) == kNewTokenWave) append_new_token<D, BS>(a, b, h, dec, l, st);
+  append_stash<D, BS>(dec, st);
+  __syncthreads();   // every wave has read the state
+  append_store_state<D, BS>(a, b, h, publish_nseg);
   if (threadIdx.x == 0 && !out.ok) atomicAdd(a.cache.status + 2, 1ull);   // the state did not fit
 }
 

@@ -487,13 +487,11 @@ __device__ __forceinline__ void decode_body(const DecodeArgs &a, const AppendArg
       for (int n = 0; n < NT; ++n) vf[n] = load_codes(vb + (16 * n + (lane & 15)) * 16);
     }
   };
-  // The workgroup that appends requests each wave's first chunk between the two halves of the
-  // append: after the loads of the append state and of the staging copy it may need (loads
-  // return in issue order, so the append does not wait behind the chunk), before the decision and
-  // the encode, so that the chunk streams in while they run.  The query is prepared meanwhile,
-  // while the staging copy is on its way.  The chunk is kept when none of its tokens is in the
-  // tail block (the only block the append writes); otherwise (or for a wave with no tokens) it is
-  // requested again afterwards.  Other workgroups request the chunk first, then prepare the query.
+  // The workgroup that appends requests each wave's first chunk after the append's decision and
+  // the loads of the staging copy it may need (loads return in issue order, so the append does not
+  // wait behind the chunk), before the encode, so that the chunk streams in while it runs.  The
+  // chunk is kept when none of its tokens is in the tail block (the only block the append writes);
+  // otherwise (or for a wave with no tokens) it is requested again afterwards.
   v4i kf[4][M];
   v4i vf[NT];
   const int tail_start = (L - 1) / BS * BS;
@@ -547,7 +545,18 @@ __device__ __forceinline__ void decode_body(const DecodeArgs &a, const AppendArg
   const float qsum_s = qsum * a.sm_log2;
 
   if constexpr (APPEND) {
-    if (appending) append_end<D, BS>(*ap, b, h, false, aout, adec, ald, st);
+    // a step that re-encodes the span, tests its window or seals the block takes the whole
+    // workgroup (with barriers); any other step writes only the new token's codes, which the wave
+    // that decodes the tail block does itself before it reads that block (its own stores precede
+    // its own loads), so the other waves start their chunks at once
+    // (a length clamped to max_seq_len leaves the new token outside every wave's tokens: then a
+    // fixed wave writes it, as the append kernel does)
+    if (appending) {
+      const bool writes_token = ald.t == L - 1 ? active && t_begin <= L - 1 && L - 1 < t_end : wave == kNewTokenWave;
+      if (append_needs_span(adec, st)) append_span<D, BS>(*ap, b, h, aout, adec, ald, st);
+      else if (st.go && writes_token) append_new_token<D, BS>(*ap, b, h, adec, ald, st);
+      append_stash<D, BS>(adec, st);
+    }
   }
   __shared__ float sh_o[kWaves][G][D];
   __shared__ float sh_m[kWaves][G], sh_l[kWaves][G];
@@ -733,6 +742,11 @@ __device__ __forceinline__ void decode_body(const DecodeArgs &a, const AppendArg
     sh_l[wave][g] = active ? l_run : 0.f;
   }
   const int done = finish_partition<D, G>(a, b, h, p, L, sh_o, sh_m, sh_l, APPEND && p == P - 1 ? aout.ns : -1);
+  if constexpr (APPEND) {
+    // the append's state stores: every wave has passed the merge's first barrier, so none is
+    // still reading the state; nothing in this launch reads what they write
+    if (appending) append_store_state<D, BS>(*ap, b, h, false);
+  }
   // an append whose state did not fit the new position (nothing was appended) is counted once
   if (appending && threadIdx.x == 0 && !aout.ok) atomicAdd(ap->cache.status + 2, 1ull);
   if (APPEND && done != kPartialOnly && threadIdx.x == 0) {
