@@ -487,17 +487,21 @@ __device__ __forceinline__ void decode_body(const DecodeArgs &a, const AppendArg
       for (int n = 0; n < NT; ++n) vf[n] = load_codes(vb + (16 * n + (lane & 15)) * 16);
     }
   };
-  // The workgroup that appends requests each wave's first chunk after the append's decision and
-  // the loads of the staging copy it may need (loads return in issue order, so the append does not
-  // wait behind the chunk), before the encode, so that the chunk streams in while it runs.  The
-  // chunk is kept when none of its tokens is in the tail block (the only block the append writes);
-  // otherwise (or for a wave with no tokens) it is requested again afterwards.
+  // Every workgroup requests each wave's first chunk as soon as it has the block ids, the one that
+  // appends too: its common steps need no load after the append's own (issued at the start), and
+  // a step that re-encodes the span waits for its staging copy behind the chunk (loads return in
+  // issue order), which costs those few workgroups less than a later first chunk costs all of
+  // them (58.0 against 59.7 us per streaming step).  The chunk is kept when none of its tokens is
+  // in the tail block (the only block the append writes); otherwise (or for a wave with no
+  // tokens) it is requested again after the append.
   v4i kf[4][M];
   v4i vf[NT];
   const int tail_start = (L - 1) / BS * BS;
   const bool early = appending && active && t_begin + kChunk <= tail_start;
+  load_k(0, kf);   // every wave (a wave with no tokens reads a valid block it does not use): a
+  load_v(0, vf);   // branch here would make the waits below count only the loads before it
   // ---- query: three signed bytes per channel, one per column of the B operand (its fp16 values
-  // are read here, before any load the append adds) ----
+  // were requested at the start, ahead of the chunk) ----
   float qv[M][16];
   float amax = 0.f, qsum = 0.f;
 #pragma unroll
@@ -523,8 +527,6 @@ __device__ __forceinline__ void decode_body(const DecodeArgs &a, const AppendArg
   if constexpr (APPEND) {
     if (appending) append_begin<D, BS>(*ap, b, h, aout, adec, ald, st);
   }
-  load_k(0, kf);   // every wave (a wave with no tokens reads a valid block it does not use): a
-  load_v(0, vf);   // branch here would make the waits below count only the loads before it
   int qexp = 0;
   if (amax > 0.f) {
     int ex;
