@@ -118,3 +118,62 @@ def test_fused_marker_format():
     cfg = dgq_data.get_config(5, batch=2, seq_len=260, append_steps=90)
     H.say("fused marker format")
     run_fused(cfg, 44, 90, (0, 45, 89), params=H.params_for(cfg, marker=True))
+
+
+def _fused_vs_separate(cfg, seed, steps, max_seq_len, corrupt=None):
+    """Both paths on two copies of one compressed cache with the given max_seq_len (which may
+    clamp the decode), optionally with one (sequence, head)'s append state made inconsistent in
+    both copies; outputs, caches and status words must agree at every step."""
+    k, v, cu, lens = dgq_data.batch_kv(cfg, seed)
+    lens = np.asarray(lens, np.int64)
+    params = H.params_for(cfg)
+    p = params.c
+    bsz = cfg.batch
+    pk = np.concatenate([k[cu[b]:cu[b] + lens[b]] for b in range(bsz)])
+    pv = np.concatenate([v[cu[b]:cu[b] + lens[b]] for b in range(bsz)])
+    pcu = torch.from_numpy(np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)).cuda()
+    table, nblk = dgq_data.block_tables(cfg, seed, lens_total=lens + steps)
+    dtable = torch.from_numpy(table).cuda()
+    caches = [Q.DGQCache(params, nblk, bsz) for _ in range(2)]
+    for c in caches:
+        Q.dgq_compress(params, torch.from_numpy(pk).cuda(), torch.from_numpy(pv).cuda(), pcu, dtable, c,
+                       int(lens.max()), int(pk.shape[0]))
+        if corrupt is not None:
+            b, h = corrupt
+            c.tail[b, h, 0] = int(lens[b]) + 1000   # r0 past every new token: the state does not fit
+    ws = [Q.workspace(Q.decode_workspace_size(params, bsz, max_seq_len)) for _ in range(2)]
+    for s in range(steps):
+        pos = lens + s
+        dpos = torch.from_numpy(pos.astype(np.int32)).cuda()
+        ktok = torch.from_numpy(np.stack([k[cu[b] + pos[b]] for b in range(bsz)])).cuda()
+        vtok = torch.from_numpy(np.stack([v[cu[b] + pos[b]] for b in range(bsz)])).cuda()
+        dq = torch.from_numpy(dgq_data.queries(cfg, seed, 0, s)).cuda()
+        Q.dgq_append(params, ktok, vtok, dpos, dtable, caches[0])
+        o_sep = Q.paged_decode_attn_int8(params, dq, caches[0], dtable, dpos + 1, max_seq_len, ws=ws[0])
+        o_fused = Q.dgq_append_decode(params, ktok, vtok, dpos, dq, dtable, caches[1], max_seq_len, ws=ws[1])
+        torch.cuda.synchronize()
+        assert torch.equal(o_sep, o_fused), f"step {s}: fused output differs"
+        assert torch.equal(caches[0].status, caches[1].status), f"step {s}: status differs"
+    _same_cache(caches[0], caches[1], table, lens + steps, p)
+    return caches[1].read_status()
+
+
+def test_fused_clamped_length_matches_separate():
+    """A length past max_seq_len: the decode attends to max_seq_len tokens (counted in status[2])
+    while the append still places the token at its position; the new token then lies outside
+    every wave's tokens and a fixed wave writes it, as in the append kernel."""
+    cfg = dgq_data.get_config(2, batch=2, seq_len=120, append_steps=8)
+    lens = np.asarray(dgq_data.batch_kv(cfg, 45)[3], np.int64)
+    max_seq_len = int(lens.max()) + 3
+    H.say("fused clamped length", lens.tolist(), max_seq_len)
+    st = _fused_vs_separate(cfg, 45, 8, max_seq_len)
+    assert st["inconsistencies"] > 0, st
+
+
+def test_fused_inconsistent_state_skipped_like_append():
+    """An append state that does not fit the new position: nothing is appended for that (sequence,
+    head) in either path, status[2] counts it once per step, and every other head is unchanged."""
+    cfg = dgq_data.get_config(5, batch=2, seq_len=150, append_steps=20)
+    H.say("fused inconsistent append state")
+    st = _fused_vs_separate(cfg, 46, 20, 150 + 20, corrupt=(1, 3))
+    assert st["inconsistencies"] == 20 and st["clamped_appends"] == 0, st
