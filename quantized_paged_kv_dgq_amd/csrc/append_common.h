@@ -191,8 +191,7 @@ __device__ __forceinline__ AppendDecision append_decide(bool want, bool own, int
   return d;
 }
 
-// The append of one token to (sequence b, kv head h), by all 256 threads of a workgroup, in two
-// halves so that a fused decode can put its first chunk's loads between them:
+// The append of one token to (sequence b, kv head h), by the four waves of a workgroup:
 //
 //  * append_begin: every wave, from its own registers (no barrier): the state, the span's new
 //    ranges (DPP and permlane reductions), and the decision unless the window test is due; then,
@@ -200,12 +199,16 @@ __device__ __forceinline__ AppendDecision append_decide(bool want, bool own, int
 //    seals, the requests for the span's fp16 staging copy (one 16-byte unit per thread and pass),
 //    the value-tile words that hold frozen tokens of the same block, and the bitmap byte a new row
 //    would mark.  It stores nothing.
-//  * append_end: the window and ring moments (window test or seal only, with one barrier), the
-//    encode and the code stores; a barrier; then the segment row, bitmap byte, row count and state
-//    stores (after the barrier, so that every wave has read the state they replace).  The code
-//    stores come before that barrier, which orders them before any later load of the tail block
-//    by the same workgroup (a decode of the tail block); other workgroups or kernels only read
-//    them after this launch.
+//  * append_span (the window test, a seal or a re-encoded span; the whole workgroup): the window
+//    and ring moments (one barrier), the encode and the code stores, then a barrier, which orders
+//    the code stores before any later load of the tail block by the same workgroup (a decode of
+//    the tail block); other workgroups or kernels only read them after this launch.
+//  * append_new_token (any other step; one wave, no barrier): the new token's codes and staging
+//    copy.  In a fused decode the wave that decodes the tail block writes them before it reads
+//    that block, so its own stores come first.
+//  * append_stash, then after a barrier append_store_state (wave 0): the status counts, the
+//    segment row, the bitmap byte, the row count and the state, stored only once every wave has
+//    read the state they replace.
 //
 // A re-encoded span's value codes go through an LDS image of the value tile and out as whole
 // 16-byte words: a value tile interleaves the tokens of a block inside each word, so the codes of
@@ -284,8 +287,8 @@ __device__ __forceinline__ uint32_t code_bytes(uint32_t w, int low) {
   return ((w & 0x7F7F7F7Fu) + (c & 0x7F7F7F7Fu)) ^ ((w ^ c) & 0x80808080u);
 }
 
-// What append_begin hands to append_end (uniform across the workgroup, except the staged units,
-// the old value words and the bitmap byte, which stay with the thread that loaded them).
+// What append_begin hands to the later parts (uniform across the workgroup, except the staged
+// units, the old value words and the bitmap byte, which stay with the thread that loaded them).
 template <int D, int BS>
 struct AppendStage {
   static constexpr int CPU = D / 8;                   // 16-byte units per token
@@ -392,7 +395,7 @@ __device__ __forceinline__ void append_begin(const AppendArgs &a, int b, int h, 
     out.chosen = dec.chosen;
   }
 
-  // 4. buffer loads of the earlier span tokens (the new one comes from the registers of wave 0),
+  // 4. buffer loads of the earlier span tokens (the new one comes from its channel pairs),
   // every one issued: a unit that is not needed gets an offset past the resource (zero, no memory
   // access), so no branch separates these loads from the caller's next ones
   const int nunits = span_len * CPU;
