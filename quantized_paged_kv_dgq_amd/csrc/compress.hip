@@ -835,11 +835,37 @@ constexpr int small_waves() { return S / kPerThread / 64; }
 constexpr bool small_cuts_ok(int S_waves, int max_segments) { return max_segments - 1 <= S_waves; }
 static_assert(small_waves<kSmallSeq>() >= kMaxCuts, "the 8192-token instance takes every cut count");
 
+// What the rounds and the range pass keep in LDS: it takes the place of the key moments b_t,
+// which nothing reads once the scores are in registers (so that the 4096-token instance fits three
+// workgroups in a compute unit's LDS).
+template <int S>
+struct SmallSelTail {
+  static constexpr int NW = small_waves<S>();
+  static constexpr int MS = kMaxCuts + 1;
+  float4 ext[S / kWin];          // sub-block extrema
+  float4 red[NW][MS];            // per-wave extrema of each segment's whole sub-blocks
+  float4 raw[kMaxCuts][2];       // cut c: (left part, right part) of the sub-block it splits
+  double gbs[2 * NW];            // wave bests (score, t) of a round, double-buffered
+  int gbt[2 * NW];
+  int cut[kMaxCuts];
+  int start[MS + 1];
+};
+template <int S>
+union SmallSelLds {
+  double bd[skewed_slots<S>()];  // key moments b_t (< 2^36, exact in double), until the scores
+  SmallSelTail<S> tail;
+};
+static_assert(sizeof(SmallSelTail<kSmallSeq / 2>) <= sizeof(double) * skewed_slots<kSmallSeq / 2>(), "fits");
+
+// Three 256-thread workgroups per compute unit for the 4096-token instance (LDS and registers
+// sized for it), one 512-thread workgroup for the 8192-token one.
+template <int S>
+constexpr int small_waves_per_simd() { return S == kSmallSeq / 2 ? 3 : 1; }
+
 template <int D, int S>
-__global__ __launch_bounds__(S / kPerThread) void select_small_kernel(CompressArgs a) {
+__global__ __launch_bounds__(S / kPerThread, small_waves_per_simd<S>()) void select_small_kernel(CompressArgs a) {
   constexpr int NT = S / kPerThread;   // threads
   constexpr int NW = small_waves<S>();
-  constexpr int MS = kMaxCuts + 1;   // segments
   const int h = blockIdx.x, b = blockIdx.y;
   int c0, L;
   bool bad_seq;
@@ -847,14 +873,17 @@ __global__ __launch_bounds__(S / kPerThread) void select_small_kernel(CompressAr
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const size_t bh = (size_t)b * a.hkv + h;
   __shared__ int sa[skewed_slots<S>()];
-  __shared__ double sbd[skewed_slots<S>()];   // key moments b_t (< 2^36, exact in double)
-  __shared__ float4 sext[S / kWin];
-  __shared__ double gbs[2 * NW];   // wave bests (score, t) of a round, double-buffered
-  __shared__ int gbt[2 * NW];
-  __shared__ float4 sred[NW][MS];
-  __shared__ int scut[kMaxCuts];
-  __shared__ int sstart[MS + 1];
+  __shared__ SmallSelLds<S> su;
   __shared__ long long sring_b[kWin];
+  double *sbd = su.bd;
+  SmallSelTail<S> &ov = su.tail;
+  float4 *sext = ov.ext;
+  double *gbs = ov.gbs;
+  int *gbt = ov.gbt;
+  auto &sred = ov.red;
+  int *scut = ov.cut;
+  int *sstart = ov.start;
+  auto &sraw = ov.raw;
   if (tid == 0 && bad_seq && h == 0) atomicAdd(a.cache.status + 2, 1ull);
 
   // ---- key moments and sub-block extrema of the sequence into LDS (all loads issued at once) ----
@@ -881,8 +910,9 @@ __global__ __launch_bounds__(S / kPerThread) void select_small_kernel(CompressAr
     sa[skew(t)] = 0;
     sbd[skew(t)] = 0.0;
   }
+  // the sub-block extrema wait in registers until the key moments' LDS is free
   const int nsub = (L + kWin - 1) / kWin;
-  if (tid < nsub) sext[tid] = a.ws_ext[bh * a.nsub + tid];
+  const float4 ext_in = tid < nsub ? a.ws_ext[bh * a.nsub + tid] : make_float4(0.f, 0.f, 0.f, 0.f);
   __syncthreads();
 
   // ---- scores of this thread's candidates t = 16 * tid + i (window sums slide over LDS) ----
@@ -919,6 +949,8 @@ __global__ __launch_bounds__(S / kPerThread) void select_small_kernel(CompressAr
       }
     }
   }
+  __syncthreads();   // every thread has read the key moments: their LDS now takes the rest
+  if (tid < nsub) sext[tid] = ext_in;
 
   // ---- greedy selection: every thread keeps its 16 scores in registers; per round one wave
   // reduction (DPP), one exchange of the 8 wave bests through LDS, and the suppression of the
@@ -1006,7 +1038,6 @@ __global__ __launch_bounds__(S / kPerThread) void select_small_kernel(CompressAr
     const float4 r = wave_minmax(my_seg == j ? my_ext : ident);
     if (lane == 0) sred[wave][j] = r;
   }
-  __shared__ float4 sraw[kMaxCuts][2];   // cut c: (left part, right part)
   if (wave + 1 < nseg) {
     const int cut = starts[wave + 1];
     float4 left = ident, right = ident;
