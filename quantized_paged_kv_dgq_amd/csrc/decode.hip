@@ -34,331 +34,11 @@
 
 namespace dgq {
 
-template <int D, int G, int BS>
-__global__ __launch_bounds__(64 * kWaves, 2) void decode_partition_kernel(DecodeArgs a) {
-  constexpr int M = D / 64;    // 64-channel slices of a key row
-  constexpr int NT = D / 16;   // 16-channel tiles of the output
-  // the kv head is rotated by the sequence index, so that every XCD serves every head (see
-  // decode_body)
-  const int p = blockIdx.x, b = blockIdx.z, h = (int)((blockIdx.y + blockIdx.z) % (unsigned)a.hkv);
-  const int wave = threadIdx.x >> 6;
-  const int lane = threadIdx.x & 63;
-  const int j = lane >> 4, col = lane & 15, g = col >> 2, piece = col & 3;
-  const bool live = (g < G) && (piece < 3);
-  const ByteSel bsel = byte_sel(piece, live);
-  const int bh = b * a.hkv + h;
-  const int span = a.part_tokens * kWaves;
-  const int wg_begin = p * span;
-
-  // Loads that do not depend on the sequence length go out together with it: the block ids of
-  // the workgroup's span, the segment-table row of this lane and the query slice of this lane.
-  const int32_t *bt = a.block_table + (size_t)b * a.max_blocks;
-  const int wblk0 = wg_begin / BS;
-  SpanBlocks<BS> span_blk;
-  span_blk.load(bt, a.max_blocks, wblk0);
-  const int ns_raw = a.nseg[bh];
-  dgq_seg_t seg_raw = {};
-  if (lane < a.seg_cap) seg_raw = a.segs[(size_t)bh * a.seg_cap + lane];
-  const int qh = h * G + (g < G ? g : 0);
-  const uint16_t *qrow = a.q + ((size_t)b * a.hq + qh) * D;
-  uint4 qraw[M][2];
-#pragma unroll
-  for (int m = 0; m < M; ++m) {
-    const uint4 *src = reinterpret_cast<const uint4 *>(qrow + 64 * m + 16 * j);
-    qraw[m][0] = src[0];
-    qraw[m][1] = src[1];
-  }
-
-  const int L_raw = a.seq_lens[b];
-  const int L = L_raw < 0 ? 0 : (L_raw > a.max_seq_len ? a.max_seq_len : L_raw);
-  if (p == 0 && threadIdx.x == 0 && h == 0 && L != L_raw) atomicAdd(a.status + 2, 1ull);
-  if (L == 0 && p == 0) {                          // an empty sequence attends to nothing: zeros
-    for (int e = threadIdx.x; e < G * D; e += 64 * kWaves) a.out[((size_t)b * a.hq + h * G) * D + e] = 0.f;
-    return;
-  }
-  if (p >= parts_of(L, span)) return;              // the whole workgroup has nothing to do
-  const WaveRange wr = wave_range(wg_begin, span, L, wave);
-  const int t_begin = wr.t_begin, t_end = wr.t_end;
-  const bool active = t_begin < t_end;
-  __shared__ int sh_blk[SpanBlocks<BS>::kBlocks];
-  span_blk.publish(wblk0, (L + BS - 1) / BS, a.num_blocks, sh_blk, a.status);
-  __syncthreads();
-  __shared__ float sh_o[kWaves][G][D];
-  __shared__ float sh_m[kWaves][G], sh_l[kWaves][G];
-
-  float m_run = -INFINITY, l_run = 0.f, mv_run = 0.f;
-  float oacc[NT * 4];   // float output of each lane (C layout), folded from the int32 sums when a maximum moves
-#pragma unroll
-  for (int r = 0; r < NT * 4; ++r) oacc[r] = 0.f;
-  float wv = 0.f;
-
-  if (active) {
-    // block ids come from sh_blk: chunk c of the wave is local chunk lc0 + c of the workgroup
-    const int lc0 = (t_begin - wg_begin) / kChunk;
-    const size_t tile_bytes = (size_t)BS * D;
-    const int8_t *kpool = a.k_pool + (size_t)h * tile_bytes;
-    const int8_t *vpool = a.v_pool + (size_t)h * tile_bytes;
-    const size_t blk_stride = (size_t)a.hkv * tile_bytes;
-
-    // Fragment loads of chunk c (64 tokens) of the partition.  Keys: tile T (16 tokens) x slice m
-    // (64 channels) per A operand; values: channel tile n (16 channels) x 64 tokens per A operand.
-    auto load_k = [&](int c, v4i (&kf)[4][M]) {
-      if constexpr (BS == 64) {
-        const int blk = __builtin_amdgcn_readfirstlane(sh_blk[lc0 + c]);
-        const int8_t *kb = kpool + (size_t)blk * blk_stride;
-#pragma unroll
-        for (int T = 0; T < 4; ++T)
-#pragma unroll
-          for (int m = 0; m < M; ++m)
-            kf[T][m] = load_codes(kb + (((T * M + m) * 64) + lane) * 16);
-      } else {
-        // 16-token blocks, or 32-token blocks made of two 16-token tiles
-        const int g4 = (lane & 15) >> 2;
-        const int8_t *kb = BS == 16 ? kpool + (size_t)sh_blk[4 * (lc0 + c) + g4] * blk_stride
-                                     : kpool + (size_t)sh_blk[2 * (lc0 + c) + (g4 >> 1)] * blk_stride + (g4 & 1) * 16 * D;
-#pragma unroll
-        for (int T = 0; T < 4; ++T)
-#pragma unroll
-          for (int m = 0; m < M; ++m)
-            kf[T][m] = load_codes(kb + ((((T * M + m) * 4 + j) * 4 + (lane & 3)) * 16));
-      }
-    };
-    auto load_v = [&](int c, v4i (&vf)[NT]) {
-      if constexpr (BS == 64) {
-        const int blk = __builtin_amdgcn_readfirstlane(sh_blk[lc0 + c]);
-        const int8_t *vb = vpool + (size_t)blk * blk_stride;
-#pragma unroll
-        for (int n = 0; n < NT; ++n) vf[n] = load_codes(vb + (n * 64 + lane) * 16);
-      } else {
-        const int8_t *vb = BS == 16 ? vpool + (size_t)sh_blk[4 * (lc0 + c) + j] * blk_stride
-                                     : vpool + (size_t)sh_blk[2 * (lc0 + c) + (j >> 1)] * blk_stride + (j & 1) * 16 * D;
-#pragma unroll
-        for (int n = 0; n < NT; ++n) vf[n] = load_codes(vb + (16 * n + (lane & 15)) * 16);
-      }
-    };
-    // the first chunk goes out before the segment rows and the query are prepared
-    const int nchunks = (t_end - t_begin + kChunk - 1) / kChunk;
-    v4i kf[4][M];
-    v4i vf[NT];
-    load_k(0, kf);
-    load_v(0, vf);
-    // ---- segment table: lane k holds row k ----
-    const int ns = min(ns_raw, a.seg_cap);
-    int s_start = INT_MAX;
-    float s_ks = 0.f, s_midk = 0.f, s_vs = 0.f, s_midv = 0.f;
-    if (lane < ns) {
-      const dgq_seg_t sg = seg_raw;
-      s_start = sg.start;
-      s_ks = sg.kscale;
-      s_midk = sg.kmin + a.code_mid * sg.kscale;
-      s_vs = sg.vscale;
-      s_midv = sg.vmin + a.code_mid * sg.vscale;
-    }
-    // the largest value scale among the segments this wave's tokens can use (rows starting after
-    // its last token cannot apply; leaving them out also keeps the result equal to the fused
-    // append + decode step, where the open span's row may change while other workgroups run)
-    float vsmax = s_start <= t_end - 1 ? s_vs : 0.f;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) vsmax = fmaxf(vsmax, __shfl_xor(vsmax, o));
-    const float wfac_unit = vsmax > 0.f ? 4194304.0f / vsmax : 0.f;   // 2^22 / vsmax
-    const float s_wf = s_vs * wfac_unit;
-    wv = live ? ldexpf(vsmax, -6 - 8 * piece) : 0.f;                // 2^(16-8*piece) * vsmax / 2^22
-
-    // ---- query: three signed bytes per channel, one per column of the B operand ----
-    float qv[M][16];
-    float amax = 0.f, qsum = 0.f;
-#pragma unroll
-    for (int m = 0; m < M; ++m) {
-      const uint4 w0 = qraw[m][0], w1 = qraw[m][1];
-      const uint32_t ws[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        qv[m][2 * e] = half_bits_to_float(ws[e] & 0xFFFFu);
-        qv[m][2 * e + 1] = half_bits_to_float(ws[e] >> 16);
-      }
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        amax = fmaxf(amax, fabsf(qv[m][e]));
-        qsum += qv[m][e];
-      }
-    }
-    amax = fmaxf(amax, __shfl_xor(amax, 16));
-    amax = fmaxf(amax, __shfl_xor(amax, 32));
-    qsum += __shfl_xor(qsum, 16);
-    qsum += __shfl_xor(qsum, 32);
-    int qexp = 0;
-    if (amax > 0.f) {
-      int ex;
-      frexpf(amax, &ex);
-      qexp = 22 - ex;   // amax * 2^qexp in [2^21, 2^22)
-    }
-    const float qmul = ldexpf(1.0f, qexp);
-    v4i qfrag[M];
-#pragma unroll
-    for (int m = 0; m < M; ++m) {
-      uint32_t wq4[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-      for (int e = 0; e < 16; ++e) wq4[e >> 2] |= sel_byte(fmaf(qv[m][e], qmul, kMagic), bsel) << (8 * (e & 3));
-      qfrag[m] = v4i{(int)wq4[0], (int)wq4[1], (int)wq4[2], (int)wq4[3]};
-    }
-    // per-lane weight of this byte's partial dot product, in log2 units of the softmax
-    const float wq = live ? ldexpf(a.sm_log2, 16 - 8 * piece - qexp) : 0.f;
-    const float qsum_s = qsum * a.sm_log2;
-
-    // segment index of token t (rows are sorted by start; row 0 starts at 0)
-    auto seg_of = [&](int t) -> int {
-      int idx = 0;
-      for (int k = 1; k < ns; ++k) idx += (t >= __builtin_amdgcn_readlane(s_start, k)) ? 1 : 0;
-      return idx;
-    };
-
-    v4i cacc[NT];   // int32 PV sums since the last fold into O
-#pragma unroll
-    for (int n = 0; n < NT; ++n) cacc[n] = v4i{0, 0, 0, 0};
-
-    for (int c = 0; c < nchunks; ++c) {
-      const int t0 = t_begin + c * kChunk;
-
-      // S^T = K . Q^T : rows = tokens of tile T, columns = (query head, byte)
-      float S[4][4];
-#pragma unroll
-      for (int T = 0; T < 4; ++T) {
-        v4i acc = {0, 0, 0, 0};
-#pragma unroll
-        for (int m = 0; m < M; ++m) acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(kf[T][m], qfrag[m], acc, 0, 0, 0);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) S[T][i] = (float)acc[i] * wq;
-      }
-      if (c + 1 < nchunks) load_k(c + 1, kf);
-#pragma unroll
-      for (int T = 0; T < 4; ++T)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float s = S[T][i];
-          s += quad_xor1(s);
-          s += quad_xor2(s);
-          S[T][i] = s;
-        }
-
-      // token of (T, i) for this lane
-      auto tok_of = [&](int T, int i) -> int {
-        return BS == 64 ? t0 + 16 * T + 4 * j + i : t0 + 16 * j + 4 * T + i;
-      };
-
-      // scores in log2 units, with the segment's (ks, midK) of every token
-      const int t_last = min(t0 + kChunk, t_end) - 1;
-      const int sf = max(__popcll(__ballot(s_start <= t0)) - 1, 0);
-      const int sl = max(__popcll(__ballot(s_start <= t_last)) - 1, 0);
-      const bool uni = sf == sl;
-      if (uni) {
-        const float ks = readlane_f(s_ks, sf), mk = readlane_f(s_midk, sf) * qsum_s;
-#pragma unroll
-        for (int T = 0; T < 4; ++T)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) S[T][i] = fmaf(ks, S[T][i], mk);
-      } else {
-#pragma unroll
-        for (int T = 0; T < 4; ++T)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int idx = seg_of(tok_of(T, i));
-            S[T][i] = fmaf(__shfl(s_ks, idx), S[T][i], __shfl(s_midk, idx) * qsum_s);
-          }
-      }
-      if (t0 + kChunk > t_end) {   // partial last chunk: tokens past the end weigh nothing
-#pragma unroll
-        for (int T = 0; T < 4; ++T)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) S[T][i] = tok_of(T, i) < t_end ? S[T][i] : -INFINITY;
-      }
-
-      // online softmax (base 2)
-      float cmax = -INFINITY;
-#pragma unroll
-      for (int T = 0; T < 4; ++T)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) cmax = fmaxf(cmax, S[T][i]);
-      cmax = max_xor32(max_xor16(cmax));
-      const float m_new = fmaxf(m_run, cmax);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      if (__ballot(m_new > m_run) != 0ull) {
-        // some head's maximum moved: fold the int32 sums (relative to the old maximum) into O
-#pragma unroll
-        for (int n = 0; n < NT; ++n) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) oacc[4 * n + i] = (oacc[4 * n + i] + (float)cacc[n][i]) * alpha;
-          cacc[n] = v4i{0, 0, 0, 0};
-        }
-      }
-      m_run = m_new;
-      float psum = 0.f, pmv = 0.f;
-      uint32_t pw[4] = {0u, 0u, 0u, 0u};
-      if (uni) {
-        const float wfs = readlane_f(s_wf, sf), mvs = readlane_f(s_midv, sf);
-#pragma unroll
-        for (int T = 0; T < 4; ++T)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float pr = __builtin_amdgcn_exp2f(S[T][i] - m_new);
-            psum += pr;
-            pw[T] |= sel_byte(fmaf(pr, wfs, kMagic), bsel) << (8 * i);
-          }
-        pmv = psum * mvs;
-      } else {
-#pragma unroll
-        for (int T = 0; T < 4; ++T)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int idx = seg_of(tok_of(T, i));
-            const float pr = __builtin_amdgcn_exp2f(S[T][i] - m_new);
-            psum += pr;
-            pmv = fmaf(pr, __shfl(s_midv, idx), pmv);
-            pw[T] |= sel_byte(fmaf(pr, __shfl(s_wf, idx), kMagic), bsel) << (8 * i);
-          }
-      }
-      l_run = fmaf(l_run, alpha, psum);
-      mv_run = fmaf(mv_run, alpha, pmv);
-      const v4i pfrag = v4i{(int)pw[0], (int)pw[1], (int)pw[2], (int)pw[3]};
-
-      // O^T += V^T . P^T : rows = channels of tile n, columns = (query head, byte)
-#pragma unroll
-      for (int n = 0; n < NT; ++n) cacc[n] = __builtin_amdgcn_mfma_i32_16x16x64_i8(vf[n], pfrag, cacc[n], 0, 0, 0);
-      if (c + 1 < nchunks) load_v(c + 1, vf);
-    }
-#pragma unroll
-    for (int n = 0; n < NT; ++n)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) oacc[4 * n + i] += (float)cacc[n][i];
-  }
-
-  // ---- epilogue: combine the byte columns and the mid term per wave, then merge the waves of
-  // the workgroup in LDS and write one partial (m, l, o) per query head ----
-  l_run += __shfl_xor(l_run, 16);
-  l_run += __shfl_xor(l_run, 32);
-  mv_run += __shfl_xor(mv_run, 16);
-  mv_run += __shfl_xor(mv_run, 32);
-#pragma unroll
-  for (int n = 0; n < NT; ++n)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float v = oacc[4 * n + i] * wv;
-      v += quad_xor1(v);
-      v += quad_xor2(v);
-      if (piece == 0 && g < G) sh_o[wave][g][16 * n + 4 * j + i] = active ? v + mv_run : 0.f;
-    }
-  if (j == 0 && piece == 0 && g < G) {
-    sh_m[wave][g] = active ? m_run : -INFINITY;
-    sh_l[wave][g] = active ? l_run : 0.f;
-  }
-  finish_partition<D, G>(a, b, h, p, L, sh_o, sh_m, sh_l);
-}
-
-// The fused append + decode step.  The same decode as decode_partition_kernel, except that
+// The decode of one workgroup; APPEND = true is the fused append + decode step, in which
 // seq_lens holds the lengths before this step's token: the workgroup of the last partition of
-// (b, h), the one whose tokens include the tail block, first appends the token (append_one) and
-// decodes with the updated segment rows; the new row count is published once every workgroup of
-// (b, h) is done.  (The plain kernel keeps its own copy of the body: compiling it through this
-// templated body, APPEND = false, made it 3-5 % slower with bit-identical results.)
+// (b, h), the one whose tokens include the tail block, first appends the token and decodes with
+// the updated segment rows; the new row count is published once every workgroup of (b, h) is
+// done.
 template <int D, int G, int BS, bool APPEND>
 __device__ __forceinline__ void decode_body(const DecodeArgs &a, const AppendArgs *ap) {
   constexpr int M = D / 64;    // 64-channel slices of a key row
@@ -759,6 +439,11 @@ __device__ __forceinline__ void decode_body(const DecodeArgs &a, const AppendArg
   }
 }
 
+
+template <int D, int G, int BS>
+__global__ __launch_bounds__(64 * kWaves, 2) void decode_partition_kernel(DecodeArgs a) {
+  decode_body<D, G, BS, false>(a, nullptr);
+}
 
 template <int D, int G, int BS>
 __global__ __launch_bounds__(64 * kWaves, 2) void append_decode_kernel(DecodeArgs a, AppendArgs ap) {
