@@ -302,7 +302,7 @@ struct AppendStage {
   dgq_seg_t R;              // row ns - 1 before the append
   int t, r0, slot0, span_len, nunits, blk, ns, ring_len, nbad;
   bool go;                  // false: the state did not fit, nothing was appended
-  bool own, wdone, window_test, seal;
+  bool window_test, seal;
 };
 
 template <int D, int BS>
@@ -434,8 +434,6 @@ __device__ __forceinline__ void append_begin(const AppendArgs &a, int b, int h, 
   st.blk = blk_t;
   st.ns = ns;
   st.ring_len = ring_len;
-  st.own = own;
-  st.wdone = wdone;
   st.window_test = window_test;
   st.seal = seal;
 }
