@@ -423,6 +423,24 @@ __global__ __launch_bounds__(256) void scores_kernel(CompressArgs a) {
   if (tile0 * 256 >= L) return;
   const int tid = threadIdx.x;
   const size_t bh = (size_t)b * a.hkv + h;
+  // the key moments of the tiles and the 16 tokens on either side, requested first (into
+  // registers) so that their round trip overlaps the extrema's
+  constexpr int NM = TW * 256 + 2 * kWin;
+  constexpr int NL = (NM + 255) / 256;
+  const int base = tile0 * 256 - kWin;
+  int ra[NL];
+  long long rb[NL];
+#pragma unroll
+  for (int u = 0; u < NL; ++u) {
+    const int i = tid + 256 * u, tok = base + i;
+    ra[u] = 0;
+    rb[u] = 0;
+    if (i < NM && tok >= 0 && tok < L) {
+      const size_t idx = (size_t)h * a.total + c0 + tok;
+      ra[u] = a.ws_a[idx];
+      rb[u] = a.ws_b[idx];
+    }
+  }
   // each tile's K/V extrema from its sub-blocks (for the segment ranges of the selection): wave q
   // takes tile tile0 + q
   if (tid < 64 * TW) {
@@ -435,22 +453,18 @@ __global__ __launch_bounds__(256) void scores_kernel(CompressArgs a) {
     if (k == 0 && tile * 256 < L) a.ws_text[bh * a.ntile + tile] = r;
   }
   if (L < 2 * kWin || tile0 * 256 > L - kWin) return;
-  __shared__ int sa[TW * 256 + 2 * kWin];
-  __shared__ long long sbm[TW * 256 + 2 * kWin];
+  __shared__ int sa[NM];
+  __shared__ long long sbm[NM];
   __shared__ int wa[TW * 256 + kWin];           // window sums: wa[i] = sa[i] + ... + sa[i + 15]
   __shared__ long long wbm[TW * 256 + kWin];
   __shared__ double best_s[TW][4];
   __shared__ int best_t[TW][4];
-  const int base = tile0 * 256 - kWin;
-  for (int i = tid; i < TW * 256 + 2 * kWin; i += 256) {
-    const int tok = base + i;
-    if (tok >= 0 && tok < L) {
-      const size_t idx = (size_t)h * a.total + c0 + tok;
-      sa[i] = a.ws_a[idx];
-      sbm[i] = a.ws_b[idx];
-    } else {
-      sa[i] = 0;
-      sbm[i] = 0;
+#pragma unroll
+  for (int u = 0; u < NL; ++u) {
+    const int i = tid + 256 * u;
+    if (i < NM) {
+      sa[i] = ra[u];
+      sbm[i] = rb[u];
     }
   }
   __syncthreads();
