@@ -546,6 +546,15 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(CompressArgs a) {
   __shared__ int cuts[kMaxCuts];
   __shared__ int starts[kMaxCuts + 2];
   if (tid == 0 && bad_seq && h == 0) atomicAdd(a.cache.status + 2, 1ull);
+  // the moments of the last min(16, L) tokens, for the append state written at the end
+  const int rl = min(kWin, L);
+  int ring_a = 0;
+  long long ring_b = 0;
+  if (tid < rl) {
+    const size_t idx = (size_t)h * a.total + c0 + (L - rl + tid);
+    ring_a = a.ws_a[idx];
+    ring_b = a.ws_b[idx];
+  }
 
   // ---- greedy selection over the tile maxima ----
   double2 *gtiles = a.ws_tile + bh * a.ntile;
@@ -695,42 +704,65 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(CompressArgs a) {
     for (int j = 0; j < MS; ++j) sred[wave][j] = ident;
   if (tid < kMaxCuts * MS) scut[tid / MS][tid % MS] = ident;
   __syncthreads();
-  {
-    const float4 *text = a.ws_text + bh * a.ntile;
-    const int ntl = (L + 255) / 256;
-    for (int i0 = 0; i0 < ntl; i0 += kSelThreads) {
-      const int i = i0 + tid;
-      float4 x = ident;
-      int j0 = -1;
-      if (i < ntl) {
-        const int t0 = 256 * i, t1 = min(t0 + 256, L);
-        j0 = seg_of(t0);
-        if (seg_of(t1 - 1) == j0) x = text[i];
-        else j0 = -1;                                // (2)
-      }
-      for (int j = 0; j < nseg; ++j) {
-        const float4 r = wave_minmax(j0 == j ? x : ident);
-        if (lane == 0) fold(sred[wave][j], r);
-      }
+  // Every load of the three parts is requested before any reduction (one round trip, not three).
+  const float4 *text = a.ws_text + bh * a.ntile;
+  const int ntl = (L + 255) / 256;
+  auto tile_ext = [&](int i, float4 &x, int &j0) {   // (1): tile i, if one segment holds it
+    x = ident;
+    j0 = -1;
+    if (i < ntl) {
+      const int t0 = 256 * i, t1 = min(t0 + 256, L);
+      j0 = seg_of(t0);
+      if (seg_of(t1 - 1) == j0) x = text[i];
+      else j0 = -1;                                  // (2)
+    }
+  };
+  float4 tx;
+  int tj;
+  tile_ext(tid, tx, tj);
+  const int g = tid >> 4, k = tid & 15;              // (2): 16-lane group g takes cut g's tile
+  const bool on = wave < (kMaxCuts + 3) / 4 && g < nc && !(g > 0 && starts[g] / 256 == starts[g + 1] / 256);
+  float4 ex = ident;
+  int ej = -1;
+  if (on) {
+    const int sb = 16 * (starts[g + 1] / 256) + k;
+    const int s0 = kWin * sb, s1 = min(s0 + kWin, L);
+    if (s0 < L) {
+      ej = seg_of(s0);
+      if (s1 <= starts[ej + 1]) ex = a.ws_ext[bh * a.nsub + sb];
+      else ej = -1;                                  // (3)
+    }
+  }
+  const bool raw_on = wave + 1 < nseg;               // (3): wave c - 1 re-reads cut c's sub-block
+  const int cut = raw_on ? starts[min(wave + 1, kMaxCuts + 1)] : 0;
+  const int t0r = cut - cut % kWin;
+  constexpr int PER_LANE = kWin * D / 64;            // halves of the sub-block per lane
+  uint4 kw[PER_LANE / 8], vw[PER_LANE / 8];
+#pragma unroll
+  for (int e = 0; e < PER_LANE / 8; ++e) {
+    kw[e] = make_uint4(0u, 0u, 0u, 0u);
+    vw[e] = make_uint4(0u, 0u, 0u, 0u);
+    const int x = lane * PER_LANE + 8 * e;
+    const int tok = t0r + x / D, d = x % D;
+    if (raw_on && cut % kWin != 0 && tok < L) {
+      const size_t off = (size_t)(c0 + tok) * a.stride_tok + (size_t)h * a.stride_head + d;
+      kw[e] = *reinterpret_cast<const uint4 *>(a.k + off);
+      vw[e] = *reinterpret_cast<const uint4 *>(a.v + off);
+    }
+  }
+
+  for (int i0 = 0; i0 < ntl; i0 += kSelThreads) {
+    float4 x = tx;
+    int j0 = tj;
+    if (i0 > 0) tile_ext(i0 + tid, x, j0);
+    for (int j = 0; j < nseg; ++j) {
+      const float4 r = wave_minmax(j0 == j ? x : ident);
+      if (lane == 0) fold(sred[wave][j], r);
     }
   }
   if (wave < (kMaxCuts + 3) / 4) {
-    const float4 *ext = a.ws_ext + bh * a.nsub;
-    const int g = tid >> 4, k = tid & 15;
-    const bool on = g < nc && !(g > 0 && starts[g] / 256 == starts[g + 1] / 256);
-    float4 x = ident;
-    int j = -1;
-    if (on) {
-      const int sb = 16 * (starts[g + 1] / 256) + k;
-      const int s0 = kWin * sb, s1 = min(s0 + kWin, L);
-      if (s0 < L) {
-        j = seg_of(s0);
-        if (s1 <= starts[j + 1]) x = ext[sb];
-        else j = -1;                                 // (3)
-      }
-    }
     for (int jj = 0; jj < nseg; ++jj) {
-      float4 r = j == jj ? x : ident;
+      float4 r = ej == jj ? ex : ident;
       auto step = [&](auto tag) {
         constexpr int C = decltype(tag)::value;
         r.x = fminf(r.x, dpp_f<C>(r.x));
@@ -745,27 +777,13 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(CompressArgs a) {
       if (on && k == 0) scut[g][jj] = r;
     }
   }
-  if (wave + 1 < nseg) {
-    const int cut = starts[wave + 1];
+  if (raw_on) {
     float4 left = ident, right = ident;
     if (cut % kWin != 0) {
-      const int t0 = cut - cut % kWin;
-      constexpr int PER_LANE = kWin * D / 64;   // halves of the sub-block per lane
-      uint4 kw[PER_LANE / 8], vw[PER_LANE / 8];
 #pragma unroll
       for (int e = 0; e < PER_LANE / 8; ++e) {
         const int x = lane * PER_LANE + 8 * e;
-        const int tok = t0 + x / D, d = x % D;
-        if (tok < L) {
-          const size_t off = (size_t)(c0 + tok) * a.stride_tok + (size_t)h * a.stride_head + d;
-          kw[e] = *reinterpret_cast<const uint4 *>(a.k + off);
-          vw[e] = *reinterpret_cast<const uint4 *>(a.v + off);
-        }
-      }
-#pragma unroll
-      for (int e = 0; e < PER_LANE / 8; ++e) {
-        const int x = lane * PER_LANE + 8 * e;
-        const int tok = t0 + x / D;
+        const int tok = t0r + x / D;
         if (tok < L) {
           const uint32_t kk[4] = {kw[e].x, kw[e].y, kw[e].z, kw[e].w}, vv[4] = {vw[e].x, vw[e].y, vw[e].z, vw[e].w};
           float4 r = ident;
@@ -805,12 +823,10 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(CompressArgs a) {
     a.cache.segs[bh * a.seg_cap + tid] = row;
   }
   // append state: open span starts at L, ring = the last min(16, L) tokens' moments
-  const int rl = min(kWin, L);
   dgq_tail_t *tl = a.cache.tail + bh;
   if (tid < kWin) {
-    const size_t idx = (size_t)h * a.total + c0 + (L - rl + tid);
-    tl->ring_a[tid] = tid < rl ? a.ws_a[idx] : 0;
-    tl->ring_b[tid] = tid < rl ? a.ws_b[idx] : 0;
+    tl->ring_a[tid] = ring_a;
+    tl->ring_b[tid] = ring_b;
   }
   if (tid < 4) tl->span_range[tid] = 0.f;
   if (tid == 0) {
