@@ -121,6 +121,21 @@ def test_compress_length_cap_and_variance_floor(name, cid, over, length_aware, m
     print(f"{name}: segments per head {counts.tolist()}")
 
 
+def test_compress_beyond_lds_tile_limit():
+    """A 1.1M-token sequence (4,297 tiles of 256 candidates): more tile maxima than the selection
+    keeps in LDS (4,096), so its greedy rounds read and update them in the workspace, and more tiles
+    than one pass of its range reduction covers (1,024 per pass).  Segments, codes and bits against
+    the oracle, then a decode over the whole sequence."""
+    cfg = dgq_data.get_config(1, seq_len=1_100_000, block_size=64)
+    assert (cfg.seq_len - 16) // 256 + 1 > 4096
+    H.say("compress beyond the LDS tile limit", cfg.seq_len)
+    params = H.params_for(cfg, max_segments=8, tau=1.5)
+    _, heads, _ = compress_and_check(cfg, 51, params=params)
+    nseg = [len(hc.segs) for hc in heads.values()]
+    print(f"segments per head {nseg}")
+    assert max(nseg) > 2
+
+
 MARKER_CASES = [
     ("tiny", 1, {}),
     ("llama_bs16", 2, dict(batch=2, seq_len=1500)),
