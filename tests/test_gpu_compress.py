@@ -136,6 +136,18 @@ def test_compress_beyond_lds_tile_limit():
     assert max(nseg) > 2
 
 
+@pytest.mark.parametrize("marker", [False, True], ids=["bitmap", "marker"])
+def test_compress_long_path_seven_cuts(marker):
+    """The tiled selection with eight segments (tau = 1 takes a cut every round, as no score is
+    below 1): seven cuts per head, some sharing a 256-token tile, so the range reduction's
+    cut-tile groups span two waves and skip tiles an earlier cut already took."""
+    cfg = dgq_data.get_config(3, seq_len=12000)
+    H.say("compress long path seven cuts", marker)
+    params = H.params_for(cfg, max_segments=8, tau=1.0, marker=marker)
+    _, heads, _ = compress_and_check(cfg, 61, params=params)
+    assert all(len(hc.segs) == 8 for hc in heads.values())
+
+
 MARKER_CASES = [
     ("tiny", 1, {}),
     ("llama_bs16", 2, dict(batch=2, seq_len=1500)),
