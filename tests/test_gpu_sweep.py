@@ -4,7 +4,8 @@ lengths (down to one token), sequential and shuffled block tables, outliers, seg
 tau 1.25..3, the length-aware cap, the variance floor, and both identifier formats.  Every case
 runs the full oracle comparison of the compress tests (segments, codes, identifiers, append state,
 decode); stream cases then append token by token, and fused cases run the fused step against the
-separate calls, all against the oracle."""
+separate calls, all against the oracle.  Long cases (8,200 to 24,000 tokens) take the tiled
+selection with the same random settings."""
 
 import numpy as np
 import pytest
@@ -46,6 +47,25 @@ def draw_case(idx: int, streaming: bool):
     return cfg, kw
 
 
+def draw_long_case(idx: int):
+    """A batch whose longest sequence takes the tiled selection (more than 8,192 tokens), with the
+    random settings of draw_case (its own seeds, so the other cases are unchanged)."""
+    rng = np.random.default_rng([2026, idx, 2])
+    hkv = int(rng.choice([1, 2]))
+    group = int(rng.choice([1, 2, 4]))
+    seq_len = int(rng.integers(8200, 24001))
+    over = dict(append_steps=0, min_len=int(rng.choice([0, 1, seq_len // 2])), batch=int(rng.integers(1, 3)),
+                hkv=hkv, hq=hkv * group, head_dim=int(rng.choice([64, 128])),
+                block_size=int(rng.choice([16, 32, 64])), seq_len=seq_len,
+                table=str(rng.choice(["sequential", "shuffled"])), outlier_frac=float(rng.choice([0.0, 0.01])),
+                nseg_choices=tuple(int(x) for x in rng.choice([2, 3, 4, 5], size=2)))
+    cfg = dgq_data.get_config(2, **over)
+    kw = dict(max_segments=int(rng.choice([2, 3, 5, 8])), tau=float(rng.choice([1.0, 1.25, 2.0, 3.0])),
+              length_aware=bool(rng.integers(0, 2)), min_var=float(rng.choice([0.0, 1e-3, 1e-2])),
+              marker=bool(rng.integers(0, 2)))
+    return cfg, kw
+
+
 @pytest.mark.parametrize("idx", range(16))
 def test_sweep_compress_decode(idx):
     cfg, kw = draw_case(idx, False)
@@ -67,3 +87,10 @@ def test_sweep_fused_step(idx):
     H.say("sweep fused", idx, cfg, kw)
     steps = cfg.append_steps
     run_fused(cfg, 300 + idx, steps, {steps // 2, steps - 1}, params=H.params_for(cfg, **kw))
+
+
+@pytest.mark.parametrize("idx", range(6))
+def test_sweep_long_compress_decode(idx):
+    cfg, kw = draw_long_case(idx)
+    H.say("sweep long compress", idx, cfg, kw)
+    compress_and_check(cfg, 400 + idx, params=H.params_for(cfg, **kw))
