@@ -157,3 +157,26 @@ def test_stream_marker_format(cid, over, steps):
     cfg = dgq_data.get_config(cid, **over)
     H.say("append marker format", cid, over)
     run_stream(cfg, 17, steps, params=H.params_for(cfg, marker=True), check_every=steps // 3)
+
+
+def growing_values(cfg, prefix, steps, seed):
+    """One sequence: keys N(0, 0.25), values whose standard deviation grows by 15 % per block, so
+    that the span of almost every appended block leaves the range of the row before it and takes a
+    row of its own, until the segment table is full."""
+    rng = np.random.default_rng(seed)
+    n = prefix + steps
+    amp = 1.15 ** (np.arange(n) // cfg.block_size)
+    k = (rng.standard_normal((n, cfg.hkv, cfg.head_dim)) * 0.5).astype(np.float16)
+    v = (rng.standard_normal((n, cfg.hkv, cfg.head_dim)) * 0.5 * amp[:, None, None]).astype(np.float16)
+    return k, v, np.array([0, n], np.int32), np.array([prefix], np.int64)
+
+
+def test_stream_fills_largest_segment_table():
+    """A 64-row segment table (the largest) filled by appended blocks, then the table-full clamp:
+    rows, codes, bits, append state, the clamp count and the decode against the oracle."""
+    cfg = dgq_data.get_config(1, batch=1, seq_len=64, append_steps=1100, block_size=16)
+    H.say("append stream through a full 64-row segment table")
+    params = H.params_for(cfg, max_segments=8, seg_capacity=64)
+    k, v, cu, lens = growing_values(cfg, 64, 1100, 7)
+    _, states = run_stream(cfg, 7, 1100, params=params, check_every=275, k=k, v=v, cu=cu, lens=lens)
+    assert all(len(st.snapshot().segs) == 64 and st.clamped > 0 for st in states.values())

@@ -35,8 +35,8 @@ def _same_cache(c1, c2, table, lens, p):
                                       PL.gather_bits(b2, table[b], h, n, p.block_size))
 
 
-def run_fused(cfg, seed, steps, checks, params=None):
-    k, v, cu, lens = dgq_data.batch_kv(cfg, seed)
+def run_fused(cfg, seed, steps, checks, params=None, data=None):
+    k, v, cu, lens = data if data is not None else dgq_data.batch_kv(cfg, seed)
     lens = np.asarray(lens, np.int64)
     params = params or H.params_for(cfg)
     p = params.c
@@ -177,3 +177,13 @@ def test_fused_inconsistent_state_skipped_like_append():
     H.say("fused inconsistent append state")
     st = _fused_vs_separate(cfg, 46, 20, 150 + 20, corrupt=(1, 3))
     assert st["inconsistencies"] == 20 and st["clamped_appends"] == 0, st
+
+
+def test_fused_fills_largest_segment_table():
+    """The fused step on a head whose appended blocks each take a row of their own, through the
+    largest segment table (64 rows) and on into the table-full clamp."""
+    from test_gpu_append import growing_values
+    cfg = dgq_data.get_config(1, batch=1, seq_len=64, append_steps=1100, block_size=16)
+    H.say("fused step through a full 64-row segment table")
+    params = H.params_for(cfg, max_segments=8, seg_capacity=64)
+    run_fused(cfg, 7, 1100, (0, 550, 1099), params=params, data=growing_values(cfg, 64, 1100, 7))
