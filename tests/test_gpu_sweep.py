@@ -5,7 +5,8 @@ tau 1.25..3, the length-aware cap, the variance floor, and both identifier forma
 runs the full oracle comparison of the compress tests (segments, codes, identifiers, append state,
 decode); stream cases then append token by token, and fused cases run the fused step against the
 separate calls, all against the oracle.  Long cases (8,200 to 24,000 tokens) take the tiled
-selection with the same random settings."""
+selection with the same random settings; long fused cases split each sequence over several
+workgroups, so the appending one hands the row count to the one that merges."""
 
 import numpy as np
 import pytest
@@ -47,14 +48,14 @@ def draw_case(idx: int, streaming: bool):
     return cfg, kw
 
 
-def draw_long_case(idx: int):
+def draw_long_case(idx: int, append_steps: int = 0):
     """A batch whose longest sequence takes the tiled selection (more than 8,192 tokens), with the
     random settings of draw_case (its own seeds, so the other cases are unchanged)."""
     rng = np.random.default_rng([2026, idx, 2])
     hkv = int(rng.choice([1, 2]))
     group = int(rng.choice([1, 2, 4]))
     seq_len = int(rng.integers(8200, 24001))
-    over = dict(append_steps=0, min_len=int(rng.choice([0, 1, seq_len // 2])), batch=int(rng.integers(1, 3)),
+    over = dict(append_steps=append_steps, min_len=int(rng.choice([0, 1, seq_len // 2])), batch=int(rng.integers(1, 3)),
                 hkv=hkv, hq=hkv * group, head_dim=int(rng.choice([64, 128])),
                 block_size=int(rng.choice([16, 32, 64])), seq_len=seq_len,
                 table=str(rng.choice(["sequential", "shuffled"])), outlier_frac=float(rng.choice([0.0, 0.01])),
@@ -94,3 +95,10 @@ def test_sweep_long_compress_decode(idx):
     cfg, kw = draw_long_case(idx)
     H.say("sweep long compress", idx, cfg, kw)
     compress_and_check(cfg, 400 + idx, params=H.params_for(cfg, **kw))
+
+
+@pytest.mark.parametrize("idx", range(6, 9))
+def test_sweep_long_fused_step(idx):
+    cfg, kw = draw_long_case(idx, append_steps=40)
+    H.say("sweep long fused", idx, cfg, kw)
+    run_fused(cfg, 500 + idx, 40, {20, 39}, params=H.params_for(cfg, **kw))
