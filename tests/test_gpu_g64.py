@@ -80,7 +80,9 @@ def run_g64(cfg, seed, steps):
     (5, dict(batch=3, seq_len=200, append_steps=70), 70),
     (2, dict(batch=2, seq_len=700, append_steps=20), 20),
     (1, dict(hq=4, block_size=64, seq_len=300, append_steps=9), 9),
-], ids=["bs64_stream", "bs16_stream", "d64_g2"])
+    (1, dict(seq_len=300, append_steps=9), 9),
+    (4, dict(batch=3, seq_len=600, hkv=4, hq=4, append_steps=10), 10),
+], ids=["bs64_stream", "bs16_stream", "d64_g2", "d64_g1", "mha_g1_ragged"])
 def test_g64_matches_oracle(cid, over, steps):
     cfg = dgq_data.get_config(cid, **over)
     H.say("g64", cid, over)
