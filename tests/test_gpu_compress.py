@@ -148,6 +148,20 @@ def test_compress_long_path_seven_cuts(marker):
     assert all(len(hc.segs) == 8 for hc in heads.values())
 
 
+def test_compress_long_batch_with_empty_and_tiny_sequences():
+    """The tiled selection (the batch's longest sequence has 9,000 tokens) on a batch that also
+    holds an empty and a 5-token sequence: no tiles, and fewer tokens than one window."""
+    cfg = dgq_data.get_config(3, batch=3, hkv=2, hq=8, seq_len=9000)
+    k, v, cu, _ = dgq_data.batch_kv(cfg, 71)
+    lens = np.array([0, 9000, 5], np.int64)
+    kk = np.concatenate([k[cu[b]:cu[b] + lens[b]] for b in range(3)])
+    vv = np.concatenate([v[cu[b]:cu[b] + lens[b]] for b in range(3)])
+    cu2 = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    H.say("compress long batch with empty and tiny sequences")
+    _, heads, _ = compress_and_check(cfg, 71, k=kk, v=vv, cu=cu2, lens=lens)
+    assert len(heads[(0, 0)].segs) == 0 and len(heads[(2, 1)].segs) == 1
+
+
 MARKER_CASES = [
     ("tiny", 1, {}),
     ("llama_bs16", 2, dict(batch=2, seq_len=1500)),
